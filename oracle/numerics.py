@@ -1,0 +1,297 @@
+"""Float64 reference forward pass of a pre-norm Llama/Qwen decoder (test infrastructure).
+
+The pages (MegaOps abstract; "Production Megakernels" lecture summary) name the
+workloads -- dense Llama-3 and Qwen3 decoders -- but never write the block out.
+This module takes the plainest standard reading, one step at a time:
+
+  xn   = RMSNorm(x; g_attn)                     eps inside the square root
+  q,k,v = xn Wq^T, xn Wk^T, xn Wv^T             no biases
+  (Qwen3) q_h, k_h = RMSNorm_hd(.; g_q / g_k)   per head, before RoPE
+  q,k  = RoPE(., p)                             rotate-half pairs (i, i + hd/2)
+  cache[p] = k, v                               stored in the cache's type
+  o_h  = softmax(q_h K_g^T / sqrt(hd)) V_g      g = h // (nq / nkv)
+  h    = x + concat(o) Wo^T
+  a    = silu(RMSNorm(h; g_ffn) Wg^T) * (RMSNorm(h; g_ffn) Wu^T)
+  x'   = h + a Wd^T
+  logits = RMSNorm(x_L; g_final) W_lm^T
+
+All arithmetic is float64.  Weights arrive as the workload's storage arrays
+(bf16 bit patterns or float32) and are widened exactly.  The only rounding to
+a narrower type is where the decoder itself stores into its KV cache, whose
+element type is part of the model (bf16 for the bf16 models).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------- storage types
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) exactly: the bf16 value is the top half of an fp32."""
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def to_f64(arr: np.ndarray) -> np.ndarray:
+    if arr.dtype == np.uint16:
+        return bf16_bits_to_f64(arr)
+    return arr.astype(np.float64)
+
+
+def store_like(x: np.ndarray, like_dtype) -> np.ndarray:
+    """Round float64 values into a cache's storage type.
+
+    float32 storage: nearest float32.  bf16 storage (uint16 bit patterns): the
+    value goes to float32 and then to bf16 by round-to-nearest, ties to even
+    on the 16 discarded bits.
+    """
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if like_dtype == np.float32:
+        return f
+    b = f.view(np.uint32).astype(np.uint64)
+    low = b & 0xFFFF
+    hi = b >> 16
+    up = (low > 0x8000) | ((low == 0x8000) & ((hi & 1) == 1))
+    return (hi + up.astype(np.uint64)).astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------- elementary ops
+
+def rms_norm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """y = x / sqrt(mean(x^2) + eps) * g over the last axis."""
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * g
+
+
+def rope_angles(pos: int, head_dim: int, theta: float) -> np.ndarray:
+    """Angles p * theta^(-2i/hd) for i < hd/2, float64."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    inv = theta ** (-2.0 * i / head_dim)
+    return float(pos) * inv
+
+
+def rope(x: np.ndarray, pos: int, theta: float) -> np.ndarray:
+    """Rotate pairs (i, i + hd/2) of the last axis by angle p * theta^(-2i/hd)."""
+    hd = x.shape[-1]
+    half = hd // 2
+    ang = rope_angles(pos, hd, theta)
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+def softmax(s: np.ndarray) -> np.ndarray:
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """Grouped-query attention of one query position.
+
+    q: [nq, hd]; K, V: [nkv, n, hd] (the n visible keys).  Query head h reads
+    KV head h // (nq / nkv).  Returns [nq, hd].
+    """
+    nq, hd = q.shape
+    nkv = K.shape[0]
+    r = nq // nkv
+    out = np.empty_like(q)
+    for h in range(nq):
+        g = h // r
+        s = (K[g] @ q[h]) / math.sqrt(hd)
+        out[h] = softmax(s) @ V[g]
+    return out
+
+
+# ----------------------------------------------------------------------------- split-KV (flash-decoding form)
+
+EMPTY_MAX = -math.inf   # marker of a split that holds no key
+
+
+def attention_split(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Unnormalised partial attention of r query heads over one split of keys.
+
+    q: [r, hd]; K, V: [n, hd] with n >= 0.  Returns (o [r, hd], m [r], l [r])
+    with m = max_j s_j, l = sum_j exp(s_j - m), o = sum_j exp(s_j - m) V_j.
+    An empty split gives o = 0, l = 0, m = EMPTY_MAX.
+    """
+    r, hd = q.shape
+    if K.shape[0] == 0:
+        return np.zeros((r, hd)), np.full(r, EMPTY_MAX), np.zeros(r)
+    s = (q @ K.T) / math.sqrt(hd)          # [r, n]
+    m = np.max(s, axis=1)
+    e = np.exp(s - m[:, None])
+    return e @ V, m, np.sum(e, axis=1)
+
+
+def combine_splits(parts: Sequence[Tuple[np.ndarray, np.ndarray, np.ndarray]]) -> np.ndarray:
+    """Merge split partials (o, m, l): out = sum_s e^(m_s - m) o_s / sum_s e^(m_s - m) l_s.
+
+    Empty splits (m_s = EMPTY_MAX) are skipped.
+    """
+    live = [p for p in parts if np.all(np.isfinite(p[1]))]
+    m = np.max(np.stack([p[1] for p in live]), axis=0)
+    num = sum(np.exp(p[1] - m)[:, None] * p[0] for p in live)
+    den = sum(np.exp(p[1] - m) * p[2] for p in live)
+    return num / den[:, None]
+
+
+# ----------------------------------------------------------------------------- model state
+
+@dataclass
+class Layer:
+    wqkv: np.ndarray
+    wo: np.ndarray
+    wgate: np.ndarray
+    wup: np.ndarray
+    wdown: np.ndarray
+    attn_norm: np.ndarray
+    ffn_norm: np.ndarray
+    q_norm: Optional[np.ndarray] = None
+    k_norm: Optional[np.ndarray] = None
+
+
+@dataclass
+class Model:
+    cfg: object                      # workloads.ModelConfig
+    layers: List[Layer]
+    embed: Optional[np.ndarray] = None
+    lm_head: Optional[np.ndarray] = None
+    final_norm: Optional[np.ndarray] = None
+
+
+def prepare_layer(raw: Dict[str, np.ndarray]) -> Layer:
+    return Layer(**{k: to_f64(v) for k, v in raw.items()})
+
+
+def prepare(cfg, raw_layers: Sequence[Dict[str, np.ndarray]], raw_global: Dict[str, np.ndarray]) -> Model:
+    return Model(cfg, [prepare_layer(r) for r in raw_layers],
+                 **{k: to_f64(v) for k, v in raw_global.items()})
+
+
+@dataclass
+class Trace:
+    """Per-step intermediates, indexed [layer][row]."""
+    x_in: List[np.ndarray] = field(default_factory=list)      # X_l, [B, H]
+    q: List[np.ndarray] = field(default_factory=list)         # after QK-norm and RoPE, [B, nq, hd]
+    k: List[np.ndarray] = field(default_factory=list)         # [B, nkv, hd]
+    v: List[np.ndarray] = field(default_factory=list)
+    attn: List[np.ndarray] = field(default_factory=list)      # concat heads, [B, nq*hd]
+    attn_branch: List[np.ndarray] = field(default_factory=list)  # attn @ Wo^T, [B, H]
+    h: List[np.ndarray] = field(default_factory=list)         # x + attn_branch
+    act: List[np.ndarray] = field(default_factory=list)       # SwiGLU output, [B, F]
+    mlp_branch: List[np.ndarray] = field(default_factory=list)
+    x_out: Optional[np.ndarray] = None                        # X_L
+    logits: Optional[np.ndarray] = None                       # [B, V]
+
+
+def _project_qkv(cfg, lw: Layer, xn: np.ndarray):
+    nq, nkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    qkv = xn @ lw.wqkv.T
+    q = qkv[..., : nq * hd].reshape(*xn.shape[:-1], nq, hd)
+    k = qkv[..., nq * hd:(nq + nkv) * hd].reshape(*xn.shape[:-1], nkv, hd)
+    v = qkv[..., (nq + nkv) * hd:].reshape(*xn.shape[:-1], nkv, hd)
+    if cfg.qk_norm:
+        q = rms_norm(q, lw.q_norm, cfg.rms_eps)
+        k = rms_norm(k, lw.k_norm, cfg.rms_eps)
+    return q, k, v
+
+
+def _mlp(cfg, lw: Layer, h: np.ndarray):
+    hn = rms_norm(h, lw.ffn_norm, cfg.rms_eps)
+    a = silu(hn @ lw.wgate.T) * (hn @ lw.wup.T)
+    return a, a @ lw.wdown.T
+
+
+def decode_step(model: Model, K: np.ndarray, V: np.ndarray, ctx_lens: Sequence[int],
+                tokens: Optional[np.ndarray] = None, x0: Optional[np.ndarray] = None) -> Trace:
+    """One decode step for B sequences.
+
+    K, V: caches [L, B, nkv, ctx_max, hd] in storage type; the new key and value
+    of row b are written at position ctx_lens[b] (0-based) and attention sees
+    positions 0..ctx_lens[b].  The caller advances ctx_lens afterwards.
+    Input rows are embedding rows of ``tokens`` or, for a model without an
+    embedding, ``x0`` [B, H].
+    """
+    cfg = model.cfg
+    x = model.embed[np.asarray(tokens)] if cfg.has_embed else np.asarray(x0, dtype=np.float64)
+    B = x.shape[0]
+    tr = Trace()
+    for l, lw in enumerate(model.layers):
+        tr.x_in.append(x)
+        q, k, v = _project_qkv(cfg, lw, rms_norm(x, lw.attn_norm, cfg.rms_eps))
+        att = np.empty((B, cfg.attn_cols))
+        qs, ks = np.empty_like(q), np.empty_like(k)
+        for b in range(B):
+            p = int(ctx_lens[b])
+            qs[b] = rope(q[b], p, cfg.rope_theta)
+            ks[b] = rope(k[b], p, cfg.rope_theta)
+            K[l, b, :, p] = store_like(ks[b], K.dtype)
+            V[l, b, :, p] = store_like(v[b], V.dtype)
+            Kb = to_f64(K[l, b, :, : p + 1])
+            Vb = to_f64(V[l, b, :, : p + 1])
+            att[b] = attention(qs[b], Kb, Vb).reshape(-1)
+        ab = att @ lw.wo.T
+        h = x + ab
+        a, mb = _mlp(cfg, lw, h)
+        x = h + mb
+        tr.q.append(qs); tr.k.append(ks); tr.v.append(v); tr.attn.append(att)
+        tr.attn_branch.append(ab); tr.h.append(h); tr.act.append(a); tr.mlp_branch.append(mb)
+    tr.x_out = x
+    if cfg.has_lm_head:
+        tr.logits = rms_norm(x, model.final_norm, cfg.rms_eps) @ model.lm_head.T
+    return tr
+
+
+def prefill(model: Model, K: np.ndarray, V: np.ndarray, tokens: np.ndarray, row: int = 0) -> Trace:
+    """Causal forward over S tokens of one sequence starting at position 0.
+
+    Writes cache positions 0..S-1 of batch row ``row``; query i attends to keys
+    0..i.  Logits are returned for the last position only ([1, V]).
+    """
+    cfg = model.cfg
+    x = model.embed[np.asarray(tokens)]
+    S = x.shape[0]
+    tr = Trace()
+    for l, lw in enumerate(model.layers):
+        tr.x_in.append(x)
+        q, k, v = _project_qkv(cfg, lw, rms_norm(x, lw.attn_norm, cfg.rms_eps))
+        qs = np.stack([rope(q[i], i, cfg.rope_theta) for i in range(S)])
+        ks = np.stack([rope(k[i], i, cfg.rope_theta) for i in range(S)])
+        K[l, row, :, :S] = store_like(ks.transpose(1, 0, 2), K.dtype)
+        V[l, row, :, :S] = store_like(v.transpose(1, 0, 2), V.dtype)
+        Kf = to_f64(K[l, row, :, :S])
+        Vf = to_f64(V[l, row, :, :S])
+        att = np.empty((S, cfg.attn_cols))
+        for i in range(S):
+            att[i] = attention(qs[i], Kf[:, : i + 1], Vf[:, : i + 1]).reshape(-1)
+        ab = att @ lw.wo.T
+        h = x + ab
+        a, mb = _mlp(cfg, lw, h)
+        x = h + mb
+        tr.q.append(qs); tr.k.append(ks); tr.v.append(v); tr.attn.append(att)
+        tr.attn_branch.append(ab); tr.h.append(h); tr.act.append(a); tr.mlp_branch.append(mb)
+    tr.x_out = x
+    if cfg.has_lm_head:
+        tr.logits = rms_norm(x[-1:], model.final_norm, cfg.rms_eps) @ model.lm_head.T
+    return tr
+
+
+def argmax_lowest(logits: np.ndarray) -> np.ndarray:
+    """Index of the largest value per row; the lowest index wins a tie."""
+    return np.argmax(logits, axis=-1).astype(np.int32)    # numpy returns the first maximum
+
+
+def max_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max |got - ref| / max |ref| over the whole tensor."""
+    ref = np.asarray(ref, dtype=np.float64)
+    den = float(np.max(np.abs(ref)))
+    return float(np.max(np.abs(np.asarray(got, dtype=np.float64) - ref))) / (den if den > 0 else 1.0)

@@ -1,0 +1,243 @@
+"""Pins of the reference queue builder: worked counts, the element-level static
+checker, exhaustive mutation testing, and the NaN-poisoned interpreter
+simulation compared with the plain forward pass."""
+import json
+import os
+import struct
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import checker as CK
+from oracle import numerics as N
+from oracle import queue_spec as QS
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+SMALL = W.WORKLOADS["layer256_f32"]
+
+
+def small_queue(plan=None, rows=1, ctx_max=129):
+    return QS.build(SMALL.model, plan or SMALL.plan, QS.MODE_DECODE, rows, ctx_max)
+
+
+def test_worked_counts_single_layer():
+    g = json.load(open(os.path.join(GOLDEN, "layer256_queue_counts.json")))
+    q = small_queue()
+    assert len(q.instrs) == g["n_instructions"]
+    counts = {}
+    waits = {}
+    for i, ins in enumerate(q.instrs):
+        name = QS.OP_NAMES[ins.op]
+        counts[name] = counts.get(name, 0) + 1
+        waits.setdefault(name, set()).add(len(q.wait_list(i)))
+    assert counts == g["instructions"]
+    assert {k: v.pop() for k, v in waits.items() if len(v) == 1} == g["waits_per_instruction"]
+    assert len(q.targets) == g["n_barriers"]
+    hist = {}
+    for t in q.targets:
+        hist[str(t)] = hist.get(str(t), 0) + 1
+    assert hist == g["targets"]
+    assert sum(len(q.wait_list(i)) for i in range(len(q.instrs))) == g["n_wait_entries"]
+    assert sum(q.targets) == len(q.instrs)
+
+
+@pytest.mark.parametrize("name", ["layer256_f32", "llama1b_b1"])
+def test_static_check_clean(name):
+    wl = W.WORKLOADS[name]
+    q = QS.build(wl.model, wl.plan, QS.MODE_DECODE, wl.run.batch, wl.run.ctx_max)
+    assert CK.static_check(wl.model, q.parts()) == []
+
+
+EDGE = [
+    dict(rows=1, ctx_max=1, plan=W.Plan(tq=16, to=16, tf=32, td=16, kb=32)),     # one split, one key
+    dict(rows=4, ctx_max=129, plan=W.Plan(tq=24, to=40, tf=50, td=7, kb=64)),    # ragged tiles
+    dict(rows=16, ctx_max=300, plan=W.Plan(tq=512, to=256, tf=688, td=256, kb=1000)),  # one tile per op
+    dict(rows=32, ctx_max=33, plan=W.Plan(tq=1, to=3, tf=5, td=9, kb=1)),        # tiny tiles, 33 splits
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: f"B{c['rows']}-ctx{c['ctx_max']}")
+def test_static_check_edge_grid(case):
+    q = small_queue(case["plan"], case["rows"], case["ctx_max"])
+    assert CK.static_check(SMALL.model, q.parts()) == []
+    assert sum(q.targets) == len(q.instrs)
+
+
+def test_static_check_prefill_queue():
+    m = W.ModelConfig(name="p", n_layers=2, hidden=64, n_q_heads=4, n_kv_heads=2, head_dim=16,
+                      ffn=96, vocab=50, rms_eps=1e-6, rope_theta=1e6, qk_norm=True)
+    q = QS.build(m, W.Plan(bm=16, bn=32), QS.MODE_PREFILL, 40, 48)
+    assert CK.static_check(m, q.parts()) == []
+    # attention on row block m waits on the k/v tiles of row blocks 0..m only
+    att = [i for i, ins in enumerate(q.instrs) if ins.op == QS.OP_P_ATTN and ins.layer == 0]
+    n_waits = [len(q.wait_list(i)) for i in att]
+    assert n_waits[0] < n_waits[-1]
+
+
+def test_queue_does_not_depend_on_runtime_context():
+    a = small_queue().parts()
+    b = small_queue().parts()
+    assert a == b
+
+
+def test_bad_arguments_rejected():
+    with pytest.raises(QS.QueueError):
+        small_queue(rows=0)
+    with pytest.raises(QS.QueueError):
+        small_queue(rows=QS.MAX_DECODE_ROWS + 1)
+    with pytest.raises(QS.QueueError):
+        small_queue(plan=W.Plan(tq=0))
+    with pytest.raises(QS.QueueError):
+        small_queue(ctx_max=0)
+    with pytest.raises(QS.QueueError):
+        QS.build(SMALL.model, W.Plan(bn=48), QS.MODE_PREFILL, 8, 8)     # 48 is not whole heads of 64
+
+
+# ----------------------------------------------------------------------------- mutations (every one must fail)
+
+def _with_waits(q, i, new_list):
+    """Re-encode instruction i's wait list as ranges after an edit."""
+    parts = q.parts()
+    p = CK.parse(parts)
+    ranges = [tuple(r) for r in p.ranges.tolist()]
+    recs = [list(r) for r in p.instr.tolist()]
+    out_ranges = []
+    for k, rec in enumerate(recs):
+        lst = new_list if k == i else p.waits_of(k)
+        rr = []
+        for b in lst:
+            if rr and rr[-1][0] + rr[-1][1] == b:
+                rr[-1] = (rr[-1][0], rr[-1][1] + 1)
+            else:
+                rr.append((b, 1))
+        rec[5], rec[6], rec[8] = len(out_ranges), len(rr), len(lst)
+        out_ranges.extend(rr)
+    meta = bytearray(parts["meta"])
+    struct.pack_into("<I", meta, 20, len(out_ranges))
+    parts = dict(parts)
+    parts["meta"] = bytes(meta)
+    parts["instr"] = b"".join(struct.pack("<HH7I", *r) for r in recs)
+    parts["waits"] = b"".join(struct.pack("<2I", *r) for r in out_ranges)
+    return parts
+
+
+def test_every_single_wait_deletion_is_caught():
+    q = small_queue()
+    total = 0
+    for i in range(len(q.instrs)):
+        wl = q.wait_list(i)
+        for k in range(len(wl)):
+            mutant = _with_waits(q, i, wl[:k] + wl[k + 1:])
+            assert CK.static_check(SMALL.model, mutant, max_errors=1), (i, k)
+            total += 1
+    assert total == 914
+
+
+def test_every_target_decrement_is_caught():
+    q = small_queue()
+    parts = q.parts()
+    for b in range(len(q.targets)):
+        t = list(q.targets)
+        t[b] -= 1
+        mutant = dict(parts, targets=struct.pack(f"<{len(t)}I", *t))
+        assert CK.static_check(SMALL.model, mutant, max_errors=1), b
+
+
+def test_every_consumer_moved_before_a_producer_is_caught():
+    q = small_queue()
+    parts = q.parts()
+    recs = [parts["instr"][32 * i: 32 * i + 32] for i in range(len(q.instrs))]
+    sig = [ins.signal for ins in q.instrs]
+    checked = 0
+    for i in range(len(q.instrs)):
+        producers = [j for j in range(len(q.instrs)) if sig[j] in set(q.wait_list(i))]
+        if not producers:
+            continue
+        j = min(producers)                       # move consumer i just ahead of its first producer
+        order = list(range(len(q.instrs)))
+        order.remove(i)
+        order.insert(j, i)
+        mutant = dict(parts, instr=b"".join(recs[k] for k in order))
+        assert CK.static_check(SMALL.model, mutant, max_errors=1), i
+        checked += 1
+    assert checked == len(q.instrs) - 32          # every instruction except the QKV tiles
+
+
+# ----------------------------------------------------------------------------- simulation
+
+def _small_inputs(ctx0=(128,), gain=0.0):
+    m, r = SMALL.model, SMALL.run
+    model = N.prepare(m, [W.gen.layer_weights(m, r.seed, l, gain) for l in range(m.n_layers)],
+                      W.gen.global_weights(m, r.seed))
+    K, V = W.gen.kv_cache(m, r)
+    x0 = W.gen.input_rows(m, r)[0]
+    return model, K, V, x0
+
+
+@pytest.mark.parametrize("workers", [1, 2, 7, 256])
+def test_simulation_matches_forward_any_schedule(workers):
+    model, K, V, x0 = _small_inputs(gain=0.1)
+    q = small_queue()
+    parts = q.parts()
+    ref = N.decode_step(model, K.copy(), V.copy(), [128], x0=x0)
+    base = CK.simulate(model, parts, K.copy(), V.copy(), [128], 1, seed=0, x0=x0)
+    for seed in range(100 if workers > 1 else 1):
+        Ks, Vs = K.copy(), V.copy()
+        res = CK.simulate(model, parts, Ks, Vs, [128], workers, seed=seed, x0=x0,
+                          reverse_ties=bool(seed & 1))
+        assert not res.deadlock and res.bad_reads == []
+        assert np.array_equal(res.x_out, base.x_out)
+        assert np.array_equal(res.counters, np.array(q.targets))
+        assert not np.any(np.isnan(res.x_out))
+    assert N.max_rel_err(base.x_out, ref.x_out) < 1e-12
+    assert np.array_equal(Ks, base.state.K)
+
+
+@pytest.mark.parametrize("ctx", [0, 1, 31, 32, 100])
+def test_simulation_short_contexts_empty_splits(ctx):
+    model, K, V, x0 = _small_inputs()
+    q = small_queue()
+    ref = N.decode_step(model, K.copy(), V.copy(), [ctx], x0=x0)
+    res = CK.simulate(model, q.parts(), K.copy(), V.copy(), [ctx], 7, seed=3, x0=x0)
+    assert not res.deadlock and res.bad_reads == []
+    assert N.max_rel_err(res.x_out, ref.x_out) < 1e-12
+
+
+def test_simulation_with_sub_queues_and_batch():
+    m = SMALL.model
+    plan = W.Plan(tq=16, to=16, tf=32, td=16, kb=32, n_queues=8)
+    q = QS.build(m, plan, QS.MODE_DECODE, 3, 129)
+    run = W.RunConfig(batch=3, ctx0=(5, 128, 64), steps=1, ctx_max=129, seed=9)
+    model = N.prepare(m, [W.gen.layer_weights(m, 9, 0, 0.1)], {})
+    K, V = W.gen.kv_cache(m, run)
+    x0 = W.gen.input_rows(m, run)[0]
+    ref = N.decode_step(model, K.copy(), V.copy(), run.ctx0, x0=x0)
+    for workers in (8, 9, 64):
+        res = CK.simulate(model, q.parts(), K.copy(), V.copy(), run.ctx0, workers, seed=workers, x0=x0)
+        assert not res.deadlock and res.bad_reads == []
+        assert N.max_rel_err(res.x_out, ref.x_out) < 1e-12
+
+
+def test_simulation_detects_missing_wait():
+    model, K, V, x0 = _small_inputs()
+    q = small_queue()
+    # drop every wait of the first O-projection tile: some schedule must read unwritten data
+    i = next(k for k, ins in enumerate(q.instrs) if ins.op == QS.OP_OPROJ)
+    mutant = _with_waits(q, i, [])
+    seen = False
+    for seed in range(20):
+        res = CK.simulate(model, mutant, K.copy(), V.copy(), [128], 64, seed=seed, x0=x0)
+        seen |= bool(res.bad_reads) or bool(np.any(np.isnan(res.x_out)))
+    assert seen
+
+
+def test_simulation_detects_deadlock():
+    model, K, V, x0 = _small_inputs()
+    q = small_queue()
+    parts = q.parts()
+    recs = [parts["instr"][32 * i: 32 * i + 32] for i in range(len(q.instrs))]
+    # put the last down-projection tile first: with one worker it waits forever
+    mutant = dict(parts, instr=b"".join([recs[-1]] + recs[:-1]))
+    res = CK.simulate(model, mutant, K.copy(), V.copy(), [128], 1, seed=0, x0=x0)
+    assert res.deadlock
