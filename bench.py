@@ -1,0 +1,240 @@
+"""Decode benchmark of the tile-synchronized decoder on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama1b_b1]
+
+A step is one teacher-forced decode step of the whole model for the workload's
+batch: embedding, every decoder layer (one megakernel launch), the LM head and
+the argmax.  The default workload is the Llama-3-1B-shaped bf16 model at batch
+1 decoding from a 1024-token cache.  Inputs (random-init weights, KV cache,
+token ids) are seeded and synthetic and are resident in HBM before timing.
+
+Prints one JSON line: the megakernel's tokens/s as `value`, the kernel-per-op
+modes (eager and HIP-graph replay) beside it, the dominant kernel's roofline
+(algorithmic bytes per launch over its event-timed average duration, against
+8 TB/s) and the float64 CPU oracle timed on a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def layer_bytes(m) -> int:
+    """Weight bytes of one decoder layer (matrices + fp32 gains)."""
+    wb = 2 if m.dtype == "bf16" else 4
+    mats = m.qkv_cols * m.hidden + m.hidden * m.attn_cols + 3 * m.ffn * m.hidden
+    gains = 2 * m.hidden + (2 * m.head_dim if m.qk_norm else 0)
+    return mats * wb + gains * 4
+
+
+def megakernel_bytes(m, ctx) -> int:
+    """Algorithmic HBM bytes of one megakernel launch: every layer's weights
+    once, the embedding rows, the cached keys/values read and the new ones written."""
+    kvb = 2 if m.dtype == "bf16" else 4
+    wb = 2 if m.dtype == "bf16" else 4
+    B = len(ctx)
+    kv_read = m.n_layers * sum(ctx) * m.n_kv_heads * m.head_dim * 2 * kvb
+    kv_write = m.n_layers * B * m.n_kv_heads * m.head_dim * 2 * kvb
+    emb = B * m.hidden * wb if m.has_embed else 0
+    return m.n_layers * layer_bytes(m) + emb + kv_read + kv_write
+
+
+def lm_head_bytes(m, B) -> int:
+    wb = 2 if m.dtype == "bf16" else 4
+    return m.vocab * m.hidden * wb + m.hidden * 4 + 4 * B * m.vocab if m.has_lm_head else 0
+
+
+def cpu_baseline(wl, raw_layers, raw_global, budget_s: float = 20.0) -> dict:
+    """The float64 oracle, step by step, on the host's cores (bounded sample)."""
+    from oracle import numerics as N
+    import workloads as W
+    m, r = wl.model, wl.run
+    t0 = time.time()
+    model = N.prepare(m, raw_layers, raw_global)
+    K, V = W.gen.kv_cache(m, r)
+    tokens = W.gen.decode_tokens(m, r)
+    prep = time.time() - t0
+    steps, spent = 0, 0.0
+    while steps < r.steps and (steps == 0 or spent + spent / steps <= budget_s):
+        ctx = [p + steps for p in r.ctx0]
+        t1 = time.time()
+        N.decode_step(model, K, V, ctx, tokens=tokens[steps])
+        spent += time.time() - t1
+        steps += 1
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(r.batch * steps / spent, 4), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{steps} teacher-forced decode steps of {wl.name} (batch {r.batch}), float64 numpy "
+                      f"on {cores} host threads; weights widened to float64 before timing ({prep:.0f} s)",
+            "ms_per_step": round(1e3 * spent / steps, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="llama1b_b1")
+    ap.add_argument("--workers-per-cu", type=int, default=1)
+    ap.add_argument("--queues", type=int, default=0, help="sub-queues (0: the workload's plan)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--modes", default="mega,kpo,kpo_graph")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import dataclasses
+    import torch
+    import tile_synchronized_decoder_amd as T
+    from tile_synchronized_decoder_amd import device as D
+    import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    if args.queues:
+        wl = dataclasses.replace(wl, plan=dataclasses.replace(wl.plan, n_queues=args.queues))
+    m, r = wl.model, wl.run
+    K_steps = min(args.steps, r.steps)
+    torch.cuda.set_device(0)
+    T.mk_set_option(T.MK_OPT_WORKERS_PER_CU, args.workers_per_cu)
+
+    t0 = time.time()
+    raw_layers = W.gen.all_layer_weights(m, r.seed)
+    raw_global = W.gen.global_weights(m, r.seed)
+    Kh, Vh = W.gen.kv_cache(m, r)
+    tokens = W.gen.decode_tokens(m, r)
+    log(f"[bench] inputs generated in {time.time() - t0:.1f} s")
+    q = T.mk_build_queue(T.make_config(m), T.make_plan(wl.plan, T.MK_DECODE, r.batch, r.ctx_max))
+    dq = D.upload_queue(q)
+    dm = D.upload_weights(raw_layers, raw_global)
+    dkv = D.upload_kv(Kh, Vh)
+    ws = D.workspace(q)
+    B = r.batch
+    tok_all = torch.from_numpy(tokens.astype(np.int32)).cuda()                       # [steps, B]
+    ctx_all = torch.tensor([[p + t for p in r.ctx0] for t in range(r.steps)], dtype=torch.int32,
+                           device="cuda")
+    logits = torch.empty((B, m.vocab), dtype=torch.float32, device="cuda")
+    nxt = torch.empty((B,), dtype=torch.int32, device="cuda")
+    tok_buf = torch.empty((B,), dtype=torch.int32, device="cuda")
+    ctx_buf = torch.empty((B,), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log(f"[bench] {wl.name}: {q.nbytes(T.MK_PART_INSTR) // 32} instructions, queue "
+        f"{q.nbytes(T.MK_PART_DEVICE) / 1e6:.2f} MB, workspace {ws.numel() / 1e6:.1f} MB")
+
+    def step(t, mode, timing=None):
+        tok_buf.copy_(tok_all[t % r.steps])
+        ctx_buf.copy_(ctx_all[t % r.steps])
+        T.mk_decode_step(q, dq, dm.w, dkv.kv, tok_buf, None, ctx_buf, B, ws, None, None, mode)
+        if timing is not None:
+            timing.append(torch.cuda.Event(enable_timing=True))
+            timing[-1].record(stream)
+        T.mk_lm_head(q, dm.w, ws, logits, nxt)
+
+    results = {}
+    modes = args.modes.split(",")
+    for name in modes:
+        mode = T.MK_KERNEL_PER_OP if name.startswith("kpo") else T.MK_MEGAKERNEL
+        graph = None
+        if name == "kpo_graph":
+            step(0, mode)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                T.mk_decode_step(q, dq, dm.w, dkv.kv, tok_buf, None, ctx_buf, B, ws, None, None, mode,
+                                 stream=torch.cuda.current_stream())
+                T.mk_lm_head(q, dm.w, ws, logits, nxt, stream=torch.cuda.current_stream())
+            torch.cuda.synchronize()
+
+        def run(t, marks=None):
+            if graph is None:
+                step(t, mode, marks)
+            else:
+                tok_buf.copy_(tok_all[t % r.steps])
+                ctx_buf.copy_(ctx_all[t % r.steps])
+                graph.replay()
+
+        for t in range(args.warmup):
+            run(t)
+        torch.cuda.synchronize()
+        # timed region: K steps, events on the launch stream before each step and after
+        # the decoder layers of each step (the megakernel / per-op launches end there)
+        starts, mids = [], []
+        ev_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for t in range(K_steps):
+            starts.append(torch.cuda.Event(enable_timing=True))
+            starts[-1].record(stream)
+            run(t, mids if graph is None else None)
+        ev_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        total_ms = starts[0].elapsed_time(ev_end)
+        per_step = [starts[i].elapsed_time(starts[i + 1]) for i in range(K_steps - 1)]
+        per_step.append(starts[-1].elapsed_time(ev_end))
+        res = {"ms_per_step": total_ms / K_steps, "tokens_per_s": B * K_steps / (total_ms / 1e3),
+               "p50_ms": float(np.percentile(per_step, 50)), "p95_ms": float(np.percentile(per_step, 95)),
+               "host_wall_tokens_per_s": B * K_steps / wall}
+        if mids:
+            layers_ms = [starts[i].elapsed_time(mids[i]) for i in range(K_steps)]
+            res["layers_ms"] = float(np.mean(layers_ms))           # reset + megakernel (or per-op launches)
+            res["lm_head_ms"] = res["ms_per_step"] - res["layers_ms"]
+        results[name] = res
+        err = T.mk_device_error(q, ws)
+        assert err.code == 0, f"device error {err.code} in mode {name}"
+        log(f"[bench] {name}: {res['ms_per_step']:.4f} ms/step, {res['tokens_per_s']:.1f} tok/s")
+
+    mega = results.get("mega", next(iter(results.values())))
+    ctx_mid = [p + K_steps // 2 for p in r.ctx0]
+    mbytes = megakernel_bytes(m, ctx_mid)
+    step_bytes = mbytes + lm_head_bytes(m, B)
+    roof = None
+    if "layers_ms" in mega:
+        ach = mbytes / (mega["layers_ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "mk_interp (decoder layers, one launch per step)",
+                "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": mbytes}
+    line = {
+        "metric": "decode tokens/s + step latency vs kernel-per-op; HBM GB/s as % of peak",
+        "value": round(mega["tokens_per_s"], 2), "unit": "tokens/s", "n_gpus": 1, "steps": K_steps,
+        "warmup": args.warmup, "ms_per_step": round(mega["ms_per_step"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "storage": m.dtype, "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.describe}", "batch": B, "context": f"{r.ctx0[0]}+",
+                   "layers": m.n_layers, "hidden": m.hidden, "vocab": m.vocab,
+                   "instructions_per_step": q.nbytes(T.MK_PART_INSTR) // 32,
+                   "workers_per_cu": args.workers_per_cu, "n_queues": wl.plan.n_queues},
+        "step_hbm_gbs": round(step_bytes / (mega["ms_per_step"] * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / (mega["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "modes": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                  for k, v in results.items()},
+        "roofline": roof,
+    }
+    if "kpo" in results or "kpo_graph" in results:
+        best = min(v["ms_per_step"] for k, v in results.items() if k.startswith("kpo"))
+        line["megakernel_speedup_vs_best_kpo"] = round(best / mega["ms_per_step"], 4)
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline ...")
+        line["cpu_baseline"] = cpu_baseline(wl, raw_layers, raw_global, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

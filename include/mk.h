@@ -1,0 +1,207 @@
+/*
+ * mk.h -- C ABI of the tile-synchronized decoder megakernel for MI355X (gfx950).
+ *
+ * One decode step (or one prefill) of a pre-norm Llama/Qwen decoder runs as a
+ * single persistent kernel.  Every workgroup is an interpreter that pops
+ * instructions from a queue in device memory; each instruction computes one
+ * tile of one intermediate tensor and first waits on barrier counters of
+ * exactly the producer tiles it reads.  The LM head runs as a separate kernel.
+ * The same op bodies also run one kernel per operator, for comparison.
+ *
+ * Sources of the method (the pages this library implements):
+ *  - MegaOps abstract: dependencies enforced on individual tiles of the
+ *    intermediate tensor a producer writes and a consumer reads, instead of
+ *    whole-kernel barriers; weight prefetch while the producer still runs.
+ *  - "Production Megakernels" lecture summary, Key takeaways: one work queue
+ *    built with symbolic sequence (S) and context (P) lengths; barriers are
+ *    tensors partitioned by dependency.  Technical details: an on-device
+ *    interpreter (a loop around a switch) whose cores atomically pop
+ *    instructions from a global queue in DRAM; memory pipelining across tiles.
+ *    Practical implications: the LM head kept outside the megakernel; the host
+ *    kept out of the hot loop.
+ *
+ * Conventions for every entry point:
+ *  - Returns MK_OK (0) or a negative mk_status.  On error nothing is launched
+ *    and mk_last_error() holds a message (thread-local).
+ *  - Pointers named d_* and the fields of mk_weights / mk_kv are device
+ *    pointers; everything else is host memory.
+ *  - The caller owns and allocates all device memory (weights, KV cache,
+ *    workspace, device queue copy, outputs).  The library allocates only the
+ *    host mk_queue object and never calls hipMalloc or synchronises, except
+ *    mk_device_error, which synchronises the given stream.
+ *  - Launches go to the caller's stream and return asynchronously.
+ *  - Calls with distinct workspaces may run concurrently; calls that share a
+ *    workspace race.
+ *  - Matrices use the [out, in] row-major layout; all layers of one kind are
+ *    stacked contiguously ([n_layers][out][in]).
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t mk_status;
+enum {
+  MK_OK = 0,
+  MK_EINVAL = -1,    /* bad argument, shape or tile plan */
+  MK_ENOMEM = -2,    /* host allocation failed */
+  MK_ELAUNCH = -3,   /* a HIP launch or runtime call failed */
+  MK_EDEVICE = -4,   /* the device reported an error (mk_device_error) */
+  MK_ENOTSUP = -5    /* valid request this build does not implement */
+};
+
+enum { MK_F32 = 0, MK_BF16 = 1 };                     /* element type of matrices and KV cache */
+enum { MK_DECODE = 0, MK_PREFILL = 1 };               /* queue mode */
+enum { MK_MEGAKERNEL = 0, MK_KERNEL_PER_OP = 1 };     /* execution mode */
+enum { MK_PART_META = 0, MK_PART_INSTR = 1, MK_PART_WAITS = 2, MK_PART_TARGETS = 3,
+       MK_PART_DEVICE = 4 };
+
+/* Decoder shape.  Norm gains are always fp32.  rope_theta: base of the rotary
+ * frequencies theta^(-2i/head_dim), pairs (i, i + head_dim/2). */
+typedef struct mk_config {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+  int32_t qk_norm;        /* per-head RMSNorm of q and k before RoPE (Qwen3) */
+  int32_t has_embed;      /* 0: input rows are given as fp32 (d_x0) */
+  int32_t has_lm_head;    /* 0: no final norm / LM head / argmax */
+  int32_t dtype;          /* MK_F32 or MK_BF16 */
+  float rms_eps;
+  double rope_theta;
+} mk_config;
+
+/* Tile plan: explicit, never inferred.  tq/to/tf/td are the output-column tile
+ * widths of the QKV, O-projection, gate/up and down GEMVs; kb keys per
+ * attention split (decode); bm x bn the prefill GEMM tile (bn holds whole
+ * heads).  rows: B for decode (1..32), S_max for prefill.  n_queues: workers
+ * pop from n_queues sub-queues; instruction i belongs to sub-queue i mod
+ * n_queues (1..64). */
+typedef struct mk_plan {
+  int32_t mode, rows, ctx_max;
+  int32_t tq, to, tf, td, kb, bm, bn;
+  int32_t n_queues;
+} mk_plan;
+
+typedef struct mk_queue mk_queue;   /* opaque, host memory */
+
+/* Build the instruction queue and its tile barriers for (cfg, plan).
+ * Host only, deterministic: equal inputs give byte-identical parts.
+ * Layout of the parts (little-endian):
+ *   META    u32 magic 'TMK1', version 1, mode, n_instr, n_barriers,
+ *           n_wait_ranges, n_segments, n_queues, rows, ctx_max, n_splits,
+ *           n_layers, tq, to, tf, td, kb, bm, bn, 0, then n_segments x
+ *           {op, layer, first, count} (maximal runs of one op of one layer)
+ *   INSTR   n_instr x 32 B {u16 op, u16 layer, u32 a0, a1, a2, wait_off,
+ *           wait_cnt, signal, n_wait}
+ *   WAITS   n_wait_ranges x {u32 first barrier, u32 count}
+ *   TARGETS n_barriers x u32 (instructions that signal each barrier)
+ *   DEVICE  INSTR | WAITS | TARGETS, each starting on a 256-byte boundary:
+ *           what mk_decode_step / mk_prefill read from d_queue.
+ * Errors: MK_EINVAL for a bad shape or plan, MK_ENOMEM. */
+mk_status mk_build_queue(const mk_config* cfg, const mk_plan* plan, mk_queue** out);
+size_t mk_queue_nbytes(const mk_queue* q, int32_t part);
+mk_status mk_queue_export(const mk_queue* q, int32_t part, void* host_dst, size_t nbytes);
+void mk_queue_free(mk_queue* q);
+
+/* Device workspace: per-layer intermediate tensors, split partials, barrier
+ * counters, queue heads, error record.  No alignment beyond 256 bytes needed.
+ * mk_workspace_offset gives the byte offset of one tensor (MK_T_*) of one
+ * layer inside it (layer 0..n_layers for MK_T_X; 0 for the others that are not
+ * per layer). Intermediates are fp32 row-major [rows][cols]. */
+enum { MK_T_X = 0, MK_T_QKV = 1, MK_T_OPART = 2, MK_T_ATT = 3, MK_T_HRES = 4, MK_T_ACT = 5,
+       MK_T_COUNTERS = 6, MK_T_HEADS = 7, MK_T_ERROR = 8, MK_T_LMPART = 9 };
+mk_status mk_workspace_nbytes(const mk_queue* q, size_t* nbytes);
+mk_status mk_workspace_offset(const mk_queue* q, int32_t tensor, int32_t layer, size_t* offset);
+
+typedef struct mk_weights {
+  const void* wqkv;        /* [L][(nq + 2 nkv) hd][H]; rows: q heads, k heads, v heads */
+  const void* wo;          /* [L][H][nq hd] */
+  const void* wgate;       /* [L][F][H] */
+  const void* wup;         /* [L][F][H] */
+  const void* wdown;       /* [L][H][F] */
+  const float* attn_norm;  /* [L][H] */
+  const float* ffn_norm;   /* [L][H] */
+  const float* q_norm;     /* [L][hd]  (qk_norm only) */
+  const float* k_norm;     /* [L][hd]  (qk_norm only) */
+  const void* embed;       /* [V][H]   (has_embed only) */
+  const void* lm_head;     /* [V][H]   (has_lm_head only) */
+  const float* final_norm; /* [H]      (has_lm_head only) */
+} mk_weights;
+
+/* KV cache: [L][rows][n_kv][ctx_max][hd] in the model dtype, keys after RoPE. */
+typedef struct mk_kv {
+  void* k;
+  void* v;
+} mk_kv;
+
+/* One decode step for `batch` sequences (must equal the queue's rows).
+ * Row b's new token sits at position d_ctx_lens[b] (< ctx_max): its key and
+ * value are written there and attention covers positions 0..d_ctx_lens[b].
+ * The caller advances d_ctx_lens between steps.  Inputs: d_tokens [batch]
+ * token ids (has_embed), else d_x0 [batch][H] fp32 rows.  Outputs: d_logits
+ * [batch][V] fp32 and d_next [batch] (argmax, lowest index on ties); either may
+ * be NULL to skip; both ignored without an LM head.  The final hidden rows are
+ * the workspace tensor MK_T_X of layer n_layers.
+ * exec_mode MK_MEGAKERNEL: counter reset, one persistent interpreter launch,
+ * LM head, argmax.  MK_KERNEL_PER_OP: the same op bodies, one launch per
+ * (layer, op), stream-ordered, no tile waits.  Both give bitwise equal results.
+ * Errors: MK_EINVAL (mismatched queue / sizes / null pointers), MK_ELAUNCH. */
+mk_status mk_decode_step(const mk_queue* q, const void* d_queue, const mk_weights* w,
+                         const mk_kv* kv, const int32_t* d_tokens, const float* d_x0,
+                         const int32_t* d_ctx_lens, int32_t batch, void* d_workspace,
+                         size_t workspace_nbytes, float* d_logits, int32_t* d_next,
+                         int32_t exec_mode, hipStream_t stream);
+
+/* The LM head on its own (the second half of mk_decode_step): final RMSNorm
+ * of the workspace's last hidden rows (MK_T_X of layer n_layers, written by a
+ * previous mk_decode_step on the same stream and workspace), the vocabulary
+ * GEMV into d_logits [rows][V] fp32, and the argmax into d_next [rows] (lowest
+ * index on ties); either output may be NULL.  The lecture summary's mixed
+ * execution keeps this op outside the megakernel; calling it separately lets
+ * a caller time the two parts.  Errors: MK_EINVAL (no LM head, sizes). */
+mk_status mk_lm_head(const mk_queue* q, const mk_weights* w, void* d_workspace, size_t workspace_nbytes,
+                     float* d_logits, int32_t* d_next, hipStream_t stream);
+
+/* Causal prefill of seq_len (<= the queue's rows) tokens of one sequence into
+ * cache row kv_row, positions 0..seq_len-1.  Row blocks at or past seq_len are
+ * skipped (the queue is built once for S_max).  d_logits_last [V] and d_next
+ * [1] receive the last position's logits and argmax. */
+mk_status mk_prefill(const mk_queue* q, const void* d_queue, const mk_weights* w,
+                     const mk_kv* kv, const int32_t* d_tokens, int32_t seq_len, int32_t kv_row,
+                     void* d_workspace, size_t workspace_nbytes, float* d_logits_last,
+                     int32_t* d_next, int32_t exec_mode, hipStream_t stream);
+
+/* Device-side error record, written by a worker whose bounded wait on a
+ * barrier expired (the kernel then drains instead of hanging). */
+typedef struct mk_dev_error {
+  uint32_t code;       /* 0 none; 1 barrier wait timed out; 2 unknown opcode;
+                          3 context length outside the cache; 4 token id outside the vocabulary */
+  uint32_t instr;      /* instruction index */
+  uint32_t barrier;    /* barrier id */
+  uint32_t value;      /* counter value seen */
+  uint32_t target;     /* target it waited for */
+} mk_dev_error;
+/* Synchronises `stream`, then copies the record out. */
+mk_status mk_device_error(const mk_queue* q, const void* d_workspace, mk_dev_error* out,
+                          hipStream_t stream);
+
+/* Tuning knobs (process-wide): */
+enum {
+  MK_OPT_WORKERS_PER_CU = 0,  /* megakernel workgroups per compute unit (default 1) */
+  MK_OPT_SPIN_LIMIT = 1,      /* polls before a barrier wait gives up (default 1<<22) */
+  MK_OPT_NUM_CUS = 2          /* read-only: compute units of the current device */
+};
+mk_status mk_set_option(int32_t key, int64_t value);
+int64_t mk_get_option(int32_t key);
+
+const char* mk_status_str(mk_status s);
+const char* mk_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

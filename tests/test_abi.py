@@ -1,0 +1,110 @@
+"""The C ABI library on the CPU: it loads, exports every entry point that
+include/mk.h declares, and its host-side queue builder (an independent C++
+implementation) produces the reference builder's bytes exactly."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tile_synchronized_decoder_amd as T
+from tile_synchronized_decoder_amd import _lib as L
+import workloads as W
+from oracle import queue_spec as QS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "mk.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mk_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    syms = declared_symbols()
+    assert len(syms) >= 13
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert sorted(L.EXPORTED) == syms
+
+
+def _both(model, plan, mode, rows, ctx_max):
+    q = T.mk_build_queue(T.make_config(model), T.make_plan(plan, mode, rows, ctx_max))
+    return q.parts(), QS.build(model, plan, mode, rows, ctx_max).parts()
+
+
+@pytest.mark.parametrize("name", ["layer256_f32", "llama1b_b1", "llama8b_b1", "llama8b_b4",
+                                  "llama1b_stream_b32"])
+def test_builder_bytes_equal_reference(name):
+    wl = W.WORKLOADS[name]
+    got, ref = _both(wl.model, wl.plan, QS.MODE_DECODE, wl.run.batch, wl.run.ctx_max)
+    for part in ref:
+        assert got[part] == ref[part], part
+
+
+EDGE = [
+    (1, 1, W.Plan(tq=16, to=16, tf=32, td=16, kb=32)),
+    (4, 129, W.Plan(tq=24, to=40, tf=50, td=7, kb=64)),
+    (16, 300, W.Plan(tq=512, to=256, tf=688, td=256, kb=1000)),
+    (32, 33, W.Plan(tq=1, to=3, tf=5, td=9, kb=1)),
+    (3, 129, W.Plan(tq=16, to=16, tf=32, td=16, kb=32, n_queues=8)),
+]
+
+
+@pytest.mark.parametrize("rows,ctx,plan", EDGE)
+def test_builder_bytes_edge_grid(rows, ctx, plan):
+    got, ref = _both(W.LLAMA_LAYER_F32, plan, QS.MODE_DECODE, rows, ctx)
+    assert got == ref
+
+
+def test_builder_bytes_gqa_one_kv_head():
+    m = W.ModelConfig(name="mqa", n_layers=2, hidden=128, n_q_heads=4, n_kv_heads=1, head_dim=64,
+                      ffn=96, vocab=10, rms_eps=1e-5, rope_theta=1e4)
+    got, ref = _both(m, W.Plan(tq=48, to=16, tf=32, td=16, kb=16), QS.MODE_DECODE, 2, 40)
+    assert got == ref
+
+
+@pytest.mark.parametrize("S,bm,bn", [(40, 16, 32), (64, 64, 64), (17, 8, 96)])
+def test_builder_bytes_prefill(S, bm, bn):
+    m = W.ModelConfig(name="p", n_layers=2, hidden=96, n_q_heads=4, n_kv_heads=2, head_dim=32,
+                      ffn=160, vocab=50, rms_eps=1e-6, rope_theta=1e6, qk_norm=True)
+    got, ref = _both(m, W.Plan(bm=bm, bn=bn), QS.MODE_PREFILL, S, 64)
+    assert got == ref
+
+
+def test_builder_bytes_prefill_qwen_shape():
+    wl = W.WORKLOADS["qwen8b_prefill"]
+    m = W.shrink(wl, n_layers=2).model
+    got, ref = _both(m, wl.plan, QS.MODE_PREFILL, 512, wl.run.ctx_max)
+    assert got == ref
+
+
+@pytest.mark.parametrize("kw", [dict(rows=0), dict(rows=33), dict(ctx_max=0), dict(tq=0), dict(kb=0),
+                                dict(n_queues=0), dict(n_queues=65)])
+def test_builder_rejects_what_the_reference_rejects(kw):
+    plan = W.Plan(**{k: v for k, v in kw.items() if k in ("tq", "kb", "n_queues")})
+    rows = kw.get("rows", 1)
+    ctx = kw.get("ctx_max", 10)
+    with pytest.raises(QS.QueueError):
+        QS.build(W.LLAMA_LAYER_F32, plan, QS.MODE_DECODE, rows, ctx)
+    with pytest.raises(L.MkError) as e:
+        T.mk_build_queue(T.make_config(W.LLAMA_LAYER_F32), T.make_plan(plan, QS.MODE_DECODE, rows, ctx))
+    assert e.value.status == L.MK_EINVAL
+
+
+def test_prefill_rejects_partial_heads():
+    with pytest.raises(L.MkError):
+        T.mk_build_queue(T.make_config(W.LLAMA_LAYER_F32), T.make_plan(W.Plan(bn=48), QS.MODE_PREFILL, 8, 8))
+
+
+def test_workspace_layout_is_consistent():
+    wl = W.WORKLOADS["llama1b_b1"]
+    q = T.mk_build_queue(T.make_config(wl.model), T.make_plan(wl.plan, 0, 1, wl.run.ctx_max))
+    total = q.workspace_nbytes()
+    offs = [q.workspace_offset(T.MK_T_X, l) for l in range(17)]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert q.workspace_offset(T.MK_T_ERROR) < total
+    with pytest.raises(L.MkError):
+        q.workspace_offset(T.MK_T_QKV, 16)

@@ -1,0 +1,222 @@
+"""GPU parity of the decode path through the C ABI against the float64 oracle.
+
+Tolerances (max |gpu - oracle| / max |oracle| per tensor, step and row): 1e-4
+for the fp32 model, 2e-2 for the bf16 models.  Megakernel and kernel-per-op
+modes run the same op bodies and must agree bit for bit.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import tile_synchronized_decoder_amd as T
+import workloads as W
+from oracle import numerics as N
+from oracle import queue_spec as QS
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32, TOL_BF16 = 1e-4, 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from _gpucase import log
+    log(f"[gpu] {torch.cuda.get_device_name(0)} lib={T.library_path()}")
+
+
+def rel_rows(got, ref):
+    return max(N.max_rel_err(got[b], ref[b]) for b in range(ref.shape[0]))
+
+
+def check_step(c, tr, tol, layers=None):
+    """Compare workspace intermediates of one step with an oracle trace."""
+    m = c.m
+    errs = {}
+    for l in (layers if layers is not None else range(m.n_layers)):
+        errs[f"att{l}"] = rel_rows(c.tensor(T.MK_T_ATT, l, m.attn_cols), tr.attn[l])
+        errs[f"h{l}"] = rel_rows(c.tensor(T.MK_T_HRES, l, m.hidden), tr.h[l])
+        errs[f"act{l}"] = rel_rows(c.tensor(T.MK_T_ACT, l, m.ffn), tr.act[l])
+        hres = c.tensor(T.MK_T_HRES, l, m.hidden)
+        xin = c.tensor(T.MK_T_X, l, m.hidden)
+        xout = c.tensor(T.MK_T_X, l + 1, m.hidden)
+        errs[f"attn_branch{l}"] = rel_rows(hres - xin, tr.attn_branch[l])
+        errs[f"mlp_branch{l}"] = rel_rows(xout - hres, tr.mlp_branch[l])
+    errs["x_out"] = rel_rows(c.tensor(T.MK_T_X, m.n_layers, m.hidden), tr.x_out)
+    if c.logits is not None:
+        lg = c.logits.cpu().numpy().astype(np.float64)
+        errs["logits"] = rel_rows(lg, tr.logits)
+        nx = c.nxt.cpu().numpy()
+        assert np.array_equal(nx, N.argmax_lowest(c.logits.cpu().numpy())), "argmax of the GPU logits"
+    worst = max(errs, key=errs.get)
+    from _gpucase import log
+    log(f"    worst {worst} = {errs[worst]:.3e}")
+    assert errs[worst] <= tol, errs
+    return errs
+
+
+# ----------------------------------------------------------------------------- single fp32 layer
+
+@pytest.fixture(scope="module")
+def small():
+    from _gpucase import make_case
+    return make_case(W.WORKLOADS["layer256_f32"], gain_jitter=0.1)
+
+
+@pytest.mark.parametrize("mode", [T.MK_MEGAKERNEL, T.MK_KERNEL_PER_OP], ids=["mega", "kpo"])
+def test_layer_fp32_matches_oracle(small, mode):
+    c = small
+    c.reset_kv()
+    c.step(0, [128], mode)
+    K, V = c.K0.copy(), c.V0.copy()
+    tr = N.decode_step(c.oracle_model(), K, V, [128], x0=c.x0[0])
+    check_step(c, tr, TOL_F32)
+    Kg, Vg = c.kv_host()
+    assert N.max_rel_err(Kg[0, 0, :, 128], K[0, 0, :, 128]) < TOL_F32
+    assert N.max_rel_err(Vg[0, 0, :, 128], V[0, 0, :, 128]) < TOL_F32
+    # only position 128 changed
+    assert np.array_equal(Kg[0, 0, :, :128], c.K0[0, 0, :, :128])
+
+
+def test_layer_modes_bitwise_equal_and_counters(small):
+    c = small
+    outs = {}
+    for mode in (T.MK_KERNEL_PER_OP, T.MK_MEGAKERNEL, T.MK_MEGAKERNEL):
+        c.reset_kv()
+        c.ws.zero_()
+        c.step(0, [128], mode)
+        snap = {k: c.tensor(kind, 0, cols) for k, kind, cols in
+                (("att", T.MK_T_ATT, 256), ("h", T.MK_T_HRES, 256), ("act", T.MK_T_ACT, 688),
+                 ("x", T.MK_T_X, 256))}
+        snap["x"] = c.tensor(T.MK_T_X, 1, 256)
+        Kg, Vg = c.kv_host()
+        snap["k"], snap["v"] = Kg, Vg
+        if mode == T.MK_MEGAKERNEL:
+            tg = np.frombuffer(c.q.export(T.MK_PART_TARGETS), dtype=np.uint32)
+            assert np.array_equal(c.counters(), tg), "counters must equal targets after the step"
+            err = T.mk_device_error(c.q, c.ws)
+            assert err.code == 0
+        outs.setdefault(mode, []).append(snap)
+    a, b, b2 = outs[T.MK_KERNEL_PER_OP][0], outs[T.MK_MEGAKERNEL][0], outs[T.MK_MEGAKERNEL][1]
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+        assert np.array_equal(b[k], b2[k]), k
+
+
+@pytest.mark.parametrize("ctx", [0, 1, 31, 32, 64, 127])
+def test_layer_fp32_short_contexts(small, ctx):
+    c = small
+    c.reset_kv()
+    c.step(0, [ctx], T.MK_MEGAKERNEL)
+    tr = N.decode_step(c.oracle_model(), c.K0.copy(), c.V0.copy(), [ctx], x0=c.x0[0])
+    check_step(c, tr, TOL_F32)
+
+
+def test_layer_fp32_batch_ragged_tiles_subqueues():
+    from _gpucase import make_case
+    wl = W.WORKLOADS["layer256_f32"]
+    wl = W.Workload("layer256_b3_ragged", wl.model,
+                    W.RunConfig(batch=3, ctx0=(5, 128, 64), steps=1, ctx_max=129, seed=9),
+                    W.Plan(tq=24, to=40, tf=56, td=24, kb=48, n_queues=8))
+    c = make_case(wl, gain_jitter=0.1)
+    tr = N.decode_step(c.oracle_model(), c.K0.copy(), c.V0.copy(), list(wl.run.ctx0), x0=c.x0[0])
+    for mode in (T.MK_MEGAKERNEL, T.MK_KERNEL_PER_OP):
+        c.reset_kv()
+        c.step(0, list(wl.run.ctx0), mode)
+        check_step(c, tr, TOL_F32)
+
+
+# ----------------------------------------------------------------------------- bf16, 1B-shaped
+
+def _shrunk_1b(layers=2, vocab=4096, batch=1, ctx0=(1024,), steps=3):
+    base = W.WORKLOADS["llama1b_b1"]
+    return W.shrink(base, n_layers=layers, vocab=vocab, batch=batch, ctx0=ctx0, steps=steps,
+                    name=f"llama1b_L{layers}_V{vocab}_B{batch}")
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+def test_bf16_shrunk_multistep_matches_oracle(batch):
+    from _gpucase import make_case, log
+    ctx0 = tuple(1024 - 37 * b for b in range(batch))
+    wl = _shrunk_1b(batch=batch, ctx0=ctx0)
+    c = make_case(wl)
+    model = c.oracle_model()
+    K, V = c.K0.copy(), c.V0.copy()
+    for t in range(wl.run.steps):
+        ctx = [p + t for p in ctx0]
+        tr = N.decode_step(model, K, V, ctx, tokens=c.tokens[t])
+        c.step(t, ctx, T.MK_MEGAKERNEL)
+        log(f"  step {t}")
+        check_step(c, tr, TOL_BF16)
+    Kg, _ = c.kv_host()
+    # the cache rows written by the steps agree with the oracle's (bf16, rounding may differ by an ulp)
+    for t in range(wl.run.steps):
+        for b in range(batch):
+            p = ctx0[b] + t
+            assert N.max_rel_err(N.to_f64(Kg[:, b, :, p]), N.to_f64(K[:, b, :, p])) < 1e-2
+
+
+def test_bf16_shrunk_modes_bitwise_equal():
+    from _gpucase import make_case
+    wl = _shrunk_1b(batch=2, ctx0=(700, 1100), steps=1)
+    c = make_case(wl)
+    res = []
+    for mode in (T.MK_MEGAKERNEL, T.MK_KERNEL_PER_OP, T.MK_MEGAKERNEL):
+        c.reset_kv()
+        c.step(0, [700, 1100], mode)
+        res.append((c.logits.cpu().numpy().copy(), c.tensor(T.MK_T_X, 2, 2048), c.kv_host()[0]))
+    for r in res[1:]:
+        for a, b in zip(res[0], r):
+            assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------------------- full Llama-3-1B shape
+
+@pytest.mark.slow
+def test_llama1b_full_size_steps():
+    """The full 16-layer, 128256-vocab model: the first steps of the timed workload."""
+    from _gpucase import make_case, log
+    wl = W.shrink(W.WORKLOADS["llama1b_b1"], steps=3)
+    c = make_case(wl)
+    model = c.oracle_model()
+    K, V = c.K0.copy(), c.V0.copy()
+    for t in range(wl.run.steps):
+        ctx = [1024 + t]
+        tr = N.decode_step(model, K, V, ctx, tokens=c.tokens[t])
+        for mode in (T.MK_KERNEL_PER_OP, T.MK_MEGAKERNEL):
+            c.step(t, ctx, mode)
+            log(f"  step {t} mode {mode}")
+            check_step(c, tr, TOL_BF16, layers=[0, 7, 15])
+
+
+# ----------------------------------------------------------------------------- failure handling
+
+def test_watchdog_reports_unreachable_barrier(small):
+    """A queue whose first barrier target can never be reached: the bounded
+    waits expire, the kernel drains, and the error record names the wait."""
+    c = small
+    parts = c.q.export(T.MK_PART_DEVICE)
+    img = np.frombuffer(parts, dtype=np.uint8).copy()
+    tg_off = (c.q.nbytes(T.MK_PART_INSTR) + 255) // 256 * 256
+    tg_off += (c.q.nbytes(T.MK_PART_WAITS) + 255) // 256 * 256
+    targets = img[tg_off: tg_off + c.q.nbytes(T.MK_PART_TARGETS)].view(np.uint32)
+    targets[0] += 1                          # QKV tile 0 signals once; nobody reaches 2
+    bad = torch.from_numpy(img).cuda()
+    old = T.mk_get_option(T.MK_OPT_SPIN_LIMIT)
+    T.mk_set_option(T.MK_OPT_SPIN_LIMIT, 20000)
+    try:
+        c.reset_kv()
+        cl = torch.tensor([128], dtype=torch.int32, device="cuda")
+        x0 = torch.from_numpy(c.x0[0]).cuda()
+        T.mk_decode_step(c.q, bad, c.dm.w, c.dkv.kv, None, x0, cl, 1, c.ws, None, None, T.MK_MEGAKERNEL)
+        err = T.mk_device_error(c.q, c.ws)
+    finally:
+        T.mk_set_option(T.MK_OPT_SPIN_LIMIT, old)
+    assert err.code == 1 and err.value < err.target
+    # the next good step clears the record and is correct again
+    c.reset_kv()
+    c.step(0, [128], T.MK_MEGAKERNEL)
+    assert T.mk_device_error(c.q, c.ws).code == 0

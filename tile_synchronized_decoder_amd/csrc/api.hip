@@ -1,0 +1,343 @@
+// C ABI of the tile-synchronized decoder: argument checks, workspace layout,
+// and the launches of one decode step (megakernel or one kernel per op).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <mutex>
+
+#include "kernels.h"
+#include "mk.h"
+#include "queue.h"
+
+namespace mkd {
+#define MK_DECL(T) Table table_##T##_1(); Table table_##T##_2(); Table table_##T##_4(); \
+  Table table_##T##_8(); Table table_##T##_16(); Table table_##T##_32();
+MK_DECL(bf16)
+MK_DECL(f32)
+#undef MK_DECL
+}  // namespace mkd
+
+namespace {
+
+using namespace mkd;
+
+// ----------------------------------------------------------------------------- kernels used only here
+
+__global__ void reset_kernel(uint32_t* counters, uint32_t n, uint32_t* heads, uint32_t nh, uint32_t* err) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  for (uint32_t k = i; k < n; k += stride) counters[k] = 0;
+  for (uint32_t k = i; k < nh * 32; k += stride) heads[k] = 0;
+  for (uint32_t k = i; k < 8; k += stride) err[k] = 0;
+}
+
+__global__ void copy_rows_kernel(float* dst, const float* src, size_t n) {
+  for (size_t k = blockIdx.x * (size_t)blockDim.x + threadIdx.x; k < n; k += (size_t)gridDim.x * blockDim.x) dst[k] = src[k];
+}
+
+__global__ __launch_bounds__(NT) void argmax_kernel(Args args) {
+  KArgs& a = kernel_args();
+  __shared__ float bv[NT];
+  __shared__ int bi[NT];
+  const int b = blockIdx.x;
+  float best = -INFINITY;
+  int besti = 0x7FFFFFFF;
+  for (int k = threadIdx.x; k < a.lm_blocks; k += NT) {
+    const float v = a.lm_val[(size_t)b * a.lm_blocks + k];
+    const int i = a.lm_idx[(size_t)b * a.lm_blocks + k];
+    if (v > best || (v == best && i < besti)) { best = v; besti = i; }
+  }
+  bv[threadIdx.x] = best;
+  bi[threadIdx.x] = besti;
+  __syncthreads();
+  for (int w = NT / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) {
+      const float v = bv[threadIdx.x + w];
+      const int i = bi[threadIdx.x + w];
+      if (v > bv[threadIdx.x] || (v == bv[threadIdx.x] && i < bi[threadIdx.x])) { bv[threadIdx.x] = v; bi[threadIdx.x] = i; }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.next[b] = bi[0];
+}
+
+
+// ----------------------------------------------------------------------------- host side
+
+struct Options {
+  int workers_per_cu = 1;
+  uint32_t spin_limit = 1u << 22;
+};
+Options g_opt;
+
+int num_cus() {
+  static int n = 0;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n = 0;
+    if (n <= 0) n = 256;
+  });
+  return n;
+}
+
+inline size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Layout {
+  size_t X, QKV, OPART, ATT, HRES, ACT, LMV, LMI, CTR, HEADS, ERR, total;
+  size_t sX, sQKV, sOP, sATT, sHRES, sACT;   // per-layer strides in floats
+  int lm_blocks;
+};
+
+Layout layout(const mk_queue* q) {
+  const mk_config& c = q->cfg;
+  const size_t M = q->plan.rows, L = c.n_layers, hd = c.head_dim, r = c.n_q_heads / c.n_kv_heads;
+  const size_t NQKV = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * hd;
+  const size_t NS = q->n_splits ? q->n_splits : 1;
+  Layout o{};
+  o.sX = up256(M * c.hidden * 4) / 4;
+  o.sQKV = up256(M * NQKV * 4) / 4;
+  o.sOP = up256(M * c.n_kv_heads * NS * (r * hd + 2 * r) * 4) / 4;
+  o.sATT = up256(M * c.n_q_heads * hd * 4) / 4;
+  o.sHRES = up256(M * c.hidden * 4) / 4;
+  o.sACT = up256(M * c.ffn * 4) / 4;
+  o.lm_blocks = c.has_lm_head ? (c.vocab + 15) / 16 : 1;
+  size_t off = 0;
+  o.X = off; off += (L + 1) * o.sX * 4;
+  o.QKV = off; off += L * o.sQKV * 4;
+  o.OPART = off; off += L * o.sOP * 4;
+  o.ATT = off; off += L * o.sATT * 4;
+  o.HRES = off; off += L * o.sHRES * 4;
+  o.ACT = off; off += L * o.sACT * 4;
+  o.LMV = off; off += up256(M * o.lm_blocks * 4);
+  o.LMI = off; off += up256(M * o.lm_blocks * 4);
+  o.CTR = off; off += up256(q->targets.size() * 4);
+  o.HEADS = off; off += up256((size_t)q->plan.n_queues * 128);
+  o.ERR = off; off += 256;
+  o.total = off;
+  return o;
+}
+
+Table pick_table(int dtype, int nb) {
+  const bool bf = dtype == MK_BF16;
+  if (nb <= 1) return bf ? table_bf16_1() : table_f32_1();
+  if (nb <= 2) return bf ? table_bf16_2() : table_f32_2();
+  if (nb <= 4) return bf ? table_bf16_4() : table_f32_4();
+  if (nb <= 8) return bf ? table_bf16_8() : table_f32_8();
+  if (nb <= 16) return bf ? table_bf16_16() : table_f32_16();
+  return bf ? table_bf16_32() : table_f32_32();
+}
+
+// Everything the kernels need except the per-call inputs and outputs.
+void fill_args(const mk_queue* q, const void* d_queue, const mk_weights* w, const mk_kv* kv, void* d_workspace,
+               const Layout& o, Args& a) {
+  const mk_config& c = q->cfg;
+  uint8_t* ws = static_cast<uint8_t*>(d_workspace);
+  const uint8_t* qd = static_cast<const uint8_t*>(d_queue);
+  a.L = c.n_layers; a.H = c.hidden; a.nq = c.n_q_heads; a.nkv = c.n_kv_heads; a.hd = c.head_dim;
+  a.r = c.n_q_heads / c.n_kv_heads; a.F = c.ffn; a.V = c.vocab;
+  a.NQKV = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim; a.NA = c.n_q_heads * c.head_dim;
+  a.M = q->plan.rows; a.NS = q->n_splits; a.kb = q->plan.kb; a.ctx_max = q->plan.ctx_max;
+  a.qk_norm = c.qk_norm; a.has_embed = c.has_embed; a.eps = c.rms_eps; a.theta = c.rope_theta;
+  a.wqkv = w->wqkv; a.wo = w->wo; a.wgate = w->wgate; a.wup = w->wup; a.wdown = w->wdown;
+  a.attn_norm = w->attn_norm; a.ffn_norm = w->ffn_norm; a.q_norm = w->q_norm; a.k_norm = w->k_norm;
+  a.embed = w->embed; a.lm_head = w->lm_head; a.final_norm = w->final_norm;
+  a.kc = kv->k; a.vc = kv->v;
+  a.X = reinterpret_cast<float*>(ws + o.X); a.QKV = reinterpret_cast<float*>(ws + o.QKV);
+  a.OPART = reinterpret_cast<float*>(ws + o.OPART); a.ATT = reinterpret_cast<float*>(ws + o.ATT);
+  a.HRES = reinterpret_cast<float*>(ws + o.HRES); a.ACT = reinterpret_cast<float*>(ws + o.ACT);
+  a.sX = o.sX; a.sQKV = o.sQKV; a.sOP = o.sOP; a.sATT = o.sATT; a.sHRES = o.sHRES; a.sACT = o.sACT;
+  a.lm_val = reinterpret_cast<float*>(ws + o.LMV); a.lm_idx = reinterpret_cast<int*>(ws + o.LMI);
+  a.lm_blocks = o.lm_blocks;
+  a.counters = reinterpret_cast<uint32_t*>(ws + o.CTR); a.heads = reinterpret_cast<uint32_t*>(ws + o.HEADS);
+  a.err = reinterpret_cast<uint32_t*>(ws + o.ERR);
+  a.instr = reinterpret_cast<const Instr*>(qd + q->dev_instr_off);
+  a.ranges = reinterpret_cast<const Range*>(qd + q->dev_waits_off);
+  a.targets = reinterpret_cast<const uint32_t*>(qd + q->dev_targets_off);
+  a.n_instr = (uint32_t)q->instr.size(); a.n_barriers = (uint32_t)q->targets.size();
+  a.n_queues = (uint32_t)q->plan.n_queues;
+}
+
+// Final RMSNorm + LM head GEMV (+ argmax) over the workspace's last hidden rows.
+hipError_t launch_lm(const Table& t, const Args& a, bool want_next, hipStream_t stream) {
+  hipError_t e = t.lm(a, stream);
+  if (e == hipSuccess && want_next) {
+    hipLaunchKernelGGL(argmax_kernel, dim3(a.M), dim3(NT), 0, stream, a);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+#define FAIL(code, ...) do { mk::set_error(__VA_ARGS__); return (code); } while (0)
+
+mk_status check_shapes(const mk_config& c) {
+  if (c.hidden % 8 || c.ffn % 8 || (c.n_q_heads * c.head_dim) % 8)
+    FAIL(MK_EINVAL, "hidden, ffn and n_q_heads*head_dim must be multiples of 8");
+  if (c.head_dim != 64 && c.head_dim != 128) FAIL(MK_ENOTSUP, "head_dim must be 64 or 128");
+  if (c.dtype == MK_F32 && c.head_dim != 64) FAIL(MK_ENOTSUP, "fp32 caches support head_dim 64 only");
+  if (c.n_q_heads / c.n_kv_heads > ATT_MAX_R) FAIL(MK_ENOTSUP, "at most %d query heads per KV head", ATT_MAX_R);
+  if (c.dtype != MK_F32 && c.dtype != MK_BF16) FAIL(MK_EINVAL, "unknown dtype");
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mk_status mk_workspace_nbytes(const mk_queue* q, size_t* nbytes) {
+  if (!q || !nbytes) FAIL(MK_EINVAL, "null argument");
+  *nbytes = layout(q).total;
+  return MK_OK;
+}
+
+mk_status mk_workspace_offset(const mk_queue* q, int32_t tensor, int32_t layer, size_t* offset) {
+  if (!q || !offset) FAIL(MK_EINVAL, "null argument");
+  const Layout o = layout(q);
+  const int L = q->cfg.n_layers;
+  const int lmax = tensor == MK_T_X ? L : (tensor <= MK_T_ACT ? L - 1 : 0);
+  if (layer < 0 || layer > lmax) FAIL(MK_EINVAL, "layer %d out of range for tensor %d", layer, tensor);
+  switch (tensor) {
+    case MK_T_X: *offset = o.X + (size_t)layer * o.sX * 4; break;
+    case MK_T_QKV: *offset = o.QKV + (size_t)layer * o.sQKV * 4; break;
+    case MK_T_OPART: *offset = o.OPART + (size_t)layer * o.sOP * 4; break;
+    case MK_T_ATT: *offset = o.ATT + (size_t)layer * o.sATT * 4; break;
+    case MK_T_HRES: *offset = o.HRES + (size_t)layer * o.sHRES * 4; break;
+    case MK_T_ACT: *offset = o.ACT + (size_t)layer * o.sACT * 4; break;
+    case MK_T_COUNTERS: *offset = o.CTR; break;
+    case MK_T_HEADS: *offset = o.HEADS; break;
+    case MK_T_ERROR: *offset = o.ERR; break;
+    case MK_T_LMPART: *offset = o.LMV; break;
+    default: FAIL(MK_EINVAL, "unknown tensor %d", tensor);
+  }
+  return MK_OK;
+}
+
+mk_status mk_decode_step(const mk_queue* q, const void* d_queue, const mk_weights* w, const mk_kv* kv,
+                         const int32_t* d_tokens, const float* d_x0, const int32_t* d_ctx_lens,
+                         int32_t batch, void* d_workspace, size_t workspace_nbytes, float* d_logits,
+                         int32_t* d_next, int32_t exec_mode, hipStream_t stream) {
+  if (!q || !d_queue || !w || !kv || !d_ctx_lens || !d_workspace) FAIL(MK_EINVAL, "null argument");
+  if (q->plan.mode != MK_DECODE) FAIL(MK_EINVAL, "queue was not built for decode");
+  const mk_config& c = q->cfg;
+  if (mk_status st = check_shapes(c)) return st;
+  if (batch != q->plan.rows) FAIL(MK_EINVAL, "batch %d differs from the queue's rows %d", batch, q->plan.rows);
+  if (exec_mode != MK_MEGAKERNEL && exec_mode != MK_KERNEL_PER_OP) FAIL(MK_EINVAL, "unknown exec_mode");
+  const int nb_bucket = q->plan.rows <= 1 ? 1 : q->plan.rows <= 2 ? 2 : q->plan.rows <= 4 ? 4 : q->plan.rows <= 8 ? 8 : q->plan.rows <= 16 ? 16 : 32;
+  const int max_rows = std::max({q->plan.tq, q->plan.to, 2 * q->plan.tf, q->plan.td, 16});
+  if (max_rows * nb_bucket > RES_FLOATS) FAIL(MK_ENOTSUP, "tile rows x batch above %d", RES_FLOATS);
+  const Layout o = layout(q);
+  if (workspace_nbytes < o.total) FAIL(MK_EINVAL, "workspace of %zu bytes, need %zu", workspace_nbytes, o.total);
+  if (c.has_embed ? (!d_tokens || !w->embed) : !d_x0) FAIL(MK_EINVAL, "missing input tokens / rows");
+  if (!w->wqkv || !w->wo || !w->wgate || !w->wup || !w->wdown || !w->attn_norm || !w->ffn_norm || !kv->k || !kv->v)
+    FAIL(MK_EINVAL, "missing weights or cache");
+  if (c.qk_norm && (!w->q_norm || !w->k_norm)) FAIL(MK_EINVAL, "missing QK-norm gains");
+  if (c.has_lm_head && (d_logits || d_next) && (!w->lm_head || !w->final_norm)) FAIL(MK_EINVAL, "missing LM head");
+
+  Args a{};
+  fill_args(q, d_queue, w, kv, d_workspace, o, a);
+  a.tokens = d_tokens; a.x0 = d_x0; a.ctx_lens = d_ctx_lens;
+  a.logits = d_logits; a.next = d_next;
+  a.spin_limit = g_opt.spin_limit;
+
+  // without an embedding the input rows are copied into X_0 by the first launch
+  if (!c.has_embed) {
+    const size_t n = (size_t)a.M * a.H;
+    hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)std::min<size_t>((n + 255) / 256, 1024)), dim3(256), 0, stream,
+                       a.X, d_x0, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) FAIL(MK_ELAUNCH, "copy of input rows: %s", hipGetErrorString(e));
+  }
+  const Table t = pick_table(c.dtype, a.M);
+  hipError_t e = hipSuccess;
+  if (exec_mode == MK_MEGAKERNEL) {
+    const int grid = num_cus() * g_opt.workers_per_cu;
+    if (grid < (int)a.n_queues) FAIL(MK_EINVAL, "fewer workers than sub-queues");
+    const uint32_t nr = a.n_barriers;
+    hipLaunchKernelGGL(reset_kernel, dim3((nr + 255) / 256 + 1), dim3(256), 0, stream, a.counters, nr, a.heads,
+                       a.n_queues, a.err);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = t.mega(a, grid, stream);
+  } else {
+    for (const mk::Segment& sg : q->segments) {
+      e = t.kpo(a, sg.op, sg.first, sg.count, stream);
+      if (e != hipSuccess) break;
+    }
+  }
+  if (e == hipSuccess && c.has_lm_head && (d_logits || d_next)) e = launch_lm(t, a, d_next != nullptr, stream);
+  if (e != hipSuccess) FAIL(MK_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return MK_OK;
+}
+
+mk_status mk_lm_head(const mk_queue* q, const mk_weights* w, void* d_workspace, size_t workspace_nbytes,
+                     float* d_logits, int32_t* d_next, hipStream_t stream) {
+  if (!q || !w || !d_workspace) FAIL(MK_EINVAL, "null argument");
+  const mk_config& c = q->cfg;
+  if (!c.has_lm_head) FAIL(MK_EINVAL, "the model has no LM head");
+  if (!w->lm_head || !w->final_norm) FAIL(MK_EINVAL, "missing LM head");
+  if (!d_logits && !d_next) return MK_OK;
+  const Layout o = layout(q);
+  if (workspace_nbytes < o.total) FAIL(MK_EINVAL, "workspace of %zu bytes, need %zu", workspace_nbytes, o.total);
+  Args a{};
+  uint8_t* ws = static_cast<uint8_t*>(d_workspace);
+  a.L = c.n_layers; a.H = c.hidden; a.V = c.vocab; a.M = q->plan.rows;
+  a.eps = c.rms_eps;
+  a.lm_head = w->lm_head; a.final_norm = w->final_norm;
+  a.X = reinterpret_cast<float*>(ws + o.X); a.sX = o.sX;
+  a.lm_val = reinterpret_cast<float*>(ws + o.LMV); a.lm_idx = reinterpret_cast<int*>(ws + o.LMI);
+  a.lm_blocks = o.lm_blocks; a.err = reinterpret_cast<uint32_t*>(ws + o.ERR);
+  a.logits = d_logits; a.next = d_next;
+  const hipError_t e = launch_lm(pick_table(c.dtype, a.M), a, d_next != nullptr, stream);
+  if (e != hipSuccess) FAIL(MK_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return MK_OK;
+}
+
+mk_status mk_prefill(const mk_queue* q, const void* d_queue, const mk_weights* w, const mk_kv* kv,
+                     const int32_t* d_tokens, int32_t seq_len, int32_t kv_row, void* d_workspace,
+                     size_t workspace_nbytes, float* d_logits_last, int32_t* d_next, int32_t exec_mode,
+                     hipStream_t stream) {
+  (void)d_queue; (void)w; (void)kv; (void)d_tokens; (void)seq_len; (void)kv_row; (void)d_workspace;
+  (void)workspace_nbytes; (void)d_logits_last; (void)d_next; (void)exec_mode; (void)stream;
+  if (!q) FAIL(MK_EINVAL, "null argument");
+  if (q->plan.mode != MK_PREFILL) FAIL(MK_EINVAL, "queue was not built for prefill");
+  FAIL(MK_ENOTSUP, "prefill op bodies are not built yet");
+}
+
+mk_status mk_device_error(const mk_queue* q, const void* d_workspace, mk_dev_error* out, hipStream_t stream) {
+  if (!q || !d_workspace || !out) FAIL(MK_EINVAL, "null argument");
+  const Layout o = layout(q);
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) FAIL(MK_EDEVICE, "stream: %s", hipGetErrorString(e));
+  uint32_t rec[8];
+  e = hipMemcpy(rec, static_cast<const uint8_t*>(d_workspace) + o.ERR, sizeof(rec), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) FAIL(MK_EDEVICE, "copy: %s", hipGetErrorString(e));
+  out->code = rec[0]; out->instr = rec[1]; out->barrier = rec[2]; out->value = rec[3]; out->target = rec[4];
+  return rec[0] ? MK_EDEVICE : MK_OK;
+}
+
+mk_status mk_set_option(int32_t key, int64_t value) {
+  switch (key) {
+    case MK_OPT_WORKERS_PER_CU:
+      if (value < 1 || value > 8) FAIL(MK_EINVAL, "workers per CU must be 1..8");
+      g_opt.workers_per_cu = (int)value; return MK_OK;
+    case MK_OPT_SPIN_LIMIT:
+      if (value < 1 || value > (int64_t)1 << 31) FAIL(MK_EINVAL, "spin limit out of range");
+      g_opt.spin_limit = (uint32_t)value; return MK_OK;
+    default: FAIL(MK_EINVAL, "unknown or read-only option %d", key);
+  }
+}
+
+int64_t mk_get_option(int32_t key) {
+  switch (key) {
+    case MK_OPT_WORKERS_PER_CU: return g_opt.workers_per_cu;
+    case MK_OPT_SPIN_LIMIT: return g_opt.spin_limit;
+    case MK_OPT_NUM_CUS: return num_cus();
+    default: return -1;
+  }
+}
+
+}  // extern "C"

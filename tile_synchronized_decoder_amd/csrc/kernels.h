@@ -1,0 +1,865 @@
+// Tile-synchronized decoder for gfx950: op bodies, the persistent interpreter,
+// the kernel-per-operator kernels and the LM head (device code, templates).
+//
+// Method (sources cited in include/mk.h): one persistent kernel whose
+// workgroups act as interpreters ("Production Megakernels" lecture summary,
+// Technical details: a loop around a switch; cores atomically pop
+// instructions from a global queue in DRAM).  Each instruction computes one
+// tile of one intermediate tensor and first waits on the counters of exactly
+// the producer tiles it reads (MegaOps abstract: tile-granular dependencies
+// instead of kernel barriers), issuing its weight loads before it waits so the
+// weights stream while producers finish (MegaOps abstract: prefetching
+// weights while the preceding kernel runs; lecture summary: memory
+// pipelining).  The decoder arithmetic is the standard pre-norm Llama/Qwen
+// block.
+//
+// gfx950 specifics: 64-lane wavefronts, 4 waves (256 threads) per workgroup,
+// one workgroup per compute unit by default; weights are streamed with
+// 16-byte non-temporal loads; barrier hand-off uses agent-scope release /
+// acquire, which on this part writes back / invalidates the per-XCD L2 so a
+// tile written on one XCD is visible on another.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <algorithm>
+#include <mutex>
+
+#include "mk.h"
+#include "queue.h"
+
+
+namespace mkd {
+
+using mk::Instr;
+using mk::Range;
+
+constexpr int NT = 256;                 // threads per workgroup
+constexpr int NWAVE = NT / 64;
+constexpr int XBUF_FLOATS = 16384;      // LDS staging of GEMV inputs (64 KB)
+constexpr int RES_FLOATS = 2048;        // LDS GEMV results (rows x batch)
+constexpr int ROWS_PER_PASS_MAX = 16;   // GEMV rows reduced per pass (4 waves x 4)
+constexpr int ATT_MAX_R = 4;            // query heads per KV head
+constexpr int ATT_CHUNK = NT;           // keys scored per attention chunk
+constexpr uint32_t ERR_TIMEOUT = 1, ERR_OPCODE = 2, ERR_CONTEXT = 3, ERR_TOKEN = 4;
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// ----------------------------------------------------------------------------- kernel arguments
+
+struct Args {
+  // shape
+  int L, H, nq, nkv, hd, r, F, V, NQKV, NA, M, NS, kb, ctx_max, qk_norm, has_embed;
+  float eps;
+  double theta;
+  // weights
+  const void* wqkv; const void* wo; const void* wgate; const void* wup; const void* wdown;
+  const float* attn_norm; const float* ffn_norm; const float* q_norm; const float* k_norm;
+  const void* embed; const void* lm_head; const float* final_norm;
+  void* kc; void* vc;
+  // workspace
+  float* X; float* QKV; float* OPART; float* ATT; float* HRES; float* ACT;
+  size_t sX, sQKV, sOP, sATT, sHRES, sACT;     // per-layer strides (floats)
+  float* lm_val; int* lm_idx; int lm_blocks;
+  uint32_t* counters; uint32_t* heads; uint32_t* err;
+  // queue
+  const Instr* instr; const Range* ranges; const uint32_t* targets;
+  uint32_t n_instr, n_barriers, n_queues;
+  // runtime inputs / outputs
+  const int* tokens; const float* x0; const int* ctx_lens;
+  float* logits; int* next;
+  uint32_t spin_limit;
+};
+
+// Device code reads the arguments in place, through a constant-address-space
+// reference to the kernel argument segment: loads stay scalar, and the
+// interpreter launders the pointer every iteration so the compiler cannot
+// hoist every op's argument loads out of the loop (which would exhaust the
+// scalar registers and spill).
+using KArgs = const __attribute__((address_space(4))) Args;
+
+__device__ __forceinline__ KArgs& kernel_args() {
+  auto p = __builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return *(KArgs*)p;
+}
+
+// The 32-byte instruction record, read once and kept in scalar registers.
+__device__ __forceinline__ Instr load_instr(KArgs& a, uint32_t idx) {
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(a.instr + idx);
+  uint32_t w[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w[k] = __builtin_amdgcn_readfirstlane(__builtin_nontemporal_load(p + k));
+  Instr in;
+  in.op = (uint16_t)(w[0] & 0xFFFF); in.layer = (uint16_t)(w[0] >> 16);
+  in.a0 = w[1]; in.a1 = w[2]; in.a2 = w[3]; in.wait_off = w[4]; in.wait_cnt = w[5]; in.signal = w[6]; in.n_wait = w[7];
+  return in;
+}
+
+// ----------------------------------------------------------------------------- small helpers
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// float -> bf16 bits, round to nearest, ties to even (finite inputs)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> {           // bf16 storage
+  static constexpr int VEC = 1;               // 16-byte words per 8 elements
+  __device__ static float get(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+  __device__ static void put(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+  __device__ static float rounded(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+  __device__ static void unpack(const v4u* w, float f[8]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      f[2 * k] = __uint_as_float(w[0][k] << 16);
+      f[2 * k + 1] = __uint_as_float(w[0][k] & 0xFFFF0000u);
+    }
+  }
+};
+template <> struct Elem<float> {
+  static constexpr int VEC = 2;
+  __device__ static float get(const float* p, size_t i) { return p[i]; }
+  __device__ static void put(float* p, size_t i, float v) { p[i] = v; }
+  __device__ static float rounded(float v) { return v; }
+  __device__ static void unpack(const v4u* w, float f[8]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { f[k] = __uint_as_float(w[0][k]); f[4 + k] = __uint_as_float(w[1][k]); }
+  }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ----------------------------------------------------------------------------- barriers
+
+__device__ __forceinline__ bool aborted(KArgs& a) {
+  return __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+}
+
+__device__ inline void record_error(KArgs& a, uint32_t code, uint32_t idx, uint32_t bar, uint32_t val, uint32_t tgt) {
+  uint32_t expected = 0;
+  if (__hip_atomic_compare_exchange_strong(a.err, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)) {
+    a.err[1] = idx; a.err[2] = bar; a.err[3] = val; a.err[4] = tgt;
+  }
+}
+
+// Block until every barrier in the instruction's wait list reaches its target.
+// Threads poll disjoint subsets; each poller then acquires at agent scope and
+// the workgroup barrier orders everyone's later reads after those acquires.
+// Returns false if the wait gave up (timeout or another worker aborted).
+__device__ __forceinline__ bool wait_tiles(KArgs& a, const Instr in, uint32_t idx) {
+  bool ok = true;
+  bool polled = false;
+  uint32_t base = 0;
+  for (uint32_t k = 0; k < in.wait_cnt; ++k) {
+    const Range rg = a.ranges[in.wait_off + k];
+    for (uint32_t j = threadIdx.x; j < rg.count && ok; j += NT) {
+      const uint32_t id = rg.first + j;
+      const uint32_t tgt = a.targets[id];
+      uint32_t spins = 0;
+      polled = true;
+      uint32_t v;
+      while ((v = __hip_atomic_load(a.counters + id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < tgt) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins >= a.spin_limit) { record_error(a, ERR_TIMEOUT, idx, id, v, tgt); ok = false; break; }
+        if ((spins & 255) == 0 && aborted(a)) { ok = false; break; }
+      }
+    }
+    base += rg.count;
+  }
+  (void)base;
+  if (polled) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return __syncthreads_and(ok) != 0;
+}
+
+// Publish this instruction's tile: every wave makes its stores visible at
+// agent scope, then one thread bumps the tile's counter.
+__device__ __forceinline__ void signal_tile(KArgs& a, const Instr in) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(a.counters + in.signal, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ----------------------------------------------------------------------------- shared memory arena
+
+struct Smem {
+  union {
+    float x[XBUF_FLOATS];                                          // GEMV input rows (gain applied)
+    struct {
+      float q[ATT_MAX_R * 128];                                    // rotated queries
+      float kn[128], vn[128];                                      // new key / value (as stored)
+      float cs[64], sn[64];                                        // rotary cos / sin
+      float p[ATT_MAX_R * ATT_CHUNK];                              // scores -> probabilities
+      float red[NWAVE * ATT_MAX_R];
+      float m[ATT_MAX_R], l[ATT_MAX_R], alpha[ATT_MAX_R];
+      uint16_t vbuf[ATT_CHUNK * 128];                              // value rows of the chunk (raw, <= 256 B each)
+    } att;
+  };
+  float res[RES_FLOATS];
+  float ss[32];
+  float ssw[NWAVE * 32];
+  uint32_t idx;
+};
+
+// ----------------------------------------------------------------------------- GEMV op bodies
+
+// Rows of a pass come from up to two matrices: row i < split reads A[row0+i],
+// row i >= split reads B[row0+i-split] (gate / up).  RPW rows per wave.
+template <typename WT, int NB, int RPW>
+struct Gemv {
+  static constexpr int ROWS = NWAVE * RPW;
+  static constexpr int WIN = 2;          // 512-column iterations per register window
+  using E = Elem<WT>;
+
+  struct Win { v4u w[WIN][RPW][E::VEC]; };
+
+  const WT* A; const WT* B; int split; int row0; int nrows; int K;
+
+  __device__ const WT* row_ptr(int i) const { return i < split ? A + (size_t)(row0 + i) * K : B + (size_t)(row0 + i - split) * K; }
+
+  // Issue the loads of iterations [it0, min(it0 + WIN, it_lim)) of this wave's rows of pass `pass`.
+  __device__ void load(Win& W, int pass, int it0, int it_lim) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < WIN; ++i)
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) {
+        const int row = pass * ROWS + wave * RPW + j;
+        const int col = (it0 + i) * 512 + lane * 8;
+        if (row < nrows && col < K && it0 + i < it_lim) {
+          const v4u* p = reinterpret_cast<const v4u*>(row_ptr(row) + col);
+#pragma unroll
+          for (int v = 0; v < E::VEC; ++v) W.w[i][j][v] = __builtin_nontemporal_load(p + v);
+        } else {
+#pragma unroll
+          for (int v = 0; v < E::VEC; ++v) W.w[i][j][v] = v4u{0, 0, 0, 0};
+        }
+      }
+  }
+
+  // Accumulate iterations [it0, it0 + WIN) against the staged inputs (columns kc0..).
+  __device__ void fma(const Win& W, int it0, int it_lim, int kc0, int kcn, int nb, const float* xs,
+                      float acc[RPW][NB]) const {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < WIN; ++i) {
+      const int col = (it0 + i) * 512 + lane * 8;
+      if (it0 + i >= it_lim || col >= K) break;
+      float wf[RPW][8];
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) E::unpack(W.w[i][j], wf[j]);
+      const int c = col - kc0;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (b >= nb) break;
+        const float4 x0 = *reinterpret_cast<const float4*>(xs + b * kcn + c);
+        const float4 x1 = *reinterpret_cast<const float4*>(xs + b * kcn + c + 4);
+        const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int j = 0; j < RPW; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[j][b] = fmaf(wf[j][e], xv[e], acc[j][b]);
+      }
+    }
+  }
+};
+
+// Stage x[b][k0:k0+kn] * gain into LDS; accumulate sum(x^2) per row when asked.
+template <int NB>
+__device__ __forceinline__ void stage_x(Smem& s, const float* x, int ldx, int nb, int k0, int kn, const float* gain, bool want_ss,
+                        float ss[NB]) {
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b >= nb) break;
+    for (int k = threadIdx.x * 4; k < kn; k += NT * 4) {
+      float4 v = *reinterpret_cast<const float4*>(x + (size_t)b * ldx + k0 + k);
+      if (want_ss) ss[b] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      if (gain) {
+        const float4 g = *reinterpret_cast<const float4*>(gain + k0 + k);
+        v.x *= g.x; v.y *= g.y; v.z *= g.z; v.w *= g.w;
+      }
+      *reinterpret_cast<float4*>(s.x + b * kn + k) = v;
+    }
+  }
+}
+
+// Full GEMV of `nrows` rows against `nb` input rows of length K, results in
+// s.res[row * NB + b] (already scaled by the row's RMSNorm factor when `norm`).
+// When `mega`, the first weight window is issued before waiting on the
+// instruction's producer tiles.  Returns false when the wait gave up.
+template <typename WT, int NB, int RPW>
+__device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW>& g, const float* x, int nb,
+                     const float* gain, bool norm, bool mega, const Instr in, uint32_t idx) {
+  using G = Gemv<WT, NB, RPW>;
+  const int K = g.K;
+  const int iters = (K + 511) / 512;
+  const int kc_max = (XBUF_FLOATS / NB) / 512 * 512;
+  const int npass = (g.nrows + G::ROWS - 1) / G::ROWS;
+  const bool single_chunk = K <= kc_max;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+
+  typename G::Win W0, W1;
+  g.load(W0, 0, 0, min(iters, kc_max / 512));          // weight prefetch, before any wait
+  if (mega && !wait_tiles(a, in, idx)) return false;
+
+  float ssl[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) ssl[b] = 0.f;
+  bool staged = false;
+
+  for (int pass = 0; pass < npass; ++pass) {
+    float acc[RPW][NB];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[j][b] = 0.f;
+    if (pass > 0) g.load(W0, pass, 0, min(iters, kc_max / 512));
+    for (int kc0 = 0; kc0 < K; kc0 += kc_max) {
+      const int kcn = min(kc_max, K - kc0);
+      if (!(single_chunk && staged)) {
+        __syncthreads();
+        stage_x<NB>(s, x, K, nb, kc0, kcn, gain, norm && pass == 0, ssl);
+        __syncthreads();
+        staged = true;
+      }
+      const int it_begin = kc0 / 512, it_end = (kc0 + kcn + 511) / 512;
+      for (int it = it_begin; it < it_end; it += 2 * G::WIN) {
+        if (it + G::WIN < it_end) g.load(W1, pass, it + G::WIN, it_end);
+        g.fma(W0, it, it_end, kc0, kcn, nb, s.x, acc);
+        if (it + G::WIN < it_end) {
+          if (it + 2 * G::WIN < it_end) g.load(W0, pass, it + 2 * G::WIN, it_end);
+          g.fma(W1, it + G::WIN, it_end, kc0, kcn, nb, s.x, acc);
+        }
+      }
+      // the next chunk restarts its window from the first iteration of the chunk
+      if (kc0 + kc_max < K) g.load(W0, pass, (kc0 + kc_max) / 512, min(iters, (kc0 + 2 * kc_max) / 512));
+    }
+    // reduce each (row, b) across the wave; lane 0 keeps the sum
+#pragma unroll
+    for (int j = 0; j < RPW; ++j)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float v = wave_sum(acc[j][b]);
+        const int row = pass * G::ROWS + wave * RPW + j;
+        if (lane == 0 && row < g.nrows && b < nb) s.res[row * NB + b] = v;
+      }
+  }
+  (void)iters;
+  if (norm) {
+    // every thread staged a disjoint part of the rows: reduce sum(x^2) over the workgroup
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float v = wave_sum(ssl[b]);
+      if (lane == 0) s.ssw[wave * 32 + b] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < nb) {
+      float t = 0.f;
+      for (int w = 0; w < NWAVE; ++w) t += s.ssw[w * 32 + threadIdx.x];
+      s.ss[threadIdx.x] = 1.0f / sqrtf(t / (float)K + a.eps);
+    }
+  }
+  __syncthreads();
+  if (norm) {
+    for (int e = threadIdx.x; e < g.nrows * nb; e += NT) {
+      const int row = e / nb, b = e - row * nb;
+      s.res[row * NB + b] *= s.ss[b];
+    }
+    __syncthreads();
+  }
+  return true;
+}
+
+template <int NB> constexpr int rpw_for() { return NB >= 16 ? 2 : 4; }
+
+// QKV(n0, n1): QKV_l[:, n0:n1] = RMSNorm(X_l) Wqkv[n0:n1]^T
+template <typename WT, int NB>
+__device__ __forceinline__ void op_qkv(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
+  constexpr int RPW = rpw_for<NB>();
+  const int l = in.layer, n0 = in.a0, n = in.a1 - in.a0;
+  const WT* W = static_cast<const WT*>(a.wqkv) + (size_t)l * a.NQKV * a.H;
+  Gemv<WT, NB, RPW> g{W, W, n, n0, n, a.H};
+  if (!gemv<WT, NB, RPW>(a, s, g, a.X + l * a.sX, a.M, a.attn_norm + (size_t)l * a.H, true, mega, in, idx)) return;
+  float* out = a.QKV + l * a.sQKV;
+  for (int e = threadIdx.x; e < n * a.M; e += NT) {
+    const int row = e / a.M, b = e - row * a.M;
+    out[(size_t)b * a.NQKV + n0 + row] = s.res[row * NB + b];
+  }
+  if (mega) signal_tile(a, in);
+}
+
+// OPROJ(n0, n1): HRES_l[:, n] = X_l[:, n] + ATT_l Wo[n]^T
+template <typename WT, int NB>
+__device__ __forceinline__ void op_oproj(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
+  constexpr int RPW = rpw_for<NB>();
+  const int l = in.layer, n0 = in.a0, n = in.a1 - in.a0;
+  const WT* W = static_cast<const WT*>(a.wo) + (size_t)l * a.H * a.NA;
+  Gemv<WT, NB, RPW> g{W, W, n, n0, n, a.NA};
+  if (!gemv<WT, NB, RPW>(a, s, g, a.ATT + l * a.sATT, a.M, nullptr, false, mega, in, idx)) return;
+  const float* xr = a.X + l * a.sX;
+  float* out = a.HRES + l * a.sHRES;
+  for (int e = threadIdx.x; e < n * a.M; e += NT) {
+    const int row = e / a.M, b = e - row * a.M;
+    const size_t o = (size_t)b * a.H + n0 + row;
+    out[o] = xr[o] + s.res[row * NB + b];
+  }
+  if (mega) signal_tile(a, in);
+}
+
+// GATEUP(n0, n1): ACT_l[:, n] = silu(RMSNorm(H) Wg[n]^T) * (RMSNorm(H) Wu[n]^T)
+template <typename WT, int NB>
+__device__ __forceinline__ void op_gateup(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
+  constexpr int RPW = rpw_for<NB>();
+  const int l = in.layer, n0 = in.a0, n = in.a1 - in.a0;
+  const WT* Wg = static_cast<const WT*>(a.wgate) + (size_t)l * a.F * a.H;
+  const WT* Wu = static_cast<const WT*>(a.wup) + (size_t)l * a.F * a.H;
+  Gemv<WT, NB, RPW> g{Wg, Wu, n, n0, 2 * n, a.H};      // rows >= n read the up matrix
+  if (!gemv<WT, NB, RPW>(a, s, g, a.HRES + l * a.sHRES, a.M, a.ffn_norm + (size_t)l * a.H, true, mega, in, idx)) return;
+  float* out = a.ACT + l * a.sACT;
+  for (int e = threadIdx.x; e < n * a.M; e += NT) {
+    const int row = e / a.M, b = e - row * a.M;
+    const float gt = s.res[row * NB + b], up = s.res[(n + row) * NB + b];
+    out[(size_t)b * a.F + n0 + row] = gt / (1.0f + expf(-gt)) * up;
+  }
+  if (mega) signal_tile(a, in);
+}
+
+// DOWN(n0, n1): X_{l+1}[:, n] = HRES_l[:, n] + ACT_l Wd[n]^T
+template <typename WT, int NB>
+__device__ __forceinline__ void op_down(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
+  constexpr int RPW = rpw_for<NB>();
+  const int l = in.layer, n0 = in.a0, n = in.a1 - in.a0;
+  const WT* W = static_cast<const WT*>(a.wdown) + (size_t)l * a.H * a.F;
+  Gemv<WT, NB, RPW> g{W, W, n, n0, n, a.F};
+  if (!gemv<WT, NB, RPW>(a, s, g, a.ACT + l * a.sACT, a.M, nullptr, false, mega, in, idx)) return;
+  const float* hr = a.HRES + l * a.sHRES;
+  float* out = a.X + (l + 1) * a.sX;
+  for (int e = threadIdx.x; e < n * a.M; e += NT) {
+    const int row = e / a.M, b = e - row * a.M;
+    const size_t o = (size_t)b * a.H + n0 + row;
+    out[o] = hr[o] + s.res[row * NB + b];
+  }
+  if (mega) signal_tile(a, in);
+}
+
+// EMBED(n0, n1): X_0[b, n0:n1] = E[token_b, n0:n1]
+template <typename WT>
+__device__ __forceinline__ void op_embed(KArgs& a, const Instr in, bool mega) {
+  const int n0 = in.a0, n = in.a1 - in.a0;
+  const WT* E = static_cast<const WT*>(a.embed);
+  for (int e = threadIdx.x; e < n * a.M; e += NT) {
+    const int b = e / n, c = e - b * n;
+    const int tok = a.tokens[b];
+    if (tok < 0 || tok >= a.V) {                 // out-of-range id: report, emit zeros
+      if (c == 0) record_error(a, ERR_TOKEN, 0xFFFFFFFFu, (uint32_t)b, (uint32_t)tok, (uint32_t)a.V);
+      a.X[(size_t)b * a.H + n0 + c] = 0.f;
+      continue;
+    }
+    a.X[(size_t)b * a.H + n0 + c] = Elem<WT>::get(E, (size_t)tok * a.H + n0 + c);
+  }
+  if (mega) signal_tile(a, in);
+}
+
+// ----------------------------------------------------------------------------- attention
+
+__device__ __forceinline__ void block_reduce_heads(Smem& s, float v[ATT_MAX_R], int r, bool is_max) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int h = 0; h < ATT_MAX_R; ++h) {
+    if (h >= r) break;
+    const float w = is_max ? wave_max(v[h]) : wave_sum(v[h]);
+    if (lane == 0) s.att.red[wave * ATT_MAX_R + h] = w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < ATT_MAX_R; ++h) {
+    if (h >= r) break;
+    float t = s.att.red[h];
+    for (int w = 1; w < NWAVE; ++w) t = is_max ? fmaxf(t, s.att.red[w * ATT_MAX_R + h]) : t + s.att.red[w * ATT_MAX_R + h];
+    v[h] = t;
+  }
+  __syncthreads();
+}
+
+// ATTN(b, g, s): partial attention of the r query heads of KV group g of row b
+// over keys [s*kb, min((s+1)*kb, pos+1)), pos = ctx_lens[b].  Applies QK-norm
+// and RoPE to q and the new k, writes the new k / v into the cache (in the
+// split that holds pos), and stores (o, m, l) for the combine.
+template <typename KT, int HD>
+__device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
+  using E = Elem<KT>;
+  constexpr int KV4 = HD * (int)sizeof(KT) / 16;          // 16-byte words per cache row
+  constexpr int HALF = HD / 2;
+  constexpr int NOUT = ATT_MAX_R * HD / NT;               // outputs (h, d) per thread, upper bound
+  constexpr int NROT = ((ATT_MAX_R + 1) * HALF + NT - 1) / NT;
+  const int l = in.layer, b = in.a0, g = in.a1, sp = in.a2;
+  const int r = a.r;
+  const int t = threadIdx.x;
+  const int pos_in = a.ctx_lens[b];
+  // a position outside the cache is reported and the row treated as having no keys
+  const bool bad_pos = pos_in < 0 || pos_in >= a.ctx_max;
+  if (bad_pos && t == 0 && sp == 0) record_error(a, ERR_CONTEXT, idx, (uint32_t)b, (uint32_t)pos_in, (uint32_t)a.ctx_max);
+  const int pos = bad_pos ? -1 : pos_in;
+  const int j0 = sp * a.kb, j1 = min(j0 + a.kb, pos + 1);
+  const size_t head_off = (((size_t)l * a.M + b) * a.nkv + g) * (size_t)a.ctx_max;   // rows of this (l, b, g)
+  KT* Kc = static_cast<KT*>(a.kc) + head_off * HD;
+  KT* Vc = static_cast<KT*>(a.vc) + head_off * HD;
+
+  // prefetch this thread's cached key row of the first chunk
+  v4u kr[KV4];
+  {
+    const int j = j0 + t;
+    if (j < j1 && j < pos) {
+      const v4u* p = reinterpret_cast<const v4u*>(Kc + (size_t)j * HD);
+#pragma unroll
+      for (int k = 0; k < KV4; ++k) kr[k] = __builtin_nontemporal_load(p + k);
+    }
+  }
+  if (mega && !wait_tiles(a, in, idx)) return;
+
+  float* slot = a.OPART + l * a.sOP + ((size_t)(b * a.nkv + g) * a.NS + sp) * (size_t)(r * HD + 2 * r);
+  if (j0 >= j1) {                                         // empty split
+    for (int e = t; e < r * HD; e += NT) slot[e] = 0.f;
+    if (t < r) { slot[r * HD + t] = -INFINITY; slot[r * HD + r + t] = 0.f; }
+    if (mega) signal_tile(a, in);
+    return;
+  }
+
+  // q (r heads), k, v of this row and group, then QK-norm and RoPE
+  const float* qkv = a.QKV + l * a.sQKV + (size_t)b * a.NQKV;
+  for (int e = t; e < r * HD; e += NT) s.att.q[e] = qkv[g * r * HD + e];
+  if (t < HD) {
+    s.att.kn[t] = qkv[a.nq * HD + g * HD + t];
+    s.att.vn[t] = qkv[(a.nq + a.nkv) * HD + g * HD + t];
+  }
+  if (t < HALF) {
+    const double inv = pow(a.theta, -2.0 * (double)t / (double)HD);
+    const double ang = (double)pos * inv;
+    s.att.cs[t] = (float)cos(ang);
+    s.att.sn[t] = (float)sin(ang);
+  }
+  __syncthreads();
+  if (a.qk_norm) {
+    // per-head RMSNorm over HD: one wave per head (the r query heads, then k)
+    const int wave = t >> 6, lane = t & 63;
+    for (int h = wave; h <= r; h += NWAVE) {
+      float* v = h < r ? s.att.q + h * HD : s.att.kn;
+      const float* gn = (h < r ? a.q_norm : a.k_norm) + (size_t)l * HD;
+      float ss = 0.f;
+      for (int d = lane; d < HD; d += 64) ss += v[d] * v[d];
+      ss = wave_sum(ss);
+      const float sc = 1.0f / sqrtf(ss / (float)HD + a.eps);
+      for (int d = lane; d < HD; d += 64) v[d] = v[d] * sc * gn[d];
+    }
+    __syncthreads();
+  }
+  {
+    // rotate pairs (i, i + HD/2) of every query head and of the key
+    float y0[NROT], y1[NROT];
+#pragma unroll
+    for (int k = 0; k < NROT; ++k) {
+      const int e = t + k * NT;
+      if (e < (r + 1) * HALF) {
+        const int h = e / HALF, i = e - h * HALF;
+        const float* v = h < r ? s.att.q + h * HD : s.att.kn;
+        const float x0 = v[i], x1 = v[i + HALF];
+        y0[k] = x0 * s.att.cs[i] - x1 * s.att.sn[i];
+        y1[k] = x1 * s.att.cs[i] + x0 * s.att.sn[i];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NROT; ++k) {
+      const int e = t + k * NT;
+      if (e < (r + 1) * HALF) {
+        const int h = e / HALF, i = e - h * HALF;
+        float* v = h < r ? s.att.q + h * HD : s.att.kn;
+        v[i] = y0[k];
+        v[i + HALF] = y1[k];
+      }
+    }
+    __syncthreads();
+  }
+  // the new key / value are used as they will be read back from the cache
+  if (t < HD) {
+    const float kq = s.att.kn[t], vq = s.att.vn[t];
+    if (j0 <= pos && pos < j1) {
+      E::put(Kc, (size_t)pos * HD + t, kq);
+      E::put(Vc, (size_t)pos * HD + t, vq);
+    }
+    s.att.kn[t] = E::rounded(kq);
+    s.att.vn[t] = E::rounded(vq);
+  }
+  if (t < r) { s.att.m[t] = -INFINITY; s.att.l[t] = 0.f; }
+  __syncthreads();
+
+  const float scale = 1.0f / sqrtf((float)HD);
+  float o_acc[NOUT];
+#pragma unroll
+  for (int k = 0; k < NOUT; ++k) o_acc[k] = 0.f;
+
+  for (int c0 = j0; c0 < j1; c0 += ATT_CHUNK) {
+    const int j = c0 + t;
+    const bool valid = j < j1;
+    float sc[ATT_MAX_R], mx[ATT_MAX_R], sum[ATT_MAX_R], alpha[ATT_MAX_R];
+#pragma unroll
+    for (int h = 0; h < ATT_MAX_R; ++h) sc[h] = 0.f;
+    if (valid) {
+      if (j == pos) {
+        for (int d = 0; d < HD; ++d) {
+          const float kv = s.att.kn[d];
+#pragma unroll
+          for (int h = 0; h < ATT_MAX_R; ++h)
+            if (h < r) sc[h] = fmaf(s.att.q[h * HD + d], kv, sc[h]);
+        }
+      } else {
+        if (c0 != j0) {
+          const v4u* p = reinterpret_cast<const v4u*>(Kc + (size_t)j * HD);
+#pragma unroll
+          for (int k = 0; k < KV4; ++k) kr[k] = __builtin_nontemporal_load(p + k);
+        }
+#pragma unroll
+        for (int k = 0; k < KV4 / E::VEC; ++k) {
+          float kf[8];
+          E::unpack(&kr[k * E::VEC], kf);
+#pragma unroll
+          for (int h = 0; h < ATT_MAX_R; ++h) {
+            if (h < r) {
+              const float4 q0 = *reinterpret_cast<const float4*>(s.att.q + h * HD + 8 * k);
+              const float4 q1 = *reinterpret_cast<const float4*>(s.att.q + h * HD + 8 * k + 4);
+              float acc = sc[h];
+              acc = fmaf(q0.x, kf[0], acc); acc = fmaf(q0.y, kf[1], acc);
+              acc = fmaf(q0.z, kf[2], acc); acc = fmaf(q0.w, kf[3], acc);
+              acc = fmaf(q1.x, kf[4], acc); acc = fmaf(q1.y, kf[5], acc);
+              acc = fmaf(q1.z, kf[6], acc); acc = fmaf(q1.w, kf[7], acc);
+              sc[h] = acc;
+            }
+          }
+        }
+      }
+      // stage this key's value row
+      KT* vrow = reinterpret_cast<KT*>(s.att.vbuf) + (size_t)t * HD;
+      if (j == pos) {
+        for (int d = 0; d < HD; ++d) E::put(vrow, d, s.att.vn[d]);
+      } else {
+        const v4u* p = reinterpret_cast<const v4u*>(Vc + (size_t)j * HD);
+        v4u* dst = reinterpret_cast<v4u*>(vrow);
+#pragma unroll
+        for (int k = 0; k < KV4; ++k) dst[k] = __builtin_nontemporal_load(p + k);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < ATT_MAX_R; ++h) {
+      sc[h] = (valid && h < r) ? sc[h] * scale : -INFINITY;
+      mx[h] = sc[h];
+    }
+    block_reduce_heads(s, mx, r, true);
+#pragma unroll
+    for (int h = 0; h < ATT_MAX_R; ++h) {
+      if (h >= r) break;
+      const float mold = s.att.m[h];
+      const float mnew = fmaxf(mold, mx[h]);
+      const float pr = valid ? expf(sc[h] - mnew) : 0.f;
+      s.att.p[h * ATT_CHUNK + t] = pr;
+      sum[h] = pr;
+      alpha[h] = expf(mold - mnew);
+    }
+    block_reduce_heads(s, sum, r, false);      // its barriers also publish p and the value rows
+    // PV: output (h, d) accumulates p[h][j] V[j][d] over the chunk
+    const int nvalid = min(ATT_CHUNK, j1 - c0);
+#pragma unroll
+    for (int k = 0; k < NOUT; ++k) {
+      const int o = t + k * NT;
+      if (o < r * HD) {
+        const int h = o / HD, d = o - h * HD;
+        float acc = 0.f;
+        const float* ph = s.att.p + h * ATT_CHUNK;
+        const KT* vb = reinterpret_cast<const KT*>(s.att.vbuf);
+        for (int jj = 0; jj < nvalid; ++jj) acc = fmaf(ph[jj], E::get(vb, (size_t)jj * HD + d), acc);
+        float al = 0.f;
+#pragma unroll
+        for (int hh = 0; hh < ATT_MAX_R; ++hh) if (hh == h) al = alpha[hh];
+        o_acc[k] = o_acc[k] * al + acc;
+      }
+    }
+    __syncthreads();
+    if (t < r) {
+      float mxt = 0.f, st = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < ATT_MAX_R; ++hh) if (hh == t) { mxt = mx[hh]; st = sum[hh]; }
+      const float mold = s.att.m[t];
+      const float mnew = fmaxf(mold, mxt);
+      s.att.l[t] = s.att.l[t] * expf(mold - mnew) + st;
+      s.att.m[t] = mnew;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < NOUT; ++k) {
+    const int o = t + k * NT;
+    if (o < r * HD) slot[o] = o_acc[k];
+  }
+  if (t < r) { slot[r * HD + t] = s.att.m[t]; slot[r * HD + r + t] = s.att.l[t]; }
+  if (mega) signal_tile(a, in);
+}
+
+// COMBINE(b, g): merge the NS split partials of row b, group g into ATT_l.
+template <int HD>
+__device__ __forceinline__ void op_combine(KArgs& a, const Instr in, uint32_t idx, bool mega) {
+  const int l = in.layer, b = in.a0, g = in.a1, r = a.r;
+  if (mega && !wait_tiles(a, in, idx)) return;
+  const size_t slot_sz = (size_t)(r * HD + 2 * r);
+  const float* base = a.OPART + l * a.sOP + (size_t)(b * a.nkv + g) * a.NS * slot_sz;
+  float* out = a.ATT + l * a.sATT + (size_t)b * a.NA + (size_t)g * r * HD;
+  for (int o = threadIdx.x; o < r * HD; o += NT) {
+    const int h = o / HD;
+    float m = -INFINITY;
+    for (int sp = 0; sp < a.NS; ++sp) m = fmaxf(m, base[sp * slot_sz + r * HD + h]);
+    float num = 0.f, den = 0.f;
+    for (int sp = 0; sp < a.NS; ++sp) {
+      const float ms = base[sp * slot_sz + r * HD + h];
+      if (ms == -INFINITY) continue;
+      const float w = expf(ms - m);
+      num = fmaf(w, base[sp * slot_sz + o], num);
+      den = fmaf(w, base[sp * slot_sz + r * HD + r + h], den);
+    }
+    out[o] = num / den;
+  }
+  if (mega) signal_tile(a, in);
+}
+
+// ----------------------------------------------------------------------------- dispatch
+
+template <typename WT, int NB>
+__device__ __forceinline__ void run_instr(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega, int only_op) {
+  const int op = only_op ? only_op : in.op;
+  switch (op) {
+    case mk::OP_EMBED: op_embed<WT>(a, in, mega); break;
+    case mk::OP_QKV: op_qkv<WT, NB>(a, s, in, idx, mega); break;
+    case mk::OP_ATTN:
+      if (a.hd == 64) op_attn<WT, 64>(a, s, in, idx, mega); else op_attn<WT, 128>(a, s, in, idx, mega);
+      break;
+    case mk::OP_COMBINE:
+      if (a.hd == 64) op_combine<64>(a, in, idx, mega); else op_combine<128>(a, in, idx, mega);
+      break;
+    case mk::OP_OPROJ: op_oproj<WT, NB>(a, s, in, idx, mega); break;
+    case mk::OP_GATEUP: op_gateup<WT, NB>(a, s, in, idx, mega); break;
+    case mk::OP_DOWN: op_down<WT, NB>(a, s, in, idx, mega); break;
+    default:
+      if (threadIdx.x == 0) record_error(a, ERR_OPCODE, idx, in.op, 0, 0);
+      break;
+  }
+}
+
+// The persistent interpreter: pop, decode, run (wait -> compute -> signal).
+template <typename WT, int NB>
+__global__ __launch_bounds__(NT) void mk_interp(Args args) {
+  __shared__ Smem s;
+  const uint32_t qi = blockIdx.x % args.n_queues;
+  for (;;) {
+    KArgs& a = kernel_args();
+    if (threadIdx.x == 0) {
+      uint32_t k = __hip_atomic_fetch_add(a.heads + qi * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t i = (uint64_t)k * a.n_queues + qi;
+      s.idx = (i < a.n_instr && !aborted(a)) ? (uint32_t)i : 0xFFFFFFFFu;
+    }
+    __syncthreads();
+    const uint32_t idx = __builtin_amdgcn_readfirstlane(s.idx);   // uniform: keep the record in SGPRs
+    __syncthreads();
+    if (idx == 0xFFFFFFFFu) break;
+    run_instr<WT, NB>(a, s, load_instr(a, idx), idx, true, 0);
+  }
+}
+
+// One launch per (layer, op): workgroup i runs instruction first + i, no waits.
+template <typename WT, int NB, int OP>
+__global__ __launch_bounds__(NT) void kpo_kernel(Args args, uint32_t first) {
+  __shared__ Smem s;
+  KArgs& a = kernel_args();
+  const uint32_t idx = first + blockIdx.x;
+  const Instr in = load_instr(a, idx);
+  if (in.op != OP) {
+    if (threadIdx.x == 0) record_error(a, ERR_OPCODE, idx, in.op, 0, 0);
+    return;
+  }
+  run_instr<WT, NB>(a, s, in, idx, false, OP);
+}
+
+// LM head: logits[b][v] = RMSNorm(X_L)[b] . W_lm[v] for 16 vocabulary rows per
+// workgroup, plus the block's (max, lowest index) per row for the argmax.
+template <typename WT, int NB>
+__global__ __launch_bounds__(NT) void lm_head_kernel(Args args) {
+  __shared__ Smem s;
+  KArgs& a = kernel_args();
+  constexpr int RPW = rpw_for<NB>();
+  constexpr int ROWS = 16;
+  const int v0 = blockIdx.x * ROWS;
+  const int n = min(ROWS, a.V - v0);
+  const WT* W = static_cast<const WT*>(a.lm_head);
+  Gemv<WT, NB, RPW> g{W, W, n, v0, n, a.H};
+  Instr none{};
+  gemv<WT, NB, RPW>(a, s, g, a.X + a.L * a.sX, a.M, a.final_norm, true, false, none, 0);
+  for (int e = threadIdx.x; e < n * a.M; e += NT) {
+    const int row = e / a.M, b = e - row * a.M;
+    if (a.logits) a.logits[(size_t)b * a.V + v0 + row] = s.res[row * NB + b];
+  }
+  if (threadIdx.x < a.M) {
+    const int b = threadIdx.x;
+    float best = s.res[b];
+    int bi = 0;
+    for (int row = 1; row < n; ++row) {
+      const float v = s.res[row * NB + b];
+      if (v > best) { best = v; bi = row; }
+    }
+    a.lm_val[(size_t)b * a.lm_blocks + blockIdx.x] = best;
+    a.lm_idx[(size_t)b * a.lm_blocks + blockIdx.x] = v0 + bi;
+  }
+}
+
+template <typename WT, int NB>
+struct Launch {
+  static hipError_t mega(const Args& a, int grid, hipStream_t st) {
+    hipLaunchKernelGGL((mk_interp<WT, NB>), dim3(grid), dim3(NT), 0, st, a);
+    return hipGetLastError();
+  }
+  static hipError_t kpo(const Args& a, uint32_t op, uint32_t first, uint32_t count, hipStream_t st) {
+    switch (op) {
+#define KPO_CASE(OPC) case OPC: hipLaunchKernelGGL((kpo_kernel<WT, NB, OPC>), dim3(count), dim3(NT), 0, st, a, first); break;
+      KPO_CASE(mk::OP_EMBED) KPO_CASE(mk::OP_QKV) KPO_CASE(mk::OP_ATTN) KPO_CASE(mk::OP_COMBINE)
+      KPO_CASE(mk::OP_OPROJ) KPO_CASE(mk::OP_GATEUP) KPO_CASE(mk::OP_DOWN)
+#undef KPO_CASE
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  static hipError_t lm(const Args& a, hipStream_t st) {
+    hipLaunchKernelGGL((lm_head_kernel<WT, NB>), dim3(a.lm_blocks), dim3(NT), 0, st, a);
+    return hipGetLastError();
+  }
+};
+
+struct Table {
+  hipError_t (*mega)(const Args&, int, hipStream_t);
+  hipError_t (*kpo)(const Args&, uint32_t, uint32_t, uint32_t, hipStream_t);
+  hipError_t (*lm)(const Args&, hipStream_t);
+};
+
+
+}  // namespace mkd
