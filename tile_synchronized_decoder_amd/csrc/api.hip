@@ -181,6 +181,7 @@ mk_status check_shapes(const mk_config& c) {
   if (c.head_dim != 64 && c.head_dim != 128) FAIL(MK_ENOTSUP, "head_dim must be 64 or 128");
   if (c.dtype == MK_F32 && c.head_dim != 64) FAIL(MK_ENOTSUP, "fp32 caches support head_dim 64 only");
   if (c.n_q_heads / c.n_kv_heads > ATT_MAX_R) FAIL(MK_ENOTSUP, "at most %d query heads per KV head", ATT_MAX_R);
+  if (NT % ((c.n_q_heads / c.n_kv_heads) * c.head_dim / 8)) FAIL(MK_ENOTSUP, "query heads per KV head must be a power of two");
   if (c.dtype != MK_F32 && c.dtype != MK_BF16) FAIL(MK_EINVAL, "unknown dtype");
   return MK_OK;
 }

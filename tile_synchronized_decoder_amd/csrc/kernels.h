@@ -160,21 +160,38 @@ __device__ inline void record_error(KArgs& a, uint32_t code, uint32_t idx, uint3
   }
 }
 
+// Tile hand-off.  Intermediate tiles are written and read with device-coherent
+// (agent-scope relaxed atomic) stores and loads, which bypass the per-XCD L2
+// copies instead of relying on whole-cache write-back / invalidate; weights and
+// the KV cache history are read-only during a step and use ordinary streaming
+// loads.  A producer waits until its coherent stores are acknowledged, then one
+// thread bumps the tile's counter; a consumer polls the counters of the tiles
+// it reads and only then issues its coherent loads.
+__device__ __forceinline__ void st_cg(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_cg(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4 ld_cg4(const float* p) {          // 16-byte aligned
+  uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<float*>(p));
+  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float4(__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
+                     __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
+}
+
 // Block until every barrier in the instruction's wait list reaches its target.
-// Threads poll disjoint subsets; each poller then acquires at agent scope and
-// the workgroup barrier orders everyone's later reads after those acquires.
-// Returns false if the wait gave up (timeout or another worker aborted).
+// Threads poll disjoint subsets.  Returns false if the wait gave up (timeout or
+// another worker aborted).
 __device__ __forceinline__ bool wait_tiles(KArgs& a, const Instr in, uint32_t idx) {
   bool ok = true;
-  bool polled = false;
-  uint32_t base = 0;
   for (uint32_t k = 0; k < in.wait_cnt; ++k) {
     const Range rg = a.ranges[in.wait_off + k];
     for (uint32_t j = threadIdx.x; j < rg.count && ok; j += NT) {
       const uint32_t id = rg.first + j;
       const uint32_t tgt = a.targets[id];
       uint32_t spins = 0;
-      polled = true;
       uint32_t v;
       while ((v = __hip_atomic_load(a.counters + id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < tgt) {
         __builtin_amdgcn_s_sleep(1);
@@ -182,19 +199,18 @@ __device__ __forceinline__ bool wait_tiles(KArgs& a, const Instr in, uint32_t id
         if ((spins & 255) == 0 && aborted(a)) { ok = false; break; }
       }
     }
-    base += rg.count;
   }
-  (void)base;
-  if (polled) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return __syncthreads_and(ok) != 0;
+  const bool all = __syncthreads_and(ok) != 0;
+  asm volatile("" ::: "memory");                 // no tile load may move above the wait
+  return all;
 }
 
-// Publish this instruction's tile: every wave makes its stores visible at
-// agent scope, then one thread bumps the tile's counter.
+// Publish this instruction's tile: every wave waits for its coherent stores to
+// be acknowledged, then one thread bumps the tile's counter.
 __device__ __forceinline__ void signal_tile(KArgs& a, const Instr in) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(a.counters + in.signal, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(a.counters + in.signal, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ----------------------------------------------------------------------------- shared memory arena
@@ -209,6 +225,8 @@ struct Smem {
       float p[ATT_MAX_R * ATT_CHUNK];                              // scores -> probabilities
       float red[NWAVE * ATT_MAX_R];
       float m[ATT_MAX_R], l[ATT_MAX_R], alpha[ATT_MAX_R];
+      float o[ATT_MAX_R * 128];                                    // running output of the split
+      float part[NT * 8];                                          // PV partial sums per key slice
       uint16_t vbuf[ATT_CHUNK * 128];                              // value rows of the chunk (raw, <= 256 B each)
     } att;
   };
@@ -225,7 +243,8 @@ struct Smem {
 template <typename WT, int NB, int RPW>
 struct Gemv {
   static constexpr int ROWS = NWAVE * RPW;
-  static constexpr int WIN = 2;          // 512-column iterations per register window
+  // 512-column iterations per register window; two windows are in flight
+  static constexpr int WIN = (Elem<WT>::VEC == 1 && NB <= 8) ? 4 : 2;
   using E = Elem<WT>;
 
   struct Win { v4u w[WIN][RPW][E::VEC]; };
@@ -289,7 +308,7 @@ __device__ __forceinline__ void stage_x(Smem& s, const float* x, int ldx, int nb
   for (int b = 0; b < NB; ++b) {
     if (b >= nb) break;
     for (int k = threadIdx.x * 4; k < kn; k += NT * 4) {
-      float4 v = *reinterpret_cast<const float4*>(x + (size_t)b * ldx + k0 + k);
+      float4 v = ld_cg4(x + (size_t)b * ldx + k0 + k);
       if (want_ss) ss[b] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
       if (gain) {
         const float4 g = *reinterpret_cast<const float4*>(gain + k0 + k);
@@ -400,7 +419,7 @@ __device__ __forceinline__ void op_qkv(KArgs& a, Smem& s, const Instr in, uint32
   float* out = a.QKV + l * a.sQKV;
   for (int e = threadIdx.x; e < n * a.M; e += NT) {
     const int row = e / a.M, b = e - row * a.M;
-    out[(size_t)b * a.NQKV + n0 + row] = s.res[row * NB + b];
+    st_cg(out + (size_t)b * a.NQKV + n0 + row, s.res[row * NB + b]);
   }
   if (mega) signal_tile(a, in);
 }
@@ -418,7 +437,7 @@ __device__ __forceinline__ void op_oproj(KArgs& a, Smem& s, const Instr in, uint
   for (int e = threadIdx.x; e < n * a.M; e += NT) {
     const int row = e / a.M, b = e - row * a.M;
     const size_t o = (size_t)b * a.H + n0 + row;
-    out[o] = xr[o] + s.res[row * NB + b];
+    st_cg(out + o, ld_cg(xr + o) + s.res[row * NB + b]);
   }
   if (mega) signal_tile(a, in);
 }
@@ -436,7 +455,7 @@ __device__ __forceinline__ void op_gateup(KArgs& a, Smem& s, const Instr in, uin
   for (int e = threadIdx.x; e < n * a.M; e += NT) {
     const int row = e / a.M, b = e - row * a.M;
     const float gt = s.res[row * NB + b], up = s.res[(n + row) * NB + b];
-    out[(size_t)b * a.F + n0 + row] = gt / (1.0f + expf(-gt)) * up;
+    st_cg(out + (size_t)b * a.F + n0 + row, gt / (1.0f + expf(-gt)) * up);
   }
   if (mega) signal_tile(a, in);
 }
@@ -454,7 +473,7 @@ __device__ __forceinline__ void op_down(KArgs& a, Smem& s, const Instr in, uint3
   for (int e = threadIdx.x; e < n * a.M; e += NT) {
     const int row = e / a.M, b = e - row * a.M;
     const size_t o = (size_t)b * a.H + n0 + row;
-    out[o] = hr[o] + s.res[row * NB + b];
+    st_cg(out + o, ld_cg(hr + o) + s.res[row * NB + b]);
   }
   if (mega) signal_tile(a, in);
 }
@@ -469,10 +488,10 @@ __device__ __forceinline__ void op_embed(KArgs& a, const Instr in, bool mega) {
     const int tok = a.tokens[b];
     if (tok < 0 || tok >= a.V) {                 // out-of-range id: report, emit zeros
       if (c == 0) record_error(a, ERR_TOKEN, 0xFFFFFFFFu, (uint32_t)b, (uint32_t)tok, (uint32_t)a.V);
-      a.X[(size_t)b * a.H + n0 + c] = 0.f;
+      st_cg(a.X + (size_t)b * a.H + n0 + c, 0.f);
       continue;
     }
-    a.X[(size_t)b * a.H + n0 + c] = Elem<WT>::get(E, (size_t)tok * a.H + n0 + c);
+    st_cg(a.X + (size_t)b * a.H + n0 + c, Elem<WT>::get(E, (size_t)tok * a.H + n0 + c));
   }
   if (mega) signal_tile(a, in);
 }
@@ -507,7 +526,6 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
   using E = Elem<KT>;
   constexpr int KV4 = HD * (int)sizeof(KT) / 16;          // 16-byte words per cache row
   constexpr int HALF = HD / 2;
-  constexpr int NOUT = ATT_MAX_R * HD / NT;               // outputs (h, d) per thread, upper bound
   constexpr int NROT = ((ATT_MAX_R + 1) * HALF + NT - 1) / NT;
   const int l = in.layer, b = in.a0, g = in.a1, sp = in.a2;
   const int r = a.r;
@@ -522,32 +540,35 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
   KT* Kc = static_cast<KT*>(a.kc) + head_off * HD;
   KT* Vc = static_cast<KT*>(a.vc) + head_off * HD;
 
-  // prefetch this thread's cached key row of the first chunk
-  v4u kr[KV4];
+  // prefetch this thread's cached key and value rows of the first chunk
+  v4u kr[KV4], vr[KV4];
   {
     const int j = j0 + t;
     if (j < j1 && j < pos) {
-      const v4u* p = reinterpret_cast<const v4u*>(Kc + (size_t)j * HD);
+      const v4u* pk = reinterpret_cast<const v4u*>(Kc + (size_t)j * HD);
+      const v4u* pv = reinterpret_cast<const v4u*>(Vc + (size_t)j * HD);
 #pragma unroll
-      for (int k = 0; k < KV4; ++k) kr[k] = __builtin_nontemporal_load(p + k);
+      for (int k = 0; k < KV4; ++k) kr[k] = __builtin_nontemporal_load(pk + k);
+#pragma unroll
+      for (int k = 0; k < KV4; ++k) vr[k] = __builtin_nontemporal_load(pv + k);
     }
   }
   if (mega && !wait_tiles(a, in, idx)) return;
 
   float* slot = a.OPART + l * a.sOP + ((size_t)(b * a.nkv + g) * a.NS + sp) * (size_t)(r * HD + 2 * r);
   if (j0 >= j1) {                                         // empty split
-    for (int e = t; e < r * HD; e += NT) slot[e] = 0.f;
-    if (t < r) { slot[r * HD + t] = -INFINITY; slot[r * HD + r + t] = 0.f; }
+    for (int e = t; e < r * HD; e += NT) st_cg(slot + e, 0.f);
+    if (t < r) { st_cg(slot + r * HD + t, -INFINITY); st_cg(slot + r * HD + r + t, 0.f); }
     if (mega) signal_tile(a, in);
     return;
   }
 
   // q (r heads), k, v of this row and group, then QK-norm and RoPE
   const float* qkv = a.QKV + l * a.sQKV + (size_t)b * a.NQKV;
-  for (int e = t; e < r * HD; e += NT) s.att.q[e] = qkv[g * r * HD + e];
+  for (int e = t; e < r * HD; e += NT) s.att.q[e] = ld_cg(qkv + g * r * HD + e);
   if (t < HD) {
-    s.att.kn[t] = qkv[a.nq * HD + g * HD + t];
-    s.att.vn[t] = qkv[(a.nq + a.nkv) * HD + g * HD + t];
+    s.att.kn[t] = ld_cg(qkv + a.nq * HD + g * HD + t);
+    s.att.vn[t] = ld_cg(qkv + (a.nq + a.nkv) * HD + g * HD + t);
   }
   if (t < HALF) {
     const double inv = pow(a.theta, -2.0 * (double)t / (double)HD);
@@ -555,6 +576,7 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
     s.att.cs[t] = (float)cos(ang);
     s.att.sn[t] = (float)sin(ang);
   }
+  for (int e = t; e < r * HD; e += NT) s.att.o[e] = 0.f;
   __syncthreads();
   if (a.qk_norm) {
     // per-head RMSNorm over HD: one wave per head (the r query heads, then k)
@@ -610,18 +632,23 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
   if (t < r) { s.att.m[t] = -INFINITY; s.att.l[t] = 0.f; }
   __syncthreads();
 
+  // PV work split: thread t sums a group of 8 output dims of one head over a
+  // strided slice of the chunk's keys
+  constexpr int G8 = HD / 8;                              // 8-dim groups per head
+  const int ngroups = r * G8;
+  const int nslice = NT / ngroups;                        // r * HD / 8 divides NT (checked on the host)
+  const int grp = t % ngroups, slc = t / ngroups;
+  const int gh = grp / G8, gd = (grp % G8) * 8;
   const float scale = 1.0f / sqrtf((float)HD);
-  float o_acc[NOUT];
-#pragma unroll
-  for (int k = 0; k < NOUT; ++k) o_acc[k] = 0.f;
 
   for (int c0 = j0; c0 < j1; c0 += ATT_CHUNK) {
     const int j = c0 + t;
     const bool valid = j < j1;
-    float sc[ATT_MAX_R], mx[ATT_MAX_R], sum[ATT_MAX_R], alpha[ATT_MAX_R];
+    float sc[ATT_MAX_R], mx[ATT_MAX_R], sum[ATT_MAX_R];
 #pragma unroll
     for (int h = 0; h < ATT_MAX_R; ++h) sc[h] = 0.f;
     if (valid) {
+      KT* vrow = reinterpret_cast<KT*>(s.att.vbuf) + (size_t)t * HD;
       if (j == pos) {
         for (int d = 0; d < HD; ++d) {
           const float kv = s.att.kn[d];
@@ -629,11 +656,15 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
           for (int h = 0; h < ATT_MAX_R; ++h)
             if (h < r) sc[h] = fmaf(s.att.q[h * HD + d], kv, sc[h]);
         }
+        for (int d = 0; d < HD; ++d) E::put(vrow, d, s.att.vn[d]);
       } else {
         if (c0 != j0) {
-          const v4u* p = reinterpret_cast<const v4u*>(Kc + (size_t)j * HD);
+          const v4u* pk = reinterpret_cast<const v4u*>(Kc + (size_t)j * HD);
+          const v4u* pv = reinterpret_cast<const v4u*>(Vc + (size_t)j * HD);
 #pragma unroll
-          for (int k = 0; k < KV4; ++k) kr[k] = __builtin_nontemporal_load(p + k);
+          for (int k = 0; k < KV4; ++k) kr[k] = __builtin_nontemporal_load(pk + k);
+#pragma unroll
+          for (int k = 0; k < KV4; ++k) vr[k] = __builtin_nontemporal_load(pv + k);
         }
 #pragma unroll
         for (int k = 0; k < KV4 / E::VEC; ++k) {
@@ -653,16 +684,9 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
             }
           }
         }
-      }
-      // stage this key's value row
-      KT* vrow = reinterpret_cast<KT*>(s.att.vbuf) + (size_t)t * HD;
-      if (j == pos) {
-        for (int d = 0; d < HD; ++d) E::put(vrow, d, s.att.vn[d]);
-      } else {
-        const v4u* p = reinterpret_cast<const v4u*>(Vc + (size_t)j * HD);
         v4u* dst = reinterpret_cast<v4u*>(vrow);
 #pragma unroll
-        for (int k = 0; k < KV4; ++k) dst[k] = __builtin_nontemporal_load(p + k);
+        for (int k = 0; k < KV4; ++k) dst[k] = vr[k];
       }
     }
 #pragma unroll
@@ -674,30 +698,38 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
 #pragma unroll
     for (int h = 0; h < ATT_MAX_R; ++h) {
       if (h >= r) break;
-      const float mold = s.att.m[h];
-      const float mnew = fmaxf(mold, mx[h]);
+      const float mnew = fmaxf(s.att.m[h], mx[h]);
       const float pr = valid ? expf(sc[h] - mnew) : 0.f;
       s.att.p[h * ATT_CHUNK + t] = pr;
       sum[h] = pr;
-      alpha[h] = expf(mold - mnew);
     }
     block_reduce_heads(s, sum, r, false);      // its barriers also publish p and the value rows
-    // PV: output (h, d) accumulates p[h][j] V[j][d] over the chunk
+    // PV partials: 8 dims of head gh over keys slc, slc + nslice, ...
     const int nvalid = min(ATT_CHUNK, j1 - c0);
+    float acc[8];
 #pragma unroll
-    for (int k = 0; k < NOUT; ++k) {
-      const int o = t + k * NT;
-      if (o < r * HD) {
-        const int h = o / HD, d = o - h * HD;
-        float acc = 0.f;
-        const float* ph = s.att.p + h * ATT_CHUNK;
-        const KT* vb = reinterpret_cast<const KT*>(s.att.vbuf);
-        for (int jj = 0; jj < nvalid; ++jj) acc = fmaf(ph[jj], E::get(vb, (size_t)jj * HD + d), acc);
-        float al = 0.f;
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    const float* ph = s.att.p + gh * ATT_CHUNK;
+    for (int jj = slc; jj < nvalid; jj += nslice) {
+      const float pj = ph[jj];
+      const KT* vrow = reinterpret_cast<const KT*>(s.att.vbuf) + (size_t)jj * HD + gd;
+      float vf[8];
+      E::unpack(reinterpret_cast<const v4u*>(vrow), vf);
 #pragma unroll
-        for (int hh = 0; hh < ATT_MAX_R; ++hh) if (hh == h) al = alpha[hh];
-        o_acc[k] = o_acc[k] * al + acc;
-      }
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(pj, vf[e], acc[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s.att.part[slc * (r * HD) + grp * 8 + e] = acc[e];
+    __syncthreads();
+    for (int o = t; o < r * HD; o += NT) {
+      const int h = o / HD;
+      float tot = 0.f;
+      for (int k = 0; k < nslice; ++k) tot += s.att.part[k * (r * HD) + o];
+      float mxh = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < ATT_MAX_R; ++hh) if (hh == h) mxh = mx[hh];
+      const float mold = s.att.m[h];
+      s.att.o[o] = s.att.o[o] * expf(mold - fmaxf(mold, mxh)) + tot;
     }
     __syncthreads();
     if (t < r) {
@@ -711,12 +743,8 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
     }
     __syncthreads();
   }
-#pragma unroll
-  for (int k = 0; k < NOUT; ++k) {
-    const int o = t + k * NT;
-    if (o < r * HD) slot[o] = o_acc[k];
-  }
-  if (t < r) { slot[r * HD + t] = s.att.m[t]; slot[r * HD + r + t] = s.att.l[t]; }
+  for (int o = t; o < r * HD; o += NT) st_cg(slot + o, s.att.o[o]);
+  if (t < r) { st_cg(slot + r * HD + t, s.att.m[t]); st_cg(slot + r * HD + r + t, s.att.l[t]); }
   if (mega) signal_tile(a, in);
 }
 
@@ -731,16 +759,16 @@ __device__ __forceinline__ void op_combine(KArgs& a, const Instr in, uint32_t id
   for (int o = threadIdx.x; o < r * HD; o += NT) {
     const int h = o / HD;
     float m = -INFINITY;
-    for (int sp = 0; sp < a.NS; ++sp) m = fmaxf(m, base[sp * slot_sz + r * HD + h]);
+    for (int sp = 0; sp < a.NS; ++sp) m = fmaxf(m, ld_cg(base + sp * slot_sz + r * HD + h));
     float num = 0.f, den = 0.f;
     for (int sp = 0; sp < a.NS; ++sp) {
-      const float ms = base[sp * slot_sz + r * HD + h];
+      const float ms = ld_cg(base + sp * slot_sz + r * HD + h);
       if (ms == -INFINITY) continue;
       const float w = expf(ms - m);
-      num = fmaf(w, base[sp * slot_sz + o], num);
-      den = fmaf(w, base[sp * slot_sz + r * HD + r + h], den);
+      num = fmaf(w, ld_cg(base + sp * slot_sz + o), num);
+      den = fmaf(w, ld_cg(base + sp * slot_sz + r * HD + r + h), den);
     }
-    out[o] = num / den;
+    st_cg(out + o, num / den);
   }
   if (mega) signal_tile(a, in);
 }
@@ -769,16 +797,26 @@ __device__ __forceinline__ void run_instr(KArgs& a, Smem& s, const Instr in, uin
 }
 
 // The persistent interpreter: pop, decode, run (wait -> compute -> signal).
+// The pop of the next instruction is issued before the current one runs, so
+// its round trip overlaps the current instruction's loads.  Sub-queue q holds
+// instructions q, q + n_queues, ... in queue order; every sub-queue is a
+// subsequence of one topological order, so popping ahead cannot deadlock.
 template <typename WT, int NB>
 __global__ __launch_bounds__(NT) void mk_interp(Args args) {
   __shared__ Smem s;
   const uint32_t qi = blockIdx.x % args.n_queues;
+  uint32_t k_next = 0;
+  if (threadIdx.x == 0) {
+    KArgs& a = kernel_args();
+    k_next = __hip_atomic_fetch_add(a.heads + qi * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   for (;;) {
     KArgs& a = kernel_args();
     if (threadIdx.x == 0) {
-      uint32_t k = __hip_atomic_fetch_add(a.heads + qi * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint64_t i = (uint64_t)k * a.n_queues + qi;
-      s.idx = (i < a.n_instr && !aborted(a)) ? (uint32_t)i : 0xFFFFFFFFu;
+      const uint64_t i = (uint64_t)k_next * a.n_queues + qi;
+      const bool go = i < a.n_instr && !aborted(a);
+      s.idx = go ? (uint32_t)i : 0xFFFFFFFFu;
+      if (go) k_next = __hip_atomic_fetch_add(a.heads + qi * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     const uint32_t idx = __builtin_amdgcn_readfirstlane(s.idx);   // uniform: keep the record in SGPRs
