@@ -92,6 +92,7 @@ def main():
     ap.add_argument("--workload", default="llama1b_b1")
     ap.add_argument("--workers-per-cu", type=int, default=1)
     ap.add_argument("--queues", type=int, default=0, help="sub-queues (0: the workload's plan)")
+    ap.add_argument("--tiles", default="", help="override tile widths, e.g. tq=16,to=8,tf=16,td=8,kb=256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--modes", default="mega,kpo,kpo_graph")
@@ -109,6 +110,9 @@ def main():
     wl = W.WORKLOADS[args.workload]
     if args.queues:
         wl = dataclasses.replace(wl, plan=dataclasses.replace(wl.plan, n_queues=args.queues))
+    if args.tiles:
+        kv = {k: int(v) for k, v in (p.split("=") for p in args.tiles.split(","))}
+        wl = dataclasses.replace(wl, plan=dataclasses.replace(wl.plan, **kv))
     m, r = wl.model, wl.run
     K_steps = min(args.steps, r.steps)
     torch.cuda.set_device(0)
@@ -220,7 +224,8 @@ def main():
         "config": {"workload": f"{wl.name}: {wl.describe}", "batch": B, "context": f"{r.ctx0[0]}+",
                    "layers": m.n_layers, "hidden": m.hidden, "vocab": m.vocab,
                    "instructions_per_step": q.nbytes(T.MK_PART_INSTR) // 32,
-                   "workers_per_cu": args.workers_per_cu, "n_queues": wl.plan.n_queues},
+                   "workers_per_cu": args.workers_per_cu, "n_queues": wl.plan.n_queues,
+                   "tiles": {k: getattr(wl.plan, k) for k in ("tq", "to", "tf", "td", "kb")}},
         "step_hbm_gbs": round(step_bytes / (mega["ms_per_step"] * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(step_bytes / (mega["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "modes": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}

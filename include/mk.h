@@ -193,7 +193,13 @@ mk_status mk_device_error(const mk_queue* q, const void* d_workspace, mk_dev_err
 enum {
   MK_OPT_WORKERS_PER_CU = 0,  /* megakernel workgroups per compute unit (default 1) */
   MK_OPT_SPIN_LIMIT = 1,      /* polls before a barrier wait gives up (default 1<<22) */
-  MK_OPT_NUM_CUS = 2          /* read-only: compute units of the current device */
+  MK_OPT_NUM_CUS = 2,         /* read-only: compute units of the current device */
+  /* Trace mode: a device buffer (value = its address) of at least 32 bytes per
+   * instruction.  While set, each megakernel instruction i writes 4 x u64 at
+   * offset 32*i: (workgroup << 32 | XCD id), pop time, time its waits ended,
+   * end time (device wall clock, 100 MHz).  Set the address to 0 to stop. */
+  MK_OPT_TRACE_BUFFER = 3,
+  MK_OPT_TRACE_BYTES = 4
 };
 mk_status mk_set_option(int32_t key, int64_t value);
 int64_t mk_get_option(int32_t key);

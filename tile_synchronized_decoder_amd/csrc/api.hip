@@ -70,6 +70,8 @@ __global__ __launch_bounds__(NT) void argmax_kernel(Args args) {
 struct Options {
   int workers_per_cu = 1;
   uint32_t spin_limit = 1u << 22;
+  unsigned long long* trace = nullptr;   // device buffer, 32 bytes per instruction
+  size_t trace_bytes = 0;
 };
 Options g_opt;
 
@@ -106,7 +108,7 @@ Layout layout(const mk_queue* q) {
   o.sATT = up256(M * c.n_q_heads * hd * 4) / 4;
   o.sHRES = up256(M * c.hidden * 4) / 4;
   o.sACT = up256(M * c.ffn * 4) / 4;
-  o.lm_blocks = c.has_lm_head ? (c.vocab + 15) / 16 : 1;
+  o.lm_blocks = c.has_lm_head ? (c.vocab + LM_ROWS - 1) / LM_ROWS : 1;
   size_t off = 0;
   o.X = off; off += (L + 1) * o.sX * 4;
   o.QKV = off; off += L * o.sQKV * 4;
@@ -133,6 +135,42 @@ Table pick_table(int dtype, int nb) {
   return bf ? table_bf16_32() : table_f32_32();
 }
 
+constexpr uint32_t kMaxLds = 160 * 1024;
+
+int nb_bucket(int rows) {
+  return rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : rows <= 8 ? 8 : rows <= 16 ? 16 : 32;
+}
+
+struct LdsLayout { uint32_t res, x, uni, bytes; };
+
+// Dynamic shared memory of one workgroup, in floats: header (index, norm
+// factors), GEMV results, then one region shared by the GEMV input staging and
+// the attention buffers.  Mirrors make_smem() in kernels.h.
+LdsLayout lds_layout(const mk_queue* q) {
+  const mk_config& c = q->cfg;
+  const mk_plan& p = q->plan;
+  const uint32_t nb = nb_bucket(p.rows);
+  auto r4 = [](uint32_t n) { return (n + 3) & ~3u; };
+  const uint32_t max_rows = std::max({p.tq, p.to, 2 * p.tf, p.td, LM_ROWS});
+  LdsLayout o{};
+  o.res = r4(max_rows * nb);
+  const uint32_t kmax = std::max({c.hidden, c.ffn, c.n_q_heads * c.head_dim});
+  o.x = std::max<uint32_t>(std::min<uint32_t>(XBUF_MAX, nb * kmax), nb * 512);
+  // keep the whole layout within one workgroup's shared memory: shrink the
+  // input staging (it is consumed in chunks of nb * 512 floats)
+  const uint32_t fixed = 4 * (4 + 32 + NWAVE * 32 + o.res) + NWAVE * RING_LINES * 1024;
+  const uint32_t room = fixed < kMaxLds ? (kMaxLds - fixed) / 4 : 0;
+  if (o.x > room) o.x = std::max<uint32_t>(room / (nb * 512) * (nb * 512), nb * 512);
+  o.x = r4(o.x);
+  const uint32_t r = c.n_q_heads / c.n_kv_heads, hd = c.head_dim;
+  const uint32_t esz = c.dtype == MK_BF16 ? 2 : 4;
+  const uint32_t att = r4(r * hd) + 2 * r4(hd) + 2 * r4(hd / 2) + r4(r * ATT_CHUNK) + r4(NWAVE * ATT_MAX_R) +
+                       3 * r4(ATT_MAX_R) + r4(r * hd) + r4(NT * 8) + (ATT_CHUNK * hd * esz + 3) / 4;
+  o.uni = std::max(NWAVE * RING_LINES * 256 + o.x, att);
+  o.bytes = 4 * (4 + 32 + NWAVE * 32 + o.res + o.uni);
+  return o;
+}
+
 // Everything the kernels need except the per-call inputs and outputs.
 void fill_args(const mk_queue* q, const void* d_queue, const mk_weights* w, const mk_kv* kv, void* d_workspace,
                const Layout& o, Args& a) {
@@ -144,6 +182,8 @@ void fill_args(const mk_queue* q, const void* d_queue, const mk_weights* w, cons
   a.NQKV = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim; a.NA = c.n_q_heads * c.head_dim;
   a.M = q->plan.rows; a.NS = q->n_splits; a.kb = q->plan.kb; a.ctx_max = q->plan.ctx_max;
   a.qk_norm = c.qk_norm; a.has_embed = c.has_embed; a.eps = c.rms_eps; a.theta = c.rope_theta;
+  for (int i = 0; i < c.head_dim / 2 && i < 64; ++i)
+    a.rope_inv[i] = std::pow((double)c.rope_theta, -2.0 * i / (double)c.head_dim);
   a.wqkv = w->wqkv; a.wo = w->wo; a.wgate = w->wgate; a.wup = w->wup; a.wdown = w->wdown;
   a.attn_norm = w->attn_norm; a.ffn_norm = w->ffn_norm; a.q_norm = w->q_norm; a.k_norm = w->k_norm;
   a.embed = w->embed; a.lm_head = w->lm_head; a.final_norm = w->final_norm;
@@ -161,6 +201,8 @@ void fill_args(const mk_queue* q, const void* d_queue, const mk_weights* w, cons
   a.targets = reinterpret_cast<const uint32_t*>(qd + q->dev_targets_off);
   a.n_instr = (uint32_t)q->instr.size(); a.n_barriers = (uint32_t)q->targets.size();
   a.n_queues = (uint32_t)q->plan.n_queues;
+  const LdsLayout ll = lds_layout(q);
+  a.lds_res = ll.res; a.lds_x = ll.x; a.lds_union = ll.uni; a.lds_bytes = ll.bytes;
 }
 
 // Final RMSNorm + LM head GEMV (+ argmax) over the workspace's last hidden rows.
@@ -228,9 +270,7 @@ mk_status mk_decode_step(const mk_queue* q, const void* d_queue, const mk_weight
   if (mk_status st = check_shapes(c)) return st;
   if (batch != q->plan.rows) FAIL(MK_EINVAL, "batch %d differs from the queue's rows %d", batch, q->plan.rows);
   if (exec_mode != MK_MEGAKERNEL && exec_mode != MK_KERNEL_PER_OP) FAIL(MK_EINVAL, "unknown exec_mode");
-  const int nb_bucket = q->plan.rows <= 1 ? 1 : q->plan.rows <= 2 ? 2 : q->plan.rows <= 4 ? 4 : q->plan.rows <= 8 ? 8 : q->plan.rows <= 16 ? 16 : 32;
-  const int max_rows = std::max({q->plan.tq, q->plan.to, 2 * q->plan.tf, q->plan.td, 16});
-  if (max_rows * nb_bucket > RES_FLOATS) FAIL(MK_ENOTSUP, "tile rows x batch above %d", RES_FLOATS);
+  if (lds_layout(q).bytes > kMaxLds) FAIL(MK_ENOTSUP, "tiles need more shared memory than a workgroup has");
   const Layout o = layout(q);
   if (workspace_nbytes < o.total) FAIL(MK_EINVAL, "workspace of %zu bytes, need %zu", workspace_nbytes, o.total);
   if (c.has_embed ? (!d_tokens || !w->embed) : !d_x0) FAIL(MK_EINVAL, "missing input tokens / rows");
@@ -244,6 +284,7 @@ mk_status mk_decode_step(const mk_queue* q, const void* d_queue, const mk_weight
   a.tokens = d_tokens; a.x0 = d_x0; a.ctx_lens = d_ctx_lens;
   a.logits = d_logits; a.next = d_next;
   a.spin_limit = g_opt.spin_limit;
+  a.trace = (g_opt.trace && g_opt.trace_bytes >= 32 * q->instr.size()) ? g_opt.trace : nullptr;
 
   // without an embedding the input rows are copied into X_0 by the first launch
   if (!c.has_embed) {
@@ -291,6 +332,9 @@ mk_status mk_lm_head(const mk_queue* q, const mk_weights* w, void* d_workspace, 
   a.X = reinterpret_cast<float*>(ws + o.X); a.sX = o.sX;
   a.lm_val = reinterpret_cast<float*>(ws + o.LMV); a.lm_idx = reinterpret_cast<int*>(ws + o.LMI);
   a.lm_blocks = o.lm_blocks; a.err = reinterpret_cast<uint32_t*>(ws + o.ERR);
+  a.r = c.n_q_heads / c.n_kv_heads; a.hd = c.head_dim;
+  const LdsLayout ll = lds_layout(q);
+  a.lds_res = ll.res; a.lds_x = ll.x; a.lds_union = ll.uni; a.lds_bytes = ll.bytes;
   a.logits = d_logits; a.next = d_next;
   const hipError_t e = launch_lm(pick_table(c.dtype, a.M), a, d_next != nullptr, stream);
   if (e != hipSuccess) FAIL(MK_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
@@ -328,6 +372,11 @@ mk_status mk_set_option(int32_t key, int64_t value) {
     case MK_OPT_SPIN_LIMIT:
       if (value < 1 || value > (int64_t)1 << 31) FAIL(MK_EINVAL, "spin limit out of range");
       g_opt.spin_limit = (uint32_t)value; return MK_OK;
+    case MK_OPT_TRACE_BUFFER:
+      g_opt.trace = reinterpret_cast<unsigned long long*>(static_cast<uintptr_t>(value)); return MK_OK;
+    case MK_OPT_TRACE_BYTES:
+      if (value < 0) FAIL(MK_EINVAL, "negative trace size");
+      g_opt.trace_bytes = (size_t)value; return MK_OK;
     default: FAIL(MK_EINVAL, "unknown or read-only option %d", key);
   }
 }
@@ -337,6 +386,8 @@ int64_t mk_get_option(int32_t key) {
     case MK_OPT_WORKERS_PER_CU: return g_opt.workers_per_cu;
     case MK_OPT_SPIN_LIMIT: return g_opt.spin_limit;
     case MK_OPT_NUM_CUS: return num_cus();
+    case MK_OPT_TRACE_BUFFER: return (int64_t)(uintptr_t)g_opt.trace;
+    case MK_OPT_TRACE_BYTES: return (int64_t)g_opt.trace_bytes;
     default: return -1;
   }
 }

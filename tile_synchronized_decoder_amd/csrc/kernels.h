@@ -39,11 +39,12 @@ using mk::Range;
 
 constexpr int NT = 256;                 // threads per workgroup
 constexpr int NWAVE = NT / 64;
-constexpr int XBUF_FLOATS = 16384;      // LDS staging of GEMV inputs (64 KB)
-constexpr int RES_FLOATS = 2048;        // LDS GEMV results (rows x batch)
+constexpr int XBUF_MAX = 16384;         // LDS staging of GEMV inputs, upper bound (64 KB)
 constexpr int ROWS_PER_PASS_MAX = 16;   // GEMV rows reduced per pass (4 waves x 4)
 constexpr int ATT_MAX_R = 4;            // query heads per KV head
 constexpr int ATT_CHUNK = NT;           // keys scored per attention chunk
+constexpr int LM_ROWS = 96;             // vocabulary rows per LM-head workgroup
+constexpr int RING_LINES = 24;          // 1 KB weight lines in flight per wave
 constexpr uint32_t ERR_TIMEOUT = 1, ERR_OPCODE = 2, ERR_CONTEXT = 3, ERR_TOKEN = 4;
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
@@ -72,6 +73,12 @@ struct Args {
   const int* tokens; const float* x0; const int* ctx_lens;
   float* logits; int* next;
   uint32_t spin_limit;
+  // dynamic shared memory layout, in floats (see lds_layout on the host)
+  uint32_t lds_res, lds_x, lds_union, lds_bytes;
+  // rotary inverse frequencies theta^(-2i/hd), i < hd/2, computed in float64 on the host
+  double rope_inv[64];
+  // optional per-instruction trace: 4 x u64 per instruction (see mk.h)
+  unsigned long long* trace;
 };
 
 // Device code reads the arguments in place, through a constant-address-space
@@ -202,6 +209,7 @@ __device__ __forceinline__ bool wait_tiles(KArgs& a, const Instr in, uint32_t id
   }
   const bool all = __syncthreads_and(ok) != 0;
   asm volatile("" ::: "memory");                 // no tile load may move above the wait
+  if (a.trace && threadIdx.x == 0) a.trace[4 * (size_t)idx + 2] = wall_clock64();
   return all;
 }
 
@@ -215,87 +223,110 @@ __device__ __forceinline__ void signal_tile(KArgs& a, const Instr in) {
 
 // ----------------------------------------------------------------------------- shared memory arena
 
-struct Smem {
-  union {
-    float x[XBUF_FLOATS];                                          // GEMV input rows (gain applied)
-    struct {
-      float q[ATT_MAX_R * 128];                                    // rotated queries
-      float kn[128], vn[128];                                      // new key / value (as stored)
-      float cs[64], sn[64];                                        // rotary cos / sin
-      float p[ATT_MAX_R * ATT_CHUNK];                              // scores -> probabilities
-      float red[NWAVE * ATT_MAX_R];
-      float m[ATT_MAX_R], l[ATT_MAX_R], alpha[ATT_MAX_R];
-      float o[ATT_MAX_R * 128];                                    // running output of the split
-      float part[NT * 8];                                          // PV partial sums per key slice
-      uint16_t vbuf[ATT_CHUNK * 128];                              // value rows of the chunk (raw, <= 256 B each)
-    } att;
-  };
-  float res[RES_FLOATS];
-  float ss[32];
-  float ssw[NWAVE * 32];
-  uint32_t idx;
+// Views into the dynamic shared memory of a workgroup.  The host sizes the
+// regions for the model and batch (Args::lds_*), so small models leave room
+// for several workgroups per compute unit.  The GEMV staging buffer and the
+// attention buffers share one region.
+struct AttSmem {
+  float* q;        // rotated queries            [r * hd]
+  float* kn;       // new key, as stored          [hd]
+  float* vn;       // new value, as stored        [hd]
+  float* cs;       // rotary cos                  [hd / 2]
+  float* sn;       // rotary sin                  [hd / 2]
+  float* p;        // probabilities of a chunk    [r * ATT_CHUNK]
+  float* red;      // cross-wave reductions       [NWAVE * ATT_MAX_R]
+  float* snew;     // scores of the new key       [ATT_MAX_R]
+  float* m;        // running max                 [ATT_MAX_R]
+  float* l;        // running sum                 [ATT_MAX_R]
+  float* o;        // running output              [r * hd]
+  float* part;     // PV partials per key slice   [NT * 8]
+  uint16_t* vbuf;  // value rows of the chunk     [ATT_CHUNK * hd] elements
 };
+struct Smem {
+  uint32_t* idx;   // popped instruction index
+  float* ss;       // per-row norm factors        [32]
+  float* ssw;      // per-wave partial sums       [NWAVE * 32]
+  float* res;      // GEMV results                [rows * NB]
+  uint8_t* ring;   // GEMV weight rings           [NWAVE][RING_LINES][1 KB]
+  float* x;        // GEMV input staging          [xcap]
+  int xcap;
+  AttSmem att;
+};
+
+extern __shared__ __align__(16) float mk_smem[];
+
+__device__ __forceinline__ Smem make_smem(KArgs& a) {
+  Smem s;
+  float* base = mk_smem;
+  s.idx = reinterpret_cast<uint32_t*>(base);
+  s.ss = base + 4;
+  s.ssw = s.ss + 32;
+  s.res = s.ssw + NWAVE * 32;
+  float* u = s.res + a.lds_res;
+  s.ring = reinterpret_cast<uint8_t*>(u);
+  s.x = u + NWAVE * RING_LINES * 256;
+  s.xcap = (int)a.lds_x;
+  const int r = a.r, hd = a.hd;
+  auto take = [&](int n) { float* p = u; u += (n + 3) & ~3; return p; };
+  s.att.q = take(r * hd);
+  s.att.kn = take(hd);
+  s.att.vn = take(hd);
+  s.att.cs = take(hd / 2);
+  s.att.sn = take(hd / 2);
+  s.att.p = take(r * ATT_CHUNK);
+  s.att.red = take(NWAVE * ATT_MAX_R);
+  s.att.snew = take(ATT_MAX_R);
+  s.att.m = take(ATT_MAX_R);
+  s.att.l = take(ATT_MAX_R);
+  s.att.o = take(r * hd);
+  s.att.part = take(NT * 8);
+  s.att.vbuf = reinterpret_cast<uint16_t*>(u);
+  return s;
+}
 
 // ----------------------------------------------------------------------------- GEMV op bodies
 
-// Rows of a pass come from up to two matrices: row i < split reads A[row0+i],
-// row i >= split reads B[row0+i-split] (gate / up).  RPW rows per wave.
+// Weights stream through a per-wave ring of 1 KB lines in shared memory, filled
+// by direct global->LDS loads (no registers held while in flight).  Lines are
+// numbered in the order the wave consumes them; the ring is filled before the
+// instruction waits on its producer tiles, then refilled one line per line
+// consumed, so RING_LINES lines stay in flight per wave.
+
+// Wait until at most N of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  asm volatile("" ::: "memory");
+}
+
+// Rows come from up to two matrices: row i < split reads A[row0+i], row
+// i >= split reads B[row0+i-split] (gate / up).  Each wave owns RPW rows of a
+// pass of ROWS rows.
 template <typename WT, int NB, int RPW>
 struct Gemv {
   static constexpr int ROWS = NWAVE * RPW;
-  // 512-column iterations per register window; two windows are in flight
-  static constexpr int WIN = (Elem<WT>::VEC == 1 && NB <= 8) ? 4 : 2;
   using E = Elem<WT>;
-
-  struct Win { v4u w[WIN][RPW][E::VEC]; };
+  static constexpr int LPI = E::VEC;     // lines per (row, 512-column iteration)
 
   const WT* A; const WT* B; int split; int row0; int nrows; int K;
 
   __device__ const WT* row_ptr(int i) const { return i < split ? A + (size_t)(row0 + i) * K : B + (size_t)(row0 + i - split) * K; }
 
-  // Issue the loads of iterations [it0, min(it0 + WIN, it_lim)) of this wave's rows of pass `pass`.
-  __device__ void load(Win& W, int pass, int it0, int it_lim) const {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  // Issue the RPW * LPI lines of one 512-column iteration `it` of pass `pass`
+  // of this wave into ring group `grp`.  Lines of rows past the tile or
+  // columns past K re-read valid addresses and are ignored by the consumer.
+  __device__ void issue_iter(uint8_t* ring, int grp, int pass, int it, int wave, int lane) const {
+    int col = it * 512 + lane * 8;
+    if (col >= K) col = 0;
 #pragma unroll
-    for (int i = 0; i < WIN; ++i)
+    for (int j = 0; j < RPW; ++j) {
+      int row = pass * ROWS + wave * RPW + j;
+      if (row >= nrows) row = 0;
+      const WT* p = row_ptr(row) + col;
 #pragma unroll
-      for (int j = 0; j < RPW; ++j) {
-        const int row = pass * ROWS + wave * RPW + j;
-        const int col = (it0 + i) * 512 + lane * 8;
-        if (row < nrows && col < K && it0 + i < it_lim) {
-          const v4u* p = reinterpret_cast<const v4u*>(row_ptr(row) + col);
-#pragma unroll
-          for (int v = 0; v < E::VEC; ++v) W.w[i][j][v] = __builtin_nontemporal_load(p + v);
-        } else {
-#pragma unroll
-          for (int v = 0; v < E::VEC; ++v) W.w[i][j][v] = v4u{0, 0, 0, 0};
-        }
-      }
-  }
-
-  // Accumulate iterations [it0, it0 + WIN) against the staged inputs (columns kc0..).
-  __device__ void fma(const Win& W, int it0, int it_lim, int kc0, int kcn, int nb, const float* xs,
-                      float acc[RPW][NB]) const {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < WIN; ++i) {
-      const int col = (it0 + i) * 512 + lane * 8;
-      if (it0 + i >= it_lim || col >= K) break;
-      float wf[RPW][8];
-#pragma unroll
-      for (int j = 0; j < RPW; ++j) E::unpack(W.w[i][j], wf[j]);
-      const int c = col - kc0;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if (b >= nb) break;
-        const float4 x0 = *reinterpret_cast<const float4*>(xs + b * kcn + c);
-        const float4 x1 = *reinterpret_cast<const float4*>(xs + b * kcn + c + 4);
-        const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-        for (int j = 0; j < RPW; ++j)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[j][b] = fmaf(wf[j][e], xv[e], acc[j][b]);
-      }
+      for (int v = 0; v < LPI; ++v)
+        __builtin_amdgcn_global_load_lds(p + v * 4, ring + ((grp * RPW + j) * LPI + v) * 1024, 16, 0, 0);
     }
   }
 };
@@ -321,27 +352,41 @@ __device__ __forceinline__ void stage_x(Smem& s, const float* x, int ldx, int nb
 
 // Full GEMV of `nrows` rows against `nb` input rows of length K, results in
 // s.res[row * NB + b] (already scaled by the row's RMSNorm factor when `norm`).
-// When `mega`, the first weight window is issued before waiting on the
-// instruction's producer tiles.  Returns false when the wait gave up.
+// When `mega`, the weight ring is filled before waiting on the instruction's
+// producer tiles.  Returns false when the wait gave up.
 template <typename WT, int NB, int RPW>
 __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW>& g, const float* x, int nb,
                      const float* gain, bool norm, bool mega, const Instr in, uint32_t idx) {
   using G = Gemv<WT, NB, RPW>;
+  using E = Elem<WT>;
   const int K = g.K;
   const int iters = (K + 511) / 512;
-  const int kc_max = (XBUF_FLOATS / NB) / 512 * 512;
+  const int kc_max = (s.xcap / NB) / 512 * 512;
   const int npass = (g.nrows + G::ROWS - 1) / G::ROWS;
   const bool single_chunk = K <= kc_max;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-
-  typename G::Win W0, W1;
-  g.load(W0, 0, 0, min(iters, kc_max / 512));          // weight prefetch, before any wait
-  if (mega && !wait_tiles(a, in, idx)) return false;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  uint8_t* ring = s.ring + wave * RING_LINES * 1024;
+  constexpr int GL = RPW * G::LPI;                     // lines per iteration group
+  constexpr int NG = RING_LINES / GL;                  // groups in the ring
+  static_assert(NG >= 2 && RING_LINES % GL == 0, "ring holds whole iteration groups");
+  const int ngroups = npass * iters;                   // groups this wave consumes
+  // refill cursor: the next (pass, iteration) to issue
+  int rp = 0, ri = 0;
+  auto issue_next = [&](int grp) {
+    g.issue_iter(ring, grp, rp, ri, wave, lane);
+    if (++ri == iters) { ri = 0; ++rp; }
+  };
+  for (int q = 0; q < min(ngroups, NG); ++q) issue_next(q);          // prefetch
+  if (mega && !wait_tiles(a, in, idx)) {
+    wait_vm<0>();                                        // drain before the ring is reused
+    return false;
+  }
 
   float ssl[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) ssl[b] = 0.f;
   bool staged = false;
+  int gi = 0;                                            // next group to consume
 
   for (int pass = 0; pass < npass; ++pass) {
     float acc[RPW][NB];
@@ -349,7 +394,6 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW>&
     for (int j = 0; j < RPW; ++j)
 #pragma unroll
       for (int b = 0; b < NB; ++b) acc[j][b] = 0.f;
-    if (pass > 0) g.load(W0, pass, 0, min(iters, kc_max / 512));
     for (int kc0 = 0; kc0 < K; kc0 += kc_max) {
       const int kcn = min(kc_max, K - kc0);
       if (!(single_chunk && staged)) {
@@ -359,16 +403,44 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW>&
         staged = true;
       }
       const int it_begin = kc0 / 512, it_end = (kc0 + kcn + 511) / 512;
-      for (int it = it_begin; it < it_end; it += 2 * G::WIN) {
-        if (it + G::WIN < it_end) g.load(W1, pass, it + G::WIN, it_end);
-        g.fma(W0, it, it_end, kc0, kcn, nb, s.x, acc);
-        if (it + G::WIN < it_end) {
-          if (it + 2 * G::WIN < it_end) g.load(W0, pass, it + 2 * G::WIN, it_end);
-          g.fma(W1, it + G::WIN, it_end, kc0, kcn, nb, s.x, acc);
+      for (int it = it_begin; it < it_end; ++it, ++gi) {
+        const int col = it * 512 + lane * 8;
+        const bool valid = col < K;
+        const int c = col - kc0;
+        // group gi has landed once at most (issued - gi - 1) groups are outstanding
+        if (gi + NG <= ngroups) wait_vm<(NG - 1) * GL>(); else wait_vm<0>();
+        const uint8_t* gbase = ring + (gi % NG) * GL * 1024 + lane * 16;
+        v4u w[RPW][G::LPI];
+#pragma unroll
+        for (int j = 0; j < RPW; ++j)
+#pragma unroll
+          for (int v = 0; v < G::LPI; ++v) w[j][v] = *reinterpret_cast<const v4u*>(gbase + (j * G::LPI + v) * 1024);
+        float xv[NB][8];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if (b < nb && valid) {
+            const float4 x0 = *reinterpret_cast<const float4*>(s.x + b * kcn + c);
+            const float4 x1 = *reinterpret_cast<const float4*>(s.x + b * kcn + c + 4);
+            xv[b][0] = x0.x; xv[b][1] = x0.y; xv[b][2] = x0.z; xv[b][3] = x0.w;
+            xv[b][4] = x1.x; xv[b][5] = x1.y; xv[b][6] = x1.z; xv[b][7] = x1.w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xv[b][e] = 0.f;
+          }
+        }
+        // the group's reads have returned: its slots can be refilled
+        __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0); vmcnt, expcnt unconstrained
+        if (gi + NG < ngroups) issue_next(gi % NG);
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) {
+          float wf[8];
+          E::unpack(w[j], wf);
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[j][b] = fmaf(wf[e], xv[b][e], acc[j][b]);
         }
       }
-      // the next chunk restarts its window from the first iteration of the chunk
-      if (kc0 + kc_max < K) g.load(W0, pass, (kc0 + kc_max) / 512, min(iters, (kc0 + 2 * kc_max) / 512));
     }
     // reduce each (row, b) across the wave; lane 0 keeps the sum
 #pragma unroll
@@ -380,7 +452,6 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW>&
         if (lane == 0 && row < g.nrows && b < nb) s.res[row * NB + b] = v;
       }
   }
-  (void)iters;
   if (norm) {
     // every thread staged a disjoint part of the rows: reduce sum(x^2) over the workgroup
 #pragma unroll
@@ -571,10 +642,15 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
     s.att.vn[t] = ld_cg(qkv + (a.nq + a.nkv) * HD + g * HD + t);
   }
   if (t < HALF) {
-    const double inv = pow(a.theta, -2.0 * (double)t / (double)HD);
-    const double ang = (double)pos * inv;
-    s.att.cs[t] = (float)cos(ang);
-    s.att.sn[t] = (float)sin(ang);
+    // angle p * theta^(-2i/hd) in float64, reduced to [-pi, pi] in float64
+    // (2 pi split in two parts), then evaluated in fp32
+    const double ang = (double)pos * a.rope_inv[t];
+    const double k = rint(ang * 0.15915494309189535);
+    const double red = fma(-k, 6.283185307179586, ang) - k * 2.4492935982947064e-16;
+    float sv, cv;
+    sincosf((float)red, &sv, &cv);
+    s.att.cs[t] = cv;
+    s.att.sn[t] = sv;
   }
   for (int e = t; e < r * HD; e += NT) s.att.o[e] = 0.f;
   __syncthreads();
@@ -631,6 +707,21 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
   }
   if (t < r) { s.att.m[t] = -INFINITY; s.att.l[t] = 0.f; }
   __syncthreads();
+  {
+    // scores of the new key (one wave per query head)
+    const int wave = t >> 6, lane = t & 63;
+    for (int h = wave; h < r; h += NWAVE) {
+      float acc = 0.f;
+      for (int d = lane; d < HD; d += 64) acc = fmaf(s.att.q[h * HD + d], s.att.kn[d], acc);
+      acc = wave_sum(acc);
+      if (lane == 0) s.att.snew[h] = acc;
+    }
+  }
+  // the chunk that holds pos gets the new value row from these threads
+  const bool has_pos = j0 <= pos && pos < j1;
+  const int pos_chunk = has_pos ? (pos - j0) / ATT_CHUNK : -1;
+  const int pos_row = has_pos ? (pos - j0) % ATT_CHUNK : 0;
+  __syncthreads();
 
   // PV work split: thread t sums a group of 8 output dims of one head over a
   // strided slice of the chunk's keys
@@ -647,16 +738,14 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
     float sc[ATT_MAX_R], mx[ATT_MAX_R], sum[ATT_MAX_R];
 #pragma unroll
     for (int h = 0; h < ATT_MAX_R; ++h) sc[h] = 0.f;
+    if (has_pos && (c0 - j0) / ATT_CHUNK == pos_chunk && t < HD)
+      E::put(reinterpret_cast<KT*>(s.att.vbuf) + (size_t)pos_row * HD, t, s.att.vn[t]);
     if (valid) {
       KT* vrow = reinterpret_cast<KT*>(s.att.vbuf) + (size_t)t * HD;
       if (j == pos) {
-        for (int d = 0; d < HD; ++d) {
-          const float kv = s.att.kn[d];
 #pragma unroll
-          for (int h = 0; h < ATT_MAX_R; ++h)
-            if (h < r) sc[h] = fmaf(s.att.q[h * HD + d], kv, sc[h]);
-        }
-        for (int d = 0; d < HD; ++d) E::put(vrow, d, s.att.vn[d]);
+        for (int h = 0; h < ATT_MAX_R; ++h)
+          if (h < r) sc[h] = s.att.snew[h];
       } else {
         if (c0 != j0) {
           const v4u* pk = reinterpret_cast<const v4u*>(Kc + (size_t)j * HD);
@@ -803,7 +892,7 @@ __device__ __forceinline__ void run_instr(KArgs& a, Smem& s, const Instr in, uin
 // subsequence of one topological order, so popping ahead cannot deadlock.
 template <typename WT, int NB>
 __global__ __launch_bounds__(NT) void mk_interp(Args args) {
-  __shared__ Smem s;
+  Smem s = make_smem(kernel_args());
   const uint32_t qi = blockIdx.x % args.n_queues;
   uint32_t k_next = 0;
   if (threadIdx.x == 0) {
@@ -815,22 +904,32 @@ __global__ __launch_bounds__(NT) void mk_interp(Args args) {
     if (threadIdx.x == 0) {
       const uint64_t i = (uint64_t)k_next * a.n_queues + qi;
       const bool go = i < a.n_instr && !aborted(a);
-      s.idx = go ? (uint32_t)i : 0xFFFFFFFFu;
+      *s.idx = go ? (uint32_t)i : 0xFFFFFFFFu;
       if (go) k_next = __hip_atomic_fetch_add(a.heads + qi * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    const uint32_t idx = __builtin_amdgcn_readfirstlane(s.idx);   // uniform: keep the record in SGPRs
+    const uint32_t idx = __builtin_amdgcn_readfirstlane(*s.idx);   // uniform: keep the record in SGPRs
     __syncthreads();
     if (idx == 0xFFFFFFFFu) break;
+    unsigned long long t0 = 0;
+    if (a.trace) t0 = wall_clock64();
     run_instr<WT, NB>(a, s, load_instr(a, idx), idx, true, 0);
+    if (a.trace && threadIdx.x == 0) {
+      unsigned long long* rec = a.trace + 4 * (size_t)idx;
+      uint32_t xcc;
+      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+      rec[0] = ((unsigned long long)blockIdx.x << 32) | (xcc & 0xF);
+      rec[1] = t0;
+      rec[3] = wall_clock64();
+    }
   }
 }
 
 // One launch per (layer, op): workgroup i runs instruction first + i, no waits.
 template <typename WT, int NB, int OP>
 __global__ __launch_bounds__(NT) void kpo_kernel(Args args, uint32_t first) {
-  __shared__ Smem s;
   KArgs& a = kernel_args();
+  Smem s = make_smem(a);
   const uint32_t idx = first + blockIdx.x;
   const Instr in = load_instr(a, idx);
   if (in.op != OP) {
@@ -844,10 +943,10 @@ __global__ __launch_bounds__(NT) void kpo_kernel(Args args, uint32_t first) {
 // workgroup, plus the block's (max, lowest index) per row for the argmax.
 template <typename WT, int NB>
 __global__ __launch_bounds__(NT) void lm_head_kernel(Args args) {
-  __shared__ Smem s;
   KArgs& a = kernel_args();
+  Smem s = make_smem(a);
   constexpr int RPW = rpw_for<NB>();
-  constexpr int ROWS = 16;
+  constexpr int ROWS = LM_ROWS;
   const int v0 = blockIdx.x * ROWS;
   const int n = min(ROWS, a.V - v0);
   const WT* W = static_cast<const WT*>(a.lm_head);
@@ -871,15 +970,36 @@ __global__ __launch_bounds__(NT) void lm_head_kernel(Args args) {
   }
 }
 
+// Kernels whose dynamic shared memory exceeds the default limit must opt in once.
+template <typename K>
+inline hipError_t allow_lds(K kernel, uint32_t bytes, uint32_t& granted) {
+  if (bytes <= granted) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) granted = bytes;
+  return e;
+}
+
 template <typename WT, int NB>
 struct Launch {
   static hipError_t mega(const Args& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((mk_interp<WT, NB>), dim3(grid), dim3(NT), 0, st, a);
+    static uint32_t granted = 64 * 1024;
+    hipError_t e = allow_lds(mk_interp<WT, NB>, a.lds_bytes, granted);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((mk_interp<WT, NB>), dim3(grid), dim3(NT), a.lds_bytes, st, a);
     return hipGetLastError();
   }
   static hipError_t kpo(const Args& a, uint32_t op, uint32_t first, uint32_t count, hipStream_t st) {
+    static uint32_t granted[mk::OP_COUNT] = {};
     switch (op) {
-#define KPO_CASE(OPC) case OPC: hipLaunchKernelGGL((kpo_kernel<WT, NB, OPC>), dim3(count), dim3(NT), 0, st, a, first); break;
+#define KPO_CASE(OPC)                                                                              \
+      case OPC: {                                                                                  \
+        if (!granted[OPC]) granted[OPC] = 64 * 1024;                                               \
+        hipError_t e = allow_lds(kpo_kernel<WT, NB, OPC>, a.lds_bytes, granted[OPC]);              \
+        if (e != hipSuccess) return e;                                                             \
+        hipLaunchKernelGGL((kpo_kernel<WT, NB, OPC>), dim3(count), dim3(NT), a.lds_bytes, st, a, first); \
+        break;                                                                                     \
+      }
       KPO_CASE(mk::OP_EMBED) KPO_CASE(mk::OP_QKV) KPO_CASE(mk::OP_ATTN) KPO_CASE(mk::OP_COMBINE)
       KPO_CASE(mk::OP_OPROJ) KPO_CASE(mk::OP_GATEUP) KPO_CASE(mk::OP_DOWN)
 #undef KPO_CASE
@@ -888,7 +1008,10 @@ struct Launch {
     return hipGetLastError();
   }
   static hipError_t lm(const Args& a, hipStream_t st) {
-    hipLaunchKernelGGL((lm_head_kernel<WT, NB>), dim3(a.lm_blocks), dim3(NT), 0, st, a);
+    static uint32_t granted = 64 * 1024;
+    hipError_t e = allow_lds(lm_head_kernel<WT, NB>, a.lds_bytes, granted);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((lm_head_kernel<WT, NB>), dim3(a.lm_blocks), dim3(NT), a.lds_bytes, st, a);
     return hipGetLastError();
   }
 };
