@@ -132,10 +132,12 @@ typedef struct mk_weights {
   const float* final_norm; /* [H]      (has_lm_head only) */
 } mk_weights;
 
-/* KV cache: [L][rows][n_kv][ctx_max][hd] in the model dtype, keys after RoPE. */
+/* KV cache: [L][rows][n_kv][ctx_max][hd] in the model dtype, keys after RoPE.
+ * rows: sequences the cache holds (decode: 0 or the batch; prefill: >= 1). */
 typedef struct mk_kv {
   void* k;
   void* v;
+  int32_t rows;
 } mk_kv;
 
 /* One decode step for `batch` sequences (must equal the queue's rows).
@@ -166,10 +168,14 @@ mk_status mk_decode_step(const mk_queue* q, const void* d_queue, const mk_weight
 mk_status mk_lm_head(const mk_queue* q, const mk_weights* w, void* d_workspace, size_t workspace_nbytes,
                      float* d_logits, int32_t* d_next, hipStream_t stream);
 
-/* Causal prefill of seq_len (<= the queue's rows) tokens of one sequence into
- * cache row kv_row, positions 0..seq_len-1.  Row blocks at or past seq_len are
- * skipped (the queue is built once for S_max).  d_logits_last [V] and d_next
- * [1] receive the last position's logits and argmax. */
+/* Causal prefill of seq_len (1 .. the queue's rows) tokens of one sequence into
+ * cache row kv_row (< kv->rows), positions 0..seq_len-1.  Row blocks at or past
+ * seq_len are no-ops (the queue is built once for S_max).  d_logits_last [V]
+ * and d_next [1] receive the last position's logits and argmax.  The GEMM
+ * tiles run on the matrix cores with bf16 operands (activations rounded to
+ * bf16 on the way in) and fp32 accumulation.  Requires a bf16 model with an
+ * embedding, head_dim 128 and 128 x 128 tiles (MK_ENOTSUP otherwise).  The
+ * per-layer hidden rows are the workspace tensors, [S_max][...] fp32. */
 mk_status mk_prefill(const mk_queue* q, const void* d_queue, const mk_weights* w,
                      const mk_kv* kv, const int32_t* d_tokens, int32_t seq_len, int32_t kv_row,
                      void* d_workspace, size_t workspace_nbytes, float* d_logits_last,

@@ -173,6 +173,29 @@ def test_bf16_shrunk_modes_bitwise_equal():
             assert np.array_equal(a, b)
 
 
+def test_bf16_separate_lm_head_matches_fused():
+    """mk_decode_step without outputs followed by mk_lm_head gives the logits
+    and argmax of mk_decode_step with outputs, bit for bit, in both modes."""
+    from _gpucase import make_case
+    wl = _shrunk_1b(batch=2, ctx0=(700, 1100), steps=1)
+    c = make_case(wl)
+    m, B = c.m, 2
+    tok = torch.from_numpy(c.tokens[0].astype(np.int32)).cuda()
+    cl = torch.tensor([700, 1100], dtype=torch.int32, device="cuda")
+    for mode in (T.MK_MEGAKERNEL, T.MK_KERNEL_PER_OP):
+        c.reset_kv()
+        c.step(0, [700, 1100], mode)
+        fused = (c.logits.cpu().numpy().copy(), c.nxt.cpu().numpy().copy())
+        c.reset_kv()
+        lg = torch.full((B, m.vocab), -1.0, dtype=torch.float32, device="cuda")
+        nx = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+        T.mk_decode_step(c.q, c.dq, c.dm.w, c.dkv.kv, tok, None, cl, B, c.ws, None, None, mode)
+        T.mk_lm_head(c.q, c.dm.w, c.ws, lg, nx)
+        torch.cuda.synchronize()
+        assert np.array_equal(lg.cpu().numpy(), fused[0])
+        assert np.array_equal(nx.cpu().numpy(), fused[1])
+
+
 # ----------------------------------------------------------------------------- full Llama-3-1B shape
 
 @pytest.mark.slow

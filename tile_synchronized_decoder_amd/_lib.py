@@ -41,7 +41,7 @@ class mk_weights(C.Structure):
 
 
 class mk_kv(C.Structure):
-    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p)]
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("rows", C.c_int32)]
 
 
 class mk_dev_error(C.Structure):

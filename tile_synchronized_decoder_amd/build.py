@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmk.so")
 OBJDIR = os.path.join(HERE, "_build")
 # (source, extra defines, object name); inst.hip is compiled once per element type x batch bucket
-UNITS = [("queue.cpp", [], "queue.o"), ("api.hip", [], "api.o")] + [
+UNITS = [("queue.cpp", [], "queue.o"), ("api.hip", [], "api.o"), ("prefill.hip", [], "prefill.o")] + [
     ("inst.hip", [f"-DMK_WT={wt}", f"-DMK_WT_NAME={name}", f"-DMK_NB={nb}"], f"inst_{name}_{nb}.o")
     for wt, name in (("uint16_t", "bf16"), ("float", "f32")) for nb in (1, 2, 4, 8, 16, 32)]
 

@@ -18,6 +18,7 @@ namespace mkd {
 MK_DECL(bf16)
 MK_DECL(f32)
 #undef MK_DECL
+Table table_prefill();
 }  // namespace mkd
 
 namespace {
@@ -141,24 +142,36 @@ int nb_bucket(int rows) {
   return rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : rows <= 8 ? 8 : rows <= 16 ? 16 : 32;
 }
 
-struct LdsLayout { uint32_t res, x, uni, bytes; };
+struct LdsLayout { uint32_t res, x, ring, uni, bytes; };
+
+// Bytes of the prefill tile region: the larger of a GEMM tile (two stages of a
+// 128 x 64 activation tile and a 256 x 64 weight tile, plus row statistics)
+// and an attention tile (Q, a 64-key K and V^T block, scores, probabilities).
+constexpr uint32_t kPrefillGemmBytes = 2 * 128 * 128 + 2 * 256 * 128 + (256 + 128) * 4;
+constexpr uint32_t kPrefillAttnBytes = 2 * 128 * 128 + 2 * 64 * 128 + 128 * 64 * 2 + 128 * 64 * 4 + 128 * 64 * 2 + 3 * 128 * 4;
 
 // Dynamic shared memory of one workgroup, in floats: header (index, norm
 // factors), GEMV results, then one region shared by the GEMV input staging and
 // the attention buffers.  Mirrors make_smem() in kernels.h.
-LdsLayout lds_layout(const mk_queue* q) {
-  const mk_config& c = q->cfg;
-  const mk_plan& p = q->plan;
+LdsLayout lds_layout(const mk_config& c, const mk_plan& p) {
+  LdsLayout o{};
+  if (p.mode == MK_PREFILL) {
+    // prefill tiles use the header and the tile region only
+    o.ring = (std::max(kPrefillGemmBytes, kPrefillAttnBytes) + 255) & ~255u;
+    o.uni = o.ring / 4;
+    o.bytes = 4 * (4 + 32 + NWAVE * 32) + o.ring;
+    return o;
+  }
   const uint32_t nb = nb_bucket(p.rows);
   auto r4 = [](uint32_t n) { return (n + 3) & ~3u; };
   const uint32_t max_rows = std::max({p.tq, p.to, 2 * p.tf, p.td, LM_ROWS});
-  LdsLayout o{};
   o.res = r4(max_rows * nb);
   const uint32_t kmax = std::max({c.hidden, c.ffn, c.n_q_heads * c.head_dim});
   o.x = std::max<uint32_t>(std::min<uint32_t>(XBUF_MAX, nb * kmax), nb * 512);
   // keep the whole layout within one workgroup's shared memory: shrink the
   // input staging (it is consumed in chunks of nb * 512 floats)
-  const uint32_t fixed = 4 * (4 + 32 + NWAVE * 32 + o.res) + NWAVE * RING_LINES * 1024;
+  o.ring = NWAVE * RING_LINES * 1024;
+  const uint32_t fixed = 4 * (4 + 32 + NWAVE * 32 + o.res) + o.ring;
   const uint32_t room = fixed < kMaxLds ? (kMaxLds - fixed) / 4 : 0;
   if (o.x > room) o.x = std::max<uint32_t>(room / (nb * 512) * (nb * 512), nb * 512);
   o.x = r4(o.x);
@@ -166,10 +179,11 @@ LdsLayout lds_layout(const mk_queue* q) {
   const uint32_t esz = c.dtype == MK_BF16 ? 2 : 4;
   const uint32_t att = r4(r * hd) + 2 * r4(hd) + 2 * r4(hd / 2) + r4(r * ATT_CHUNK) + r4(NWAVE * ATT_MAX_R) +
                        3 * r4(ATT_MAX_R) + r4(r * hd) + r4(NT * 8) + (ATT_CHUNK * hd * esz + 3) / 4;
-  o.uni = std::max(NWAVE * RING_LINES * 256 + o.x, att);
+  o.uni = std::max(o.ring / 4 + o.x, att);
   o.bytes = 4 * (4 + 32 + NWAVE * 32 + o.res + o.uni);
   return o;
 }
+LdsLayout lds_layout(const mk_queue* q) { return lds_layout(q->cfg, q->plan); }
 
 // Everything the kernels need except the per-call inputs and outputs.
 void fill_args(const mk_queue* q, const void* d_queue, const mk_weights* w, const mk_kv* kv, void* d_workspace,
@@ -202,11 +216,16 @@ void fill_args(const mk_queue* q, const void* d_queue, const mk_weights* w, cons
   a.n_instr = (uint32_t)q->instr.size(); a.n_barriers = (uint32_t)q->targets.size();
   a.n_queues = (uint32_t)q->plan.n_queues;
   const LdsLayout ll = lds_layout(q);
-  a.lds_res = ll.res; a.lds_x = ll.x; a.lds_union = ll.uni; a.lds_bytes = ll.bytes;
+  a.lds_res = ll.res; a.lds_x = ll.x; a.lds_union = ll.uni; a.lds_bytes = ll.bytes; a.lds_ring = ll.ring;
+  a.M_cache = kv && kv->rows > 0 ? kv->rows : q->plan.rows;
+  a.lm_x = a.X + (size_t)c.n_layers * a.sX;
 }
 
 // Final RMSNorm + LM head GEMV (+ argmax) over the workspace's last hidden rows.
 hipError_t launch_lm(const Table& t, const Args& a, bool want_next, hipStream_t stream) {
+  // every buffer the LM-head kernels touch, and the staging offset past the ring
+  if (!a.lm_x || !a.lm_head || !a.final_norm || !a.lm_val || !a.lm_idx || !a.lds_ring || a.M < 1)
+    return hipErrorInvalidValue;
   hipError_t e = t.lm(a, stream);
   if (e == hipSuccess && want_next) {
     hipLaunchKernelGGL(argmax_kernel, dim3(a.M), dim3(NT), 0, stream, a);
@@ -278,6 +297,7 @@ mk_status mk_decode_step(const mk_queue* q, const void* d_queue, const mk_weight
     FAIL(MK_EINVAL, "missing weights or cache");
   if (c.qk_norm && (!w->q_norm || !w->k_norm)) FAIL(MK_EINVAL, "missing QK-norm gains");
   if (c.has_lm_head && (d_logits || d_next) && (!w->lm_head || !w->final_norm)) FAIL(MK_EINVAL, "missing LM head");
+  if (kv->rows != 0 && kv->rows != q->plan.rows) FAIL(MK_EINVAL, "decode cache rows must equal the batch");
 
   Args a{};
   fill_args(q, d_queue, w, kv, d_workspace, o, a);
@@ -333,8 +353,9 @@ mk_status mk_lm_head(const mk_queue* q, const mk_weights* w, void* d_workspace, 
   a.lm_val = reinterpret_cast<float*>(ws + o.LMV); a.lm_idx = reinterpret_cast<int*>(ws + o.LMI);
   a.lm_blocks = o.lm_blocks; a.err = reinterpret_cast<uint32_t*>(ws + o.ERR);
   a.r = c.n_q_heads / c.n_kv_heads; a.hd = c.head_dim;
+  a.lm_x = a.X + (size_t)c.n_layers * a.sX;
   const LdsLayout ll = lds_layout(q);
-  a.lds_res = ll.res; a.lds_x = ll.x; a.lds_union = ll.uni; a.lds_bytes = ll.bytes;
+  a.lds_res = ll.res; a.lds_x = ll.x; a.lds_union = ll.uni; a.lds_bytes = ll.bytes; a.lds_ring = ll.ring;
   a.logits = d_logits; a.next = d_next;
   const hipError_t e = launch_lm(pick_table(c.dtype, a.M), a, d_next != nullptr, stream);
   if (e != hipSuccess) FAIL(MK_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
@@ -345,11 +366,61 @@ mk_status mk_prefill(const mk_queue* q, const void* d_queue, const mk_weights* w
                      const int32_t* d_tokens, int32_t seq_len, int32_t kv_row, void* d_workspace,
                      size_t workspace_nbytes, float* d_logits_last, int32_t* d_next, int32_t exec_mode,
                      hipStream_t stream) {
-  (void)d_queue; (void)w; (void)kv; (void)d_tokens; (void)seq_len; (void)kv_row; (void)d_workspace;
-  (void)workspace_nbytes; (void)d_logits_last; (void)d_next; (void)exec_mode; (void)stream;
-  if (!q) FAIL(MK_EINVAL, "null argument");
+  if (!q || !d_queue || !w || !kv || !d_tokens || !d_workspace) FAIL(MK_EINVAL, "null argument");
   if (q->plan.mode != MK_PREFILL) FAIL(MK_EINVAL, "queue was not built for prefill");
-  FAIL(MK_ENOTSUP, "prefill op bodies are not built yet");
+  const mk_config& c = q->cfg;
+  if (mk_status st = check_shapes(c)) return st;
+  if (c.dtype != MK_BF16 || !c.has_embed) FAIL(MK_ENOTSUP, "prefill needs a bf16 model with an embedding");
+  if (c.head_dim != 128 || q->plan.bm != 128 || q->plan.bn != 128)
+    FAIL(MK_ENOTSUP, "prefill tiles are 128 x 128 over 128-wide heads");
+  if (c.hidden % 64 || c.ffn % 64 || (c.n_q_heads * c.head_dim) % 64) FAIL(MK_ENOTSUP, "prefill K dimensions must be multiples of 64");
+  if (seq_len < 1 || seq_len > q->plan.rows) FAIL(MK_EINVAL, "seq_len %d outside 1..%d", seq_len, q->plan.rows);
+  if (kv->rows < 1 || kv_row < 0 || kv_row >= kv->rows) FAIL(MK_EINVAL, "kv_row outside the cache rows");
+  if (exec_mode != MK_MEGAKERNEL && exec_mode != MK_KERNEL_PER_OP) FAIL(MK_EINVAL, "unknown exec_mode");
+  if (lds_layout(q).bytes > kMaxLds) FAIL(MK_ENOTSUP, "tiles need more shared memory than a workgroup has");
+  const Layout o = layout(q);
+  if (workspace_nbytes < o.total) FAIL(MK_EINVAL, "workspace of %zu bytes, need %zu", workspace_nbytes, o.total);
+  if (!w->wqkv || !w->wo || !w->wgate || !w->wup || !w->wdown || !w->attn_norm || !w->ffn_norm || !w->embed ||
+      !kv->k || !kv->v)
+    FAIL(MK_EINVAL, "missing weights or cache");
+  if (c.qk_norm && (!w->q_norm || !w->k_norm)) FAIL(MK_EINVAL, "missing QK-norm gains");
+  if ((d_logits_last || d_next) && (!c.has_lm_head || !w->lm_head || !w->final_norm)) FAIL(MK_EINVAL, "missing LM head");
+
+  Args a{};
+  fill_args(q, d_queue, w, kv, d_workspace, o, a);
+  a.tokens = d_tokens; a.seq_len = seq_len; a.kv_row = kv_row; a.M_cache = kv->rows;
+  a.spin_limit = g_opt.spin_limit;
+  a.trace = (g_opt.trace && g_opt.trace_bytes >= 32 * q->instr.size()) ? g_opt.trace : nullptr;
+  const Table t = table_prefill();
+  hipError_t e = hipSuccess;
+  if (exec_mode == MK_MEGAKERNEL) {
+    const int grid = num_cus() * g_opt.workers_per_cu;
+    if (grid < (int)a.n_queues) FAIL(MK_EINVAL, "fewer workers than sub-queues");
+    const uint32_t nr = a.n_barriers;
+    hipLaunchKernelGGL(reset_kernel, dim3((nr + 255) / 256 + 1), dim3(256), 0, stream, a.counters, nr, a.heads,
+                       a.n_queues, a.err);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = t.mega(a, grid, stream);
+  } else {
+    for (const mk::Segment& sg : q->segments) {
+      e = t.kpo(a, sg.op, sg.first, sg.count, stream);
+      if (e != hipSuccess) break;
+    }
+  }
+  if (e == hipSuccess && (d_logits_last || d_next)) {
+    // LM head on the last prompt position only
+    Args lm = a;
+    lm.M = 1;
+    mk_plan lp = q->plan;                 // the LM head's GEMV runs with the one-row decode layout
+    lp.mode = MK_DECODE; lp.rows = 1;
+    const LdsLayout ll = lds_layout(c, lp);
+    lm.lds_res = ll.res; lm.lds_x = ll.x; lm.lds_union = ll.uni; lm.lds_bytes = ll.bytes; lm.lds_ring = ll.ring;
+    lm.lm_x = a.X + (size_t)c.n_layers * a.sX + (size_t)(seq_len - 1) * c.hidden;
+    lm.logits = d_logits_last; lm.next = d_next;
+    e = launch_lm(pick_table(c.dtype, 1), lm, d_next != nullptr, stream);
+  }
+  if (e != hipSuccess) FAIL(MK_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return MK_OK;
 }
 
 mk_status mk_device_error(const mk_queue* q, const void* d_workspace, mk_dev_error* out, hipStream_t stream) {

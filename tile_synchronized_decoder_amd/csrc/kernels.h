@@ -79,6 +79,10 @@ struct Args {
   double rope_inv[64];
   // optional per-instruction trace: 4 x u64 per instruction (see mk.h)
   unsigned long long* trace;
+  // prefill: runtime prompt length, cache row written, rows of the cache allocation
+  int seq_len, kv_row, M_cache;
+  uint32_t lds_ring;             // bytes of the ring / prefill tile region
+  const float* lm_x;             // LM head input rows
 };
 
 // Device code reads the arguments in place, through a constant-address-space
@@ -191,21 +195,22 @@ __device__ __forceinline__ float4 ld_cg4(const float* p) {          // 16-byte a
 // Block until every barrier in the instruction's wait list reaches its target.
 // Threads poll disjoint subsets.  Returns false if the wait gave up (timeout or
 // another worker aborted).
+__device__ __forceinline__ bool poll_counter(KArgs& a, const uint32_t* ctr, uint32_t tgt, uint32_t idx, uint32_t id) {
+  uint32_t spins = 0, v;
+  while ((v = __hip_atomic_load(const_cast<uint32_t*>(ctr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < tgt) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins >= a.spin_limit) { record_error(a, ERR_TIMEOUT, idx, id, v, tgt); return false; }
+    if ((spins & 255) == 0 && aborted(a)) return false;
+  }
+  return true;
+}
+
 __device__ __forceinline__ bool wait_tiles(KArgs& a, const Instr in, uint32_t idx) {
   bool ok = true;
   for (uint32_t k = 0; k < in.wait_cnt; ++k) {
     const Range rg = a.ranges[in.wait_off + k];
-    for (uint32_t j = threadIdx.x; j < rg.count && ok; j += NT) {
-      const uint32_t id = rg.first + j;
-      const uint32_t tgt = a.targets[id];
-      uint32_t spins = 0;
-      uint32_t v;
-      while ((v = __hip_atomic_load(a.counters + id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < tgt) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins >= a.spin_limit) { record_error(a, ERR_TIMEOUT, idx, id, v, tgt); ok = false; break; }
-        if ((spins & 255) == 0 && aborted(a)) { ok = false; break; }
-      }
-    }
+    for (uint32_t j = threadIdx.x; j < rg.count && ok; j += NT)
+      ok = poll_counter(a, a.counters + rg.first + j, a.targets[rg.first + j], idx, rg.first + j);
   }
   const bool all = __syncthreads_and(ok) != 0;
   asm volatile("" ::: "memory");                 // no tile load may move above the wait
@@ -264,7 +269,7 @@ __device__ __forceinline__ Smem make_smem(KArgs& a) {
   s.res = s.ssw + NWAVE * 32;
   float* u = s.res + a.lds_res;
   s.ring = reinterpret_cast<uint8_t*>(u);
-  s.x = u + NWAVE * RING_LINES * 256;
+  s.x = u + a.lds_ring / 4;
   s.xcap = (int)a.lds_x;
   const int r = a.r, hd = a.hd;
   auto take = [&](int n) { float* p = u; u += (n + 3) & ~3; return p; };
@@ -839,23 +844,31 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
 
 // COMBINE(b, g): merge the NS split partials of row b, group g into ATT_l.
 template <int HD>
-__device__ __forceinline__ void op_combine(KArgs& a, const Instr in, uint32_t idx, bool mega) {
+__device__ __forceinline__ void op_combine(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
   const int l = in.layer, b = in.a0, g = in.a1, r = a.r;
   if (mega && !wait_tiles(a, in, idx)) return;
-  const size_t slot_sz = (size_t)(r * HD + 2 * r);
+  const int slot_sz = r * HD + 2 * r;
+  const int total = a.NS * slot_sz;
   const float* base = a.OPART + l * a.sOP + (size_t)(b * a.nkv + g) * a.NS * slot_sz;
   float* out = a.ATT + l * a.sATT + (size_t)b * a.NA + (size_t)g * r * HD;
+  // all split partials at once into shared memory (independent coherent loads)
+  const bool staged = total <= s.xcap;
+  if (staged) {
+    for (int e = threadIdx.x; e < total; e += NT) s.x[e] = ld_cg(base + e);
+    __syncthreads();
+  }
+  auto part = [&](int e) { return staged ? s.x[e] : ld_cg(base + e); };
   for (int o = threadIdx.x; o < r * HD; o += NT) {
     const int h = o / HD;
     float m = -INFINITY;
-    for (int sp = 0; sp < a.NS; ++sp) m = fmaxf(m, ld_cg(base + sp * slot_sz + r * HD + h));
+    for (int sp = 0; sp < a.NS; ++sp) m = fmaxf(m, part(sp * slot_sz + r * HD + h));
     float num = 0.f, den = 0.f;
     for (int sp = 0; sp < a.NS; ++sp) {
-      const float ms = ld_cg(base + sp * slot_sz + r * HD + h);
+      const float ms = part(sp * slot_sz + r * HD + h);
       if (ms == -INFINITY) continue;
       const float w = expf(ms - m);
-      num = fmaf(w, ld_cg(base + sp * slot_sz + o), num);
-      den = fmaf(w, ld_cg(base + sp * slot_sz + r * HD + r + h), den);
+      num = fmaf(w, part(sp * slot_sz + o), num);
+      den = fmaf(w, part(sp * slot_sz + r * HD + r + h), den);
     }
     st_cg(out + o, num / den);
   }
@@ -874,7 +887,7 @@ __device__ __forceinline__ void run_instr(KArgs& a, Smem& s, const Instr in, uin
       if (a.hd == 64) op_attn<WT, 64>(a, s, in, idx, mega); else op_attn<WT, 128>(a, s, in, idx, mega);
       break;
     case mk::OP_COMBINE:
-      if (a.hd == 64) op_combine<64>(a, in, idx, mega); else op_combine<128>(a, in, idx, mega);
+      if (a.hd == 64) op_combine<64>(a, s, in, idx, mega); else op_combine<128>(a, s, in, idx, mega);
       break;
     case mk::OP_OPROJ: op_oproj<WT, NB>(a, s, in, idx, mega); break;
     case mk::OP_GATEUP: op_gateup<WT, NB>(a, s, in, idx, mega); break;
@@ -952,7 +965,7 @@ __global__ __launch_bounds__(NT) void lm_head_kernel(Args args) {
   const WT* W = static_cast<const WT*>(a.lm_head);
   Gemv<WT, NB, RPW> g{W, W, n, v0, n, a.H};
   Instr none{};
-  gemv<WT, NB, RPW>(a, s, g, a.X + a.L * a.sX, a.M, a.final_norm, true, false, none, 0);
+  gemv<WT, NB, RPW>(a, s, g, a.lm_x, a.M, a.final_norm, true, false, none, 0);
   for (int e = threadIdx.x; e < n * a.M; e += NT) {
     const int row = e / a.M, b = e - row * a.M;
     if (a.logits) a.logits[(size_t)b * a.V + v0 + row] = s.res[row * NB + b];
@@ -979,6 +992,101 @@ inline hipError_t allow_lds(K kernel, uint32_t bytes, uint32_t& granted) {
   if (e == hipSuccess) granted = bytes;
   return e;
 }
+
+#ifdef MK_PREFILL_UNIT
+#include "prefill.h"
+
+__device__ __forceinline__ void run_prefill_instr(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega, int only_op) {
+  const int op = only_op ? only_op : in.op;
+  switch (op) {
+    case mk::OP_P_EMBED: op_p_embed(a, in, idx, mega); break;
+    case mk::OP_P_QKV: op_p_qkv(a, s, in, idx, mega); break;
+    case mk::OP_P_ATTN: op_p_attn(a, s, in, idx, mega); break;
+    case mk::OP_P_OPROJ: op_p_resid(a, s, in, idx, mega, false); break;
+    case mk::OP_P_GATEUP: op_p_gateup(a, s, in, idx, mega); break;
+    case mk::OP_P_DOWN: op_p_resid(a, s, in, idx, mega, true); break;
+    default:
+      if (threadIdx.x == 0) record_error(a, ERR_OPCODE, idx, in.op, 0, 0);
+      break;
+  }
+}
+
+// The prefill interpreter (bf16 models): same pop / wait / signal loop over the
+// prefill queue's 2-D tiles.
+__global__ __launch_bounds__(NT) void mk_interp_prefill(Args args) {
+  Smem s = make_smem(kernel_args());
+  const uint32_t qi = blockIdx.x % args.n_queues;
+  uint32_t k_next = 0;
+  if (threadIdx.x == 0) {
+    KArgs& a = kernel_args();
+    k_next = __hip_atomic_fetch_add(a.heads + qi * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  for (;;) {
+    KArgs& a = kernel_args();
+    if (threadIdx.x == 0) {
+      const uint64_t i = (uint64_t)k_next * a.n_queues + qi;
+      const bool go = i < a.n_instr && !aborted(a);
+      *s.idx = go ? (uint32_t)i : 0xFFFFFFFFu;
+      if (go) k_next = __hip_atomic_fetch_add(a.heads + qi * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    const uint32_t idx = __builtin_amdgcn_readfirstlane(*s.idx);
+    __syncthreads();
+    if (idx == 0xFFFFFFFFu) break;
+    unsigned long long t0 = 0;
+    if (a.trace) t0 = wall_clock64();
+    run_prefill_instr(a, s, load_instr(a, idx), idx, true, 0);
+    if (a.trace && threadIdx.x == 0) {
+      unsigned long long* rec = a.trace + 4 * (size_t)idx;
+      rec[0] = (unsigned long long)blockIdx.x << 32;
+      rec[1] = t0;
+      rec[3] = wall_clock64();
+    }
+  }
+}
+
+template <int OP>
+__global__ __launch_bounds__(NT) void kpo_prefill(Args args, uint32_t first) {
+  KArgs& a = kernel_args();
+  Smem s = make_smem(a);
+  const uint32_t idx = first + blockIdx.x;
+  const Instr in = load_instr(a, idx);
+  if (in.op != OP) {
+    if (threadIdx.x == 0) record_error(a, ERR_OPCODE, idx, in.op, 0, 0);
+    return;
+  }
+  run_prefill_instr(a, s, in, idx, false, OP);
+}
+
+struct PrefillLaunch {
+  static hipError_t mega(const Args& a, int grid, hipStream_t st) {
+    static uint32_t granted = 64 * 1024;
+    hipError_t e = allow_lds(mk_interp_prefill, a.lds_bytes, granted);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mk_interp_prefill, dim3(grid), dim3(NT), a.lds_bytes, st, a);
+    return hipGetLastError();
+  }
+  static hipError_t kpo(const Args& a, uint32_t op, uint32_t first, uint32_t count, hipStream_t st) {
+    static uint32_t granted[mk::OP_COUNT] = {};
+    switch (op) {
+#define KPO_CASE(OPC)                                                                              \
+      case OPC: {                                                                                  \
+        if (!granted[OPC]) granted[OPC] = 64 * 1024;                                               \
+        hipError_t e = allow_lds(kpo_prefill<OPC>, a.lds_bytes, granted[OPC]);                     \
+        if (e != hipSuccess) return e;                                                             \
+        hipLaunchKernelGGL((kpo_prefill<OPC>), dim3(count), dim3(NT), a.lds_bytes, st, a, first);  \
+        break;                                                                                     \
+      }
+      KPO_CASE(mk::OP_P_EMBED) KPO_CASE(mk::OP_P_QKV) KPO_CASE(mk::OP_P_ATTN) KPO_CASE(mk::OP_P_OPROJ)
+      KPO_CASE(mk::OP_P_GATEUP) KPO_CASE(mk::OP_P_DOWN)
+#undef KPO_CASE
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+};
+
+#endif  // MK_PREFILL_UNIT
 
 template <typename WT, int NB>
 struct Launch {

@@ -57,7 +57,7 @@ class DeviceKV:
 
 def upload_kv(K: np.ndarray, V: np.ndarray, device="cuda") -> DeviceKV:
     d = DeviceKV(_to_dev(K, device), _to_dev(V, device))
-    d.kv.k, d.kv.v = d.k.data_ptr(), d.v.data_ptr()
+    d.kv.k, d.kv.v, d.kv.rows = d.k.data_ptr(), d.v.data_ptr(), K.shape[1]
     return d
 
 
