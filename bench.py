@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--modes", default="mega,kpo,kpo_graph")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before the modes, copy MIB MiB device to device three times: a plain copy "
+                         "kernel of known size that hardware byte counters can be scaled by")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -150,6 +153,15 @@ def main():
             timing.append(torch.cuda.Event(enable_timing=True))
             timing[-1].record(stream)
         T.mk_lm_head(q, dm.w, ws, logits, nxt)
+
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration * 2 ** 20 // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 x {args.copy_calibration} MiB")
+        del src, dst
 
     results = {}
     modes = args.modes.split(",")
@@ -211,10 +223,14 @@ def main():
     step_bytes = mbytes + lm_head_bytes(m, B)
     roof = None
     if "layers_ms" in mega:
+        from tile_synchronized_decoder_amd.profiling import read_traffic
         ach = mbytes / (mega["layers_ms"] * 1e-3) / 1e9
+        # HBM bytes per launch counted by FETCH_SIZE / WRITE_SIZE in a separate profiled run of
+        # this workload (null when the kernel sources changed since)
+        traffic = read_traffic(os.path.join(ROOT, "profiles", f"mk_interp_{wl.name}_traffic.md"))
         roof = {"bound": "hbm", "kernel": "mk_interp (decoder layers, one launch per step)",
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": mbytes}
     line = {
         "metric": "decode tokens/s + step latency vs kernel-per-op; HBM GB/s as % of peak",

@@ -79,7 +79,8 @@ typedef struct mk_config {
  * attention split (decode); bm x bn the prefill GEMM tile (bn holds whole
  * heads).  rows: B for decode (1..32), S_max for prefill.  n_queues: workers
  * pop from n_queues sub-queues; instruction i belongs to sub-queue i mod
- * n_queues (1..64). */
+ * n_queues (1..1024; with as many sub-queues as workers the assignment of
+ * instructions to workers is static). */
 typedef struct mk_plan {
   int32_t mode, rows, ctx_max;
   int32_t tq, to, tf, td, kb, bm, bn;
@@ -200,10 +201,12 @@ enum {
   MK_OPT_WORKERS_PER_CU = 0,  /* megakernel workgroups per compute unit (default 1) */
   MK_OPT_SPIN_LIMIT = 1,      /* polls before a barrier wait gives up (default 1<<22) */
   MK_OPT_NUM_CUS = 2,         /* read-only: compute units of the current device */
-  /* Trace mode: a device buffer (value = its address) of at least 32 bytes per
-   * instruction.  While set, each megakernel instruction i writes 4 x u64 at
-   * offset 32*i: (workgroup << 32 | XCD id), pop time, time its waits ended,
-   * end time (device wall clock, 100 MHz).  Set the address to 0 to stop. */
+  /* Trace mode: a device buffer (value = its address) of at least 64 bytes per
+   * instruction.  While set, each megakernel instruction i writes 8 x u64 at
+   * offset 64*i: (workgroup << 32 | XCD id), pop time, time its waits ended,
+   * phase A (inputs staged), phase B (main loop done), end time, 0, 0 (device
+   * wall clock, 100 MHz; a phase an op does not have stays 0).  Set the
+   * address to 0 to stop. */
   MK_OPT_TRACE_BUFFER = 3,
   MK_OPT_TRACE_BYTES = 4
 };

@@ -58,7 +58,7 @@ OP_NAMES = {1: "EMBED", 2: "QKV", 3: "ATTN", 4: "COMBINE", 5: "OPROJ", 6: "GATEU
 # tensor kinds within a layer, in tensor order
 T_QKV, T_OPART, T_ATT, T_HRES, T_ACT, T_XNEXT = range(6)
 MAX_DECODE_ROWS = 32
-MAX_QUEUES = 64
+MAX_QUEUES = 1024
 
 
 class QueueError(ValueError):

@@ -82,7 +82,7 @@ def test_builder_bytes_prefill_qwen_shape():
 
 
 @pytest.mark.parametrize("kw", [dict(rows=0), dict(rows=33), dict(ctx_max=0), dict(tq=0), dict(kb=0),
-                                dict(n_queues=0), dict(n_queues=65)])
+                                dict(n_queues=0), dict(n_queues=1025)])
 def test_builder_rejects_what_the_reference_rejects(kw):
     plan = W.Plan(**{k: v for k, v in kw.items() if k in ("tq", "kb", "n_queues")})
     rows = kw.get("rows", 1)

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(NT) void argmax_kernel(Args args) {
 struct Options {
   int workers_per_cu = 1;
   uint32_t spin_limit = 1u << 22;
-  unsigned long long* trace = nullptr;   // device buffer, 32 bytes per instruction
+  unsigned long long* trace = nullptr;   // device buffer, 64 bytes per instruction
   size_t trace_bytes = 0;
 };
 Options g_opt;
@@ -304,7 +304,7 @@ mk_status mk_decode_step(const mk_queue* q, const void* d_queue, const mk_weight
   a.tokens = d_tokens; a.x0 = d_x0; a.ctx_lens = d_ctx_lens;
   a.logits = d_logits; a.next = d_next;
   a.spin_limit = g_opt.spin_limit;
-  a.trace = (g_opt.trace && g_opt.trace_bytes >= 32 * q->instr.size()) ? g_opt.trace : nullptr;
+  a.trace = (g_opt.trace && g_opt.trace_bytes >= 64 * q->instr.size()) ? g_opt.trace : nullptr;
 
   // without an embedding the input rows are copied into X_0 by the first launch
   if (!c.has_embed) {
@@ -390,7 +390,7 @@ mk_status mk_prefill(const mk_queue* q, const void* d_queue, const mk_weights* w
   fill_args(q, d_queue, w, kv, d_workspace, o, a);
   a.tokens = d_tokens; a.seq_len = seq_len; a.kv_row = kv_row; a.M_cache = kv->rows;
   a.spin_limit = g_opt.spin_limit;
-  a.trace = (g_opt.trace && g_opt.trace_bytes >= 32 * q->instr.size()) ? g_opt.trace : nullptr;
+  a.trace = (g_opt.trace && g_opt.trace_bytes >= 64 * q->instr.size()) ? g_opt.trace : nullptr;
   const Table t = table_prefill();
   hipError_t e = hipSuccess;
   if (exec_mode == MK_MEGAKERNEL) {

@@ -77,7 +77,7 @@ struct Args {
   uint32_t lds_res, lds_x, lds_union, lds_bytes;
   // rotary inverse frequencies theta^(-2i/hd), i < hd/2, computed in float64 on the host
   double rope_inv[64];
-  // optional per-instruction trace: 4 x u64 per instruction (see mk.h)
+  // optional per-instruction trace: TRACE_WORDS x u64 per instruction (see mk.h)
   unsigned long long* trace;
   // prefill: runtime prompt length, cache row written, rows of the cache allocation
   int seq_len, kv_row, M_cache;
@@ -159,6 +159,14 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // ----------------------------------------------------------------------------- barriers
 
+// Trace record of instruction idx: TRACE_WORDS x u64, (workgroup << 32 | XCD),
+// pop, waits ended, phase A, phase B, end (device wall clock).  Phase A / B
+// mark the op body's inner steps (inputs staged / main loop done).
+constexpr int TRACE_WORDS = 8;
+__device__ __forceinline__ void trace_mark(KArgs& a, uint32_t idx, int slot) {
+  if (a.trace && threadIdx.x == 0) a.trace[TRACE_WORDS * (size_t)idx + slot] = wall_clock64();
+}
+
 __device__ __forceinline__ bool aborted(KArgs& a) {
   return __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
 }
@@ -214,7 +222,7 @@ __device__ __forceinline__ bool wait_tiles(KArgs& a, const Instr in, uint32_t id
   }
   const bool all = __syncthreads_and(ok) != 0;
   asm volatile("" ::: "memory");                 // no tile load may move above the wait
-  if (a.trace && threadIdx.x == 0) a.trace[4 * (size_t)idx + 2] = wall_clock64();
+  trace_mark(a, idx, 2);
   return all;
 }
 
@@ -405,6 +413,7 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW>&
         __syncthreads();
         stage_x<NB>(s, x, K, nb, kc0, kcn, gain, norm && pass == 0, ssl);
         __syncthreads();
+        if (mega && !staged) trace_mark(a, idx, 3);
         staged = true;
       }
       const int it_begin = kc0 / 512, it_end = (kc0 + kcn + 511) / 512;
@@ -457,6 +466,7 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW>&
         if (lane == 0 && row < g.nrows && b < nb) s.res[row * NB + b] = v;
       }
   }
+  if (mega) trace_mark(a, idx, 4);
   if (norm) {
     // every thread staged a disjoint part of the rows: reduce sum(x^2) over the workgroup
 #pragma unroll
@@ -722,6 +732,7 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
       if (lane == 0) s.att.snew[h] = acc;
     }
   }
+  if (mega) trace_mark(a, idx, 3);
   // the chunk that holds pos gets the new value row from these threads
   const bool has_pos = j0 <= pos && pos < j1;
   const int pos_chunk = has_pos ? (pos - j0) / ATT_CHUNK : -1;
@@ -837,6 +848,7 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
     }
     __syncthreads();
   }
+  if (mega) trace_mark(a, idx, 4);
   for (int o = t; o < r * HD; o += NT) st_cg(slot + o, s.att.o[o]);
   if (t < r) { st_cg(slot + r * HD + t, s.att.m[t]); st_cg(slot + r * HD + r + t, s.att.l[t]); }
   if (mega) signal_tile(a, in);
@@ -857,6 +869,7 @@ __device__ __forceinline__ void op_combine(KArgs& a, Smem& s, const Instr in, ui
     for (int e = threadIdx.x; e < total; e += NT) s.x[e] = ld_cg(base + e);
     __syncthreads();
   }
+  if (mega) trace_mark(a, idx, 3);
   auto part = [&](int e) { return staged ? s.x[e] : ld_cg(base + e); };
   for (int o = threadIdx.x; o < r * HD; o += NT) {
     const int h = o / HD;
@@ -928,12 +941,12 @@ __global__ __launch_bounds__(NT) void mk_interp(Args args) {
     if (a.trace) t0 = wall_clock64();
     run_instr<WT, NB>(a, s, load_instr(a, idx), idx, true, 0);
     if (a.trace && threadIdx.x == 0) {
-      unsigned long long* rec = a.trace + 4 * (size_t)idx;
+      unsigned long long* rec = a.trace + TRACE_WORDS * (size_t)idx;
       uint32_t xcc;
       asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
       rec[0] = ((unsigned long long)blockIdx.x << 32) | (xcc & 0xF);
       rec[1] = t0;
-      rec[3] = wall_clock64();
+      rec[5] = wall_clock64();
     }
   }
 }
@@ -1037,10 +1050,10 @@ __global__ __launch_bounds__(NT) void mk_interp_prefill(Args args) {
     if (a.trace) t0 = wall_clock64();
     run_prefill_instr(a, s, load_instr(a, idx), idx, true, 0);
     if (a.trace && threadIdx.x == 0) {
-      unsigned long long* rec = a.trace + 4 * (size_t)idx;
+      unsigned long long* rec = a.trace + TRACE_WORDS * (size_t)idx;
       rec[0] = (unsigned long long)blockIdx.x << 32;
       rec[1] = t0;
-      rec[3] = wall_clock64();
+      rec[5] = wall_clock64();
     }
   }
 }

@@ -193,6 +193,7 @@ __device__ __forceinline__ bool p_gemm(KArgs& a, Smem& s, const PGemm& g, PAcc& 
     wait_vm<0>();
     __syncthreads();
   }
+  if (mega) trace_mark(a, idx, 4);
   // row scales: each row's two threads hold halves of sum(x^2)
   rs[t] = ss;
   __syncthreads();

@@ -16,7 +16,7 @@ enum Op : uint16_t {
 constexpr uint32_t kMagic = 0x314B4D54u;   // "TMK1"
 constexpr uint32_t kVersion = 1;
 constexpr int kMaxDecodeRows = 32;
-constexpr int kMaxQueues = 64;
+constexpr int kMaxQueues = 1024;
 
 struct Instr {            // 32 bytes, the INSTR record
   uint16_t op, layer;
