@@ -251,14 +251,16 @@ def decode_step(model: Model, K: np.ndarray, V: np.ndarray, ctx_lens: Sequence[i
     return tr
 
 
-def prefill(model: Model, K: np.ndarray, V: np.ndarray, tokens: np.ndarray, row: int = 0) -> Trace:
+def prefill(model: Model, K: np.ndarray, V: np.ndarray, tokens: Optional[np.ndarray] = None, row: int = 0,
+            x0: Optional[np.ndarray] = None) -> Trace:
     """Causal forward over S tokens of one sequence starting at position 0.
 
     Writes cache positions 0..S-1 of batch row ``row``; query i attends to keys
-    0..i.  Logits are returned for the last position only ([1, V]).
+    0..i.  Input rows are the embedding rows of ``tokens`` or, given instead,
+    ``x0`` [S, H].  Logits are returned for the last position only ([1, V]).
     """
     cfg = model.cfg
-    x = model.embed[np.asarray(tokens)]
+    x = model.embed[np.asarray(tokens)] if x0 is None else np.asarray(x0, dtype=np.float64)
     S = x.shape[0]
     tr = Trace()
     for l, lw in enumerate(model.layers):

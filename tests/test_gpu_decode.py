@@ -137,10 +137,10 @@ def _shrunk_1b(layers=2, vocab=4096, batch=1, ctx0=(1024,), steps=3):
                     name=f"llama1b_L{layers}_V{vocab}_B{batch}")
 
 
-@pytest.mark.parametrize("batch", [1, 4])
+@pytest.mark.parametrize("batch", [1, 4, 32])
 def test_bf16_shrunk_multistep_matches_oracle(batch):
     from _gpucase import make_case, log
-    ctx0 = tuple(1024 - 37 * b for b in range(batch))
+    ctx0 = tuple(1024 - 29 * b for b in range(batch))
     wl = _shrunk_1b(batch=batch, ctx0=ctx0)
     c = make_case(wl)
     model = c.oracle_model()

@@ -1,0 +1,240 @@
+"""GPU parity at the full benchmark shapes, on sampled outputs.
+
+The float64 oracle cannot run a whole 8B-shaped model step by step in a test,
+so each check feeds the GPU's own input rows of a sampled layer to the oracle's
+one-layer forward (with the cache contents the GPU step started from) and
+compares that layer's outputs; the LM head is checked on sampled vocabulary
+rows from the GPU's final hidden rows.  Every layer runs on the GPU in the
+launch configuration the benchmark times (default tiles, one sub-queue).
+
+Tolerance 2e-2 (bf16 models), as for the small cases.
+"""
+import dataclasses
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import tile_synchronized_decoder_amd as T
+from tile_synchronized_decoder_amd import device as D
+import workloads as W
+from oracle import numerics as N
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+TOL = 2e-2
+VOCAB_SAMPLE = 2048
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _log(*a):
+    from _gpucase import log
+    log(*a)
+
+
+def one_layer(m, raw_layer):
+    cfg1 = dataclasses.replace(m, n_layers=1, has_embed=False, has_lm_head=False, vocab=0)
+    return N.prepare(cfg1, [raw_layer], {})
+
+
+def rel_rows(got, ref):
+    return max(N.max_rel_err(got[b], ref[b]) for b in range(ref.shape[0]))
+
+
+def cache_layer(dkv: D.DeviceKV, l: int):
+    """Host copy of one layer of the device cache, [rows, nkv, ctx_max, hd] bf16 bits."""
+    return (dkv.k[l].cpu().numpy().view(np.uint16), dkv.v[l].cpu().numpy().view(np.uint16))
+
+
+def check_decode_layers(m, raw_layers, ws_tensor, before, dkv, ctx, layers):
+    """before[l] = (K, V) of layer l before the step."""
+    errs = {}
+    for l in layers:
+        x_in = ws_tensor(T.MK_T_X, l, m.hidden)
+        K0, V0 = before[l]
+        K, V = K0[None].copy(), V0[None].copy()
+        tr = N.decode_step(one_layer(m, raw_layers[l]), K, V, ctx, x0=x_in)
+        errs[f"att{l}"] = rel_rows(ws_tensor(T.MK_T_ATT, l, m.attn_cols), tr.attn[0])
+        errs[f"h{l}"] = rel_rows(ws_tensor(T.MK_T_HRES, l, m.hidden), tr.h[0])
+        errs[f"act{l}"] = rel_rows(ws_tensor(T.MK_T_ACT, l, m.ffn), tr.act[0])
+        errs[f"x{l + 1}"] = rel_rows(ws_tensor(T.MK_T_X, l + 1, m.hidden), tr.x_out)
+        Kg, Vg = cache_layer(dkv, l)
+        for b, p in enumerate(ctx):
+            errs[f"k{l}"] = max(errs.get(f"k{l}", 0.0), N.max_rel_err(N.to_f64(Kg[b, :, p]), N.to_f64(K[0, b, :, p])))
+            errs[f"v{l}"] = max(errs.get(f"v{l}", 0.0), N.max_rel_err(N.to_f64(Vg[b, :, p]), N.to_f64(V[0, b, :, p])))
+    return errs
+
+
+def check_lm_head(m, raw_global, x_last, logits, seed):
+    """Sampled vocabulary rows (plus each row's GPU argmax) against the oracle."""
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([rng.choice(m.vocab, VOCAB_SAMPLE, replace=False), np.argmax(logits, axis=1)]))
+    w = N.to_f64(raw_global["lm_head"][rows])
+    xn = N.rms_norm(x_last, N.to_f64(raw_global["final_norm"]), m.rms_eps)
+    ref = xn @ w.T
+    return rel_rows(logits[:, rows].astype(np.float64), ref)
+
+
+class Decoder:
+    """Device state of one decode workload at its full shape."""
+
+    def __init__(self, wl: W.Workload, raw_layers, raw_global, dm):
+        m, r = wl.model, wl.run
+        self.wl, self.m, self.r = wl, m, r
+        self.raw_layers, self.raw_global, self.dm = raw_layers, raw_global, dm
+        K, V = W.gen.kv_cache(m, r)
+        self.dkv = D.upload_kv(K, V)
+        del K, V
+        self.tokens = W.gen.decode_tokens(m, r)
+        self.q = T.mk_build_queue(T.make_config(m), T.make_plan(wl.plan, T.MK_DECODE, r.batch, r.ctx_max))
+        self.dq = D.upload_queue(self.q)
+        self.ws = D.workspace(self.q)
+        self.logits = torch.zeros((r.batch, m.vocab), dtype=torch.float32, device="cuda")
+        self.nxt = torch.zeros((r.batch,), dtype=torch.int32, device="cuda")
+
+    def ws_tensor(self, kind, layer, cols):
+        return D.ws_view(self.ws, self.q, kind, layer, (self.r.batch, cols)).cpu().numpy().astype(np.float64)
+
+    def step(self, t, mode):
+        ctx = [p + t for p in self.r.ctx0]
+        T.mk_decode_step(self.q, self.dq, self.dm.w, self.dkv.kv,
+                         torch.from_numpy(self.tokens[t].astype(np.int32)).cuda(), None,
+                         torch.tensor(ctx, dtype=torch.int32, device="cuda"), self.r.batch, self.ws,
+                         self.logits, self.nxt, mode)
+        torch.cuda.synchronize()
+        e = T.mk_device_error(self.q, self.ws)
+        assert e.code == 0, (e.code, e.instr, e.barrier, e.value, e.target)
+        return ctx
+
+    def check_step(self, t, layers, mode=T.MK_MEGAKERNEL):
+        before = {l: cache_layer(self.dkv, l) for l in layers}
+        ctx = self.step(t, mode)
+        errs = check_decode_layers(self.m, self.raw_layers, self.ws_tensor, before, self.dkv, ctx, layers)
+        lg = self.logits.cpu().numpy()
+        errs["logits"] = check_lm_head(self.m, self.raw_global, self.ws_tensor(T.MK_T_X, self.m.n_layers, self.m.hidden),
+                                       lg, seed=t)
+        assert np.array_equal(self.nxt.cpu().numpy(), N.argmax_lowest(lg))
+        worst = max(errs, key=errs.get)
+        _log(f"    {self.wl.name} step {t}: worst {worst} = {errs[worst]:.3e}")
+        assert errs[worst] <= TOL, errs
+
+
+_CACHE = {}
+
+
+def _weights(m, seed):
+    key = (m.name, seed)
+    if key not in _CACHE:
+        _CACHE.clear()
+        gc.collect()
+        torch.cuda.empty_cache()
+        raw_layers = W.gen.all_layer_weights(m, seed)
+        raw_global = W.gen.global_weights(m, seed)
+        _CACHE[key] = (raw_layers, raw_global, D.upload_weights(raw_layers, raw_global))
+    return _CACHE[key]
+
+
+@pytest.mark.parametrize("name", ["llama8b_b1", "llama8b_b4", "llama8b_b16"])
+def test_llama8b_decode_sampled_layers(name):
+    """Llama-3-8B shape at context 4096, batch 1 / 4 / 16: layers 0, 15, 31 and
+    the LM head of the first step; at batch 4 the kernel-per-op step is bit-identical."""
+    wl = W.WORKLOADS[name]
+    _log(f"[fullsize] {name}")
+    raw_layers, raw_global, dm = _weights(wl.model, wl.run.seed)
+    d = Decoder(wl, raw_layers, raw_global, dm)
+    d.check_step(0, [0, 15, 31])
+    if wl.run.batch == 4:
+        mega = (d.logits.cpu().numpy().copy(), d.ws_tensor(T.MK_T_X, 32, 4096))
+        # restore the cache entries step 0 wrote, then run the same step per op
+        K, V = W.gen.kv_cache(wl.model, wl.run)
+        d.dkv.k.copy_(torch.from_numpy(K.view(np.int16)))
+        d.dkv.v.copy_(torch.from_numpy(V.view(np.int16)))
+        del K, V
+        d.step(0, T.MK_KERNEL_PER_OP)
+        assert np.array_equal(d.logits.cpu().numpy(), mega[0])
+        assert np.array_equal(d.ws_tensor(T.MK_T_X, 32, 4096), mega[1])
+    del d
+    torch.cuda.empty_cache()
+
+
+def test_llama1b_stream_b32_sampled_layers():
+    """Batch 32 with per-sequence contexts U{256..8192}: two consecutive steps,
+    layers 0, 8, 15 and the LM head."""
+    wl = W.WORKLOADS["llama1b_stream_b32"]
+    _log(f"[fullsize] {wl.name} contexts {min(wl.run.ctx0)}..{max(wl.run.ctx0)}")
+    raw_layers, raw_global, dm = _weights(wl.model, wl.run.seed)
+    d = Decoder(wl, raw_layers, raw_global, dm)
+    for t in range(2):
+        d.check_step(t, [0, 8, 15])
+    del d
+    torch.cuda.empty_cache()
+
+
+def test_qwen8b_prefill_then_decode_sampled_layers():
+    """Qwen3-8B shape with QK-norm: prefill of 2048 tokens (layers 0 and 35 on all
+    rows, the last row's logits), then two decode steps on the cache it wrote."""
+    wl = W.WORKLOADS["qwen8b_prefill"]
+    m, r = wl.model, wl.run
+    S = r.prefill_len
+    _log(f"[fullsize] {wl.name} prefill {S}")
+    raw_layers, raw_global, dm = _weights(m, r.seed)
+    K, V = W.gen.kv_cache(m, r)                 # empty cache, one row
+    dkv = D.upload_kv(K, V)
+    tokens = W.gen.prefill_tokens(m, r)
+    qp = T.mk_build_queue(T.make_config(m), T.make_plan(wl.plan, T.MK_PREFILL, S, r.ctx_max))
+    dqp, wsp = D.upload_queue(qp), D.workspace(qp)
+    logits = torch.zeros((m.vocab,), dtype=torch.float32, device="cuda")
+    nxt = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    T.mk_prefill(qp, dqp, dm.w, dkv.kv, torch.from_numpy(tokens).cuda(), S, 0, wsp, logits, nxt, T.MK_MEGAKERNEL)
+    torch.cuda.synchronize()
+    e = T.mk_device_error(qp, wsp)
+    assert e.code == 0, (e.code, e.instr, e.barrier)
+
+    def wsp_tensor(kind, layer, cols):
+        return D.ws_view(wsp, qp, kind, layer, (S, cols)).cpu().numpy().astype(np.float64)
+
+    errs = {}
+    for l in (0, 35):
+        x_in = wsp_tensor(T.MK_T_X, l, m.hidden)
+        Kl = np.zeros((1, 1, m.n_kv_heads, r.ctx_max, m.head_dim), dtype=np.uint16)
+        Vl = np.zeros_like(Kl)
+        tr = N.prefill(one_layer(m, raw_layers[l]), Kl, Vl, x0=x_in, row=0)
+        errs[f"att{l}"] = N.max_rel_err(wsp_tensor(T.MK_T_ATT, l, m.attn_cols), tr.attn[0])
+        errs[f"h{l}"] = N.max_rel_err(wsp_tensor(T.MK_T_HRES, l, m.hidden), tr.h[0])
+        errs[f"act{l}"] = N.max_rel_err(wsp_tensor(T.MK_T_ACT, l, m.ffn), tr.act[0])
+        errs[f"x{l + 1}"] = N.max_rel_err(wsp_tensor(T.MK_T_X, l + 1, m.hidden), tr.x_out)
+        Kg, Vg = cache_layer(dkv, l)
+        errs[f"k{l}"] = N.max_rel_err(N.to_f64(Kg[0, :, :S]), N.to_f64(Kl[0, 0, :, :S]))
+        errs[f"v{l}"] = N.max_rel_err(N.to_f64(Vg[0, :, :S]), N.to_f64(Vl[0, 0, :, :S]))
+        _log(f"    prefill layer {l} checked")
+    lg = logits.cpu().numpy()[None, :]
+    errs["logits"] = check_lm_head(m, raw_global, wsp_tensor(T.MK_T_X, m.n_layers, m.hidden)[S - 1:S], lg, seed=7)
+    assert int(nxt.item()) == int(N.argmax_lowest(lg)[0])
+    worst = max(errs, key=errs.get)
+    _log(f"    prefill: worst {worst} = {errs[worst]:.3e}")
+    assert errs[worst] <= TOL, errs
+    del wsp
+    torch.cuda.empty_cache()
+
+    # decode on the prefilled cache (row 0), positions S, S + 1
+    wl_dec = dataclasses.replace(wl, run=dataclasses.replace(r, ctx0=(S,)))
+
+    class PrefilledDecoder(Decoder):
+        def __init__(self):
+            self.wl, self.m, self.r = wl_dec, m, wl_dec.run
+            self.raw_layers, self.raw_global, self.dm, self.dkv = raw_layers, raw_global, dm, dkv
+            self.tokens = W.gen.decode_tokens(m, wl_dec.run)
+            self.q = T.mk_build_queue(T.make_config(m), T.make_plan(wl.plan, T.MK_DECODE, 1, r.ctx_max))
+            self.dq, self.ws = D.upload_queue(self.q), D.workspace(self.q)
+            self.logits = torch.zeros((1, m.vocab), dtype=torch.float32, device="cuda")
+            self.nxt = torch.zeros((1,), dtype=torch.int32, device="cuda")
+
+    dd = PrefilledDecoder()
+    for t in range(2):
+        dd.check_step(t, [0, 35])

@@ -170,7 +170,7 @@ LdsLayout lds_layout(const mk_config& c, const mk_plan& p) {
   o.x = std::max<uint32_t>(std::min<uint32_t>(XBUF_MAX, nb * kmax), nb * 512);
   // keep the whole layout within one workgroup's shared memory: shrink the
   // input staging (it is consumed in chunks of nb * 512 floats)
-  o.ring = NWAVE * RING_LINES * 1024;
+  o.ring = NWAVE * ring_lines_for(nb) * 1024;
   const uint32_t fixed = 4 * (4 + 32 + NWAVE * 32 + o.res) + o.ring;
   const uint32_t room = fixed < kMaxLds ? (kMaxLds - fixed) / 4 : 0;
   if (o.x > room) o.x = std::max<uint32_t>(room / (nb * 512) * (nb * 512), nb * 512);

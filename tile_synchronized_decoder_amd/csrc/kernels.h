@@ -44,7 +44,10 @@ constexpr int ROWS_PER_PASS_MAX = 16;   // GEMV rows reduced per pass (4 waves x
 constexpr int ATT_MAX_R = 4;            // query heads per KV head
 constexpr int ATT_CHUNK = NT;           // keys scored per attention chunk
 constexpr int LM_ROWS = 96;             // vocabulary rows per LM-head workgroup
-constexpr int RING_LINES = 24;          // 1 KB weight lines in flight per wave
+// 1 KB weight lines in flight per wave: 24 (96 KB per workgroup); 12 at 32
+// input rows, where the staged inputs need the room (32 x 512 floats per chunk)
+template <int NB> constexpr int ring_lines() { return NB >= 32 ? 12 : 24; }
+constexpr int ring_lines_for(int nb) { return nb >= 32 ? 12 : 24; }
 constexpr uint32_t ERR_TIMEOUT = 1, ERR_OPCODE = 2, ERR_CONTEXT = 3, ERR_TOKEN = 4;
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
@@ -260,7 +263,7 @@ struct Smem {
   float* ss;       // per-row norm factors        [32]
   float* ssw;      // per-wave partial sums       [NWAVE * 32]
   float* res;      // GEMV results                [rows * NB]
-  uint8_t* ring;   // GEMV weight rings           [NWAVE][RING_LINES][1 KB]
+  uint8_t* ring;   // GEMV weight rings           [NWAVE][ring lines][1 KB]
   float* x;        // GEMV input staging          [xcap]
   int xcap;
   AttSmem att;
@@ -303,7 +306,7 @@ __device__ __forceinline__ Smem make_smem(KArgs& a) {
 // by direct global->LDS loads (no registers held while in flight).  Lines are
 // numbered in the order the wave consumes them; the ring is filled before the
 // instruction waits on its producer tiles, then refilled one line per line
-// consumed, so RING_LINES lines stay in flight per wave.
+// consumed, so the ring's lines stay in flight per wave.
 
 // Wait until at most N of this wave's vector-memory operations are outstanding.
 template <int N>
@@ -378,6 +381,7 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW>&
   const int npass = (g.nrows + G::ROWS - 1) / G::ROWS;
   const bool single_chunk = K <= kc_max;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  constexpr int RING_LINES = ring_lines<NB>();
   uint8_t* ring = s.ring + wave * RING_LINES * 1024;
   constexpr int GL = RPW * G::LPI;                     // lines per iteration group
   constexpr int NG = RING_LINES / GL;                  // groups in the ring
