@@ -133,8 +133,9 @@ def test_layer_fp32_batch_ragged_tiles_subqueues():
 
 def _shrunk_1b(layers=2, vocab=4096, batch=1, ctx0=(1024,), steps=3):
     base = W.WORKLOADS["llama1b_b1"]
-    return W.shrink(base, n_layers=layers, vocab=vocab, batch=batch, ctx0=ctx0, steps=steps,
-                    name=f"llama1b_L{layers}_V{vocab}_B{batch}")
+    wl = W.shrink(base, n_layers=layers, vocab=vocab, batch=batch, ctx0=ctx0, steps=steps,
+                  name=f"llama1b_L{layers}_V{vocab}_B{batch}")
+    return dataclasses.replace(wl, plan=W.Plan())         # one shared sub-queue, default tiles
 
 
 @pytest.mark.parametrize("batch", [1, 4, 32])
@@ -171,6 +172,30 @@ def test_bf16_shrunk_modes_bitwise_equal():
     for r in res[1:]:
         for a, b in zip(res[0], r):
             assert np.array_equal(a, b)
+
+
+def test_bf16_one_subqueue_per_worker():
+    """With as many sub-queues as workers every worker runs a fixed list of
+    instructions (no pops, records loaded one ahead); results match the oracle
+    and the kernel-per-op mode bit for bit, also with 256-tile GEMV ops."""
+    from _gpucase import make_case, log
+    ncu = T.mk_get_option(T.MK_OPT_NUM_CUS)
+    base = _shrunk_1b(batch=2, ctx0=(700, 1100), steps=2)
+    for tiles in (dict(), dict(tq=12, to=8, tf=32, td=8, kb=128)):
+        wl = dataclasses.replace(base, plan=dataclasses.replace(base.plan, n_queues=ncu, **tiles))
+        c = make_case(wl)
+        model = c.oracle_model()
+        K, V = c.K0.copy(), c.V0.copy()
+        for t in range(wl.run.steps):
+            ctx = [700 + t, 1100 + t]
+            tr = N.decode_step(model, K, V, ctx, tokens=c.tokens[t])
+            c.step(t, ctx, T.MK_MEGAKERNEL)
+            log(f"  tiles {tiles} step {t}")
+            check_step(c, tr, TOL_BF16)
+            mega = (c.logits.cpu().numpy().copy(), c.tensor(T.MK_T_X, 2, 2048))
+            c.step(t, ctx, T.MK_KERNEL_PER_OP)
+            assert np.array_equal(c.logits.cpu().numpy(), mega[0])
+            assert np.array_equal(c.tensor(T.MK_T_X, 2, 2048), mega[1])
 
 
 def test_bf16_separate_lm_head_matches_fused():

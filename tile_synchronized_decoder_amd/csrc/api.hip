@@ -151,15 +151,16 @@ constexpr uint32_t kPrefillGemmBytes = 2 * 128 * 128 + 2 * 256 * 128 + (256 + 12
 constexpr uint32_t kPrefillAttnBytes = 2 * 128 * 128 + 2 * 64 * 128 + 128 * 64 * 2 + 128 * 64 * 4 + 128 * 64 * 2 + 3 * 128 * 4;
 
 // Dynamic shared memory of one workgroup, in floats: header (index, norm
-// factors), GEMV results, then one region shared by the GEMV input staging and
-// the attention buffers.  Mirrors make_smem() in kernels.h.
+// factors), GEMV results, residual rows, then one region shared by the weight
+// ring plus GEMV input staging and the attention buffers.  Mirrors make_smem()
+// in kernels.h.
 LdsLayout lds_layout(const mk_config& c, const mk_plan& p) {
   LdsLayout o{};
   if (p.mode == MK_PREFILL) {
     // prefill tiles use the header and the tile region only
     o.ring = (std::max(kPrefillGemmBytes, kPrefillAttnBytes) + 255) & ~255u;
     o.uni = o.ring / 4;
-    o.bytes = 4 * (4 + 32 + NWAVE * 32) + o.ring;
+    o.bytes = 4 * (16 + 32 + NWAVE * 32) + o.ring;
     return o;
   }
   const uint32_t nb = nb_bucket(p.rows);
@@ -171,7 +172,7 @@ LdsLayout lds_layout(const mk_config& c, const mk_plan& p) {
   // keep the whole layout within one workgroup's shared memory: shrink the
   // input staging (it is consumed in chunks of nb * 512 floats)
   o.ring = NWAVE * ring_lines_for(nb) * 1024;
-  const uint32_t fixed = 4 * (4 + 32 + NWAVE * 32 + o.res) + o.ring;
+  const uint32_t fixed = 4 * (16 + 32 + NWAVE * 32 + 2 * o.res) + o.ring;
   const uint32_t room = fixed < kMaxLds ? (kMaxLds - fixed) / 4 : 0;
   if (o.x > room) o.x = std::max<uint32_t>(room / (nb * 512) * (nb * 512), nb * 512);
   o.x = r4(o.x);
@@ -180,7 +181,7 @@ LdsLayout lds_layout(const mk_config& c, const mk_plan& p) {
   const uint32_t att = r4(r * hd) + 2 * r4(hd) + 2 * r4(hd / 2) + r4(r * ATT_CHUNK) + r4(NWAVE * ATT_MAX_R) +
                        3 * r4(ATT_MAX_R) + r4(r * hd) + r4(NT * 8) + (ATT_CHUNK * hd * esz + 3) / 4;
   o.uni = std::max(o.ring / 4 + o.x, att);
-  o.bytes = 4 * (4 + 32 + NWAVE * 32 + o.res + o.uni);
+  o.bytes = 4 * (16 + 32 + NWAVE * 32 + 2 * o.res + o.uni);
   return o;
 }
 LdsLayout lds_layout(const mk_queue* q) { return lds_layout(q->cfg, q->plan); }
@@ -448,6 +449,7 @@ mk_status mk_set_option(int32_t key, int64_t value) {
     case MK_OPT_TRACE_BYTES:
       if (value < 0) FAIL(MK_EINVAL, "negative trace size");
       g_opt.trace_bytes = (size_t)value; return MK_OK;
+
     default: FAIL(MK_EINVAL, "unknown or read-only option %d", key);
   }
 }

@@ -43,7 +43,7 @@ constexpr int XBUF_MAX = 16384;         // LDS staging of GEMV inputs, upper bou
 constexpr int ROWS_PER_PASS_MAX = 16;   // GEMV rows reduced per pass (4 waves x 4)
 constexpr int ATT_MAX_R = 4;            // query heads per KV head
 constexpr int ATT_CHUNK = NT;           // keys scored per attention chunk
-constexpr int LM_ROWS = 96;             // vocabulary rows per LM-head workgroup
+constexpr int LM_ROWS = 64;             // vocabulary rows per LM-head workgroup
 // 1 KB weight lines in flight per wave: 24 (96 KB per workgroup); 12 at 32
 // input rows, where the staged inputs need the room (32 x 512 floats per chunk)
 template <int NB> constexpr int ring_lines() { return NB >= 32 ? 12 : 24; }
@@ -259,10 +259,11 @@ struct AttSmem {
   uint16_t* vbuf;  // value rows of the chunk     [ATT_CHUNK * hd] elements
 };
 struct Smem {
-  uint32_t* idx;   // popped instruction index
+  uint32_t* idx;   // [0] current instruction index, [8..15] its record
   float* ss;       // per-row norm factors        [32]
   float* ssw;      // per-wave partial sums       [NWAVE * 32]
   float* res;      // GEMV results                [rows * NB]
+  float* resid;    // residual rows of the tile   [rows * NB]
   uint8_t* ring;   // GEMV weight rings           [NWAVE][ring lines][1 KB]
   float* x;        // GEMV input staging          [xcap]
   int xcap;
@@ -275,10 +276,11 @@ __device__ __forceinline__ Smem make_smem(KArgs& a) {
   Smem s;
   float* base = mk_smem;
   s.idx = reinterpret_cast<uint32_t*>(base);
-  s.ss = base + 4;
+  s.ss = base + 16;
   s.ssw = s.ss + 32;
   s.res = s.ssw + NWAVE * 32;
-  float* u = s.res + a.lds_res;
+  s.resid = s.res + a.lds_res;
+  float* u = s.resid + a.lds_res;
   s.ring = reinterpret_cast<uint8_t*>(u);
   s.x = u + a.lds_ring / 4;
   s.xcap = (int)a.lds_x;
@@ -348,31 +350,68 @@ struct Gemv {
 };
 
 // Stage x[b][k0:k0+kn] * gain into LDS; accumulate sum(x^2) per row when asked.
+// The loads go out in batches of U per thread before any of them is used, so a
+// chunk costs one memory round trip rather than one per element.  `resid`
+// (nullable) adds s.resid[row * NB + b] = resid[b * resid_ld + row] for rows
+// < resid_rows; the first NT of them are loaded in the same round trip.
 template <int NB>
-__device__ __forceinline__ void stage_x(Smem& s, const float* x, int ldx, int nb, int k0, int kn, const float* gain, bool want_ss,
-                        float ss[NB]) {
+__device__ __forceinline__ void stage_x(Smem& s, const float* x, int ldx, int nb, int k0, int kn, const float* gain,
+                                        bool want_ss, float ss[NB], const float* resid, int resid_ld, int resid_rows) {
+  constexpr int U = 8;
+  const int t = threadIdx.x;
+  const bool has_r = resid && t < resid_rows * nb;
+  const int rrow = has_r ? t / nb : 0, rb = has_r ? t - rrow * nb : 0;
+  const float rv = has_r ? ld_cg(resid + (size_t)rb * resid_ld + rrow) : 0.f;
+  const int q4 = kn >> 2;                                // float4 per row (kn is a multiple of 8)
+  const int total = nb * q4;
+  for (int u0 = t; u0 < total; u0 += NT * U) {
+    float4 v[U], g[U];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    if (b >= nb) break;
-    for (int k = threadIdx.x * 4; k < kn; k += NT * 4) {
-      float4 v = ld_cg4(x + (size_t)b * ldx + k0 + k);
-      if (want_ss) ss[b] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-      if (gain) {
-        const float4 g = *reinterpret_cast<const float4*>(gain + k0 + k);
-        v.x *= g.x; v.y *= g.y; v.z *= g.z; v.w *= g.w;
+    for (int j = 0; j < U; ++j) {
+      const int u = u0 + j * NT;
+      if (u < total) {
+        const int b = u / q4, k = (u - b * q4) * 4;
+        v[j] = ld_cg4(x + (size_t)b * ldx + k0 + k);
+        if (gain) g[j] = *reinterpret_cast<const float4*>(gain + k0 + k);
       }
-      *reinterpret_cast<float4*>(s.x + b * kn + k) = v;
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int u = u0 + j * NT;
+      if (u < total) {
+        const int b = u / q4, k = (u - b * q4) * 4;
+        float4 w = v[j];
+        if (want_ss) {
+          const float sq = w.x * w.x + w.y * w.y + w.z * w.z + w.w * w.w;
+#pragma unroll
+          for (int bb = 0; bb < NB; ++bb) if (bb == b) ss[bb] += sq;
+        }
+        if (gain) { w.x *= g[j].x; w.y *= g[j].y; w.z *= g[j].z; w.w *= g[j].w; }
+        *reinterpret_cast<float4*>(s.x + b * kn + k) = w;
+      }
+    }
+  }
+  if (has_r) s.resid[rrow * NB + rb] = rv;
+  // residual values beyond one per thread (many input rows)
+  if (resid) {
+    for (int e = t + NT; e < resid_rows * nb; e += NT) {
+      const int row = e / nb, b = e - row * nb;
+      s.resid[row * NB + b] = ld_cg(resid + (size_t)b * resid_ld + row);
     }
   }
 }
 
 // Full GEMV of `nrows` rows against `nb` input rows of length K, results in
 // s.res[row * NB + b] (already scaled by the row's RMSNorm factor when `norm`).
-// When `mega`, the weight ring is filled before waiting on the instruction's
-// producer tiles.  Returns false when the wait gave up.
+// Each wave streams its rows' weight lines through its ring in consumption
+// order; the ring is filled before waiting on the instruction's producer tiles
+// and refilled one group per group consumed.  `resid` (nullable) is staged
+// with the inputs: s.resid[row * NB + b] = resid[b * resid_ld + row].
+// Returns false when the wait gave up.
 template <typename WT, int NB, int RPW>
 __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW>& g, const float* x, int nb,
-                     const float* gain, bool norm, bool mega, const Instr in, uint32_t idx) {
+                     const float* gain, bool norm, bool mega, const Instr in, uint32_t idx,
+                     const float* resid, int resid_ld) {
   using G = Gemv<WT, NB, RPW>;
   using E = Elem<WT>;
   const int K = g.K;
@@ -415,7 +454,8 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW>&
       const int kcn = min(kc_max, K - kc0);
       if (!(single_chunk && staged)) {
         __syncthreads();
-        stage_x<NB>(s, x, K, nb, kc0, kcn, gain, norm && pass == 0, ssl);
+        stage_x<NB>(s, x, K, nb, kc0, kcn, gain, norm && pass == 0, ssl, staged ? nullptr : resid, resid_ld,
+                    g.nrows);
         __syncthreads();
         if (mega && !staged) trace_mark(a, idx, 3);
         staged = true;
@@ -498,72 +538,76 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW>&
 
 template <int NB> constexpr int rpw_for() { return NB >= 16 ? 2 : 4; }
 
-// QKV(n0, n1): QKV_l[:, n0:n1] = RMSNorm(X_l) Wqkv[n0:n1]^T
+// The weight rows a GEMV instruction streams (op, layer, columns [a0, a1)),
+// or false for other ops.
 template <typename WT, int NB>
-__device__ __forceinline__ void op_qkv(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
-  constexpr int RPW = rpw_for<NB>();
+__device__ __forceinline__ bool gemv_of(KArgs& a, const Instr in, Gemv<WT, NB, rpw_for<NB>()>& g) {
   const int l = in.layer, n0 = in.a0, n = in.a1 - in.a0;
-  const WT* W = static_cast<const WT*>(a.wqkv) + (size_t)l * a.NQKV * a.H;
-  Gemv<WT, NB, RPW> g{W, W, n, n0, n, a.H};
-  if (!gemv<WT, NB, RPW>(a, s, g, a.X + l * a.sX, a.M, a.attn_norm + (size_t)l * a.H, true, mega, in, idx)) return;
-  float* out = a.QKV + l * a.sQKV;
-  for (int e = threadIdx.x; e < n * a.M; e += NT) {
-    const int row = e / a.M, b = e - row * a.M;
-    st_cg(out + (size_t)b * a.NQKV + n0 + row, s.res[row * NB + b]);
+  switch (in.op) {
+    case mk::OP_QKV: {
+      const WT* W = static_cast<const WT*>(a.wqkv) + (size_t)l * a.NQKV * a.H;
+      g = {W, W, n, n0, n, a.H};
+      return true;
+    }
+    case mk::OP_OPROJ: {
+      const WT* W = static_cast<const WT*>(a.wo) + (size_t)l * a.H * a.NA;
+      g = {W, W, n, n0, n, a.NA};
+      return true;
+    }
+    case mk::OP_GATEUP: {
+      const WT* Wg = static_cast<const WT*>(a.wgate) + (size_t)l * a.F * a.H;
+      const WT* Wu = static_cast<const WT*>(a.wup) + (size_t)l * a.F * a.H;
+      g = {Wg, Wu, n, n0, 2 * n, a.H};                  // rows >= n read the up matrix
+      return true;
+    }
+    case mk::OP_DOWN: {
+      const WT* W = static_cast<const WT*>(a.wdown) + (size_t)l * a.H * a.F;
+      g = {W, W, n, n0, n, a.F};
+      return true;
+    }
+    default:
+      return false;
   }
-  if (mega) signal_tile(a, in);
 }
 
-// OPROJ(n0, n1): HRES_l[:, n] = X_l[:, n] + ATT_l Wo[n]^T
+// The GEMV ops: QKV (RMSNorm(X_l) Wqkv^T), OPROJ (X_l + ATT_l Wo^T), GATEUP
+// (silu(RMSNorm(H) Wg^T) * (RMSNorm(H) Wu^T)) and DOWN (HRES_l + ACT_l Wd^T),
+// each over output columns [a0, a1).
 template <typename WT, int NB>
-__device__ __forceinline__ void op_oproj(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
+__device__ __forceinline__ void op_gemv(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
   constexpr int RPW = rpw_for<NB>();
+  using G = Gemv<WT, NB, RPW>;
   const int l = in.layer, n0 = in.a0, n = in.a1 - in.a0;
-  const WT* W = static_cast<const WT*>(a.wo) + (size_t)l * a.H * a.NA;
-  Gemv<WT, NB, RPW> g{W, W, n, n0, n, a.NA};
-  if (!gemv<WT, NB, RPW>(a, s, g, a.ATT + l * a.sATT, a.M, nullptr, false, mega, in, idx)) return;
-  const float* xr = a.X + l * a.sX;
-  float* out = a.HRES + l * a.sHRES;
-  for (int e = threadIdx.x; e < n * a.M; e += NT) {
-    const int row = e / a.M, b = e - row * a.M;
-    const size_t o = (size_t)b * a.H + n0 + row;
-    st_cg(out + o, ld_cg(xr + o) + s.res[row * NB + b]);
+  G g{};
+  gemv_of<WT, NB>(a, in, g);
+  const int op = in.op;
+  const float* x;
+  const float* gain = nullptr;
+  const float* resid = nullptr;
+  int ld = 0;
+  if (op == mk::OP_QKV) {
+    x = a.X + l * a.sX; gain = a.attn_norm + (size_t)l * a.H;
+  } else if (op == mk::OP_OPROJ) {
+    x = a.ATT + l * a.sATT; resid = a.X + l * a.sX + n0; ld = a.H;
+  } else if (op == mk::OP_GATEUP) {
+    x = a.HRES + l * a.sHRES; gain = a.ffn_norm + (size_t)l * a.H;
+  } else {
+    x = a.ACT + l * a.sACT; resid = a.HRES + l * a.sHRES + n0; ld = a.H;
   }
-  if (mega) signal_tile(a, in);
-}
-
-// GATEUP(n0, n1): ACT_l[:, n] = silu(RMSNorm(H) Wg[n]^T) * (RMSNorm(H) Wu[n]^T)
-template <typename WT, int NB>
-__device__ __forceinline__ void op_gateup(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
-  constexpr int RPW = rpw_for<NB>();
-  const int l = in.layer, n0 = in.a0, n = in.a1 - in.a0;
-  const WT* Wg = static_cast<const WT*>(a.wgate) + (size_t)l * a.F * a.H;
-  const WT* Wu = static_cast<const WT*>(a.wup) + (size_t)l * a.F * a.H;
-  Gemv<WT, NB, RPW> g{Wg, Wu, n, n0, 2 * n, a.H};      // rows >= n read the up matrix
-  if (!gemv<WT, NB, RPW>(a, s, g, a.HRES + l * a.sHRES, a.M, a.ffn_norm + (size_t)l * a.H, true, mega, in, idx)) return;
-  float* out = a.ACT + l * a.sACT;
-  for (int e = threadIdx.x; e < n * a.M; e += NT) {
-    const int row = e / a.M, b = e - row * a.M;
-    const float gt = s.res[row * NB + b], up = s.res[(n + row) * NB + b];
-    st_cg(out + (size_t)b * a.F + n0 + row, gt / (1.0f + expf(-gt)) * up);
-  }
-  if (mega) signal_tile(a, in);
-}
-
-// DOWN(n0, n1): X_{l+1}[:, n] = HRES_l[:, n] + ACT_l Wd[n]^T
-template <typename WT, int NB>
-__device__ __forceinline__ void op_down(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
-  constexpr int RPW = rpw_for<NB>();
-  const int l = in.layer, n0 = in.a0, n = in.a1 - in.a0;
-  const WT* W = static_cast<const WT*>(a.wdown) + (size_t)l * a.H * a.F;
-  Gemv<WT, NB, RPW> g{W, W, n, n0, n, a.F};
-  if (!gemv<WT, NB, RPW>(a, s, g, a.ACT + l * a.sACT, a.M, nullptr, false, mega, in, idx)) return;
-  const float* hr = a.HRES + l * a.sHRES;
-  float* out = a.X + (l + 1) * a.sX;
-  for (int e = threadIdx.x; e < n * a.M; e += NT) {
-    const int row = e / a.M, b = e - row * a.M;
-    const size_t o = (size_t)b * a.H + n0 + row;
-    st_cg(out + o, ld_cg(hr + o) + s.res[row * NB + b]);
+  if (!gemv<WT, NB, RPW>(a, s, g, x, a.M, gain, gain != nullptr, mega, in, idx, resid, ld)) return;
+  {
+    for (int e = threadIdx.x; e < n * a.M; e += NT) {
+      const int row = e / a.M, b = e - row * a.M;
+      if (op == mk::OP_QKV) {
+        st_cg(a.QKV + l * a.sQKV + (size_t)b * a.NQKV + n0 + row, s.res[row * NB + b]);
+      } else if (op == mk::OP_GATEUP) {
+        const float gt = s.res[row * NB + b], up = s.res[(n + row) * NB + b];
+        st_cg(a.ACT + l * a.sACT + (size_t)b * a.F + n0 + row, gt / (1.0f + expf(-gt)) * up);
+      } else {
+        float* out = op == mk::OP_OPROJ ? a.HRES + l * a.sHRES : a.X + (l + 1) * a.sX;
+        st_cg(out + (size_t)b * a.H + n0 + row, s.resid[row * NB + b] + s.res[row * NB + b]);
+      }
+    }
   }
   if (mega) signal_tile(a, in);
 }
@@ -655,10 +699,18 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
 
   // q (r heads), k, v of this row and group, then QK-norm and RoPE
   const float* qkv = a.QKV + l * a.sQKV + (size_t)b * a.NQKV;
-  for (int e = t; e < r * HD; e += NT) s.att.q[e] = ld_cg(qkv + g * r * HD + e);
-  if (t < HD) {
-    s.att.kn[t] = ld_cg(qkv + a.nq * HD + g * HD + t);
-    s.att.vn[t] = ld_cg(qkv + (a.nq + a.nkv) * HD + g * HD + t);
+  {
+    // all of this row's q, k and v loads in flight at once (r * HD <= 2 * NT)
+    float qv[2], kv = 0.f, vv = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) qv[j] = t + j * NT < r * HD ? ld_cg(qkv + g * r * HD + t + j * NT) : 0.f;
+    if (t < HD) {
+      kv = ld_cg(qkv + a.nq * HD + g * HD + t);
+      vv = ld_cg(qkv + (a.nq + a.nkv) * HD + g * HD + t);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) if (t + j * NT < r * HD) s.att.q[t + j * NT] = qv[j];
+    if (t < HD) { s.att.kn[t] = kv; s.att.vn[t] = vv; }
   }
   if (t < HALF) {
     // angle p * theta^(-2i/hd) in float64, reduced to [-pi, pi] in float64
@@ -870,7 +922,14 @@ __device__ __forceinline__ void op_combine(KArgs& a, Smem& s, const Instr in, ui
   // all split partials at once into shared memory (independent coherent loads)
   const bool staged = total <= s.xcap;
   if (staged) {
-    for (int e = threadIdx.x; e < total; e += NT) s.x[e] = ld_cg(base + e);
+    constexpr int U = 8;                                  // U loads per thread in flight at once
+    for (int e0 = threadIdx.x; e0 < total; e0 += NT * U) {
+      float v[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) if (e0 + j * NT < total) v[j] = ld_cg(base + e0 + j * NT);
+#pragma unroll
+      for (int j = 0; j < U; ++j) if (e0 + j * NT < total) s.x[e0 + j * NT] = v[j];
+    }
     __syncthreads();
   }
   if (mega) trace_mark(a, idx, 3);
@@ -899,16 +958,15 @@ __device__ __forceinline__ void run_instr(KArgs& a, Smem& s, const Instr in, uin
   const int op = only_op ? only_op : in.op;
   switch (op) {
     case mk::OP_EMBED: op_embed<WT>(a, in, mega); break;
-    case mk::OP_QKV: op_qkv<WT, NB>(a, s, in, idx, mega); break;
+    case mk::OP_QKV: case mk::OP_OPROJ: case mk::OP_GATEUP: case mk::OP_DOWN:
+      op_gemv<WT, NB>(a, s, in, idx, mega);
+      break;
     case mk::OP_ATTN:
       if (a.hd == 64) op_attn<WT, 64>(a, s, in, idx, mega); else op_attn<WT, 128>(a, s, in, idx, mega);
       break;
     case mk::OP_COMBINE:
       if (a.hd == 64) op_combine<64>(a, s, in, idx, mega); else op_combine<128>(a, s, in, idx, mega);
       break;
-    case mk::OP_OPROJ: op_oproj<WT, NB>(a, s, in, idx, mega); break;
-    case mk::OP_GATEUP: op_gateup<WT, NB>(a, s, in, idx, mega); break;
-    case mk::OP_DOWN: op_down<WT, NB>(a, s, in, idx, mega); break;
     default:
       if (threadIdx.x == 0) record_error(a, ERR_OPCODE, idx, in.op, 0, 0);
       break;
@@ -917,33 +975,63 @@ __device__ __forceinline__ void run_instr(KArgs& a, Smem& s, const Instr in, uin
 
 // The persistent interpreter: pop, decode, run (wait -> compute -> signal).
 // The pop of the next instruction is issued before the current one runs, so
-// its round trip overlaps the current instruction's loads.  Sub-queue q holds
+// its round trip overlaps the current instruction's loads; with one sub-queue
+// per worker there is nothing to pop.  Sub-queue q holds
 // instructions q, q + n_queues, ... in queue order; every sub-queue is a
 // subsequence of one topological order, so popping ahead cannot deadlock.
 template <typename WT, int NB>
 __global__ __launch_bounds__(NT) void mk_interp(Args args) {
   Smem s = make_smem(kernel_args());
-  const uint32_t qi = blockIdx.x % args.n_queues;
-  uint32_t k_next = 0;
-  if (threadIdx.x == 0) {
+  const uint32_t nq = args.n_queues;
+  const uint32_t qi = blockIdx.x % nq;
+  // One sub-queue per worker: the worker runs instructions qi, qi + nq, ... and
+  // needs no pops; each instruction's record is loaded one iteration ahead.
+  const bool fixed = nq == gridDim.x;
+  uint32_t k_next = 0;                           // thread 0 (shared sub-queues): popped position
+  uint32_t abort_seen = 0;                       // thread 0: error word, read one instruction ago
+  uint32_t word = 0;                             // lanes 0..7 (fixed): next record, in flight
+  if (threadIdx.x == 0 && !fixed) {
     KArgs& a = kernel_args();
     k_next = __hip_atomic_fetch_add(a.heads + qi * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  for (;;) {
+  if (fixed && threadIdx.x < 8 && qi < args.n_instr) {
     KArgs& a = kernel_args();
+    word = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.instr + qi) + threadIdx.x);
+  }
+  for (uint32_t it = 0;; ++it) {
+    KArgs& a = kernel_args();
+    const uint64_t fi = (uint64_t)qi + (uint64_t)it * nq;         // fixed order: this iteration's instruction
     if (threadIdx.x == 0) {
-      const uint64_t i = (uint64_t)k_next * a.n_queues + qi;
-      const bool go = i < a.n_instr && !aborted(a);
-      *s.idx = go ? (uint32_t)i : 0xFFFFFFFFu;
-      if (go) k_next = __hip_atomic_fetch_add(a.heads + qi * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t i = fixed ? fi : (uint64_t)k_next * nq + qi;
+      const bool go = i < a.n_instr && abort_seen == 0;
+      s.idx[0] = go ? (uint32_t)i : 0xFFFFFFFFu;
+      if (go && !fixed)
+        k_next = __hip_atomic_fetch_add(a.heads + qi * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // a worker that recorded an error stops the others at their next pop; the
+      // read's round trip overlaps this instruction
+      abort_seen = __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (fixed && threadIdx.x < 8) {
+      s.idx[8 + threadIdx.x] = word;             // this instruction's record, loaded an iteration ago
+      const uint64_t j = fi + nq;
+      word = j < a.n_instr ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.instr + j) + threadIdx.x) : 0u;
     }
     __syncthreads();
-    const uint32_t idx = __builtin_amdgcn_readfirstlane(*s.idx);   // uniform: keep the record in SGPRs
+    const uint32_t idx = __builtin_amdgcn_readfirstlane(s.idx[0]);   // uniform: keep the record in SGPRs
+    Instr in;
+    if (fixed) {
+      uint32_t w[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w[k] = __builtin_amdgcn_readfirstlane(s.idx[8 + k]);
+      in.op = (uint16_t)(w[0] & 0xFFFF); in.layer = (uint16_t)(w[0] >> 16);
+      in.a0 = w[1]; in.a1 = w[2]; in.a2 = w[3]; in.wait_off = w[4]; in.wait_cnt = w[5]; in.signal = w[6]; in.n_wait = w[7];
+    }
     __syncthreads();
     if (idx == 0xFFFFFFFFu) break;
+    if (!fixed) in = load_instr(a, idx);
     unsigned long long t0 = 0;
     if (a.trace) t0 = wall_clock64();
-    run_instr<WT, NB>(a, s, load_instr(a, idx), idx, true, 0);
+    run_instr<WT, NB>(a, s, in, idx, true, 0);
     if (a.trace && threadIdx.x == 0) {
       unsigned long long* rec = a.trace + TRACE_WORDS * (size_t)idx;
       uint32_t xcc;
@@ -953,6 +1041,7 @@ __global__ __launch_bounds__(NT) void mk_interp(Args args) {
       rec[5] = wall_clock64();
     }
   }
+  wait_vm<0>();                                  // no weight loads may outlive the workgroup
 }
 
 // One launch per (layer, op): workgroup i runs instruction first + i, no waits.
@@ -982,7 +1071,7 @@ __global__ __launch_bounds__(NT) void lm_head_kernel(Args args) {
   const WT* W = static_cast<const WT*>(a.lm_head);
   Gemv<WT, NB, RPW> g{W, W, n, v0, n, a.H};
   Instr none{};
-  gemv<WT, NB, RPW>(a, s, g, a.lm_x, a.M, a.final_norm, true, false, none, 0);
+  gemv<WT, NB, RPW>(a, s, g, a.lm_x, a.M, a.final_norm, true, false, none, 0, nullptr, 0);
   for (int e = threadIdx.x; e < n * a.M; e += NT) {
     const int row = e / a.M, b = e - row * a.M;
     if (a.logits) a.logits[(size_t)b * a.V + v0 + row] = s.res[row * NB + b];
@@ -997,6 +1086,139 @@ __global__ __launch_bounds__(NT) void lm_head_kernel(Args args) {
     }
     a.lm_val[(size_t)b * a.lm_blocks + blockIdx.x] = best;
     a.lm_idx[(size_t)b * a.lm_blocks + blockIdx.x] = v0 + bi;
+  }
+}
+
+// LM head for a few input rows (NB <= 4): the normalised rows sit in shared
+// memory and every lane streams its weight slices straight into registers,
+// 16 loads of 16 bytes in flight per lane, with many workgroups per compute
+// unit (no weight ring), so the vocabulary matrix streams at full bandwidth.
+// Wave w of workgroup i owns rows i * LM_ROWS + w * 16 .. + 16; per row a
+// lane sums its 8-column slices of every 512-column block, then the wave
+// reduces.  Same outputs as lm_head_kernel: logits and the block's (max,
+// lowest index) per input row.
+constexpr int LMF_RPW = LM_ROWS / NWAVE;      // rows per wave
+template <typename WT, int NB>
+__global__ __launch_bounds__(NT) void lm_head_regs(Args args) {
+  using E = Elem<WT>;
+  constexpr int VEC = E::VEC;
+  constexpr int RB = 4, UB = 4 / VEC;          // rows x 512-column blocks per batch of loads
+  KArgs& a = kernel_args();
+  extern __shared__ __align__(16) float lm_smem[];
+  float* xs = lm_smem;                         // [NB][H] = x * gain
+  float* red = lm_smem + NB * a.H;             // [NWAVE][NB] partial sums, then [NB] scales
+  float* bestv = red + NWAVE * NB + NB;        // [NWAVE][NB]
+  int* besti = reinterpret_cast<int*>(bestv + NWAVE * NB);
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int H = a.H, nb = a.M;
+  // stage the normalised input rows
+  float ss[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    ss[b] = 0.f;
+    if (b >= nb) continue;
+    for (int k = t * 4; k < H; k += NT * 4) {
+      float4 v = *reinterpret_cast<const float4*>(a.lm_x + (size_t)b * H + k);
+      const float4 g = *reinterpret_cast<const float4*>(a.final_norm + k);
+      ss[b] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      v.x *= g.x; v.y *= g.y; v.z *= g.z; v.w *= g.w;
+      *reinterpret_cast<float4*>(xs + b * H + k) = v;
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const float w = wave_sum(ss[b]);
+    if (lane == 0) red[wave * NB + b] = w;
+  }
+  __syncthreads();
+  if (t < nb) {
+    float tot = 0.f;
+    for (int w = 0; w < NWAVE; ++w) tot += red[w * NB + t];
+    red[NWAVE * NB + t] = 1.0f / sqrtf(tot / (float)H + a.eps);
+  }
+  __syncthreads();
+  float scale[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) scale[b] = b < nb ? red[NWAVE * NB + b] : 0.f;
+
+  const WT* W = static_cast<const WT*>(a.lm_head);
+  const int iters = (H + 511) / 512;
+  const int r0 = blockIdx.x * LM_ROWS + wave * LMF_RPW;
+  float bv[NB];
+  int bi[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) { bv[b] = -INFINITY; bi[b] = 0x7FFFFFFF; }
+  for (int jr = 0; jr < LMF_RPW; jr += RB) {
+    float acc[RB][NB];
+#pragma unroll
+    for (int j = 0; j < RB; ++j)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[j][b] = 0.f;
+    for (int it0 = 0; it0 < iters; it0 += UB) {
+      v4u w[RB][UB][VEC];
+#pragma unroll
+      for (int j = 0; j < RB; ++j) {
+        const int row = min(r0 + jr + j, a.V - 1);
+#pragma unroll
+        for (int u = 0; u < UB; ++u) {
+          const int col = (it0 + u) * 512 + lane * 8;
+          const v4u* p = reinterpret_cast<const v4u*>(W + (size_t)row * H + min(col, H - 8));
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) w[j][u][v] = __builtin_nontemporal_load(p + v);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int col = (it0 + u) * 512 + lane * 8;
+        if (col >= H) continue;
+        float xv[NB][8];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const float4 x0 = *reinterpret_cast<const float4*>(xs + b * H + col);
+          const float4 x1 = *reinterpret_cast<const float4*>(xs + b * H + col + 4);
+          xv[b][0] = x0.x; xv[b][1] = x0.y; xv[b][2] = x0.z; xv[b][3] = x0.w;
+          xv[b][4] = x1.x; xv[b][5] = x1.y; xv[b][6] = x1.z; xv[b][7] = x1.w;
+        }
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+          float wf[8];
+          E::unpack(w[j][u], wf);
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[j][b] = fmaf(wf[e], xv[b][e], acc[j][b]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      const int row = r0 + jr + j;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float v = wave_sum(acc[j][b]) * scale[b];
+        if (b < nb && row < a.V) {
+          if (lane == 0 && a.logits) a.logits[(size_t)b * a.V + row] = v;
+          if (v > bv[b]) { bv[b] = v; bi[b] = row; }        // rows ascend: the first maximum wins
+        }
+      }
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) { bestv[wave * NB + b] = bv[b]; besti[wave * NB + b] = bi[b]; }
+  }
+  __syncthreads();
+  if (t < nb) {
+    float best = bestv[t];
+    int bidx = besti[t];
+    for (int w = 1; w < NWAVE; ++w) {
+      const float v = bestv[w * NB + t];
+      const int i = besti[w * NB + t];
+      if (v > best || (v == best && i < bidx)) { best = v; bidx = i; }
+    }
+    a.lm_val[(size_t)t * a.lm_blocks + blockIdx.x] = best;
+    a.lm_idx[(size_t)t * a.lm_blocks + blockIdx.x] = bidx;
   }
 }
 
@@ -1133,6 +1355,14 @@ struct Launch {
     return hipGetLastError();
   }
   static hipError_t lm(const Args& a, hipStream_t st) {
+    if constexpr (NB <= 4) {
+      // normalised rows + per-wave partials in shared memory
+      const uint32_t bytes = 4u * (NB * a.H + NWAVE * NB + NB + 2 * NWAVE * NB);
+      if (a.H % 8 == 0 && bytes <= 64 * 1024) {
+        hipLaunchKernelGGL((lm_head_regs<WT, NB>), dim3(a.lm_blocks), dim3(NT), bytes, st, a);
+        return hipGetLastError();
+      }
+    }
     static uint32_t granted = 64 * 1024;
     hipError_t e = allow_lds(lm_head_kernel<WT, NB>, a.lds_bytes, granted);
     if (e != hipSuccess) return e;

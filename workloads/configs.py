@@ -127,7 +127,7 @@ WORKLOADS = {
     "llama1b_b1": Workload(
         "llama1b_b1", LLAMA_1B,
         RunConfig(batch=1, ctx0=(1024,), steps=128, ctx_max=1152, seed=2),
-        Plan(),
+        Plan(tf=32, td=8, n_queues=256),
         "Llama-3-1B-shaped bf16, batch 1, 128 decode steps from a 1024-token cache"),
     "llama8b_b1": Workload(
         "llama8b_b1", LLAMA_8B,
