@@ -177,9 +177,7 @@ LdsLayout lds_layout(const mk_config& c, const mk_plan& p) {
   if (o.x > room) o.x = std::max<uint32_t>(room / (nb * 512) * (nb * 512), nb * 512);
   o.x = r4(o.x);
   const uint32_t r = c.n_q_heads / c.n_kv_heads, hd = c.head_dim;
-  const uint32_t esz = c.dtype == MK_BF16 ? 2 : 4;
-  const uint32_t att = r4(r * hd) + 2 * r4(hd) + 2 * r4(hd / 2) + r4(r * ATT_CHUNK) + r4(NWAVE * ATT_MAX_R) +
-                       3 * r4(ATT_MAX_R) + r4(r * hd) + r4(NT * 8) + (ATT_CHUNK * hd * esz + 3) / 4;
+  const uint32_t att = r4(r * hd) + 2 * r4(hd) + 2 * r4(hd / 2) + 2 * r4(NWAVE * ATT_MAX_R) + r4(NWAVE * r * hd);
   o.uni = std::max(o.ring / 4 + o.x, att);
   o.bytes = 4 * (16 + 32 + NWAVE * 32 + 2 * o.res + o.uni);
   return o;

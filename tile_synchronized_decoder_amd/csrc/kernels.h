@@ -42,7 +42,6 @@ constexpr int NWAVE = NT / 64;
 constexpr int XBUF_MAX = 16384;         // LDS staging of GEMV inputs, upper bound (64 KB)
 constexpr int ROWS_PER_PASS_MAX = 16;   // GEMV rows reduced per pass (4 waves x 4)
 constexpr int ATT_MAX_R = 4;            // query heads per KV head
-constexpr int ATT_CHUNK = NT;           // keys scored per attention chunk
 constexpr int LM_ROWS = 64;             // vocabulary rows per LM-head workgroup
 // 1 KB weight lines in flight per wave: 24 (96 KB per workgroup); 12 at 32
 // input rows, where the staged inputs need the room (32 x 512 floats per chunk)
@@ -249,14 +248,9 @@ struct AttSmem {
   float* vn;       // new value, as stored        [hd]
   float* cs;       // rotary cos                  [hd / 2]
   float* sn;       // rotary sin                  [hd / 2]
-  float* p;        // probabilities of a chunk    [r * ATT_CHUNK]
-  float* red;      // cross-wave reductions       [NWAVE * ATT_MAX_R]
-  float* snew;     // scores of the new key       [ATT_MAX_R]
-  float* m;        // running max                 [ATT_MAX_R]
-  float* l;        // running sum                 [ATT_MAX_R]
-  float* o;        // running output              [r * hd]
-  float* part;     // PV partials per key slice   [NT * 8]
-  uint16_t* vbuf;  // value rows of the chunk     [ATT_CHUNK * hd] elements
+  float* p;        // per-wave sums               [NWAVE * ATT_MAX_R]
+  float* red;      // per-wave maxima             [NWAVE * ATT_MAX_R]
+  float* part;     // per-wave outputs            [NWAVE * r * hd]
 };
 struct Smem {
   uint32_t* idx;   // [0] current instruction index, [8..15] its record
@@ -291,14 +285,9 @@ __device__ __forceinline__ Smem make_smem(KArgs& a) {
   s.att.vn = take(hd);
   s.att.cs = take(hd / 2);
   s.att.sn = take(hd / 2);
-  s.att.p = take(r * ATT_CHUNK);
+  s.att.p = take(NWAVE * ATT_MAX_R);
   s.att.red = take(NWAVE * ATT_MAX_R);
-  s.att.snew = take(ATT_MAX_R);
-  s.att.m = take(ATT_MAX_R);
-  s.att.l = take(ATT_MAX_R);
-  s.att.o = take(r * hd);
-  s.att.part = take(NT * 8);
-  s.att.vbuf = reinterpret_cast<uint16_t*>(u);
+  s.att.part = take(NWAVE * r * hd);
   return s;
 }
 
@@ -632,38 +621,63 @@ __device__ __forceinline__ void op_embed(KArgs& a, const Instr in, bool mega) {
 
 // ----------------------------------------------------------------------------- attention
 
-__device__ __forceinline__ void block_reduce_heads(Smem& s, float v[ATT_MAX_R], int r, bool is_max) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-  for (int h = 0; h < ATT_MAX_R; ++h) {
-    if (h >= r) break;
-    const float w = is_max ? wave_max(v[h]) : wave_sum(v[h]);
-    if (lane == 0) s.att.red[wave * ATT_MAX_R + h] = w;
+// Cross-lane helpers for the attention tile: DPP moves within a 16-lane row,
+// lane permutes across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum over the LPK (8 or 16) lanes of an aligned lane group; every lane gets it.
+template <int LPK>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  v += dpp_mov<0xB1>(v);                 // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);                 // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);                // row_half_mirror
+  if constexpr (LPK == 16) v += dpp_mov<0x140>(v);   // row_mirror
+  return v;
+}
+// Combine the lanes that share (lane % LPK) across the 64 / LPK groups.
+template <int LPK, bool MAX>
+__device__ __forceinline__ float across_groups(float v) {
+  if constexpr (LPK == 8) {
+    const float w = dpp_mov<0x128>(v);   // row_ror:8 = lane ^ 8
+    v = MAX ? fmaxf(v, w) : v + w;
   }
-  __syncthreads();
 #pragma unroll
-  for (int h = 0; h < ATT_MAX_R; ++h) {
-    if (h >= r) break;
-    float t = s.att.red[h];
-    for (int w = 1; w < NWAVE; ++w) t = is_max ? fmaxf(t, s.att.red[w * ATT_MAX_R + h]) : t + s.att.red[w * ATT_MAX_R + h];
-    v[h] = t;
+  for (int o = 16; o < 64; o <<= 1) {
+    const float w = __shfl_xor(v, o, 64);
+    v = MAX ? fmaxf(v, w) : v + w;
   }
-  __syncthreads();
+  return v;
 }
 
 // ATTN(b, g, s): partial attention of the r query heads of KV group g of row b
 // over keys [s*kb, min((s+1)*kb, pos+1)), pos = ctx_lens[b].  Applies QK-norm
 // and RoPE to q and the new k, writes the new k / v into the cache (in the
 // split that holds pos), and stores (o, m, l) for the combine.
+// ATTN(b, g, s): partial attention of the r query heads of KV group g of row b
+// over keys [s * kb, min((s + 1) * kb, P_b + 1)), as (unnormalised o, max m,
+// sum l) per head.  Lane mapping: HD / 8 lanes share a key, each holding 8
+// of its dims, so a wave covers 64 / (HD / 8) keys per round and the
+// workgroup 4x that; the dot products reduce over the key's lanes with
+// shuffles, the softmax state lives in registers per key lane group, and the
+// groups and waves merge once at the end.  The cached rows of the first 8
+// rounds are loaded before the tile waits.
 template <typename KT, int HD>
 __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
   using E = Elem<KT>;
-  constexpr int KV4 = HD * (int)sizeof(KT) / 16;          // 16-byte words per cache row
   constexpr int HALF = HD / 2;
   constexpr int NROT = ((ATT_MAX_R + 1) * HALF + NT - 1) / NT;
+  constexpr int LPK = HD / 8;                       // lanes per key
+  constexpr int KPW = 64 / LPK;                     // keys per wave per round
+  constexpr int KPR = KPW * NWAVE;                  // keys per round
+  constexpr int RPC = 8;                            // rounds per chunk (held in registers)
+  constexpr int WPE = E::VEC;                       // 16-byte words per 8 elements
   const int l = in.layer, b = in.a0, g = in.a1, sp = in.a2;
   const int r = a.r;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int kk = lane / LPK, ds = lane % LPK;       // key of the lane in a round, its 8-dim slice
   const int pos_in = a.ctx_lens[b];
   // a position outside the cache is reported and the row treated as having no keys
   const bool bad_pos = pos_in < 0 || pos_in >= a.ctx_max;
@@ -673,20 +687,26 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
   const size_t head_off = (((size_t)l * a.M + b) * a.nkv + g) * (size_t)a.ctx_max;   // rows of this (l, b, g)
   KT* Kc = static_cast<KT*>(a.kc) + head_off * HD;
   KT* Vc = static_cast<KT*>(a.vc) + head_off * HD;
+  auto key_of = [&](int rd) { return j0 + rd * KPR + wave * KPW + kk; };
 
-  // prefetch this thread's cached key and value rows of the first chunk
-  v4u kr[KV4], vr[KV4];
-  {
-    const int j = j0 + t;
-    if (j < j1 && j < pos) {
-      const v4u* pk = reinterpret_cast<const v4u*>(Kc + (size_t)j * HD);
-      const v4u* pv = reinterpret_cast<const v4u*>(Vc + (size_t)j * HD);
+  // this lane's 8-dim slices of the cached keys / values of one chunk of rounds
+  v4u kr[RPC][WPE], vr[RPC][WPE];
+  auto load_chunk = [&](int c0) {
 #pragma unroll
-      for (int k = 0; k < KV4; ++k) kr[k] = __builtin_nontemporal_load(pk + k);
+    for (int rd = 0; rd < RPC; ++rd) {
+      const int j = key_of(c0 + rd);
+      if (j < j1 && j < pos) {
+        const v4u* pk = reinterpret_cast<const v4u*>(Kc + (size_t)j * HD + ds * 8);
+        const v4u* pv = reinterpret_cast<const v4u*>(Vc + (size_t)j * HD + ds * 8);
 #pragma unroll
-      for (int k = 0; k < KV4; ++k) vr[k] = __builtin_nontemporal_load(pv + k);
+        for (int w = 0; w < WPE; ++w) { kr[rd][w] = __builtin_nontemporal_load(pk + w); vr[rd][w] = __builtin_nontemporal_load(pv + w); }
+      } else {                                          // no cached row: zeros (its weight is 0, never NaN * 0)
+#pragma unroll
+        for (int w = 0; w < WPE; ++w) { kr[rd][w] = v4u{0u, 0u, 0u, 0u}; vr[rd][w] = v4u{0u, 0u, 0u, 0u}; }
+      }
     }
-  }
+  };
+  load_chunk(0);
   if (mega && !wait_tiles(a, in, idx)) return;
 
   float* slot = a.OPART + l * a.sOP + ((size_t)(b * a.nkv + g) * a.NS + sp) * (size_t)(r * HD + 2 * r);
@@ -723,7 +743,6 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
     s.att.cs[t] = cv;
     s.att.sn[t] = sv;
   }
-  for (int e = t; e < r * HD; e += NT) s.att.o[e] = 0.f;
   __syncthreads();
   if (a.qk_norm) {
     // per-head RMSNorm over HD: one wave per head (the r query heads, then k)
@@ -776,137 +795,134 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
     s.att.kn[t] = E::rounded(kq);
     s.att.vn[t] = E::rounded(vq);
   }
-  if (t < r) { s.att.m[t] = -INFINITY; s.att.l[t] = 0.f; }
   __syncthreads();
-  {
-    // scores of the new key (one wave per query head)
-    const int wave = t >> 6, lane = t & 63;
-    for (int h = wave; h < r; h += NWAVE) {
-      float acc = 0.f;
-      for (int d = lane; d < HD; d += 64) acc = fmaf(s.att.q[h * HD + d], s.att.kn[d], acc);
-      acc = wave_sum(acc);
-      if (lane == 0) s.att.snew[h] = acc;
-    }
-  }
   if (mega) trace_mark(a, idx, 3);
-  // the chunk that holds pos gets the new value row from these threads
-  const bool has_pos = j0 <= pos && pos < j1;
-  const int pos_chunk = has_pos ? (pos - j0) / ATT_CHUNK : -1;
-  const int pos_row = has_pos ? (pos - j0) % ATT_CHUNK : 0;
-  __syncthreads();
 
-  // PV work split: thread t sums a group of 8 output dims of one head over a
-  // strided slice of the chunk's keys
-  constexpr int G8 = HD / 8;                              // 8-dim groups per head
-  const int ngroups = r * G8;
-  const int nslice = NT / ngroups;                        // r * HD / 8 divides NT (checked on the host)
-  const int grp = t % ngroups, slc = t / ngroups;
-  const int gh = grp / G8, gd = (grp % G8) * 8;
-  const float scale = 1.0f / sqrtf((float)HD);
-
-  for (int c0 = j0; c0 < j1; c0 += ATT_CHUNK) {
-    const int j = c0 + t;
-    const bool valid = j < j1;
-    float sc[ATT_MAX_R], mx[ATT_MAX_R], sum[ATT_MAX_R];
+  // registers: the lane's query slices, the new key / value slices, softmax state
+  float qv[ATT_MAX_R][8], knv[8], vnv[8];
 #pragma unroll
-    for (int h = 0; h < ATT_MAX_R; ++h) sc[h] = 0.f;
-    if (has_pos && (c0 - j0) / ATT_CHUNK == pos_chunk && t < HD)
-      E::put(reinterpret_cast<KT*>(s.att.vbuf) + (size_t)pos_row * HD, t, s.att.vn[t]);
-    if (valid) {
-      KT* vrow = reinterpret_cast<KT*>(s.att.vbuf) + (size_t)t * HD;
+  for (int h = 0; h < ATT_MAX_R; ++h) {
+    const float4 q0 = h < r ? *reinterpret_cast<const float4*>(s.att.q + h * HD + ds * 8) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 q1 = h < r ? *reinterpret_cast<const float4*>(s.att.q + h * HD + ds * 8 + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    qv[h][0] = q0.x; qv[h][1] = q0.y; qv[h][2] = q0.z; qv[h][3] = q0.w;
+    qv[h][4] = q1.x; qv[h][5] = q1.y; qv[h][6] = q1.z; qv[h][7] = q1.w;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { knv[e] = s.att.kn[ds * 8 + e]; vnv[e] = s.att.vn[ds * 8 + e]; }
+  // scores are kept in log2 units (scaled by log2(e) / sqrt(HD)), so every
+  // exponential is one v_exp_f32; m is converted back to natural units at the end
+  constexpr float LOG2E = 1.4426950408889634f;
+  const float scale = LOG2E / sqrtf((float)HD);
+  float m_run[ATT_MAX_R], l_run[ATT_MAX_R], o_run[ATT_MAX_R][8];
+#pragma unroll
+  for (int h = 0; h < ATT_MAX_R; ++h) {
+    m_run[h] = -INFINITY; l_run[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o_run[h][e] = 0.f;
+  }
+  const int nrounds = (j1 - j0 + KPR - 1) / KPR;
+  for (int c0 = 0; c0 < nrounds; c0 += RPC) {
+    if (c0 > 0) load_chunk(c0);
+    float sc[RPC][ATT_MAX_R];
+#pragma unroll
+    for (int rd = 0; rd < RPC; ++rd) {
+      const int j = key_of(c0 + rd);
+      float kf[8];
+      E::unpack(kr[rd], kf);
       if (j == pos) {
 #pragma unroll
-        for (int h = 0; h < ATT_MAX_R; ++h)
-          if (h < r) sc[h] = s.att.snew[h];
-      } else {
-        if (c0 != j0) {
-          const v4u* pk = reinterpret_cast<const v4u*>(Kc + (size_t)j * HD);
-          const v4u* pv = reinterpret_cast<const v4u*>(Vc + (size_t)j * HD);
+        for (int e = 0; e < 8; ++e) kf[e] = knv[e];
+      }
 #pragma unroll
-          for (int k = 0; k < KV4; ++k) kr[k] = __builtin_nontemporal_load(pk + k);
+      for (int h = 0; h < ATT_MAX_R; ++h) {
+        float p = 0.f;
 #pragma unroll
-          for (int k = 0; k < KV4; ++k) vr[k] = __builtin_nontemporal_load(pv + k);
-        }
-#pragma unroll
-        for (int k = 0; k < KV4 / E::VEC; ++k) {
-          float kf[8];
-          E::unpack(&kr[k * E::VEC], kf);
-#pragma unroll
-          for (int h = 0; h < ATT_MAX_R; ++h) {
-            if (h < r) {
-              const float4 q0 = *reinterpret_cast<const float4*>(s.att.q + h * HD + 8 * k);
-              const float4 q1 = *reinterpret_cast<const float4*>(s.att.q + h * HD + 8 * k + 4);
-              float acc = sc[h];
-              acc = fmaf(q0.x, kf[0], acc); acc = fmaf(q0.y, kf[1], acc);
-              acc = fmaf(q0.z, kf[2], acc); acc = fmaf(q0.w, kf[3], acc);
-              acc = fmaf(q1.x, kf[4], acc); acc = fmaf(q1.y, kf[5], acc);
-              acc = fmaf(q1.z, kf[6], acc); acc = fmaf(q1.w, kf[7], acc);
-              sc[h] = acc;
-            }
-          }
-        }
-        v4u* dst = reinterpret_cast<v4u*>(vrow);
-#pragma unroll
-        for (int k = 0; k < KV4; ++k) dst[k] = vr[k];
+        for (int e = 0; e < 8; ++e) p = fmaf(qv[h][e], kf[e], p);
+        p = lane_group_sum<LPK>(p);
+        sc[rd][h] = (j < j1 && h < r) ? p * scale : -INFINITY;
       }
     }
 #pragma unroll
     for (int h = 0; h < ATT_MAX_R; ++h) {
-      sc[h] = (valid && h < r) ? sc[h] * scale : -INFINITY;
-      mx[h] = sc[h];
+      float mc = sc[0][h];
+#pragma unroll
+      for (int rd = 1; rd < RPC; ++rd) mc = fmaxf(mc, sc[rd][h]);
+      const float mnew = fmaxf(m_run[h], mc);
+      const float al = m_run[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[h] - mnew);
+      l_run[h] *= al;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o_run[h][e] *= al;
+      m_run[h] = mnew;
     }
-    block_reduce_heads(s, mx, r, true);
+#pragma unroll
+    for (int rd = 0; rd < RPC; ++rd) {
+      const int j = key_of(c0 + rd);
+      float vf[8];
+      E::unpack(vr[rd], vf);
+      if (j == pos) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vf[e] = vnv[e];
+      }
+#pragma unroll
+      for (int h = 0; h < ATT_MAX_R; ++h) {
+        const float p = sc[rd][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[rd][h] - m_run[h]);
+        l_run[h] += p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o_run[h][e] = fmaf(p, vf[e], o_run[h][e]);
+      }
+    }
+  }
+  if (mega) trace_mark(a, idx, 4);
+
+  // merge the key lane groups of the wave (lanes with the same slice ds)
+#pragma unroll
+  for (int h = 0; h < ATT_MAX_R; ++h) {
+    const float M = across_groups<LPK, true>(m_run[h]);
+    const float f = m_run[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[h] - M);
+    const float L = across_groups<LPK, false>(l_run[h] * f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o_run[h][e] = across_groups<LPK, false>(o_run[h][e] * f);
+    m_run[h] = M; l_run[h] = L;
+  }
+  // then the waves, through shared memory
+  float* wo = s.att.part;                                 // [NWAVE][r * HD]
+  float* wm = s.att.red;                                  // [NWAVE][ATT_MAX_R]
+  float* wl = s.att.p;                                    // [NWAVE][ATT_MAX_R]
+  if (kk == 0) {
 #pragma unroll
     for (int h = 0; h < ATT_MAX_R; ++h) {
       if (h >= r) break;
-      const float mnew = fmaxf(s.att.m[h], mx[h]);
-      const float pr = valid ? expf(sc[h] - mnew) : 0.f;
-      s.att.p[h * ATT_CHUNK + t] = pr;
-      sum[h] = pr;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wo[wave * r * HD + h * HD + ds * 8 + e] = o_run[h][e];
     }
-    block_reduce_heads(s, sum, r, false);      // its barriers also publish p and the value rows
-    // PV partials: 8 dims of head gh over keys slc, slc + nslice, ...
-    const int nvalid = min(ATT_CHUNK, j1 - c0);
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    const float* ph = s.att.p + gh * ATT_CHUNK;
-    for (int jj = slc; jj < nvalid; jj += nslice) {
-      const float pj = ph[jj];
-      const KT* vrow = reinterpret_cast<const KT*>(s.att.vbuf) + (size_t)jj * HD + gd;
-      float vf[8];
-      E::unpack(reinterpret_cast<const v4u*>(vrow), vf);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(pj, vf[e], acc[e]);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s.att.part[slc * (r * HD) + grp * 8 + e] = acc[e];
-    __syncthreads();
-    for (int o = t; o < r * HD; o += NT) {
-      const int h = o / HD;
-      float tot = 0.f;
-      for (int k = 0; k < nslice; ++k) tot += s.att.part[k * (r * HD) + o];
-      float mxh = 0.f;
-#pragma unroll
-      for (int hh = 0; hh < ATT_MAX_R; ++hh) if (hh == h) mxh = mx[hh];
-      const float mold = s.att.m[h];
-      s.att.o[o] = s.att.o[o] * expf(mold - fmaxf(mold, mxh)) + tot;
-    }
-    __syncthreads();
-    if (t < r) {
-      float mxt = 0.f, st = 0.f;
-#pragma unroll
-      for (int hh = 0; hh < ATT_MAX_R; ++hh) if (hh == t) { mxt = mx[hh]; st = sum[hh]; }
-      const float mold = s.att.m[t];
-      const float mnew = fmaxf(mold, mxt);
-      s.att.l[t] = s.att.l[t] * expf(mold - mnew) + st;
-      s.att.m[t] = mnew;
-    }
-    __syncthreads();
   }
-  if (mega) trace_mark(a, idx, 4);
-  for (int o = t; o < r * HD; o += NT) st_cg(slot + o, s.att.o[o]);
-  if (t < r) { st_cg(slot + r * HD + t, s.att.m[t]); st_cg(slot + r * HD + r + t, s.att.l[t]); }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < ATT_MAX_R; ++h) { wm[wave * ATT_MAX_R + h] = m_run[h]; wl[wave * ATT_MAX_R + h] = l_run[h]; }
+  }
+  __syncthreads();
+  for (int o = t; o < r * HD; o += NT) {
+    const int h = o / HD;
+    float M = wm[h];
+    for (int w = 1; w < NWAVE; ++w) M = fmaxf(M, wm[w * ATT_MAX_R + h]);
+    float num = 0.f;
+    for (int w = 0; w < NWAVE; ++w) {
+      const float mw = wm[w * ATT_MAX_R + h];
+      if (mw != -INFINITY) num = fmaf(__builtin_amdgcn_exp2f(mw - M), wo[w * r * HD + o], num);
+    }
+    st_cg(slot + o, num);
+  }
+  if (t < r) {
+    float M = wm[t];
+    for (int w = 1; w < NWAVE; ++w) M = fmaxf(M, wm[w * ATT_MAX_R + t]);
+    float L = 0.f;
+    for (int w = 0; w < NWAVE; ++w) {
+      const float mw = wm[w * ATT_MAX_R + t];
+      if (mw != -INFINITY) L = fmaf(__builtin_amdgcn_exp2f(mw - M), wl[w * ATT_MAX_R + t], L);
+    }
+    st_cg(slot + r * HD + t, M * 0.6931471805599453f);          // back to natural units
+    st_cg(slot + r * HD + r + t, L);
+  }
   if (mega) signal_tile(a, in);
 }
 
