@@ -525,12 +525,15 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW>&
   return true;
 }
 
+// Rows per wave per pass: 4 (16-row passes) for a few input rows, 2 for many
+// (register pressure).  Tiles of at most 8 rows always use 2, so no wave
+// streams placeholder rows.
 template <int NB> constexpr int rpw_for() { return NB >= 16 ? 2 : 4; }
 
 // The weight rows a GEMV instruction streams (op, layer, columns [a0, a1)),
 // or false for other ops.
-template <typename WT, int NB>
-__device__ __forceinline__ bool gemv_of(KArgs& a, const Instr in, Gemv<WT, NB, rpw_for<NB>()>& g) {
+template <typename WT, int NB, int RPW>
+__device__ __forceinline__ bool gemv_of(KArgs& a, const Instr in, Gemv<WT, NB, RPW>& g) {
   const int l = in.layer, n0 = in.a0, n = in.a1 - in.a0;
   switch (in.op) {
     case mk::OP_QKV: {
@@ -562,13 +565,12 @@ __device__ __forceinline__ bool gemv_of(KArgs& a, const Instr in, Gemv<WT, NB, r
 // The GEMV ops: QKV (RMSNorm(X_l) Wqkv^T), OPROJ (X_l + ATT_l Wo^T), GATEUP
 // (silu(RMSNorm(H) Wg^T) * (RMSNorm(H) Wu^T)) and DOWN (HRES_l + ACT_l Wd^T),
 // each over output columns [a0, a1).
-template <typename WT, int NB>
-__device__ __forceinline__ void op_gemv(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
-  constexpr int RPW = rpw_for<NB>();
+template <typename WT, int NB, int RPW>
+__device__ __forceinline__ void op_gemv_rpw(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
   using G = Gemv<WT, NB, RPW>;
   const int l = in.layer, n0 = in.a0, n = in.a1 - in.a0;
   G g{};
-  gemv_of<WT, NB>(a, in, g);
+  gemv_of<WT, NB, RPW>(a, in, g);
   const int op = in.op;
   const float* x;
   const float* gain = nullptr;
@@ -599,6 +601,16 @@ __device__ __forceinline__ void op_gemv(KArgs& a, Smem& s, const Instr in, uint3
     }
   }
   if (mega) signal_tile(a, in);
+}
+
+template <typename WT, int NB>
+__device__ __forceinline__ void op_gemv(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
+  constexpr int RPW = rpw_for<NB>();
+  const int rows = (in.op == mk::OP_GATEUP ? 2 : 1) * (int)(in.a1 - in.a0);
+  if constexpr (RPW != 2) {
+    if (rows <= 2 * NWAVE) { op_gemv_rpw<WT, NB, 2>(a, s, in, idx, mega); return; }
+  }
+  op_gemv_rpw<WT, NB, RPW>(a, s, in, idx, mega);
 }
 
 // EMBED(n0, n1): X_0[b, n0:n1] = E[token_b, n0:n1]
