@@ -54,6 +54,17 @@ def megakernel_bytes(m, ctx) -> int:
     return m.n_layers * layer_bytes(m) + emb + kv_read + kv_write
 
 
+def prefill_flops(m, S) -> int:
+    """Matrix FLOPs of a causal prefill of S tokens: the layer GEMMs, the causal
+    attention products (QK^T and PV over keys 0..i), and the LM head on the last row."""
+    mats = m.qkv_cols * m.hidden + m.hidden * m.attn_cols + 3 * m.ffn * m.hidden
+    attn = 4 * m.n_q_heads * m.head_dim * S * (S + 1) // 2
+    return m.n_layers * (2 * S * mats + attn) + (2 * m.vocab * m.hidden if m.has_lm_head else 0)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
 def lm_head_bytes(m, B) -> int:
     wb = 2 if m.dtype == "bf16" else 4
     return m.vocab * m.hidden * wb + m.hidden * 4 + 4 * B * m.vocab if m.has_lm_head else 0
@@ -133,6 +144,41 @@ def main():
     dkv = D.upload_kv(Kh, Vh)
     ws = D.workspace(q)
     B = r.batch
+    prefill_res = None
+    if r.prefill_len:
+        # causal prefill of the prompt into the (empty) cache, timed per call in both modes;
+        # the decode steps below continue from the cache the last call wrote
+        S = r.prefill_len
+        qp = T.mk_build_queue(T.make_config(m), T.make_plan(wl.plan, T.MK_PREFILL, S, r.ctx_max))
+        dqp, wsp = D.upload_queue(qp), D.workspace(qp)
+        ptok = torch.from_numpy(W.gen.prefill_tokens(m, r)).cuda()
+        plg = torch.empty((m.vocab,), dtype=torch.float32, device="cuda")
+        pnx = torch.empty((1,), dtype=torch.int32, device="cuda")
+        prefill_res = {"tokens": S, "flops": prefill_flops(m, S), "modes": {}}
+        for name in ("mega", "kpo"):
+            mode = T.MK_MEGAKERNEL if name == "mega" else T.MK_KERNEL_PER_OP
+            for _ in range(2):
+                T.mk_prefill(qp, dqp, dm.w, dkv.kv, ptok, S, 0, wsp, plg, pnx, mode)
+            torch.cuda.synchronize()
+            n_runs = 5
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(torch.cuda.current_stream())
+            for _ in range(n_runs):
+                T.mk_prefill(qp, dqp, dm.w, dkv.kv, ptok, S, 0, wsp, plg, pnx, mode)
+            e1.record(torch.cuda.current_stream())
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / n_runs
+            err = T.mk_device_error(qp, wsp)
+            assert err.code == 0, f"device error {err.code} in prefill mode {name}"
+            tf = prefill_res["flops"] / (ms * 1e-3) / 1e12
+            prefill_res["modes"][name] = {"ms": round(ms, 4), "tokens_per_s": round(S / (ms * 1e-3), 1),
+                                          "tflops": round(tf, 1)}
+            log(f"[bench] prefill {name}: {ms:.3f} ms, {tf:.1f} TFLOP/s")
+        best = prefill_res["modes"]["mega"]["tflops"]
+        prefill_res["roofline"] = {"bound": "mfma", "achieved": best, "peak": MFMA_BF16_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(best / MFMA_BF16_PEAK_TFLOPS, 4),
+                                   "traffic": None}
+        del wsp
     tok_all = torch.from_numpy(tokens.astype(np.int32)).cuda()                       # [steps, B]
     ctx_all = torch.tensor([[p + t for p in r.ctx0] for t in range(r.steps)], dtype=torch.int32,
                            device="cuda")
@@ -248,6 +294,8 @@ def main():
                   for k, v in results.items()},
         "roofline": roof,
     }
+    if prefill_res is not None:
+        line["prefill"] = prefill_res
     if "kpo" in results or "kpo_graph" in results:
         best = min(v["ms_per_step"] for k, v in results.items() if k.startswith("kpo"))
         line["megakernel_speedup_vs_best_kpo"] = round(best / mega["ms_per_step"], 4)

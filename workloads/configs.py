@@ -110,6 +110,11 @@ QWEN_8B = ModelConfig(
     head_dim=128, ffn=12288, vocab=151936, rms_eps=1e-6, rope_theta=1e6, qk_norm=True)
 
 
+# Plans of the benchmark workloads: one sub-queue per worker of an MI355X (256
+# compute units) and tile widths that give each GEMV op about 256 tiles.
+PLAN_8B = Plan(tq=24, to=16, tf=56, td=16, n_queues=256)
+
+
 def _stream_ctx0(seed: int, batch: int, lo: int, hi: int) -> Tuple[int, ...]:
     # per-sequence starting contexts, uniform integers in [lo, hi], seeded
     import numpy as np
@@ -131,25 +136,25 @@ WORKLOADS = {
         "Llama-3-1B-shaped bf16, batch 1, 128 decode steps from a 1024-token cache"),
     "llama8b_b1": Workload(
         "llama8b_b1", LLAMA_8B,
-        RunConfig(batch=1, ctx0=(4096,), steps=128, ctx_max=4224, seed=3), Plan(),
+        RunConfig(batch=1, ctx0=(4096,), steps=128, ctx_max=4224, seed=3), PLAN_8B,
         "Llama-3-8B-shaped bf16, batch 1, context 4096"),
     "llama8b_b4": Workload(
         "llama8b_b4", LLAMA_8B,
-        RunConfig(batch=4, ctx0=(4096,) * 4, steps=128, ctx_max=4224, seed=3), Plan(),
+        RunConfig(batch=4, ctx0=(4096,) * 4, steps=128, ctx_max=4224, seed=3), PLAN_8B,
         "Llama-3-8B-shaped bf16, batch 4, context 4096"),
     "llama8b_b16": Workload(
         "llama8b_b16", LLAMA_8B,
-        RunConfig(batch=16, ctx0=(4096,) * 16, steps=128, ctx_max=4224, seed=3), Plan(),
+        RunConfig(batch=16, ctx0=(4096,) * 16, steps=128, ctx_max=4224, seed=3), PLAN_8B,
         "Llama-3-8B-shaped bf16, batch 16, context 4096"),
     "qwen8b_prefill": Workload(
         "qwen8b_prefill", QWEN_8B,
         RunConfig(batch=1, ctx0=(2048,), steps=64, ctx_max=2112, seed=4, prefill_len=2048,
-                  init_cache=False), Plan(),
+                  init_cache=False), Plan(tq=24, to=16, tf=48, td=16, n_queues=256),
         "Qwen3-8B-shaped bf16 with QK-norm: prefill of 2048 tokens, then 64 decode steps"),
     "llama1b_stream_b32": Workload(
         "llama1b_stream_b32", LLAMA_1B,
         RunConfig(batch=32, ctx0=_stream_ctx0(5, 32, 256, 8192), steps=256, ctx_max=8448, seed=5),
-        Plan(),
+        Plan(tf=32, td=8, kb=1024, n_queues=256),
         "Llama-3-1B-shaped bf16 streaming decode, batch 32, contexts U{256..8192}, 256 steps"),
 }
 
