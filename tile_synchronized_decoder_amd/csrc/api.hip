@@ -145,9 +145,9 @@ int nb_bucket(int rows) {
 struct LdsLayout { uint32_t res, x, ring, uni, bytes; };
 
 // Bytes of the prefill tile region: the larger of a GEMM tile (two stages of a
-// 128 x 64 activation tile and a 256 x 64 weight tile, plus row statistics)
+// 128 x 64 activation tile, three of a 256 x 64 weight tile, row statistics)
 // and an attention tile (Q, a 64-key K and V^T block, scores, probabilities).
-constexpr uint32_t kPrefillGemmBytes = 2 * 128 * 128 + 2 * 256 * 128 + (256 + 128) * 4;
+constexpr uint32_t kPrefillGemmBytes = 2 * 128 * 128 + 3 * 256 * 128 + (256 + 128) * 4;
 constexpr uint32_t kPrefillAttnBytes = 2 * 128 * 128 + 2 * 64 * 128 + 128 * 64 * 2 + 128 * 64 * 4 + 128 * 64 * 2 + 3 * 128 * 4;
 
 // Dynamic shared memory of one workgroup, in floats: header (index, norm

@@ -299,6 +299,26 @@ __device__ __forceinline__ Smem make_smem(KArgs& a) {
 // instruction waits on its producer tiles, then refilled one line per line
 // consumed, so the ring's lines stay in flight per wave.
 
+// One 16-byte-per-lane global->LDS load (64 lanes fill 1 KB at `lds`, lane i
+// at lds + 16 i).  Issued through inline assembly so that the compiler does
+// not treat every later shared-memory read as depending on it (it would wait
+// for all outstanding loads before each read); the code that consumes the
+// data waits for it explicitly with wait_vm.  POL 1 adds sc1 (device-coherent).
+// The prefill GEMM pipeline and the decode GEMV of large models use it.  The
+// decode GEMV of small models keeps the compiler's builtin: the extra waits
+// it implies throttle each workgroup's weight stream, which measured faster
+// there (less memory-queue delay for the latency-critical barrier and input
+// loads of other tiles).
+template <int POL>
+__device__ __forceinline__ void dma_lds16(const void* src, void* lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)lds)));
+  if constexpr (POL == 0)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(l) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off sc1" ::"v"(src), "s"(l) : "memory", "m0");
+}
+
 // Wait until at most N of this wave's vector-memory operations are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -310,7 +330,7 @@ __device__ __forceinline__ void wait_vm() {
 // Rows come from up to two matrices: row i < split reads A[row0+i], row
 // i >= split reads B[row0+i-split] (gate / up).  Each wave owns RPW rows of a
 // pass of ROWS rows.
-template <typename WT, int NB, int RPW>
+template <typename WT, int NB, int RPW, bool PIPE = false>
 struct Gemv {
   static constexpr int ROWS = NWAVE * RPW;
   using E = Elem<WT>;
@@ -333,7 +353,8 @@ struct Gemv {
       const WT* p = row_ptr(row) + col;
 #pragma unroll
       for (int v = 0; v < LPI; ++v)
-        __builtin_amdgcn_global_load_lds(p + v * 4, ring + ((grp * RPW + j) * LPI + v) * 1024, 16, 0, 0);
+        if constexpr (PIPE) dma_lds16<0>(p + v * 4, ring + ((grp * RPW + j) * LPI + v) * 1024);
+        else __builtin_amdgcn_global_load_lds(p + v * 4, ring + ((grp * RPW + j) * LPI + v) * 1024, 16, 0, 0);
     }
   }
 };
@@ -397,11 +418,11 @@ __device__ __forceinline__ void stage_x(Smem& s, const float* x, int ldx, int nb
 // and refilled one group per group consumed.  `resid` (nullable) is staged
 // with the inputs: s.resid[row * NB + b] = resid[b * resid_ld + row].
 // Returns false when the wait gave up.
-template <typename WT, int NB, int RPW>
-__device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW>& g, const float* x, int nb,
+template <typename WT, int NB, int RPW, bool PIPE>
+__device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, PIPE>& g, const float* x, int nb,
                      const float* gain, bool norm, bool mega, const Instr in, uint32_t idx,
                      const float* resid, int resid_ld) {
-  using G = Gemv<WT, NB, RPW>;
+  using G = Gemv<WT, NB, RPW, PIPE>;
   using E = Elem<WT>;
   const int K = g.K;
   const int iters = (K + 511) / 512;
@@ -532,8 +553,8 @@ template <int NB> constexpr int rpw_for() { return NB >= 16 ? 2 : 4; }
 
 // The weight rows a GEMV instruction streams (op, layer, columns [a0, a1)),
 // or false for other ops.
-template <typename WT, int NB, int RPW>
-__device__ __forceinline__ bool gemv_of(KArgs& a, const Instr in, Gemv<WT, NB, RPW>& g) {
+template <typename WT, int NB, int RPW, bool PIPE>
+__device__ __forceinline__ bool gemv_of(KArgs& a, const Instr in, Gemv<WT, NB, RPW, PIPE>& g) {
   const int l = in.layer, n0 = in.a0, n = in.a1 - in.a0;
   switch (in.op) {
     case mk::OP_QKV: {
@@ -565,12 +586,12 @@ __device__ __forceinline__ bool gemv_of(KArgs& a, const Instr in, Gemv<WT, NB, R
 // The GEMV ops: QKV (RMSNorm(X_l) Wqkv^T), OPROJ (X_l + ATT_l Wo^T), GATEUP
 // (silu(RMSNorm(H) Wg^T) * (RMSNorm(H) Wu^T)) and DOWN (HRES_l + ACT_l Wd^T),
 // each over output columns [a0, a1).
-template <typename WT, int NB, int RPW>
+template <typename WT, int NB, int RPW, bool PIPE>
 __device__ __forceinline__ void op_gemv_rpw(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
-  using G = Gemv<WT, NB, RPW>;
+  using G = Gemv<WT, NB, RPW, PIPE>;
   const int l = in.layer, n0 = in.a0, n = in.a1 - in.a0;
   G g{};
-  gemv_of<WT, NB, RPW>(a, in, g);
+  gemv_of<WT, NB, RPW, PIPE>(a, in, g);
   const int op = in.op;
   const float* x;
   const float* gain = nullptr;
@@ -585,7 +606,7 @@ __device__ __forceinline__ void op_gemv_rpw(KArgs& a, Smem& s, const Instr in, u
   } else {
     x = a.ACT + l * a.sACT; resid = a.HRES + l * a.sHRES + n0; ld = a.H;
   }
-  if (!gemv<WT, NB, RPW>(a, s, g, x, a.M, gain, gain != nullptr, mega, in, idx, resid, ld)) return;
+  if (!gemv<WT, NB, RPW, PIPE>(a, s, g, x, a.M, gain, gain != nullptr, mega, in, idx, resid, ld)) return;
   {
     for (int e = threadIdx.x; e < n * a.M; e += NT) {
       const int row = e / a.M, b = e - row * a.M;
@@ -607,10 +628,20 @@ template <typename WT, int NB>
 __device__ __forceinline__ void op_gemv(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
   constexpr int RPW = rpw_for<NB>();
   const int rows = (in.op == mk::OP_GATEUP ? 2 : 1) * (int)(in.a1 - in.a0);
-  if constexpr (RPW != 2) {
-    if (rows <= 2 * NWAVE) { op_gemv_rpw<WT, NB, 2>(a, s, in, idx, mega); return; }
+  // Hidden size 4096 and up: weight lines are issued so that the compiler does
+  // not serialise the ring (long K loops gain from the full ring depth); below
+  // that the serialised ring measured faster in the megakernel.
+  if (a.H >= 4096) {
+    if constexpr (RPW != 2) {
+      if (rows <= 2 * NWAVE) { op_gemv_rpw<WT, NB, 2, true>(a, s, in, idx, mega); return; }
+    }
+    op_gemv_rpw<WT, NB, RPW, true>(a, s, in, idx, mega);
+    return;
   }
-  op_gemv_rpw<WT, NB, RPW>(a, s, in, idx, mega);
+  if constexpr (RPW != 2) {
+    if (rows <= 2 * NWAVE) { op_gemv_rpw<WT, NB, 2, false>(a, s, in, idx, mega); return; }
+  }
+  op_gemv_rpw<WT, NB, RPW, false>(a, s, in, idx, mega);
 }
 
 // EMBED(n0, n1): X_0[b, n0:n1] = E[token_b, n0:n1]
@@ -1097,9 +1128,9 @@ __global__ __launch_bounds__(NT) void lm_head_kernel(Args args) {
   const int v0 = blockIdx.x * ROWS;
   const int n = min(ROWS, a.V - v0);
   const WT* W = static_cast<const WT*>(a.lm_head);
-  Gemv<WT, NB, RPW> g{W, W, n, v0, n, a.H};
+  Gemv<WT, NB, RPW, false> g{W, W, n, v0, n, a.H};
   Instr none{};
-  gemv<WT, NB, RPW>(a, s, g, a.lm_x, a.M, a.final_norm, true, false, none, 0, nullptr, 0);
+  gemv<WT, NB, RPW, false>(a, s, g, a.lm_x, a.M, a.final_norm, true, false, none, 0, nullptr, 0);
   for (int e = threadIdx.x; e < n * a.M; e += NT) {
     const int row = e / a.M, b = e - row * a.M;
     if (a.logits) a.logits[(size_t)b * a.V + v0 + row] = s.res[row * NB + b];

@@ -51,7 +51,17 @@ __device__ __forceinline__ v4u ld_cg_v4u(const void* p) {
 __device__ __forceinline__ void st_cg_u32(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-constexpr int DMA_DEVICE_COHERENT = 16;   // cache-policy bit sc1 of a global-to-LDS load
+
+// Activation tiles (X, QKV, ATT, HRES, ACT) are read with ordinary L2-cached
+// loads, so the many column tiles of one row block share them through L2
+// instead of each fetching them from memory.  This is safe because every
+// 128-byte line of these tensors is written by exactly one producer tile
+// (column tiles are 128 floats wide, rows a multiple of 64 floats), with
+// device-coherent stores, and is first read on any XCD only after that
+// tile's barrier was observed; no L2 holds a copy from before the launch
+// (caches are written back and invalidated at kernel boundaries).
+__device__ __forceinline__ float4 ld_act4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float ld_act(const float* p) { return *p; }
 
 // Rotary cos / sin of position `pos` and pair index i, angle reduced in float64.
 __device__ __forceinline__ void rope_cs(KArgs& a, int pos, int i, float& c, float& s) {
@@ -86,36 +96,40 @@ __device__ __forceinline__ void p_issue_b(const PGemm& g, uint8_t* b, int ks, in
     int wr = g.n0 + (row % PBN);
     if (wr >= g.n_total) wr = g.n_total - 1;
     const uint16_t* src = (half ? g.w1 : g.w0) + (size_t)wr * g.K + ks * PKS + c * 8;
-    __builtin_amdgcn_global_load_lds(src, b + d * 1024, 16, 0, 0);
+    dma_lds16<0>(src, b + d * 1024);
   }
 }
 
-// Load A of K step ks (fp32 -> x gain -> bf16) into registers.
+// Activation operand of K step ks: this thread's 32 floats of one row (rows
+// past the tile read as zeros).  The loads are only issued here; p_store_a
+// consumes them, so they overlap the matrix-core work of the current step.
 struct PARegs { float4 v[8]; };
 
-__device__ __forceinline__ void p_load_a(const PGemm& g, int ks, PARegs& r, float& ss) {
+__device__ __forceinline__ void p_load_a(const PGemm& g, int ks, PARegs& r) {
   const int t = threadIdx.x, row = t >> 1, half = t & 1;
   const int k0 = ks * PKS + half * 32;
   if (row < g.rows) {
     const float* src = g.x + (size_t)(g.r0 + row) * g.K + k0;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) r.v[q] = ld_cg4(src + 4 * q);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      ss += r.v[q].x * r.v[q].x + r.v[q].y * r.v[q].y + r.v[q].z * r.v[q].z + r.v[q].w * r.v[q].w;
-      if (g.gain) {
-        const float4 gg = *reinterpret_cast<const float4*>(g.gain + k0 + 4 * q);
-        r.v[q].x *= gg.x; r.v[q].y *= gg.y; r.v[q].z *= gg.z; r.v[q].w *= gg.w;
-      }
-    }
+    for (int q = 0; q < 8; ++q) r.v[q] = ld_act4(src + 4 * q);
   } else {
 #pragma unroll
     for (int q = 0; q < 8; ++q) r.v[q] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
 
-__device__ __forceinline__ void p_store_a(uint8_t* a, const PARegs& r) {
+// Sum of squares (RMSNorm), gain, bf16 rounding, swizzled store into LDS.
+__device__ __forceinline__ void p_store_a(const PGemm& g, int ks, uint8_t* a, PARegs& r, float& ss) {
   const int t = threadIdx.x, row = t >> 1, half = t & 1;
+  const int k0 = ks * PKS + half * 32;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    ss += r.v[q].x * r.v[q].x + r.v[q].y * r.v[q].y + r.v[q].z * r.v[q].z + r.v[q].w * r.v[q].w;
+    if (g.gain) {
+      const float4 gg = *reinterpret_cast<const float4*>(g.gain + k0 + 4 * q);
+      r.v[q].x *= gg.x; r.v[q].y *= gg.y; r.v[q].z *= gg.z; r.v[q].w *= gg.w;
+    }
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const float4 u = r.v[2 * q], w = r.v[2 * q + 1];
@@ -151,22 +165,32 @@ __device__ __forceinline__ void p_mfma_step(const uint8_t* a, const uint8_t* b, 
   }
 }
 
-// Full K loop of one tile, double buffered: the weight DMA of step ks+1 and the
-// activation loads of step ks+1 are in flight while step ks runs on the matrix
-// cores.  The first weight step is issued before the tile waits (`mega`).
-// Leaves the row scales (RMSNorm factors, or 1) in s.x[0 .. PBM).
+// LDS of a GEMM tile: two activation stages, three weight stages, then the
+// row statistics ([NT] partial sums, then [PBM] row scales).
+constexpr int P_BSTAGES = 3;
+__device__ __forceinline__ float* p_row_stats(Smem& s, bool two_mats) {
+  return reinterpret_cast<float*>(s.ring + 2 * PBM * 128 + P_BSTAGES * (two_mats ? 2 : 1) * PBN * 128);
+}
+
+// Full K loop of one tile.  Weights are DMA'd two K steps ahead (three
+// stages), activations one step ahead through registers; the loads of the
+// next steps are in flight while the current step runs on the matrix cores.
+// The first two weight steps are issued before the tile waits (`mega`).
+// Leaves the row scales (RMSNorm factors, or 1) in p_row_stats()[NT ..].
 __device__ __forceinline__ bool p_gemm(KArgs& a, Smem& s, const PGemm& g, PAcc& acc, PAcc* acc_up, bool mega,
                                        const Instr in, uint32_t idx) {
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int bbytes = (g.w1 ? 2 : 1) * PBN * 128;
-  uint8_t* abuf[2] = {s.ring, s.ring + PBM * 128};
-  uint8_t* bbuf[2] = {s.ring + 2 * PBM * 128, s.ring + 2 * PBM * 128 + bbytes};
-  float* rs = reinterpret_cast<float*>(s.ring + 2 * PBM * 128 + 2 * bbytes);   // [NT] then [PBM]
+  const bool two = g.w1 != nullptr;
+  const int bbytes = (two ? 2 : 1) * PBN * 128;
+  uint8_t* abase = s.ring;                               // two activation stages
+  uint8_t* bbase = s.ring + 2 * PBM * 128;
+  float* rs = p_row_stats(s, two);
   const int nks = g.K / PKS;
 
-  p_issue_b(g, bbuf[0], 0, wave, lane);
+  p_issue_b(g, bbase, 0, wave, lane);
+  if (nks > 1) p_issue_b(g, bbase + bbytes, 1, wave, lane);
   if (mega && !wait_tiles(a, in, idx)) { wait_vm<0>(); return false; }
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
@@ -177,21 +201,29 @@ __device__ __forceinline__ bool p_gemm(KArgs& a, Smem& s, const PGemm& g, PAcc& 
     }
   float ss = 0.f;
   PARegs ar;
-  p_load_a(g, 0, ar, ss);
-  p_store_a(abuf[0], ar);
+  p_load_a(g, 0, ar);
   wait_vm<0>();
+  p_store_a(g, 0, abase, ar, ss);
   __syncthreads();
+  int bcur = 0;                                          // stage of step ks
   for (int ks = 0; ks < nks; ++ks) {
-    const int cur = ks & 1, nxt = cur ^ 1;
-    const bool more = ks + 1 < nks;
+    const int cur = ks & 1;
+    const bool more = ks + 1 < nks, more2 = ks + 2 < nks;
+    if (more) p_load_a(g, ks + 1, ar);
+    const int b2 = bcur + 2 >= P_BSTAGES ? bcur + 2 - P_BSTAGES : bcur + 2;
+    if (more2) p_issue_b(g, bbase + b2 * bbytes, ks + 2, wave, lane);
+    p_mfma_step(abase + cur * (PBM * 128), bbase + bcur * bbytes, acc, acc_up, wm, wn, lane);
     if (more) {
-      p_issue_b(g, bbuf[nxt], ks + 1, wave, lane);
-      p_load_a(g, ks + 1, ar, ss);
+      // the activations of step ks + 1 (issued before the weights of step ks + 2) and the
+      // weights of step ks + 1 (issued a step earlier) have landed once only the weight
+      // loads of step ks + 2 may still be outstanding
+      if (!more2) wait_vm<0>();
+      else if (two) wait_vm<2 * PBN / 8 / NWAVE>();
+      else wait_vm<PBN / 8 / NWAVE>();
+      p_store_a(g, ks + 1, abase + (cur ^ 1) * (PBM * 128), ar, ss);
     }
-    p_mfma_step(abuf[cur], bbuf[cur], acc, acc_up, wm, wn, lane);
-    if (more) p_store_a(abuf[nxt], ar);
-    wait_vm<0>();
     __syncthreads();
+    bcur = bcur + 1 == P_BSTAGES ? 0 : bcur + 1;
   }
   if (mega) trace_mark(a, idx, 4);
   // row scales: each row's two threads hold halves of sum(x^2)
@@ -244,7 +276,7 @@ __device__ __forceinline__ void op_p_qkv(KArgs& a, Smem& s, const Instr in, uint
   PAcc acc;
   if (!p_gemm(a, s, g, acc, nullptr, mega, in, idx)) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
-  const float* rs = reinterpret_cast<const float*>(s.ring + 2 * PBM * 128 + 2 * PBN * 128) + NT;
+  const float* rs = p_row_stats(s, false) + NT;
   // stage the scaled tile (fp32 [128][128]) over the operand buffers
   float* ct = reinterpret_cast<float*>(s.ring);
   __syncthreads();
@@ -333,7 +365,7 @@ __device__ __forceinline__ void op_p_resid(KArgs& a, Smem& s, const Instr in, ui
         const int row = p_row(wm, mi, v, lane), col = n0 + p_col(wn, ni, lane);
         if (row < rows && col < a.H) {
           const size_t o = (size_t)(r0 + row) * a.H + col;
-          st_cg(out + o, ld_cg(res + o) + acc.c[mi][ni][v]);
+          st_cg(out + o, ld_act(res + o) + acc.c[mi][ni][v]);
         }
       }
   if (mega) signal_tile(a, in);
@@ -353,7 +385,7 @@ __device__ __forceinline__ void op_p_gateup(KArgs& a, Smem& s, const Instr in, u
   PAcc acc, up;
   if (!p_gemm(a, s, g, acc, &up, mega, in, idx)) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
-  const float* rs = reinterpret_cast<const float*>(s.ring + 2 * PBM * 128 + 4 * PBN * 128) + NT;
+  const float* rs = p_row_stats(s, true) + NT;
   float* out = a.ACT + l * a.sACT;
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
@@ -407,7 +439,7 @@ __device__ __forceinline__ void op_p_attn(KArgs& a, Smem& s, const Instr in, uin
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       float4 u = make_float4(0.f, 0.f, 0.f, 0.f), w = u;
-      if (row < rows) { u = ld_cg4(src + 8 * q); w = ld_cg4(src + 8 * q + 4); }
+      if (row < rows) { u = ld_act4(src + 8 * q); w = ld_act4(src + 8 * q + 4); }
       v4u pk = {pack_bf16(u.x, u.y), pack_bf16(u.z, u.w), pack_bf16(w.x, w.y), pack_bf16(w.z, w.w)};
       *reinterpret_cast<v4u*>(qs + half * PBM * 128 + row * 128 + swz(row, q) * 16) = pk;
     }
@@ -429,8 +461,7 @@ __device__ __forceinline__ void op_p_attn(KArgs& a, Smem& s, const Instr in, uin
       const int half = d / (PKB / 8), key = (d % (PKB / 8)) * 8 + lane / 8;
       const int c = (lane % 8) ^ (key & 7);
       const int kk = min(k0 + key, nkeys - 1);
-      __builtin_amdgcn_global_load_lds(Kc + (size_t)kk * HD + half * 64 + c * 8, ks + d * 1024, 16, 0,
-                                       DMA_DEVICE_COHERENT);
+      dma_lds16<1>(Kc + (size_t)kk * HD + half * 64 + c * 8, ks + d * 1024);
     }
     // V block transposed: thread t reads 8 dims of one key and scatters them
     for (int e = t; e < PKB * (HD / 8); e += NT) {
