@@ -39,14 +39,16 @@ using mk::Range;
 
 constexpr int NT = 256;                 // threads per workgroup
 constexpr int NWAVE = NT / 64;
-constexpr int XBUF_MAX = 16384;         // LDS staging of GEMV inputs, upper bound (64 KB)
+constexpr int XBUF_MAX = 36864;         // LDS staging of GEMV inputs, upper bound (144 KB)
 constexpr int ROWS_PER_PASS_MAX = 16;   // GEMV rows reduced per pass (4 waves x 4)
 constexpr int ATT_MAX_R = 4;            // query heads per KV head
 constexpr int LM_ROWS = 64;             // vocabulary rows per LM-head workgroup
 // 1 KB weight lines in flight per wave: 24 (96 KB per workgroup); 12 at 32
 // input rows, where the staged inputs need the room (32 x 512 floats per chunk)
-template <int NB> constexpr int ring_lines() { return NB >= 32 ? 12 : 24; }
-constexpr int ring_lines_for(int nb) { return nb >= 32 ? 12 : 24; }
+// Weight lines (1 KB) in flight per wave.  Batched GEMVs do more arithmetic per
+// line and need the shared memory for their inputs, so their rings are shorter.
+constexpr int ring_lines_for(int nb) { return nb <= 2 ? 24 : nb <= 8 ? 16 : 8; }
+template <int NB> constexpr int ring_lines() { return ring_lines_for(NB); }
 constexpr uint32_t ERR_TIMEOUT = 1, ERR_OPCODE = 2, ERR_CONTEXT = 3, ERR_TOKEN = 4;
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
@@ -148,11 +150,64 @@ template <> struct Elem<float> {
   }
 };
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// Cross-lane helpers: DPP moves within a 16-lane row, lane permutes across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum over the LPK (8 or 16) lanes of an aligned lane group; every lane gets it.
+template <int LPK>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  v += dpp_mov<0xB1>(v);                 // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);                 // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);                // row_half_mirror
+  if constexpr (LPK == 16) v += dpp_mov<0x140>(v);   // row_mirror
   return v;
 }
+// Sum over the wave; every lane gets the same value.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = lane_group_sum<16>(v);
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+// Exchange with the lane whose bit M differs (bits above M equal): lane
+// permutes for bits 5 and 4, DPP mirrors and quad permutes within a row below.
+template <int M>
+__device__ __forceinline__ float xchg_bit(float v) {
+  if constexpr (M == 5) return __shfl_xor(v, 32, 64);
+  else if constexpr (M == 4) return __shfl_xor(v, 16, 64);
+  else if constexpr (M == 3) return dpp_mov<0x140>(v);     // row_mirror: lane ^ 15 within the row
+  else if constexpr (M == 2) return dpp_mov<0x141>(v);     // row_half_mirror: lane ^ 7 within 8
+  else if constexpr (M == 1) return dpp_mov<0x4E>(v);      // quad_perm [2,3,0,1]
+  else return dpp_mov<0xB1>(v);                            // quad_perm [1,0,3,2]
+}
+// Sums of N values per lane over the wave, N a power of two up to 64, with
+// about two exchanges per value instead of one full reduction each: every
+// step over lane bit M (5 down to 0) keeps half of the remaining values, the
+// half chosen by that bit, and adds the partner's copy of it; once one value
+// is left the steps just add.  On return v[0] of lane l is the total of value
+// index l >> (6 - log2 N), identical in all lanes of that index.
+template <int N, int M = 5>
+__device__ __forceinline__ void wave_sum_many(float* v, int lane) {
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "power of two up to 64");
+  if constexpr (M >= 0) {
+    if constexpr (N > 1) {
+      const bool hi = (lane >> M) & 1;
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) {
+        const float keep = hi ? v[N / 2 + i] : v[i];
+        const float send = hi ? v[i] : v[N / 2 + i];
+        v[i] = keep + xchg_bit<M>(send);
+      }
+      wave_sum_many<N / 2, M - 1>(v, lane);
+    } else {
+      v[0] += xchg_bit<M>(v[0]);
+      wave_sum_many<1, M - 1>(v, lane);
+    }
+  }
+}
+template <int N> constexpr int log2_of() { return N <= 1 ? 0 : 1 + log2_of<N / 2>(); }
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -304,11 +359,11 @@ __device__ __forceinline__ Smem make_smem(KArgs& a) {
 // not treat every later shared-memory read as depending on it (it would wait
 // for all outstanding loads before each read); the code that consumes the
 // data waits for it explicitly with wait_vm.  POL 1 adds sc1 (device-coherent).
-// The prefill GEMM pipeline and the decode GEMV of large models use it.  The
-// decode GEMV of small models keeps the compiler's builtin: the extra waits
-// it implies throttle each workgroup's weight stream, which measured faster
-// there (less memory-queue delay for the latency-critical barrier and input
-// loads of other tiles).
+// The prefill GEMM pipeline and the decode GEMVs of large models or batched
+// inputs use it.  The single-row decode GEMV of small models keeps the
+// compiler's builtin: the extra waits it implies throttle each workgroup's
+// weight stream, which measured faster there (less memory-queue delay for the
+// latency-critical barrier and input loads of other tiles).
 template <int POL>
 __device__ __forceinline__ void dma_lds16(const void* src, void* lds) {
   const uint32_t l = __builtin_amdgcn_readfirstlane(
@@ -413,10 +468,14 @@ __device__ __forceinline__ void stage_x(Smem& s, const float* x, int ldx, int nb
 
 // Full GEMV of `nrows` rows against `nb` input rows of length K, results in
 // s.res[row * NB + b] (already scaled by the row's RMSNorm factor when `norm`).
-// Each wave streams its rows' weight lines through its ring in consumption
-// order; the ring is filled before waiting on the instruction's producer tiles
-// and refilled one group per group consumed.  `resid` (nullable) is staged
-// with the inputs: s.resid[row * NB + b] = resid[b * resid_ld + row].
+// The inputs are staged in column chunks as large as the shared memory allows;
+// each chunk is staged once and every pass of RPW rows per wave runs over it
+// before the next chunk, so the partial sums of a row add up in s.res across
+// chunks (owned by one wave, in chunk order).  Each wave streams its rows'
+// weight lines through its ring in that consumption order; the ring is filled
+// before waiting on the instruction's producer tiles and refilled one group
+// per group consumed.  `resid` (nullable) is staged with the first chunk:
+// s.resid[row * NB + b] = resid[b * resid_ld + row].
 // Returns false when the wait gave up.
 template <typename WT, int NB, int RPW, bool PIPE>
 __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, PIPE>& g, const float* x, int nb,
@@ -426,9 +485,9 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, 
   using E = Elem<WT>;
   const int K = g.K;
   const int iters = (K + 511) / 512;
-  const int kc_max = (s.xcap / NB) / 512 * 512;
+  const int ipc = (s.xcap / NB) / 512;                 // 512-column iterations per staged chunk
+  const int kc_max = ipc * 512;
   const int npass = (g.nrows + G::ROWS - 1) / G::ROWS;
-  const bool single_chunk = K <= kc_max;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   constexpr int RING_LINES = ring_lines<NB>();
   uint8_t* ring = s.ring + wave * RING_LINES * 1024;
@@ -436,11 +495,14 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, 
   constexpr int NG = RING_LINES / GL;                  // groups in the ring
   static_assert(NG >= 2 && RING_LINES % GL == 0, "ring holds whole iteration groups");
   const int ngroups = npass * iters;                   // groups this wave consumes
-  // refill cursor: the next (pass, iteration) to issue
-  int rp = 0, ri = 0;
+  // refill cursor: the next (chunk, pass, iteration) to issue
+  int rb = 0, re = min(ipc, iters), rp = 0, ri = 0;   // chunk [rb, re) of iterations
   auto issue_next = [&](int grp) {
     g.issue_iter(ring, grp, rp, ri, wave, lane);
-    if (++ri == iters) { ri = 0; ++rp; }
+    if (++ri == re) {
+      ri = rb;
+      if (++rp == npass) { rp = 0; rb = re; re = min(re + ipc, iters); ri = rb; }
+    }
   };
   for (int q = 0; q < min(ngroups, NG); ++q) issue_next(q);          // prefetch
   if (mega && !wait_tiles(a, in, idx)) {
@@ -451,26 +513,21 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, 
   float ssl[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) ssl[b] = 0.f;
-  bool staged = false;
   int gi = 0;                                            // next group to consume
 
-  for (int pass = 0; pass < npass; ++pass) {
-    float acc[RPW][NB];
+  for (int kc0 = 0; kc0 < K; kc0 += kc_max) {
+    const int kcn = min(kc_max, K - kc0);
+    if (kc0 > 0) __syncthreads();                        // every wave is done with the previous chunk
+    stage_x<NB>(s, x, K, nb, kc0, kcn, gain, norm, ssl, kc0 == 0 ? resid : nullptr, resid_ld, g.nrows);
+    __syncthreads();
+    if (mega && kc0 == 0) trace_mark(a, idx, 3);
+    const int it_begin = kc0 / 512, it_end = (kc0 + kcn + 511) / 512;
+    for (int pass = 0; pass < npass; ++pass) {
+      float acc[RPW][NB];
 #pragma unroll
-    for (int j = 0; j < RPW; ++j)
+      for (int j = 0; j < RPW; ++j)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) acc[j][b] = 0.f;
-    for (int kc0 = 0; kc0 < K; kc0 += kc_max) {
-      const int kcn = min(kc_max, K - kc0);
-      if (!(single_chunk && staged)) {
-        __syncthreads();
-        stage_x<NB>(s, x, K, nb, kc0, kcn, gain, norm && pass == 0, ssl, staged ? nullptr : resid, resid_ld,
-                    g.nrows);
-        __syncthreads();
-        if (mega && !staged) trace_mark(a, idx, 3);
-        staged = true;
-      }
-      const int it_begin = kc0 / 512, it_end = (kc0 + kcn + 511) / 512;
+        for (int b = 0; b < NB; ++b) acc[j][b] = 0.f;
       for (int it = it_begin; it < it_end; ++it, ++gi) {
         const int col = it * 512 + lane * 8;
         const bool valid = col < K;
@@ -483,42 +540,42 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, 
         for (int j = 0; j < RPW; ++j)
 #pragma unroll
           for (int v = 0; v < G::LPI; ++v) w[j][v] = *reinterpret_cast<const v4u*>(gbase + (j * G::LPI + v) * 1024);
-        float xv[NB][8];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          if (b < nb && valid) {
-            const float4 x0 = *reinterpret_cast<const float4*>(s.x + b * kcn + c);
-            const float4 x1 = *reinterpret_cast<const float4*>(s.x + b * kcn + c + 4);
-            xv[b][0] = x0.x; xv[b][1] = x0.y; xv[b][2] = x0.z; xv[b][3] = x0.w;
-            xv[b][4] = x1.x; xv[b][5] = x1.y; xv[b][6] = x1.z; xv[b][7] = x1.w;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xv[b][e] = 0.f;
-          }
-        }
         // the group's reads have returned: its slots can be refilled
         __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0); vmcnt, expcnt unconstrained
         if (gi + NG < ngroups) issue_next(gi % NG);
+        float wf[RPW][8];
 #pragma unroll
-        for (int j = 0; j < RPW; ++j) {
-          float wf[8];
-          E::unpack(w[j], wf);
+        for (int j = 0; j < RPW; ++j) E::unpack(w[j], wf[j]);
+        // one input row at a time against all of the wave's rows
 #pragma unroll
-          for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b) {
+          float xv[8];
+          if (b < nb && valid) {
+            const float4 x0 = *reinterpret_cast<const float4*>(s.x + b * kcn + c);
+            const float4 x1 = *reinterpret_cast<const float4*>(s.x + b * kcn + c + 4);
+            xv[0] = x0.x; xv[1] = x0.y; xv[2] = x0.z; xv[3] = x0.w;
+            xv[4] = x1.x; xv[5] = x1.y; xv[6] = x1.z; xv[7] = x1.w;
+          } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[j][b] = fmaf(wf[e], xv[b][e], acc[j][b]);
+            for (int e = 0; e < 8; ++e) xv[e] = 0.f;
+          }
+#pragma unroll
+          for (int j = 0; j < RPW; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[j][b] = fmaf(wf[j][e], xv[e], acc[j][b]);
         }
       }
-    }
-    // reduce each (row, b) across the wave; lane 0 keeps the sum
-#pragma unroll
-    for (int j = 0; j < RPW; ++j)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float v = wave_sum(acc[j][b]);
+      // reduce every (row, b) across the wave at once; the first lane holding
+      // a total adds it to the row's sum
+      constexpr int NV = RPW * NB, SH = 6 - log2_of<NV>();
+      wave_sum_many<NV>(&acc[0][0], lane);
+      {
+        const int vi = lane >> SH, j = vi / NB, b = vi - j * NB;
         const int row = pass * G::ROWS + wave * RPW + j;
-        if (lane == 0 && row < g.nrows && b < nb) s.res[row * NB + b] = v;
+        if ((lane & ((1 << SH) - 1)) == 0 && row < g.nrows && b < nb)
+          s.res[row * NB + b] = kc0 == 0 ? acc[0][0] : s.res[row * NB + b] + acc[0][0];
       }
+    }
   }
   if (mega) trace_mark(a, idx, 4);
   if (norm) {
@@ -628,10 +685,11 @@ template <typename WT, int NB>
 __device__ __forceinline__ void op_gemv(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
   constexpr int RPW = rpw_for<NB>();
   const int rows = (in.op == mk::OP_GATEUP ? 2 : 1) * (int)(in.a1 - in.a0);
-  // Hidden size 4096 and up: weight lines are issued so that the compiler does
-  // not serialise the ring (long K loops gain from the full ring depth); below
-  // that the serialised ring measured faster in the megakernel.
-  if (a.H >= 4096) {
+  // Batched inputs or hidden size 4096 and up: weight lines are issued so that
+  // the compiler does not serialise the ring (it would wait for every line in
+  // flight before each read of the staged inputs); a single input row of a
+  // smaller model measured faster with the serialised ring.
+  if (NB > 1 || a.H >= 4096) {
     if constexpr (RPW != 2) {
       if (rows <= 2 * NWAVE) { op_gemv_rpw<WT, NB, 2, true>(a, s, in, idx, mega); return; }
     }
@@ -664,21 +722,6 @@ __device__ __forceinline__ void op_embed(KArgs& a, const Instr in, bool mega) {
 
 // ----------------------------------------------------------------------------- attention
 
-// Cross-lane helpers for the attention tile: DPP moves within a 16-lane row,
-// lane permutes across rows.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-// Sum over the LPK (8 or 16) lanes of an aligned lane group; every lane gets it.
-template <int LPK>
-__device__ __forceinline__ float lane_group_sum(float v) {
-  v += dpp_mov<0xB1>(v);                 // quad_perm [1,0,3,2]
-  v += dpp_mov<0x4E>(v);                 // quad_perm [2,3,0,1]
-  v += dpp_mov<0x141>(v);                // row_half_mirror
-  if constexpr (LPK == 16) v += dpp_mov<0x140>(v);   // row_mirror
-  return v;
-}
 // Combine the lanes that share (lane % LPK) across the 64 / LPK groups.
 template <int LPK, bool MAX>
 __device__ __forceinline__ float across_groups(float v) {
@@ -1128,9 +1171,9 @@ __global__ __launch_bounds__(NT) void lm_head_kernel(Args args) {
   const int v0 = blockIdx.x * ROWS;
   const int n = min(ROWS, a.V - v0);
   const WT* W = static_cast<const WT*>(a.lm_head);
-  Gemv<WT, NB, RPW, false> g{W, W, n, v0, n, a.H};
+  Gemv<WT, NB, RPW, (NB > 1)> g{W, W, n, v0, n, a.H};
   Instr none{};
-  gemv<WT, NB, RPW, false>(a, s, g, a.lm_x, a.M, a.final_norm, true, false, none, 0, nullptr, 0);
+  gemv<WT, NB, RPW, (NB > 1)>(a, s, g, a.lm_x, a.M, a.final_norm, true, false, none, 0, nullptr, 0);
   for (int e = threadIdx.x; e < n * a.M; e += NT) {
     const int row = e / a.M, b = e - row * a.M;
     if (a.logits) a.logits[(size_t)b * a.V + v0 + row] = s.res[row * NB + b];
