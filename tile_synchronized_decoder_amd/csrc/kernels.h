@@ -487,6 +487,7 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, 
   const int iters = (K + 511) / 512;
   const int ipc = (s.xcap / NB) / 512;                 // 512-column iterations per staged chunk
   const int kc_max = ipc * 512;
+  const int nch = (iters + ipc - 1) / ipc;
   const int npass = (g.nrows + G::ROWS - 1) / G::ROWS;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   constexpr int RING_LINES = ring_lines<NB>();
@@ -515,12 +516,13 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, 
   for (int b = 0; b < NB; ++b) ssl[b] = 0.f;
   int gi = 0;                                            // next group to consume
 
-  for (int kc0 = 0; kc0 < K; kc0 += kc_max) {
+  for (int ci = 0; ci < nch; ++ci) {
+    const int kc0 = ci * kc_max;
     const int kcn = min(kc_max, K - kc0);
-    if (kc0 > 0) __syncthreads();                        // every wave is done with the previous chunk
-    stage_x<NB>(s, x, K, nb, kc0, kcn, gain, norm, ssl, kc0 == 0 ? resid : nullptr, resid_ld, g.nrows);
+    if (ci > 0) __syncthreads();                         // every wave is done with the previous chunk
+    stage_x<NB>(s, x, K, nb, kc0, kcn, gain, norm, ssl, ci == 0 ? resid : nullptr, resid_ld, g.nrows);
     __syncthreads();
-    if (mega && kc0 == 0) trace_mark(a, idx, 3);
+    if (mega && ci == 0) trace_mark(a, idx, 3);
     const int it_begin = kc0 / 512, it_end = (kc0 + kcn + 511) / 512;
     for (int pass = 0; pass < npass; ++pass) {
       float acc[RPW][NB];
@@ -531,7 +533,8 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, 
       for (int it = it_begin; it < it_end; ++it, ++gi) {
         const int col = it * 512 + lane * 8;
         const bool valid = col < K;
-        const int c = col - kc0;
+        // batched inputs: columns past K read column 0 and their weights are zeroed below
+        const int c = (NB <= 2 || valid) ? col - kc0 : 0;
         // group gi has landed once at most (issued - gi - 1) groups are outstanding
         if (gi + NG <= ngroups) wait_vm<(NG - 1) * GL>(); else wait_vm<0>();
         const uint8_t* gbase = ring + (gi % NG) * GL * 1024 + lane * 16;
@@ -545,19 +548,25 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, 
         if (gi + NG < ngroups) issue_next(gi % NG);
         float wf[RPW][8];
 #pragma unroll
-        for (int j = 0; j < RPW; ++j) E::unpack(w[j], wf[j]);
-        // one input row at a time against all of the wave's rows
+        for (int j = 0; j < RPW; ++j) {
+          E::unpack(w[j], wf[j]);
+          if (NB > 2 && (K & 511) && !valid) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wf[j][e] = 0.f;
+          }
+        }
+        // one input row at a time against all of the wave's rows.  Batched
+        // inputs read without branches: rows past nb read whatever the staging
+        // area holds (in bounds: NB * kc_max <= xcap) and their sums are never
+        // stored.  One or two rows keep the branch (measured faster there).
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          float xv[8];
-          if (b < nb && valid) {
+          float xv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          if (NB > 2 || (b < nb && valid)) {
             const float4 x0 = *reinterpret_cast<const float4*>(s.x + b * kcn + c);
             const float4 x1 = *reinterpret_cast<const float4*>(s.x + b * kcn + c + 4);
             xv[0] = x0.x; xv[1] = x0.y; xv[2] = x0.z; xv[3] = x0.w;
             xv[4] = x1.x; xv[5] = x1.y; xv[6] = x1.z; xv[7] = x1.w;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xv[e] = 0.f;
           }
 #pragma unroll
           for (int j = 0; j < RPW; ++j)
@@ -573,7 +582,7 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, 
         const int vi = lane >> SH, j = vi / NB, b = vi - j * NB;
         const int row = pass * G::ROWS + wave * RPW + j;
         if ((lane & ((1 << SH) - 1)) == 0 && row < g.nrows && b < nb)
-          s.res[row * NB + b] = kc0 == 0 ? acc[0][0] : s.res[row * NB + b] + acc[0][0];
+          s.res[row * NB + b] = ci == 0 ? acc[0][0] : s.res[row * NB + b] + acc[0][0];
       }
     }
   }
@@ -1012,6 +1021,43 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
   if (mega) signal_tile(a, in);
 }
 
+// Log-sum-exp merge of NS split partials (o[r*HD], m[r], l[r] per split, slot_sz
+// floats apart, read through rd) into out[r*HD].
+template <int HD, typename RD>
+__device__ __forceinline__ void combine_rows(const float* src, float* out, int r, int NS, int slot_sz, RD rd) {
+  constexpr int G8 = 8;
+  auto part = [&](int e) { return rd(src + e); };
+  for (int o = threadIdx.x; o < r * HD; o += NT) {
+    const int h = o / HD;
+    const int em = r * HD + h, el = r * HD + r + h;
+    float m = -INFINITY;
+    for (int sp0 = 0; sp0 < NS; sp0 += G8) {
+      float v[G8];
+#pragma unroll
+      for (int j = 0; j < G8; ++j) v[j] = part(min(sp0 + j, NS - 1) * slot_sz + em);
+#pragma unroll
+      for (int j = 0; j < G8; ++j) m = fmaxf(m, v[j]);       // clamped repeats do not change the max
+    }
+    float num = 0.f, den = 0.f;
+    for (int sp0 = 0; sp0 < NS; sp0 += G8) {
+      float ms[G8], ov[G8], lv[G8];
+#pragma unroll
+      for (int j = 0; j < G8; ++j) {
+        const int e = min(sp0 + j, NS - 1) * slot_sz;
+        ms[j] = part(e + em); ov[j] = part(e + o); lv[j] = part(e + el);
+      }
+#pragma unroll
+      for (int j = 0; j < G8; ++j) {
+        if (sp0 + j >= NS || ms[j] == -INFINITY) continue;
+        const float w = expf(ms[j] - m);
+        num = fmaf(w, ov[j], num);
+        den = fmaf(w, lv[j], den);
+      }
+    }
+    st_cg(out + o, num / den);
+  }
+}
+
 // COMBINE(b, g): merge the NS split partials of row b, group g into ATT_l.
 template <int HD>
 __device__ __forceinline__ void op_combine(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
@@ -1035,23 +1081,14 @@ __device__ __forceinline__ void op_combine(KArgs& a, Smem& s, const Instr in, ui
     __syncthreads();
   }
   if (mega) trace_mark(a, idx, 3);
-  auto part = [&](int e) { return staged ? s.x[e] : ld_cg(base + e); };
-  for (int o = threadIdx.x; o < r * HD; o += NT) {
-    const int h = o / HD;
-    float m = -INFINITY;
-    for (int sp = 0; sp < a.NS; ++sp) m = fmaxf(m, part(sp * slot_sz + r * HD + h));
-    float num = 0.f, den = 0.f;
-    for (int sp = 0; sp < a.NS; ++sp) {
-      const float ms = part(sp * slot_sz + r * HD + h);
-      if (ms == -INFINITY) continue;
-      const float w = expf(ms - m);
-      num = fmaf(w, part(sp * slot_sz + o), num);
-      den = fmaf(w, part(sp * slot_sz + r * HD + r + h), den);
-    }
-    st_cg(out + o, num / den);
-  }
+  // Splits are read eight at a time with clamped indices, so the loads of a
+  // group are independent of each other and of the running max / sums (one
+  // shared-memory round trip per eight splits rather than per split).
+  if (staged) combine_rows<HD>(s.x, out, r, a.NS, slot_sz, [](const float* p) { return *p; });
+  else combine_rows<HD>(base, out, r, a.NS, slot_sz, [](const float* p) { return ld_cg(p); });
   if (mega) signal_tile(a, in);
 }
+
 
 // ----------------------------------------------------------------------------- dispatch
 

@@ -4,6 +4,9 @@
     python -m tile_synchronized_decoder_amd.profiling traffic FETCH_counter_collection.csv \
         WRITE_counter_collection.csv --kernel mk_interp --copy-mib 1024 --algorithmic BYTES --command "..."
 
+    python -m tile_synchronized_decoder_amd.profiling mfma RUN_counter_collection.csv \
+        --kernel mk_interp_prefill --flops FLOPS --command "..."
+
 `traffic` turns the FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch) of
 one kernel into HBM bytes per launch.  Each counter is scaled by what it reads
 for a plain device copy of known size in the same run (rocclr's copyBuffer
@@ -98,6 +101,32 @@ def traffic_markdown(fetch_csv: str, write_csv: str, kernel: str, copy_mib: int,
     return "\n".join(lines)
 
 
+def mfma_markdown(pmc_csv: str, kernel: str, flops: int, command: str) -> str:
+    """Matrix-core evidence for the kernels of one --pmc run that collected the
+    derived counters MfmaUtil (busy cycles of the MFMA units over all SIMDs and
+    the GPU's active cycles) and MfmaFlopsBF16 (bf16 MFMA operations)."""
+    util = _per_kernel(pmc_csv, "MfmaUtil")
+    fl = _per_kernel(pmc_csv, "MfmaFlopsBF16")
+    lines = ["# Matrix-core use per dispatch from hardware counters", "",
+             "Command:", "", "```", command, "```", "",
+             "| kernel | dispatches | MfmaUtil % (median) | bf16 MFMA FLOP per dispatch (median) |",
+             "|---|---|---|---|"]
+    for name in sorted(set(util) | set(fl), key=lambda n: -(_median(fl, n) or 0)):
+        u, f = _median(util, name), _median(fl, name)
+        if not f:
+            continue
+        short = name.replace("|", "/")
+        short = short if len(short) <= 80 else short[:77] + "..."
+        lines.append(f"| `{short}` | {len(fl.get(name, []))} | {u or 0:.1f} | {f:.4g} |")
+    f_k, u_k = _median(fl, kernel), _median(util, kernel)
+    if f_k:
+        lines += ["", f"Kernel `{kernel}`: algorithmic matrix FLOP per launch {flops}; the counters count "
+                  f"{f_k:.6g} ({f_k / flops:.4f} x algorithmic); MFMA units busy {u_k:.1f}% of the active cycles.",
+                  "", f"mfma_util_percent: {u_k:.2f}", f"mfma_flops_per_launch: {int(round(f_k))}",
+                  f"algorithmic_flops_per_launch: {flops}", ""]
+    return "\n".join(lines)
+
+
 def read_traffic(path: str) -> Optional[int]:
     """The traffic figure of a summary, or None when it is missing or the kernel
     sources changed since it was taken."""
@@ -129,9 +158,16 @@ def main():
     t.add_argument("--copy-mib", type=int, required=True)
     t.add_argument("--algorithmic", type=int, required=True)
     t.add_argument("--command", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("csv")
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--flops", type=int, required=True)
+    m.add_argument("--command", required=True)
     a = ap.parse_args()
     if a.what == "stats":
         print(stats_markdown(a.csv, a.command), end="")
+    elif a.what == "mfma":
+        print(mfma_markdown(a.csv, a.kernel, a.flops, a.command), end="")
     else:
         print(traffic_markdown(a.fetch_csv, a.write_csv, a.kernel, a.copy_mib, a.algorithmic, a.command), end="")
 
