@@ -78,13 +78,17 @@ def cpu_baseline(wl, raw_layers, raw_global, budget_s: float = 20.0) -> dict:
     t0 = time.time()
     model = N.prepare(m, raw_layers, raw_global)
     K, V = W.gen.kv_cache(m, r)
-    tokens = W.gen.decode_tokens(m, r)
+    tokens = W.gen.decode_tokens(m, r) if m.has_embed else None
+    x0 = None if m.has_embed else W.gen.input_rows(m, r)
     prep = time.time() - t0
     steps, spent = 0, 0.0
     while steps < r.steps and (steps == 0 or spent + spent / steps <= budget_s):
         ctx = [p + steps for p in r.ctx0]
         t1 = time.time()
-        N.decode_step(model, K, V, ctx, tokens=tokens[steps])
+        if m.has_embed:
+            N.decode_step(model, K, V, ctx, tokens=tokens[steps])
+        else:
+            N.decode_step(model, K, V, ctx, x0=x0[steps])
         spent += time.time() - t1
         steps += 1
     cores = len(os.sched_getaffinity(0))
@@ -179,7 +183,10 @@ def main():
                                    "unit": "TFLOP/s", "frac": round(best / MFMA_BF16_PEAK_TFLOPS, 4),
                                    "traffic": None}
         del wsp
-    tok_all = torch.from_numpy(tokens.astype(np.int32)).cuda()                       # [steps, B]
+    # input rows: token ids, or for a model without an embedding its given rows [steps, B, H]
+    tok_all = torch.from_numpy(tokens.astype(np.int32)).cuda() if m.has_embed else None
+    x0_all = None if m.has_embed else torch.from_numpy(W.gen.input_rows(m, r)).cuda()
+    x0_buf = None if m.has_embed else torch.empty_like(x0_all[0])
     ctx_all = torch.tensor([[p + t for p in r.ctx0] for t in range(r.steps)], dtype=torch.int32,
                            device="cuda")
     logits = torch.empty((B, m.vocab), dtype=torch.float32, device="cuda")
@@ -191,14 +198,25 @@ def main():
     log(f"[bench] {wl.name}: {q.nbytes(T.MK_PART_INSTR) // 32} instructions, queue "
         f"{q.nbytes(T.MK_PART_DEVICE) / 1e6:.2f} MB, workspace {ws.numel() / 1e6:.1f} MB")
 
-    def step(t, mode, timing=None):
-        tok_buf.copy_(tok_all[t % r.steps])
+    def set_inputs(t):
+        if m.has_embed:
+            tok_buf.copy_(tok_all[t % r.steps])
+        else:
+            x0_buf.copy_(x0_all[t % r.steps])
         ctx_buf.copy_(ctx_all[t % r.steps])
-        T.mk_decode_step(q, dq, dm.w, dkv.kv, tok_buf, None, ctx_buf, B, ws, None, None, mode)
+
+    def launch(mode, stream_=None):
+        T.mk_decode_step(q, dq, dm.w, dkv.kv, tok_buf if m.has_embed else None, x0_buf, ctx_buf, B, ws, None,
+                         None, mode, stream=stream_)
+
+    def step(t, mode, timing=None):
+        set_inputs(t)
+        launch(mode)
         if timing is not None:
             timing.append(torch.cuda.Event(enable_timing=True))
             timing[-1].record(stream)
-        T.mk_lm_head(q, dm.w, ws, logits, nxt)
+        if m.has_lm_head:
+            T.mk_lm_head(q, dm.w, ws, logits, nxt)
 
     if args.copy_calibration:
         src = torch.ones(args.copy_calibration * 2 ** 20 // 4, dtype=torch.float32, device="cuda")
@@ -219,17 +237,16 @@ def main():
             torch.cuda.synchronize()
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
-                T.mk_decode_step(q, dq, dm.w, dkv.kv, tok_buf, None, ctx_buf, B, ws, None, None, mode,
-                                 stream=torch.cuda.current_stream())
-                T.mk_lm_head(q, dm.w, ws, logits, nxt, stream=torch.cuda.current_stream())
+                launch(mode, torch.cuda.current_stream())
+                if m.has_lm_head:
+                    T.mk_lm_head(q, dm.w, ws, logits, nxt, stream=torch.cuda.current_stream())
             torch.cuda.synchronize()
 
         def run(t, marks=None):
             if graph is None:
                 step(t, mode, marks)
             else:
-                tok_buf.copy_(tok_all[t % r.steps])
-                ctx_buf.copy_(ctx_all[t % r.steps])
+                set_inputs(t)
                 graph.replay()
 
         for t in range(args.warmup):

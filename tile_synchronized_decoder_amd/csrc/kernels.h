@@ -47,7 +47,7 @@ constexpr int LM_ROWS = 64;             // vocabulary rows per LM-head workgroup
 // input rows, where the staged inputs need the room (32 x 512 floats per chunk)
 // Weight lines (1 KB) in flight per wave.  Batched GEMVs do more arithmetic per
 // line and need the shared memory for their inputs, so their rings are shorter.
-constexpr int ring_lines_for(int nb) { return nb <= 2 ? 24 : nb <= 8 ? 16 : 8; }
+constexpr int ring_lines_for(int nb) { return nb <= 2 ? 24 : 16; }
 template <int NB> constexpr int ring_lines() { return ring_lines_for(NB); }
 constexpr uint32_t ERR_TIMEOUT = 1, ERR_OPCODE = 2, ERR_CONTEXT = 3, ERR_TOKEN = 4;
 
@@ -612,10 +612,10 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, 
   return true;
 }
 
-// Rows per wave per pass: 4 (16-row passes) for a few input rows, 2 for many
+// Rows per wave per pass: 4 (16-row passes) up to 16 input rows, 2 for 32
 // (register pressure).  Tiles of at most 8 rows always use 2, so no wave
 // streams placeholder rows.
-template <int NB> constexpr int rpw_for() { return NB >= 16 ? 2 : 4; }
+template <int NB> constexpr int rpw_for() { return NB >= 32 ? 2 : 4; }
 
 // The weight rows a GEMV instruction streams (op, layer, columns [a0, a1)),
 // or false for other ops.
