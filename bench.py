@@ -108,6 +108,8 @@ def main():
     ap.add_argument("--workers-per-cu", type=int, default=1)
     ap.add_argument("--queues", type=int, default=0, help="sub-queues (0: the workload's plan)")
     ap.add_argument("--tiles", default="", help="override tile widths, e.g. tq=16,to=8,tf=16,td=8,kb=256")
+    ap.add_argument("--gemv-pipe", type=int, default=0,
+                    help="decode GEMV weight issue: 0 by shape, 1 pipelined, 2 compiler-ordered")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--modes", default="mega,kpo,kpo_graph")
@@ -135,6 +137,7 @@ def main():
     K_steps = min(args.steps, r.steps)
     torch.cuda.set_device(0)
     T.mk_set_option(T.MK_OPT_WORKERS_PER_CU, args.workers_per_cu)
+    T.mk_set_option(T.MK_OPT_GEMV_PIPE, args.gemv_pipe)
 
     t0 = time.time()
     raw_layers = W.gen.all_layer_weights(m, r.seed)

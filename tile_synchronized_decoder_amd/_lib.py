@@ -18,7 +18,8 @@ MK_MEGAKERNEL, MK_KERNEL_PER_OP = 0, 1
 MK_PART_META, MK_PART_INSTR, MK_PART_WAITS, MK_PART_TARGETS, MK_PART_DEVICE = range(5)
 (MK_T_X, MK_T_QKV, MK_T_OPART, MK_T_ATT, MK_T_HRES, MK_T_ACT, MK_T_COUNTERS, MK_T_HEADS,
  MK_T_ERROR, MK_T_LMPART) = range(10)
-MK_OPT_WORKERS_PER_CU, MK_OPT_SPIN_LIMIT, MK_OPT_NUM_CUS, MK_OPT_TRACE_BUFFER, MK_OPT_TRACE_BYTES = range(5)
+(MK_OPT_WORKERS_PER_CU, MK_OPT_SPIN_LIMIT, MK_OPT_NUM_CUS, MK_OPT_TRACE_BUFFER, MK_OPT_TRACE_BYTES,
+ MK_OPT_GEMV_PIPE) = range(6)
 
 
 class mk_config(C.Structure):

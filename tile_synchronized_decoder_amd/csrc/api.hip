@@ -73,6 +73,7 @@ struct Options {
   uint32_t spin_limit = 1u << 22;
   unsigned long long* trace = nullptr;   // device buffer, 64 bytes per instruction
   size_t trace_bytes = 0;
+  int gemv_pipe = 0;                     // 0: by shape, 1: pipelined issue, 2: compiler-ordered issue
 };
 Options g_opt;
 
@@ -303,6 +304,7 @@ mk_status mk_decode_step(const mk_queue* q, const void* d_queue, const mk_weight
   a.tokens = d_tokens; a.x0 = d_x0; a.ctx_lens = d_ctx_lens;
   a.logits = d_logits; a.next = d_next;
   a.spin_limit = g_opt.spin_limit;
+  a.gemv_pipe = g_opt.gemv_pipe;
   a.trace = (g_opt.trace && g_opt.trace_bytes >= 64 * q->instr.size()) ? g_opt.trace : nullptr;
 
   // without an embedding the input rows are copied into X_0 by the first launch
@@ -389,6 +391,7 @@ mk_status mk_prefill(const mk_queue* q, const void* d_queue, const mk_weights* w
   fill_args(q, d_queue, w, kv, d_workspace, o, a);
   a.tokens = d_tokens; a.seq_len = seq_len; a.kv_row = kv_row; a.M_cache = kv->rows;
   a.spin_limit = g_opt.spin_limit;
+  a.gemv_pipe = g_opt.gemv_pipe;
   a.trace = (g_opt.trace && g_opt.trace_bytes >= 64 * q->instr.size()) ? g_opt.trace : nullptr;
   const Table t = table_prefill();
   hipError_t e = hipSuccess;
@@ -447,6 +450,9 @@ mk_status mk_set_option(int32_t key, int64_t value) {
     case MK_OPT_TRACE_BYTES:
       if (value < 0) FAIL(MK_EINVAL, "negative trace size");
       g_opt.trace_bytes = (size_t)value; return MK_OK;
+    case MK_OPT_GEMV_PIPE:
+      if (value < 0 || value > 2) FAIL(MK_EINVAL, "GEMV issue mode must be 0, 1 or 2");
+      g_opt.gemv_pipe = (int)value; return MK_OK;
 
     default: FAIL(MK_EINVAL, "unknown or read-only option %d", key);
   }
@@ -459,6 +465,7 @@ int64_t mk_get_option(int32_t key) {
     case MK_OPT_NUM_CUS: return num_cus();
     case MK_OPT_TRACE_BUFFER: return (int64_t)(uintptr_t)g_opt.trace;
     case MK_OPT_TRACE_BYTES: return (int64_t)g_opt.trace_bytes;
+    case MK_OPT_GEMV_PIPE: return g_opt.gemv_pipe;
     default: return -1;
   }
 }

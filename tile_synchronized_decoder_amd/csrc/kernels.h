@@ -47,7 +47,10 @@ constexpr int LM_ROWS = 64;             // vocabulary rows per LM-head workgroup
 // input rows, where the staged inputs need the room (32 x 512 floats per chunk)
 // Weight lines (1 KB) in flight per wave.  Batched GEMVs do more arithmetic per
 // line and need the shared memory for their inputs, so their rings are shorter.
-constexpr int ring_lines_for(int nb) { return nb <= 2 ? 24 : 16; }
+#ifndef MK_RING_LINES_SMALL
+#define MK_RING_LINES_SMALL 24
+#endif
+constexpr int ring_lines_for(int nb) { return nb <= 2 ? MK_RING_LINES_SMALL : 16; }
 template <int NB> constexpr int ring_lines() { return ring_lines_for(NB); }
 constexpr uint32_t ERR_TIMEOUT = 1, ERR_OPCODE = 2, ERR_CONTEXT = 3, ERR_TOKEN = 4;
 
@@ -87,6 +90,7 @@ struct Args {
   int seq_len, kv_row, M_cache;
   uint32_t lds_ring;             // bytes of the ring / prefill tile region
   const float* lm_x;             // LM head input rows
+  int gemv_pipe;                 // decode GEMV weight issue: 0 by shape, 1 pipelined, 2 compiler-ordered
 };
 
 // Device code reads the arguments in place, through a constant-address-space
@@ -494,7 +498,7 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, 
   uint8_t* ring = s.ring + wave * RING_LINES * 1024;
   constexpr int GL = RPW * G::LPI;                     // lines per iteration group
   constexpr int NG = RING_LINES / GL;                  // groups in the ring
-  static_assert(NG >= 2 && RING_LINES % GL == 0, "ring holds whole iteration groups");
+  static_assert(NG >= 2, "ring holds at least two iteration groups");   // whole groups; spare lines unused
   const int ngroups = npass * iters;                   // groups this wave consumes
   // refill cursor: the next (chunk, pass, iteration) to issue
   int rb = 0, re = min(ipc, iters), rp = 0, ri = 0;   // chunk [rb, re) of iterations
@@ -698,7 +702,8 @@ __device__ __forceinline__ void op_gemv(KArgs& a, Smem& s, const Instr in, uint3
   // the compiler does not serialise the ring (it would wait for every line in
   // flight before each read of the staged inputs); a single input row of a
   // smaller model measured faster with the serialised ring.
-  if (NB > 1 || a.H >= 4096) {
+  const bool pipe = a.gemv_pipe == 1 || (a.gemv_pipe == 0 && (NB > 1 || a.H >= 4096));
+  if (pipe) {
     if constexpr (RPW != 2) {
       if (rows <= 2 * NWAVE) { op_gemv_rpw<WT, NB, 2, true>(a, s, in, idx, mega); return; }
     }
