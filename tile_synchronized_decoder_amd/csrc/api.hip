@@ -96,6 +96,9 @@ struct Layout {
   size_t X, QKV, OPART, ATT, HRES, ACT, LMV, LMI, CTR, HEADS, ERR, total;
   size_t sX, sQKV, sOP, sATT, sHRES, sACT;   // per-layer strides in floats
   int lm_blocks;
+  // prefill only: bf16 GEMM operands and per-row sums of squares (after ERR)
+  size_t XB, XSS, HB, HSS, ATTB, ACTB;
+  size_t sXB, sXSS, sATTB, sACTB;            // per-layer strides in elements
 };
 
 Layout layout(const mk_queue* q) {
@@ -123,6 +126,22 @@ Layout layout(const mk_queue* q) {
   o.CTR = off; off += up256(q->targets.size() * 4);
   o.HEADS = off; off += up256((size_t)q->plan.n_queues * 128);
   o.ERR = off; off += 256;
+  if (q->plan.mode == MK_PREFILL) {
+    // bf16 copies of the GEMM activation operands, written by their producer
+    // tiles (with the consumer's RMSNorm gain folded in for X and HRES), and
+    // sums of squares of X / HRES rows per 128-column tile
+    const size_t nss = (c.hidden + 127) / 128;
+    o.sXB = up256(M * c.hidden * 2) / 2;
+    o.sXSS = up256(M * nss * 4) / 4;
+    o.sATTB = up256(M * c.n_q_heads * hd * 2) / 2;
+    o.sACTB = up256(M * c.ffn * 2) / 2;
+    o.XB = off; off += L * o.sXB * 2;
+    o.XSS = off; off += L * o.sXSS * 4;
+    o.HB = off; off += L * o.sXB * 2;
+    o.HSS = off; off += L * o.sXSS * 4;
+    o.ATTB = off; off += L * o.sATTB * 2;
+    o.ACTB = off; off += L * o.sACTB * 2;
+  }
   o.total = off;
   return o;
 }
@@ -148,7 +167,7 @@ struct LdsLayout { uint32_t res, x, ring, uni, bytes; };
 // Bytes of the prefill tile region: the larger of a GEMM tile (two stages of a
 // 128 x 64 activation tile, three of a 256 x 64 weight tile, row statistics)
 // and an attention tile (Q, a 64-key K and V^T block, scores, probabilities).
-constexpr uint32_t kPrefillGemmBytes = 2 * 128 * 128 + 3 * 256 * 128 + (256 + 128) * 4;
+constexpr uint32_t kPrefillGemmBytes = 3 * 128 * 128 + 3 * 256 * 128 + (256 + 128) * 4;
 constexpr uint32_t kPrefillAttnBytes = 2 * 128 * 128 + 2 * 64 * 128 + 128 * 64 * 2 + 128 * 64 * 4 + 128 * 64 * 2 + 3 * 128 * 4;
 
 // Dynamic shared memory of one workgroup, in floats: header (index, norm
@@ -208,6 +227,12 @@ void fill_args(const mk_queue* q, const void* d_queue, const mk_weights* w, cons
   a.sX = o.sX; a.sQKV = o.sQKV; a.sOP = o.sOP; a.sATT = o.sATT; a.sHRES = o.sHRES; a.sACT = o.sACT;
   a.lm_val = reinterpret_cast<float*>(ws + o.LMV); a.lm_idx = reinterpret_cast<int*>(ws + o.LMI);
   a.lm_blocks = o.lm_blocks;
+  if (q->plan.mode == MK_PREFILL) {
+    a.XB = reinterpret_cast<uint16_t*>(ws + o.XB); a.XSS = reinterpret_cast<float*>(ws + o.XSS);
+    a.HB = reinterpret_cast<uint16_t*>(ws + o.HB); a.HSS = reinterpret_cast<float*>(ws + o.HSS);
+    a.ATTB = reinterpret_cast<uint16_t*>(ws + o.ATTB); a.ACTB = reinterpret_cast<uint16_t*>(ws + o.ACTB);
+    a.sXB = o.sXB; a.sXSS = o.sXSS; a.sATTB = o.sATTB; a.sACTB = o.sACTB;
+  }
   a.counters = reinterpret_cast<uint32_t*>(ws + o.CTR); a.heads = reinterpret_cast<uint32_t*>(ws + o.HEADS);
   a.err = reinterpret_cast<uint32_t*>(ws + o.ERR);
   a.instr = reinterpret_cast<const Instr*>(qd + q->dev_instr_off);
@@ -324,7 +349,7 @@ mk_status mk_decode_step(const mk_queue* q, const void* d_queue, const mk_weight
     hipLaunchKernelGGL(reset_kernel, dim3((nr + 255) / 256 + 1), dim3(256), 0, stream, a.counters, nr, a.heads,
                        a.n_queues, a.err);
     e = hipGetLastError();
-    if (e == hipSuccess) e = t.mega(a, grid, stream);
+    if (e == hipSuccess) e = t.mega(a, grid, g_opt.workers_per_cu, stream);
   } else {
     for (const mk::Segment& sg : q->segments) {
       e = t.kpo(a, sg.op, sg.first, sg.count, stream);
@@ -332,6 +357,9 @@ mk_status mk_decode_step(const mk_queue* q, const void* d_queue, const mk_weight
     }
   }
   if (e == hipSuccess && c.has_lm_head && (d_logits || d_next)) e = launch_lm(t, a, d_next != nullptr, stream);
+  if (e == hipErrorCooperativeLaunchTooLarge)
+    FAIL(MK_ENOTSUP, "%d megakernel workgroups per compute unit do not fit its registers / shared memory",
+         g_opt.workers_per_cu);
   if (e != hipSuccess) FAIL(MK_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
   return MK_OK;
 }
@@ -374,7 +402,8 @@ mk_status mk_prefill(const mk_queue* q, const void* d_queue, const mk_weights* w
   if (c.dtype != MK_BF16 || !c.has_embed) FAIL(MK_ENOTSUP, "prefill needs a bf16 model with an embedding");
   if (c.head_dim != 128 || q->plan.bm != 128 || q->plan.bn != 128)
     FAIL(MK_ENOTSUP, "prefill tiles are 128 x 128 over 128-wide heads");
-  if (c.hidden % 64 || c.ffn % 64 || (c.n_q_heads * c.head_dim) % 64) FAIL(MK_ENOTSUP, "prefill K dimensions must be multiples of 64");
+  if (c.hidden % 128 || c.ffn % 64 || (c.n_q_heads * c.head_dim) % 64)
+    FAIL(MK_ENOTSUP, "prefill needs the hidden size a multiple of 128 and the other K dimensions of 64");
   if (seq_len < 1 || seq_len > q->plan.rows) FAIL(MK_EINVAL, "seq_len %d outside 1..%d", seq_len, q->plan.rows);
   if (kv->rows < 1 || kv_row < 0 || kv_row >= kv->rows) FAIL(MK_EINVAL, "kv_row outside the cache rows");
   if (exec_mode != MK_MEGAKERNEL && exec_mode != MK_KERNEL_PER_OP) FAIL(MK_EINVAL, "unknown exec_mode");
@@ -402,7 +431,7 @@ mk_status mk_prefill(const mk_queue* q, const void* d_queue, const mk_weights* w
     hipLaunchKernelGGL(reset_kernel, dim3((nr + 255) / 256 + 1), dim3(256), 0, stream, a.counters, nr, a.heads,
                        a.n_queues, a.err);
     e = hipGetLastError();
-    if (e == hipSuccess) e = t.mega(a, grid, stream);
+    if (e == hipSuccess) e = t.mega(a, grid, g_opt.workers_per_cu, stream);
   } else {
     for (const mk::Segment& sg : q->segments) {
       e = t.kpo(a, sg.op, sg.first, sg.count, stream);
@@ -421,6 +450,9 @@ mk_status mk_prefill(const mk_queue* q, const void* d_queue, const mk_weights* w
     lm.logits = d_logits_last; lm.next = d_next;
     e = launch_lm(pick_table(c.dtype, 1), lm, d_next != nullptr, stream);
   }
+  if (e == hipErrorCooperativeLaunchTooLarge)
+    FAIL(MK_ENOTSUP, "%d megakernel workgroups per compute unit do not fit its registers / shared memory",
+         g_opt.workers_per_cu);
   if (e != hipSuccess) FAIL(MK_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
   return MK_OK;
 }

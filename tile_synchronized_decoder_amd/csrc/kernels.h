@@ -91,6 +91,11 @@ struct Args {
   uint32_t lds_ring;             // bytes of the ring / prefill tile region
   const float* lm_x;             // LM head input rows
   int gemv_pipe;                 // decode GEMV weight issue: 0 by shape, 1 pipelined, 2 compiler-ordered
+  // prefill: bf16 GEMM operands (X and HRES with the consumer's RMSNorm gain
+  // applied), per-row sums of squares of X / HRES per 128-column tile
+  uint16_t* XB; uint16_t* HB; uint16_t* ATTB; uint16_t* ACTB;
+  float* XSS; float* HSS;
+  size_t sXB, sXSS, sATTB, sACTB;              // per-layer strides (elements)
 };
 
 // Device code reads the arguments in place, through a constant-address-space
@@ -1376,6 +1381,17 @@ inline hipError_t allow_lds(K kernel, uint32_t bytes, uint32_t& granted) {
   return e;
 }
 
+// A persistent interpreter needs all of its workgroups resident at once (a
+// worker waits on tiles other workers produce): refuse a launch of `per_cu`
+// workgroups per compute unit that registers or shared memory do not allow.
+template <typename K>
+inline hipError_t check_resident(K kernel, uint32_t lds_bytes, int per_cu) {
+  int fit = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, kernel, NT, lds_bytes);
+  if (e != hipSuccess) return e;
+  return fit >= per_cu ? hipSuccess : hipErrorCooperativeLaunchTooLarge;
+}
+
 #ifdef MK_PREFILL_UNIT
 #include "prefill.h"
 
@@ -1442,9 +1458,10 @@ __global__ __launch_bounds__(NT) void kpo_prefill(Args args, uint32_t first) {
 }
 
 struct PrefillLaunch {
-  static hipError_t mega(const Args& a, int grid, hipStream_t st) {
+  static hipError_t mega(const Args& a, int grid, int per_cu, hipStream_t st) {
     static uint32_t granted = 64 * 1024;
     hipError_t e = allow_lds(mk_interp_prefill, a.lds_bytes, granted);
+    if (e == hipSuccess) e = check_resident(mk_interp_prefill, a.lds_bytes, per_cu);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(mk_interp_prefill, dim3(grid), dim3(NT), a.lds_bytes, st, a);
     return hipGetLastError();
@@ -1473,9 +1490,10 @@ struct PrefillLaunch {
 
 template <typename WT, int NB>
 struct Launch {
-  static hipError_t mega(const Args& a, int grid, hipStream_t st) {
+  static hipError_t mega(const Args& a, int grid, int per_cu, hipStream_t st) {
     static uint32_t granted = 64 * 1024;
     hipError_t e = allow_lds(mk_interp<WT, NB>, a.lds_bytes, granted);
+    if (e == hipSuccess) e = check_resident(mk_interp<WT, NB>, a.lds_bytes, per_cu);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((mk_interp<WT, NB>), dim3(grid), dim3(NT), a.lds_bytes, st, a);
     return hipGetLastError();
@@ -1516,7 +1534,7 @@ struct Launch {
 };
 
 struct Table {
-  hipError_t (*mega)(const Args&, int, hipStream_t);
+  hipError_t (*mega)(const Args&, int, int, hipStream_t);
   hipError_t (*kpo)(const Args&, uint32_t, uint32_t, uint32_t, hipStream_t);
   hipError_t (*lm)(const Args&, hipStream_t);
 };

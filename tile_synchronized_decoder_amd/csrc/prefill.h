@@ -29,8 +29,14 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7
 
 __device__ __forceinline__ bf16x8 as_bf16x8(v4u v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (lo in the low half), round to nearest even:
+// one v_cvt_pk_bf16_f32 (the same result as f32_to_bf16 for finite values).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // One chunk (8 consecutive k) of an operand row from a swizzled 128-byte-row tile.
@@ -49,6 +55,9 @@ __device__ __forceinline__ v4u ld_cg_v4u(const void* p) {
   return v4u{(uint32_t)x, (uint32_t)(x >> 32), (uint32_t)y, (uint32_t)(y >> 32)};
 }
 __device__ __forceinline__ void st_cg_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_cg_u64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -74,9 +83,10 @@ __device__ __forceinline__ void rope_cs(KArgs& a, int pos, int i, float& c, floa
 // ---------------------------------------------------------------------------- GEMM tile
 
 struct PGemm {
-  const float* x;          // A rows (fp32 workspace), leading dimension K
-  const float* gain;       // RMSNorm gain applied to A (nullable)
-  bool norm;               // scale each output row by RMSNorm(A row)
+  const uint16_t* xb;      // A rows (bf16, any RMSNorm gain already applied), leading dimension K
+  const float* ss;         // RMSNorm: per-row sums of squares of the fp32 rows per 128-column tile
+                           // [row][nss], or null (no normalisation)
+  int nss;
   const uint16_t* w0;      // weight rows for the first 128 columns
   const uint16_t* w1;      // second matrix (gate/up: up rows), or null
   int n0, n_total;         // first output column; rows of the weight matrix
@@ -100,41 +110,17 @@ __device__ __forceinline__ void p_issue_b(const PGemm& g, uint8_t* b, int ks, in
   }
 }
 
-// Activation operand of K step ks: this thread's 32 floats of one row (rows
-// past the tile read as zeros).  The loads are only issued here; p_store_a
-// consumes them, so they overlap the matrix-core work of the current step.
-struct PARegs { float4 v[8]; };
-
-__device__ __forceinline__ void p_load_a(const PGemm& g, int ks, PARegs& r) {
-  const int t = threadIdx.x, row = t >> 1, half = t & 1;
-  const int k0 = ks * PKS + half * 32;
-  if (row < g.rows) {
-    const float* src = g.x + (size_t)(g.r0 + row) * g.K + k0;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) r.v[q] = ld_act4(src + 4 * q);
-  } else {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) r.v[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-}
-
-// Sum of squares (RMSNorm), gain, bf16 rounding, swizzled store into LDS.
-__device__ __forceinline__ void p_store_a(const PGemm& g, int ks, uint8_t* a, PARegs& r, float& ss) {
-  const int t = threadIdx.x, row = t >> 1, half = t & 1;
-  const int k0 = ks * PKS + half * 32;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    ss += r.v[q].x * r.v[q].x + r.v[q].y * r.v[q].y + r.v[q].z * r.v[q].z + r.v[q].w * r.v[q].w;
-    if (g.gain) {
-      const float4 gg = *reinterpret_cast<const float4*>(g.gain + k0 + 4 * q);
-      r.v[q].x *= gg.x; r.v[q].y *= gg.y; r.v[q].z *= gg.z; r.v[q].w *= gg.w;
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float4 u = r.v[2 * q], w = r.v[2 * q + 1];
-    v4u pk = {pack_bf16(u.x, u.y), pack_bf16(u.z, u.w), pack_bf16(w.x, w.y), pack_bf16(w.z, w.w)};
-    *reinterpret_cast<v4u*>(a + row * 128 + swz(row, half * 4 + q) * 16) = pk;
+// Issue the activation DMA of K step ks into LDS tile `abuf` (128 rows of
+// 128 B, same swizzle as the weights).  Rows past the tile re-read the tile's
+// first row; their products are never stored.  The activation lines were
+// written once in this launch by their producer tiles, with device-coherent
+// stores, and are read only after those tiles' barriers (see ld_act).
+__device__ __forceinline__ void p_issue_a(const PGemm& g, uint8_t* abuf, int ks, int wave, int lane) {
+  for (int d = wave; d < PBM / 8; d += NWAVE) {
+    const int row = d * 8 + lane / 8;
+    const int c = (lane % 8) ^ (row & 7);
+    const uint16_t* src = g.xb + (size_t)(g.r0 + (row < g.rows ? row : 0)) * g.K + ks * PKS + c * 8;
+    dma_lds16<0>(src, abuf + d * 1024);
   }
 }
 
@@ -165,18 +151,20 @@ __device__ __forceinline__ void p_mfma_step(const uint8_t* a, const uint8_t* b, 
   }
 }
 
-// LDS of a GEMM tile: two activation stages, three weight stages, then the
-// row statistics ([NT] partial sums, then [PBM] row scales).
+// LDS of a GEMM tile: three activation stages, three weight stages, then the
+// row statistics ([NT] scratch, then [PBM] row scales).
 constexpr int P_BSTAGES = 3;
 __device__ __forceinline__ float* p_row_stats(Smem& s, bool two_mats) {
-  return reinterpret_cast<float*>(s.ring + 2 * PBM * 128 + P_BSTAGES * (two_mats ? 2 : 1) * PBN * 128);
+  return reinterpret_cast<float*>(s.ring + P_BSTAGES * PBM * 128 + P_BSTAGES * (two_mats ? 2 : 1) * PBN * 128);
 }
 
-// Full K loop of one tile.  Weights are DMA'd two K steps ahead (three
-// stages), activations one step ahead through registers; the loads of the
-// next steps are in flight while the current step runs on the matrix cores.
-// The first two weight steps are issued before the tile waits (`mega`).
-// Leaves the row scales (RMSNorm factors, or 1) in p_row_stats()[NT ..].
+// Full K loop of one tile.  Activations (bf16) and weights are DMA'd into
+// LDS two K steps ahead of the matrix cores (three stages each); nothing in
+// the loop is a register load, so the only waits are the explicit ones, and
+// the loads of the next two steps stay in flight while the current step runs.
+// The first two weight steps are issued before the tile waits (`mega`), the
+// activations after it.  Leaves the row scales (RMSNorm factors, or 1) in
+// p_row_stats()[NT ..].
 __device__ __forceinline__ bool p_gemm(KArgs& a, Smem& s, const PGemm& g, PAcc& acc, PAcc* acc_up, bool mega,
                                        const Instr in, uint32_t idx) {
   const int t = threadIdx.x, lane = t & 63;
@@ -184,14 +172,39 @@ __device__ __forceinline__ bool p_gemm(KArgs& a, Smem& s, const PGemm& g, PAcc& 
   const int wm = wave >> 1, wn = wave & 1;
   const bool two = g.w1 != nullptr;
   const int bbytes = (two ? 2 : 1) * PBN * 128;
-  uint8_t* abase = s.ring;                               // two activation stages
-  uint8_t* bbase = s.ring + 2 * PBM * 128;
+  constexpr int ABYTES = PBM * 128;
+  uint8_t* abase = s.ring;                               // three activation stages
+  uint8_t* bbase = s.ring + P_BSTAGES * ABYTES;          // three weight stages
   float* rs = p_row_stats(s, two);
   const int nks = g.K / PKS;
 
   p_issue_b(g, bbase, 0, wave, lane);
   if (nks > 1) p_issue_b(g, bbase + bbytes, 1, wave, lane);
   if (mega && !wait_tiles(a, in, idx)) { wait_vm<0>(); return false; }
+  // row scales from the producers' sums of squares: two threads per row, each
+  // summing half of the column tiles in order (loads issued eight at a time),
+  // then first half + second half.  Done before the activation DMAs so the
+  // wait for these loads does not also wait for them.
+  {
+    const int row = t >> 1, half = t & 1;
+    float tot = 0.f;
+    if (g.ss) {
+      const int hn = (g.nss + 1) / 2, c0 = half * hn, c1 = min(g.nss, c0 + hn);
+      const float* p = g.ss + (size_t)(g.r0 + (row < g.rows ? row : 0)) * g.nss;
+      for (int c = c0; c < c1; c += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = c + j < c1 ? ld_act(p + c + j) : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tot += v[j];
+      }
+    }
+    const float other = __shfl_xor(tot, 1, 64);
+    const float sum = half ? other + tot : tot + other;
+    if (half == 0) rs[NT + row] = g.ss ? 1.0f / sqrtf(sum / (float)g.K + a.eps) : 1.0f;
+  }
+  p_issue_a(g, abase, 0, wave, lane);
+  if (nks > 1) p_issue_a(g, abase + ABYTES, 1, wave, lane);
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -199,42 +212,97 @@ __device__ __forceinline__ bool p_gemm(KArgs& a, Smem& s, const PGemm& g, PAcc& 
       acc.c[mi][ni] = (f32x16){};
       if (acc_up) acc_up->c[mi][ni] = (f32x16){};
     }
-  float ss = 0.f;
-  PARegs ar;
-  p_load_a(g, 0, ar);
-  wait_vm<0>();
-  p_store_a(g, 0, abase, ar, ss);
+  constexpr int NA_ = PBM / 8 / NWAVE;                   // activation DMAs per wave per step
+  // step 0's loads (and everything before them) have landed once at most step 1's are outstanding
+  if (nks > 1) {
+    if (two) wait_vm<NA_ + 2 * PBN / 8 / NWAVE>(); else wait_vm<NA_ + PBN / 8 / NWAVE>();
+  } else {
+    wait_vm<0>();
+  }
   __syncthreads();
-  int bcur = 0;                                          // stage of step ks
+  int cur = 0;                                           // stage of step ks
   for (int ks = 0; ks < nks; ++ks) {
-    const int cur = ks & 1;
     const bool more = ks + 1 < nks, more2 = ks + 2 < nks;
-    if (more) p_load_a(g, ks + 1, ar);
-    const int b2 = bcur + 2 >= P_BSTAGES ? bcur + 2 - P_BSTAGES : bcur + 2;
-    if (more2) p_issue_b(g, bbase + b2 * bbytes, ks + 2, wave, lane);
-    p_mfma_step(abase + cur * (PBM * 128), bbase + bcur * bbytes, acc, acc_up, wm, wn, lane);
+    const int c2 = cur + 2 >= P_BSTAGES ? cur + 2 - P_BSTAGES : cur + 2;
+    if (more2) {
+      p_issue_b(g, bbase + c2 * bbytes, ks + 2, wave, lane);
+      p_issue_a(g, abase + c2 * ABYTES, ks + 2, wave, lane);
+    }
+    p_mfma_step(abase + cur * ABYTES, bbase + cur * bbytes, acc, acc_up, wm, wn, lane);
     if (more) {
-      // the activations of step ks + 1 (issued before the weights of step ks + 2) and the
-      // weights of step ks + 1 (issued a step earlier) have landed once only the weight
-      // loads of step ks + 2 may still be outstanding
+      // step ks + 1's loads have landed once only step ks + 2's may be outstanding
       if (!more2) wait_vm<0>();
-      else if (two) wait_vm<2 * PBN / 8 / NWAVE>();
-      else wait_vm<PBN / 8 / NWAVE>();
-      p_store_a(g, ks + 1, abase + (cur ^ 1) * (PBM * 128), ar, ss);
+      else if (two) wait_vm<NA_ + 2 * PBN / 8 / NWAVE>();
+      else wait_vm<NA_ + PBN / 8 / NWAVE>();
     }
     __syncthreads();
-    bcur = bcur + 1 == P_BSTAGES ? 0 : bcur + 1;
+    cur = cur + 1 == P_BSTAGES ? 0 : cur + 1;
   }
   if (mega) trace_mark(a, idx, 4);
-  // row scales: each row's two threads hold halves of sum(x^2)
-  rs[t] = ss;
-  __syncthreads();
-  if (t < PBM) {
-    const float tot = rs[2 * t] + rs[2 * t + 1];
-    rs[NT + t] = g.norm ? 1.0f / sqrtf(tot / (float)g.K + a.eps) : 1.0f;
-  }
-  __syncthreads();
   return true;
+}
+
+// Write one 128 x 128 fp32 tile staged in shared memory (ct[row][col], col
+// relative to n0) as output rows: out[r][n0 + col] = ct (+ res[r][n0 + col]),
+// and optionally a bf16 copy (times gain[n0 + col] when given) and the row's
+// sum of squares over the tile's columns into ss[r][n0 / 128].  Sixteen
+// threads cover one row's 128 columns, 8 consecutive columns each, so the
+// stores of a wave are contiguous 512-byte runs.  Columns at or past ncols
+// (a multiple of 8) and rows at or past `rows` are skipped.
+struct PRowOut {
+  float* out; const float* res; int ld;      // fp32 output / residual rows, leading dimension
+  uint16_t* outb; const float* gain;          // bf16 copy (same leading dimension) or null
+  float* ss; int nss;                         // sums of squares [row][nss] or null
+  int n0, ncols, r0, rows;
+};
+
+__device__ __forceinline__ void p_write_rows(const float* ct, const PRowOut& p) {
+  const int t = threadIdx.x, sub = t & 15, c = sub * 8;
+  for (int pass = 0; pass < PBM / (NT / 16); ++pass) {
+    const int row = pass * (NT / 16) + (t >> 4);
+    const bool valid = row < p.rows && p.n0 + c < p.ncols;
+    float x[8];
+    {
+      const float4 u = *reinterpret_cast<const float4*>(ct + row * PBN + c);
+      const float4 w = *reinterpret_cast<const float4*>(ct + row * PBN + c + 4);
+      x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
+    }
+    float sq = 0.f;
+    if (valid) {
+      const size_t o = (size_t)(p.r0 + row) * p.ld + p.n0 + c;
+      if (p.res) {
+        const float4 u = ld_act4(p.res + o), w = ld_act4(p.res + o + 4);
+        x[0] += u.x; x[1] += u.y; x[2] += u.z; x[3] += u.w; x[4] += w.x; x[5] += w.y; x[6] += w.z; x[7] += w.w;
+      }
+      uint64_t* d = reinterpret_cast<uint64_t*>(p.out + o);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        st_cg_u64(d + k, (uint64_t)__float_as_uint(x[2 * k]) | ((uint64_t)__float_as_uint(x[2 * k + 1]) << 32));
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sq += x[k] * x[k];
+      if (p.outb) {
+        float y[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[k] = x[k];
+        if (p.gain) {
+          const float4 u = *reinterpret_cast<const float4*>(p.gain + p.n0 + c);
+          const float4 w = *reinterpret_cast<const float4*>(p.gain + p.n0 + c + 4);
+          y[0] *= u.x; y[1] *= u.y; y[2] *= u.z; y[3] *= u.w; y[4] *= w.x; y[5] *= w.y; y[6] *= w.z; y[7] *= w.w;
+        }
+        uint64_t* db = reinterpret_cast<uint64_t*>(p.outb + o);
+        st_cg_u64(db, (uint64_t)pack_bf16(y[0], y[1]) | ((uint64_t)pack_bf16(y[2], y[3]) << 32));
+        st_cg_u64(db + 1, (uint64_t)pack_bf16(y[4], y[5]) | ((uint64_t)pack_bf16(y[6], y[7]) << 32));
+      }
+    }
+    if (p.ss) {
+      // the 16 threads of the row, in a fixed order
+      sq += __shfl_xor(sq, 8, 16);
+      sq += __shfl_xor(sq, 4, 16);
+      sq += __shfl_xor(sq, 2, 16);
+      sq += __shfl_xor(sq, 1, 16);
+      if (sub == 0 && row < p.rows) st_cg(p.ss + (size_t)(p.r0 + row) * p.nss + p.n0 / PBN, sq);
+    }
+  }
 }
 
 // Element (row, col) of accumulator value v of block (mi, ni) of wave (wm, wn).
@@ -243,21 +311,54 @@ __device__ __forceinline__ int p_col(int wn, int ni, int lane) { return wn * 64 
 
 __device__ __forceinline__ bool p_block_live(KArgs& a, int m) { return m * PBM < a.seq_len; }
 
-// P_EMBED(m): X_0 rows of block m = embedding rows of their tokens.
+// P_EMBED(m): X_0 rows of block m = embedding rows of their tokens, plus the
+// bf16 copy times the first layer's attention-norm gain and the rows' sums of
+// squares per 128 columns (the QKV tiles' operands).  Each thread moves 8
+// consecutive columns: one 16-byte load of bf16, four 8-byte device-coherent
+// stores of fp32 and two of bf16; 16 consecutive threads cover 128 columns.
 __device__ __forceinline__ void op_p_embed(KArgs& a, const Instr in, uint32_t idx, bool mega) {
   const int m = in.a0;
   const uint16_t* E = static_cast<const uint16_t*>(a.embed);
+  const float* gain = a.attn_norm;                        // layer 0
   const int r0 = m * PBM, rows = max(0, min(PBM, a.seq_len - r0));
-  for (int e = threadIdx.x; e < rows * a.H; e += NT) {
-    const int row = e / a.H, c = e - row * a.H;
-    const int tok = a.tokens[r0 + row];
-    float v = 0.f;
-    if (tok < 0 || tok >= a.V) {
-      if (c == 0) record_error(a, ERR_TOKEN, idx, (uint32_t)(r0 + row), (uint32_t)tok, (uint32_t)a.V);
-    } else {
-      v = bf16_to_f32(E[(size_t)tok * a.H + c]);
+  const int c8 = a.H / 8;                                 // prefill needs the hidden size a multiple of 128
+  const int nss = (a.H + PBN - 1) / PBN;
+  const int n = rows * c8;                                // a multiple of 8; groups of 16 threads stay together
+  for (int e0 = 0; e0 < n; e0 += NT) {
+    const int e = e0 + threadIdx.x;
+    const bool live = e < n;
+    const int row = live ? e / c8 : 0, c = live ? (e - row * c8) * 8 : 0;
+    float sq = 0.f;
+    if (live) {
+      const int tok = a.tokens[r0 + row];
+      v4u w = {0u, 0u, 0u, 0u};
+      if (tok < 0 || tok >= a.V) {
+        if (c == 0) record_error(a, ERR_TOKEN, idx, (uint32_t)(r0 + row), (uint32_t)tok, (uint32_t)a.V);
+      } else {
+        w = *reinterpret_cast<const v4u*>(E + (size_t)tok * a.H + c);
+      }
+      float x[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {                       // the bf16 bits are the high half of each float
+        x[2 * k] = __uint_as_float(w[k] << 16);
+        x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+      }
+      const size_t o = (size_t)(r0 + row) * a.H + c;
+      uint64_t* dst = reinterpret_cast<uint64_t*>(a.X + o);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        st_cg_u64(dst + k, (uint64_t)__float_as_uint(x[2 * k]) | ((uint64_t)__float_as_uint(x[2 * k + 1]) << 32));
+#pragma unroll
+      for (int k = 0; k < 8; ++k) { sq += x[k] * x[k]; x[k] *= gain[c + k]; }
+      uint64_t* db = reinterpret_cast<uint64_t*>(a.XB + o);
+      st_cg_u64(db, (uint64_t)pack_bf16(x[0], x[1]) | ((uint64_t)pack_bf16(x[2], x[3]) << 32));
+      st_cg_u64(db + 1, (uint64_t)pack_bf16(x[4], x[5]) | ((uint64_t)pack_bf16(x[6], x[7]) << 32));
     }
-    st_cg(a.X + (size_t)(r0 + row) * a.H + c, v);
+    sq += __shfl_xor(sq, 8, 16);
+    sq += __shfl_xor(sq, 4, 16);
+    sq += __shfl_xor(sq, 2, 16);
+    sq += __shfl_xor(sq, 1, 16);
+    if (live && (threadIdx.x & 15) == 0) st_cg(a.XSS + (size_t)(r0 + row) * nss + c / PBN, sq);
   }
   if (mega) signal_tile(a, in);
 }
@@ -271,7 +372,7 @@ __device__ __forceinline__ void op_p_qkv(KArgs& a, Smem& s, const Instr in, uint
     return;
   }
   const int r0 = m * PBM, rows = min(PBM, a.seq_len - r0);
-  PGemm g{a.X + l * a.sX, a.attn_norm + (size_t)l * a.H, true,
+  PGemm g{a.XB + l * a.sXB, a.XSS + l * a.sXSS, (a.H + PBN - 1) / PBN,
           static_cast<const uint16_t*>(a.wqkv) + (size_t)l * a.NQKV * a.H, nullptr, n0, a.NQKV, a.H, r0, rows};
   PAcc acc;
   if (!p_gemm(a, s, g, acc, nullptr, mega, in, idx)) return;
@@ -321,19 +422,30 @@ __device__ __forceinline__ void op_p_qkv(KArgs& a, Smem& s, const Instr in, uint
     }
   }
   if (row < rows) {
+    // 8-byte device-coherent stores: two floats, or four bf16 of the cache row
     float* out = a.QKV + l * a.sQKV + (size_t)pos * a.NQKV + n0;
+    uint64_t* o0 = reinterpret_cast<uint64_t*>(out + part * 32);
+    uint64_t* o1 = reinterpret_cast<uint64_t*>(out + HALF + part * 32);
+    auto two = [](float lo, float hi) {
+      return (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
+    };
 #pragma unroll
-    for (int k = 0; k < 32; ++k) { st_cg(out + part * 32 + k, x0[k]); st_cg(out + HALF + part * 32 + k, x1[k]); }
+    for (int k = 0; k < 16; ++k) {
+      st_cg_u64(o0 + k, two(x0[2 * k], x0[2 * k + 1]));
+      st_cg_u64(o1 + k, two(x1[2 * k], x1[2 * k + 1]));
+    }
     if (!is_q) {
       const int gidx = hh - a.nq - (is_k ? 0 : a.nkv);
       uint16_t* cache = static_cast<uint16_t*>(is_k ? a.kc : a.vc) +
                         ((((size_t)l * a.M_cache + a.kv_row) * a.nkv + gidx) * a.ctx_max + pos) * PBN;
-      uint32_t* c0 = reinterpret_cast<uint32_t*>(cache + part * 32);
-      uint32_t* c1 = reinterpret_cast<uint32_t*>(cache + HALF + part * 32);
+      uint64_t* c0 = reinterpret_cast<uint64_t*>(cache + part * 32);
+      uint64_t* c1 = reinterpret_cast<uint64_t*>(cache + HALF + part * 32);
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        st_cg_u32(c0 + k, pack_bf16(x0[2 * k], x0[2 * k + 1]));
-        st_cg_u32(c1 + k, pack_bf16(x1[2 * k], x1[2 * k + 1]));
+      for (int k = 0; k < 8; ++k) {
+        st_cg_u64(c0 + k, (uint64_t)pack_bf16(x0[4 * k], x0[4 * k + 1]) |
+                              ((uint64_t)pack_bf16(x0[4 * k + 2], x0[4 * k + 3]) << 32));
+        st_cg_u64(c1 + k, (uint64_t)pack_bf16(x1[4 * k], x1[4 * k + 1]) |
+                              ((uint64_t)pack_bf16(x1[4 * k + 2], x1[4 * k + 3]) << 32));
       }
     }
   }
@@ -349,25 +461,29 @@ __device__ __forceinline__ void op_p_resid(KArgs& a, Smem& s, const Instr in, ui
   }
   const int r0 = m * PBM, rows = min(PBM, a.seq_len - r0);
   const int K = down ? a.F : a.NA;
-  PGemm g{down ? a.ACT + l * a.sACT : a.ATT + l * a.sATT, nullptr, false,
+  PGemm g{down ? a.ACTB + l * a.sACTB : a.ATTB + l * a.sATTB, nullptr, 0,
           static_cast<const uint16_t*>(down ? a.wdown : a.wo) + (size_t)l * a.H * K, nullptr, n0, a.H, K, r0, rows};
   PAcc acc;
   if (!p_gemm(a, s, g, acc, nullptr, mega, in, idx)) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
-  const float* res = down ? a.HRES + l * a.sHRES : a.X + l * a.sX;
-  float* out = down ? a.X + (l + 1) * a.sX : a.HRES + l * a.sHRES;
+  float* ct = reinterpret_cast<float*>(s.ring);          // [128][128] fp32 over the operand stages
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = p_row(wm, mi, v, lane), col = n0 + p_col(wn, ni, lane);
-        if (row < rows && col < a.H) {
-          const size_t o = (size_t)(r0 + row) * a.H + col;
-          st_cg(out + o, ld_act(res + o) + acc.c[mi][ni][v]);
-        }
-      }
+      for (int v = 0; v < 16; ++v) ct[p_row(wm, mi, v, lane) * PBN + p_col(wn, ni, lane)] = acc.c[mi][ni][v];
+  __syncthreads();
+  // O-projection: HRES_l = X_l + ATT W_o^T, plus its bf16 copy times the FFN
+  // norm gain and row sums of squares for the gate/up tiles.  Down: X_{l+1} =
+  // HRES_l + ACT W_d^T, plus the same for the next layer's QKV tiles.
+  const int nss = (a.H + PBN - 1) / PBN;
+  const bool next = !down || l + 1 < a.L;
+  PRowOut o{down ? a.X + (l + 1) * a.sX : a.HRES + l * a.sHRES, down ? a.HRES + l * a.sHRES : a.X + l * a.sX, a.H,
+            next ? (down ? a.XB + (l + 1) * a.sXB : a.HB + l * a.sXB) : nullptr,
+            next ? (down ? a.attn_norm + (size_t)(l + 1) * a.H : a.ffn_norm + (size_t)l * a.H) : nullptr,
+            next ? (down ? a.XSS + (l + 1) * a.sXSS : a.HSS + l * a.sXSS) : nullptr, nss, n0, a.H, r0, rows};
+  p_write_rows(ct, o);
   if (mega) signal_tile(a, in);
 }
 
@@ -379,26 +495,27 @@ __device__ __forceinline__ void op_p_gateup(KArgs& a, Smem& s, const Instr in, u
     return;
   }
   const int r0 = m * PBM, rows = min(PBM, a.seq_len - r0);
-  PGemm g{a.HRES + l * a.sHRES, a.ffn_norm + (size_t)l * a.H, true,
+  PGemm g{a.HB + l * a.sXB, a.HSS + l * a.sXSS, (a.H + PBN - 1) / PBN,
           static_cast<const uint16_t*>(a.wgate) + (size_t)l * a.F * a.H,
           static_cast<const uint16_t*>(a.wup) + (size_t)l * a.F * a.H, n0, a.F, a.H, r0, rows};
   PAcc acc, up;
   if (!p_gemm(a, s, g, acc, &up, mega, in, idx)) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
   const float* rs = p_row_stats(s, true) + NT;
-  float* out = a.ACT + l * a.sACT;
+  float* ct = reinterpret_cast<float*>(s.ring);          // [128][128] fp32 over the operand stages
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = p_row(wm, mi, v, lane), col = n0 + p_col(wn, ni, lane);
-        if (row < rows && col < a.F) {
-          const float gt = acc.c[mi][ni][v] * rs[row], u = up.c[mi][ni][v] * rs[row];
-          st_cg(out + (size_t)(r0 + row) * a.F + col, gt / (1.0f + expf(-gt)) * u);
-        }
+        const int row = p_row(wm, mi, v, lane);
+        const float gt = acc.c[mi][ni][v] * rs[row], u = up.c[mi][ni][v] * rs[row];
+        ct[row * PBN + p_col(wn, ni, lane)] = gt / (1.0f + expf(-gt)) * u;
       }
+  __syncthreads();
+  PRowOut o{a.ACT + l * a.sACT, nullptr, a.F, a.ACTB + l * a.sACTB, nullptr, nullptr, 0, n0, a.F, r0, rows};
+  p_write_rows(ct, o);
   if (mega) signal_tile(a, in);
 }
 
@@ -557,15 +674,19 @@ __device__ __forceinline__ void op_p_attn(KArgs& a, Smem& s, const Instr in, uin
     }
   }
   __syncthreads();
-  float* out = a.ATT + l * a.sATT;
+  // ATT_l rows of head h, and their bf16 copy for the O-projection tiles
+  float* ct = reinterpret_cast<float*>(s.ring);          // [128][128] over Q, K and V^T (done)
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = p_row(wm, mi, v, lane), dim = p_col(wn, ni, lane);
-        if (row < rows) st_cg(out + (size_t)(r0 + row) * a.NA + h * HD + dim, o.c[mi][ni][v] / lrow[row]);
+        const int row = p_row(wm, mi, v, lane);
+        ct[row * PBN + p_col(wn, ni, lane)] = o.c[mi][ni][v] / lrow[row];
       }
+  __syncthreads();
+  PRowOut po{a.ATT + l * a.sATT, nullptr, a.NA, a.ATTB + l * a.sATTB, nullptr, nullptr, 0, h * HD, a.NA, r0, rows};
+  p_write_rows(ct, po);
   if (mega) signal_tile(a, in);
 }
