@@ -168,7 +168,7 @@ struct LdsLayout { uint32_t res, x, ring, uni, bytes; };
 // 128 x 64 activation tile, three of a 256 x 64 weight tile, row statistics)
 // and an attention tile (Q, a 64-key K and V^T block, scores, probabilities).
 constexpr uint32_t kPrefillGemmBytes = 3 * 128 * 128 + 3 * 256 * 128 + (256 + 128) * 4;
-constexpr uint32_t kPrefillAttnBytes = 2 * 128 * 128 + 2 * 64 * 128 + 128 * 64 * 2 + 128 * 64 * 4 + 128 * 64 * 2 + 3 * 128 * 4;
+constexpr uint32_t kPrefillAttnBytes = 2 * 128 * 128 + 2 * (2 * 64 * 128) + 128 * 64 * 2 + 128 * 64 * 4 + 128 * 64 * 2 + 3 * 128 * 4;
 
 // Dynamic shared memory of one workgroup, in floats: header (index, norm
 // factors), GEMV results, residual rows, then one region shared by the weight

@@ -323,42 +323,51 @@ __device__ __forceinline__ void op_p_embed(KArgs& a, const Instr in, uint32_t id
   const int r0 = m * PBM, rows = max(0, min(PBM, a.seq_len - r0));
   const int c8 = a.H / 8;                                 // prefill needs the hidden size a multiple of 128
   const int nss = (a.H + PBN - 1) / PBN;
-  const int n = rows * c8;                                // a multiple of 8; groups of 16 threads stay together
-  for (int e0 = 0; e0 < n; e0 += NT) {
-    const int e = e0 + threadIdx.x;
-    const bool live = e < n;
-    const int row = live ? e / c8 : 0, c = live ? (e - row * c8) * 8 : 0;
-    float sq = 0.f;
-    if (live) {
-      const int tok = a.tokens[r0 + row];
-      v4u w = {0u, 0u, 0u, 0u};
-      if (tok < 0 || tok >= a.V) {
-        if (c == 0) record_error(a, ERR_TOKEN, idx, (uint32_t)(r0 + row), (uint32_t)tok, (uint32_t)a.V);
-      } else {
-        w = *reinterpret_cast<const v4u*>(E + (size_t)tok * a.H + c);
-      }
-      float x[8];
+  const int n = rows * c8;                                // a multiple of 16: groups of 16 threads stay together
+  constexpr int U = 4;                                    // row chunks per thread in flight at once
+  for (int e0 = 0; e0 < n; e0 += NT * U) {
+    v4u w[U];
+    int tok[U];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {                       // the bf16 bits are the high half of each float
-        x[2 * k] = __uint_as_float(w[k] << 16);
-        x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-      }
-      const size_t o = (size_t)(r0 + row) * a.H + c;
-      uint64_t* dst = reinterpret_cast<uint64_t*>(a.X + o);
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        st_cg_u64(dst + k, (uint64_t)__float_as_uint(x[2 * k]) | ((uint64_t)__float_as_uint(x[2 * k + 1]) << 32));
-#pragma unroll
-      for (int k = 0; k < 8; ++k) { sq += x[k] * x[k]; x[k] *= gain[c + k]; }
-      uint64_t* db = reinterpret_cast<uint64_t*>(a.XB + o);
-      st_cg_u64(db, (uint64_t)pack_bf16(x[0], x[1]) | ((uint64_t)pack_bf16(x[2], x[3]) << 32));
-      st_cg_u64(db + 1, (uint64_t)pack_bf16(x[4], x[5]) | ((uint64_t)pack_bf16(x[6], x[7]) << 32));
+    for (int j = 0; j < U; ++j) {
+      const int e = e0 + j * NT + threadIdx.x;
+      const int row = e < n ? e / c8 : 0, c = e < n ? (e - row * c8) * 8 : 0;
+      tok[j] = e < n ? a.tokens[r0 + row] : 0;
+      const bool ok = e < n && tok[j] >= 0 && tok[j] < a.V;
+      w[j] = ok ? *reinterpret_cast<const v4u*>(E + (size_t)tok[j] * a.H + c) : v4u{0u, 0u, 0u, 0u};
     }
-    sq += __shfl_xor(sq, 8, 16);
-    sq += __shfl_xor(sq, 4, 16);
-    sq += __shfl_xor(sq, 2, 16);
-    sq += __shfl_xor(sq, 1, 16);
-    if (live && (threadIdx.x & 15) == 0) st_cg(a.XSS + (size_t)(r0 + row) * nss + c / PBN, sq);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int e = e0 + j * NT + threadIdx.x;
+      const bool live = e < n;
+      const int row = live ? e / c8 : 0, c = live ? (e - row * c8) * 8 : 0;
+      float sq = 0.f;
+      if (live) {
+        if ((tok[j] < 0 || tok[j] >= a.V) && c == 0)
+          record_error(a, ERR_TOKEN, idx, (uint32_t)(r0 + row), (uint32_t)tok[j], (uint32_t)a.V);
+        float x[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {                     // the bf16 bits are the high half of each float
+          x[2 * k] = __uint_as_float(w[j][k] << 16);
+          x[2 * k + 1] = __uint_as_float(w[j][k] & 0xFFFF0000u);
+        }
+        const size_t o = (size_t)(r0 + row) * a.H + c;
+        uint64_t* dst = reinterpret_cast<uint64_t*>(a.X + o);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          st_cg_u64(dst + k, (uint64_t)__float_as_uint(x[2 * k]) | ((uint64_t)__float_as_uint(x[2 * k + 1]) << 32));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { sq += x[k] * x[k]; x[k] *= gain[c + k]; }
+        uint64_t* db = reinterpret_cast<uint64_t*>(a.XB + o);
+        st_cg_u64(db, (uint64_t)pack_bf16(x[0], x[1]) | ((uint64_t)pack_bf16(x[2], x[3]) << 32));
+        st_cg_u64(db + 1, (uint64_t)pack_bf16(x[4], x[5]) | ((uint64_t)pack_bf16(x[6], x[7]) << 32));
+      }
+      sq += __shfl_xor(sq, 8, 16);
+      sq += __shfl_xor(sq, 4, 16);
+      sq += __shfl_xor(sq, 2, 16);
+      sq += __shfl_xor(sq, 1, 16);
+      if (live && (threadIdx.x & 15) == 0) st_cg(a.XSS + (size_t)(r0 + row) * nss + c / PBN, sq);
+    }
   }
   if (mega) signal_tile(a, in);
 }
@@ -525,7 +534,8 @@ __device__ __forceinline__ void op_p_gateup(KArgs& a, Smem& s, const Instr in, u
 // block, read back from the KV cache (bf16) that the QKV tiles wrote.
 // Shared memory: Q [128][128] bf16 (32 KB, 2 chunk-sets of 64 dims),
 // K block [64][128] (16 KB), V^T block [128 dims][64 keys] (16 KB),
-// S [128][64] fp32 (32 KB), P [128][64] bf16 (16 KB), row statistics.
+// S [128][64] fp32 (32 KB), P [128][64] bf16 (16 KB), row statistics, and a
+// second K block (16 KB) so the next block's keys load during this one.
 __device__ __forceinline__ void op_p_attn(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
   constexpr int HD = PBN;
   const int l = in.layer, m = in.a0, h = in.a1;
@@ -547,7 +557,12 @@ __device__ __forceinline__ void op_p_attn(KArgs& a, Smem& s, const Instr in, uin
   float* mrow = reinterpret_cast<float*>(pb + PBM * PKB * 2);
   float* lrow = mrow + PBM;
   float* arow = lrow + PBM;
-  const float scale = 1.0f / sqrtf((float)HD);
+  // scores are kept in log2 units (scaled by log2(e) / sqrt(HD)), so every
+  // exponential is one v_exp_f32; only the normalised output leaves the tile
+  const float scale = 1.4426950408889634f / sqrtf((float)HD);
+  // S[row][key] sits at float4 slot (key / 4) ^ (row & 15) of its row, so the
+  // sixteen rows a wave's softmax reads at once hit distinct banks
+  auto sidx = [](int row, int key) { return row * PKB + ((((key >> 2) ^ (row & 15)) << 2) | (key & 3)); };
 
   // Q rows (fp32 post-RoPE) -> bf16, two 64-dim halves
   {
@@ -571,36 +586,49 @@ __device__ __forceinline__ void op_p_attn(KArgs& a, Smem& s, const Instr in, uin
   const uint16_t* Kc = static_cast<const uint16_t*>(a.kc) + cache_rows * HD;
   const uint16_t* Vc = static_cast<const uint16_t*>(a.vc) + cache_rows * HD;
   const int nkeys = r0 + rows;                           // causal: keys 0 .. last row
-  for (int k0 = 0; k0 < nkeys; k0 += PKB) {
-    __syncthreads();
-    // K block: 64 keys x 128 dims as two 64-dim halves (DMA, swizzled)
-    for (int d = wave; d < 2 * PKB / 8; d += NWAVE) {     // 16 DMA lines of 1 KB
+  // Key blocks are double-buffered: block b + 1's keys (DMA) and values (into
+  // registers, transposed into LDS at the top of block b + 1) load while block
+  // b runs on the matrix cores.
+  uint8_t* const kb1 = reinterpret_cast<uint8_t*>(arow + PBM);      // second K block, after the row statistics
+  constexpr int VPT = PKB * (HD / 8) / NT;               // 16-byte value loads per thread per block
+  v4u vr[VPT];
+  auto load_block = [&](int k0, uint8_t* kdst) {
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {                      // values: 8 dims of one key per load, lanes on consecutive keys
+      const int e = t + j * NT, key = e % PKB, d8 = (e / PKB) * 8;
+      vr[j] = ld_cg_v4u(Vc + (size_t)min(k0 + key, nkeys - 1) * HD + d8);
+    }
+    for (int d = wave; d < 2 * PKB / 8; d += NWAVE) {     // keys: 64 x 128 dims as two 64-dim halves, 16 DMA lines
       const int half = d / (PKB / 8), key = (d % (PKB / 8)) * 8 + lane / 8;
       const int c = (lane % 8) ^ (key & 7);
-      const int kk = min(k0 + key, nkeys - 1);
-      dma_lds16<1>(Kc + (size_t)kk * HD + half * 64 + c * 8, ks + d * 1024);
+      dma_lds16<1>(Kc + (size_t)min(k0 + key, nkeys - 1) * HD + half * 64 + c * 8, kdst + d * 1024);
     }
-    // V block transposed: thread t reads 8 dims of one key and scatters them
-    for (int e = t; e < PKB * (HD / 8); e += NT) {
-      const int key = e / (HD / 8), d8 = (e % (HD / 8)) * 8;
-      const int kk = min(k0 + key, nkeys - 1);
-      const v4u v = ld_cg_v4u(Vc + (size_t)kk * HD + d8);
-      const uint16_t* hv = reinterpret_cast<const uint16_t*>(&v);
+  };
+  load_block(0, ks);
+  for (int k0 = 0, b = 0; k0 < nkeys; k0 += PKB, ++b) {
+    __syncthreads();                                     // the previous block is done with V^T and P
+    // V block transposed: each thread scatters the 8 dims of its loaded keys
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int dim = d8 + j;
-        *reinterpret_cast<uint16_t*>(vt + dim * 128 + swz(dim, key / 8) * 16 + (key % 8) * 2) = hv[j];
+    for (int j = 0; j < VPT; ++j) {
+      const int e = t + j * NT, key = e % PKB, d8 = (e / PKB) * 8;
+      const uint16_t* hv = reinterpret_cast<const uint16_t*>(&vr[j]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int dim = d8 + q;
+        *reinterpret_cast<uint16_t*>(vt + dim * 128 + swz(dim, key / 8) * 16 + (key % 8) * 2) = hv[q];
       }
     }
-    wait_vm<0>();
+    wait_vm<0>();                                        // this block's key DMA has landed
+    if (k0 + PKB < nkeys) load_block(k0 + PKB, (b & 1) ? ks : kb1);
     __syncthreads();
+    const uint8_t* kb = (b & 1) ? kb1 : ks;
     // S = Q K^T: [128 rows][64 keys]; wave (wm, wn) computes rows wm*64.., keys wn*32..
     {
       f32x16 sc[2] = {(f32x16){}, (f32x16){}};
 #pragma unroll
       for (int kk = 0; kk < HD / 16; ++kk) {
         const int half = kk / 4, chunk = (kk % 4) * 2 + (lane >> 5);
-        const bf16x8 bfr = ld_frag(ks + half * PKB * 128, wn * 32 + (lane & 31), chunk);
+        const bf16x8 bfr = ld_frag(kb + half * PKB * 128, wn * 32 + (lane & 31), chunk);
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
           sc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -612,16 +640,22 @@ __device__ __forceinline__ void op_p_attn(KArgs& a, Smem& s, const Instr in, uin
         for (int v = 0; v < 16; ++v) {
           const int row = p_row(wm, mi, v, lane), key = wn * 32 + (lane & 31);
           const bool ok = k0 + key <= r0 + row && k0 + key < nkeys;
-          sm[row * PKB + key] = ok ? sc[mi][v] * scale : -INFINITY;
+          sm[sidx(row, key)] = ok ? sc[mi][v] * scale : -INFINITY;
         }
     }
     __syncthreads();
-    // online softmax per row: two threads per row, 32 keys each
+    // online softmax per row: two threads per row, 32 keys each (eight float4 reads)
     {
       const int row = t >> 1, half = t & 1;
+      float sv[32];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(sm + sidx(row, half * 32 + 4 * q));
+        sv[4 * q] = v.x; sv[4 * q + 1] = v.y; sv[4 * q + 2] = v.z; sv[4 * q + 3] = v.w;
+      }
       float mx = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < 32; ++k) mx = fmaxf(mx, sm[row * PKB + half * 32 + k]);
+      for (int k = 0; k < 32; ++k) mx = fmaxf(mx, sv[k]);
       mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
       const float mold = mrow[row];
       const float mnew = fmaxf(mold, mx);
@@ -629,8 +663,8 @@ __device__ __forceinline__ void op_p_attn(KArgs& a, Smem& s, const Instr in, uin
       uint32_t pk[16];
 #pragma unroll
       for (int k = 0; k < 32; k += 2) {
-        const float p0 = mnew == -INFINITY ? 0.f : expf(sm[row * PKB + half * 32 + k] - mnew);
-        const float p1 = mnew == -INFINITY ? 0.f : expf(sm[row * PKB + half * 32 + k + 1] - mnew);
+        const float p0 = mnew == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[k] - mnew);
+        const float p1 = mnew == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[k + 1] - mnew);
         sum += p0 + p1;
         pk[k / 2] = pack_bf16(p0, p1);
       }
@@ -642,7 +676,7 @@ __device__ __forceinline__ void op_p_attn(KArgs& a, Smem& s, const Instr in, uin
       }
       __syncthreads();
       if (half == 0) {
-        const float al = mold == -INFINITY ? 0.f : expf(mold - mnew);
+        const float al = mold == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mold - mnew);
         arow[row] = al;
         lrow[row] = lrow[row] * al + sum;
         mrow[row] = mnew;
