@@ -184,7 +184,10 @@ __device__ __forceinline__ bool p_gemm(KArgs& a, Smem& s, const PGemm& g, PAcc& 
   // row scales from the producers' sums of squares: two threads per row, each
   // summing half of the column tiles in order (loads issued eight at a time),
   // then first half + second half.  Done before the activation DMAs so the
-  // wait for these loads does not also wait for them.
+  // wait for these loads does not also wait for them.  Unlike the activation
+  // lines, one 128-byte line of partial sums has many producer tiles (one
+  // float each), so an L2 may hold a copy made before all of them wrote:
+  // these loads are device-coherent.
   {
     const int row = t >> 1, half = t & 1;
     float tot = 0.f;
@@ -194,7 +197,7 @@ __device__ __forceinline__ bool p_gemm(KArgs& a, Smem& s, const PGemm& g, PAcc& 
       for (int c = c0; c < c1; c += 8) {
         float v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = c + j < c1 ? ld_act(p + c + j) : 0.f;
+        for (int j = 0; j < 8; ++j) v[j] = c + j < c1 ? ld_cg(p + c + j) : 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) tot += v[j];
       }
@@ -213,12 +216,12 @@ __device__ __forceinline__ bool p_gemm(KArgs& a, Smem& s, const PGemm& g, PAcc& 
       if (acc_up) acc_up->c[mi][ni] = (f32x16){};
     }
   constexpr int NA_ = PBM / 8 / NWAVE;                   // activation DMAs per wave per step
-  // step 0's loads (and everything before them) have landed once at most step 1's are outstanding
-  if (nks > 1) {
-    if (two) wait_vm<NA_ + 2 * PBN / 8 / NWAVE>(); else wait_vm<NA_ + PBN / 8 / NWAVE>();
-  } else {
-    wait_vm<0>();
-  }
+  // Issue order so far: weights of steps 0 and 1 (before the wait), then the
+  // activations of step 0 and of step 1.  Step 0 (and step 1's weights) have
+  // landed once only step 1's activations may be outstanding; from then on each
+  // loop step issues (weights, activations) of one step and waits for the
+  // previous one.
+  if (nks > 1) wait_vm<NA_>(); else wait_vm<0>();
   __syncthreads();
   int cur = 0;                                           // stage of step ks
   for (int ks = 0; ks < nks; ++ks) {
