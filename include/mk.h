@@ -109,7 +109,10 @@ mk_status mk_queue_export(const mk_queue* q, int32_t part, void* host_dst, size_
 void mk_queue_free(mk_queue* q);
 
 /* Device workspace: per-layer intermediate tensors, split partials, barrier
- * counters, queue heads, error record.  No alignment beyond 256 bytes needed.
+ * counters, queue heads, error record; for a prefill queue also the bf16
+ * copies of the GEMM activation operands and per-row sums of squares that the
+ * producer tiles write for their consumers.  No alignment beyond 256 bytes
+ * needed.
  * mk_workspace_offset gives the byte offset of one tensor (MK_T_*) of one
  * layer inside it (layer 0..n_layers for MK_T_X; 0 for the others that are not
  * per layer). Intermediates are fp32 row-major [rows][cols]. */
@@ -173,10 +176,12 @@ mk_status mk_lm_head(const mk_queue* q, const mk_weights* w, void* d_workspace, 
  * cache row kv_row (< kv->rows), positions 0..seq_len-1.  Row blocks at or past
  * seq_len are no-ops (the queue is built once for S_max).  d_logits_last [V]
  * and d_next [1] receive the last position's logits and argmax.  The GEMM
- * tiles run on the matrix cores with bf16 operands (activations rounded to
- * bf16 on the way in) and fp32 accumulation.  Requires a bf16 model with an
- * embedding, head_dim 128 and 128 x 128 tiles (MK_ENOTSUP otherwise).  The
- * per-layer hidden rows are the workspace tensors, [S_max][...] fp32. */
+ * tiles run on the matrix cores with bf16 operands (each producer tile also
+ * writes its output rounded to bf16, times the consuming RMSNorm's gain where
+ * there is one) and fp32 accumulation.  Requires a bf16 model with an
+ * embedding, hidden size a multiple of 128, the FFN and attention widths
+ * multiples of 64, head_dim 128 and 128 x 128 tiles (MK_ENOTSUP otherwise).
+ * The per-layer hidden rows are the workspace tensors, [S_max][...] fp32. */
 mk_status mk_prefill(const mk_queue* q, const void* d_queue, const mk_weights* w,
                      const mk_kv* kv, const int32_t* d_tokens, int32_t seq_len, int32_t kv_row,
                      void* d_workspace, size_t workspace_nbytes, float* d_logits_last,
@@ -198,7 +203,10 @@ mk_status mk_device_error(const mk_queue* q, const void* d_workspace, mk_dev_err
 
 /* Tuning knobs (process-wide): */
 enum {
-  MK_OPT_WORKERS_PER_CU = 0,  /* megakernel workgroups per compute unit (default 1) */
+  MK_OPT_WORKERS_PER_CU = 0,  /* megakernel workgroups per compute unit (default 1); a
+                               * launch whose workgroups the registers or shared memory
+                               * cannot all hold at once is refused with MK_ENOTSUP
+                               * (a worker waits on tiles of others, so all must run) */
   MK_OPT_SPIN_LIMIT = 1,      /* polls before a barrier wait gives up (default 1<<22) */
   MK_OPT_NUM_CUS = 2,         /* read-only: compute units of the current device */
   /* Trace mode: a device buffer (value = its address) of at least 64 bytes per

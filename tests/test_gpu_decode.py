@@ -268,3 +268,23 @@ def test_watchdog_reports_unreachable_barrier(small):
     c.reset_kv()
     c.step(0, [128], T.MK_MEGAKERNEL)
     assert T.mk_device_error(c.q, c.ws).code == 0
+
+
+def test_workers_that_cannot_all_be_resident_are_refused(small):
+    """A persistent interpreter needs every workgroup resident at once (workers
+    wait on each other's tiles).  Eight workgroups per compute unit do not fit
+    the interpreter's shared memory: the launch is refused up front, nothing
+    runs, and the default launch works again afterwards."""
+    c = small
+    old = T.mk_get_option(T.MK_OPT_WORKERS_PER_CU)
+    T.mk_set_option(T.MK_OPT_WORKERS_PER_CU, 8)
+    try:
+        c.reset_kv()
+        with pytest.raises(T.MkError) as ei:
+            c.step(0, [128], T.MK_MEGAKERNEL)
+        assert ei.value.status == T.MK_ENOTSUP
+    finally:
+        T.mk_set_option(T.MK_OPT_WORKERS_PER_CU, old)
+    c.reset_kv()
+    c.step(0, [128], T.MK_MEGAKERNEL)
+    assert T.mk_device_error(c.q, c.ws).code == 0
