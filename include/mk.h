@@ -85,6 +85,10 @@ typedef struct mk_plan {
   int32_t mode, rows, ctx_max;
   int32_t tq, to, tf, td, kb, bm, bn;
   int32_t n_queues;
+  int32_t fuse_combine;   /* decode: 1 = no split-combine instructions; each
+                           * O-projection tile waits on the attention split
+                           * partials and merges them while staging (0 or 1;
+                           * recorded in the META word after bn) */
 } mk_plan;
 
 typedef struct mk_queue mk_queue;   /* opaque, host memory */
@@ -94,7 +98,8 @@ typedef struct mk_queue mk_queue;   /* opaque, host memory */
  * Layout of the parts (little-endian):
  *   META    u32 magic 'TMK1', version 1, mode, n_instr, n_barriers,
  *           n_wait_ranges, n_segments, n_queues, rows, ctx_max, n_splits,
- *           n_layers, tq, to, tf, td, kb, bm, bn, 0, then n_segments x
+ *           n_layers, tq, to, tf, td, kb, bm, bn, flags (bit 0: fused
+ *           split combines), then n_segments x
  *           {op, layer, first, count} (maximal runs of one op of one layer)
  *   INSTR   n_instr x 32 B {u16 op, u16 layer, u32 a0, a1, a2, wait_off,
  *           wait_cnt, signal, n_wait}

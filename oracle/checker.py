@@ -49,6 +49,7 @@ class Parsed:
     n_splits: int
     n_layers: int
     plan: Tuple[int, ...]
+    flags: int                   # bit 0: split combines fused into the O-projection
     segments: List[Tuple[int, int, int, int]]
     instr: np.ndarray            # [n, 9] int64: op, layer, a0, a1, a2, wait_off, wait_cnt, signal, n_wait
     ranges: np.ndarray           # [n_ranges, 2]
@@ -83,7 +84,7 @@ def parse(parts: Dict[str, bytes]) -> Parsed:
     targets = np.frombuffer(parts["targets"], dtype="<u4").astype(np.int64)
     if len(ranges) != n_rng or len(targets) != n_bar:
         raise ValueError("part sizes")
-    return Parsed(h[2], n_instr, n_bar, h[7], h[8], h[9], h[10], h[11], tuple(h[12:19]), segs,
+    return Parsed(h[2], n_instr, n_bar, h[7], h[8], h[9], h[10], h[11], tuple(h[12:19]), h[19], segs,
                   instr, ranges, targets)
 
 
@@ -129,7 +130,8 @@ class Space:
             b, g = a0, a1
             return (ATT, slice(b, b + 1), slice(g * r * hd, (g + 1) * r * hd)), [(OP, slice(b, b + 1), slice(g, g + 1))]
         if op == QS.OP_OPROJ:
-            return (HR, allr, slice(a0, a1)), [(ATT, allr, slice(0, nq * hd)), (X, allr, slice(a0, a1))]
+            att = (OP, allr, slice(0, nkv)) if p.flags & 1 else (ATT, allr, slice(0, nq * hd))
+            return (HR, allr, slice(a0, a1)), [att, (X, allr, slice(a0, a1))]
         if op == QS.OP_GATEUP:
             return (ACT, allr, slice(a0, a1)), [(HR, allr, slice(0, H))]
         if op == QS.OP_DOWN:
@@ -328,7 +330,20 @@ class DecodeState:
             out = N.combine_splits([(sl[:, :hd], sl[:, hd], sl[:, hd + 1]) for sl in slots])
             return put(ATT, slice(b, b + 1), slice(g * r * hd, (g + 1) * r * hd), out.reshape(1, -1))
         if op == QS.OP_OPROJ:
-            att = self.read(i, ATT, slice(0, M), slice(0, nq * hd))
+            if self.p.flags & 1:
+                # fused: merge every (row, KV head)'s split partials here
+                att = np.empty((M, nq * hd))
+                for b in range(M):
+                    for g in range(nkv):
+                        if not self.done[OPT][b, g]:
+                            self.bad_reads.append(f"instr {i} read unwritten split partials")
+                            att[b, g * r * hd:(g + 1) * r * hd] = np.nan
+                            continue
+                        slots = self.opart[l][b, g]
+                        out = N.combine_splits([(sl[:, :hd], sl[:, hd], sl[:, hd + 1]) for sl in slots])
+                        att[b, g * r * hd:(g + 1) * r * hd] = out.reshape(-1)
+            else:
+                att = self.read(i, ATT, slice(0, M), slice(0, nq * hd))
             xres = self.read(i, X, slice(0, M), slice(a0, a1))
             return put(HR, slice(0, M), slice(a0, a1), xres + att @ lw.wo[a0:a1].T)
         if op == QS.OP_GATEUP:

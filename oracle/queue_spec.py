@@ -28,11 +28,17 @@ What the pages leave open and this module fixes (the plainest reading):
   tiles.  The context length only enters through NS = ceil(ctx_max / KB)
   splits, so the queue is independent of the runtime context (and of the
   runtime prompt length in prefill, whose unused row blocks become no-ops).
+* With the plan's ``fuse_combine`` set (decode), the split combines are not
+  instructions of their own: each O-projection tile reads the split partials
+  of every (row, KV head) in place of the attention output and merges them
+  while staging its inputs; the attention-output tensor then has no tiles.
+  The META word after bn records the flag.
 
 Byte layout (little-endian), shared with the GPU library's C builder:
 
 META    u32 magic 'TMK1', version, mode, n_instr, n_barriers, n_wait_ranges, n_segments,
-        n_queues, rows, ctx_max, n_splits, n_layers, tq, to, tf, td, kb, bm, bn, 0,
+        n_queues, rows, ctx_max, n_splits, n_layers, tq, to, tf, td, kb, bm, bn, flags
+        (bit 0: split combines fused into the O-projection),
         then n_segments x {u32 op, layer, first, count} (maximal runs of one op of one layer)
 INSTR   n_instr x 32 B {u16 op, u16 layer, u32 a0, a1, a2, wait_off, wait_cnt, signal, n_wait}
         (wait_off/wait_cnt index WAITS ranges; n_wait = barriers waited on in total)
@@ -102,6 +108,7 @@ class Queue:
     n_layers: int
     plan: Tuple[int, ...]              # tq, to, tf, td, kb, bm, bn
     n_queues: int
+    flags: int = 0
     instrs: List[Instr] = field(default_factory=list)
     waits: List[Tuple[int, int]] = field(default_factory=list)      # (first, count) ranges
     targets: List[int] = field(default_factory=list)
@@ -112,7 +119,7 @@ class Queue:
     def meta_bytes(self) -> bytes:
         head = struct.pack("<20I", MAGIC, VERSION, self.mode, len(self.instrs), len(self.targets),
                            len(self.waits), len(self.segments), self.n_queues, self.rows,
-                           self.ctx_max, self.n_splits, self.n_layers, *self.plan, 0)
+                           self.ctx_max, self.n_splits, self.n_layers, *self.plan, self.flags)
         return head + b"".join(struct.pack("<4I", *s) for s in self.segments)
 
     def instr_bytes(self) -> bytes:
@@ -162,6 +169,8 @@ def _check(model, plan, mode: int, rows: int, ctx_max: int) -> None:
         raise QueueError("rows and ctx_max must be positive")
     if not 1 <= plan.n_queues <= MAX_QUEUES:
         raise QueueError("n_queues out of range")
+    if getattr(plan, "fuse_combine", 0) not in (0, 1):
+        raise QueueError("fuse_combine must be 0 or 1")
     if mode == MODE_DECODE:
         if rows > MAX_DECODE_ROWS:
             raise QueueError("decode rows above the maximum")
@@ -201,13 +210,16 @@ def _decode_instrs(model, plan, M: int, NS: int) -> List[Instr]:
                     out.append(Instr(OP_ATTN, l, b, g, s, (OP, (b, b + 1, g, g + 1)),
                                      [(QKV, (b, b + 1) + qc), (QKV, (b, b + 1) + kc),
                                       (QKV, (b, b + 1) + vc)]))
-        for g in range(nkv):
-            for b in range(M):
-                out.append(Instr(OP_COMBINE, l, b, g, 0, (ATT, (b, b + 1, g * r * hd, (g + 1) * r * hd)),
-                                 [(OP, (b, b + 1, g, g + 1))]))
+        fused = getattr(plan, "fuse_combine", 0)
+        if not fused:
+            for g in range(nkv):
+                for b in range(M):
+                    out.append(Instr(OP_COMBINE, l, b, g, 0, (ATT, (b, b + 1, g * r * hd, (g + 1) * r * hd)),
+                                     [(OP, (b, b + 1, g, g + 1))]))
+        att_read = (OP, (0, M, 0, nkv)) if fused else (ATT, (0, M, 0, NA))
         for n0, n1 in _tiles(H, plan.to):
             out.append(Instr(OP_OPROJ, l, n0, n1, 0, (HR, (0, M, n0, n1)),
-                             [(ATT, (0, M, 0, NA)), (X, (0, M, n0, n1))]))
+                             [att_read, (X, (0, M, n0, n1))]))
         for n0, n1 in _tiles(F, plan.tf):
             out.append(Instr(OP_GATEUP, l, n0, n1, 0, (ACT, (0, M, n0, n1)), [(HR, (0, M, 0, H))]))
         for n0, n1 in _tiles(H, plan.td):
@@ -258,8 +270,9 @@ def build(model, plan, mode: int, rows: int, ctx_max: int) -> Queue:
     NS = math.ceil(ctx_max / plan.kb) if mode == MODE_DECODE else 0
     instrs = (_decode_instrs(model, plan, rows, NS) if mode == MODE_DECODE
               else _prefill_instrs(model, plan, rows))
+    flags = 1 if mode == MODE_DECODE and getattr(plan, "fuse_combine", 0) else 0
     q = Queue(mode, rows, ctx_max, NS, model.n_layers,
-              (plan.tq, plan.to, plan.tf, plan.td, plan.kb, plan.bm, plan.bn), plan.n_queues)
+              (plan.tq, plan.to, plan.tf, plan.td, plan.kb, plan.bm, plan.bn), plan.n_queues, flags)
 
     # barriers: one per distinct written tile, numbered by first write
     tile_id: Dict[Tuple[int, Box], int] = {}

@@ -108,3 +108,32 @@ def test_workspace_layout_is_consistent():
     assert q.workspace_offset(T.MK_T_ERROR) < total
     with pytest.raises(L.MkError):
         q.workspace_offset(T.MK_T_QKV, 16)
+
+
+@pytest.mark.parametrize("rows,ctx,plan", [
+    (1, 129, W.Plan(tq=16, to=16, tf=32, td=16, kb=32, fuse_combine=1)),
+    (3, 129, W.Plan(tq=24, to=40, tf=50, td=7, kb=64, n_queues=8, fuse_combine=1)),
+    (32, 33, W.Plan(tq=1, to=3, tf=5, td=9, kb=1, fuse_combine=1)),
+])
+def test_builder_bytes_fused_combine(rows, ctx, plan):
+    """Queues whose split combines are fused into the O-projection: byte-identical."""
+    got, ref = _both(W.LLAMA_LAYER_F32, plan, QS.MODE_DECODE, rows, ctx)
+    assert got == ref
+
+
+def test_builder_bytes_fused_combine_llama1b():
+    wl = W.WORKLOADS["llama1b_b1"]
+    import dataclasses
+    plan = dataclasses.replace(wl.plan, fuse_combine=1)
+    got, ref = _both(wl.model, plan, QS.MODE_DECODE, wl.run.batch, wl.run.ctx_max)
+    assert got == ref
+
+
+def test_builder_rejects_bad_fuse_flag():
+    wl = W.WORKLOADS["layer256_f32"]
+    import dataclasses
+    plan = dataclasses.replace(wl.plan, fuse_combine=2)
+    with pytest.raises(T.MkError):
+        T.mk_build_queue(T.make_config(wl.model), T.make_plan(plan, QS.MODE_DECODE, 1, 129))
+    with pytest.raises(QS.QueueError):
+        QS.build(wl.model, plan, QS.MODE_DECODE, 1, 129)

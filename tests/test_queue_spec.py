@@ -241,3 +241,62 @@ def test_simulation_detects_deadlock():
     mutant = dict(parts, instr=b"".join([recs[-1]] + recs[:-1]))
     res = CK.simulate(model, mutant, K.copy(), V.copy(), [128], 1, seed=0, x0=x0)
     assert res.deadlock
+
+
+# ----------------------------------------------------------------------------- fused split combines
+
+def _fused(plan):
+    import dataclasses
+    return dataclasses.replace(plan, fuse_combine=1)
+
+
+def test_fused_combine_queue_shape():
+    """Fused: no COMBINE instructions, one barrier fewer per (layer, row, KV head),
+    the O-projection waits on every split-partial tile, the META flag is set."""
+    wl = W.WORKLOADS["layer256_f32"]
+    m, M = wl.model, 3
+    q0 = QS.build(m, wl.plan, QS.MODE_DECODE, M, 129)
+    q1 = QS.build(m, _fused(wl.plan), QS.MODE_DECODE, M, 129)
+    assert not any(i.op == QS.OP_COMBINE for i in q1.instrs)
+    assert len(q1.instrs) == len(q0.instrs) - m.n_layers * M * m.n_kv_heads
+    assert len(q1.targets) == len(q0.targets) - m.n_layers * M * m.n_kv_heads
+    assert sum(q1.targets) == len(q1.instrs)
+    assert struct.unpack_from("<20I", q1.meta_bytes())[19] == 1
+    assert struct.unpack_from("<20I", q0.meta_bytes())[19] == 0
+    oproj = next(i for i in q1.instrs if i.op == QS.OP_OPROJ)
+    opart = {k for k, (t, _) in enumerate(q1.tiles) if t == QS.tensor_order(0, QS.T_OPART)}
+    assert opart <= set(q1.wait_list(q1.instrs.index(oproj)))
+    assert CK.static_check(m, q1.parts()) == []
+
+
+@pytest.mark.parametrize("workers", [1, 7, 256])
+def test_fused_combine_simulation_matches_forward(workers):
+    model, K, V, x0 = _small_inputs(gain=0.1)
+    wl = W.WORKLOADS["layer256_f32"]
+    q = QS.build(wl.model, _fused(wl.plan), QS.MODE_DECODE, 1, 129)
+    ref = N.decode_step(model, K.copy(), V.copy(), [128], x0=x0)
+    base = CK.simulate(model, q.parts(), K.copy(), V.copy(), [128], 1, seed=0, x0=x0)
+    assert N.max_rel_err(base.x_out, ref.x_out) < 1e-12
+    for seed in range(30 if workers > 1 else 1):
+        res = CK.simulate(model, q.parts(), K.copy(), V.copy(), [128], workers, seed=seed, x0=x0,
+                          reverse_ties=bool(seed & 1))
+        assert not res.deadlock and res.bad_reads == []
+        assert np.array_equal(res.x_out, base.x_out)
+        assert np.array_equal(res.counters, np.array(q.targets))
+
+
+def test_fused_combine_simulation_detects_missing_split_wait():
+    """Drop the O-projection's waits on the split partials (keep its residual
+    wait): some schedule must read a split partial before it is written."""
+    model, K, V, x0 = _small_inputs()
+    wl = W.WORKLOADS["layer256_f32"]
+    q = QS.build(wl.model, _fused(wl.plan), QS.MODE_DECODE, 1, 129)
+    i = next(k for k, ins in enumerate(q.instrs) if ins.op == QS.OP_OPROJ)
+    opart = {k for k, (t, _) in enumerate(q.tiles) if t == QS.tensor_order(0, QS.T_OPART)}
+    mutant = _with_waits(q, i, [b for b in q.wait_list(i) if b not in opart])
+    seen = False
+    for seed in range(20):
+        res = CK.simulate(model, mutant, K.copy(), V.copy(), [128], 64, seed=seed, x0=x0)
+        seen |= bool(res.bad_reads) or bool(np.any(np.isnan(res.x_out)))
+    assert seen
+    assert CK.static_check(wl.model, mutant) != []

@@ -194,12 +194,22 @@ LdsLayout lds_layout(const mk_config& c, const mk_plan& p) {
   o.ring = NWAVE * ring_lines_for(nb) * 1024;
   const uint32_t fixed = 4 * (16 + 32 + NWAVE * 32 + 2 * o.res) + o.ring;
   const uint32_t room = fixed < kMaxLds ? (kMaxLds - fixed) / 4 : 0;
+  // fused split combines: the O-projection stages all of its input rows at once
+  // (whole 512-column iterations) followed by every split partial of the rows
+  uint32_t fused_need = 0;
+  if (p.fuse_combine) {
+    const uint32_t r = c.n_q_heads / c.n_kv_heads, NA = c.n_q_heads * c.head_dim;
+    const uint32_t NS = (p.ctx_max + p.kb - 1) / p.kb;
+    fused_need = nb * ((NA + 511) / 512 * 512) + p.rows * c.n_kv_heads * NS * (r * c.head_dim + 2 * r);
+    o.x = std::max(o.x, fused_need);
+  }
   if (o.x > room) o.x = std::max<uint32_t>(room / (nb * 512) * (nb * 512), nb * 512);
   o.x = r4(o.x);
   const uint32_t r = c.n_q_heads / c.n_kv_heads, hd = c.head_dim;
   const uint32_t att = r4(r * hd) + 2 * r4(hd) + 2 * r4(hd / 2) + 2 * r4(NWAVE * ATT_MAX_R) + r4(NWAVE * r * hd);
   o.uni = std::max(o.ring / 4 + o.x, att);
   o.bytes = 4 * (16 + 32 + NWAVE * 32 + 2 * o.res + o.uni);
+  if (o.x < fused_need) o.bytes = kMaxLds + 1;            // does not fit: refused by the callers
   return o;
 }
 LdsLayout lds_layout(const mk_queue* q) { return lds_layout(q->cfg, q->plan); }
@@ -240,6 +250,7 @@ void fill_args(const mk_queue* q, const void* d_queue, const mk_weights* w, cons
   a.targets = reinterpret_cast<const uint32_t*>(qd + q->dev_targets_off);
   a.n_instr = (uint32_t)q->instr.size(); a.n_barriers = (uint32_t)q->targets.size();
   a.n_queues = (uint32_t)q->plan.n_queues;
+  a.fuse_combine = q->plan.mode == MK_DECODE && q->plan.fuse_combine;
   const LdsLayout ll = lds_layout(q);
   a.lds_res = ll.res; a.lds_x = ll.x; a.lds_union = ll.uni; a.lds_bytes = ll.bytes; a.lds_ring = ll.ring;
   a.M_cache = kv && kv->rows > 0 ? kv->rows : q->plan.rows;

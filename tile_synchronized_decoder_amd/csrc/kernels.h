@@ -91,6 +91,7 @@ struct Args {
   uint32_t lds_ring;             // bytes of the ring / prefill tile region
   const float* lm_x;             // LM head input rows
   int gemv_pipe;                 // decode GEMV weight issue: 0 by shape, 1 pipelined, 2 compiler-ordered
+  int fuse_combine;              // decode queue without split combines: O-projection merges the partials
   // prefill: bf16 GEMM operands (X and HRES with the consumer's RMSNorm gain
   // applied), per-row sums of squares of X / HRES per 128-column tile
   uint16_t* XB; uint16_t* HB; uint16_t* ATTB; uint16_t* ACTB;
@@ -475,6 +476,61 @@ __device__ __forceinline__ void stage_x(Smem& s, const float* x, int ldx, int nb
   }
 }
 
+// O-projection input rows of a queue whose split combines are fused into the
+// O-projection: ATT[b][col] for all nb rows and the K = nq * hd columns, merged
+// from the attention splits' partials (o | m | l per split, as COMBINE does)
+// instead of read from ATT.  Every partial of the layer's nb rows is first
+// copied into shared memory after the staged rows (one block of coherent
+// 16-byte loads), then each thread merges its columns.  The residual values
+// are staged as stage_x does.  The host sizes the staging area for this.
+template <int NB>
+__device__ __forceinline__ void stage_att_fused(KArgs& a, Smem& s, int l, int nb, int K, const float* resid,
+                                                int resid_ld, int resid_rows) {
+  const int r = a.r, hd = a.hd, NS = a.NS, rhd = r * hd;
+  const int slot_sz = rhd + 2 * r;
+  float* P = s.x + NB * K;                                   // staged partials [nb][nkv][NS][slot]
+  const float* src = a.OPART + l * a.sOP;
+  const int total = nb * a.nkv * NS * slot_sz;
+  const int t = threadIdx.x;
+  const bool has_r = resid && t < resid_rows * nb;
+  const int rrow = has_r ? t / nb : 0, rb = has_r ? t - rrow * nb : 0;
+  const float rv = has_r ? ld_cg(resid + (size_t)rb * resid_ld + rrow) : 0.f;
+  constexpr int U = 8;
+  const int q4 = total >> 2;
+  for (int u0 = t; u0 < q4; u0 += NT * U) {
+    float4 v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) if (u0 + j * NT < q4) v[j] = ld_cg4(src + 4 * (u0 + j * NT));
+#pragma unroll
+    for (int j = 0; j < U; ++j) if (u0 + j * NT < q4) *reinterpret_cast<float4*>(P + 4 * (u0 + j * NT)) = v[j];
+  }
+  for (int e = 4 * q4 + t; e < total; e += NT) P[e] = ld_cg(src + e);
+  if (has_r) s.resid[rrow * NB + rb] = rv;
+  if (resid) {
+    for (int e = t + NT; e < resid_rows * nb; e += NT) {
+      const int row = e / nb, b = e - row * nb;
+      s.resid[row * NB + b] = ld_cg(resid + (size_t)b * resid_ld + row);
+    }
+  }
+  __syncthreads();
+  for (int e = t; e < nb * K; e += NT) {
+    const int b = e / K, col = e - b * K;
+    const int g = col / rhd, o = col - g * rhd, h = o / hd;
+    const float* pb = P + (size_t)(b * a.nkv + g) * NS * slot_sz;
+    float m = -INFINITY;
+    for (int sp = 0; sp < NS; ++sp) m = fmaxf(m, pb[sp * slot_sz + rhd + h]);
+    float num = 0.f, den = 0.f;
+    for (int sp = 0; sp < NS; ++sp) {
+      const float ms = pb[sp * slot_sz + rhd + h];
+      if (ms == -INFINITY) continue;
+      const float w = expf(ms - m);
+      num = fmaf(w, pb[sp * slot_sz + o], num);
+      den = fmaf(w, pb[sp * slot_sz + rhd + r + h], den);
+    }
+    s.x[b * K + col] = num / den;
+  }
+}
+
 // Full GEMV of `nrows` rows against `nb` input rows of length K, results in
 // s.res[row * NB + b] (already scaled by the row's RMSNorm factor when `norm`).
 // The inputs are staged in column chunks as large as the shared memory allows;
@@ -529,7 +585,8 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, 
     const int kc0 = ci * kc_max;
     const int kcn = min(kc_max, K - kc0);
     if (ci > 0) __syncthreads();                         // every wave is done with the previous chunk
-    stage_x<NB>(s, x, K, nb, kc0, kcn, gain, norm, ssl, ci == 0 ? resid : nullptr, resid_ld, g.nrows);
+    if (x) stage_x<NB>(s, x, K, nb, kc0, kcn, gain, norm, ssl, ci == 0 ? resid : nullptr, resid_ld, g.nrows);
+    else stage_att_fused<NB>(a, s, in.layer, nb, K, resid, resid_ld, g.nrows);   // one chunk (host-sized)
     __syncthreads();
     if (mega && ci == 0) trace_mark(a, idx, 3);
     const int it_begin = kc0 / 512, it_end = (kc0 + kcn + 511) / 512;
@@ -675,7 +732,7 @@ __device__ __forceinline__ void op_gemv_rpw(KArgs& a, Smem& s, const Instr in, u
   if (op == mk::OP_QKV) {
     x = a.X + l * a.sX; gain = a.attn_norm + (size_t)l * a.H;
   } else if (op == mk::OP_OPROJ) {
-    x = a.ATT + l * a.sATT; resid = a.X + l * a.sX + n0; ld = a.H;
+    x = a.fuse_combine ? nullptr : a.ATT + l * a.sATT; resid = a.X + l * a.sX + n0; ld = a.H;
   } else if (op == mk::OP_GATEUP) {
     x = a.HRES + l * a.sHRES; gain = a.ffn_norm + (size_t)l * a.H;
   } else {

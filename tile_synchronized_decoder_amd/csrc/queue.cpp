@@ -76,11 +76,15 @@ struct Builder {
     q->n_splits = NS;
     const uint32_t nX = cdiv(H, p.td), nQ = cdiv(NQKV, p.tq), nO = cdiv(H, p.to), nF = cdiv(F, p.tf);
     const uint32_t L0 = c.has_embed ? nX : 0;
-    const uint32_t per_layer = nQ + 2 * M * nkv + nO + nF + nX;
+    // fused: the split combines are dropped and each O-projection tile waits on
+    // the split partials itself (no attention-output tiles)
+    const bool fused = p.fuse_combine != 0;
+    const uint32_t natt = fused ? 0 : M * nkv;
+    const uint32_t per_layer = nQ + M * nkv + natt + nO + nF + nX;
     auto qkv_id = [&](uint32_t l, uint32_t n) { return L0 + l * per_layer + n; };
     auto op_id = [&](uint32_t l, uint32_t b, uint32_t g) { return qkv_id(l, nQ) + b * nkv + g; };
     auto att_id = [&](uint32_t l, uint32_t g, uint32_t b) { return qkv_id(l, nQ) + M * nkv + g * M + b; };
-    auto hres_id = [&](uint32_t l, uint32_t n) { return qkv_id(l, nQ) + 2 * M * nkv + n; };
+    auto hres_id = [&](uint32_t l, uint32_t n) { return qkv_id(l, nQ) + M * nkv + natt + n; };
     auto act_id = [&](uint32_t l, uint32_t n) { return hres_id(l, nO) + n; };
     auto xn_id = [&](uint32_t l, uint32_t n) { return act_id(l, nF) + n; };
     auto x_exists = [&](uint32_t l) { return l > 0 || c.has_embed; };
@@ -116,14 +120,21 @@ struct Builder {
           for (uint32_t s = 0; s < NS; ++s) emit(OP_ATTN, l, b, g, s, op_id(l, b, g), w);
           q->targets[op_id(l, b, g)] = NS;
         }
-      for (uint32_t g = 0; g < nkv; ++g)
-        for (uint32_t b = 0; b < M; ++b)
-          emit(OP_COMBINE, l, b, g, 0, att_id(l, g, b), {{op_id(l, b, g), 1}});
+      if (!fused)
+        for (uint32_t g = 0; g < nkv; ++g)
+          for (uint32_t b = 0; b < M; ++b)
+            emit(OP_COMBINE, l, b, g, 0, att_id(l, g, b), {{op_id(l, b, g), 1}});
       for (uint32_t n = 0; n < nO; ++n) {
         uint32_t n0 = n * p.to, n1 = std::min((n + 1) * p.to, H);
         std::vector<std::pair<uint32_t, uint32_t>> w;
         if (x_exists(l)) w.push_back({x_id(l, n0 / p.td), (n1 - 1) / p.td - n0 / p.td + 1});
-        w.push_back({att_id(l, 0, 0), nkv * M});
+        if (fused) {
+          // split-partial tiles in (KV head, row) order, as the reads sort
+          for (uint32_t g = 0; g < nkv; ++g)
+            for (uint32_t b = 0; b < M; ++b) w.push_back({op_id(l, b, g), 1});
+        } else {
+          w.push_back({att_id(l, 0, 0), nkv * M});
+        }
         emit(OP_OPROJ, l, n0, n1, 0, hres_id(l, n), w);
       }
       for (uint32_t n = 0; n < nF; ++n)
@@ -214,6 +225,7 @@ const char* validate(const mk_config& c, const mk_plan& p) {
   if (c.n_layers > 65535) return "too many layers";
   if (p.rows <= 0 || p.ctx_max <= 0) return "rows and ctx_max must be positive";
   if (p.n_queues < 1 || p.n_queues > kMaxQueues) return "n_queues out of range";
+  if (p.fuse_combine != 0 && p.fuse_combine != 1) return "fuse_combine must be 0 or 1";
   if (p.mode == MK_DECODE) {
     if (p.rows > kMaxDecodeRows) return "decode rows above the maximum";
     if (std::min({p.tq, p.to, p.tf, p.td, p.kb}) <= 0) return "tile sizes must be positive";
@@ -294,7 +306,8 @@ mk_status mk_queue_export(const mk_queue* q, int32_t part, void* host_dst, size_
                         (uint32_t)q->segments.size(), (uint32_t)p.n_queues, (uint32_t)p.rows,
                         (uint32_t)p.ctx_max, q->n_splits, (uint32_t)q->cfg.n_layers,
                         (uint32_t)p.tq, (uint32_t)p.to, (uint32_t)p.tf, (uint32_t)p.td,
-                        (uint32_t)p.kb, (uint32_t)p.bm, (uint32_t)p.bn, 0};
+                        (uint32_t)p.kb, (uint32_t)p.bm, (uint32_t)p.bn,
+                        (p.mode == MK_DECODE && p.fuse_combine) ? 1u : 0u};
       std::memcpy(d, h, sizeof(h));
       if (!q->segments.empty()) std::memcpy(d + 80, q->segments.data(), 16 * q->segments.size());
       break;

@@ -61,6 +61,9 @@ class Plan:
     down GEMVs.  kb: keys per attention split.  bm/bn: prefill GEMM tile.
     n_queues: number of sub-queues the workers pop from (instruction i belongs to
     sub-queue i mod n_queues).
+    fuse_combine: decode only; 1 drops the split-combine instructions: each
+    O-projection tile waits on the attention splits' partials and merges them
+    itself while staging its inputs (one barrier hand-off fewer per layer).
     """
     tq: int = 16
     to: int = 16
@@ -70,6 +73,7 @@ class Plan:
     bm: int = 128
     bn: int = 128
     n_queues: int = 1
+    fuse_combine: int = 0
 
 
 @dataclass(frozen=True)
