@@ -33,11 +33,15 @@ def rel_rows(got, ref):
 
 
 def check_step(c, tr, tol, layers=None):
-    """Compare workspace intermediates of one step with an oracle trace."""
+    """Compare workspace intermediates of one step with an oracle trace.  A
+    queue with fused split combines writes no attention-output tensor (the
+    O-projection merges the partials itself); its error shows in HRES."""
     m = c.m
     errs = {}
+    fused = getattr(c.wl.plan, "fuse_combine", 0)
     for l in (layers if layers is not None else range(m.n_layers)):
-        errs[f"att{l}"] = rel_rows(c.tensor(T.MK_T_ATT, l, m.attn_cols), tr.attn[l])
+        if not fused:
+            errs[f"att{l}"] = rel_rows(c.tensor(T.MK_T_ATT, l, m.attn_cols), tr.attn[l])
         errs[f"h{l}"] = rel_rows(c.tensor(T.MK_T_HRES, l, m.hidden), tr.h[l])
         errs[f"act{l}"] = rel_rows(c.tensor(T.MK_T_ACT, l, m.ffn), tr.act[l])
         hres = c.tensor(T.MK_T_HRES, l, m.hidden)
@@ -288,3 +292,66 @@ def test_workers_that_cannot_all_be_resident_are_refused(small):
     c.reset_kv()
     c.step(0, [128], T.MK_MEGAKERNEL)
     assert T.mk_device_error(c.q, c.ws).code == 0
+
+
+# ----------------------------------------------------------------------------- fused split combines
+
+def _fused(wl, **kw):
+    return dataclasses.replace(wl, plan=dataclasses.replace(wl.plan, fuse_combine=1, **kw))
+
+
+@pytest.mark.parametrize("ctx", [0, 31, 128])
+def test_fused_combine_fp32_layer_both_modes(ctx):
+    """Split combines fused into the O-projection: oracle parity on the fp32
+    layer (5 splits, empty ones at short contexts), megakernel and per-op bit
+    for bit, counters equal to targets."""
+    from _gpucase import make_case
+    c = make_case(_fused(W.WORKLOADS["layer256_f32"]), gain_jitter=0.1)
+    outs = []
+    for mode in (T.MK_MEGAKERNEL, T.MK_KERNEL_PER_OP):
+        c.reset_kv()
+        c.ws.zero_()
+        c.step(0, [ctx], mode)
+        tr = N.decode_step(c.oracle_model(), c.K0.copy(), c.V0.copy(), [ctx], x0=c.x0[0])
+        check_step(c, tr, TOL_F32)
+        outs.append((c.tensor(T.MK_T_HRES, 0, 256), c.tensor(T.MK_T_X, 1, 256)))
+        if mode == T.MK_MEGAKERNEL:
+            tg = np.frombuffer(c.q.export(T.MK_PART_TARGETS), dtype=np.uint32)
+            assert np.array_equal(c.counters(), tg)
+            assert T.mk_device_error(c.q, c.ws).code == 0
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("ctx0", [(1024,), (100,)])
+def test_fused_combine_bf16_multistep(ctx0):
+    """The 1B shape at batch 1 (five 256-key splits, all but one empty at
+    context 100): three steps against the oracle, megakernel = per-op."""
+    from _gpucase import make_case, log
+    wl = _fused(_shrunk_1b(batch=1, ctx0=ctx0))
+    c = make_case(wl)
+    model = c.oracle_model()
+    K, V = c.K0.copy(), c.V0.copy()
+    for t in range(wl.run.steps):
+        ctx = [p + t for p in ctx0]
+        tr = N.decode_step(model, K, V, ctx, tokens=c.tokens[t])
+        c.step(t, ctx, T.MK_MEGAKERNEL)
+        log(f"  fused step {t}")
+        check_step(c, tr, TOL_BF16)
+        mega = (c.logits.cpu().numpy().copy(), c.tensor(T.MK_T_X, wl.model.n_layers, 2048))
+        c.step(t, ctx, T.MK_KERNEL_PER_OP)
+        assert np.array_equal(c.logits.cpu().numpy(), mega[0])
+        assert np.array_equal(c.tensor(T.MK_T_X, wl.model.n_layers, 2048), mega[1])
+
+
+def test_fused_combine_refused_when_partials_do_not_fit():
+    """Many splits (8-key splits of an 8448-position cache): the O-projection
+    cannot stage every partial in shared memory, so the step is refused before
+    anything runs."""
+    from _gpucase import make_case
+    wl = _fused(W.WORKLOADS["layer256_f32"], kb=8)
+    wl = dataclasses.replace(wl, run=dataclasses.replace(wl.run, ctx_max=8448))
+    c = make_case(wl)
+    with pytest.raises(T.MkError) as ei:
+        c.step(0, [128], T.MK_MEGAKERNEL)
+    assert ei.value.status == T.MK_ENOTSUP

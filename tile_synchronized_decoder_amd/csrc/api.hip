@@ -200,7 +200,8 @@ LdsLayout lds_layout(const mk_config& c, const mk_plan& p) {
   if (p.fuse_combine) {
     const uint32_t r = c.n_q_heads / c.n_kv_heads, NA = c.n_q_heads * c.head_dim;
     const uint32_t NS = (p.ctx_max + p.kb - 1) / p.kb;
-    fused_need = nb * ((NA + 511) / 512 * 512) + p.rows * c.n_kv_heads * NS * (r * c.head_dim + 2 * r);
+    fused_need = nb * ((NA + 511) / 512 * 512) + p.rows * c.n_kv_heads * NS * (r * c.head_dim + 2 * r) +
+                 p.rows * c.n_kv_heads * r * NS;           // rows, partials, merge weights
     o.x = std::max(o.x, fused_need);
   }
   if (o.x > room) o.x = std::max<uint32_t>(room / (nb * 512) * (nb * 512), nb * 512);

@@ -481,8 +481,10 @@ __device__ __forceinline__ void stage_x(Smem& s, const float* x, int ldx, int nb
 // from the attention splits' partials (o | m | l per split, as COMBINE does)
 // instead of read from ATT.  Every partial of the layer's nb rows is first
 // copied into shared memory after the staged rows (one block of coherent
-// 16-byte loads), then each thread merges its columns.  The residual values
-// are staged as stage_x does.  The host sizes the staging area for this.
+// 16-byte loads); the merge weights of each (row, KV head, query head) are
+// computed once, then each column is one weighted sum over the splits.  The
+// residual values are staged as stage_x does.  The host sizes the staging
+// area for this.
 template <int NB>
 __device__ __forceinline__ void stage_att_fused(KArgs& a, Smem& s, int l, int nb, int K, const float* resid,
                                                 int resid_ld, int resid_rows) {
@@ -495,7 +497,7 @@ __device__ __forceinline__ void stage_att_fused(KArgs& a, Smem& s, int l, int nb
   const bool has_r = resid && t < resid_rows * nb;
   const int rrow = has_r ? t / nb : 0, rb = has_r ? t - rrow * nb : 0;
   const float rv = has_r ? ld_cg(resid + (size_t)rb * resid_ld + rrow) : 0.f;
-  constexpr int U = 8;
+  constexpr int U = 16;
   const int q4 = total >> 2;
   for (int u0 = t; u0 < q4; u0 += NT * U) {
     float4 v[U];
@@ -513,21 +515,33 @@ __device__ __forceinline__ void stage_att_fused(KArgs& a, Smem& s, int l, int nb
     }
   }
   __syncthreads();
+  // per (row, KV head, query head): split weights e^(m_s - m) / sum_s e^(m_s - m) l_s
+  // (0 for empty splits), once, into shared memory after the partials
+  float* W = P + total;                                      // [nb][nkv][r][NS]
+  for (int e = t; e < nb * a.nkv * r; e += NT) {
+    const int bg = e / r, h = e - bg * r;
+    const float* pb = P + (size_t)bg * NS * slot_sz;
+    float m = -INFINITY;
+    for (int sp = 0; sp < NS; ++sp) m = fmaxf(m, pb[sp * slot_sz + rhd + h]);
+    float den = 0.f;
+    for (int sp = 0; sp < NS; ++sp) {
+      const float ms = pb[sp * slot_sz + rhd + h];
+      const float w = ms == -INFINITY ? 0.f : expf(ms - m);
+      W[(size_t)e * NS + sp] = w;
+      den = fmaf(w, pb[sp * slot_sz + rhd + r + h], den);
+    }
+    const float inv = 1.0f / den;
+    for (int sp = 0; sp < NS; ++sp) W[(size_t)e * NS + sp] *= inv;
+  }
+  __syncthreads();
   for (int e = t; e < nb * K; e += NT) {
     const int b = e / K, col = e - b * K;
     const int g = col / rhd, o = col - g * rhd, h = o / hd;
-    const float* pb = P + (size_t)(b * a.nkv + g) * NS * slot_sz;
-    float m = -INFINITY;
-    for (int sp = 0; sp < NS; ++sp) m = fmaxf(m, pb[sp * slot_sz + rhd + h]);
-    float num = 0.f, den = 0.f;
-    for (int sp = 0; sp < NS; ++sp) {
-      const float ms = pb[sp * slot_sz + rhd + h];
-      if (ms == -INFINITY) continue;
-      const float w = expf(ms - m);
-      num = fmaf(w, pb[sp * slot_sz + o], num);
-      den = fmaf(w, pb[sp * slot_sz + rhd + r + h], den);
-    }
-    s.x[b * K + col] = num / den;
+    const float* pb = P + (size_t)(b * a.nkv + g) * NS * slot_sz + o;
+    const float* w = W + ((size_t)(b * a.nkv + g) * r + h) * NS;
+    float acc = 0.f;
+    for (int sp = 0; sp < NS; ++sp) acc = fmaf(w[sp], pb[sp * slot_sz], acc);
+    s.x[b * K + col] = acc;
   }
 }
 
