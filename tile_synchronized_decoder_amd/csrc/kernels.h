@@ -484,9 +484,11 @@ __device__ __forceinline__ void stage_x(Smem& s, const float* x, int ldx, int nb
 // 16-byte loads); the merge weights of each (row, KV head, query head) are
 // computed once, then each column is one weighted sum over the splits.  The
 // residual values are staged as stage_x does.  The host sizes the staging
-// area for this.
+// area for this.  Kept out of line: it is inlined into no GEMV body, so the
+// unfused path's code stays as it was (the interpreter's size matters for the
+// instruction cache).
 template <int NB>
-__device__ __forceinline__ void stage_att_fused(KArgs& a, Smem& s, int l, int nb, int K, const float* resid,
+__device__ __attribute__((noinline)) void stage_att_fused(KArgs& a, Smem& s, int l, int nb, int K, const float* resid,
                                                 int resid_ld, int resid_rows) {
   const int r = a.r, hd = a.hd, NS = a.NS, rhd = r * hd;
   const int slot_sz = rhd + 2 * r;
