@@ -560,7 +560,7 @@ __device__ __attribute__((noinline)) void stage_att_fused(KArgs& a, Smem& s, int
 // Returns false when the wait gave up.
 template <typename WT, int NB, int RPW, bool PIPE>
 __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, PIPE>& g, const float* x, int nb,
-                     const float* gain, bool norm, bool mega, const Instr in, uint32_t idx,
+                     const float* gain, bool norm, bool mega, bool fused, const Instr in, uint32_t idx,
                      const float* resid, int resid_ld) {
   using G = Gemv<WT, NB, RPW, PIPE>;
   using E = Elem<WT>;
@@ -601,7 +601,7 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, 
     const int kc0 = ci * kc_max;
     const int kcn = min(kc_max, K - kc0);
     if (ci > 0) __syncthreads();                         // every wave is done with the previous chunk
-    if (x) stage_x<NB>(s, x, K, nb, kc0, kcn, gain, norm, ssl, ci == 0 ? resid : nullptr, resid_ld, g.nrows);
+    if (!fused) stage_x<NB>(s, x, K, nb, kc0, kcn, gain, norm, ssl, ci == 0 ? resid : nullptr, resid_ld, g.nrows);
     else stage_att_fused<NB>(a, s, in.layer, nb, K, resid, resid_ld, g.nrows);   // one chunk (host-sized)
     __syncthreads();
     if (mega && ci == 0) trace_mark(a, idx, 3);
@@ -735,7 +735,7 @@ __device__ __forceinline__ bool gemv_of(KArgs& a, const Instr in, Gemv<WT, NB, R
 // (silu(RMSNorm(H) Wg^T) * (RMSNorm(H) Wu^T)) and DOWN (HRES_l + ACT_l Wd^T),
 // each over output columns [a0, a1).
 template <typename WT, int NB, int RPW, bool PIPE>
-__device__ __forceinline__ void op_gemv_rpw(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
+__device__ __forceinline__ void op_gemv_rpw(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega, bool fused) {
   using G = Gemv<WT, NB, RPW, PIPE>;
   const int l = in.layer, n0 = in.a0, n = in.a1 - in.a0;
   G g{};
@@ -748,13 +748,13 @@ __device__ __forceinline__ void op_gemv_rpw(KArgs& a, Smem& s, const Instr in, u
   if (op == mk::OP_QKV) {
     x = a.X + l * a.sX; gain = a.attn_norm + (size_t)l * a.H;
   } else if (op == mk::OP_OPROJ) {
-    x = a.fuse_combine ? nullptr : a.ATT + l * a.sATT; resid = a.X + l * a.sX + n0; ld = a.H;
+    x = fused ? nullptr : a.ATT + l * a.sATT; resid = a.X + l * a.sX + n0; ld = a.H;
   } else if (op == mk::OP_GATEUP) {
     x = a.HRES + l * a.sHRES; gain = a.ffn_norm + (size_t)l * a.H;
   } else {
     x = a.ACT + l * a.sACT; resid = a.HRES + l * a.sHRES + n0; ld = a.H;
   }
-  if (!gemv<WT, NB, RPW, PIPE>(a, s, g, x, a.M, gain, gain != nullptr, mega, in, idx, resid, ld)) return;
+  if (!gemv<WT, NB, RPW, PIPE>(a, s, g, x, a.M, gain, gain != nullptr, mega, fused, in, idx, resid, ld)) return;
   {
     for (int e = threadIdx.x; e < n * a.M; e += NT) {
       const int row = e / a.M, b = e - row * a.M;
@@ -773,7 +773,11 @@ __device__ __forceinline__ void op_gemv_rpw(KArgs& a, Smem& s, const Instr in, u
 }
 
 template <typename WT, int NB>
-__device__ __forceinline__ void op_gemv(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
+// `fused`: an O-projection of a queue with fused split combines (merges the
+// split partials itself).  The per-op kernels decide it at compile time (a
+// separate O-projection kernel for fused queues), so the other per-op GEMV
+// kernels carry none of its code or registers.
+__device__ __forceinline__ void op_gemv(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega, bool fused) {
   constexpr int RPW = rpw_for<NB>();
   const int rows = (in.op == mk::OP_GATEUP ? 2 : 1) * (int)(in.a1 - in.a0);
   // Batched inputs or hidden size 4096 and up: weight lines are issued so that
@@ -783,15 +787,15 @@ __device__ __forceinline__ void op_gemv(KArgs& a, Smem& s, const Instr in, uint3
   const bool pipe = a.gemv_pipe == 1 || (a.gemv_pipe == 0 && (NB > 1 || a.H >= 4096));
   if (pipe) {
     if constexpr (RPW != 2) {
-      if (rows <= 2 * NWAVE) { op_gemv_rpw<WT, NB, 2, true>(a, s, in, idx, mega); return; }
+      if (rows <= 2 * NWAVE) { op_gemv_rpw<WT, NB, 2, true>(a, s, in, idx, mega, fused); return; }
     }
-    op_gemv_rpw<WT, NB, RPW, true>(a, s, in, idx, mega);
+    op_gemv_rpw<WT, NB, RPW, true>(a, s, in, idx, mega, fused);
     return;
   }
   if constexpr (RPW != 2) {
-    if (rows <= 2 * NWAVE) { op_gemv_rpw<WT, NB, 2, false>(a, s, in, idx, mega); return; }
+    if (rows <= 2 * NWAVE) { op_gemv_rpw<WT, NB, 2, false>(a, s, in, idx, mega, fused); return; }
   }
-  op_gemv_rpw<WT, NB, RPW, false>(a, s, in, idx, mega);
+  op_gemv_rpw<WT, NB, RPW, false>(a, s, in, idx, mega, fused);
 }
 
 // EMBED(n0, n1): X_0[b, n0:n1] = E[token_b, n0:n1]
@@ -1175,13 +1179,23 @@ __device__ __forceinline__ void op_combine(KArgs& a, Smem& s, const Instr in, ui
 
 // ----------------------------------------------------------------------------- dispatch
 
+// Per-op launch code of the O-projection of a queue with fused split combines
+// (never an opcode of the queue: the records say OP_OPROJ).
+constexpr int KPO_OPROJ_FUSED = 100;
+
 template <typename WT, int NB>
 __device__ __forceinline__ void run_instr(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega, int only_op) {
   const int op = only_op ? only_op : in.op;
   switch (op) {
     case mk::OP_EMBED: op_embed<WT>(a, in, mega); break;
     case mk::OP_QKV: case mk::OP_OPROJ: case mk::OP_GATEUP: case mk::OP_DOWN:
-      op_gemv<WT, NB>(a, s, in, idx, mega);
+      // one GEMV body for the four ops (the interpreter's code size matters for
+      // the instruction cache); only the megakernel's O-projection of a fused
+      // queue merges split partials, a per-op kernel never does here
+      op_gemv<WT, NB>(a, s, in, idx, mega, op == mk::OP_OPROJ && mega && a.fuse_combine);
+      break;
+    case KPO_OPROJ_FUSED:                                // per-op kernels only (folds away elsewhere)
+      if (only_op == KPO_OPROJ_FUSED) op_gemv<WT, NB>(a, s, in, idx, mega, true);
       break;
     case mk::OP_ATTN:
       if (a.hd == 64) op_attn<WT, 64>(a, s, in, idx, mega); else op_attn<WT, 128>(a, s, in, idx, mega);
@@ -1273,7 +1287,7 @@ __global__ __launch_bounds__(NT) void kpo_kernel(Args args, uint32_t first) {
   Smem s = make_smem(a);
   const uint32_t idx = first + blockIdx.x;
   const Instr in = load_instr(a, idx);
-  if (in.op != OP) {
+  if (in.op != (OP == KPO_OPROJ_FUSED ? mk::OP_OPROJ : OP)) {
     if (threadIdx.x == 0) record_error(a, ERR_OPCODE, idx, in.op, 0, 0);
     return;
   }
@@ -1293,7 +1307,7 @@ __global__ __launch_bounds__(NT) void lm_head_kernel(Args args) {
   const WT* W = static_cast<const WT*>(a.lm_head);
   Gemv<WT, NB, RPW, (NB > 1)> g{W, W, n, v0, n, a.H};
   Instr none{};
-  gemv<WT, NB, RPW, (NB > 1)>(a, s, g, a.lm_x, a.M, a.final_norm, true, false, none, 0, nullptr, 0);
+  gemv<WT, NB, RPW, (NB > 1)>(a, s, g, a.lm_x, a.M, a.final_norm, true, false, false, none, 0, nullptr, 0);
   for (int e = threadIdx.x; e < n * a.M; e += NT) {
     const int row = e / a.M, b = e - row * a.M;
     if (a.logits) a.logits[(size_t)b * a.V + v0 + row] = s.res[row * NB + b];
@@ -1523,7 +1537,7 @@ __global__ __launch_bounds__(NT) void kpo_prefill(Args args, uint32_t first) {
   Smem s = make_smem(a);
   const uint32_t idx = first + blockIdx.x;
   const Instr in = load_instr(a, idx);
-  if (in.op != OP) {
+  if (in.op != (OP == KPO_OPROJ_FUSED ? mk::OP_OPROJ : OP)) {
     if (threadIdx.x == 0) record_error(a, ERR_OPCODE, idx, in.op, 0, 0);
     return;
   }
@@ -1572,7 +1586,8 @@ struct Launch {
     return hipGetLastError();
   }
   static hipError_t kpo(const Args& a, uint32_t op, uint32_t first, uint32_t count, hipStream_t st) {
-    static uint32_t granted[mk::OP_COUNT] = {};
+    static uint32_t granted[KPO_OPROJ_FUSED + 1] = {};
+    if (op == mk::OP_OPROJ && a.fuse_combine) op = KPO_OPROJ_FUSED;
     switch (op) {
 #define KPO_CASE(OPC)                                                                              \
       case OPC: {                                                                                  \
@@ -1583,7 +1598,7 @@ struct Launch {
         break;                                                                                     \
       }
       KPO_CASE(mk::OP_EMBED) KPO_CASE(mk::OP_QKV) KPO_CASE(mk::OP_ATTN) KPO_CASE(mk::OP_COMBINE)
-      KPO_CASE(mk::OP_OPROJ) KPO_CASE(mk::OP_GATEUP) KPO_CASE(mk::OP_DOWN)
+      KPO_CASE(mk::OP_OPROJ) KPO_CASE(mk::OP_GATEUP) KPO_CASE(mk::OP_DOWN) KPO_CASE(KPO_OPROJ_FUSED)
 #undef KPO_CASE
       default: return hipErrorInvalidValue;
     }
