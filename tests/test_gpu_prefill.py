@@ -224,3 +224,16 @@ def test_prefill_bad_token_reports_device_error(small):
                  T.MK_MEGAKERNEL)
     e = T.mk_device_error(small.q, small.ws)
     assert e.code == 4 and e.barrier == 5 and e.value == SMALL.vocab + 3
+
+
+def test_prefill_rejects_hidden_not_multiple_of_128(small):
+    """The embedding and GEMM epilogues sum squares over 128-column groups of the
+    hidden rows: a hidden size of 192 is refused before anything runs."""
+    m = dataclasses.replace(SMALL, name="qwen-shaped-h192", hidden=192)
+    plan = W.Plan(bm=128, bn=128)
+    q = T.mk_build_queue(T.make_config(m), T.make_plan(plan, T.MK_PREFILL, 128, 256))
+    tok = torch.zeros((128,), dtype=torch.int32, device="cuda")
+    with pytest.raises(T.MkError) as ei:
+        T.mk_prefill(q, small.dq, small.dm.w, small.dkv.kv, tok, 16, 0, small.ws, small.logits, small.nxt,
+                     T.MK_MEGAKERNEL)
+    assert ei.value.status == T.MK_ENOTSUP
