@@ -261,7 +261,23 @@ struct PRowOut {
 
 __device__ __forceinline__ void p_write_rows(const float* ct, const PRowOut& p) {
   const int t = threadIdx.x, sub = t & 15, c = sub * 8;
-  for (int pass = 0; pass < PBM / (NT / 16); ++pass) {
+  constexpr int NPASS = PBM / (NT / 16);
+  // every pass's residual values are loaded up front (one memory round trip
+  // rather than one per pass: the stores of a pass would otherwise keep the
+  // next pass's loads from being issued early)
+  float4 rr[NPASS][2];
+  if (p.res) {
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+      const int row = pass * (NT / 16) + (t >> 4);
+      const bool valid = row < p.rows && p.n0 + c < p.ncols;
+      const size_t o = (size_t)(p.r0 + (valid ? row : 0)) * p.ld + p.n0 + (valid ? c : 0);
+      rr[pass][0] = ld_act4(p.res + o);
+      rr[pass][1] = ld_act4(p.res + o + 4);
+    }
+  }
+#pragma unroll
+  for (int pass = 0; pass < NPASS; ++pass) {
     const int row = pass * (NT / 16) + (t >> 4);
     const bool valid = row < p.rows && p.n0 + c < p.ncols;
     float x[8];
@@ -274,7 +290,7 @@ __device__ __forceinline__ void p_write_rows(const float* ct, const PRowOut& p) 
     if (valid) {
       const size_t o = (size_t)(p.r0 + row) * p.ld + p.n0 + c;
       if (p.res) {
-        const float4 u = ld_act4(p.res + o), w = ld_act4(p.res + o + 4);
+        const float4 u = rr[pass][0], w = rr[pass][1];
         x[0] += u.x; x[1] += u.y; x[2] += u.z; x[3] += u.w; x[4] += w.x; x[5] += w.y; x[6] += w.z; x[7] += w.w;
       }
       uint64_t* d = reinterpret_cast<uint64_t*>(p.out + o);
@@ -375,6 +391,11 @@ __device__ __forceinline__ void op_p_embed(KArgs& a, const Instr in, uint32_t id
   if (mega) signal_tile(a, in);
 }
 
+// Row stride of the QKV epilogue's staged tile: 4 floats of padding, so the
+// 32 rows that the lanes of one half-wave read at the same column fall in
+// different banks.
+constexpr int CT_QLD = PBN + 4;
+
 // P_QKV(m, n0, n1): one head's columns of QKV for row block m, with the
 // RMSNorm row scale, QK-norm and RoPE (q, k), the KV-cache write (k, v).
 __device__ __forceinline__ void op_p_qkv(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
@@ -400,7 +421,7 @@ __device__ __forceinline__ void op_p_qkv(KArgs& a, Smem& s, const Instr in, uint
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = p_row(wm, mi, v, lane), col = p_col(wn, ni, lane);
-        ct[row * PBN + col] = acc.c[mi][ni][v] * rs[row];
+        ct[row * CT_QLD + col] = acc.c[mi][ni][v] * rs[row];
       }
   __syncthreads();
   const int hh = n0 / PBN;                        // head index within [q | k | v]
@@ -409,7 +430,7 @@ __device__ __forceinline__ void op_p_qkv(KArgs& a, Smem& s, const Instr in, uint
   const int HALF = PBN / 2;
   float x0[32], x1[32];
 #pragma unroll
-  for (int k = 0; k < 32; ++k) { x0[k] = ct[row * PBN + part * 32 + k]; x1[k] = ct[row * PBN + HALF + part * 32 + k]; }
+  for (int k = 0; k < 32; ++k) { x0[k] = ct[row * CT_QLD + part * 32 + k]; x1[k] = ct[row * CT_QLD + HALF + part * 32 + k]; }
   if ((is_q || is_k) && a.qk_norm) {
     float ssq = 0.f;
 #pragma unroll
@@ -523,7 +544,7 @@ __device__ __forceinline__ void op_p_gateup(KArgs& a, Smem& s, const Instr in, u
       for (int v = 0; v < 16; ++v) {
         const int row = p_row(wm, mi, v, lane);
         const float gt = acc.c[mi][ni][v] * rs[row], u = up.c[mi][ni][v] * rs[row];
-        ct[row * PBN + p_col(wn, ni, lane)] = gt / (1.0f + expf(-gt)) * u;
+        ct[row * PBN + p_col(wn, ni, lane)] = gt / (1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gt)) * u;
       }
   __syncthreads();
   PRowOut o{a.ACT + l * a.sACT, nullptr, a.F, a.ACTB + l * a.sACTB, nullptr, nullptr, 0, n0, a.F, r0, rows};
