@@ -137,3 +137,22 @@ def test_builder_rejects_bad_fuse_flag():
         T.mk_build_queue(T.make_config(wl.model), T.make_plan(plan, QS.MODE_DECODE, 1, 129))
     with pytest.raises(QS.QueueError):
         QS.build(wl.model, plan, QS.MODE_DECODE, 1, 129)
+
+
+def test_options_validate_and_round_trip():
+    """Process-wide options are host state: out-of-range values are refused
+    (status, no change), valid ones read back."""
+    for key, good, bad in ((T.MK_OPT_GEMV_PIPE, (0, 1, 2), (-1, 3)),
+                           (T.MK_OPT_WORKERS_PER_CU, (1, 2), (0, 9)),
+                           (T.MK_OPT_SPIN_LIMIT, (1, 1 << 20), (0,))):
+        old = T.mk_get_option(key)
+        try:
+            for v in good:
+                T.mk_set_option(key, v)
+                assert T.mk_get_option(key) == v
+            for v in bad:
+                with pytest.raises(T.MkError):
+                    T.mk_set_option(key, v)
+                assert T.mk_get_option(key) == good[-1]
+        finally:
+            T.mk_set_option(key, old)
