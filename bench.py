@@ -156,7 +156,7 @@ def main():
         # causal prefill of the prompt into the (empty) cache, timed per call in both modes;
         # the decode steps below continue from the cache the last call wrote
         S = r.prefill_len
-        qp = T.mk_build_queue(T.make_config(m), T.make_plan(wl.plan, T.MK_PREFILL, S, r.ctx_max))
+        qp = T.mk_build_queue(T.make_config(m), T.make_plan(wl.plan.for_prefill(), T.MK_PREFILL, S, r.ctx_max))
         dqp, wsp = D.upload_queue(qp), D.workspace(qp)
         ptok = torch.from_numpy(W.gen.prefill_tokens(m, r)).cuda()
         plg = torch.empty((m.vocab,), dtype=torch.float32, device="cuda")

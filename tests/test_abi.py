@@ -79,6 +79,8 @@ def test_builder_bytes_prefill_qwen_shape():
     m = W.shrink(wl, n_layers=2).model
     got, ref = _both(m, wl.plan, QS.MODE_PREFILL, 512, wl.run.ctx_max)
     assert got == ref
+    got, ref = _both(m, wl.plan.for_prefill(), QS.MODE_PREFILL, 512, wl.run.ctx_max)   # its own sub-queues
+    assert got == ref
 
 
 @pytest.mark.parametrize("kw", [dict(rows=0), dict(rows=33), dict(ctx_max=0), dict(tq=0), dict(kb=0),

@@ -187,7 +187,7 @@ def test_qwen8b_prefill_then_decode_sampled_layers():
     K, V = W.gen.kv_cache(m, r)                 # empty cache, one row
     dkv = D.upload_kv(K, V)
     tokens = W.gen.prefill_tokens(m, r)
-    qp = T.mk_build_queue(T.make_config(m), T.make_plan(wl.plan, T.MK_PREFILL, S, r.ctx_max))
+    qp = T.mk_build_queue(T.make_config(m), T.make_plan(wl.plan.for_prefill(), T.MK_PREFILL, S, r.ctx_max))
     dqp, wsp = D.upload_queue(qp), D.workspace(qp)
     logits = torch.zeros((m.vocab,), dtype=torch.float32, device="cuda")
     nxt = torch.zeros((1,), dtype=torch.int32, device="cuda")

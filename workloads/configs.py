@@ -64,6 +64,9 @@ class Plan:
     fuse_combine: decode only; 1 drops the split-combine instructions: each
     O-projection tile waits on the attention splits' partials and merges them
     itself while staging its inputs (one barrier hand-off fewer per layer).
+    prefill_queues: sub-queues of the prefill queue (0: n_queues).  Prefill
+    instructions are long, so shared sub-queues (workers pop dynamically) cost
+    little and balance the causal attention tiles' unequal lengths.
     """
     tq: int = 16
     to: int = 16
@@ -74,6 +77,11 @@ class Plan:
     bn: int = 128
     n_queues: int = 1
     fuse_combine: int = 0
+    prefill_queues: int = 0
+
+    def for_prefill(self) -> "Plan":
+        """The plan of the prefill queue (its own sub-queue count)."""
+        return dataclasses.replace(self, n_queues=self.prefill_queues or self.n_queues)
 
 
 @dataclass(frozen=True)
@@ -153,7 +161,7 @@ WORKLOADS = {
     "qwen8b_prefill": Workload(
         "qwen8b_prefill", QWEN_8B,
         RunConfig(batch=1, ctx0=(2048,), steps=64, ctx_max=2112, seed=4, prefill_len=2048,
-                  init_cache=False), Plan(tq=24, to=16, tf=48, td=16, n_queues=256),
+                  init_cache=False), Plan(tq=24, to=16, tf=48, td=16, n_queues=256, prefill_queues=8),
         "Qwen3-8B-shaped bf16 with QK-norm: prefill of 2048 tokens, then 64 decode steps"),
     "llama1b_stream_b32": Workload(
         "llama1b_stream_b32", LLAMA_1B,
