@@ -109,7 +109,7 @@ def main():
     ap.add_argument("--queues", type=int, default=0, help="sub-queues (0: the workload's plan)")
     ap.add_argument("--tiles", default="", help="override tile widths, e.g. tq=16,to=8,tf=16,td=8,kb=256")
     ap.add_argument("--gemv-pipe", type=int, default=0,
-                    help="decode GEMV weight issue: 0 by shape, 1 pipelined, 2 compiler-ordered")
+                    help="decode GEMV weight issue: 0 or 1 pipelined (default), 2 compiler-ordered")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--modes", default="mega,kpo,kpo_graph")

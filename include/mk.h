@@ -222,10 +222,10 @@ enum {
    * address to 0 to stop. */
   MK_OPT_TRACE_BUFFER = 3,
   MK_OPT_TRACE_BYTES = 4,
-  /* How decode GEMVs issue their weight lines: 0 (default) chooses by shape,
-   * 1 always keeps the ring's lines in flight while staged inputs are read,
-   * 2 always lets the compiler order them (it waits for every line in flight
-   * before each read of the staged inputs).  Results are identical. */
+  /* How decode GEMVs issue their weight lines: 0 (default) and 1 keep the
+   * ring's lines in flight while staged inputs are read, 2 lets the compiler
+   * order them (it waits for every line in flight before each read of the
+   * staged inputs).  Results are identical. */
   MK_OPT_GEMV_PIPE = 5
 };
 mk_status mk_set_option(int32_t key, int64_t value);

@@ -73,7 +73,7 @@ struct Options {
   uint32_t spin_limit = 1u << 22;
   unsigned long long* trace = nullptr;   // device buffer, 64 bytes per instruction
   size_t trace_bytes = 0;
-  int gemv_pipe = 0;                     // 0: by shape, 1: pipelined issue, 2: compiler-ordered issue
+  int gemv_pipe = 0;                     // 0, 1: pipelined issue; 2: compiler-ordered issue
 };
 Options g_opt;
 

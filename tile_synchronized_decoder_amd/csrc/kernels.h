@@ -90,7 +90,7 @@ struct Args {
   int seq_len, kv_row, M_cache;
   uint32_t lds_ring;             // bytes of the ring / prefill tile region
   const float* lm_x;             // LM head input rows
-  int gemv_pipe;                 // decode GEMV weight issue: 0 by shape, 1 pipelined, 2 compiler-ordered
+  int gemv_pipe;                 // decode GEMV weight issue: 0, 1 pipelined; 2 compiler-ordered
   int fuse_combine;              // decode queue without split combines: O-projection merges the partials
   // prefill: bf16 GEMM operands (X and HRES with the consumer's RMSNorm gain
   // applied), per-row sums of squares of X / HRES per 128-column tile
@@ -369,11 +369,8 @@ __device__ __forceinline__ Smem make_smem(KArgs& a) {
 // not treat every later shared-memory read as depending on it (it would wait
 // for all outstanding loads before each read); the code that consumes the
 // data waits for it explicitly with wait_vm.  POL 1 adds sc1 (device-coherent).
-// The prefill GEMM pipeline and the decode GEMVs of large models or batched
-// inputs use it.  The single-row decode GEMV of small models keeps the
-// compiler's builtin: the extra waits it implies throttle each workgroup's
-// weight stream, which measured faster there (less memory-queue delay for the
-// latency-critical barrier and input loads of other tiles).
+// The prefill GEMM pipeline and the decode GEMVs use it; the compiler's builtin
+// remains as the MK_OPT_GEMV_PIPE = 2 variant of the decode GEMVs.
 template <int POL>
 __device__ __forceinline__ void dma_lds16(const void* src, void* lds) {
   const uint32_t l = __builtin_amdgcn_readfirstlane(
@@ -780,11 +777,12 @@ template <typename WT, int NB>
 __device__ __forceinline__ void op_gemv(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega, bool fused) {
   constexpr int RPW = rpw_for<NB>();
   const int rows = (in.op == mk::OP_GATEUP ? 2 : 1) * (int)(in.a1 - in.a0);
-  // Batched inputs or hidden size 4096 and up: weight lines are issued so that
-  // the compiler does not serialise the ring (it would wait for every line in
-  // flight before each read of the staged inputs); a single input row of a
-  // smaller model measured faster with the serialised ring.
-  const bool pipe = a.gemv_pipe == 1 || (a.gemv_pipe == 0 && (NB > 1 || a.H >= 4096));
+  // Weight lines are issued so that the compiler does not serialise the ring
+  // (with its builtin it waits for every line in flight before each read of the
+  // staged inputs).  The compiler-ordered issue stays selectable
+  // (MK_OPT_GEMV_PIPE = 2): 1.107 against 1.035 ms per step for the 1B shape at
+  // batch 1.
+  const bool pipe = a.gemv_pipe != 2;
   if (pipe) {
     if constexpr (RPW != 2) {
       if (rows <= 2 * NWAVE) { op_gemv_rpw<WT, NB, 2, true>(a, s, in, idx, mega, fused); return; }
