@@ -43,12 +43,12 @@ constexpr int XBUF_MAX = 36864;         // LDS staging of GEMV inputs, upper bou
 constexpr int ROWS_PER_PASS_MAX = 16;   // GEMV rows reduced per pass (4 waves x 4)
 constexpr int ATT_MAX_R = 4;            // query heads per KV head
 constexpr int LM_ROWS = 64;             // vocabulary rows per LM-head workgroup
-// 1 KB weight lines in flight per wave: 24 (96 KB per workgroup); 12 at 32
-// input rows, where the staged inputs need the room (32 x 512 floats per chunk)
-// Weight lines (1 KB) in flight per wave.  Batched GEMVs do more arithmetic per
-// line and need the shared memory for their inputs, so their rings are shorter.
+// Weight lines (1 KB) in flight per wave: 20 for one or two input rows (80 KB
+// per workgroup; 16, 24, 28 and 32 measured slower for the 1B shape), 16 for
+// more.  Batched GEMVs do more arithmetic per line and need the shared memory
+// for their inputs, so their rings are shorter.
 #ifndef MK_RING_LINES_SMALL
-#define MK_RING_LINES_SMALL 24
+#define MK_RING_LINES_SMALL 20
 #endif
 constexpr int ring_lines_for(int nb) { return nb <= 2 ? MK_RING_LINES_SMALL : 16; }
 template <int NB> constexpr int ring_lines() { return ring_lines_for(NB); }
@@ -869,24 +869,25 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
   KT* Vc = static_cast<KT*>(a.vc) + head_off * HD;
   auto key_of = [&](int rd) { return j0 + rd * KPR + wave * KPW + kk; };
 
-  // this lane's 8-dim slices of the cached keys / values of one chunk of rounds
+  // this lane's 8-dim slices of the cached keys / values of one chunk of rounds;
+  // rows without a cached key read as zeros (weight 0, never NaN * 0)
   v4u kr[RPC][WPE], vr[RPC][WPE];
-  auto load_chunk = [&](int c0) {
+  auto load_rows = [&](v4u (&dst)[RPC][WPE], const KT* base, int c0) {
 #pragma unroll
     for (int rd = 0; rd < RPC; ++rd) {
       const int j = key_of(c0 + rd);
       if (j < j1 && j < pos) {
-        const v4u* pk = reinterpret_cast<const v4u*>(Kc + (size_t)j * HD + ds * 8);
-        const v4u* pv = reinterpret_cast<const v4u*>(Vc + (size_t)j * HD + ds * 8);
+        const v4u* p = reinterpret_cast<const v4u*>(base + (size_t)j * HD + ds * 8);
 #pragma unroll
-        for (int w = 0; w < WPE; ++w) { kr[rd][w] = __builtin_nontemporal_load(pk + w); vr[rd][w] = __builtin_nontemporal_load(pv + w); }
-      } else {                                          // no cached row: zeros (its weight is 0, never NaN * 0)
+        for (int w = 0; w < WPE; ++w) dst[rd][w] = __builtin_nontemporal_load(p + w);
+      } else {
 #pragma unroll
-        for (int w = 0; w < WPE; ++w) { kr[rd][w] = v4u{0u, 0u, 0u, 0u}; vr[rd][w] = v4u{0u, 0u, 0u, 0u}; }
+        for (int w = 0; w < WPE; ++w) dst[rd][w] = v4u{0u, 0u, 0u, 0u};
       }
     }
   };
-  load_chunk(0);
+  load_rows(kr, Kc, 0);
+  load_rows(vr, Vc, 0);
   if (mega && !wait_tiles(a, in, idx)) return;
 
   float* slot = a.OPART + l * a.sOP + ((size_t)(b * a.nkv + g) * a.NS + sp) * (size_t)(r * HD + 2 * r);
@@ -1001,8 +1002,10 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
     for (int e = 0; e < 8; ++e) o_run[h][e] = 0.f;
   }
   const int nrounds = (j1 - j0 + KPR - 1) / KPR;
+  // The next chunk's keys are requested once this chunk's scores are formed and
+  // its values once they are summed, so each load overlaps the other half.
   for (int c0 = 0; c0 < nrounds; c0 += RPC) {
-    if (c0 > 0) load_chunk(c0);
+    const bool more = c0 + RPC < nrounds;
     float sc[RPC][ATT_MAX_R];
 #pragma unroll
     for (int rd = 0; rd < RPC; ++rd) {
@@ -1022,6 +1025,7 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
         sc[rd][h] = (j < j1 && h < r) ? p * scale : -INFINITY;
       }
     }
+    if (more) load_rows(kr, Kc, c0 + RPC);
 #pragma unroll
     for (int h = 0; h < ATT_MAX_R; ++h) {
       float mc = sc[0][h];
@@ -1051,6 +1055,7 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
         for (int e = 0; e < 8; ++e) o_run[h][e] = fmaf(p, vf[e], o_run[h][e]);
       }
     }
+    if (more) load_rows(vr, Vc, c0 + RPC);
   }
   if (mega) trace_mark(a, idx, 4);
 
