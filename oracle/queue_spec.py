@@ -21,7 +21,9 @@ What the pages leave open and this module fixes (the plainest reading):
   column start, row start).  It is stored as ranges: maximal runs of that
   ordered list whose barrier ids are consecutive become one (first, count).
 * Queue order is canonical: embedding tiles, then per layer the QKV tiles, the
-  attention splits (row, KV head, split), the split combines (KV head, row) --
+  attention splits (split-major: for split s, the (row, KV head) pairs in
+  order starting s rows on, cyclically, so that the instructions a worker
+  takes by position span several rows), the split combines (KV head, row) --
   the order in which their output tiles lie along the columns, so a reader of
   the whole attention output waits on one run of consecutive barriers -- then
   the O-projection, gate/up and down tiles (decode); the prefill queue has the same shape over 2-D row x column
@@ -201,15 +203,17 @@ def _decode_instrs(model, plan, M: int, NS: int) -> List[Instr]:
         HR, ACT, XN = tensor_order(l, T_HRES), tensor_order(l, T_ACT), tensor_order(l, T_XNEXT)
         for n0, n1 in _tiles(NQKV, plan.tq):
             out.append(Instr(OP_QKV, l, n0, n1, 0, (QKV, (0, M, n0, n1)), [(X, (0, M, 0, H))]))
-        for b in range(M):
-            for g in range(nkv):
+        # split-major; the (row, KV head) pairs are rotated by one row per split
+        P = M * nkv
+        for s in range(NS):
+            for t in range(P):
+                b, g = divmod((t + s * nkv) % P, nkv)
                 qc = (g * r * hd, (g + 1) * r * hd)
                 kc = (nq * hd + g * hd, nq * hd + (g + 1) * hd)
                 vc = ((nq + nkv) * hd + g * hd, (nq + nkv) * hd + (g + 1) * hd)
-                for s in range(NS):
-                    out.append(Instr(OP_ATTN, l, b, g, s, (OP, (b, b + 1, g, g + 1)),
-                                     [(QKV, (b, b + 1) + qc), (QKV, (b, b + 1) + kc),
-                                      (QKV, (b, b + 1) + vc)]))
+                out.append(Instr(OP_ATTN, l, b, g, s, (OP, (b, b + 1, g, g + 1)),
+                                 [(QKV, (b, b + 1) + qc), (QKV, (b, b + 1) + kc),
+                                  (QKV, (b, b + 1) + vc)]))
         fused = getattr(plan, "fuse_combine", 0)
         if not fused:
             for g in range(nkv):

@@ -102,6 +102,13 @@ struct Builder {
         if (x_exists(l)) w.push_back({x_id(l, 0), nX});
         emit(OP_QKV, l, n * p.tq, std::min((n + 1) * p.tq, NQKV), 0, qkv_id(l, n), w);
       }
+      // Splits are emitted split-major, the (row, KV head) pairs rotated by one
+      // row per split, so that a worker's share of a layer's splits spans
+      // several rows: with ragged contexts the later splits of a row are short
+      // or empty, and a worker holding one split index for many rows would
+      // hold only full or only empty splits.
+      const uint32_t P = M * nkv;
+      std::vector<std::vector<std::pair<uint32_t, uint32_t>>> att_waits(P);
       for (uint32_t b = 0; b < M; ++b)
         for (uint32_t g = 0; g < nkv; ++g) {
           // column intervals of q (group g), k_g and v_g, as QKV tile-index intervals
@@ -115,10 +122,13 @@ struct Builder {
             else
               tiles.push_back({t0, t1});
           }
-          std::vector<std::pair<uint32_t, uint32_t>> w;
-          for (auto& t : tiles) w.push_back({qkv_id(l, t.first), t.second - t.first + 1});
-          for (uint32_t s = 0; s < NS; ++s) emit(OP_ATTN, l, b, g, s, op_id(l, b, g), w);
+          for (auto& t : tiles) att_waits[b * nkv + g].push_back({qkv_id(l, t.first), t.second - t.first + 1});
           q->targets[op_id(l, b, g)] = NS;
+        }
+      for (uint32_t s = 0; s < NS; ++s)
+        for (uint32_t t = 0; t < P; ++t) {
+          const uint32_t pr = (t + s * nkv) % P, b = pr / nkv, g = pr % nkv;
+          emit(OP_ATTN, l, b, g, s, op_id(l, b, g), att_waits[pr]);
         }
       if (!fused)
         for (uint32_t g = 0; g < nkv; ++g)
