@@ -1,0 +1,136 @@
+"""The step-time predictor: closed-form schedules, and a longest path over the
+explicit dependency graph of a real queue."""
+import numpy as np
+import pytest
+
+import tile_synchronized_decoder_amd as T
+from tile_synchronized_decoder_amd import predict as P
+import workloads as W
+
+
+def _graph(ops, waits, signals, n_barriers, n_queues):
+    """Hand-made graph: waits[i] is a list of (first, count) ranges."""
+    ranges, off, cnt = [], [], []
+    for w in waits:
+        off.append(len(ranges)); cnt.append(len(w)); ranges.extend(w)
+    targets = np.zeros(n_barriers, dtype=np.int64)
+    for s in signals:
+        targets[s] += 1
+    return P.Graph(op=np.array(ops), layer=np.zeros(len(ops), dtype=np.int64), wait_off=np.array(off),
+                   wait_cnt=np.array(cnt), signal=np.array(signals),
+                   ranges=np.array(ranges, dtype=np.int64).reshape(-1, 2), targets=targets,
+                   n_queues=n_queues)
+
+
+def test_chain_across_workers_adds_durations_and_hops():
+    g = _graph([2, 5, 6], [[], [(0, 1)], [(1, 1)]], [0, 1, 2], 3, 3)
+    step, start, end = P.simulate(g, {2: 3.0, 5: 4.0, 6: 5.0}, hop=0.5)
+    assert step == pytest.approx(3 + 0.5 + 4 + 0.5 + 5)
+    assert start.tolist() == pytest.approx([0, 3.5, 8.0])
+
+
+def test_one_worker_serialises_independent_instructions():
+    g = _graph([2, 2, 2], [[], [], []], [0, 1, 2], 3, 3)
+    assert P.simulate(g, {2: 2.0}, n_workers=1)[0] == pytest.approx(6.0)
+    assert P.simulate(g, {2: 2.0})[0] == pytest.approx(2.0)
+
+
+def test_waiting_on_several_signallers_takes_the_last():
+    # barrier 0 has two writers of different lengths; the reader waits for both
+    g = _graph([2, 6, 7], [[], [], [(0, 1)]], [0, 0, 1], 2, 3)
+    step, start, _ = P.simulate(g, {2: 1.0, 6: 7.0, 7: 1.0}, hop=0.25)
+    assert start[2] == pytest.approx(7.25) and step == pytest.approx(8.25)
+
+
+def test_prefetch_overlaps_only_the_wait():
+    # the consumer's worker is free at 0; its input is ready at 10 + hop
+    g = _graph([6, 7], [[], [(0, 1)]], [0, 1], 2, 2)
+    d = {6: 10.0, 7: 6.0}
+    assert P.simulate(g, d, hop=1.0, prefetch={7: 4.0})[0] == pytest.approx(11 + 6 - 4)
+    assert P.simulate(g, d, hop=1.0, prefetch={7: 100.0})[0] == pytest.approx(11 + 6 - 6)
+    # free later than ready: nothing to overlap
+    g2 = _graph([6, 6, 7], [[], [], [(0, 1)]], [0, 2, 1], 3, 2)
+    assert P.simulate(g2, {6: 10.0, 7: 6.0}, hop=0.0, prefetch={7: 4.0})[0] == pytest.approx(10 + 6)
+
+
+def _longest_path(g, dur, hop):
+    """Earliest finish over an explicit DAG: edges from a worker's previous
+    instruction (weight 0) and from every writer of a waited barrier (weight hop),
+    relaxed in topological order found by Kahn's algorithm."""
+    n, nw = len(g.op), g.n_queues
+    writers = {}
+    for i, s in enumerate(g.signal.tolist()):
+        writers.setdefault(s, []).append(i)
+    preds = [[] for _ in range(n)]
+    for i in range(n):
+        if i >= nw:
+            preds[i].append((i - nw, 0.0))
+        for k in range(g.wait_off[i], g.wait_off[i] + g.wait_cnt[i]):
+            first, count = g.ranges[k]
+            for b in range(first, first + count):
+                preds[i].extend((j, hop) for j in writers[b])
+    succ = [[] for _ in range(n)]
+    indeg = [0] * n
+    for i in range(n):
+        for j, _ in preds[i]:
+            succ[j].append(i); indeg[i] += 1
+    order = [i for i in range(n) if indeg[i] == 0]
+    fin = np.zeros(n)
+    for i in order:                      # order grows while it is walked
+        st = max([fin[j] + w for j, w in preds[i]], default=0.0)
+        fin[i] = st + dur[int(g.op[i])]
+        for k in succ[i]:
+            indeg[k] -= 1
+            if indeg[k] == 0:
+                order.append(k)
+    assert len(order) == n, "dependency cycle"
+    return fin.max()
+
+
+@pytest.mark.parametrize("name", ["layer256_f32", "llama1b_b1"])
+def test_simulation_equals_longest_path_on_a_real_queue(name):
+    wl = W.WORKLOADS[name]
+    if name == "llama1b_b1":
+        wl = W.configs.shrink(wl, n_layers=2, vocab=256)
+    m, r = wl.model, wl.run
+    q = T.mk_build_queue(T.make_config(m), T.make_plan(wl.plan, T.MK_DECODE, r.batch, r.ctx_max))
+    g = P.graph_from_parts(q.parts())
+    rng = np.random.default_rng(5)
+    dur = {op: float(rng.uniform(1, 10)) for op in range(1, 8)}
+    step, _, _ = P.simulate(g, dur, hop=0.7)
+    assert step == pytest.approx(_longest_path(g, dur, 0.7))
+
+
+def test_kpo_step_counts_one_launch_per_layer_and_op():
+    g = _graph([1, 2, 3, 2], [[], [], [], []], [0, 1, 2, 3], 4, 4)
+    g.layer = np.array([0, 0, 0, 1])
+    assert P.kpo_step(g, {1: 1.0, 2: 2.0, 3: 3.0}, gap_us=0.5) == pytest.approx(1 + 2 + 3 + 2 + 4 * 0.5)
+
+
+def test_kernel_names_map_to_ops():
+    rows = [("void mkd::kpo_kernel<unsigned short, 1, 6>(mkd::Args, unsigned int)", 17590.0),
+            ("void mkd::kpo_kernel<float, 32, 100>(mkd::Args, unsigned int)", 9000.0),
+            ("void mkd::mk_interp<unsigned short, 1>(mkd::Args)", 911000.0)]
+    assert P.kpo_kernel_us(rows) == {6: pytest.approx(17.59), 5: pytest.approx(9.0)}
+
+
+def test_per_instruction_time_divides_by_rounds():
+    assert P.per_instruction_us({3: 120.0, 6: 17.0}, {3: 2304, 6: 256}, 256) == {
+        3: pytest.approx(120.0 / 9), 6: pytest.approx(17.0)}
+
+
+def test_shared_sub_queue_goes_to_the_first_free_worker():
+    # one sub-queue, two workers: the long first instruction keeps worker 0 busy
+    # while worker 1 takes the three short ones in turn
+    g = _graph([6, 2, 2, 2], [[], [], [], []], [0, 1, 2, 3], 4, 1)
+    step, start, _ = P.simulate(g, {6: 5.0, 2: 1.0}, n_workers=2)
+    assert step == pytest.approx(5.0) and start.tolist() == pytest.approx([0, 0, 1, 2])
+
+
+def test_kernel_summary_tables_parse():
+    import os
+    path = os.path.join(os.path.dirname(__file__), "..", "profiles", "mk_interp_llama1b_b1_kernels.md")
+    rows = P.read_kernel_stats_md(path)
+    k = P.kpo_kernel_us(rows)
+    assert set(k) >= {2, 3, 4, 5, 6, 7} and all(v > 0 for v in k.values())
+    assert any("mk_interp<" in n for n, _ in rows)
