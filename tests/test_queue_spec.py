@@ -300,3 +300,14 @@ def test_fused_combine_simulation_detects_missing_split_wait():
         seen |= bool(res.bad_reads) or bool(np.any(np.isnan(res.x_out)))
     assert seen
     assert CK.static_check(wl.model, mutant) != []
+
+
+def test_attention_splits_are_split_major_and_rotated():
+    """Hand-worked order for 3 rows x 2 KV heads x 3 splits: split s starts at
+    the pair s rows on and wraps, so a worker taking every n-th instruction by
+    position meets several rows."""
+    q = QS.build(W.LLAMA_LAYER_F32, W.Plan(tq=16, to=16, tf=32, td=16, kb=32), QS.MODE_DECODE, 3, 96)
+    att = [(i.a0, i.a1, i.a2) for i in q.instrs if i.op == QS.OP_ATTN]
+    assert att == [(0, 0, 0), (0, 1, 0), (1, 0, 0), (1, 1, 0), (2, 0, 0), (2, 1, 0),
+                   (1, 0, 1), (1, 1, 1), (2, 0, 1), (2, 1, 1), (0, 0, 1), (0, 1, 1),
+                   (2, 0, 2), (2, 1, 2), (0, 0, 2), (0, 1, 2), (1, 0, 2), (1, 1, 2)]
