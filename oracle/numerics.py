@@ -15,8 +15,10 @@ This module takes the plainest standard reading, one step at a time:
   x'   = h + a Wd^T
   logits = RMSNorm(x_L; g_final) W_lm^T
 
-All arithmetic is float64.  Weights arrive as the workload's storage arrays
-(bf16 bit patterns or float32) and are widened exactly.  The only rounding to
+All arithmetic is float64 (the timed CPU baseline runs the same functions on
+float32 weights).  Weights arrive as the workload's storage arrays (bf16 bit
+patterns or float32) and are widened exactly.  Rotary angles are always
+computed in float64.  The only rounding to
 a narrower type is where the decoder itself stores into its KV cache, whose
 element type is part of the model (bf16 for the bf16 models).
 """
@@ -40,6 +42,15 @@ def to_f64(arr: np.ndarray) -> np.ndarray:
     if arr.dtype == np.uint16:
         return bf16_bits_to_f64(arr)
     return arr.astype(np.float64)
+
+
+def widen(arr: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """Storage values (bf16 bit patterns or float32) as ``dtype`` (float64, or
+    float32 for the timed CPU baseline); exact for both: a bf16 value is an
+    fp32 value."""
+    if arr.dtype == np.uint16:
+        return (arr.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(dtype, copy=False)
+    return arr.astype(dtype, copy=False)
 
 
 def store_like(x: np.ndarray, like_dtype) -> np.ndarray:
@@ -79,7 +90,7 @@ def rope(x: np.ndarray, pos: int, theta: float) -> np.ndarray:
     hd = x.shape[-1]
     half = hd // 2
     ang = rope_angles(pos, hd, theta)
-    c, s = np.cos(ang), np.sin(ang)
+    c, s = np.cos(ang).astype(x.dtype), np.sin(ang).astype(x.dtype)
     a, b = x[..., :half], x[..., half:]
     return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
 
@@ -168,13 +179,16 @@ class Model:
     final_norm: Optional[np.ndarray] = None
 
 
-def prepare_layer(raw: Dict[str, np.ndarray]) -> Layer:
-    return Layer(**{k: to_f64(v) for k, v in raw.items()})
+def prepare_layer(raw: Dict[str, np.ndarray], dtype=np.float64) -> Layer:
+    """One layer's weights widened to ``dtype``: float64 for parity; the timed
+    CPU baseline runs the same functions on float32 weights."""
+    return Layer(**{k: widen(v, dtype) for k, v in raw.items()})
 
 
-def prepare(cfg, raw_layers: Sequence[Dict[str, np.ndarray]], raw_global: Dict[str, np.ndarray]) -> Model:
-    return Model(cfg, [prepare_layer(r) for r in raw_layers],
-                 **{k: to_f64(v) for k, v in raw_global.items()})
+def prepare(cfg, raw_layers: Sequence[Dict[str, np.ndarray]], raw_global: Dict[str, np.ndarray],
+            dtype=np.float64) -> Model:
+    return Model(cfg, [prepare_layer(r, dtype) for r in raw_layers],
+                 **{k: widen(v, dtype) for k, v in raw_global.items()})
 
 
 @dataclass
@@ -211,6 +225,98 @@ def _mlp(cfg, lw: Layer, h: np.ndarray):
     return a, a @ lw.wdown.T
 
 
+def causal_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """Grouped-query attention of S consecutive positions starting at 0.
+
+    q: [S, nq, hd]; K, V: [nkv, S, hd].  Query i of head h sees keys 0..i of
+    KV head h // (nq / nkv): the score matrix of each head with the entries
+    above the diagonal set to -inf, then a row softmax.  Returns [S, nq, hd].
+    """
+    S, nq, hd = q.shape
+    r = nq // K.shape[0]
+    future = np.triu(np.ones((S, S), dtype=bool), 1)        # key j > query i
+    out = np.empty_like(q)
+    for h in range(nq):
+        g = h // r
+        s = (q[:, h] @ K[g].T) / math.sqrt(hd)              # [S, S]
+        s[future] = -np.inf
+        out[:, h] = softmax(s) @ V[g]
+    return out
+
+
+@dataclass
+class LayerTrace:
+    """One layer's intermediates for all rows (decode) or positions (prefill)."""
+    q: np.ndarray               # after QK-norm and RoPE, [B, nq, hd]
+    k: np.ndarray               # [B, nkv, hd]
+    v: np.ndarray
+    attn: np.ndarray            # concat heads, [B, nq*hd]
+    attn_branch: np.ndarray     # attn @ Wo^T, [B, H]
+    h: np.ndarray               # x + attn_branch
+    act: np.ndarray             # SwiGLU output, [B, F]
+    mlp_branch: np.ndarray
+    x_out: np.ndarray           # h + mlp_branch
+
+
+def _finish_layer(cfg, lw: Layer, x, qs, ks, v, att) -> LayerTrace:
+    ab = att @ lw.wo.T
+    h = x + ab
+    a, mb = _mlp(cfg, lw, h)
+    return LayerTrace(qs, ks, v, att, ab, h, a, mb, h + mb)
+
+
+def decode_layer(cfg, lw: Layer, x: np.ndarray, K: np.ndarray, V: np.ndarray,
+                 ctx_lens: Sequence[int]) -> LayerTrace:
+    """One decoder layer of a decode step for B rows x [B, H].
+
+    K, V: this layer's cache [B, nkv, ctx_max, hd] in storage type; the new key
+    and value of row b are written at position ctx_lens[b] (0-based) and
+    attention sees positions 0..ctx_lens[b].
+    """
+    ft = lw.wo.dtype
+    B = x.shape[0]
+    q, k, v = _project_qkv(cfg, lw, rms_norm(x, lw.attn_norm, cfg.rms_eps))
+    att = np.empty((B, cfg.attn_cols), dtype=ft)
+    qs, ks = np.empty_like(q), np.empty_like(k)
+    for b in range(B):
+        p = int(ctx_lens[b])
+        qs[b] = rope(q[b], p, cfg.rope_theta)
+        ks[b] = rope(k[b], p, cfg.rope_theta)
+        K[b, :, p] = store_like(ks[b], K.dtype)
+        V[b, :, p] = store_like(v[b], V.dtype)
+        att[b] = attention(qs[b], widen(K[b, :, : p + 1], ft), widen(V[b, :, : p + 1], ft)).reshape(-1)
+    return _finish_layer(cfg, lw, x, qs, ks, v, att)
+
+
+def prefill_layer(cfg, lw: Layer, x: np.ndarray, K: np.ndarray, V: np.ndarray, row: int = 0) -> LayerTrace:
+    """One decoder layer of a causal prefill of S positions x [S, H] from position 0.
+
+    K, V: this layer's cache [rows, nkv, ctx_max, hd]; positions 0..S-1 of cache
+    row ``row`` are written, and query i attends to keys 0..i.
+    """
+    ft = lw.wo.dtype
+    S = x.shape[0]
+    q, k, v = _project_qkv(cfg, lw, rms_norm(x, lw.attn_norm, cfg.rms_eps))
+    qs = np.stack([rope(q[i], i, cfg.rope_theta) for i in range(S)])
+    ks = np.stack([rope(k[i], i, cfg.rope_theta) for i in range(S)])
+    K[row, :, :S] = store_like(ks.transpose(1, 0, 2), K.dtype)
+    V[row, :, :S] = store_like(v.transpose(1, 0, 2), V.dtype)
+    att = causal_attention(qs, widen(K[row, :, :S], ft), widen(V[row, :, :S], ft)).reshape(S, -1)
+    return _finish_layer(cfg, lw, x, qs, ks, v, att)
+
+
+def lm_head(cfg, x: np.ndarray, final_norm: np.ndarray, w_lm: np.ndarray) -> np.ndarray:
+    """Logits of the rows x [B, H]: RMSNorm(x; g_final) W_lm^T."""
+    return rms_norm(x, final_norm, cfg.rms_eps) @ w_lm.T
+
+
+def _append(tr: Trace, x: np.ndarray, lt: LayerTrace) -> None:
+    tr.x_in.append(x)
+    tr.q.append(lt.q); tr.k.append(lt.k); tr.v.append(lt.v); tr.attn.append(lt.attn)
+    tr.attn_branch.append(lt.attn_branch); tr.h.append(lt.h); tr.act.append(lt.act)
+    tr.mlp_branch.append(lt.mlp_branch)
+
+
 def decode_step(model: Model, K: np.ndarray, V: np.ndarray, ctx_lens: Sequence[int],
                 tokens: Optional[np.ndarray] = None, x0: Optional[np.ndarray] = None) -> Trace:
     """One decode step for B sequences.
@@ -222,32 +328,16 @@ def decode_step(model: Model, K: np.ndarray, V: np.ndarray, ctx_lens: Sequence[i
     embedding, ``x0`` [B, H].
     """
     cfg = model.cfg
-    x = model.embed[np.asarray(tokens)] if cfg.has_embed else np.asarray(x0, dtype=np.float64)
-    B = x.shape[0]
+    ft = model.layers[0].wo.dtype
+    x = model.embed[np.asarray(tokens)] if cfg.has_embed else np.asarray(x0, dtype=ft)
     tr = Trace()
     for l, lw in enumerate(model.layers):
-        tr.x_in.append(x)
-        q, k, v = _project_qkv(cfg, lw, rms_norm(x, lw.attn_norm, cfg.rms_eps))
-        att = np.empty((B, cfg.attn_cols))
-        qs, ks = np.empty_like(q), np.empty_like(k)
-        for b in range(B):
-            p = int(ctx_lens[b])
-            qs[b] = rope(q[b], p, cfg.rope_theta)
-            ks[b] = rope(k[b], p, cfg.rope_theta)
-            K[l, b, :, p] = store_like(ks[b], K.dtype)
-            V[l, b, :, p] = store_like(v[b], V.dtype)
-            Kb = to_f64(K[l, b, :, : p + 1])
-            Vb = to_f64(V[l, b, :, : p + 1])
-            att[b] = attention(qs[b], Kb, Vb).reshape(-1)
-        ab = att @ lw.wo.T
-        h = x + ab
-        a, mb = _mlp(cfg, lw, h)
-        x = h + mb
-        tr.q.append(qs); tr.k.append(ks); tr.v.append(v); tr.attn.append(att)
-        tr.attn_branch.append(ab); tr.h.append(h); tr.act.append(a); tr.mlp_branch.append(mb)
+        lt = decode_layer(cfg, lw, x, K[l], V[l], ctx_lens)
+        _append(tr, x, lt)
+        x = lt.x_out
     tr.x_out = x
     if cfg.has_lm_head:
-        tr.logits = rms_norm(x, model.final_norm, cfg.rms_eps) @ model.lm_head.T
+        tr.logits = lm_head(cfg, x, model.final_norm, model.lm_head)
     return tr
 
 
@@ -260,30 +350,16 @@ def prefill(model: Model, K: np.ndarray, V: np.ndarray, tokens: Optional[np.ndar
     ``x0`` [S, H].  Logits are returned for the last position only ([1, V]).
     """
     cfg = model.cfg
-    x = model.embed[np.asarray(tokens)] if x0 is None else np.asarray(x0, dtype=np.float64)
-    S = x.shape[0]
+    ft = model.layers[0].wo.dtype
+    x = model.embed[np.asarray(tokens)] if x0 is None else np.asarray(x0, dtype=ft)
     tr = Trace()
     for l, lw in enumerate(model.layers):
-        tr.x_in.append(x)
-        q, k, v = _project_qkv(cfg, lw, rms_norm(x, lw.attn_norm, cfg.rms_eps))
-        qs = np.stack([rope(q[i], i, cfg.rope_theta) for i in range(S)])
-        ks = np.stack([rope(k[i], i, cfg.rope_theta) for i in range(S)])
-        K[l, row, :, :S] = store_like(ks.transpose(1, 0, 2), K.dtype)
-        V[l, row, :, :S] = store_like(v.transpose(1, 0, 2), V.dtype)
-        Kf = to_f64(K[l, row, :, :S])
-        Vf = to_f64(V[l, row, :, :S])
-        att = np.empty((S, cfg.attn_cols))
-        for i in range(S):
-            att[i] = attention(qs[i], Kf[:, : i + 1], Vf[:, : i + 1]).reshape(-1)
-        ab = att @ lw.wo.T
-        h = x + ab
-        a, mb = _mlp(cfg, lw, h)
-        x = h + mb
-        tr.q.append(qs); tr.k.append(ks); tr.v.append(v); tr.attn.append(att)
-        tr.attn_branch.append(ab); tr.h.append(h); tr.act.append(a); tr.mlp_branch.append(mb)
+        lt = prefill_layer(cfg, lw, x, K[l], V[l], row)
+        _append(tr, x, lt)
+        x = lt.x_out
     tr.x_out = x
     if cfg.has_lm_head:
-        tr.logits = rms_norm(x[-1:], model.final_norm, cfg.rms_eps) @ model.lm_head.T
+        tr.logits = lm_head(cfg, x[-1:], model.final_norm, model.lm_head)
     return tr
 
 
@@ -293,7 +369,25 @@ def argmax_lowest(logits: np.ndarray) -> np.ndarray:
 
 
 def max_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
-    """max |got - ref| / max |ref| over the whole tensor."""
+    """max |got - ref| / max |ref| over the whole tensor (the absolute error when
+    the reference is all zero).  The infinity-norm form keeps near-zero entries
+    of a tensor from dominating the figure."""
+    got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
+    if got.shape != ref.shape:
+        raise ValueError(f"shapes differ: {got.shape} vs {ref.shape}")
+    if got.size == 0:
+        return 0.0
     den = float(np.max(np.abs(ref)))
-    return float(np.max(np.abs(np.asarray(got, dtype=np.float64) - ref))) / (den if den > 0 else 1.0)
+    return float(np.max(np.abs(got - ref))) / (den if den > 0 else 1.0)
+
+
+def max_rel_err_rows(got: np.ndarray, ref: np.ndarray) -> float:
+    """The largest max_rel_err over the rows of the leading axis (one row per
+    sequence, or per position): a small row is judged against its own scale,
+    not against the largest row of the batch."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if got.shape != ref.shape:
+        raise ValueError(f"shapes differ: {got.shape} vs {ref.shape}")
+    return max((max_rel_err(got[b], ref[b]) for b in range(ref.shape[0])), default=0.0)

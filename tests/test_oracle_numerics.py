@@ -304,3 +304,79 @@ def test_teacher_forced_decode_equals_causal_prefill(cfg):
 def test_argmax_lowest_index_wins_ties():
     a = np.array([[0.0, 3.0, 1.0, 3.0], [5.0, 5.0, 5.0, 5.0]])
     assert list(N.argmax_lowest(a)) == [1, 0]
+
+
+# ----------------------------------------------------------------------------- error metric (R13)
+
+def test_max_rel_err_hand_worked_values():
+    # |diff| = (0, 0, 1), max |ref| = 4
+    assert N.max_rel_err(np.array([1.0, 2.0, 3.0]), np.array([1.0, 2.0, 4.0])) == 0.25
+    # an error in the negative direction counts as much as a positive one
+    assert N.max_rel_err(np.array([0.5, 2.0]), np.array([1.0, 2.0])) == 0.25
+    assert N.max_rel_err(np.array([1.0, 2.0]), np.array([0.5, 2.0])) == 0.25
+    # the scale is the largest magnitude of the reference, negative entries included
+    assert N.max_rel_err(np.array([-3.0, 1.0]), np.array([-4.0, 1.0])) == 0.25
+    # the scale is the reference's, not the result's
+    assert N.max_rel_err(np.array([8.0, 0.0]), np.array([4.0, 0.0])) == 1.0
+    # an all-zero reference gives the absolute error
+    assert N.max_rel_err(np.array([0.0, -1e-3]), np.array([0.0, 0.0])) == 1e-3
+    # identical tensors, and empty ones
+    assert N.max_rel_err(np.array([[1.5, -2.0]]), np.array([[1.5, -2.0]])) == 0.0
+    assert N.max_rel_err(np.zeros((0, 3)), np.zeros((0, 3))) == 0.0
+    # a 2-D tensor is judged as a whole: max |diff| 0.5 over max |ref| 100
+    got = np.array([[100.0, 0.0], [1.5, 0.0]])
+    ref = np.array([[100.0, 0.0], [1.0, 0.0]])
+    assert N.max_rel_err(got, ref) == 0.005
+    with pytest.raises(ValueError):
+        N.max_rel_err(np.zeros(3), np.zeros(4))
+
+
+def test_max_rel_err_rows_judges_each_row_on_its_own_scale():
+    got = np.array([[100.0, 0.0], [1.5, 0.0]])
+    ref = np.array([[100.0, 0.0], [1.0, 0.0]])
+    # row 0 is exact, row 1 is off by 0.5 against a scale of 1
+    assert N.max_rel_err_rows(got, ref) == 0.5
+    # rows of a 3-D tensor: row 1 has |diff| 2 over max |ref| 8
+    ref3 = np.arange(16, dtype=np.float64).reshape(2, 2, 4) - 8.0
+    got3 = ref3.copy()
+    got3[1, 0, 0] -= 2.0
+    assert N.max_rel_err_rows(got3, ref3) == 2.0 / 7.0
+    got3[0, 1, 3] += 4.0
+    assert N.max_rel_err_rows(got3, ref3) == 0.5
+    assert N.max_rel_err_rows(np.zeros((0, 2)), np.zeros((0, 2))) == 0.0
+
+
+@pytest.mark.parametrize("nq,nkv,S,hd", [(4, 2, 9, 8), (8, 8, 5, 4), (6, 1, 17, 6)])
+def test_causal_attention_equals_one_position_at_a_time(nq, nkv, S, hd):
+    """The masked score-matrix form of prefill attention against the decode
+    attention of each position over its visible keys 0..i."""
+    g = rng(nq * S)
+    q = g.standard_normal((S, nq, hd))
+    K = g.standard_normal((nkv, S, hd))
+    V = g.standard_normal((nkv, S, hd))
+    got = N.causal_attention(q, K, V)
+    for i in range(S):
+        want = N.attention(q[i], K[:, : i + 1], V[:, : i + 1])
+        assert np.max(np.abs(got[i] - want)) < 1e-12
+    # position 0 sees only key 0: the output is its value
+    for h in range(nq):
+        assert np.allclose(got[0, h], V[h // (nq // nkv), 0], atol=1e-15)
+
+
+def test_float32_widening_runs_the_same_functions():
+    """The CPU baseline's float32 model: weights widened exactly (bf16 values are
+    fp32 values), and a step within fp32 rounding of the float64 oracle."""
+    cfg = ModelConfig("t", 2, 64, 4, 2, 16, 96, 50, 1e-5, 1e4)
+    run = RunConfig(batch=2, ctx0=(5, 9), steps=1, ctx_max=12, seed=3)
+    raw = gen.all_layer_weights(cfg, 3, gain_jitter=0.1)
+    glob = gen.global_weights(cfg, 3, gain_jitter=0.1)
+    m64 = N.prepare(cfg, raw, glob)
+    m32 = N.prepare(cfg, raw, glob, dtype=np.float32)
+    assert m32.layers[0].wqkv.dtype == np.float32
+    assert np.array_equal(m32.layers[1].wdown.astype(np.float64), m64.layers[1].wdown)
+    K, V = gen.kv_cache(cfg, run)
+    toks = gen.decode_tokens(cfg, run)[0]
+    t64 = N.decode_step(m64, K.copy(), V.copy(), run.ctx0, tokens=toks)
+    t32 = N.decode_step(m32, K.copy(), V.copy(), run.ctx0, tokens=toks)
+    assert t32.logits.dtype == np.float32
+    assert N.max_rel_err_rows(t32.logits, t64.logits) < 1e-5
