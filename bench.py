@@ -1,17 +1,20 @@
 """Decode benchmark of the tile-synchronized decoder on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama1b_b1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b_b1]
 
 A step is one teacher-forced decode step of the whole model for the workload's
 batch: embedding, every decoder layer (one megakernel launch), the LM head and
-the argmax.  The default workload is the Llama-3-1B-shaped bf16 model at batch
-1 decoding from a 1024-token cache.  Inputs (random-init weights, KV cache,
-token ids) are seeded and synthetic and are resident in HBM before timing.
+the argmax.  The default workload is the largest single-GPU one: the
+Llama-3-8B-shaped bf16 model at batch 1, decoding from a 4096-token cache.  The
+Llama-3-1B-shaped batch-1 workload runs after it and is reported under
+"extra".  Inputs (random-init weights, KV cache, token ids) are seeded and
+synthetic and are resident in HBM before timing.
 
 Prints one JSON line: the megakernel's tokens/s as `value`, the kernel-per-op
-modes (eager and HIP-graph replay) beside it, the dominant kernel's roofline
-(algorithmic bytes per launch over its event-timed average duration, against
-8 TB/s) and the float64 CPU oracle timed on a bounded sample on the host.
+modes (eager, and the library's HIP-graph mode) beside it, the dominant
+kernel's roofline (algorithmic bytes per launch over its event-timed average
+duration, against 8 TB/s) and the CPU oracle run on float32 weights, timed on a
+bounded sample on the host.
 """
 from __future__ import annotations
 
@@ -70,14 +73,29 @@ def lm_head_bytes(m, B) -> int:
     return m.vocab * m.hidden * wb + m.hidden * 4 + 4 * B * m.vocab if m.has_lm_head else 0
 
 
-def cpu_baseline(wl, raw_layers, raw_global, budget_s: float = 20.0) -> dict:
-    """The float64 oracle, step by step, on the host's cores (bounded sample)."""
+def cpu_model_name() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, raw_layers, raw_global, Kh, Vh, budget_s: float = 20.0) -> dict:
+    """The oracle's decode step run on float32 weights (numpy and its BLAS),
+    step by step, on the host's cores, over a bounded number of steps."""
+    from concurrent.futures import ThreadPoolExecutor
+    import numpy as np
     from oracle import numerics as N
     import workloads as W
     m, r = wl.model, wl.run
     t0 = time.time()
-    model = N.prepare(m, raw_layers, raw_global)
-    K, V = W.gen.kv_cache(m, r)
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        layers = list(ex.map(lambda raw: N.prepare_layer(raw, np.float32), raw_layers))
+    model = N.Model(m, layers, **{k: N.widen(v, np.float32) for k, v in raw_global.items()})
+    K, V = Kh.copy(), Vh.copy()
     tokens = W.gen.decode_tokens(m, r) if m.has_embed else None
     x0 = None if m.has_embed else W.gen.input_rows(m, r)
     prep = time.time() - t0
@@ -92,59 +110,32 @@ def cpu_baseline(wl, raw_layers, raw_global, budget_s: float = 20.0) -> dict:
         spent += time.time() - t1
         steps += 1
     cores = len(os.sched_getaffinity(0))
+    threads = os.environ.get("OMP_NUM_THREADS", str(cores))
     return {"value": round(r.batch * steps / spent, 4), "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{steps} teacher-forced decode steps of {wl.name} (batch {r.batch}), float64 numpy "
-                      f"on {cores} host threads; weights widened to float64 before timing ({prep:.0f} s)",
-            "ms_per_step": round(1e3 * spent / steps, 2)}
+            "sample": f"{steps} teacher-forced decode steps of {wl.name} (batch {r.batch}), the oracle's "
+                      f"decode step on float32 weights (numpy; BLAS threads {threads}) on {cores} host cores "
+                      f"of a {cpu_model_name()}; weights widened to float32 before timing ({prep:.0f} s)",
+            "cpu_model": cpu_model_name(), "ms_per_step": round(1e3 * spent / steps, 2)}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=128)
-    ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="llama1b_b1")
-    ap.add_argument("--workers-per-cu", type=int, default=1)
-    ap.add_argument("--queues", type=int, default=0, help="sub-queues (0: the workload's plan)")
-    ap.add_argument("--tiles", default="", help="override tile widths, e.g. tq=16,to=8,tf=16,td=8,kb=256")
-    ap.add_argument("--gemv-pipe", type=int, default=0,
-                    help="decode GEMV weight issue: 0 or 1 pipelined (default), 2 compiler-ordered")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=20.0)
-    ap.add_argument("--modes", default="mega,kpo,kpo_graph")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="before the modes, copy MIB MiB device to device three times: a plain copy "
-                         "kernel of known size that hardware byte counters can be scaled by")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
-        sys.exit(2)
-
-    import dataclasses
+def run_workload(wl, args, modes, with_prefill=True):
+    """Generate and upload one workload's inputs, then time its decode steps in
+    each mode (and its prefill when it has one).  Returns the results and the
+    host arrays the CPU baseline reuses."""
     import torch
     import tile_synchronized_decoder_amd as T
     from tile_synchronized_decoder_amd import device as D
     import workloads as W
 
-    wl = W.WORKLOADS[args.workload]
-    if args.queues:
-        wl = dataclasses.replace(wl, plan=dataclasses.replace(wl.plan, n_queues=args.queues))
-    if args.tiles:
-        kv = {k: int(v) for k, v in (p.split("=") for p in args.tiles.split(","))}
-        wl = dataclasses.replace(wl, plan=dataclasses.replace(wl.plan, **kv))
     m, r = wl.model, wl.run
     K_steps = min(args.steps, r.steps)
-    torch.cuda.set_device(0)
-    T.mk_set_option(T.MK_OPT_WORKERS_PER_CU, args.workers_per_cu)
-    T.mk_set_option(T.MK_OPT_GEMV_PIPE, args.gemv_pipe)
-
     t0 = time.time()
-    raw_layers = W.gen.all_layer_weights(m, r.seed)
+    raw_layers = W.gen.all_layer_weights(m, r.seed, threads=16)
     raw_global = W.gen.global_weights(m, r.seed)
-    Kh, Vh = W.gen.kv_cache(m, r)
+    Kh, Vh = W.gen.kv_cache(m, r, threads=16)
     tokens = W.gen.decode_tokens(m, r)
-    log(f"[bench] inputs generated in {time.time() - t0:.1f} s")
+    log(f"[bench] {wl.name}: inputs generated in {time.time() - t0:.1f} s")
     q = T.mk_build_queue(T.make_config(m), T.make_plan(wl.plan, T.MK_DECODE, r.batch, r.ctx_max))
     dq = D.upload_queue(q)
     dm = D.upload_weights(raw_layers, raw_global)
@@ -152,7 +143,7 @@ def main():
     ws = D.workspace(q)
     B = r.batch
     prefill_res = None
-    if r.prefill_len:
+    if r.prefill_len and with_prefill:
         # causal prefill of the prompt into the (empty) cache, timed per call in both modes;
         # the decode steps below continue from the cache the last call wrote
         S = r.prefill_len
@@ -208,16 +199,18 @@ def main():
             x0_buf.copy_(x0_all[t % r.steps])
         ctx_buf.copy_(ctx_all[t % r.steps])
 
-    def launch(mode, stream_=None):
-        T.mk_decode_step(q, dq, dm.w, dkv.kv, tok_buf if m.has_embed else None, x0_buf, ctx_buf, B, ws, None,
-                         None, mode, stream=stream_)
-
-    def step(t, mode, timing=None):
+    def step(t, mode, marks=None):
         set_inputs(t)
-        launch(mode)
-        if timing is not None:
-            timing.append(torch.cuda.Event(enable_timing=True))
-            timing[-1].record(stream)
+        if mode == T.MK_KERNEL_PER_OP_GRAPH:
+            # the library replays one HIP graph of the per-op launches and the LM head
+            T.mk_decode_step(q, dq, dm.w, dkv.kv, tok_buf if m.has_embed else None, x0_buf, ctx_buf, B, ws,
+                             logits if m.has_lm_head else None, nxt if m.has_lm_head else None, mode)
+            return
+        T.mk_decode_step(q, dq, dm.w, dkv.kv, tok_buf if m.has_embed else None, x0_buf, ctx_buf, B, ws, None,
+                         None, mode)
+        if marks is not None:
+            marks.append(torch.cuda.Event(enable_timing=True))
+            marks[-1].record(stream)
         if m.has_lm_head:
             T.mk_lm_head(q, dm.w, ws, logits, nxt)
 
@@ -230,30 +223,12 @@ def main():
         log(f"[bench] copy calibration: 3 x {args.copy_calibration} MiB")
         del src, dst
 
+    mode_of = {"mega": T.MK_MEGAKERNEL, "kpo": T.MK_KERNEL_PER_OP, "kpo_graph": T.MK_KERNEL_PER_OP_GRAPH}
     results = {}
-    modes = args.modes.split(",")
     for name in modes:
-        mode = T.MK_KERNEL_PER_OP if name.startswith("kpo") else T.MK_MEGAKERNEL
-        graph = None
-        if name == "kpo_graph":
-            step(0, mode)
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                launch(mode, torch.cuda.current_stream())
-                if m.has_lm_head:
-                    T.mk_lm_head(q, dm.w, ws, logits, nxt, stream=torch.cuda.current_stream())
-            torch.cuda.synchronize()
-
-        def run(t, marks=None):
-            if graph is None:
-                step(t, mode, marks)
-            else:
-                set_inputs(t)
-                graph.replay()
-
+        mode = mode_of[name]
         for t in range(args.warmup):
-            run(t)
+            step(t, mode)
         torch.cuda.synchronize()
         # timed region: K steps, events on the launch stream before each step and after
         # the decoder layers of each step (the megakernel / per-op launches end there)
@@ -264,7 +239,7 @@ def main():
         for t in range(K_steps):
             starts.append(torch.cuda.Event(enable_timing=True))
             starts[-1].record(stream)
-            run(t, mids if graph is None else None)
+            step(t, mode, mids)
         ev_end.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
@@ -281,47 +256,119 @@ def main():
         results[name] = res
         err = T.mk_device_error(q, ws)
         assert err.code == 0, f"device error {err.code} in mode {name}"
-        log(f"[bench] {name}: {res['ms_per_step']:.4f} ms/step, {res['tokens_per_s']:.1f} tok/s")
+        log(f"[bench] {wl.name} {name}: {res['ms_per_step']:.4f} ms/step, {res['tokens_per_s']:.1f} tok/s")
 
     mega = results.get("mega", next(iter(results.values())))
     ctx_mid = [p + K_steps // 2 for p in r.ctx0]
     mbytes = megakernel_bytes(m, ctx_mid)
     step_bytes = mbytes + lm_head_bytes(m, B)
-    roof = None
+    out = {"workload": wl, "steps": K_steps, "results": results, "prefill": prefill_res,
+           "instructions": q.nbytes(T.MK_PART_INSTR) // 32,
+           "step_hbm_gbs": step_bytes / (mega["ms_per_step"] * 1e-3) / 1e9}
     if "layers_ms" in mega:
         from tile_synchronized_decoder_amd.profiling import read_traffic
         ach = mbytes / (mega["layers_ms"] * 1e-3) / 1e9
         # HBM bytes per launch counted by FETCH_SIZE / WRITE_SIZE in a separate profiled run of
         # this workload (null when the kernel sources changed since)
         traffic = read_traffic(os.path.join(ROOT, "profiles", f"mk_interp_{wl.name}_traffic.md"))
-        roof = {"bound": "hbm", "kernel": "mk_interp (decoder layers, one launch per step)",
-                "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes_per_launch": mbytes}
+        out["roofline"] = {"bound": "hbm", "kernel": "mk_interp (decoder layers, one launch per step)",
+                           "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                           "algorithmic_bytes_per_launch": mbytes}
+    kpos = [v["ms_per_step"] for k, v in results.items() if k.startswith("kpo")]
+    if kpos and "mega" in results:
+        out["speedup"] = round(min(kpos) / mega["ms_per_step"], 4)
+    out["host"] = (raw_layers, raw_global, Kh, Vh)
+    del dm, dkv, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def _rounded(results):
+    return {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+            for k, v in results.items()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="llama8b_b1")
+    ap.add_argument("--extra", default="llama1b_b1",
+                    help="comma-separated workloads also timed and reported under 'extra' ('' for none)")
+    ap.add_argument("--workers-per-cu", type=int, default=1)
+    ap.add_argument("--queues", type=int, default=0, help="sub-queues (0: the workload's plan)")
+    ap.add_argument("--tiles", default="", help="override tile widths, e.g. tq=16,to=8,tf=16,td=8,kb=256")
+    ap.add_argument("--gemv-pipe", type=int, default=0,
+                    help="decode GEMV weight issue: 0 or 1 pipelined (default), 2 compiler-ordered")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--modes", default="mega,kpo,kpo_graph")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before the modes, copy MIB MiB device to device three times: a plain copy "
+                         "kernel of known size that hardware byte counters can be scaled by")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only (no collectives or sharding are built); "
+                                   "--gpus must be 1"}))
+        sys.exit(2)
+
+    import dataclasses
+    import torch
+    import tile_synchronized_decoder_amd as T
+    import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    if args.queues:
+        wl = dataclasses.replace(wl, plan=dataclasses.replace(wl.plan, n_queues=args.queues))
+    if args.tiles:
+        kv = {k: int(v) for k, v in (p.split("=") for p in args.tiles.split(","))}
+        wl = dataclasses.replace(wl, plan=dataclasses.replace(wl.plan, **kv))
+    m, r = wl.model, wl.run
+    torch.cuda.set_device(0)
+    T.mk_set_option(T.MK_OPT_WORKERS_PER_CU, args.workers_per_cu)
+    T.mk_set_option(T.MK_OPT_GEMV_PIPE, args.gemv_pipe)
+    modes = args.modes.split(",")
+
+    head = run_workload(wl, args, modes)
+    res = head["results"]
+    mega = res.get("mega", next(iter(res.values())))
+    B = r.batch
     line = {
         "metric": "decode tokens/s + step latency vs kernel-per-op; HBM GB/s as % of peak",
-        "value": round(mega["tokens_per_s"], 2), "unit": "tokens/s", "n_gpus": 1, "steps": K_steps,
+        "value": round(mega["tokens_per_s"], 2), "unit": "tokens/s", "n_gpus": 1, "steps": head["steps"],
         "warmup": args.warmup, "ms_per_step": round(mega["ms_per_step"], 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "storage": m.dtype, "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.describe}", "batch": B, "context": f"{r.ctx0[0]}+",
                    "layers": m.n_layers, "hidden": m.hidden, "vocab": m.vocab,
-                   "instructions_per_step": q.nbytes(T.MK_PART_INSTR) // 32,
+                   "instructions_per_step": head["instructions"],
                    "workers_per_cu": args.workers_per_cu, "n_queues": wl.plan.n_queues,
                    "tiles": {k: getattr(wl.plan, k) for k in ("tq", "to", "tf", "td", "kb")}},
-        "step_hbm_gbs": round(step_bytes / (mega["ms_per_step"] * 1e-3) / 1e9, 1),
-        "step_hbm_frac": round(step_bytes / (mega["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "modes": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                  for k, v in results.items()},
-        "roofline": roof,
+        "step_hbm_gbs": round(head["step_hbm_gbs"], 1),
+        "step_hbm_frac": round(head["step_hbm_gbs"] / HBM_PEAK_GBS, 4),
+        "modes": _rounded(res),
+        "roofline": head.get("roofline"),
     }
-    if prefill_res is not None:
-        line["prefill"] = prefill_res
-    if "kpo" in results or "kpo_graph" in results:
-        best = min(v["ms_per_step"] for k, v in results.items() if k.startswith("kpo"))
-        line["megakernel_speedup_vs_best_kpo"] = round(best / mega["ms_per_step"], 4)
+    if head["prefill"] is not None:
+        line["prefill"] = head["prefill"]
+    if "speedup" in head:
+        line["megakernel_speedup_vs_best_kpo"] = head["speedup"]
+    host = head.pop("host")
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
-        line["cpu_baseline"] = cpu_baseline(wl, raw_layers, raw_global, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(wl, *host, budget_s=args.cpu_budget)
+    del host, head
+    extra = {}
+    for name in [n for n in args.extra.split(",") if n and n != wl.name]:
+        ex = run_workload(W.WORKLOADS[name], args, modes, with_prefill=False)
+        ex.pop("host")
+        extra[name] = {"describe": ex["workload"].describe, "steps": ex["steps"],
+                       "modes": _rounded(ex["results"]), "roofline": ex.get("roofline"),
+                       "step_hbm_frac": round(ex["step_hbm_gbs"] / HBM_PEAK_GBS, 4),
+                       "megakernel_speedup_vs_best_kpo": ex.get("speedup")}
+    if extra:
+        line["extra"] = extra
     print(json.dumps(line), flush=True)
 
 

@@ -8,7 +8,8 @@
  * exactly the producer tiles it reads.  The LM head runs as a separate kernel.
  * The same op bodies also run one kernel per operator, for comparison.
  *
- * Sources of the method (the pages this library implements):
+ * Sources of the method (the pages this library implements; each entry point
+ * below names the passage it follows):
  *  - MegaOps abstract: dependencies enforced on individual tiles of the
  *    intermediate tensor a producer writes and a consumer reads, instead of
  *    whole-kernel barriers; weight prefetch while the producer still runs.
@@ -21,16 +22,27 @@
  *    kept out of the hot loop.
  *
  * Conventions for every entry point:
- *  - Returns MK_OK (0) or a negative mk_status.  On error nothing is launched
- *    and mk_last_error() holds a message (thread-local).
+ *  - Returns MK_OK (0) or a negative mk_status.  On error nothing is enqueued
+ *    (every check, including the kernels' shared-memory and residency limits,
+ *    runs before the first launch) and mk_last_error() holds a message
+ *    (thread-local).
  *  - Pointers named d_* and the fields of mk_weights / mk_kv are device
  *    pointers; everything else is host memory.
  *  - The caller owns and allocates all device memory (weights, KV cache,
  *    workspace, device queue copy, outputs).  The library allocates only the
- *    host mk_queue object and never calls hipMalloc or synchronises, except
- *    mk_device_error, which synchronises the given stream.
+ *    host mk_queue object (and, in MK_KERNEL_PER_OP_GRAPH mode, the HIP
+ *    runtime's graph objects) and never calls hipMalloc; it never
+ *    synchronises, except mk_device_error, which synchronises the given
+ *    stream, and the eviction of a cached graph (see MK_KERNEL_PER_OP_GRAPH).
  *  - Launches go to the caller's stream and return asynchronously.
- *  - Calls with distinct workspaces may run concurrently; calls that share a
+ *  - Host-side state (options, kernel attributes, the graph cache) is guarded
+ *    by one process-wide lock, so the entry points may be called from several
+ *    threads.  On the device: kernel-per-op calls (eager or graph) with
+ *    distinct workspaces may run concurrently on different streams.  A
+ *    megakernel call (decode or prefill) needs every one of its workgroups
+ *    resident at once, and two megakernels in flight on one device can hold
+ *    the compute units the other needs: megakernel calls must be serialised
+ *    per device (one stream, or ordered streams).  Calls that share a
  *    workspace race.
  *  - Matrices use the [out, in] row-major layout; all layers of one kind are
  *    stacked contiguously ([n_layers][out][in]).
@@ -58,7 +70,10 @@ enum {
 
 enum { MK_F32 = 0, MK_BF16 = 1 };                     /* element type of matrices and KV cache */
 enum { MK_DECODE = 0, MK_PREFILL = 1 };               /* queue mode */
-enum { MK_MEGAKERNEL = 0, MK_KERNEL_PER_OP = 1 };     /* execution mode */
+/* Execution modes: the persistent interpreter; the same op bodies one kernel
+ * per (layer, op) segment in stream order; and those per-op launches captured
+ * into a HIP graph and replayed (decode only). */
+enum { MK_MEGAKERNEL = 0, MK_KERNEL_PER_OP = 1, MK_KERNEL_PER_OP_GRAPH = 2 };
 enum { MK_PART_META = 0, MK_PART_INSTR = 1, MK_PART_WAITS = 2, MK_PART_TARGETS = 3,
        MK_PART_DEVICE = 4 };
 
@@ -94,6 +109,10 @@ typedef struct mk_plan {
 typedef struct mk_queue mk_queue;   /* opaque, host memory */
 
 /* Build the instruction queue and its tile barriers for (cfg, plan).
+ * Follows the lecture summary's Key takeaways (a single work queue built once
+ * with the sequence and context lengths symbolic; barriers are tensors
+ * partitioned by dependency) and the MegaOps abstract (each dependency is on
+ * the tiles of the intermediate tensor a consumer reads).
  * Host only, deterministic: equal inputs give byte-identical parts.
  * Layout of the parts (little-endian):
  *   META    u32 magic 'TMK1', version 1, mode, n_instr, n_barriers,
@@ -107,20 +126,28 @@ typedef struct mk_queue mk_queue;   /* opaque, host memory */
  *   TARGETS n_barriers x u32 (instructions that signal each barrier)
  *   DEVICE  INSTR | WAITS | TARGETS, each starting on a 256-byte boundary:
  *           what mk_decode_step / mk_prefill read from d_queue.
+ * Ownership: *out is a host object the caller releases with mk_queue_free.
  * Errors: MK_EINVAL for a bad shape or plan, MK_ENOMEM. */
 mk_status mk_build_queue(const mk_config* cfg, const mk_plan* plan, mk_queue** out);
+/* Bytes of one part (0 for an unknown part or a NULL queue). */
 size_t mk_queue_nbytes(const mk_queue* q, int32_t part);
+/* Copy one part into host_dst, which holds exactly mk_queue_nbytes(q, part)
+ * bytes (MK_EINVAL otherwise).  The caller uploads the DEVICE part into device
+ * memory it owns (the lecture summary's queue in DRAM). */
 mk_status mk_queue_export(const mk_queue* q, int32_t part, void* host_dst, size_t nbytes);
+/* Release a queue (NULL is ignored), with any HIP graphs captured for it. */
 void mk_queue_free(mk_queue* q);
 
 /* Device workspace: per-layer intermediate tensors, split partials, barrier
- * counters, queue heads, error record; for a prefill queue also the bf16
- * copies of the GEMM activation operands and per-row sums of squares that the
- * producer tiles write for their consumers.  No alignment beyond 256 bytes
- * needed.
+ * counters (the lecture summary's barriers as tensors; the MegaOps abstract's
+ * per-tile dependencies), queue heads, error record; for a prefill queue also
+ * the bf16 copies of the GEMM activation operands and per-row sums of squares
+ * that the producer tiles write for their consumers.  No alignment beyond 256
+ * bytes needed.
  * mk_workspace_offset gives the byte offset of one tensor (MK_T_*) of one
  * layer inside it (layer 0..n_layers for MK_T_X; 0 for the others that are not
- * per layer). Intermediates are fp32 row-major [rows][cols]. */
+ * per layer). Intermediates are fp32 row-major [rows][cols].
+ * Errors: MK_EINVAL (NULL arguments, unknown tensor, layer out of range). */
 enum { MK_T_X = 0, MK_T_QKV = 1, MK_T_OPART = 2, MK_T_ATT = 3, MK_T_HRES = 4, MK_T_ACT = 5,
        MK_T_COUNTERS = 6, MK_T_HEADS = 7, MK_T_ERROR = 8, MK_T_LMPART = 9 };
 mk_status mk_workspace_nbytes(const mk_queue* q, size_t* nbytes);
@@ -150,17 +177,33 @@ typedef struct mk_kv {
 } mk_kv;
 
 /* One decode step for `batch` sequences (must equal the queue's rows).
+ * Follows the lecture summary's Technical details (the persistent
+ * interpreter: every workgroup pops instructions from the queue in device
+ * memory, runs one tile each; memory pipelining across tiles) and the MegaOps
+ * abstract (a consumer tile starts once the producer tiles it reads are done,
+ * streaming its weights while it waits).
  * Row b's new token sits at position d_ctx_lens[b] (< ctx_max): its key and
  * value are written there and attention covers positions 0..d_ctx_lens[b].
- * The caller advances d_ctx_lens between steps.  Inputs: d_tokens [batch]
- * token ids (has_embed), else d_x0 [batch][H] fp32 rows.  Outputs: d_logits
- * [batch][V] fp32 and d_next [batch] (argmax, lowest index on ties); either may
- * be NULL to skip; both ignored without an LM head.  The final hidden rows are
- * the workspace tensor MK_T_X of layer n_layers.
+ * The caller advances d_ctx_lens between steps (the library keeps no state
+ * between steps).  Inputs: d_tokens [batch] token ids (has_embed), else d_x0
+ * [batch][H] fp32 rows.  Outputs: d_logits [batch][V] fp32 and d_next [batch]
+ * (argmax, lowest index on ties); either may be NULL to skip; both ignored
+ * without an LM head.  The final hidden rows are the workspace tensor MK_T_X
+ * of layer n_layers.
  * exec_mode MK_MEGAKERNEL: counter reset, one persistent interpreter launch,
- * LM head, argmax.  MK_KERNEL_PER_OP: the same op bodies, one launch per
- * (layer, op), stream-ordered, no tile waits.  Both give bitwise equal results.
- * Errors: MK_EINVAL (mismatched queue / sizes / null pointers), MK_ELAUNCH. */
+ * LM head, argmax.  MK_KERNEL_PER_OP: error-record reset, the same op bodies,
+ * one launch per (layer, op), stream-ordered, no tile waits (the whole-kernel
+ * barriers the MegaOps abstract measures against).  MK_KERNEL_PER_OP_GRAPH:
+ * the per-op launches of the first call with a given set of arguments
+ * (pointers, queue, options) are captured into a HIP graph that this and later
+ * calls with the same arguments replay; the kernels read tokens, context
+ * lengths and inputs from device memory, so a replay sees their current
+ * values.  At most 16 graphs are cached (least recently used evicted, after
+ * waiting for its last replay); mk_queue_free drops a queue's graphs.  All
+ * three modes give bitwise equal results.
+ * Errors: MK_EINVAL (mismatched queue / sizes / null pointers), MK_ENOTSUP
+ * (tiles that do not fit a workgroup's shared memory; megakernel workgroups
+ * that cannot all be resident), MK_ELAUNCH. */
 mk_status mk_decode_step(const mk_queue* q, const void* d_queue, const mk_weights* w,
                          const mk_kv* kv, const int32_t* d_tokens, const float* d_x0,
                          const int32_t* d_ctx_lens, int32_t batch, void* d_workspace,
@@ -171,29 +214,38 @@ mk_status mk_decode_step(const mk_queue* q, const void* d_queue, const mk_weight
  * of the workspace's last hidden rows (MK_T_X of layer n_layers, written by a
  * previous mk_decode_step on the same stream and workspace), the vocabulary
  * GEMV into d_logits [rows][V] fp32, and the argmax into d_next [rows] (lowest
- * index on ties); either output may be NULL.  The lecture summary's mixed
- * execution keeps this op outside the megakernel; calling it separately lets
- * a caller time the two parts.  Errors: MK_EINVAL (no LM head, sizes). */
+ * index on ties); either output may be NULL.  Follows the lecture summary's
+ * Practical implications: the LM head stays outside the megakernel (mixed
+ * execution); calling it separately lets a caller time the two parts.
+ * Errors: MK_EINVAL (no LM head, not a decode queue, sizes), MK_ELAUNCH. */
 mk_status mk_lm_head(const mk_queue* q, const mk_weights* w, void* d_workspace, size_t workspace_nbytes,
                      float* d_logits, int32_t* d_next, hipStream_t stream);
 
 /* Causal prefill of seq_len (1 .. the queue's rows) tokens of one sequence into
- * cache row kv_row (< kv->rows), positions 0..seq_len-1.  Row blocks at or past
- * seq_len are no-ops (the queue is built once for S_max).  d_logits_last [V]
- * and d_next [1] receive the last position's logits and argmax.  The GEMM
- * tiles run on the matrix cores with bf16 operands (each producer tile also
- * writes its output rounded to bf16, times the consuming RMSNorm's gain where
- * there is one) and fp32 accumulation.  Requires a bf16 model with an
- * embedding, hidden size a multiple of 128, the FFN and attention widths
- * multiples of 64, head_dim 128 and 128 x 128 tiles (MK_ENOTSUP otherwise).
- * The per-layer hidden rows are the workspace tensors, [S_max][...] fp32. */
+ * cache row kv_row (< kv->rows), positions 0..seq_len-1.  Follows the lecture
+ * summary's Key takeaways (the queue is built once for S_max with the sequence
+ * length symbolic: row blocks at or past seq_len are no-ops that still signal)
+ * and Technical details (the same interpreter over the prefill queue; an
+ * attention tile of row block m waits only on the key / value tiles of row
+ * blocks <= m).  d_logits_last [V] and d_next [1] receive the last position's
+ * logits and argmax (the LM head as a separate kernel, Practical
+ * implications).  The GEMM tiles run on the matrix cores with bf16 operands
+ * (each producer tile also writes its output rounded to bf16, times the
+ * consuming RMSNorm's gain where there is one) and fp32 accumulation.
+ * Requires a bf16 model with an embedding, hidden size a multiple of 128, the
+ * FFN and attention widths multiples of 64, head_dim 128 and 128 x 128 tiles
+ * (MK_ENOTSUP otherwise).  exec_mode: MK_MEGAKERNEL or MK_KERNEL_PER_OP.  The
+ * per-layer hidden rows are the workspace tensors, [S_max][...] fp32.
+ * Errors: MK_EINVAL, MK_ENOTSUP, MK_ELAUNCH. */
 mk_status mk_prefill(const mk_queue* q, const void* d_queue, const mk_weights* w,
                      const mk_kv* kv, const int32_t* d_tokens, int32_t seq_len, int32_t kv_row,
                      void* d_workspace, size_t workspace_nbytes, float* d_logits_last,
                      int32_t* d_next, int32_t exec_mode, hipStream_t stream);
 
 /* Device-side error record, written by a worker whose bounded wait on a
- * barrier expired (the kernel then drains instead of hanging). */
+ * barrier expired (the kernel then drains instead of hanging), or by an op
+ * that met an input outside its range.  Not from the pages: the library's own
+ * watchdog.  Every call clears it before its first kernel runs. */
 typedef struct mk_dev_error {
   uint32_t code;       /* 0 none; 1 barrier wait timed out; 2 unknown opcode;
                           3 context length outside the cache; 4 token id outside the vocabulary */
@@ -202,11 +254,12 @@ typedef struct mk_dev_error {
   uint32_t value;      /* counter value seen */
   uint32_t target;     /* target it waited for */
 } mk_dev_error;
-/* Synchronises `stream`, then copies the record out. */
+/* Synchronises `stream`, then copies the record out.  Returns MK_EDEVICE when
+ * the record holds an error, MK_OK otherwise. */
 mk_status mk_device_error(const mk_queue* q, const void* d_workspace, mk_dev_error* out,
                           hipStream_t stream);
 
-/* Tuning knobs (process-wide): */
+/* Tuning knobs (process-wide; not from the pages): */
 enum {
   MK_OPT_WORKERS_PER_CU = 0,  /* megakernel workgroups per compute unit (default 1); a
                                * launch whose workgroups the registers or shared memory
@@ -226,11 +279,20 @@ enum {
    * ring's lines in flight while staged inputs are read, 2 lets the compiler
    * order them (it waits for every line in flight before each read of the
    * staged inputs).  Results are identical. */
-  MK_OPT_GEMV_PIPE = 5
+  MK_OPT_GEMV_PIPE = 5,
+  /* Race check: a non-zero 32-bit seed makes every tile's producer stall for a
+   * pseudo-random time drawn from (seed, instruction index), 0 to about 50 us,
+   * before it stores the tile.  A consumer that read a tile without waiting
+   * for its barrier would then read the workspace's previous contents.
+   * Results are identical to a run without it; 0 (default) turns it off. */
+  MK_OPT_DELAY_SEED = 6
 };
+/* Errors: MK_EINVAL for an unknown or read-only key or a value out of range. */
 mk_status mk_set_option(int32_t key, int64_t value);
+/* The option's value, or -1 for an unknown key. */
 int64_t mk_get_option(int32_t key);
 
+/* Static name of a status, and the calling thread's last error message. */
 const char* mk_status_str(mk_status s);
 const char* mk_last_error(void);
 

@@ -146,7 +146,8 @@ def test_options_validate_and_round_trip():
     (status, no change), valid ones read back."""
     for key, good, bad in ((T.MK_OPT_GEMV_PIPE, (0, 1, 2), (-1, 3)),
                            (T.MK_OPT_WORKERS_PER_CU, (1, 2), (0, 9)),
-                           (T.MK_OPT_SPIN_LIMIT, (1, 1 << 20), (0,))):
+                           (T.MK_OPT_SPIN_LIMIT, (1, 1 << 20), (0,)),
+                           (T.MK_OPT_DELAY_SEED, (0, 7, 0xFFFFFFFF), (-1, 1 << 32))):
         old = T.mk_get_option(key)
         try:
             for v in good:
@@ -158,3 +159,25 @@ def test_options_validate_and_round_trip():
                 assert T.mk_get_option(key) == good[-1]
         finally:
             T.mk_set_option(key, old)
+
+
+def test_decode_refuses_unknown_exec_mode_and_graph_prefill():
+    """Argument checks run before anything touches a device: an unknown
+    execution mode is refused, and prefill has no graph mode."""
+    import ctypes as C
+    wl = W.WORKLOADS["layer256_f32"]
+    q = T.mk_build_queue(T.make_config(wl.model), T.make_plan(wl.plan, T.MK_DECODE, 1, 129))
+    w, kv = L.mk_weights(), L.mk_kv()
+    fake = C.c_void_p(0x1000)
+    st = L.lib().mk_decode_step(q.handle, fake, C.byref(w), C.byref(kv), None, fake, fake, 1, fake,
+                                1 << 30, None, None, 7, None)
+    assert st == T.MK_EINVAL
+    assert b"null" in L.lib().mk_last_error() or b"exec_mode" in L.lib().mk_last_error()
+
+
+def test_queue_free_accepts_null_and_frees_once():
+    L.lib().mk_queue_free(None)
+    wl = W.WORKLOADS["layer256_f32"]
+    q = T.mk_build_queue(T.make_config(wl.model), T.make_plan(wl.plan, T.MK_DECODE, 1, 129))
+    q.close()
+    q.close()

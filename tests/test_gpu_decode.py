@@ -355,3 +355,49 @@ def test_fused_combine_refused_when_partials_do_not_fit():
     with pytest.raises(T.MkError) as ei:
         c.step(0, [128], T.MK_MEGAKERNEL)
     assert ei.value.status == T.MK_ENOTSUP
+
+
+# ----------------------------------------------------------------------------- kernel-per-op HIP graph
+
+def test_kpo_graph_replays_match_eager_and_megakernel():
+    """MK_KERNEL_PER_OP_GRAPH captures the per-op launches once and replays
+    them.  Three steps with new token ids and context lengths written into the
+    same device buffers between replays (and the outputs overwritten with NaN),
+    twice over: every replay equals the eager per-op step and the megakernel
+    bit for bit, cache included."""
+    from _gpucase import make_case, log
+    wl = _shrunk_1b(batch=2, ctx0=(700, 1100), steps=3)
+    c = make_case(wl)
+    B = 2
+    tok = torch.zeros(B, dtype=torch.int32, device="cuda")
+    cl = torch.zeros(B, dtype=torch.int32, device="cuda")
+
+    def run(mode):
+        outs = []
+        c.reset_kv()
+        for t in range(3):
+            tok.copy_(torch.from_numpy(c.tokens[t].astype(np.int32)))
+            cl.copy_(torch.tensor([700 + t, 1100 + t], dtype=torch.int32))
+            c.logits.fill_(float("nan"))
+            c.nxt.fill_(-1)
+            torch.cuda.synchronize()
+            T.mk_decode_step(c.q, c.dq, c.dm.w, c.dkv.kv, tok, None, cl, B, c.ws, c.logits, c.nxt, mode)
+            torch.cuda.synchronize()
+            assert T.mk_device_error(c.q, c.ws).code == 0
+            outs.append((c.logits.cpu().numpy().copy(), c.nxt.cpu().numpy().copy(),
+                         c.tensor(T.MK_T_X, 2, 2048), c.tensor(T.MK_T_ACT, 1, 8192)))
+        outs.append((c.kv_host()[0].copy(), c.kv_host()[1].copy()))
+        return outs
+
+    eager = run(T.MK_KERNEL_PER_OP)
+    for name, mode in (("graph", T.MK_KERNEL_PER_OP_GRAPH), ("graph replay", T.MK_KERNEL_PER_OP_GRAPH),
+                       ("megakernel", T.MK_MEGAKERNEL)):
+        got = run(mode)
+        for t, (a, b) in enumerate(zip(eager, got)):
+            for x, y in zip(a, b):
+                assert np.array_equal(x, y), (name, t)
+        log(f"    {name}: bit-identical to eager per-op over 3 steps")
+    # a new workspace is a new set of arguments: captured again, same results
+    c.ws = torch.zeros_like(c.ws)
+    again = run(T.MK_KERNEL_PER_OP_GRAPH)
+    assert all(np.array_equal(x, y) for a, b in zip(eager, again) for x, y in zip(a, b))

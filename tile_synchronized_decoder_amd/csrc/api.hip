@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <mutex>
+#include <vector>
 
 #include "kernels.h"
 #include "mk.h"
@@ -74,8 +75,15 @@ struct Options {
   unsigned long long* trace = nullptr;   // device buffer, 64 bytes per instruction
   size_t trace_bytes = 0;
   int gemv_pipe = 0;                     // 0, 1: pipelined issue; 2: compiler-ordered issue
+  uint32_t delay_seed = 0;               // race check: seeded stalls before tile stores
 };
 Options g_opt;
+
+// One process-wide lock over the library's host state: the options, the
+// kernels' shared-memory opt-ins and the graph cache.  Every entry point that
+// reads or writes them holds it; launches are asynchronous, so it is held only
+// while a call enqueues its work.
+std::mutex g_mu;
 
 int num_cus() {
   static int n = 0;
@@ -284,7 +292,197 @@ mk_status check_shapes(const mk_config& c) {
   return MK_OK;
 }
 
+// A refusal from the preparation step, as a status.
+mk_status prep_status(hipError_t e) {
+  if (e == hipSuccess) return MK_OK;
+  if (e == hipErrorCooperativeLaunchTooLarge)
+    FAIL(MK_ENOTSUP, "%d megakernel workgroups per compute unit do not fit its registers / shared memory",
+         g_opt.workers_per_cu);
+  FAIL(MK_ELAUNCH, "kernel set-up failed: %s", hipGetErrorString(e));
+}
+
+// The launches of one decode step on `stream`, after every check passed:
+// input rows, then (megakernel) the counter / head / error reset and one
+// interpreter launch, or (per op) the error reset and one launch per segment;
+// then the LM head and argmax.
+hipError_t enqueue_decode(const mk_queue* q, const Args& a, const Table& t, int exec_mode, bool want_lm,
+                          bool want_next, hipStream_t stream) {
+  if (!q->cfg.has_embed) {
+    // without an embedding the input rows are copied into X_0 by the first launch
+    const size_t n = (size_t)a.M * a.H;
+    hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)std::min<size_t>((n + 255) / 256, 1024)), dim3(256), 0,
+                       stream, a.X, a.x0, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const bool mega = exec_mode == MK_MEGAKERNEL;
+  const uint32_t nr = mega ? a.n_barriers : 0, nh = mega ? a.n_queues : 0;
+  hipLaunchKernelGGL(reset_kernel, dim3((nr + 255) / 256 + 1), dim3(256), 0, stream, a.counters, nr, a.heads, nh,
+                     a.err);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (mega) {
+    e = t.mega(a, num_cus() * g_opt.workers_per_cu, stream);
+  } else {
+    for (const mk::Segment& sg : q->segments) {
+      e = t.kpo(a, sg.op, sg.first, sg.count, stream);
+      if (e != hipSuccess) break;
+    }
+  }
+  if (e == hipSuccess && want_lm) e = launch_lm(t, a, want_next, stream);
+  return e;
+}
+
+// ----------------------------------------------------------------------------- kernel-per-op HIP graphs
+
+// MK_KERNEL_PER_OP_GRAPH: the per-op launches of a step are captured once per
+// distinct set of call arguments (every pointer, the queue, the options the
+// kernels read) into an instantiated HIP graph, which later calls with the same
+// arguments replay on the caller's stream.  The kernels read token ids,
+// context lengths and inputs from device memory at run time, so a replay sees
+// their current values.  At most kMaxGraphs graphs are kept; evicting one (or
+// freeing its queue) first waits for its last replay to finish.
+constexpr size_t kMaxGraphs = 16;
+struct GraphEntry {
+  std::vector<uint64_t> key;
+  hipGraphExec_t exec = nullptr;
+  hipEvent_t done = nullptr;       // recorded after each replay
+  uint64_t last_use = 0;
+};
+std::vector<GraphEntry> g_graphs;
+uint64_t g_graph_clock = 0;
+hipStream_t g_capture_stream[kMaxDevices] = {};
+
+void drop_graph(GraphEntry& g) {
+  if (g.done) { hipEventSynchronize(g.done); hipEventDestroy(g.done); }
+  if (g.exec) hipGraphExecDestroy(g.exec);
+  g.exec = nullptr; g.done = nullptr;
+}
+
+template <typename T> uint64_t u64(T v) { return (uint64_t)(uintptr_t)v; }
+
+std::vector<uint64_t> graph_key(const mk_queue* q, int dev, const void* d_queue, const mk_weights* w, const mk_kv* kv,
+                                const int32_t* tok, const float* x0, const int32_t* ctx, const void* ws,
+                                size_t ws_bytes, const float* logits, const int32_t* next, const Args& a) {
+  return {q->serial, (uint64_t)dev, u64(d_queue), u64(w->wqkv), u64(w->wo), u64(w->wgate), u64(w->wup),
+          u64(w->wdown), u64(w->attn_norm), u64(w->ffn_norm), u64(w->q_norm), u64(w->k_norm), u64(w->embed),
+          u64(w->lm_head), u64(w->final_norm), u64(kv->k), u64(kv->v), (uint64_t)kv->rows, u64(tok), u64(x0),
+          u64(ctx), u64(ws), (uint64_t)ws_bytes, u64(logits), u64(next), (uint64_t)a.gemv_pipe, u64(a.trace),
+          (uint64_t)a.spin_limit, (uint64_t)a.delay_seed};
+}
+
+mk_status graph_step(const mk_queue* q, const Args& a, const Table& t, std::vector<uint64_t> key, bool want_lm,
+                     bool want_next, hipStream_t stream) {
+  GraphEntry* hit = nullptr;
+  for (GraphEntry& g : g_graphs)
+    if (g.key == key) { hit = &g; break; }
+  if (!hit) {
+    const int dev = (int)key[1];
+    if (!g_capture_stream[dev]) {
+      hipError_t e = hipStreamCreateWithFlags(&g_capture_stream[dev], hipStreamNonBlocking);
+      if (e != hipSuccess) FAIL(MK_ELAUNCH, "capture stream: %s", hipGetErrorString(e));
+    }
+    hipStream_t cs = g_capture_stream[dev];
+    hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) FAIL(MK_ELAUNCH, "begin capture: %s", hipGetErrorString(e));
+    const hipError_t el = enqueue_decode(q, a, t, MK_KERNEL_PER_OP, want_lm, want_next, cs);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(cs, &graph);
+    if (el != hipSuccess || e != hipSuccess) {
+      if (graph) hipGraphDestroy(graph);
+      FAIL(MK_ELAUNCH, "capture of the per-op launches: %s", hipGetErrorString(el != hipSuccess ? el : e));
+    }
+    GraphEntry ne;
+    ne.key = std::move(key);
+    e = hipGraphInstantiate(&ne.exec, graph, nullptr, nullptr, 0);
+    hipGraphDestroy(graph);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ne.done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      drop_graph(ne);
+      FAIL(MK_ELAUNCH, "graph instantiation: %s", hipGetErrorString(e));
+    }
+    if (g_graphs.size() >= kMaxGraphs) {
+      auto lru = std::min_element(g_graphs.begin(), g_graphs.end(),
+                                  [](const GraphEntry& x, const GraphEntry& y) { return x.last_use < y.last_use; });
+      drop_graph(*lru);
+      g_graphs.erase(lru);
+    }
+    g_graphs.push_back(std::move(ne));
+    hit = &g_graphs.back();
+  }
+  hit->last_use = ++g_graph_clock;
+  hipError_t e = hipGraphLaunch(hit->exec, stream);
+  if (e == hipSuccess) e = hipEventRecord(hit->done, stream);
+  if (e != hipSuccess) FAIL(MK_ELAUNCH, "graph launch: %s", hipGetErrorString(e));
+  return MK_OK;
+}
+
+// The common body of a decode step into a given workspace.
+mk_status decode_impl(const mk_queue* q, const void* d_queue, const mk_weights* w, const mk_kv* kv,
+                      const int32_t* d_tokens, const float* d_x0, const int32_t* d_ctx_lens, int32_t batch,
+                      void* d_workspace, size_t workspace_nbytes, float* d_logits, int32_t* d_next,
+                      int32_t exec_mode, hipStream_t stream) {
+  if (!q || !d_queue || !w || !kv || !d_ctx_lens || !d_workspace) FAIL(MK_EINVAL, "null argument");
+  if (q->plan.mode != MK_DECODE) FAIL(MK_EINVAL, "queue was not built for decode");
+  const mk_config& c = q->cfg;
+  if (mk_status st = check_shapes(c)) return st;
+  if (batch != q->plan.rows) FAIL(MK_EINVAL, "batch %d differs from the queue's rows %d", batch, q->plan.rows);
+  if (exec_mode != MK_MEGAKERNEL && exec_mode != MK_KERNEL_PER_OP && exec_mode != MK_KERNEL_PER_OP_GRAPH)
+    FAIL(MK_EINVAL, "unknown exec_mode");
+  if (lds_layout(q).bytes > kMaxLds) FAIL(MK_ENOTSUP, "tiles need more shared memory than a workgroup has");
+  const Layout o = layout(q);
+  if (workspace_nbytes < o.total) FAIL(MK_EINVAL, "workspace of %zu bytes, need %zu", workspace_nbytes, o.total);
+  if (c.has_embed ? (!d_tokens || !w->embed) : !d_x0) FAIL(MK_EINVAL, "missing input tokens / rows");
+  if (!w->wqkv || !w->wo || !w->wgate || !w->wup || !w->wdown || !w->attn_norm || !w->ffn_norm || !kv->k || !kv->v)
+    FAIL(MK_EINVAL, "missing weights or cache");
+  if (c.qk_norm && (!w->q_norm || !w->k_norm)) FAIL(MK_EINVAL, "missing QK-norm gains");
+  if (c.has_lm_head && (d_logits || d_next) && (!w->lm_head || !w->final_norm)) FAIL(MK_EINVAL, "missing LM head");
+  if (kv->rows != 0 && kv->rows != q->plan.rows) FAIL(MK_EINVAL, "decode cache rows must equal the batch");
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) FAIL(MK_ELAUNCH, "no current device");
+  if (exec_mode == MK_MEGAKERNEL && num_cus() * g_opt.workers_per_cu < q->plan.n_queues)
+    FAIL(MK_EINVAL, "fewer workers than sub-queues");
+
+  Args a{};
+  fill_args(q, d_queue, w, kv, d_workspace, o, a);
+  a.tokens = d_tokens; a.x0 = d_x0; a.ctx_lens = d_ctx_lens;
+  a.logits = d_logits; a.next = d_next;
+  a.spin_limit = g_opt.spin_limit;
+  a.gemv_pipe = g_opt.gemv_pipe;
+  a.delay_seed = g_opt.delay_seed;
+  a.trace = (g_opt.trace && g_opt.trace_bytes >= 64 * q->instr.size()) ? g_opt.trace : nullptr;
+
+  const Table t = pick_table(c.dtype, a.M);
+  const bool want_lm = c.has_lm_head && (d_logits || d_next);
+  hipError_t e = t.prep(a, exec_mode == MK_MEGAKERNEL ? MK_MEGAKERNEL : MK_KERNEL_PER_OP, g_opt.workers_per_cu);
+  if (e == hipSuccess && want_lm) e = t.prep_lm(a);
+  if (mk_status st = prep_status(e)) return st;
+  if (exec_mode == MK_KERNEL_PER_OP_GRAPH)
+    return graph_step(q, a, t,
+                      graph_key(q, dev, d_queue, w, kv, d_tokens, d_x0, d_ctx_lens, d_workspace, workspace_nbytes,
+                                d_logits, d_next, a),
+                      want_lm, d_next != nullptr, stream);
+  e = enqueue_decode(q, a, t, exec_mode, want_lm, d_next != nullptr, stream);
+  if (e != hipSuccess) FAIL(MK_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return MK_OK;
+}
+
 }  // namespace
+
+namespace mk {
+// Called by mk_queue_free: the graphs captured for a queue die with it.
+void forget_graphs(uint64_t serial) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  for (size_t i = 0; i < g_graphs.size();) {
+    if (g_graphs[i].key[0] == serial) {
+      drop_graph(g_graphs[i]);
+      g_graphs.erase(g_graphs.begin() + i);
+    } else {
+      ++i;
+    }
+  }
+}
+}  // namespace mk
 
 extern "C" {
 
@@ -320,69 +518,20 @@ mk_status mk_decode_step(const mk_queue* q, const void* d_queue, const mk_weight
                          const int32_t* d_tokens, const float* d_x0, const int32_t* d_ctx_lens,
                          int32_t batch, void* d_workspace, size_t workspace_nbytes, float* d_logits,
                          int32_t* d_next, int32_t exec_mode, hipStream_t stream) {
-  if (!q || !d_queue || !w || !kv || !d_ctx_lens || !d_workspace) FAIL(MK_EINVAL, "null argument");
-  if (q->plan.mode != MK_DECODE) FAIL(MK_EINVAL, "queue was not built for decode");
-  const mk_config& c = q->cfg;
-  if (mk_status st = check_shapes(c)) return st;
-  if (batch != q->plan.rows) FAIL(MK_EINVAL, "batch %d differs from the queue's rows %d", batch, q->plan.rows);
-  if (exec_mode != MK_MEGAKERNEL && exec_mode != MK_KERNEL_PER_OP) FAIL(MK_EINVAL, "unknown exec_mode");
-  if (lds_layout(q).bytes > kMaxLds) FAIL(MK_ENOTSUP, "tiles need more shared memory than a workgroup has");
-  const Layout o = layout(q);
-  if (workspace_nbytes < o.total) FAIL(MK_EINVAL, "workspace of %zu bytes, need %zu", workspace_nbytes, o.total);
-  if (c.has_embed ? (!d_tokens || !w->embed) : !d_x0) FAIL(MK_EINVAL, "missing input tokens / rows");
-  if (!w->wqkv || !w->wo || !w->wgate || !w->wup || !w->wdown || !w->attn_norm || !w->ffn_norm || !kv->k || !kv->v)
-    FAIL(MK_EINVAL, "missing weights or cache");
-  if (c.qk_norm && (!w->q_norm || !w->k_norm)) FAIL(MK_EINVAL, "missing QK-norm gains");
-  if (c.has_lm_head && (d_logits || d_next) && (!w->lm_head || !w->final_norm)) FAIL(MK_EINVAL, "missing LM head");
-  if (kv->rows != 0 && kv->rows != q->plan.rows) FAIL(MK_EINVAL, "decode cache rows must equal the batch");
-
-  Args a{};
-  fill_args(q, d_queue, w, kv, d_workspace, o, a);
-  a.tokens = d_tokens; a.x0 = d_x0; a.ctx_lens = d_ctx_lens;
-  a.logits = d_logits; a.next = d_next;
-  a.spin_limit = g_opt.spin_limit;
-  a.gemv_pipe = g_opt.gemv_pipe;
-  a.trace = (g_opt.trace && g_opt.trace_bytes >= 64 * q->instr.size()) ? g_opt.trace : nullptr;
-
-  // without an embedding the input rows are copied into X_0 by the first launch
-  if (!c.has_embed) {
-    const size_t n = (size_t)a.M * a.H;
-    hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)std::min<size_t>((n + 255) / 256, 1024)), dim3(256), 0, stream,
-                       a.X, d_x0, n);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) FAIL(MK_ELAUNCH, "copy of input rows: %s", hipGetErrorString(e));
-  }
-  const Table t = pick_table(c.dtype, a.M);
-  hipError_t e = hipSuccess;
-  if (exec_mode == MK_MEGAKERNEL) {
-    const int grid = num_cus() * g_opt.workers_per_cu;
-    if (grid < (int)a.n_queues) FAIL(MK_EINVAL, "fewer workers than sub-queues");
-    const uint32_t nr = a.n_barriers;
-    hipLaunchKernelGGL(reset_kernel, dim3((nr + 255) / 256 + 1), dim3(256), 0, stream, a.counters, nr, a.heads,
-                       a.n_queues, a.err);
-    e = hipGetLastError();
-    if (e == hipSuccess) e = t.mega(a, grid, g_opt.workers_per_cu, stream);
-  } else {
-    for (const mk::Segment& sg : q->segments) {
-      e = t.kpo(a, sg.op, sg.first, sg.count, stream);
-      if (e != hipSuccess) break;
-    }
-  }
-  if (e == hipSuccess && c.has_lm_head && (d_logits || d_next)) e = launch_lm(t, a, d_next != nullptr, stream);
-  if (e == hipErrorCooperativeLaunchTooLarge)
-    FAIL(MK_ENOTSUP, "%d megakernel workgroups per compute unit do not fit its registers / shared memory",
-         g_opt.workers_per_cu);
-  if (e != hipSuccess) FAIL(MK_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
-  return MK_OK;
+  std::lock_guard<std::mutex> lk(g_mu);
+  return decode_impl(q, d_queue, w, kv, d_tokens, d_x0, d_ctx_lens, batch, d_workspace, workspace_nbytes, d_logits,
+                     d_next, exec_mode, stream);
 }
 
 mk_status mk_lm_head(const mk_queue* q, const mk_weights* w, void* d_workspace, size_t workspace_nbytes,
                      float* d_logits, int32_t* d_next, hipStream_t stream) {
+  std::lock_guard<std::mutex> lk(g_mu);
   if (!q || !w || !d_workspace) FAIL(MK_EINVAL, "null argument");
   const mk_config& c = q->cfg;
   if (!c.has_lm_head) FAIL(MK_EINVAL, "the model has no LM head");
   if (!w->lm_head || !w->final_norm) FAIL(MK_EINVAL, "missing LM head");
   if (!d_logits && !d_next) return MK_OK;
+  if (q->plan.mode != MK_DECODE) FAIL(MK_EINVAL, "queue was not built for decode");
   const Layout o = layout(q);
   if (workspace_nbytes < o.total) FAIL(MK_EINVAL, "workspace of %zu bytes, need %zu", workspace_nbytes, o.total);
   Args a{};
@@ -398,7 +547,9 @@ mk_status mk_lm_head(const mk_queue* q, const mk_weights* w, void* d_workspace, 
   const LdsLayout ll = lds_layout(q);
   a.lds_res = ll.res; a.lds_x = ll.x; a.lds_union = ll.uni; a.lds_bytes = ll.bytes; a.lds_ring = ll.ring;
   a.logits = d_logits; a.next = d_next;
-  const hipError_t e = launch_lm(pick_table(c.dtype, a.M), a, d_next != nullptr, stream);
+  const Table t = pick_table(c.dtype, a.M);
+  if (mk_status st = prep_status(t.prep_lm(a))) return st;
+  const hipError_t e = launch_lm(t, a, d_next != nullptr, stream);
   if (e != hipSuccess) FAIL(MK_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
   return MK_OK;
 }
@@ -407,6 +558,7 @@ mk_status mk_prefill(const mk_queue* q, const void* d_queue, const mk_weights* w
                      const int32_t* d_tokens, int32_t seq_len, int32_t kv_row, void* d_workspace,
                      size_t workspace_nbytes, float* d_logits_last, int32_t* d_next, int32_t exec_mode,
                      hipStream_t stream) {
+  std::lock_guard<std::mutex> lk(g_mu);
   if (!q || !d_queue || !w || !kv || !d_tokens || !d_workspace) FAIL(MK_EINVAL, "null argument");
   if (q->plan.mode != MK_PREFILL) FAIL(MK_EINVAL, "queue was not built for prefill");
   const mk_config& c = q->cfg;
@@ -427,44 +579,50 @@ mk_status mk_prefill(const mk_queue* q, const void* d_queue, const mk_weights* w
     FAIL(MK_EINVAL, "missing weights or cache");
   if (c.qk_norm && (!w->q_norm || !w->k_norm)) FAIL(MK_EINVAL, "missing QK-norm gains");
   if ((d_logits_last || d_next) && (!c.has_lm_head || !w->lm_head || !w->final_norm)) FAIL(MK_EINVAL, "missing LM head");
+  if (exec_mode == MK_MEGAKERNEL && num_cus() * g_opt.workers_per_cu < q->plan.n_queues)
+    FAIL(MK_EINVAL, "fewer workers than sub-queues");
 
   Args a{};
   fill_args(q, d_queue, w, kv, d_workspace, o, a);
   a.tokens = d_tokens; a.seq_len = seq_len; a.kv_row = kv_row; a.M_cache = kv->rows;
   a.spin_limit = g_opt.spin_limit;
   a.gemv_pipe = g_opt.gemv_pipe;
+  a.delay_seed = g_opt.delay_seed;
   a.trace = (g_opt.trace && g_opt.trace_bytes >= 64 * q->instr.size()) ? g_opt.trace : nullptr;
-  const Table t = table_prefill();
-  hipError_t e = hipSuccess;
-  if (exec_mode == MK_MEGAKERNEL) {
-    const int grid = num_cus() * g_opt.workers_per_cu;
-    if (grid < (int)a.n_queues) FAIL(MK_EINVAL, "fewer workers than sub-queues");
-    const uint32_t nr = a.n_barriers;
-    hipLaunchKernelGGL(reset_kernel, dim3((nr + 255) / 256 + 1), dim3(256), 0, stream, a.counters, nr, a.heads,
-                       a.n_queues, a.err);
-    e = hipGetLastError();
-    if (e == hipSuccess) e = t.mega(a, grid, g_opt.workers_per_cu, stream);
-  } else {
-    for (const mk::Segment& sg : q->segments) {
-      e = t.kpo(a, sg.op, sg.first, sg.count, stream);
-      if (e != hipSuccess) break;
-    }
-  }
-  if (e == hipSuccess && (d_logits_last || d_next)) {
-    // LM head on the last prompt position only
-    Args lm = a;
+  // LM head on the last prompt position only, with the one-row decode layout
+  const bool want_lm = d_logits_last || d_next;
+  Args lm = a;
+  if (want_lm) {
     lm.M = 1;
-    mk_plan lp = q->plan;                 // the LM head's GEMV runs with the one-row decode layout
+    mk_plan lp = q->plan;
     lp.mode = MK_DECODE; lp.rows = 1;
     const LdsLayout ll = lds_layout(c, lp);
     lm.lds_res = ll.res; lm.lds_x = ll.x; lm.lds_union = ll.uni; lm.lds_bytes = ll.bytes; lm.lds_ring = ll.ring;
     lm.lm_x = a.X + (size_t)c.n_layers * a.sX + (size_t)(seq_len - 1) * c.hidden;
     lm.logits = d_logits_last; lm.next = d_next;
-    e = launch_lm(pick_table(c.dtype, 1), lm, d_next != nullptr, stream);
   }
-  if (e == hipErrorCooperativeLaunchTooLarge)
-    FAIL(MK_ENOTSUP, "%d megakernel workgroups per compute unit do not fit its registers / shared memory",
-         g_opt.workers_per_cu);
+  const Table t = table_prefill();
+  const Table tl = pick_table(c.dtype, 1);
+  hipError_t e = t.prep(a, exec_mode, g_opt.workers_per_cu);
+  if (e == hipSuccess && want_lm) e = tl.prep_lm(lm);
+  if (mk_status st = prep_status(e)) return st;
+
+  const bool mega = exec_mode == MK_MEGAKERNEL;
+  const uint32_t nr = mega ? a.n_barriers : 0, nh = mega ? a.n_queues : 0;
+  hipLaunchKernelGGL(reset_kernel, dim3((nr + 255) / 256 + 1), dim3(256), 0, stream, a.counters, nr, a.heads, nh,
+                     a.err);
+  e = hipGetLastError();
+  if (e == hipSuccess) {
+    if (mega) {
+      e = t.mega(a, num_cus() * g_opt.workers_per_cu, stream);
+    } else {
+      for (const mk::Segment& sg : q->segments) {
+        e = t.kpo(a, sg.op, sg.first, sg.count, stream);
+        if (e != hipSuccess) break;
+      }
+    }
+  }
+  if (e == hipSuccess && want_lm) e = launch_lm(tl, lm, d_next != nullptr, stream);
   if (e != hipSuccess) FAIL(MK_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
   return MK_OK;
 }
@@ -482,6 +640,7 @@ mk_status mk_device_error(const mk_queue* q, const void* d_workspace, mk_dev_err
 }
 
 mk_status mk_set_option(int32_t key, int64_t value) {
+  std::lock_guard<std::mutex> lk(g_mu);
   switch (key) {
     case MK_OPT_WORKERS_PER_CU:
       if (value < 1 || value > 8) FAIL(MK_EINVAL, "workers per CU must be 1..8");
@@ -497,19 +656,23 @@ mk_status mk_set_option(int32_t key, int64_t value) {
     case MK_OPT_GEMV_PIPE:
       if (value < 0 || value > 2) FAIL(MK_EINVAL, "GEMV issue mode must be 0, 1 or 2");
       g_opt.gemv_pipe = (int)value; return MK_OK;
-
+    case MK_OPT_DELAY_SEED:
+      if (value < 0 || value > 0xFFFFFFFFll) FAIL(MK_EINVAL, "delay seed must fit 32 bits");
+      g_opt.delay_seed = (uint32_t)value; return MK_OK;
     default: FAIL(MK_EINVAL, "unknown or read-only option %d", key);
   }
 }
 
 int64_t mk_get_option(int32_t key) {
+  if (key == MK_OPT_NUM_CUS) return num_cus();
+  std::lock_guard<std::mutex> lk(g_mu);
   switch (key) {
     case MK_OPT_WORKERS_PER_CU: return g_opt.workers_per_cu;
     case MK_OPT_SPIN_LIMIT: return g_opt.spin_limit;
-    case MK_OPT_NUM_CUS: return num_cus();
     case MK_OPT_TRACE_BUFFER: return (int64_t)(uintptr_t)g_opt.trace;
     case MK_OPT_TRACE_BYTES: return (int64_t)g_opt.trace_bytes;
     case MK_OPT_GEMV_PIPE: return g_opt.gemv_pipe;
+    case MK_OPT_DELAY_SEED: return g_opt.delay_seed;
     default: return -1;
   }
 }

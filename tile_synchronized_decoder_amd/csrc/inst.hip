@@ -12,6 +12,7 @@
 
 namespace mkd {
 Table MK_CAT(table_, MK_WT_NAME, MK_NB)() {
-  return {Launch<MK_WT, MK_NB>::mega, Launch<MK_WT, MK_NB>::kpo, Launch<MK_WT, MK_NB>::lm};
+  using LT = Launch<MK_WT, MK_NB>;
+  return {LT::prep, LT::mega, LT::kpo, LT::prep_lm, LT::lm};
 }
 }  // namespace mkd

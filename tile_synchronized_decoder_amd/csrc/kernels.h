@@ -14,10 +14,14 @@
 // block.
 //
 // gfx950 specifics: 64-lane wavefronts, 4 waves (256 threads) per workgroup,
-// one workgroup per compute unit by default; weights are streamed with
-// 16-byte non-temporal loads; barrier hand-off uses agent-scope release /
-// acquire, which on this part writes back / invalidates the per-XCD L2 so a
-// tile written on one XCD is visible on another.
+// one workgroup per compute unit by default; weights stream into shared
+// memory by direct-to-LDS loads.  The tile hand-off does not use whole-cache
+// release / acquire (on this part that writes back or invalidates every
+// per-XCD L2): intermediate tiles are stored and loaded only with agent-scope
+// (sc1) atomic accesses, which are coherent across the XCDs' L2 caches; a
+// producer waits until its stores are acknowledged (vmcnt 0) before one
+// thread bumps the tile's counter, and a consumer issues its tile loads only
+// after its poll of the counter has returned.  See signal_tile / wait_tiles.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -92,6 +96,7 @@ struct Args {
   const float* lm_x;             // LM head input rows
   int gemv_pipe;                 // decode GEMV weight issue: 0, 1 pipelined; 2 compiler-ordered
   int fuse_combine;              // decode queue without split combines: O-projection merges the partials
+  uint32_t delay_seed;           // race check: seeded stall before each tile's stores (0: off)
   // prefill: bf16 GEMM operands (X and HRES with the consumer's RMSNorm gain
   // applied), per-row sums of squares of X / HRES per 128-column tile
   uint16_t* XB; uint16_t* HB; uint16_t* ATTB; uint16_t* ACTB;
@@ -291,6 +296,18 @@ __device__ __forceinline__ bool wait_tiles(KArgs& a, const Instr in, uint32_t id
   asm volatile("" ::: "memory");                 // no tile load may move above the wait
   trace_mark(a, idx, 2);
   return all;
+}
+
+// Race check (option MK_OPT_DELAY_SEED): before it stores its tile, a producer
+// stalls for a pseudo-random time drawn from (seed, instruction index), 0 to
+// about 50 us, so a consumer that read a tile without waiting for it would read
+// the workspace's previous (poisoned) contents.  Uniform across the workgroup.
+__device__ __forceinline__ void inject_delay(KArgs& a, uint32_t idx) {
+  if (a.delay_seed == 0) return;
+  uint32_t h = (idx + 1u) * 0x9E3779B1u ^ a.delay_seed;     // a 32-bit integer mix (murmur3 finaliser)
+  h ^= h >> 16; h *= 0x85EBCA6Bu; h ^= h >> 13; h *= 0xC2B2AE35u; h ^= h >> 16;
+  const uint32_t n = __builtin_amdgcn_readfirstlane(h & 15u);
+  for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(127);
 }
 
 // Publish this instruction's tile: every wave waits for its coherent stores to
@@ -752,6 +769,7 @@ __device__ __forceinline__ void op_gemv_rpw(KArgs& a, Smem& s, const Instr in, u
     x = a.ACT + l * a.sACT; resid = a.HRES + l * a.sHRES + n0; ld = a.H;
   }
   if (!gemv<WT, NB, RPW, PIPE>(a, s, g, x, a.M, gain, gain != nullptr, mega, fused, in, idx, resid, ld)) return;
+  inject_delay(a, idx);
   {
     for (int e = threadIdx.x; e < n * a.M; e += NT) {
       const int row = e / a.M, b = e - row * a.M;
@@ -798,9 +816,10 @@ __device__ __forceinline__ void op_gemv(KArgs& a, Smem& s, const Instr in, uint3
 
 // EMBED(n0, n1): X_0[b, n0:n1] = E[token_b, n0:n1]
 template <typename WT>
-__device__ __forceinline__ void op_embed(KArgs& a, const Instr in, bool mega) {
+__device__ __forceinline__ void op_embed(KArgs& a, const Instr in, uint32_t idx, bool mega) {
   const int n0 = in.a0, n = in.a1 - in.a0;
   const WT* E = static_cast<const WT*>(a.embed);
+  inject_delay(a, idx);
   for (int e = threadIdx.x; e < n * a.M; e += NT) {
     const int b = e / n, c = e - b * n;
     const int tok = a.tokens[b];
@@ -889,6 +908,7 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
   load_rows(kr, Kc, 0);
   load_rows(vr, Vc, 0);
   if (mega && !wait_tiles(a, in, idx)) return;
+  inject_delay(a, idx);
 
   float* slot = a.OPART + l * a.sOP + ((size_t)(b * a.nkv + g) * a.NS + sp) * (size_t)(r * HD + 2 * r);
   if (j0 >= j1) {                                         // empty split
@@ -1153,6 +1173,7 @@ template <int HD>
 __device__ __forceinline__ void op_combine(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
   const int l = in.layer, b = in.a0, g = in.a1, r = a.r;
   if (mega && !wait_tiles(a, in, idx)) return;
+  inject_delay(a, idx);
   const int slot_sz = r * HD + 2 * r;
   const int total = a.NS * slot_sz;
   const float* base = a.OPART + l * a.sOP + (size_t)(b * a.nkv + g) * a.NS * slot_sz;
@@ -1190,7 +1211,7 @@ template <typename WT, int NB>
 __device__ __forceinline__ void run_instr(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega, int only_op) {
   const int op = only_op ? only_op : in.op;
   switch (op) {
-    case mk::OP_EMBED: op_embed<WT>(a, in, mega); break;
+    case mk::OP_EMBED: op_embed<WT>(a, in, idx, mega); break;
     case mk::OP_QKV: case mk::OP_OPROJ: case mk::OP_GATEUP: case mk::OP_DOWN:
       // one GEMV body for the four ops (the interpreter's code size matters for
       // the instruction cache); only the megakernel's O-projection of a fused
@@ -1461,13 +1482,19 @@ __global__ __launch_bounds__(NT) void lm_head_regs(Args args) {
   }
 }
 
-// Kernels whose dynamic shared memory exceeds the default limit must opt in once.
+// Kernels whose dynamic shared memory exceeds the default limit must opt in,
+// once per device.  `granted` holds the bytes granted so far per device; the
+// callers hold the library's lock.
+constexpr int kMaxDevices = 64;
 template <typename K>
-inline hipError_t allow_lds(K kernel, uint32_t bytes, uint32_t& granted) {
-  if (bytes <= granted) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) granted = bytes;
+inline hipError_t allow_lds(K kernel, uint32_t bytes, uint32_t (&granted)[kMaxDevices]) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (bytes <= 64 * 1024 || bytes <= granted[dev]) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) granted[dev] = bytes;
   return e;
 }
 
@@ -1548,25 +1575,31 @@ __global__ __launch_bounds__(NT) void kpo_prefill(Args args, uint32_t first) {
 }
 
 struct PrefillLaunch {
-  static hipError_t mega(const Args& a, int grid, int per_cu, hipStream_t st) {
-    static uint32_t granted = 64 * 1024;
-    hipError_t e = allow_lds(mk_interp_prefill, a.lds_bytes, granted);
-    if (e == hipSuccess) e = check_resident(mk_interp_prefill, a.lds_bytes, per_cu);
-    if (e != hipSuccess) return e;
+  // Everything that can refuse a call, before anything is enqueued.
+  static hipError_t prep(const Args& a, int exec_mode, int per_cu) {
+    if (exec_mode == MK_MEGAKERNEL) {
+      static uint32_t granted[kMaxDevices] = {};
+      hipError_t e = allow_lds(mk_interp_prefill, a.lds_bytes, granted);
+      return e == hipSuccess ? check_resident(mk_interp_prefill, a.lds_bytes, per_cu) : e;
+    }
+    static uint32_t granted[mk::OP_COUNT][kMaxDevices] = {};
+    hipError_t e = hipSuccess;
+#define PREP_CASE(OPC) if (e == hipSuccess) e = allow_lds(kpo_prefill<OPC>, a.lds_bytes, granted[OPC]);
+    PREP_CASE(mk::OP_P_EMBED) PREP_CASE(mk::OP_P_QKV) PREP_CASE(mk::OP_P_ATTN) PREP_CASE(mk::OP_P_OPROJ)
+    PREP_CASE(mk::OP_P_GATEUP) PREP_CASE(mk::OP_P_DOWN)
+#undef PREP_CASE
+    return e;
+  }
+  static hipError_t mega(const Args& a, int grid, hipStream_t st) {
     hipLaunchKernelGGL(mk_interp_prefill, dim3(grid), dim3(NT), a.lds_bytes, st, a);
     return hipGetLastError();
   }
   static hipError_t kpo(const Args& a, uint32_t op, uint32_t first, uint32_t count, hipStream_t st) {
-    static uint32_t granted[mk::OP_COUNT] = {};
     switch (op) {
 #define KPO_CASE(OPC)                                                                              \
-      case OPC: {                                                                                  \
-        if (!granted[OPC]) granted[OPC] = 64 * 1024;                                               \
-        hipError_t e = allow_lds(kpo_prefill<OPC>, a.lds_bytes, granted[OPC]);                     \
-        if (e != hipSuccess) return e;                                                             \
+      case OPC:                                                                                    \
         hipLaunchKernelGGL((kpo_prefill<OPC>), dim3(count), dim3(NT), a.lds_bytes, st, a, first);  \
-        break;                                                                                     \
-      }
+        break;
       KPO_CASE(mk::OP_P_EMBED) KPO_CASE(mk::OP_P_QKV) KPO_CASE(mk::OP_P_ATTN) KPO_CASE(mk::OP_P_OPROJ)
       KPO_CASE(mk::OP_P_GATEUP) KPO_CASE(mk::OP_P_DOWN)
 #undef KPO_CASE
@@ -1580,26 +1613,34 @@ struct PrefillLaunch {
 
 template <typename WT, int NB>
 struct Launch {
-  static hipError_t mega(const Args& a, int grid, int per_cu, hipStream_t st) {
-    static uint32_t granted = 64 * 1024;
-    hipError_t e = allow_lds(mk_interp<WT, NB>, a.lds_bytes, granted);
-    if (e == hipSuccess) e = check_resident(mk_interp<WT, NB>, a.lds_bytes, per_cu);
-    if (e != hipSuccess) return e;
+  // Everything that can refuse a call, before anything is enqueued: the shared
+  // memory opt-in of every kernel the call may launch and, for the megakernel,
+  // that all of its workgroups can be resident at once.
+  static hipError_t prep(const Args& a, int exec_mode, int per_cu) {
+    if (exec_mode == MK_MEGAKERNEL) {
+      static uint32_t granted[kMaxDevices] = {};
+      hipError_t e = allow_lds(mk_interp<WT, NB>, a.lds_bytes, granted);
+      return e == hipSuccess ? check_resident(mk_interp<WT, NB>, a.lds_bytes, per_cu) : e;
+    }
+    static uint32_t granted[KPO_OPROJ_FUSED + 1][kMaxDevices] = {};
+    hipError_t e = hipSuccess;
+#define PREP_CASE(OPC) if (e == hipSuccess) e = allow_lds(kpo_kernel<WT, NB, OPC>, a.lds_bytes, granted[OPC]);
+    PREP_CASE(mk::OP_EMBED) PREP_CASE(mk::OP_QKV) PREP_CASE(mk::OP_ATTN) PREP_CASE(mk::OP_COMBINE)
+    PREP_CASE(mk::OP_OPROJ) PREP_CASE(mk::OP_GATEUP) PREP_CASE(mk::OP_DOWN) PREP_CASE(KPO_OPROJ_FUSED)
+#undef PREP_CASE
+    return e;
+  }
+  static hipError_t mega(const Args& a, int grid, hipStream_t st) {
     hipLaunchKernelGGL((mk_interp<WT, NB>), dim3(grid), dim3(NT), a.lds_bytes, st, a);
     return hipGetLastError();
   }
   static hipError_t kpo(const Args& a, uint32_t op, uint32_t first, uint32_t count, hipStream_t st) {
-    static uint32_t granted[KPO_OPROJ_FUSED + 1] = {};
     if (op == mk::OP_OPROJ && a.fuse_combine) op = KPO_OPROJ_FUSED;
     switch (op) {
 #define KPO_CASE(OPC)                                                                              \
-      case OPC: {                                                                                  \
-        if (!granted[OPC]) granted[OPC] = 64 * 1024;                                               \
-        hipError_t e = allow_lds(kpo_kernel<WT, NB, OPC>, a.lds_bytes, granted[OPC]);              \
-        if (e != hipSuccess) return e;                                                             \
+      case OPC:                                                                                    \
         hipLaunchKernelGGL((kpo_kernel<WT, NB, OPC>), dim3(count), dim3(NT), a.lds_bytes, st, a, first); \
-        break;                                                                                     \
-      }
+        break;
       KPO_CASE(mk::OP_EMBED) KPO_CASE(mk::OP_QKV) KPO_CASE(mk::OP_ATTN) KPO_CASE(mk::OP_COMBINE)
       KPO_CASE(mk::OP_OPROJ) KPO_CASE(mk::OP_GATEUP) KPO_CASE(mk::OP_DOWN) KPO_CASE(KPO_OPROJ_FUSED)
 #undef KPO_CASE
@@ -1607,26 +1648,32 @@ struct Launch {
     }
     return hipGetLastError();
   }
+  // The LM head's kernel and its shared memory: for up to 4 rows the register
+  // streaming kernel (normalised rows + per-wave partials), else the ring GEMV.
+  static bool lm_regs(const Args& a) {
+    return NB <= 4 && a.H % 8 == 0 && 4u * (NB * a.H + NWAVE * NB + NB + 2 * NWAVE * NB) <= 64 * 1024;
+  }
+  static hipError_t prep_lm(const Args& a) {
+    if (lm_regs(a)) return hipSuccess;
+    static uint32_t granted[kMaxDevices] = {};
+    return allow_lds(lm_head_kernel<WT, NB>, a.lds_bytes, granted);
+  }
   static hipError_t lm(const Args& a, hipStream_t st) {
-    if constexpr (NB <= 4) {
-      // normalised rows + per-wave partials in shared memory
+    if (lm_regs(a)) {
       const uint32_t bytes = 4u * (NB * a.H + NWAVE * NB + NB + 2 * NWAVE * NB);
-      if (a.H % 8 == 0 && bytes <= 64 * 1024) {
-        hipLaunchKernelGGL((lm_head_regs<WT, NB>), dim3(a.lm_blocks), dim3(NT), bytes, st, a);
-        return hipGetLastError();
-      }
+      hipLaunchKernelGGL((lm_head_regs<WT, NB>), dim3(a.lm_blocks), dim3(NT), bytes, st, a);
+    } else {
+      hipLaunchKernelGGL((lm_head_kernel<WT, NB>), dim3(a.lm_blocks), dim3(NT), a.lds_bytes, st, a);
     }
-    static uint32_t granted = 64 * 1024;
-    hipError_t e = allow_lds(lm_head_kernel<WT, NB>, a.lds_bytes, granted);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((lm_head_kernel<WT, NB>), dim3(a.lm_blocks), dim3(NT), a.lds_bytes, st, a);
     return hipGetLastError();
   }
 };
 
 struct Table {
-  hipError_t (*mega)(const Args&, int, int, hipStream_t);
-  hipError_t (*kpo)(const Args&, uint32_t, uint32_t, uint32_t, hipStream_t);
+  hipError_t (*prep)(const Args&, int exec_mode, int per_cu);
+  hipError_t (*mega)(const Args&, int grid, hipStream_t);
+  hipError_t (*kpo)(const Args&, uint32_t op, uint32_t first, uint32_t count, hipStream_t);
+  hipError_t (*prep_lm)(const Args&);
   hipError_t (*lm)(const Args&, hipStream_t);
 };
 

@@ -343,6 +343,7 @@ __device__ __forceinline__ void op_p_embed(KArgs& a, const Instr in, uint32_t id
   const int c8 = a.H / 8;                                 // prefill needs the hidden size a multiple of 128
   const int nss = (a.H + PBN - 1) / PBN;
   const int n = rows * c8;                                // a multiple of 16: groups of 16 threads stay together
+  inject_delay(a, idx);
   constexpr int U = 4;                                    // row chunks per thread in flight at once
   for (int e0 = 0; e0 < n; e0 += NT * U) {
     v4u w[U];
@@ -426,6 +427,7 @@ __device__ __forceinline__ void op_p_qkv(KArgs& a, Smem& s, const Instr in, uint
   __syncthreads();
   const int hh = n0 / PBN;                        // head index within [q | k | v]
   const bool is_q = hh < a.nq, is_k = !is_q && hh < a.nq + a.nkv;
+  inject_delay(a, idx);
   const int row = t >> 1, part = t & 1;           // two threads per row: pairs [part*32, part*32+32)
   const int HALF = PBN / 2;
   float x0[32], x1[32];
@@ -516,6 +518,7 @@ __device__ __forceinline__ void op_p_resid(KArgs& a, Smem& s, const Instr in, ui
             next ? (down ? a.XB + (l + 1) * a.sXB : a.HB + l * a.sXB) : nullptr,
             next ? (down ? a.attn_norm + (size_t)(l + 1) * a.H : a.ffn_norm + (size_t)l * a.H) : nullptr,
             next ? (down ? a.XSS + (l + 1) * a.sXSS : a.HSS + l * a.sXSS) : nullptr, nss, n0, a.H, r0, rows};
+  inject_delay(a, idx);
   p_write_rows(ct, o);
   if (mega) signal_tile(a, in);
 }
@@ -548,6 +551,7 @@ __device__ __forceinline__ void op_p_gateup(KArgs& a, Smem& s, const Instr in, u
       }
   __syncthreads();
   PRowOut o{a.ACT + l * a.sACT, nullptr, a.F, a.ACTB + l * a.sACTB, nullptr, nullptr, 0, n0, a.F, r0, rows};
+  inject_delay(a, idx);
   p_write_rows(ct, o);
   if (mega) signal_tile(a, in);
 }
@@ -745,6 +749,7 @@ __device__ __forceinline__ void op_p_attn(KArgs& a, Smem& s, const Instr in, uin
       }
   __syncthreads();
   PRowOut po{a.ATT + l * a.sATT, nullptr, a.NA, a.ATTB + l * a.sATTB, nullptr, nullptr, 0, h * HD, a.NA, r0, rows};
+  inject_delay(a, idx);
   p_write_rows(ct, po);
   if (mega) signal_tile(a, in);
 }

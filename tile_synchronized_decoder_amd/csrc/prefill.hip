@@ -4,5 +4,5 @@
 #include "kernels.h"
 
 namespace mkd {
-Table table_prefill() { return {PrefillLaunch::mega, PrefillLaunch::kpo, nullptr}; }
+Table table_prefill() { return {PrefillLaunch::prep, PrefillLaunch::mega, PrefillLaunch::kpo, nullptr, nullptr}; }
 }  // namespace mkd

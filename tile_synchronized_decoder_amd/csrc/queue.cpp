@@ -17,6 +17,7 @@
 // intervals its read region overlaps, sorted by (tensor, column, row) and
 // stored as runs of consecutive ids.
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -271,6 +272,8 @@ mk_status mk_build_queue(const mk_config* cfg, const mk_plan* plan, mk_queue** o
   mk_queue* q = new (std::nothrow) mk_queue();
   if (!q) { mk::set_error("out of host memory"); return MK_ENOMEM; }
   try {
+    static std::atomic<uint64_t> next_serial{1};
+    q->serial = next_serial.fetch_add(1);
     q->cfg = *cfg;
     q->plan = *plan;
     mk::Builder b{q, q->cfg, q->plan};
@@ -335,7 +338,11 @@ mk_status mk_queue_export(const mk_queue* q, int32_t part, void* host_dst, size_
   return MK_OK;
 }
 
-void mk_queue_free(mk_queue* q) { delete q; }
+void mk_queue_free(mk_queue* q) {
+  if (!q) return;
+  mk::forget_graphs(q->serial);
+  delete q;
+}
 
 const char* mk_last_error(void) { return mk::last_error(); }
 

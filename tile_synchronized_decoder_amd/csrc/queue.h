@@ -35,6 +35,7 @@ struct Segment { uint32_t op, layer, first, count; };
 struct mk_queue {
   mk_config cfg;
   mk_plan plan;
+  uint64_t serial = 0;    // unique per queue built in this process (keys the graph cache)
   uint32_t n_splits = 0;
   std::vector<mk::Instr> instr;
   std::vector<mk::Range> waits;
@@ -46,4 +47,5 @@ struct mk_queue {
 
 namespace mk {
 void set_error(const char* fmt, ...);
+void forget_graphs(uint64_t serial);   // drops the HIP graphs captured for a queue
 }

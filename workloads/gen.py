@@ -102,20 +102,32 @@ def global_weights(model: ModelConfig, seed: int, gain_jitter: float = 0.0) -> D
     return out
 
 
-def kv_cache_layer(model: ModelConfig, run: RunConfig, layer: int) -> Tuple[np.ndarray, np.ndarray]:
-    """K and V of one layer, [B, n_kv, ctx_max, hd] in the model's storage type."""
+def kv_cache_layer(model: ModelConfig, run: RunConfig, layer: int,
+                   threads: int = 1) -> Tuple[np.ndarray, np.ndarray]:
+    """K and V of one layer, [B, n_kv, ctx_max, hd] in the model's storage type.
+    Row b's keys and values have streams of their own, so row b is the same
+    whatever the batch (given the same seed and starting context)."""
     B, G, C, hd = run.batch, model.n_kv_heads, run.ctx_max, model.head_dim
     dt = np.uint16 if model.dtype == BF16 else np.float32
     K = np.zeros((B, G, C, hd), dtype=dt)
     V = np.zeros((B, G, C, hd), dtype=dt)
     if not run.init_cache:
         return K, V
-    for b in range(B):
+
+    def fill(job):
+        b, which = job
         p0 = run.ctx0[b]
-        for which, dst in ((0, K), (1, V)):
-            g = _rng(run.seed, K_KV, layer, (b * 2 + which))
-            x = _normal(g, (G, p0, hd), 1.0)
-            dst[b, :, :p0, :] = f32_to_bf16_bits(x) if model.dtype == BF16 else x
+        g = _rng(run.seed, K_KV, layer, (b * 2 + which))
+        x = _normal(g, (G, p0, hd), 1.0)
+        (K, V)[which][b, :, :p0, :] = f32_to_bf16_bits(x) if model.dtype == BF16 else x
+
+    jobs = [(b, which) for b in range(B) for which in (0, 1)]
+    if threads > 1:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill, jobs))
+    else:
+        for j in jobs:
+            fill(j)
     return K, V
 
 
