@@ -210,6 +210,28 @@ mk_status mk_decode_step(const mk_queue* q, const void* d_queue, const mk_weight
                          size_t workspace_nbytes, float* d_logits, int32_t* d_next,
                          int32_t exec_mode, hipStream_t stream);
 
+/* mk_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory or pass one (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  The step's workspace is a
+ * static device array of MK_STATIC_SCRATCH_BYTES (64 MiB) inside the library,
+ * one per device, held until the process ends; no hipMalloc, hipFree or
+ * allocating library routine is called.  A queue whose workspace
+ * (mk_workspace_nbytes) exceeds it is refused with MK_EINVAL.  exec_mode:
+ * MK_MEGAKERNEL or MK_KERNEL_PER_OP (graph mode allocates: MK_EINVAL).  The
+ * other arguments and the results are those of mk_decode_step.  d_error
+ * (nullable, device, 8 x u32) receives the step's device error record
+ * (mk_dev_error, then 3 zero words) when the step ends, since the scratch
+ * holding it is not the caller's.  Every call on a device shares that
+ * device's scratch and leaves its contents there (counters and the error
+ * record are cleared at the start of each call): calls that overlap on one
+ * device race, whatever their streams. */
+#define MK_STATIC_SCRATCH_BYTES (64u << 20)
+mk_status mk_decode_step_static(const mk_queue* q, const void* d_queue, const mk_weights* w,
+                                const mk_kv* kv, const int32_t* d_tokens, const float* d_x0,
+                                const int32_t* d_ctx_lens, int32_t batch, float* d_logits,
+                                int32_t* d_next, uint32_t* d_error, int32_t exec_mode,
+                                hipStream_t stream);
+
 /* The LM head on its own (the second half of mk_decode_step): final RMSNorm
  * of the workspace's last hidden rows (MK_T_X of layer n_layers, written by a
  * previous mk_decode_step on the same stream and workspace), the vocabulary

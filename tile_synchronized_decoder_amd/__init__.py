@@ -14,7 +14,7 @@ from typing import Dict, Optional
 from . import _lib as _L
 from ._lib import (MK_OK, MK_EINVAL, MK_ENOMEM, MK_ELAUNCH, MK_EDEVICE, MK_ENOTSUP,
                    MK_BF16, MK_DECODE, MK_F32, MK_KERNEL_PER_OP, MK_KERNEL_PER_OP_GRAPH, MK_MEGAKERNEL, MK_PREFILL,
-                   MK_PART_DEVICE, MK_PART_INSTR, MK_PART_META, MK_PART_TARGETS, MK_PART_WAITS,
+                   MK_PART_DEVICE, MK_PART_INSTR, MK_PART_META, MK_PART_TARGETS, MK_PART_WAITS, MK_STATIC_SCRATCH_BYTES,
                    MK_T_ACT, MK_T_ATT, MK_T_COUNTERS, MK_T_ERROR, MK_T_HEADS, MK_T_HRES,
                    MK_T_OPART, MK_T_QKV, MK_T_X, MK_OPT_NUM_CUS, MK_OPT_SPIN_LIMIT, MK_OPT_TRACE_BUFFER,
                    MK_OPT_TRACE_BYTES, MK_OPT_GEMV_PIPE, MK_OPT_DELAY_SEED,
@@ -102,6 +102,14 @@ def mk_decode_step(q: Queue, d_queue, w: mk_weights, kv: mk_kv, tokens, x0, ctx_
                                      _ptr(x0), _ptr(ctx_lens), batch, _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _ptr(logits),
                                      _ptr(next_tokens), exec_mode, _stream(stream)), "mk_decode_step")
+
+
+def mk_decode_step_static(q: Queue, d_queue, w: mk_weights, kv: mk_kv, tokens, x0, ctx_lens, batch: int,
+                          logits, next_tokens, error=None, exec_mode: int = MK_MEGAKERNEL, stream=None) -> None:
+    """mk_decode_step on the library's static device scratch (no workspace)."""
+    _L.check(_L.lib().mk_decode_step_static(q.handle, _ptr(d_queue), C.byref(w), C.byref(kv), _ptr(tokens),
+                                            _ptr(x0), _ptr(ctx_lens), batch, _ptr(logits), _ptr(next_tokens),
+                                            _ptr(error), exec_mode, _stream(stream)), "mk_decode_step_static")
 
 
 def mk_lm_head(q: Queue, w: mk_weights, workspace, logits, next_tokens, stream=None) -> None:

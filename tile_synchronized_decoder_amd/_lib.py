@@ -16,6 +16,7 @@ MK_F32, MK_BF16 = 0, 1
 MK_DECODE, MK_PREFILL = 0, 1
 MK_MEGAKERNEL, MK_KERNEL_PER_OP, MK_KERNEL_PER_OP_GRAPH = 0, 1, 2
 MK_PART_META, MK_PART_INSTR, MK_PART_WAITS, MK_PART_TARGETS, MK_PART_DEVICE = range(5)
+MK_STATIC_SCRATCH_BYTES = 64 << 20
 (MK_T_X, MK_T_QKV, MK_T_OPART, MK_T_ATT, MK_T_HRES, MK_T_ACT, MK_T_COUNTERS, MK_T_HEADS,
  MK_T_ERROR, MK_T_LMPART) = range(10)
 (MK_OPT_WORKERS_PER_CU, MK_OPT_SPIN_LIMIT, MK_OPT_NUM_CUS, MK_OPT_TRACE_BUFFER, MK_OPT_TRACE_BYTES,
@@ -71,6 +72,8 @@ def lib() -> C.CDLL:
         "mk_workspace_offset": (I32, [VP, I32, I32, P(SZ)]),
         "mk_decode_step": (I32, [VP, VP, P(mk_weights), P(mk_kv), VP, VP, VP, I32, VP, SZ, VP, VP,
                                  I32, VP]),
+        "mk_decode_step_static": (I32, [VP, VP, P(mk_weights), P(mk_kv), VP, VP, VP, I32, VP, VP, VP, I32,
+                                        VP]),
         "mk_lm_head": (I32, [VP, P(mk_weights), VP, SZ, VP, VP, VP]),
         "mk_prefill": (I32, [VP, VP, P(mk_weights), P(mk_kv), VP, I32, I32, VP, SZ, VP, VP, I32, VP]),
         "mk_device_error": (I32, [VP, VP, P(mk_dev_error), VP]),
@@ -88,7 +91,8 @@ def lib() -> C.CDLL:
 
 
 EXPORTED = ["mk_build_queue", "mk_queue_nbytes", "mk_queue_export", "mk_queue_free",
-            "mk_workspace_nbytes", "mk_workspace_offset", "mk_decode_step", "mk_lm_head", "mk_prefill",
+            "mk_workspace_nbytes", "mk_workspace_offset", "mk_decode_step", "mk_decode_step_static",
+            "mk_lm_head", "mk_prefill",
             "mk_device_error", "mk_set_option", "mk_get_option", "mk_status_str", "mk_last_error"]
 
 

@@ -467,6 +467,35 @@ mk_status decode_impl(const mk_queue* q, const void* d_queue, const mk_weights* 
   return MK_OK;
 }
 
+// ----------------------------------------------------------------------------- static scratch
+
+// The workspace of mk_decode_step_static: a file-scope device array, one copy
+// per device the library runs on, held until the process ends.  Host code never
+// uses the array's name as an address (on the host it is only a stand-in): the
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+void* g_scratch[kMaxDevices] = {};
+
+__global__ void copy_words_kernel(uint32_t* dst, const uint32_t* src, uint32_t n) {
+  if (threadIdx.x < n) dst[threadIdx.x] = src[threadIdx.x];
+}
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+mk_status scratch_of_device(int dev, void** out) {
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) FAIL(MK_ELAUNCH, "address of the static scratch: %s", hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MK_OK;
+}
 }  // namespace
 
 namespace mk {
@@ -521,6 +550,33 @@ mk_status mk_decode_step(const mk_queue* q, const void* d_queue, const mk_weight
   std::lock_guard<std::mutex> lk(g_mu);
   return decode_impl(q, d_queue, w, kv, d_tokens, d_x0, d_ctx_lens, batch, d_workspace, workspace_nbytes, d_logits,
                      d_next, exec_mode, stream);
+}
+
+mk_status mk_decode_step_static(const mk_queue* q, const void* d_queue, const mk_weights* w, const mk_kv* kv,
+                                const int32_t* d_tokens, const float* d_x0, const int32_t* d_ctx_lens,
+                                int32_t batch, float* d_logits, int32_t* d_next, uint32_t* d_error,
+                                int32_t exec_mode, hipStream_t stream) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!q) FAIL(MK_EINVAL, "null argument");
+  if (exec_mode == MK_KERNEL_PER_OP_GRAPH)
+    FAIL(MK_EINVAL, "the static-scratch step has no graph mode (instantiating a graph allocates)");
+  const size_t need = layout(q).total;
+  if (need > kScratchBytes)
+    FAIL(MK_EINVAL, "the step needs %zu bytes of workspace; the static scratch holds %zu", need, kScratchBytes);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) FAIL(MK_ELAUNCH, "no current device");
+  void* ws = nullptr;
+  if (mk_status st = scratch_of_device(dev, &ws)) return st;
+  if (mk_status st = decode_impl(q, d_queue, w, kv, d_tokens, d_x0, d_ctx_lens, batch, ws, kScratchBytes,
+                                 d_logits, d_next, exec_mode, stream))
+    return st;
+  if (d_error) {
+    hipLaunchKernelGGL(copy_words_kernel, dim3(1), dim3(64), 0, stream, d_error,
+                       reinterpret_cast<const uint32_t*>(static_cast<uint8_t*>(ws) + layout(q).ERR), 8u);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) FAIL(MK_ELAUNCH, "copy of the error record: %s", hipGetErrorString(e));
+  }
+  return MK_OK;
 }
 
 mk_status mk_lm_head(const mk_queue* q, const mk_weights* w, void* d_workspace, size_t workspace_nbytes,
