@@ -103,7 +103,14 @@ typedef struct mk_plan {
   int32_t fuse_combine;   /* decode: 1 = no split-combine instructions; each
                            * O-projection tile waits on the attention split
                            * partials and merges them while staging (0 or 1;
-                           * recorded in the META word after bn) */
+                           * recorded in bit 0 of the META word after bn) */
+  int32_t loop;           /* decode: 1 = a queue for mk_decode_loop (persistent
+                           * multi-step decode): each step ends with LM-head
+                           * tiles of 64 vocabulary rows (LMHEAD) and one argmax
+                           * per row (ARGMAX), and the next step's embedding
+                           * tiles wait on the previous step's argmax (flagged
+                           * waits); needs an embedding and an LM head (0 or 1;
+                           * recorded in bit 1 of the META word after bn) */
 } mk_plan;
 
 typedef struct mk_queue mk_queue;   /* opaque, host memory */
@@ -118,11 +125,14 @@ typedef struct mk_queue mk_queue;   /* opaque, host memory */
  *   META    u32 magic 'TMK1', version 1, mode, n_instr, n_barriers,
  *           n_wait_ranges, n_segments, n_queues, rows, ctx_max, n_splits,
  *           n_layers, tq, to, tf, td, kb, bm, bn, flags (bit 0: fused
- *           split combines), then n_segments x
+ *           split combines; bit 1: loop queue), then n_segments x
  *           {op, layer, first, count} (maximal runs of one op of one layer)
  *   INSTR   n_instr x 32 B {u16 op, u16 layer, u32 a0, a1, a2, wait_off,
  *           wait_cnt, signal, n_wait}
- *   WAITS   n_wait_ranges x {u32 first barrier, u32 count}
+ *   WAITS   n_wait_ranges x {u32 first barrier, u32 count}; bit 31 of count
+ *           marks barriers of the previous step (loop queues: at step t a
+ *           same-step barrier is complete at target * (t + 1) signals, a
+ *           previous-step one at target * t)
  *   TARGETS n_barriers x u32 (instructions that signal each barrier)
  *   DEVICE  INSTR | WAITS | TARGETS, each starting on a 256-byte boundary:
  *           what mk_decode_step / mk_prefill read from d_queue.

@@ -14,13 +14,25 @@ summary):
     it waits on sits earlier in the queue, so a global pop in queue order can
     never deadlock, and (4) wait lists are in the documented order.
 
+    For a loop queue (several decode steps in one launch) it also checks (5)
+    that buffers can be reused across steps: every instruction must be an
+    ancestor of some ARGMAX and a descendant of some EMBED tile of its step,
+    through same-step waits, and every EMBED tile waits on all of the previous
+    step's ARGMAX; then no instruction of step t + 1 can overwrite a tile
+    before every reader of it in step t is done.
+
 ``simulate``  runs the queue with K virtual workers that pop in queue order
     (round-robin over sub-queues when the queue has several), block on their
-    wait lists, and take random times.  Each instruction runs its tile body on
-    float64 state that holds NaN until written; inputs are read when the body
-    starts and outputs land when it ends.  Any read of an unwritten element is
-    reported, as is a deadlock.  The result can be compared bit for bit across
-    worker counts and schedules, and with the plain forward pass.
+    wait lists, and take random times; a loop queue runs T steps, the queue
+    repeated T times, with counters that are never cleared (a same-step wait at
+    step t needs target * (t + 1) signals, a previous-step wait target * t).
+    Each instruction runs its tile body on float64 state that holds NaN until
+    written, and every element carries the step that last wrote it; inputs are
+    read when the body starts and outputs land when it ends.  A read of an
+    element not written in the expected step (unwritten, stale or already
+    overwritten by the next step) is reported, as is a deadlock.  The result
+    can be compared bit for bit across worker counts and schedules, and with
+    the plain forward pass.
 """
 from __future__ import annotations
 
@@ -55,12 +67,19 @@ class Parsed:
     ranges: np.ndarray           # [n_ranges, 2]
     targets: np.ndarray          # [n_barriers]
 
-    def waits_of(self, i: int) -> List[int]:
+    def waits_of(self, i: int, prev: bool = False) -> List[int]:
+        """Barrier ids instruction i waits on in its own step (or, with
+        ``prev``, the previous step's), in wait-list order."""
         off, cnt = int(self.instr[i, 5]), int(self.instr[i, 6])
         out: List[int] = []
         for f, c in self.ranges[off: off + cnt]:
-            out.extend(range(int(f), int(f) + int(c)))
+            if bool(int(c) & QS.PREV) == prev:
+                out.extend(range(int(f), int(f) + (int(c) & ~QS.PREV)))
         return out
+
+    @property
+    def loop(self) -> bool:
+        return bool(self.flags & 2)
 
 
 def parse(parts: Dict[str, bytes]) -> Parsed:
@@ -104,9 +123,20 @@ class Space:
             self.shapes[QS.tensor_order(l, QS.T_HRES)] = (M, H)
             self.shapes[QS.tensor_order(l, QS.T_ACT)] = (M, F)
             self.shapes[QS.tensor_order(l, QS.T_XNEXT)] = (M, H)
+        if p.loop:
+            self.shapes[QS.logits_tensor(model.n_layers)] = (M, model.vocab)
+            self.shapes[QS.next_tensor(model.n_layers)] = (M, 1)
 
     def regions(self, op: int, layer: int, a0: int, a1: int, a2: int):
-        """(write, reads) as (tensor, row slice, col slice), rebuilt from the opcode."""
+        """(write, reads, previous-step reads) as (tensor, row slice, col slice),
+        rebuilt from the opcode."""
+        w, reads = self._regions(op, layer, a0, a1, a2)
+        prev = []
+        if self.p.loop and op == QS.OP_EMBED:
+            prev = [(QS.next_tensor(self.model.n_layers), slice(0, self.p.rows), slice(0, 1))]
+        return w, reads, prev
+
+    def _regions(self, op: int, layer: int, a0: int, a1: int, a2: int):
         m, p = self.model, self.p
         M, H, F, hd = p.rows, m.hidden, m.ffn, m.head_dim
         nq, nkv, r = m.n_q_heads, m.n_kv_heads, m.n_q_heads // m.n_kv_heads
@@ -136,6 +166,12 @@ class Space:
             return (ACT, allr, slice(a0, a1)), [(HR, allr, slice(0, H))]
         if op == QS.OP_DOWN:
             return (XN, allr, slice(a0, a1)), [(ACT, allr, slice(0, F)), (HR, allr, slice(a0, a1))]
+        if op == QS.OP_LMHEAD and p.loop:
+            XL, LG = QS.x_tensor(m.n_layers), QS.logits_tensor(m.n_layers)
+            return (LG, allr, slice(a0, a1)), [(XL, allr, slice(0, H))]
+        if op == QS.OP_ARGMAX and p.loop:
+            LG, NX = QS.logits_tensor(m.n_layers), QS.next_tensor(m.n_layers)
+            return (NX, slice(a0, a0 + 1), slice(0, 1)), [(LG, slice(a0, a0 + 1), slice(0, m.vocab))]
         bm = p.plan[5]
         rows = lambda mb: slice(mb * bm, min((mb + 1) * bm, M))
         upto = lambda mb: slice(0, min((mb + 1) * bm, M))
@@ -177,12 +213,12 @@ def static_check(model, parts: Dict[str, bytes], max_errors: int = 20) -> List[s
             regions.append(None)
             continue
         try:
-            w, reads = sp.regions(op, layer, a0, a1, a2)
+            w, reads, prev_reads = sp.regions(op, layer, a0, a1, a2)
         except Exception as e:          # noqa: BLE001 -- report, do not crash the checker
             err(f"instr {i}: {e}")
             regions.append(None)
             continue
-        regions.append((w, reads))
+        regions.append((w, reads, prev_reads))
         signallers.setdefault(sig, []).append(i)
         t, rs, cs = w
         cur = writer[t][rs, cs]
@@ -209,71 +245,105 @@ def static_check(model, parts: Dict[str, bytes], max_errors: int = 20) -> List[s
             rr, cc = np.nonzero(wmap == bid)
             bbox[int(bid)] = (t, int(cc.min()), int(rr.min()))
 
-    for i in range(n):
-        if regions[i] is None:
-            continue
-        _, reads = regions[i]
+    def needed(reads):
         need = set()
         for t, rs, cs in reads:
             ids = writer[t][rs, cs]
             need.update(int(v) for v in np.unique(ids[ids >= 0]))
+        return need
+
+    same_waits: List[List[int]] = [[] for _ in range(n)]
+    for i in range(n):
+        if regions[i] is None:
+            continue
+        _, reads, prev_reads = regions[i]
         try:
-            waits = p.waits_of(i)
+            waits, pwaits = p.waits_of(i), p.waits_of(i, prev=True)
         except Exception:                # noqa: BLE001
             err(f"instr {i}: wait ranges out of range")
             continue
-        if int(p.instr[i, 8]) != len(waits):
-            err(f"instr {i}: n_wait {int(p.instr[i, 8])} != {len(waits)}")
-        got = set(waits)
-        if len(got) != len(waits):
-            err(f"instr {i}: duplicate waits")
-        missing, extra = need - got, got - need
-        if missing:                                             # (2) coverage
-            err(f"instr {i} ({QS.OP_NAMES.get(int(p.instr[i, 0]))}): missing waits {sorted(missing)[:5]}")
-        if extra:
-            err(f"instr {i}: waits on tiles it does not read {sorted(extra)[:5]}")
-        for bid in got:                                         # (3) topological order
-            if bid in last_sig and last_sig[bid] >= i:
-                err(f"instr {i}: waits on barrier {bid} whose producer {last_sig[bid]} is not earlier")
-            if bid not in first_sig:
-                err(f"instr {i}: waits on barrier {bid} that nobody signals")
-        keys = [bbox.get(b, (0, 0, 0)) for b in waits]          # (4) documented order
-        if keys != sorted(keys):
-            err(f"instr {i}: wait list out of order")
+        same_waits[i] = waits
+        if int(p.instr[i, 8]) != len(waits) + len(pwaits):
+            err(f"instr {i}: n_wait {int(p.instr[i, 8])} != {len(waits) + len(pwaits)}")
+        if pwaits and not p.loop:
+            err(f"instr {i}: previous-step waits in a single-step queue")
+        for kind, lst, reg in (("", waits, reads), ("previous-step ", pwaits, prev_reads)):
+            got, need = set(lst), needed(reg)
+            if len(got) != len(lst):
+                err(f"instr {i}: duplicate {kind}waits")
+            missing, extra = need - got, got - need
+            if missing:                                         # (2) coverage
+                err(f"instr {i} ({QS.OP_NAMES.get(int(p.instr[i, 0]))}): missing {kind}waits {sorted(missing)[:5]}")
+            if extra:
+                err(f"instr {i}: {kind}waits on tiles it does not read {sorted(extra)[:5]}")
+            for bid in got:
+                if bid not in first_sig:
+                    err(f"instr {i}: waits on barrier {bid} that nobody signals")
+                elif not kind and last_sig[bid] >= i:           # (3) topological order
+                    err(f"instr {i}: waits on barrier {bid} whose producer {last_sig[bid]} is not earlier")
+            keys = [bbox.get(b, (0, 0, 0)) for b in lst]        # (4) documented order
+            if keys != sorted(keys):
+                err(f"instr {i}: {kind}wait list out of order")
+
+    if p.loop:                                                  # (5) reuse across steps
+        ops = p.instr[:, 0]
+        from_embed = [False] * n
+        consumers: List[List[int]] = [[] for _ in range(n)]
+        for i in range(n):
+            prods = [j for b in same_waits[i] for j in signallers.get(b, []) if j < i]
+            for j in prods:
+                consumers[j].append(i)
+            from_embed[i] = int(ops[i]) == QS.OP_EMBED or any(from_embed[j] for j in prods)
+        to_argmax = [False] * n
+        for i in reversed(range(n)):
+            to_argmax[i] = int(ops[i]) == QS.OP_ARGMAX or any(to_argmax[c] for c in consumers[i])
+        for i in range(n):
+            if not from_embed[i]:
+                err(f"instr {i}: descends from no embedding tile of its step (may overwrite a tile the "
+                    f"previous step still reads)")
+            if not to_argmax[i]:
+                err(f"instr {i}: leads to no argmax of its step (the next step may overwrite what it reads)")
     return errs
 
 
 # ----------------------------------------------------------------------------- tile bodies and simulation
 
 class DecodeState:
-    """Float64 intermediate tensors of one decode step, NaN until written."""
+    """Float64 intermediate tensors of a run of decode steps, NaN until written.
+    Every element records the step that last wrote it (-1: never)."""
 
     def __init__(self, model: N.Model, p: Parsed, K: np.ndarray, V: np.ndarray,
-                 ctx_lens: Sequence[int], tokens=None, x0=None):
+                 ctx_lens: Sequence[int], tokens=None, x0=None, feedback: bool = False):
         cfg = model.cfg
         self.model, self.cfg, self.p = model, cfg, p
         self.K, self.V, self.ctx = K, V, [int(c) for c in ctx_lens]
         sp = Space(cfg, p)
         self.t = {t: np.full(s, np.nan) for t, s in sp.shapes.items()}
-        self.done = {t: np.zeros(s, dtype=bool) for t, s in sp.shapes.items()}
-        # split partials: [M, nkv, NS, r, hd + 2]  (o | m | l)
+        self.ver = {t: np.full(s, -1, dtype=np.int64) for t, s in sp.shapes.items()}
+        # split partials: [M, nkv, NS, r, hd + 2]  (o | m | l), and the step of each slot
         r = cfg.n_q_heads // cfg.n_kv_heads
         self.opart = {l: np.full((p.rows, cfg.n_kv_heads, p.n_splits, r, cfg.head_dim + 2), np.nan)
                       for l in range(cfg.n_layers)}
+        self.opart_ver = {l: np.full((p.rows, cfg.n_kv_heads, p.n_splits), -1, dtype=np.int64)
+                          for l in range(cfg.n_layers)}
         if not cfg.has_embed:
             self.t[0][:] = x0
-            self.done[0][:] = True
-        self.tokens = tokens
+            self.ver[0][:] = 0
+        # token ids: [B] for one step, or [steps][B] (teacher-forced, or the first row only
+        # when the argmax feeds the next step)
+        self.tokens = None if tokens is None else np.atleast_2d(np.asarray(tokens))
+        self.feedback = feedback
+        self.logits: Dict[int, np.ndarray] = {}       # step -> [M, V] (loop queues)
+        self.next: Dict[int, np.ndarray] = {}         # step -> [M]
         self.bad_reads: List[str] = []
 
-    def read(self, i: int, t: int, rs: slice, cs: slice) -> np.ndarray:
-        ok = self.done[t][rs, cs]
-        if not np.all(ok):
-            self.bad_reads.append(f"instr {i} read unwritten elements of tensor {t}")
+    def read(self, i: int, step: int, t: int, rs: slice, cs: slice, want: int) -> np.ndarray:
+        if not np.all(self.ver[t][rs, cs] == want):
+            self.bad_reads.append(f"instr {i} (step {step}) read elements of tensor {t} not written in step {want}")
         return self.t[t][rs, cs].copy()
 
-    def body(self, i: int):
-        """Compute instruction i from the current state; returns a commit closure."""
+    def body(self, i: int, step: int = 0):
+        """Compute instruction i of `step` from the current state; returns a commit closure."""
         op, l, a0, a1, a2 = (int(v) for v in self.p.instr[i, :5])
         cfg, lw = self.cfg, (self.model.layers[l] if self.model.layers else None)
         M, H, hd = self.p.rows, cfg.hidden, cfg.head_dim
@@ -283,29 +353,50 @@ class DecodeState:
         QKV, OPT = QS.tensor_order(l, QS.T_QKV), QS.tensor_order(l, QS.T_OPART)
         ATT, HR = QS.tensor_order(l, QS.T_ATT), QS.tensor_order(l, QS.T_HRES)
         ACT, XN = QS.tensor_order(l, QS.T_ACT), QS.tensor_order(l, QS.T_XNEXT)
+        rd = lambda t, rs, cs: self.read(i, step, t, rs, cs, step)
 
-        def put(t, rs, cs, val):
+        def put(t, rs, cs, val, also=None):
             def commit():
                 self.t[t][rs, cs] = val
-                self.done[t][rs, cs] = True
+                self.ver[t][rs, cs] = step
+                if also:
+                    also()
             return commit
 
+        def merged(b, g):
+            """The merged attention output of (row b, KV head g), NaN if a split
+            partial was not written in this step."""
+            if not np.all(self.opart_ver[l][b, g] == step):
+                self.bad_reads.append(f"instr {i} (step {step}) read split partials not written in step {step}")
+                return np.full(r * hd, np.nan)
+            slots = self.opart[l][b, g]                     # [NS, r, hd + 2] = (o | m | l)
+            if np.any(np.isnan(slots)):                     # computed from unwritten inputs upstream
+                return np.full(r * hd, np.nan)
+            return N.combine_splits([(sl[:, :hd], sl[:, hd], sl[:, hd + 1]) for sl in slots]).reshape(-1)
+
         if op == QS.OP_EMBED:
-            val = self.model.embed[np.asarray(self.tokens)][:, a0:a1]
-            return put(0, slice(0, M), slice(a0, a1), val)
+            if self.feedback and step > 0:
+                NX = QS.next_tensor(cfg.n_layers)
+                got = self.read(i, step, NX, slice(0, M), slice(0, 1), step - 1)[:, 0]
+                if not np.all(np.isfinite(got)):               # not written yet: reported above
+                    return put(0, slice(0, M), slice(a0, a1), np.full((M, a1 - a0), np.nan))
+                tok = got.astype(np.int64)
+            else:
+                tok = self.tokens[step]
+            return put(0, slice(0, M), slice(a0, a1), self.model.embed[np.asarray(tok)][:, a0:a1])
         if op == QS.OP_QKV:
-            xn = N.rms_norm(self.read(i, X, slice(0, M), slice(0, H)), lw.attn_norm, cfg.rms_eps)
+            xn = N.rms_norm(rd(X, slice(0, M), slice(0, H)), lw.attn_norm, cfg.rms_eps)
             return put(QKV, slice(0, M), slice(a0, a1), xn @ lw.wqkv[a0:a1].T)
         if op == QS.OP_ATTN:
             b, g, s = a0, a1, a2
             row = slice(b, b + 1)
-            q = self.read(i, QKV, row, slice(g * r * hd, (g + 1) * r * hd)).reshape(r, hd)
-            k = self.read(i, QKV, row, slice(nq * hd + g * hd, nq * hd + (g + 1) * hd)).reshape(hd)
-            v = self.read(i, QKV, row, slice((nq + nkv) * hd + g * hd, (nq + nkv) * hd + (g + 1) * hd)).reshape(hd)
+            q = rd(QKV, row, slice(g * r * hd, (g + 1) * r * hd)).reshape(r, hd)
+            k = rd(QKV, row, slice(nq * hd + g * hd, nq * hd + (g + 1) * hd)).reshape(hd)
+            v = rd(QKV, row, slice((nq + nkv) * hd + g * hd, (nq + nkv) * hd + (g + 1) * hd)).reshape(hd)
             if cfg.qk_norm:
                 q = N.rms_norm(q, lw.q_norm, cfg.rms_eps)
                 k = N.rms_norm(k, lw.k_norm, cfg.rms_eps)
-            pos = self.ctx[b]
+            pos = self.ctx[b] + step
             q, k = N.rope(q, pos, cfg.rope_theta), N.rope(k, pos, cfg.rope_theta)
             kb = self.p.plan[4]
             j0, j1 = s * kb, min((s + 1) * kb, pos + 1)
@@ -319,41 +410,48 @@ class DecodeState:
 
             def commit():
                 self.opart[l][b, g, s] = part
-                self.done[OPT][b, g] = bool(np.all(~np.isnan(self.opart[l][b, g])))
-                self.t[OPT][b, g] = 0.0
+                self.opart_ver[l][b, g, s] = step
+                if np.all(self.opart_ver[l][b, g] == step):
+                    self.t[OPT][b, g] = 0.0
+                    self.ver[OPT][b, g] = step
             return commit
         if op == QS.OP_COMBINE:
             b, g = a0, a1
-            if not self.done[OPT][b, g]:
-                self.bad_reads.append(f"instr {i} read unwritten split partials")
-            slots = self.opart[l][b, g]                     # [NS, r, hd + 2] = (o | m | l)
-            out = N.combine_splits([(sl[:, :hd], sl[:, hd], sl[:, hd + 1]) for sl in slots])
-            return put(ATT, slice(b, b + 1), slice(g * r * hd, (g + 1) * r * hd), out.reshape(1, -1))
+            return put(ATT, slice(b, b + 1), slice(g * r * hd, (g + 1) * r * hd), merged(b, g)[None, :])
         if op == QS.OP_OPROJ:
             if self.p.flags & 1:
                 # fused: merge every (row, KV head)'s split partials here
                 att = np.empty((M, nq * hd))
                 for b in range(M):
                     for g in range(nkv):
-                        if not self.done[OPT][b, g]:
-                            self.bad_reads.append(f"instr {i} read unwritten split partials")
-                            att[b, g * r * hd:(g + 1) * r * hd] = np.nan
-                            continue
-                        slots = self.opart[l][b, g]
-                        out = N.combine_splits([(sl[:, :hd], sl[:, hd], sl[:, hd + 1]) for sl in slots])
-                        att[b, g * r * hd:(g + 1) * r * hd] = out.reshape(-1)
+                        att[b, g * r * hd:(g + 1) * r * hd] = merged(b, g)
             else:
-                att = self.read(i, ATT, slice(0, M), slice(0, nq * hd))
-            xres = self.read(i, X, slice(0, M), slice(a0, a1))
+                att = rd(ATT, slice(0, M), slice(0, nq * hd))
+            xres = rd(X, slice(0, M), slice(a0, a1))
             return put(HR, slice(0, M), slice(a0, a1), xres + att @ lw.wo[a0:a1].T)
         if op == QS.OP_GATEUP:
-            hn = N.rms_norm(self.read(i, HR, slice(0, M), slice(0, H)), lw.ffn_norm, cfg.rms_eps)
+            hn = N.rms_norm(rd(HR, slice(0, M), slice(0, H)), lw.ffn_norm, cfg.rms_eps)
             val = N.silu(hn @ lw.wgate[a0:a1].T) * (hn @ lw.wup[a0:a1].T)
             return put(ACT, slice(0, M), slice(a0, a1), val)
         if op == QS.OP_DOWN:
-            a = self.read(i, ACT, slice(0, M), slice(0, cfg.ffn))
-            hres = self.read(i, HR, slice(0, M), slice(a0, a1))
+            a = rd(ACT, slice(0, M), slice(0, cfg.ffn))
+            hres = rd(HR, slice(0, M), slice(a0, a1))
             return put(XN, slice(0, M), slice(a0, a1), hres + a @ lw.wdown[a0:a1].T)
+        if op == QS.OP_LMHEAD:
+            XL, LG = QS.x_tensor(cfg.n_layers), QS.logits_tensor(cfg.n_layers)
+            val = N.lm_head(cfg, rd(XL, slice(0, M), slice(0, H)), self.model.final_norm, self.model.lm_head[a0:a1])
+
+            def keep():
+                self.logits.setdefault(step, np.full((M, cfg.vocab), np.nan))[:, a0:a1] = val
+            return put(LG, slice(0, M), slice(a0, a1), val, keep)
+        if op == QS.OP_ARGMAX:
+            b = a0
+            LG, NX = QS.logits_tensor(cfg.n_layers), QS.next_tensor(cfg.n_layers)
+            idx = int(N.argmax_lowest(rd(LG, slice(b, b + 1), slice(0, cfg.vocab)))[0])
+
+            def keep():
+                self.next.setdefault(step, np.full(M, -1, dtype=np.int64))[b] = idx
+            return put(NX, slice(b, b + 1), slice(0, 1), np.array([[float(idx)]]), keep)
         raise ValueError(f"opcode {op} has no decode tile body")
 
 
@@ -364,61 +462,74 @@ class SimResult:
     x_out: np.ndarray
     counters: np.ndarray
     state: DecodeState
-    order: List[int]
+    order: List[Tuple[int, int]]        # (step, instruction) in start order
 
 
 def simulate(model: N.Model, parts: Dict[str, bytes], K: np.ndarray, V: np.ndarray,
              ctx_lens: Sequence[int], workers: int, seed: int, tokens=None, x0=None,
-             reverse_ties: bool = False) -> SimResult:
-    """Event simulation of ``workers`` interpreters executing one decode step."""
+             reverse_ties: bool = False, steps: int = 1, feedback: bool = False) -> SimResult:
+    """Event simulation of ``workers`` interpreters executing ``steps`` decode
+    steps of the queue (more than one only for a loop queue): the queue's
+    instructions repeated ``steps`` times, sub-queue k holding positions
+    k, k + n_queues, ... of that sequence.  Step t of row b sits at position
+    ctx_lens[b] + t; with ``feedback`` each step after the first embeds the
+    previous step's argmax, otherwise ``tokens[t]``."""
     p = parse(parts)
-    st = DecodeState(model, p, K, V, ctx_lens, tokens, x0)
+    if steps > 1 and not p.loop:
+        raise ValueError("only a loop queue runs several steps in one launch")
+    st = DecodeState(model, p, K, V, ctx_lens, tokens, x0, feedback)
     rng = np.random.Generator(np.random.PCG64(seed))
     nq_ = max(1, p.n_queues)
     heads = [0] * nq_
     counters = np.zeros(p.n_barriers, dtype=np.int64)
     waits = [p.waits_of(i) for i in range(p.n_instr)]
+    pwaits = [p.waits_of(i, prev=True) for i in range(p.n_instr)]
+    total = steps * p.n_instr
 
     def pop(w):
         qi = w % nq_
-        # sub-queue qi holds instructions qi, qi + nq_, qi + 2 nq_, ...
-        idx = qi + heads[qi] * nq_
+        # sub-queue qi holds positions qi, qi + nq_, qi + 2 nq_, ... of the repeated queue
+        k = qi + heads[qi] * nq_
         heads[qi] += 1
-        return idx if idx < p.n_instr else None
+        return (k // p.n_instr, k % p.n_instr) if k < total else None
+
+    def ready(step, i):
+        return (all(counters[b] >= p.targets[b] * (step + 1) for b in waits[i]) and
+                all(counters[b] >= p.targets[b] * step for b in pwaits[i]))
 
     now = 0.0
-    events: List[Tuple[float, int, int, int]] = []   # (end time, tiebreak, worker, instr)
-    pending: Dict[Tuple[int, int], object] = {}
-    waiting: Dict[int, int] = {}
-    started: List[int] = []
+    events: List[Tuple[float, int, int, Tuple[int, int]]] = []   # (end time, tiebreak, worker, (step, instr))
+    pending: Dict[Tuple[int, Tuple[int, int]], object] = {}
+    waiting: Dict[int, Tuple[int, int]] = {}
+    started: List[Tuple[int, int]] = []
     seq = 0
     for w in range(workers):
-        i = pop(w)
-        if i is not None:
-            waiting[w] = i
+        job = pop(w)
+        if job is not None:
+            waiting[w] = job
     while True:
         # start every waiting worker whose barriers are complete (inputs read now)
         progressed = True
         while progressed:
             progressed = False
             for w in sorted(waiting, reverse=reverse_ties):
-                i = waiting[w]
-                if all(counters[b] >= p.targets[b] for b in waits[i]):
-                    pending[(w, i)] = st.body(i)
+                step, i = waiting[w]
+                if ready(step, i):
+                    pending[(w, (step, i))] = st.body(i, step)
                     del waiting[w]
-                    started.append(i)
+                    started.append((step, i))
                     seq += 1
-                    heapq.heappush(events, (now + float(rng.uniform(0.2, 2.0)), seq, w, i))
+                    heapq.heappush(events, (now + float(rng.uniform(0.2, 2.0)), seq, w, (step, i)))
                     progressed = True
         if not events:
             break
         # the earliest running instruction ends: outputs land, then its barrier is signalled
-        now, _, w, i = heapq.heappop(events)
-        pending.pop((w, i))()
-        counters[int(p.instr[i, 7])] += 1
+        now, _, w, job = heapq.heappop(events)
+        pending.pop((w, job))()
+        counters[int(p.instr[job[1], 7])] += 1
         nxt = pop(w)
         if nxt is not None:
             waiting[w] = nxt
-    deadlock = bool(waiting) or len(started) != p.n_instr
+    deadlock = bool(waiting) or len(started) != total
     x_out = st.t[QS.x_tensor(model.cfg.n_layers)]
     return SimResult(deadlock, st.bad_reads, x_out, counters, st, started)

@@ -35,16 +35,31 @@ What the pages leave open and this module fixes (the plainest reading):
   of every (row, KV head) in place of the attention output and merges them
   while staging its inputs; the attention-output tensor then has no tiles.
   The META word after bn records the flag.
+* With the plan's ``loop`` set (decode, persistent multi-step decode; the
+  lecture summary's practical implications keep the host out of the hot
+  loop), one queue describes one step of a run of T steps that one launch
+  executes in order.  After the layers come the LM-head tiles LMHEAD(v0, v1)
+  (64 vocabulary rows each, reading all of X_L and writing that tile of the
+  logits) and one ARGMAX(b) per row (reading its whole logits row and writing
+  the row's next token).  Every EMBED tile reads the next-token tensor of the
+  previous step: those waits form ranges of their own, after the same-step
+  ones, marked by bit 31 of the range count (PREV).  At step t a worker waits
+  until a same-step barrier's counter reaches target * (t + 1), a
+  previous-step one until target * t, so the counters are cleared once per
+  launch.  Buffers are reused across steps; that is safe because every
+  instruction of a step is an ancestor of some ARGMAX and every instruction
+  descends from some EMBED tile, which waits for all of the previous step's
+  ARGMAX (the checker verifies both).  The META flags word gets bit 1.
 
 Byte layout (little-endian), shared with the GPU library's C builder:
 
 META    u32 magic 'TMK1', version, mode, n_instr, n_barriers, n_wait_ranges, n_segments,
         n_queues, rows, ctx_max, n_splits, n_layers, tq, to, tf, td, kb, bm, bn, flags
-        (bit 0: split combines fused into the O-projection),
+        (bit 0: split combines fused into the O-projection; bit 1: multi-step loop queue),
         then n_segments x {u32 op, layer, first, count} (maximal runs of one op of one layer)
 INSTR   n_instr x 32 B {u16 op, u16 layer, u32 a0, a1, a2, wait_off, wait_cnt, signal, n_wait}
         (wait_off/wait_cnt index WAITS ranges; n_wait = barriers waited on in total)
-WAITS   n_wait_ranges x {u32 first barrier id, u32 count}
+WAITS   n_wait_ranges x {u32 first barrier id, u32 count} (count bit 31: previous-step barriers)
 TARGETS n_barriers x u32
 """
 from __future__ import annotations
@@ -60,8 +75,12 @@ MODE_DECODE, MODE_PREFILL = 0, 1
 
 OP_EMBED, OP_QKV, OP_ATTN, OP_COMBINE, OP_OPROJ, OP_GATEUP, OP_DOWN = 1, 2, 3, 4, 5, 6, 7
 OP_P_EMBED, OP_P_QKV, OP_P_ATTN, OP_P_OPROJ, OP_P_GATEUP, OP_P_DOWN = 8, 9, 10, 11, 12, 13
+OP_LMHEAD, OP_ARGMAX = 14, 15
 OP_NAMES = {1: "EMBED", 2: "QKV", 3: "ATTN", 4: "COMBINE", 5: "OPROJ", 6: "GATEUP", 7: "DOWN",
-            8: "P_EMBED", 9: "P_QKV", 10: "P_ATTN", 11: "P_OPROJ", 12: "P_GATEUP", 13: "P_DOWN"}
+            8: "P_EMBED", 9: "P_QKV", 10: "P_ATTN", 11: "P_OPROJ", 12: "P_GATEUP", 13: "P_DOWN",
+            14: "LMHEAD", 15: "ARGMAX"}
+LM_TILE = 64                  # vocabulary rows per LM-head tile of a loop queue
+PREV = 0x80000000             # range-count flag: barriers of the previous step
 
 # tensor kinds within a layer, in tensor order
 T_QKV, T_OPART, T_ATT, T_HRES, T_ACT, T_XNEXT = range(6)
@@ -83,6 +102,16 @@ def x_tensor(layer: int) -> int:
     return 0 if layer == 0 else tensor_order(layer - 1, T_XNEXT)
 
 
+def logits_tensor(n_layers: int) -> int:
+    """Tensor index of the logits [rows, V] of a loop queue (after the layers)."""
+    return 1 + 6 * n_layers
+
+
+def next_tensor(n_layers: int) -> int:
+    """Tensor index of the next tokens [rows, 1] of a loop queue."""
+    return 2 + 6 * n_layers
+
+
 Box = Tuple[int, int, int, int]        # row0, row1, col0, col1 (half-open)
 
 
@@ -95,6 +124,7 @@ class Instr:
     a2: int
     write: Tuple[int, Box]
     reads: List[Tuple[int, Box]]
+    prev_reads: List[Tuple[int, Box]] = field(default_factory=list)   # the previous step's tiles
     wait_off: int = 0
     wait_cnt: int = 0
     signal: int = 0
@@ -131,12 +161,14 @@ class Queue:
     def waits_bytes(self) -> bytes:
         return b"".join(struct.pack("<2I", f, c) for f, c in self.waits)
 
-    def wait_list(self, i: int) -> List[int]:
-        """Expanded barrier ids instruction i waits on, in wait-list order."""
+    def wait_list(self, i: int, prev: bool = False) -> List[int]:
+        """Expanded barrier ids instruction i waits on in its own step (or, with
+        ``prev``, in the previous step), in wait-list order."""
         ins = self.instrs[i]
         out: List[int] = []
         for f, c in self.waits[ins.wait_off: ins.wait_off + ins.wait_cnt]:
-            out.extend(range(f, f + c))
+            if bool(c & PREV) == prev:
+                out.extend(range(f, f + (c & ~PREV)))
         return out
 
     def targets_bytes(self) -> bytes:
@@ -173,6 +205,10 @@ def _check(model, plan, mode: int, rows: int, ctx_max: int) -> None:
         raise QueueError("n_queues out of range")
     if getattr(plan, "fuse_combine", 0) not in (0, 1):
         raise QueueError("fuse_combine must be 0 or 1")
+    if getattr(plan, "loop", 0) not in (0, 1):
+        raise QueueError("loop must be 0 or 1")
+    if getattr(plan, "loop", 0) and (mode != MODE_DECODE or not model.has_embed or not model.has_lm_head):
+        raise QueueError("a loop queue decodes a model with an embedding and an LM head")
     if mode == MODE_DECODE:
         if rows > MAX_DECODE_ROWS:
             raise QueueError("decode rows above the maximum")
@@ -194,9 +230,12 @@ def _decode_instrs(model, plan, M: int, NS: int) -> List[Instr]:
     nq, nkv, r = model.n_q_heads, model.n_kv_heads, model.group
     NQKV, NA = model.qkv_cols, model.attn_cols
     out: List[Instr] = []
+    loop = getattr(plan, "loop", 0)
+    NEXT, LOGITS = next_tensor(model.n_layers), logits_tensor(model.n_layers)
     if model.has_embed:
         for n0, n1 in _tiles(H, plan.td):
-            out.append(Instr(OP_EMBED, 0, n0, n1, 0, (0, (0, M, n0, n1)), []))
+            out.append(Instr(OP_EMBED, 0, n0, n1, 0, (0, (0, M, n0, n1)), [],
+                             [(NEXT, (0, M, 0, 1))] if loop else []))
     for l in range(model.n_layers):
         X = x_tensor(l)
         QKV, OP, ATT = tensor_order(l, T_QKV), tensor_order(l, T_OPART), tensor_order(l, T_ATT)
@@ -229,6 +268,13 @@ def _decode_instrs(model, plan, M: int, NS: int) -> List[Instr]:
         for n0, n1 in _tiles(H, plan.td):
             out.append(Instr(OP_DOWN, l, n0, n1, 0, (XN, (0, M, n0, n1)),
                              [(ACT, (0, M, 0, F)), (HR, (0, M, n0, n1))]))
+    if loop:
+        XL = x_tensor(model.n_layers)
+        for v0, v1 in _tiles(model.vocab, LM_TILE):
+            out.append(Instr(OP_LMHEAD, 0, v0, v1, 0, (LOGITS, (0, M, v0, v1)), [(XL, (0, M, 0, H))]))
+        for b in range(M):
+            out.append(Instr(OP_ARGMAX, 0, b, 0, 0, (NEXT, (b, b + 1, 0, 1)),
+                             [(LOGITS, (b, b + 1, 0, model.vocab))]))
     return out
 
 
@@ -275,6 +321,8 @@ def build(model, plan, mode: int, rows: int, ctx_max: int) -> Queue:
     instrs = (_decode_instrs(model, plan, rows, NS) if mode == MODE_DECODE
               else _prefill_instrs(model, plan, rows))
     flags = 1 if mode == MODE_DECODE and getattr(plan, "fuse_combine", 0) else 0
+    if getattr(plan, "loop", 0):
+        flags |= 2
     q = Queue(mode, rows, ctx_max, NS, model.n_layers,
               (plan.tq, plan.to, plan.tf, plan.td, plan.kb, plan.bm, plan.bn), plan.n_queues, flags)
 
@@ -292,10 +340,11 @@ def build(model, plan, mode: int, rows: int, ctx_max: int) -> Queue:
     for (t, box), bid in tile_id.items():
         by_tensor.setdefault(t, []).append((box, bid))
 
-    # wait lists: every written tile intersecting a read region
-    for ins in instrs:
+    # wait lists: every written tile intersecting a read region; the previous
+    # step's tiles (loop queues) form ranges of their own, flagged, after them
+    def wait_ranges(reads, flag):
         found = set()
-        for t, rbox in ins.reads:
+        for t, rbox in reads:
             for box, bid in by_tensor.get(t, []):
                 if _overlap(box, rbox):
                     found.add((t, box[2], box[0], bid))
@@ -306,8 +355,13 @@ def build(model, plan, mode: int, rows: int, ctx_max: int) -> Queue:
                 ranges[-1] = (ranges[-1][0], ranges[-1][1] + 1)
             else:
                 ranges.append((bid, 1))
-        ins.wait_off, ins.wait_cnt, ins.n_wait = len(q.waits), len(ranges), len(ws)
-        q.waits.extend(ranges)
+        return [(f, c | flag) for f, c in ranges], len(ws)
+
+    for ins in instrs:
+        same, n_same = wait_ranges(ins.reads, 0)
+        prev, n_prev = wait_ranges(ins.prev_reads, PREV)
+        ins.wait_off, ins.wait_cnt, ins.n_wait = len(q.waits), len(same) + len(prev), n_same + n_prev
+        q.waits.extend(same + prev)
     q.instrs = instrs
 
     # maximal runs of one (op, layer), for launching one kernel per op

@@ -2,6 +2,7 @@
 include/mk.h declares, and its host-side queue builder (an independent C++
 implementation) produces the reference builder's bytes exactly."""
 import ctypes
+import dataclasses
 import os
 import re
 
@@ -181,3 +182,21 @@ def test_queue_free_accepts_null_and_frees_once():
     q = T.mk_build_queue(T.make_config(wl.model), T.make_plan(wl.plan, T.MK_DECODE, 1, 129))
     q.close()
     q.close()
+
+
+@pytest.mark.parametrize("name,rows", [("llama1b_b1", 1), ("llama1b_b1", 3), ("llama8b_b1", 1)])
+def test_builder_bytes_loop_queue(name, rows):
+    """Loop queues (persistent multi-step decode): LM-head tiles, argmax rows and
+    the embedding tiles' previous-step waits agree byte for byte."""
+    wl = W.WORKLOADS[name]
+    plan = dataclasses.replace(wl.plan, loop=1)
+    got, ref = _both(wl.model, plan, QS.MODE_DECODE, rows, wl.run.ctx_max)
+    for part in ref:
+        assert got[part] == ref[part], part
+
+
+def test_builder_rejects_loop_without_lm_head():
+    wl = W.WORKLOADS["layer256_f32"]
+    with pytest.raises(T.MkError):
+        T.mk_build_queue(T.make_config(wl.model), T.make_plan(dataclasses.replace(wl.plan, loop=1), T.MK_DECODE,
+                                                              1, 129))

@@ -311,3 +311,154 @@ def test_attention_splits_are_split_major_and_rotated():
     assert att == [(0, 0, 0), (0, 1, 0), (1, 0, 0), (1, 1, 0), (2, 0, 0), (2, 1, 0),
                    (1, 0, 1), (1, 1, 1), (2, 0, 1), (2, 1, 1), (0, 0, 1), (0, 1, 1),
                    (2, 0, 2), (2, 1, 2), (0, 0, 2), (0, 1, 2), (1, 0, 2), (1, 1, 2)]
+
+
+# ----------------------------------------------------------------------------- loop queues (multi-step decode)
+
+TINY = W.ModelConfig("tiny-loop", n_layers=2, hidden=64, n_q_heads=4, n_kv_heads=2, head_dim=16, ffn=96,
+                     vocab=200, rms_eps=1e-5, rope_theta=1e4)
+TINY_PLAN = W.Plan(tq=16, to=16, tf=32, td=16, kb=8, loop=1)
+TINY_RUN = W.RunConfig(batch=2, ctx0=(9, 13), steps=3, ctx_max=20, seed=21)
+
+
+def _tiny(plan=TINY_PLAN):
+    q = QS.build(TINY, plan, QS.MODE_DECODE, TINY_RUN.batch, TINY_RUN.ctx_max)
+    model = N.prepare(TINY, W.gen.all_layer_weights(TINY, TINY_RUN.seed, 0.1),
+                      W.gen.global_weights(TINY, TINY_RUN.seed, 0.1))
+    K, V = W.gen.kv_cache(TINY, TINY_RUN)
+    return q, model, K, V, W.gen.decode_tokens(TINY, TINY_RUN)
+
+
+def test_loop_queue_shape():
+    """One step of a loop queue: the single-step queue, then ceil(V / 64) LM-head
+    tiles and one argmax per row; every embedding tile waits (flagged as the
+    previous step's) on all argmax barriers, in one range."""
+    import dataclasses
+    q, *_ = _tiny()
+    q1 = QS.build(TINY, dataclasses.replace(TINY_PLAN, loop=0), QS.MODE_DECODE, 2, 20)
+    nV = -(-TINY.vocab // QS.LM_TILE)
+    assert len(q.instrs) == len(q1.instrs) + nV + 2
+    assert [i.op for i in q.instrs[len(q1.instrs):]] == [QS.OP_LMHEAD] * nV + [QS.OP_ARGMAX] * 2
+    assert q.flags == 2 and q1.flags == 0
+    next_ids = [q.instrs[-2].signal, q.instrs[-1].signal]
+    for ins in q.instrs:
+        if ins.op == QS.OP_EMBED:
+            assert q.waits[ins.wait_off: ins.wait_off + ins.wait_cnt] == [(next_ids[0], 2 | QS.PREV)]
+            assert q.wait_list(ins_index := q.instrs.index(ins)) == []
+            assert q.wait_list(ins_index, prev=True) == next_ids
+    lm = [i for i in q.instrs if i.op == QS.OP_LMHEAD]
+    assert [(i.a0, i.a1) for i in lm] == [(0, 64), (64, 128), (128, 192), (192, 200)]
+    assert sum(q.targets) == len(q.instrs)
+    assert CK.static_check(TINY, q.parts()) == []
+
+
+def test_loop_queue_refused_without_embedding_or_lm_head():
+    import dataclasses
+    with pytest.raises(QS.QueueError):
+        QS.build(W.LLAMA_LAYER_F32, dataclasses.replace(SMALL.plan, loop=1), QS.MODE_DECODE, 1, 129)
+    with pytest.raises(QS.QueueError):
+        QS.build(TINY, TINY_PLAN, QS.MODE_PREFILL, 16, 20)
+
+
+def _with_ranges(parts, i, ranges):
+    """Replace instruction i's wait ranges (re-encoding every record's offsets)."""
+    p = CK.parse(parts)
+    recs = [list(r) for r in p.instr.tolist()]
+    out = []
+    for k, rec in enumerate(recs):
+        rr = ranges if k == i else [tuple(x) for x in p.ranges[rec[5]: rec[5] + rec[6]].tolist()]
+        rec[5], rec[6] = len(out), len(rr)
+        rec[8] = sum(c & ~QS.PREV for _, c in rr)
+        out.extend(rr)
+    meta = bytearray(parts["meta"])
+    struct.pack_into("<I", meta, 20, len(out))
+    return dict(parts, meta=bytes(meta), instr=b"".join(struct.pack("<HH7I", *r) for r in recs),
+                waits=b"".join(struct.pack("<2I", *r) for r in out))
+
+
+def test_loop_every_single_wait_deletion_is_caught():
+    """Exhaustive on the tiny loop queue, previous-step waits included."""
+    q, *_ = _tiny()
+    parts = q.parts()
+    total = 0
+    for i in range(len(q.instrs)):
+        for prev in (False, True):
+            wl = q.wait_list(i, prev=prev)
+            other = [(f, c) for f, c in q.waits[q.instrs[i].wait_off: q.instrs[i].wait_off + q.instrs[i].wait_cnt]
+                     if bool(c & QS.PREV) != prev]
+            for k in range(len(wl)):
+                keep = wl[:k] + wl[k + 1:]
+                rr = [(b, 1 | (QS.PREV if prev else 0)) for b in keep]
+                mutant = _with_ranges(parts, i, (other + rr) if prev else (rr + other))
+                assert CK.static_check(TINY, mutant, max_errors=1), (i, prev, k)
+                total += 1
+    assert total == sum(i.n_wait for i in q.instrs)
+
+
+def test_loop_previous_step_flag_is_checked():
+    """An embedding tile whose argmax waits lose the previous-step flag waits on
+    producers later in the queue: refused (it could never start)."""
+    q, *_ = _tiny()
+    i = next(k for k, ins in enumerate(q.instrs) if ins.op == QS.OP_EMBED)
+    f, c = q.waits[q.instrs[i].wait_off]
+    mutant = _with_ranges(q.parts(), i, [(f, c & ~QS.PREV)])
+    assert any("not earlier" in e for e in CK.static_check(TINY, mutant))
+
+
+@pytest.mark.parametrize("workers", [1, 2, 7, 64])
+def test_loop_simulation_teacher_forced_matches_oracle(workers):
+    """Three steps in one run, any schedule: every step's logits equal the
+    oracle's teacher-forced step (float64, same tile bodies) and are identical
+    across schedules; counters end at 3 x targets; the cache holds all steps."""
+    q, model, K, V, tokens = _tiny()
+    parts = q.parts()
+    Kr, Vr = K.copy(), V.copy()
+    ref = [N.decode_step(model, Kr, Vr, [p + t for p in TINY_RUN.ctx0], tokens=tokens[t]) for t in range(3)]
+    base = None
+    for seed in range(25 if workers > 1 else 1):
+        Ks, Vs = K.copy(), V.copy()
+        res = CK.simulate(model, parts, Ks, Vs, TINY_RUN.ctx0, workers, seed=seed, tokens=tokens[:3],
+                          steps=3, reverse_ties=bool(seed & 1))
+        assert not res.deadlock and res.bad_reads == []
+        assert np.array_equal(res.counters, 3 * np.array(q.targets))
+        got = [res.state.logits[t] for t in range(3)]
+        for t in range(3):
+            assert N.max_rel_err_rows(got[t], ref[t].logits) < 1e-12
+            assert np.array_equal(res.state.next[t], N.argmax_lowest(got[t]))
+        if base is None:
+            base = got
+        assert all(np.array_equal(a, b) for a, b in zip(base, got))
+        assert np.array_equal(Ks, Kr) and np.array_equal(Vs, Vr)
+
+
+def test_loop_simulation_greedy_feedback():
+    """With the argmax fed back, step t + 1 embeds step t's argmax: the same as
+    teacher-forcing with that chain of tokens."""
+    q, model, K, V, tokens = _tiny()
+    res = CK.simulate(model, q.parts(), K.copy(), V.copy(), TINY_RUN.ctx0, 7, seed=5, tokens=tokens[:1],
+                      steps=3, feedback=True)
+    assert not res.deadlock and res.bad_reads == []
+    chain = [tokens[0], res.state.next[0], res.state.next[1]]
+    Kr, Vr = K.copy(), V.copy()
+    for t in range(3):
+        tr = N.decode_step(model, Kr, Vr, [p + t for p in TINY_RUN.ctx0], tokens=chain[t])
+        assert N.max_rel_err_rows(res.state.logits[t], tr.logits) < 1e-12
+        assert np.array_equal(res.state.next[t], N.argmax_lowest(tr.logits))
+
+
+def test_loop_simulation_detects_missing_previous_step_wait():
+    """Embedding tiles that do not wait for the previous step's argmax: some
+    schedule overwrites X_0 while the previous step still reads it, or embeds
+    a token that is not yet there."""
+    q, model, K, V, tokens = _tiny()
+    parts = q.parts()
+    for i, ins in enumerate(q.instrs):
+        if ins.op == QS.OP_EMBED:
+            parts = _with_ranges(parts, i, [])
+    assert CK.static_check(TINY, parts) != []
+    seen = False
+    for seed in range(20):
+        res = CK.simulate(model, parts, K.copy(), V.copy(), TINY_RUN.ctx0, 64, seed=seed, tokens=tokens[:1],
+                          steps=3, feedback=True)
+        seen |= bool(res.bad_reads)
+    assert seen

@@ -54,8 +54,11 @@ struct Builder {
   const mk_config& c;
   const mk_plan& p;
 
+  // `prev_runs` (loop queues): barriers of the previous step, stored as their
+  // own ranges after the same-step ones, with kPrevStep set in the count.
   void emit(uint16_t op, uint32_t layer, uint32_t a0, uint32_t a1, uint32_t a2, uint32_t signal,
-            const std::vector<std::pair<uint32_t, uint32_t>>& runs) {
+            const std::vector<std::pair<uint32_t, uint32_t>>& runs,
+            const std::vector<std::pair<uint32_t, uint32_t>>& prev_runs = {}) {
     Instr in{};
     in.op = op;
     in.layer = static_cast<uint16_t>(layer);
@@ -63,9 +66,12 @@ struct Builder {
     in.signal = signal;
     WaitBuilder wb{&q->waits, static_cast<uint32_t>(q->waits.size())};
     for (auto& r : runs) wb.add_run(r.first, r.second);
+    WaitBuilder wp{&q->waits, static_cast<uint32_t>(q->waits.size())};
+    for (auto& r : prev_runs) wp.add_run(r.first, r.second);
+    for (size_t k = wp.first_range; k < q->waits.size(); ++k) q->waits[k].count |= kPrevStep;
     in.wait_off = wb.first_range;
     in.wait_cnt = static_cast<uint32_t>(q->waits.size()) - wb.first_range;
-    in.n_wait = wb.n;
+    in.n_wait = wb.n + wp.n;
     q->instr.push_back(in);
   }
 
@@ -91,12 +97,21 @@ struct Builder {
     auto x_exists = [&](uint32_t l) { return l > 0 || c.has_embed; };
     auto x_id = [&](uint32_t l, uint32_t n) { return l == 0 ? n : xn_id(l - 1, n); };
 
-    const uint32_t n_bar = L0 + c.n_layers * per_layer;
+    // loop queues: LM-head tiles and one argmax per row after the layers
+    const bool loop = p.loop != 0;
+    const uint32_t nV = loop ? cdiv(c.vocab, kLmTile) : 0, nN = loop ? M : 0;
+    const uint32_t tail = L0 + c.n_layers * per_layer;
+    auto logits_id = [&](uint32_t j) { return tail + j; };
+    auto next_id = [&](uint32_t b) { return tail + nV + b; };
+    const uint32_t n_bar = tail + nV + nN;
     q->targets.assign(n_bar, 1);
 
     if (c.has_embed)
-      for (uint32_t n = 0; n < nX; ++n)
-        emit(OP_EMBED, 0, n * p.td, std::min((n + 1) * p.td, H), 0, n, {});
+      for (uint32_t n = 0; n < nX; ++n) {
+        std::vector<std::pair<uint32_t, uint32_t>> prev;
+        if (loop) prev.push_back({next_id(0), M});
+        emit(OP_EMBED, 0, n * p.td, std::min((n + 1) * p.td, H), 0, n, {}, prev);
+      }
     for (uint32_t l = 0; l < (uint32_t)c.n_layers; ++l) {
       for (uint32_t n = 0; n < nQ; ++n) {
         std::vector<std::pair<uint32_t, uint32_t>> w;
@@ -155,6 +170,12 @@ struct Builder {
         emit(OP_DOWN, l, n0, n1, 0, xn_id(l, n),
              {{hres_id(l, n0 / p.to), (n1 - 1) / p.to - n0 / p.to + 1}, {act_id(l, 0), nF}});
       }
+    }
+    if (loop) {
+      for (uint32_t j = 0; j < nV; ++j)
+        emit(OP_LMHEAD, 0, j * kLmTile, std::min((j + 1) * kLmTile, (uint32_t)c.vocab), 0, logits_id(j),
+             {{x_id(c.n_layers, 0), nX}});
+      for (uint32_t b = 0; b < M; ++b) emit(OP_ARGMAX, 0, b, 0, 0, next_id(b), {{logits_id(0), nV}});
     }
   }
 
@@ -237,6 +258,9 @@ const char* validate(const mk_config& c, const mk_plan& p) {
   if (p.rows <= 0 || p.ctx_max <= 0) return "rows and ctx_max must be positive";
   if (p.n_queues < 1 || p.n_queues > kMaxQueues) return "n_queues out of range";
   if (p.fuse_combine != 0 && p.fuse_combine != 1) return "fuse_combine must be 0 or 1";
+  if (p.loop != 0 && p.loop != 1) return "loop must be 0 or 1";
+  if (p.loop && (p.mode != MK_DECODE || !c.has_embed || !c.has_lm_head))
+    return "a loop queue decodes a model with an embedding and an LM head";
   if (p.mode == MK_DECODE) {
     if (p.rows > kMaxDecodeRows) return "decode rows above the maximum";
     if (std::min({p.tq, p.to, p.tf, p.td, p.kb}) <= 0) return "tile sizes must be positive";
@@ -320,7 +344,7 @@ mk_status mk_queue_export(const mk_queue* q, int32_t part, void* host_dst, size_
                         (uint32_t)p.ctx_max, q->n_splits, (uint32_t)q->cfg.n_layers,
                         (uint32_t)p.tq, (uint32_t)p.to, (uint32_t)p.tf, (uint32_t)p.td,
                         (uint32_t)p.kb, (uint32_t)p.bm, (uint32_t)p.bn,
-                        (p.mode == MK_DECODE && p.fuse_combine) ? 1u : 0u};
+                        ((p.mode == MK_DECODE && p.fuse_combine) ? 1u : 0u) | (p.loop ? 2u : 0u)};
       std::memcpy(d, h, sizeof(h));
       if (!q->segments.empty()) std::memcpy(d + 80, q->segments.data(), 16 * q->segments.size());
       break;

@@ -10,8 +10,11 @@ namespace mk {
 enum Op : uint16_t {
   OP_EMBED = 1, OP_QKV = 2, OP_ATTN = 3, OP_COMBINE = 4, OP_OPROJ = 5, OP_GATEUP = 6, OP_DOWN = 7,
   OP_P_EMBED = 8, OP_P_QKV = 9, OP_P_ATTN = 10, OP_P_OPROJ = 11, OP_P_GATEUP = 12, OP_P_DOWN = 13,
-  OP_COUNT = 14
+  OP_LMHEAD = 14, OP_ARGMAX = 15,
+  OP_COUNT = 16
 };
+constexpr uint32_t kLmTile = 64;            // vocabulary rows per LM-head tile of a loop queue
+constexpr uint32_t kPrevStep = 0x80000000u; // wait-range count flag: the previous step's barriers
 
 constexpr uint32_t kMagic = 0x314B4D54u;   // "TMK1"
 constexpr uint32_t kVersion = 1;

@@ -67,6 +67,9 @@ class Plan:
     prefill_queues: sub-queues of the prefill queue (0: n_queues).  Prefill
     instructions are long, so shared sub-queues (workers pop dynamically) cost
     little and balance the causal attention tiles' unequal lengths.
+    loop: decode only; 1 builds a queue for persistent multi-step decode: each
+    step ends with LM-head tiles (64 vocabulary rows each) and one argmax per
+    row, and the next step's embedding tiles wait on the previous step's argmax.
     """
     tq: int = 16
     to: int = 16
@@ -78,10 +81,11 @@ class Plan:
     n_queues: int = 1
     fuse_combine: int = 0
     prefill_queues: int = 0
+    loop: int = 0
 
     def for_prefill(self) -> "Plan":
         """The plan of the prefill queue (its own sub-queue count)."""
-        return dataclasses.replace(self, n_queues=self.prefill_queues or self.n_queues)
+        return dataclasses.replace(self, n_queues=self.prefill_queues or self.n_queues, loop=0)
 
 
 @dataclass(frozen=True)
