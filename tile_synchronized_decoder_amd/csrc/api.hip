@@ -104,8 +104,8 @@ struct Layout {
   size_t X, QKV, OPART, ATT, HRES, ACT, LMV, LMI, CTR, HEADS, ERR, total;
   size_t sX, sQKV, sOP, sATT, sHRES, sACT;   // per-layer strides in floats
   int lm_blocks;
-  // prefill only: bf16 GEMM operands and per-row sums of squares (after ERR)
-  size_t XB, XSS, HB, HSS, ATTB, ACTB;
+  // prefill only: bf16 GEMM operands (hi and lo parts) and per-row sums of squares (after ERR)
+  size_t XB, XSS, HB, HSS, ATTB, ACTB, XBL, HBL, ATTBL, ACTBL;
   size_t sXB, sXSS, sATTB, sACTB;            // per-layer strides in elements
 };
 
@@ -136,8 +136,8 @@ Layout layout(const mk_queue* q) {
   o.ERR = off; off += 256;
   if (q->plan.mode == MK_PREFILL) {
     // bf16 copies of the GEMM activation operands, written by their producer
-    // tiles (with the consumer's RMSNorm gain folded in for X and HRES), and
-    // sums of squares of X / HRES rows per 128-column tile
+    // tiles (with the consumer's RMSNorm gain folded in for X and HRES) as hi
+    // and lo parts, and sums of squares of X / HRES rows per 128-column tile
     const size_t nss = (c.hidden + 127) / 128;
     o.sXB = up256(M * c.hidden * 2) / 2;
     o.sXSS = up256(M * nss * 4) / 4;
@@ -149,6 +149,10 @@ Layout layout(const mk_queue* q) {
     o.HSS = off; off += L * o.sXSS * 4;
     o.ATTB = off; off += L * o.sATTB * 2;
     o.ACTB = off; off += L * o.sACTB * 2;
+    o.XBL = off; off += L * o.sXB * 2;
+    o.HBL = off; off += L * o.sXB * 2;
+    o.ATTBL = off; off += L * o.sATTB * 2;
+    o.ACTBL = off; off += L * o.sACTB * 2;
   }
   o.total = off;
   return o;
@@ -172,11 +176,16 @@ int nb_bucket(int rows) {
 
 struct LdsLayout { uint32_t res, x, ring, uni, bytes; };
 
-// Bytes of the prefill tile region: the larger of a GEMM tile (two stages of a
-// 128 x 64 activation tile, three of a 256 x 64 weight tile, row statistics)
-// and an attention tile (Q, a 64-key K and V^T block, scores, probabilities).
-constexpr uint32_t kPrefillGemmBytes = 3 * 128 * 128 + 3 * 256 * 128 + (256 + 128) * 4;
-constexpr uint32_t kPrefillAttnBytes = 2 * 128 * 128 + 2 * (2 * 64 * 128) + 128 * 64 * 2 + 128 * 64 * 4 + 128 * 64 * 2 + 3 * 128 * 4;
+// Bytes of the prefill tile region: the largest of a single-matrix GEMM tile
+// (three stages of a 128 x 64 activation tile as hi and lo parts and of a
+// 128 x 64 weight tile, row statistics), the gate/up tile (two stages of the
+// activation pair and of a 256 x 64 weight tile) and an attention tile over 64
+// query rows (Q as hi and lo, two 64-key K blocks, a V^T block, scores, the
+// probabilities as hi and lo, row statistics).
+constexpr uint32_t kPrefillGemmBytes = 3 * (2 * 128 * 128 + 128 * 128) + (256 + 128) * 4;
+constexpr uint32_t kPrefillGateUpBytes = 2 * (2 * 128 * 128 + 256 * 128) + (256 + 128) * 4;
+constexpr uint32_t kPrefillAttnBytes = 2 * (2 * 64 * 128) + 2 * (2 * 64 * 128) + 128 * 64 * 2 + 64 * 64 * 4 +
+                                       2 * 64 * 64 * 2 + 3 * 64 * 4;
 
 // Dynamic shared memory of one workgroup, in floats: header (index, norm
 // factors), GEMV results, residual rows, then one region shared by the weight
@@ -186,7 +195,7 @@ LdsLayout lds_layout(const mk_config& c, const mk_plan& p) {
   LdsLayout o{};
   if (p.mode == MK_PREFILL) {
     // prefill tiles use the header and the tile region only
-    o.ring = (std::max(kPrefillGemmBytes, kPrefillAttnBytes) + 255) & ~255u;
+    o.ring = (std::max({kPrefillGemmBytes, kPrefillGateUpBytes, kPrefillAttnBytes}) + 255) & ~255u;
     o.uni = o.ring / 4;
     o.bytes = 4 * (16 + 32 + NWAVE * 32) + o.ring;
     return o;
@@ -250,6 +259,8 @@ void fill_args(const mk_queue* q, const void* d_queue, const mk_weights* w, cons
     a.XB = reinterpret_cast<uint16_t*>(ws + o.XB); a.XSS = reinterpret_cast<float*>(ws + o.XSS);
     a.HB = reinterpret_cast<uint16_t*>(ws + o.HB); a.HSS = reinterpret_cast<float*>(ws + o.HSS);
     a.ATTB = reinterpret_cast<uint16_t*>(ws + o.ATTB); a.ACTB = reinterpret_cast<uint16_t*>(ws + o.ACTB);
+    a.XBL = reinterpret_cast<uint16_t*>(ws + o.XBL); a.HBL = reinterpret_cast<uint16_t*>(ws + o.HBL);
+    a.ATTBL = reinterpret_cast<uint16_t*>(ws + o.ATTBL); a.ACTBL = reinterpret_cast<uint16_t*>(ws + o.ACTBL);
     a.sXB = o.sXB; a.sXSS = o.sXSS; a.sATTB = o.sATTB; a.sACTB = o.sACTB;
   }
   a.counters = reinterpret_cast<uint32_t*>(ws + o.CTR); a.heads = reinterpret_cast<uint32_t*>(ws + o.HEADS);

@@ -98,8 +98,10 @@ struct Args {
   int fuse_combine;              // decode queue without split combines: O-projection merges the partials
   uint32_t delay_seed;           // race check: seeded stall before each tile's stores (0: off)
   // prefill: bf16 GEMM operands (X and HRES with the consumer's RMSNorm gain
-  // applied), per-row sums of squares of X / HRES per 128-column tile
+  // applied), each as a pair: hi = bf16(y) and lo = bf16(y - hi), per-row sums
+  // of squares of X / HRES per 128-column tile
   uint16_t* XB; uint16_t* HB; uint16_t* ATTB; uint16_t* ACTB;
+  uint16_t* XBL; uint16_t* HBL; uint16_t* ATTBL; uint16_t* ACTBL;
   float* XSS; float* HSS;
   size_t sXB, sXSS, sATTB, sACTB;              // per-layer strides (elements)
 };
