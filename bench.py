@@ -11,7 +11,8 @@ Llama-3-1B-shaped batch-1 workload runs after it and is reported under
 synthetic and are resident in HBM before timing.
 
 Prints one JSON line: the megakernel's tokens/s as `value`, the kernel-per-op
-modes (eager, and the library's HIP-graph mode) beside it, the dominant
+modes (eager, and the library's HIP-graph mode) and the persistent multi-step
+mode (all timed steps in one launch, LM head and argmax inside it) beside it, the dominant
 kernel's roofline (algorithmic bytes per launch over its event-timed average
 duration, against 8 TB/s) and the CPU oracle run on float32 weights, timed on a
 bounded sample on the host.
@@ -128,6 +129,7 @@ def run_workload(wl, args, modes, with_prefill=True):
     from tile_synchronized_decoder_amd import device as D
     import workloads as W
 
+    import dataclasses
     m, r = wl.model, wl.run
     K_steps = min(args.steps, r.steps)
     t0 = time.time()
@@ -226,6 +228,38 @@ def run_workload(wl, args, modes, with_prefill=True):
     mode_of = {"mega": T.MK_MEGAKERNEL, "kpo": T.MK_KERNEL_PER_OP, "kpo_graph": T.MK_KERNEL_PER_OP_GRAPH}
     results = {}
     for name in modes:
+        if name == "loop":
+            # persistent multi-step decode: all K timed steps in one launch of a loop queue,
+            # the LM head and argmax inside it (teacher-forced with the same token ids)
+            if not (m.has_embed and m.has_lm_head and m.dtype == "bf16"):
+                continue
+            ql = T.mk_build_queue(T.make_config(m), T.make_plan(dataclasses.replace(wl.plan, loop=1), T.MK_DECODE,
+                                                                r.batch, r.ctx_max))
+            dql, wsl = D.upload_queue(ql), D.workspace(ql)
+            lg_all = torch.empty((K_steps, B, m.vocab), dtype=torch.float32, device="cuda")
+            nx_all = torch.empty((K_steps, B), dtype=torch.int32, device="cuda")
+            toks, ctx0 = tok_all[:K_steps].contiguous(), ctx_all[0].clone()
+
+            def run_loop(k):
+                T.mk_decode_loop(ql, dql, dm.w, dkv.kv, toks, ctx0, B, k, 0, wsl, lg_all, nx_all)
+
+            run_loop(min(max(args.warmup, 1), K_steps))
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            w0 = time.perf_counter()
+            e0.record(stream)
+            run_loop(K_steps)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - w0
+            total_ms = e0.elapsed_time(e1)
+            err = T.mk_device_error(ql, wsl)
+            assert err.code == 0, f"device error {err.code} in the multi-step loop"
+            results[name] = {"ms_per_step": total_ms / K_steps, "tokens_per_s": B * K_steps / (total_ms / 1e3),
+                             "steps_per_launch": K_steps, "host_wall_tokens_per_s": B * K_steps / wall}
+            log(f"[bench] {wl.name} loop: {total_ms / K_steps:.4f} ms/step ({K_steps} steps in one launch)")
+            del wsl, lg_all
+            continue
         mode = mode_of[name]
         for t in range(args.warmup):
             step(t, mode)
@@ -276,6 +310,8 @@ def run_workload(wl, args, modes, with_prefill=True):
                            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                            "algorithmic_bytes_per_launch": mbytes}
     kpos = [v["ms_per_step"] for k, v in results.items() if k.startswith("kpo")]
+    if "loop" in results and "mega" in results:
+        out["loop_speedup_vs_mega"] = round(mega["ms_per_step"] / results["loop"]["ms_per_step"], 4)
     if kpos and "mega" in results:
         out["speedup"] = round(min(kpos) / mega["ms_per_step"], 4)
     out["host"] = (raw_layers, raw_global, Kh, Vh)
@@ -304,7 +340,7 @@ def main():
                     help="decode GEMV weight issue: 0 or 1 pipelined (default), 2 compiler-ordered")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
-    ap.add_argument("--modes", default="mega,kpo,kpo_graph")
+    ap.add_argument("--modes", default="mega,kpo,kpo_graph,loop")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the modes, copy MIB MiB device to device three times: a plain copy "
                          "kernel of known size that hardware byte counters can be scaled by")
@@ -354,6 +390,8 @@ def main():
         line["prefill"] = head["prefill"]
     if "speedup" in head:
         line["megakernel_speedup_vs_best_kpo"] = head["speedup"]
+    if "loop_speedup_vs_mega" in head:
+        line["loop_speedup_vs_mega"] = head["loop_speedup_vs_mega"]
     host = head.pop("host")
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
@@ -366,7 +404,8 @@ def main():
         extra[name] = {"describe": ex["workload"].describe, "steps": ex["steps"],
                        "modes": _rounded(ex["results"]), "roofline": ex.get("roofline"),
                        "step_hbm_frac": round(ex["step_hbm_gbs"] / HBM_PEAK_GBS, 4),
-                       "megakernel_speedup_vs_best_kpo": ex.get("speedup")}
+                       "megakernel_speedup_vs_best_kpo": ex.get("speedup"),
+                       "loop_speedup_vs_mega": ex.get("loop_speedup_vs_mega")}
     if extra:
         line["extra"] = extra
     print(json.dumps(line), flush=True)

@@ -213,12 +213,35 @@ typedef struct mk_kv {
  * three modes give bitwise equal results.
  * Errors: MK_EINVAL (mismatched queue / sizes / null pointers), MK_ENOTSUP
  * (tiles that do not fit a workgroup's shared memory; megakernel workgroups
- * that cannot all be resident), MK_ELAUNCH. */
+ * that cannot all be resident), MK_ELAUNCH.  A loop queue is refused (it runs
+ * through mk_decode_loop). */
 mk_status mk_decode_step(const mk_queue* q, const void* d_queue, const mk_weights* w,
                          const mk_kv* kv, const int32_t* d_tokens, const float* d_x0,
                          const int32_t* d_ctx_lens, int32_t batch, void* d_workspace,
                          size_t workspace_nbytes, float* d_logits, int32_t* d_next,
                          int32_t exec_mode, hipStream_t stream);
+
+/* Persistent multi-step decode: `steps` decode steps of a loop queue
+ * (mk_plan.loop = 1) in one launch.  Follows the lecture summary's Practical
+ * implications (the host stays out of the hot loop; the forward pass
+ * re-executes on the device): the interpreter runs the queue `steps` times,
+ * each step's LM-head tiles and per-row argmax inside the megakernel, and the
+ * next step's embedding tiles wait (tile-granular) on the previous step's
+ * argmax.  Counters are cleared once, before the launch.
+ * Step t of row b sits at position d_ctx_lens[b] + t (the caller's d_ctx_lens
+ * is not changed; a position outside the cache is a device error).
+ * feedback 0 (teacher-forced): d_tokens is [steps][batch], step t embeds
+ * d_tokens[t]; feedback 1 (greedy): d_tokens is [batch], step 0 embeds it and
+ * step t > 0 embeds the argmax of step t - 1.  d_next [steps][batch] (required)
+ * receives every step's argmax (lowest index on ties); d_logits [steps][batch][V]
+ * fp32 (nullable) every step's logits.  The final hidden rows of the last step
+ * are the workspace tensor MK_T_X of layer n_layers.  bf16 models only.
+ * Errors: MK_EINVAL (not a loop queue, sizes, null pointers), MK_ENOTSUP
+ * (fp32 model; workgroups that cannot all be resident), MK_ELAUNCH. */
+mk_status mk_decode_loop(const mk_queue* q, const void* d_queue, const mk_weights* w, const mk_kv* kv,
+                         const int32_t* d_tokens, const int32_t* d_ctx_lens, int32_t batch, int32_t steps,
+                         int32_t feedback, void* d_workspace, size_t workspace_nbytes, float* d_logits,
+                         int32_t* d_next, hipStream_t stream);
 
 /* mk_decode_step without a workspace argument, for callers that cannot
  * allocate device memory or pass one (code under HIP graph capture, tight

@@ -112,6 +112,15 @@ def mk_decode_step_static(q: Queue, d_queue, w: mk_weights, kv: mk_kv, tokens, x
                                             _ptr(error), exec_mode, _stream(stream)), "mk_decode_step_static")
 
 
+def mk_decode_loop(q: Queue, d_queue, w: mk_weights, kv: mk_kv, tokens, ctx_lens, batch: int, steps: int,
+                   feedback: int, workspace, logits, next_tokens, stream=None) -> None:
+    """`steps` decode steps of a loop queue in one launch (see include/mk.h)."""
+    _L.check(_L.lib().mk_decode_loop(q.handle, _ptr(d_queue), C.byref(w), C.byref(kv), _ptr(tokens),
+                                     _ptr(ctx_lens), batch, steps, feedback, _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _ptr(logits),
+                                     _ptr(next_tokens), _stream(stream)), "mk_decode_loop")
+
+
 def mk_lm_head(q: Queue, w: mk_weights, workspace, logits, next_tokens, stream=None) -> None:
     _L.check(_L.lib().mk_lm_head(q.handle, C.byref(w), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _ptr(logits),

@@ -74,6 +74,7 @@ def lib() -> C.CDLL:
                                  I32, VP]),
         "mk_decode_step_static": (I32, [VP, VP, P(mk_weights), P(mk_kv), VP, VP, VP, I32, VP, VP, VP, I32,
                                         VP]),
+        "mk_decode_loop": (I32, [VP, VP, P(mk_weights), P(mk_kv), VP, VP, I32, I32, I32, VP, SZ, VP, VP, VP]),
         "mk_lm_head": (I32, [VP, P(mk_weights), VP, SZ, VP, VP, VP]),
         "mk_prefill": (I32, [VP, VP, P(mk_weights), P(mk_kv), VP, I32, I32, VP, SZ, VP, VP, I32, VP]),
         "mk_device_error": (I32, [VP, VP, P(mk_dev_error), VP]),
@@ -91,7 +92,7 @@ def lib() -> C.CDLL:
 
 
 EXPORTED = ["mk_build_queue", "mk_queue_nbytes", "mk_queue_export", "mk_queue_free",
-            "mk_workspace_nbytes", "mk_workspace_offset", "mk_decode_step", "mk_decode_step_static",
+            "mk_workspace_nbytes", "mk_workspace_offset", "mk_decode_step", "mk_decode_step_static", "mk_decode_loop",
             "mk_lm_head", "mk_prefill",
             "mk_device_error", "mk_set_option", "mk_get_option", "mk_status_str", "mk_last_error"]
 

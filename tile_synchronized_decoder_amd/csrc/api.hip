@@ -435,6 +435,7 @@ mk_status decode_impl(const mk_queue* q, const void* d_queue, const mk_weights* 
                       int32_t exec_mode, hipStream_t stream) {
   if (!q || !d_queue || !w || !kv || !d_ctx_lens || !d_workspace) FAIL(MK_EINVAL, "null argument");
   if (q->plan.mode != MK_DECODE) FAIL(MK_EINVAL, "queue was not built for decode");
+  if (q->plan.loop) FAIL(MK_EINVAL, "a loop queue runs through mk_decode_loop");
   const mk_config& c = q->cfg;
   if (mk_status st = check_shapes(c)) return st;
   if (batch != q->plan.rows) FAIL(MK_EINVAL, "batch %d differs from the queue's rows %d", batch, q->plan.rows);
@@ -587,6 +588,51 @@ mk_status mk_decode_step_static(const mk_queue* q, const void* d_queue, const mk
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) FAIL(MK_ELAUNCH, "copy of the error record: %s", hipGetErrorString(e));
   }
+  return MK_OK;
+}
+
+mk_status mk_decode_loop(const mk_queue* q, const void* d_queue, const mk_weights* w, const mk_kv* kv,
+                         const int32_t* d_tokens, const int32_t* d_ctx_lens, int32_t batch, int32_t steps,
+                         int32_t feedback, void* d_workspace, size_t workspace_nbytes, float* d_logits,
+                         int32_t* d_next, hipStream_t stream) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!q || !d_queue || !w || !kv || !d_tokens || !d_ctx_lens || !d_workspace || !d_next)
+    FAIL(MK_EINVAL, "null argument");
+  if (q->plan.mode != MK_DECODE || !q->plan.loop) FAIL(MK_EINVAL, "the queue was not built as a loop queue");
+  const mk_config& c = q->cfg;
+  if (mk_status st = check_shapes(c)) return st;
+  if (c.dtype != MK_BF16) FAIL(MK_ENOTSUP, "multi-step decode is built for bf16 models");
+  if (batch != q->plan.rows) FAIL(MK_EINVAL, "batch %d differs from the queue's rows %d", batch, q->plan.rows);
+  if (steps < 1) FAIL(MK_EINVAL, "steps must be positive");
+  if (feedback != 0 && feedback != 1) FAIL(MK_EINVAL, "feedback must be 0 or 1");
+  if ((uint64_t)steps * q->instr.size() > 0xFFFFFFFEull) FAIL(MK_EINVAL, "too many steps for one launch");
+  if (lds_layout(q).bytes > kMaxLds) FAIL(MK_ENOTSUP, "tiles need more shared memory than a workgroup has");
+  const Layout o = layout(q);
+  if (workspace_nbytes < o.total) FAIL(MK_EINVAL, "workspace of %zu bytes, need %zu", workspace_nbytes, o.total);
+  if (!w->wqkv || !w->wo || !w->wgate || !w->wup || !w->wdown || !w->attn_norm || !w->ffn_norm || !w->embed ||
+      !w->lm_head || !w->final_norm || !kv->k || !kv->v)
+    FAIL(MK_EINVAL, "missing weights or cache");
+  if (c.qk_norm && (!w->q_norm || !w->k_norm)) FAIL(MK_EINVAL, "missing QK-norm gains");
+  if (kv->rows != 0 && kv->rows != q->plan.rows) FAIL(MK_EINVAL, "decode cache rows must equal the batch");
+  if (num_cus() * g_opt.workers_per_cu < q->plan.n_queues) FAIL(MK_EINVAL, "fewer workers than sub-queues");
+
+  Args a{};
+  fill_args(q, d_queue, w, kv, d_workspace, o, a);
+  a.tokens = d_tokens; a.ctx_lens = d_ctx_lens;
+  a.logits = d_logits; a.next = nullptr; a.next_all = d_next;
+  a.steps = steps; a.feedback = feedback;
+  a.spin_limit = g_opt.spin_limit;
+  a.gemv_pipe = g_opt.gemv_pipe;
+  a.delay_seed = g_opt.delay_seed;
+  a.trace = (g_opt.trace && g_opt.trace_bytes >= 64 * q->instr.size()) ? g_opt.trace : nullptr;
+  const Table t = pick_table(c.dtype, a.M);
+  if (!t.loop) FAIL(MK_ENOTSUP, "no multi-step interpreter for this model");
+  if (mk_status st = prep_status(t.prep(a, kLoopMode, g_opt.workers_per_cu))) return st;
+  hipLaunchKernelGGL(reset_kernel, dim3((a.n_barriers + 255) / 256 + 1), dim3(256), 0, stream, a.counters,
+                     a.n_barriers, a.heads, a.n_queues, a.err);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = t.loop(a, num_cus() * g_opt.workers_per_cu, stream);
+  if (e != hipSuccess) FAIL(MK_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
   return MK_OK;
 }
 

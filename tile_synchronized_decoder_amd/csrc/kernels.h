@@ -97,6 +97,11 @@ struct Args {
   int gemv_pipe;                 // decode GEMV weight issue: 0, 1 pipelined; 2 compiler-ordered
   int fuse_combine;              // decode queue without split combines: O-projection merges the partials
   uint32_t delay_seed;           // race check: seeded stall before each tile's stores (0: off)
+  // persistent multi-step decode (loop queues): steps of the run, 1 = embed the
+  // previous step's argmax (else tokens[step][row]), the argmax of every step
+  // [steps][rows] (logits, when given, are [steps][rows][V])
+  int steps, feedback;
+  int* next_all;
   // prefill: bf16 GEMM operands (X and HRES with the consumer's RMSNorm gain
   // applied), each as a pair: hi = bf16(y) and lo = bf16(y - hi), per-row sums
   // of squares of X / HRES per 128-column tile
@@ -119,13 +124,19 @@ __device__ __forceinline__ KArgs& kernel_args() {
   return *(KArgs*)p;
 }
 
+// An instruction as the op bodies see it: the 32-byte record plus the step of
+// a multi-step run it belongs to (0 outside mk_decode_loop).
+struct Task : Instr {
+  uint32_t step = 0;
+};
+
 // The 32-byte instruction record, read once and kept in scalar registers.
-__device__ __forceinline__ Instr load_instr(KArgs& a, uint32_t idx) {
+__device__ __forceinline__ Task load_instr(KArgs& a, uint32_t idx) {
   const uint32_t* p = reinterpret_cast<const uint32_t*>(a.instr + idx);
   uint32_t w[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) w[k] = __builtin_amdgcn_readfirstlane(__builtin_nontemporal_load(p + k));
-  Instr in;
+  Task in;
   in.op = (uint16_t)(w[0] & 0xFFFF); in.layer = (uint16_t)(w[0] >> 16);
   in.a0 = w[1]; in.a1 = w[2]; in.a2 = w[3]; in.wait_off = w[4]; in.wait_cnt = w[5]; in.signal = w[6]; in.n_wait = w[7];
   return in;
@@ -274,6 +285,13 @@ __device__ __forceinline__ float4 ld_cg4(const float* p) {          // 16-byte a
                      __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
 }
 
+__device__ __forceinline__ int ld_cg_i32(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_cg_i32(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Block until every barrier in the instruction's wait list reaches its target.
 // Threads poll disjoint subsets.  Returns false if the wait gave up (timeout or
 // another worker aborted).
@@ -287,12 +305,17 @@ __device__ __forceinline__ bool poll_counter(KArgs& a, const uint32_t* ctr, uint
   return true;
 }
 
-__device__ __forceinline__ bool wait_tiles(KArgs& a, const Instr in, uint32_t idx) {
+// Counters are cleared once per launch: in step t of a multi-step run a barrier
+// of the same step is complete at target * (t + 1) signals, one of the previous
+// step (a wait range whose count has bit 31 set) at target * t.
+__device__ __forceinline__ bool wait_tiles(KArgs& a, const Task in, uint32_t idx) {
   bool ok = true;
   for (uint32_t k = 0; k < in.wait_cnt; ++k) {
     const Range rg = a.ranges[in.wait_off + k];
-    for (uint32_t j = threadIdx.x; j < rg.count && ok; j += NT)
-      ok = poll_counter(a, a.counters + rg.first + j, a.targets[rg.first + j], idx, rg.first + j);
+    const uint32_t cnt = rg.count & 0x7FFFFFFFu;
+    const uint32_t mul = (rg.count & 0x80000000u) ? in.step : in.step + 1;
+    for (uint32_t j = threadIdx.x; j < cnt && ok; j += NT)
+      ok = poll_counter(a, a.counters + rg.first + j, a.targets[rg.first + j] * mul, idx, rg.first + j);
   }
   const bool all = __syncthreads_and(ok) != 0;
   asm volatile("" ::: "memory");                 // no tile load may move above the wait
@@ -314,7 +337,7 @@ __device__ __forceinline__ void inject_delay(KArgs& a, uint32_t idx) {
 
 // Publish this instruction's tile: every wave waits for its coherent stores to
 // be acknowledged, then one thread bumps the tile's counter.
-__device__ __forceinline__ void signal_tile(KArgs& a, const Instr in) {
+__device__ __forceinline__ void signal_tile(KArgs& a, const Task in) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) __hip_atomic_fetch_add(a.counters + in.signal, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -576,7 +599,7 @@ __device__ __attribute__((noinline)) void stage_att_fused(KArgs& a, Smem& s, int
 // Returns false when the wait gave up.
 template <typename WT, int NB, int RPW, bool PIPE>
 __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, PIPE>& g, const float* x, int nb,
-                     const float* gain, bool norm, bool mega, bool fused, const Instr in, uint32_t idx,
+                     const float* gain, bool norm, bool mega, bool fused, const Task in, uint32_t idx,
                      const float* resid, int resid_ld) {
   using G = Gemv<WT, NB, RPW, PIPE>;
   using E = Elem<WT>;
@@ -718,7 +741,7 @@ template <int NB> constexpr int rpw_for() { return NB >= 32 ? 2 : 4; }
 // The weight rows a GEMV instruction streams (op, layer, columns [a0, a1)),
 // or false for other ops.
 template <typename WT, int NB, int RPW, bool PIPE>
-__device__ __forceinline__ bool gemv_of(KArgs& a, const Instr in, Gemv<WT, NB, RPW, PIPE>& g) {
+__device__ __forceinline__ bool gemv_of(KArgs& a, const Task in, Gemv<WT, NB, RPW, PIPE>& g) {
   const int l = in.layer, n0 = in.a0, n = in.a1 - in.a0;
   switch (in.op) {
     case mk::OP_QKV: {
@@ -742,6 +765,11 @@ __device__ __forceinline__ bool gemv_of(KArgs& a, const Instr in, Gemv<WT, NB, R
       g = {W, W, n, n0, n, a.F};
       return true;
     }
+    case mk::OP_LMHEAD: {                               // loop queues: LM-head rows [a0, a1)
+      const WT* W = static_cast<const WT*>(a.lm_head);
+      g = {W, W, n, n0, n, a.H};
+      return true;
+    }
     default:
       return false;
   }
@@ -751,7 +779,7 @@ __device__ __forceinline__ bool gemv_of(KArgs& a, const Instr in, Gemv<WT, NB, R
 // (silu(RMSNorm(H) Wg^T) * (RMSNorm(H) Wu^T)) and DOWN (HRES_l + ACT_l Wd^T),
 // each over output columns [a0, a1).
 template <typename WT, int NB, int RPW, bool PIPE>
-__device__ __forceinline__ void op_gemv_rpw(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega, bool fused) {
+__device__ __forceinline__ void op_gemv_rpw(KArgs& a, Smem& s, const Task in, uint32_t idx, bool mega, bool fused) {
   using G = Gemv<WT, NB, RPW, PIPE>;
   const int l = in.layer, n0 = in.a0, n = in.a1 - in.a0;
   G g{};
@@ -767,6 +795,8 @@ __device__ __forceinline__ void op_gemv_rpw(KArgs& a, Smem& s, const Instr in, u
     x = fused ? nullptr : a.ATT + l * a.sATT; resid = a.X + l * a.sX + n0; ld = a.H;
   } else if (op == mk::OP_GATEUP) {
     x = a.HRES + l * a.sHRES; gain = a.ffn_norm + (size_t)l * a.H;
+  } else if (op == mk::OP_LMHEAD) {
+    x = a.lm_x; gain = a.final_norm;
   } else {
     x = a.ACT + l * a.sACT; resid = a.HRES + l * a.sHRES + n0; ld = a.H;
   }
@@ -780,11 +810,25 @@ __device__ __forceinline__ void op_gemv_rpw(KArgs& a, Smem& s, const Instr in, u
       } else if (op == mk::OP_GATEUP) {
         const float gt = s.res[row * NB + b], up = s.res[(n + row) * NB + b];
         st_cg(a.ACT + l * a.sACT + (size_t)b * a.F + n0 + row, gt / (1.0f + expf(-gt)) * up);
+      } else if (op == mk::OP_LMHEAD) {
+        if (a.logits) a.logits[((size_t)in.step * a.M + b) * a.V + n0 + row] = s.res[row * NB + b];
       } else {
         float* out = op == mk::OP_OPROJ ? a.HRES + l * a.sHRES : a.X + (l + 1) * a.sX;
         st_cg(out + (size_t)b * a.H + n0 + row, s.resid[row * NB + b] + s.res[row * NB + b]);
       }
     }
+  }
+  if (op == mk::OP_LMHEAD && threadIdx.x < a.M) {
+    // the tile's (largest logit, lowest index among equals) of each row, for the argmax
+    const int b = threadIdx.x;
+    float best = s.res[b];
+    int bi = 0;
+    for (int row = 1; row < n; ++row) {
+      const float v = s.res[row * NB + b];
+      if (v > best) { best = v; bi = row; }
+    }
+    st_cg(a.lm_val + (size_t)b * a.lm_blocks + n0 / LM_ROWS, best);
+    st_cg_i32(a.lm_idx + (size_t)b * a.lm_blocks + n0 / LM_ROWS, n0 + bi);
   }
   if (mega) signal_tile(a, in);
 }
@@ -794,7 +838,7 @@ template <typename WT, int NB>
 // split partials itself).  The per-op kernels decide it at compile time (a
 // separate O-projection kernel for fused queues), so the other per-op GEMV
 // kernels carry none of its code or registers.
-__device__ __forceinline__ void op_gemv(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega, bool fused) {
+__device__ __forceinline__ void op_gemv(KArgs& a, Smem& s, const Task in, uint32_t idx, bool mega, bool fused) {
   constexpr int RPW = rpw_for<NB>();
   const int rows = (in.op == mk::OP_GATEUP ? 2 : 1) * (int)(in.a1 - in.a0);
   // Weight lines are issued so that the compiler does not serialise the ring
@@ -818,13 +862,19 @@ __device__ __forceinline__ void op_gemv(KArgs& a, Smem& s, const Instr in, uint3
 
 // EMBED(n0, n1): X_0[b, n0:n1] = E[token_b, n0:n1]
 template <typename WT>
-__device__ __forceinline__ void op_embed(KArgs& a, const Instr in, uint32_t idx, bool mega) {
+__device__ __forceinline__ void op_embed(KArgs& a, const Task in, uint32_t idx, bool mega) {
   const int n0 = in.a0, n = in.a1 - in.a0;
   const WT* E = static_cast<const WT*>(a.embed);
+  // loop queues: wait for the previous step's argmax (its tokens, and the end of
+  // every reader of this tile in that step); single-step queues wait on nothing
+  if (mega && in.wait_cnt && !wait_tiles(a, in, idx)) return;
   inject_delay(a, idx);
   for (int e = threadIdx.x; e < n * a.M; e += NT) {
     const int b = e / n, c = e - b * n;
-    const int tok = a.tokens[b];
+    // a multi-step run with feedback embeds the previous step's argmax (written
+    // in this launch by another workgroup: a device-coherent load)
+    const int tok = (a.feedback && in.step > 0) ? ld_cg_i32(a.next_all + (size_t)(in.step - 1) * a.M + b)
+                                                : a.tokens[(size_t)in.step * a.M + b];
     if (tok < 0 || tok >= a.V) {                 // out-of-range id: report, emit zeros
       if (c == 0) record_error(a, ERR_TOKEN, 0xFFFFFFFFu, (uint32_t)b, (uint32_t)tok, (uint32_t)a.V);
       st_cg(a.X + (size_t)b * a.H + n0 + c, 0.f);
@@ -865,7 +915,7 @@ __device__ __forceinline__ float across_groups(float v) {
 // groups and waves merge once at the end.  The cached rows of the first 8
 // rounds are loaded before the tile waits.
 template <typename KT, int HD>
-__device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
+__device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Task in, uint32_t idx, bool mega) {
   using E = Elem<KT>;
   constexpr int HALF = HD / 2;
   constexpr int NROT = ((ATT_MAX_R + 1) * HALF + NT - 1) / NT;
@@ -879,7 +929,7 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Instr in, uint3
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int kk = lane / LPK, ds = lane % LPK;       // key of the lane in a round, its 8-dim slice
-  const int pos_in = a.ctx_lens[b];
+  const int pos_in = a.ctx_lens[b] + (int)in.step;      // step t of a run sits t positions on
   // a position outside the cache is reported and the row treated as having no keys
   const bool bad_pos = pos_in < 0 || pos_in >= a.ctx_max;
   if (bad_pos && t == 0 && sp == 0) record_error(a, ERR_CONTEXT, idx, (uint32_t)b, (uint32_t)pos_in, (uint32_t)a.ctx_max);
@@ -1172,7 +1222,7 @@ __device__ __forceinline__ void combine_rows(const float* src, float* out, int r
 
 // COMBINE(b, g): merge the NS split partials of row b, group g into ATT_l.
 template <int HD>
-__device__ __forceinline__ void op_combine(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
+__device__ __forceinline__ void op_combine(KArgs& a, Smem& s, const Task in, uint32_t idx, bool mega) {
   const int l = in.layer, b = in.a0, g = in.a1, r = a.r;
   if (mega && !wait_tiles(a, in, idx)) return;
   inject_delay(a, idx);
@@ -1203,16 +1253,54 @@ __device__ __forceinline__ void op_combine(KArgs& a, Smem& s, const Instr in, ui
 }
 
 
+// ARGMAX(b) (loop queues): the largest logit of row b over the LM-head tiles'
+// partial maxima (lowest index among equals), stored as the step's next token.
+__device__ __forceinline__ void op_argmax(KArgs& a, Smem& s, const Task in, uint32_t idx, bool mega) {
+  if (mega && !wait_tiles(a, in, idx)) return;
+  const int b = in.a0, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  float best = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  for (int k = t; k < a.lm_blocks; k += NT) {
+    const float v = ld_cg(a.lm_val + (size_t)b * a.lm_blocks + k);
+    const int i = ld_cg_i32(a.lm_idx + (size_t)b * a.lm_blocks + k);
+    if (v > best || (v == best && i < bi)) { best = v; bi = i; }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+  }
+  if (lane == 0) { s.ssw[wave] = best; s.ssw[NWAVE + wave] = __int_as_float(bi); }
+  __syncthreads();
+  inject_delay(a, idx);
+  if (t == 0) {
+    for (int w = 1; w < NWAVE; ++w) {
+      const float v = s.ssw[w];
+      const int i = __float_as_int(s.ssw[NWAVE + w]);
+      if (v > best || (v == best && i < bi)) { best = v; bi = i; }
+    }
+    st_cg_i32(a.next_all + (size_t)in.step * a.M + b, bi);
+  }
+  if (mega) signal_tile(a, in);
+}
+
 // ----------------------------------------------------------------------------- dispatch
 
 // Per-op launch code of the O-projection of a queue with fused split combines
 // (never an opcode of the queue: the records say OP_OPROJ).
 constexpr int KPO_OPROJ_FUSED = 100;
 
-template <typename WT, int NB>
-__device__ __forceinline__ void run_instr(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega, int only_op) {
+template <typename WT, int NB, bool LOOP = false>
+__device__ __forceinline__ void run_instr(KArgs& a, Smem& s, const Task in, uint32_t idx, bool mega, int only_op) {
   const int op = only_op ? only_op : in.op;
   switch (op) {
+    case mk::OP_LMHEAD:                                  // loop queues only
+      if constexpr (LOOP) op_gemv<WT, NB>(a, s, in, idx, mega, false);
+      break;
+    case mk::OP_ARGMAX:
+      if constexpr (LOOP) op_argmax(a, s, in, idx, mega);
+      break;
     case mk::OP_EMBED: op_embed<WT>(a, in, idx, mega); break;
     case mk::OP_QKV: case mk::OP_OPROJ: case mk::OP_GATEUP: case mk::OP_DOWN:
       // one GEMV body for the four ops (the interpreter's code size matters for
@@ -1241,14 +1329,24 @@ __device__ __forceinline__ void run_instr(KArgs& a, Smem& s, const Instr in, uin
 // per worker there is nothing to pop.  Sub-queue q holds
 // instructions q, q + n_queues, ... in queue order; every sub-queue is a
 // subsequence of one topological order, so popping ahead cannot deadlock.
-template <typename WT, int NB>
+// LOOP (persistent multi-step decode, loop queues): the sequence is the queue
+// repeated a.steps times, position k being instruction k mod n_instr of step
+// k / n_instr; the repeated queue is still in topological order (a step's
+// embedding waits only on the previous step's argmax), so the same argument
+// holds and the host launches once for all steps.
+template <typename WT, int NB, bool LOOP = false>
 __global__ __launch_bounds__(NT) void mk_interp(Args args) {
   Smem s = make_smem(kernel_args());
   const uint32_t nq = args.n_queues;
   const uint32_t qi = blockIdx.x % nq;
-  // One sub-queue per worker: the worker runs instructions qi, qi + nq, ... and
+  const uint64_t total = LOOP ? (uint64_t)args.n_instr * (uint64_t)args.steps : args.n_instr;
+  // One sub-queue per worker: the worker runs positions qi, qi + nq, ... and
   // needs no pops; each instruction's record is loaded one iteration ahead.
   const bool fixed = nq == gridDim.x;
+  auto instr_of = [&](uint64_t k) -> uint32_t {
+    if constexpr (LOOP) return (uint32_t)(k % args.n_instr);
+    else return (uint32_t)k;
+  };
   uint32_t k_next = 0;                           // thread 0 (shared sub-queues): popped position
   uint32_t abort_seen = 0;                       // thread 0: error word, read one instruction ago
   uint32_t word = 0;                             // lanes 0..7 (fixed): next record, in flight
@@ -1256,17 +1354,17 @@ __global__ __launch_bounds__(NT) void mk_interp(Args args) {
     KArgs& a = kernel_args();
     k_next = __hip_atomic_fetch_add(a.heads + qi * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (fixed && threadIdx.x < 8 && qi < args.n_instr) {
+  if (fixed && threadIdx.x < 8 && qi < total) {
     KArgs& a = kernel_args();
-    word = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.instr + qi) + threadIdx.x);
+    word = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.instr + instr_of(qi)) + threadIdx.x);
   }
   for (uint32_t it = 0;; ++it) {
     KArgs& a = kernel_args();
-    const uint64_t fi = (uint64_t)qi + (uint64_t)it * nq;         // fixed order: this iteration's instruction
+    const uint64_t fi = (uint64_t)qi + (uint64_t)it * nq;         // fixed order: this iteration's position
     if (threadIdx.x == 0) {
-      const uint64_t i = fixed ? fi : (uint64_t)k_next * nq + qi;
-      const bool go = i < a.n_instr && abort_seen == 0;
-      s.idx[0] = go ? (uint32_t)i : 0xFFFFFFFFu;
+      const uint64_t k = fixed ? fi : (uint64_t)k_next * nq + qi;
+      const bool go = k < total && abort_seen == 0;
+      s.idx[0] = go ? (uint32_t)k : 0xFFFFFFFFu;
       if (go && !fixed)
         k_next = __hip_atomic_fetch_add(a.heads + qi * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       // a worker that recorded an error stops the others at their next pop; the
@@ -1276,11 +1374,12 @@ __global__ __launch_bounds__(NT) void mk_interp(Args args) {
     if (fixed && threadIdx.x < 8) {
       s.idx[8 + threadIdx.x] = word;             // this instruction's record, loaded an iteration ago
       const uint64_t j = fi + nq;
-      word = j < a.n_instr ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.instr + j) + threadIdx.x) : 0u;
+      word = j < total ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.instr + instr_of(j)) + threadIdx.x)
+                       : 0u;
     }
     __syncthreads();
-    const uint32_t idx = __builtin_amdgcn_readfirstlane(s.idx[0]);   // uniform: keep the record in SGPRs
-    Instr in;
+    const uint32_t pos = __builtin_amdgcn_readfirstlane(s.idx[0]);   // uniform: keep the record in SGPRs
+    Task in;
     if (fixed) {
       uint32_t w[8];
 #pragma unroll
@@ -1289,11 +1388,13 @@ __global__ __launch_bounds__(NT) void mk_interp(Args args) {
       in.a0 = w[1]; in.a1 = w[2]; in.a2 = w[3]; in.wait_off = w[4]; in.wait_cnt = w[5]; in.signal = w[6]; in.n_wait = w[7];
     }
     __syncthreads();
-    if (idx == 0xFFFFFFFFu) break;
+    if (pos == 0xFFFFFFFFu) break;
+    const uint32_t idx = instr_of(pos);
     if (!fixed) in = load_instr(a, idx);
+    if constexpr (LOOP) in.step = pos / a.n_instr;
     unsigned long long t0 = 0;
     if (a.trace) t0 = wall_clock64();
-    run_instr<WT, NB>(a, s, in, idx, true, 0);
+    run_instr<WT, NB, LOOP>(a, s, in, idx, true, 0);
     if (a.trace && threadIdx.x == 0) {
       unsigned long long* rec = a.trace + TRACE_WORDS * (size_t)idx;
       uint32_t xcc;
@@ -1312,7 +1413,7 @@ __global__ __launch_bounds__(NT) void kpo_kernel(Args args, uint32_t first) {
   KArgs& a = kernel_args();
   Smem s = make_smem(a);
   const uint32_t idx = first + blockIdx.x;
-  const Instr in = load_instr(a, idx);
+  const Task in = load_instr(a, idx);
   if (in.op != (OP == KPO_OPROJ_FUSED ? mk::OP_OPROJ : OP)) {
     if (threadIdx.x == 0) record_error(a, ERR_OPCODE, idx, in.op, 0, 0);
     return;
@@ -1332,7 +1433,7 @@ __global__ __launch_bounds__(NT) void lm_head_kernel(Args args) {
   const int n = min(ROWS, a.V - v0);
   const WT* W = static_cast<const WT*>(a.lm_head);
   Gemv<WT, NB, RPW, (NB > 1)> g{W, W, n, v0, n, a.H};
-  Instr none{};
+  Task none{};
   gemv<WT, NB, RPW, (NB > 1)>(a, s, g, a.lm_x, a.M, a.final_norm, true, false, false, none, 0, nullptr, 0);
   for (int e = threadIdx.x; e < n * a.M; e += NT) {
     const int row = e / a.M, b = e - row * a.M;
@@ -1514,7 +1615,7 @@ inline hipError_t check_resident(K kernel, uint32_t lds_bytes, int per_cu) {
 #ifdef MK_PREFILL_UNIT
 #include "prefill.h"
 
-__device__ __forceinline__ void run_prefill_instr(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega, int only_op) {
+__device__ __forceinline__ void run_prefill_instr(KArgs& a, Smem& s, const Task in, uint32_t idx, bool mega, int only_op) {
   const int op = only_op ? only_op : in.op;
   switch (op) {
     case mk::OP_P_EMBED: op_p_embed(a, in, idx, mega); break;
@@ -1568,7 +1669,7 @@ __global__ __launch_bounds__(NT) void kpo_prefill(Args args, uint32_t first) {
   KArgs& a = kernel_args();
   Smem s = make_smem(a);
   const uint32_t idx = first + blockIdx.x;
-  const Instr in = load_instr(a, idx);
+  const Task in = load_instr(a, idx);
   if (in.op != (OP == KPO_OPROJ_FUSED ? mk::OP_OPROJ : OP)) {
     if (threadIdx.x == 0) record_error(a, ERR_OPCODE, idx, in.op, 0, 0);
     return;
@@ -1613,8 +1714,14 @@ struct PrefillLaunch {
 
 #endif  // MK_PREFILL_UNIT
 
+// Execution mode of the preparation step for the multi-step interpreter.
+constexpr int kLoopMode = 100;
+
 template <typename WT, int NB>
 struct Launch {
+  // The multi-step interpreter is built for bf16 models (those with an
+  // embedding and an LM head here); for fp32 ones the entry point refuses.
+  static constexpr bool kHasLoop = sizeof(WT) == 2;
   // Everything that can refuse a call, before anything is enqueued: the shared
   // memory opt-in of every kernel the call may launch and, for the megakernel,
   // that all of its workgroups can be resident at once.
@@ -1623,6 +1730,14 @@ struct Launch {
       static uint32_t granted[kMaxDevices] = {};
       hipError_t e = allow_lds(mk_interp<WT, NB>, a.lds_bytes, granted);
       return e == hipSuccess ? check_resident(mk_interp<WT, NB>, a.lds_bytes, per_cu) : e;
+    }
+    if (exec_mode == kLoopMode) {
+      if constexpr (kHasLoop) {
+        static uint32_t granted[kMaxDevices] = {};
+        hipError_t e = allow_lds(mk_interp<WT, NB, true>, a.lds_bytes, granted);
+        return e == hipSuccess ? check_resident(mk_interp<WT, NB, true>, a.lds_bytes, per_cu) : e;
+      }
+      return hipErrorInvalidValue;
     }
     static uint32_t granted[KPO_OPROJ_FUSED + 1][kMaxDevices] = {};
     hipError_t e = hipSuccess;
@@ -1635,6 +1750,14 @@ struct Launch {
   static hipError_t mega(const Args& a, int grid, hipStream_t st) {
     hipLaunchKernelGGL((mk_interp<WT, NB>), dim3(grid), dim3(NT), a.lds_bytes, st, a);
     return hipGetLastError();
+  }
+  // Persistent multi-step decode: the interpreter over a loop queue, a.steps times.
+  static hipError_t loop(const Args& a, int grid, hipStream_t st) {
+    if constexpr (kHasLoop) {
+      hipLaunchKernelGGL((mk_interp<WT, NB, true>), dim3(grid), dim3(NT), a.lds_bytes, st, a);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
   }
   static hipError_t kpo(const Args& a, uint32_t op, uint32_t first, uint32_t count, hipStream_t st) {
     if (op == mk::OP_OPROJ && a.fuse_combine) op = KPO_OPROJ_FUSED;
@@ -1674,6 +1797,7 @@ struct Launch {
 struct Table {
   hipError_t (*prep)(const Args&, int exec_mode, int per_cu);
   hipError_t (*mega)(const Args&, int grid, hipStream_t);
+  hipError_t (*loop)(const Args&, int grid, hipStream_t);
   hipError_t (*kpo)(const Args&, uint32_t op, uint32_t first, uint32_t count, hipStream_t);
   hipError_t (*prep_lm)(const Args&);
   hipError_t (*lm)(const Args&, hipStream_t);

@@ -205,7 +205,7 @@ __device__ __forceinline__ float* p_row_stats(Smem& s, bool two_mats) {
 // others pass their one accumulator twice and never touch acc_up.
 template <bool TWO>
 __device__ __forceinline__ bool p_gemm(KArgs& a, Smem& s, const PGemm& g, PAcc& acc, PAcc& acc_up, bool mega,
-                                       const Instr in, uint32_t idx) {
+                                       const Task in, uint32_t idx) {
   constexpr int S = TWO ? 2 : 3;                         // stages (matches p_stages)
   constexpr int D = S - 1;                               // K steps of lookahead
   const int t = threadIdx.x, lane = t & 63;
@@ -381,7 +381,7 @@ __device__ __forceinline__ bool p_block_live(KArgs& a, int m) { return m * PBM <
 // the rows' sums of squares per 128 columns (the QKV tiles' operands).  Each thread moves 8
 // consecutive columns: one 16-byte load of bf16, four 8-byte device-coherent
 // stores of fp32 and two of bf16; 16 consecutive threads cover 128 columns.
-__device__ __forceinline__ void op_p_embed(KArgs& a, const Instr in, uint32_t idx, bool mega) {
+__device__ __forceinline__ void op_p_embed(KArgs& a, const Task in, uint32_t idx, bool mega) {
   const int m = in.a0;
   const uint16_t* E = static_cast<const uint16_t*>(a.embed);
   const float* gain = a.attn_norm;                        // layer 0
@@ -450,7 +450,7 @@ constexpr int CT_QLD = PBN + 4;
 
 // P_QKV(m, n0, n1): one head's columns of QKV for row block m, with the
 // RMSNorm row scale, QK-norm and RoPE (q, k), the KV-cache write (k, v).
-__device__ __forceinline__ void op_p_qkv(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
+__device__ __forceinline__ void op_p_qkv(KArgs& a, Smem& s, const Task in, uint32_t idx, bool mega) {
   const int l = in.layer, m = in.a0, n0 = in.a1;
   if (!p_block_live(a, m)) {
     if (mega && wait_tiles(a, in, idx)) signal_tile(a, in);
@@ -539,7 +539,7 @@ __device__ __forceinline__ void op_p_qkv(KArgs& a, Smem& s, const Instr in, uint
 }
 
 // P_OPROJ / P_DOWN: out = residual + A W^T (A = ATT_l / ACT_l; residual = X_l / HRES_l).
-__device__ __forceinline__ void op_p_resid(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega, bool down) {
+__device__ __forceinline__ void op_p_resid(KArgs& a, Smem& s, const Task in, uint32_t idx, bool mega, bool down) {
   const int l = in.layer, m = in.a0, n0 = in.a1;
   if (!p_block_live(a, m)) {
     if (mega && wait_tiles(a, in, idx)) signal_tile(a, in);
@@ -577,7 +577,7 @@ __device__ __forceinline__ void op_p_resid(KArgs& a, Smem& s, const Instr in, ui
 }
 
 // P_GATEUP: ACT = silu(RMSNorm(H) Wg^T) * (RMSNorm(H) Wu^T) for 128 columns.
-__device__ __forceinline__ void op_p_gateup(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
+__device__ __forceinline__ void op_p_gateup(KArgs& a, Smem& s, const Task in, uint32_t idx, bool mega) {
   const int l = in.layer, m = in.a0, n0 = in.a1;
   if (!p_block_live(a, m)) {
     if (mega && wait_tiles(a, in, idx)) signal_tile(a, in);
@@ -623,7 +623,7 @@ __device__ __forceinline__ void op_p_gateup(KArgs& a, Smem& s, const Instr in, u
 // are bf16 values, so S = (Q_hi + Q_lo) K^T and O = (P_hi + P_lo) V are taken
 // as two products each.
 constexpr int PAH = 64;                                   // query rows per half
-__device__ __forceinline__ void op_p_attn(KArgs& a, Smem& s, const Instr in, uint32_t idx, bool mega) {
+__device__ __forceinline__ void op_p_attn(KArgs& a, Smem& s, const Task in, uint32_t idx, bool mega) {
   constexpr int HD = PBN;
   const int l = in.layer, m = in.a0, h = in.a1;
   const int g = h / a.r;
