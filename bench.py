@@ -11,8 +11,10 @@ Llama-3-1B-shaped batch-1 workload runs after it and is reported under
 synthetic and are resident in HBM before timing.
 
 Prints one JSON line: the megakernel's tokens/s as `value`, the kernel-per-op
-modes (eager, and the library's HIP-graph mode) and the persistent multi-step
-mode (all timed steps in one launch, LM head and argmax inside it) beside it, the dominant
+modes (eager, and the library's HIP-graph mode), the multi-stream mode (one
+kernel per segment on S streams, synchronised on tiles) and the persistent
+multi-step mode (all timed steps in one launch, LM head and argmax inside it)
+beside it, the dominant
 kernel's roofline (algorithmic bytes per launch over its event-timed average
 duration, against 8 TB/s) and the CPU oracle run on float32 weights, timed on a
 bounded sample on the host.
@@ -260,7 +262,12 @@ def run_workload(wl, args, modes, with_prefill=True):
             log(f"[bench] {wl.name} loop: {total_ms / K_steps:.4f} ms/step ({K_steps} steps in one launch)")
             del wsl, lg_all
             continue
-        mode = mode_of[name]
+        if name.startswith("ms"):
+            # multi-stream mode: one kernel per segment on `streams` internal streams, tile waits
+            T.mk_set_option(T.MK_OPT_STREAMS, int(name[2:]))
+            mode = T.MK_MULTI_STREAM
+        else:
+            mode = mode_of[name]
         for t in range(args.warmup):
             step(t, mode)
         torch.cuda.synchronize()
@@ -314,6 +321,9 @@ def run_workload(wl, args, modes, with_prefill=True):
         out["loop_speedup_vs_mega"] = round(mega["ms_per_step"] / results["loop"]["ms_per_step"], 4)
     if kpos and "mega" in results:
         out["speedup"] = round(min(kpos) / mega["ms_per_step"], 4)
+    mss = [v["ms_per_step"] for k, v in results.items() if k.startswith("ms")]
+    if mss and "mega" in results:
+        out["ms_speedup"] = round(min(mss) / mega["ms_per_step"], 4)
     out["host"] = (raw_layers, raw_global, Kh, Vh)
     del dm, dkv, ws
     torch.cuda.empty_cache()
@@ -340,7 +350,8 @@ def main():
                     help="decode GEMV weight issue: 0 or 1 pipelined (default), 2 compiler-ordered")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
-    ap.add_argument("--modes", default="mega,kpo,kpo_graph,loop")
+    ap.add_argument("--modes", default="mega,kpo,kpo_graph,loop,ms2,ms4",
+                    help="mega, kpo, kpo_graph, loop, and msS: the multi-stream mode on S streams")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the modes, copy MIB MiB device to device three times: a plain copy "
                          "kernel of known size that hardware byte counters can be scaled by")
@@ -392,6 +403,8 @@ def main():
         line["megakernel_speedup_vs_best_kpo"] = head["speedup"]
     if "loop_speedup_vs_mega" in head:
         line["loop_speedup_vs_mega"] = head["loop_speedup_vs_mega"]
+    if "ms_speedup" in head:
+        line["megakernel_speedup_vs_best_multi_stream"] = head["ms_speedup"]
     host = head.pop("host")
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
@@ -405,7 +418,8 @@ def main():
                        "modes": _rounded(ex["results"]), "roofline": ex.get("roofline"),
                        "step_hbm_frac": round(ex["step_hbm_gbs"] / HBM_PEAK_GBS, 4),
                        "megakernel_speedup_vs_best_kpo": ex.get("speedup"),
-                       "loop_speedup_vs_mega": ex.get("loop_speedup_vs_mega")}
+                       "loop_speedup_vs_mega": ex.get("loop_speedup_vs_mega"),
+                       "megakernel_speedup_vs_best_multi_stream": ex.get("ms_speedup")}
     if extra:
         line["extra"] = extra
     print(json.dumps(line), flush=True)

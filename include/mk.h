@@ -71,9 +71,10 @@ enum {
 enum { MK_F32 = 0, MK_BF16 = 1 };                     /* element type of matrices and KV cache */
 enum { MK_DECODE = 0, MK_PREFILL = 1 };               /* queue mode */
 /* Execution modes: the persistent interpreter; the same op bodies one kernel
- * per (layer, op) segment in stream order; and those per-op launches captured
- * into a HIP graph and replayed (decode only). */
-enum { MK_MEGAKERNEL = 0, MK_KERNEL_PER_OP = 1, MK_KERNEL_PER_OP_GRAPH = 2 };
+ * per (layer, op) segment in stream order; those per-op launches captured
+ * into a HIP graph and replayed (decode only); and one kernel per segment on
+ * several streams, synchronised on tiles (decode only). */
+enum { MK_MEGAKERNEL = 0, MK_KERNEL_PER_OP = 1, MK_KERNEL_PER_OP_GRAPH = 2, MK_MULTI_STREAM = 3 };
 enum { MK_PART_META = 0, MK_PART_INSTR = 1, MK_PART_WAITS = 2, MK_PART_TARGETS = 3,
        MK_PART_DEVICE = 4 };
 
@@ -209,8 +210,20 @@ typedef struct mk_kv {
  * calls with the same arguments replay; the kernels read tokens, context
  * lengths and inputs from device memory, so a replay sees their current
  * values.  At most 16 graphs are cached (least recently used evicted, after
- * waiting for its last replay); mk_queue_free drops a queue's graphs.  All
- * three modes give bitwise equal results.
+ * waiting for its last replay); mk_queue_free drops a queue's graphs.
+ * MK_MULTI_STREAM (the MegaOps abstract's multi-stream form: dependent kernels
+ * overlap and synchronise on tiles of the intermediate tensor, no fusion):
+ * counter reset, then one kernel per (layer, op) segment, the segments dealt
+ * round-robin to MK_OPT_STREAMS internal streams (default priority, created on
+ * a device's first such call and kept until the process ends), each
+ * instruction waiting on and signalling the megakernel's tile counters; the
+ * caller's stream waits for all of them before the LM head.  Each kernel gets
+ * 8 * floor(workers_per_cu * (CUs / 8) / streams) workgroups, which stride
+ * over its instructions, so the at most `streams` kernels active at once
+ * are resident together and every wait ends.  Like the megakernel, a
+ * multi-stream call needs those compute units: serialise it with other
+ * megakernel or multi-stream calls on the device.  All four modes give
+ * bitwise equal results.
  * Errors: MK_EINVAL (mismatched queue / sizes / null pointers), MK_ENOTSUP
  * (tiles that do not fit a workgroup's shared memory; megakernel workgroups
  * that cannot all be resident), MK_ELAUNCH.  A loop queue is refused (it runs
@@ -250,7 +263,8 @@ mk_status mk_decode_loop(const mk_queue* q, const void* d_queue, const mk_weight
  * one per device, held until the process ends; no hipMalloc, hipFree or
  * allocating library routine is called.  A queue whose workspace
  * (mk_workspace_nbytes) exceeds it is refused with MK_EINVAL.  exec_mode:
- * MK_MEGAKERNEL or MK_KERNEL_PER_OP (graph mode allocates: MK_EINVAL).  The
+ * MK_MEGAKERNEL or MK_KERNEL_PER_OP (graph and multi-stream modes allocate
+ * runtime objects: MK_EINVAL).  The
  * other arguments and the results are those of mk_decode_step.  d_error
  * (nullable, device, 8 x u32) receives the step's device error record
  * (mk_dev_error, then 3 zero words) when the step ends, since the scratch
@@ -340,7 +354,9 @@ enum {
    * before it stores the tile.  A consumer that read a tile without waiting
    * for its barrier would then read the workspace's previous contents.
    * Results are identical to a run without it; 0 (default) turns it off. */
-  MK_OPT_DELAY_SEED = 6
+  MK_OPT_DELAY_SEED = 6,
+  /* Internal streams of MK_MULTI_STREAM, 1..8 (default 2). */
+  MK_OPT_STREAMS = 7
 };
 /* Errors: MK_EINVAL for an unknown or read-only key or a value out of range. */
 mk_status mk_set_option(int32_t key, int64_t value);

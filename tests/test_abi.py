@@ -148,7 +148,8 @@ def test_options_validate_and_round_trip():
     for key, good, bad in ((T.MK_OPT_GEMV_PIPE, (0, 1, 2), (-1, 3)),
                            (T.MK_OPT_WORKERS_PER_CU, (1, 2), (0, 9)),
                            (T.MK_OPT_SPIN_LIMIT, (1, 1 << 20), (0,)),
-                           (T.MK_OPT_DELAY_SEED, (0, 7, 0xFFFFFFFF), (-1, 1 << 32))):
+                           (T.MK_OPT_DELAY_SEED, (0, 7, 0xFFFFFFFF), (-1, 1 << 32)),
+                           (T.MK_OPT_STREAMS, (1, 8, 2), (0, 9))):
         old = T.mk_get_option(key)
         try:
             for v in good:
@@ -174,6 +175,21 @@ def test_decode_refuses_unknown_exec_mode_and_graph_prefill():
                                 1 << 30, None, None, 7, None)
     assert st == T.MK_EINVAL
     assert b"null" in L.lib().mk_last_error() or b"exec_mode" in L.lib().mk_last_error()
+
+
+def test_static_step_refuses_modes_that_allocate():
+    """The static-scratch step has neither graph nor multi-stream mode (both
+    create runtime objects); the refusal comes before any device call."""
+    import ctypes as C
+    wl = W.WORKLOADS["layer256_f32"]
+    q = T.mk_build_queue(T.make_config(wl.model), T.make_plan(wl.plan, T.MK_DECODE, 1, 129))
+    w, kv = L.mk_weights(), L.mk_kv()
+    fake = C.c_void_p(0x1000)
+    for mode in (T.MK_KERNEL_PER_OP_GRAPH, T.MK_MULTI_STREAM):
+        st = L.lib().mk_decode_step_static(q.handle, fake, C.byref(w), C.byref(kv), None, fake, fake, 1, None,
+                                           None, None, mode, None)
+        assert st == T.MK_EINVAL, mode
+        assert b"static-scratch" in L.lib().mk_last_error()
 
 
 def test_queue_free_accepts_null_and_frees_once():

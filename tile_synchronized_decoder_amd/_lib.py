@@ -14,13 +14,13 @@ LIB_PATH = os.path.join(HERE, "libmk.so")
 MK_OK, MK_EINVAL, MK_ENOMEM, MK_ELAUNCH, MK_EDEVICE, MK_ENOTSUP = 0, -1, -2, -3, -4, -5
 MK_F32, MK_BF16 = 0, 1
 MK_DECODE, MK_PREFILL = 0, 1
-MK_MEGAKERNEL, MK_KERNEL_PER_OP, MK_KERNEL_PER_OP_GRAPH = 0, 1, 2
+MK_MEGAKERNEL, MK_KERNEL_PER_OP, MK_KERNEL_PER_OP_GRAPH, MK_MULTI_STREAM = 0, 1, 2, 3
 MK_PART_META, MK_PART_INSTR, MK_PART_WAITS, MK_PART_TARGETS, MK_PART_DEVICE = range(5)
 MK_STATIC_SCRATCH_BYTES = 64 << 20
 (MK_T_X, MK_T_QKV, MK_T_OPART, MK_T_ATT, MK_T_HRES, MK_T_ACT, MK_T_COUNTERS, MK_T_HEADS,
  MK_T_ERROR, MK_T_LMPART) = range(10)
 (MK_OPT_WORKERS_PER_CU, MK_OPT_SPIN_LIMIT, MK_OPT_NUM_CUS, MK_OPT_TRACE_BUFFER, MK_OPT_TRACE_BYTES,
- MK_OPT_GEMV_PIPE, MK_OPT_DELAY_SEED) = range(7)
+ MK_OPT_GEMV_PIPE, MK_OPT_DELAY_SEED, MK_OPT_STREAMS) = range(8)
 
 
 class mk_config(C.Structure):

@@ -76,6 +76,7 @@ struct Options {
   size_t trace_bytes = 0;
   int gemv_pipe = 0;                     // 0, 1: pipelined issue; 2: compiler-ordered issue
   uint32_t delay_seed = 0;               // race check: seeded stalls before tile stores
+  int streams = 2;                       // multi-stream mode: internal streams per device
 };
 Options g_opt;
 
@@ -312,12 +313,74 @@ mk_status prep_status(hipError_t e) {
   FAIL(MK_ELAUNCH, "kernel set-up failed: %s", hipGetErrorString(e));
 }
 
+// ----------------------------------------------------------------------------- multi-stream mode
+
+// MK_MULTI_STREAM: the step's (layer, op) segments go round-robin to S
+// internal streams of the device (default priority, created on first use and
+// kept for the process).  A fork event on the caller's stream, after the
+// counter reset, starts them; the caller's stream waits on a join event of
+// each before the LM head.  Segment k + 1 runs while segment k still does and
+// waits on its tiles through the barrier counters.
+//
+// Progress: a stream runs one kernel at a time, so at most S segment kernels
+// are active.  Each gets G = 8 * floor(per_cu * (CUs / 8) / S) workgroups (a
+// multiple of the 8 XCDs, among which a dispatch's workgroups are spread
+// evenly), and each kernel fits per_cu workgroups on a compute unit, so the
+// active kernels' workgroups are resident together.  Every wait is on a
+// segment enqueued earlier, which is active or done: no workgroup waits on one
+// that cannot be scheduled.
+constexpr int kMaxStreams = 8;
+constexpr int kXcds = 8;
+struct StreamSet {
+  hipStream_t st[kMaxStreams] = {};
+  hipEvent_t join[kMaxStreams] = {};
+  hipEvent_t fork = nullptr;
+};
+StreamSet g_streams[kMaxDevices];
+
+hipError_t stream_set(int dev, int n, StreamSet*& out) {
+  StreamSet& ss = g_streams[dev];
+  hipError_t e = hipSuccess;
+  if (!ss.fork) e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
+  for (int i = 0; i < n && e == hipSuccess; ++i) {
+    if (!ss.st[i]) e = hipStreamCreateWithFlags(&ss.st[i], hipStreamNonBlocking);
+    if (e == hipSuccess && !ss.join[i]) e = hipEventCreateWithFlags(&ss.join[i], hipEventDisableTiming);
+  }
+  out = &ss;
+  return e;
+}
+
+int ms_grid(int streams) {
+  return kXcds * ((g_opt.workers_per_cu * (num_cus() / kXcds)) / streams);
+}
+
+hipError_t enqueue_multi_stream(const mk_queue* q, const Args& a, const Table& t, StreamSet& ss, int n,
+                                hipStream_t stream) {
+  const uint32_t grid = (uint32_t)ms_grid(n);
+  hipError_t e = hipEventRecord(ss.fork, stream);
+  for (int i = 0; i < n && e == hipSuccess; ++i) e = hipStreamWaitEvent(ss.st[i], ss.fork, 0);
+  size_t k = 0;
+  for (const mk::Segment& sg : q->segments) {
+    if (e != hipSuccess) break;
+    e = t.ms(a, sg.op, sg.first, sg.count, std::min(grid, sg.count), ss.st[k++ % n]);
+  }
+  // join every stream, also after a failed launch, so the caller's stream never
+  // runs ahead of work already enqueued
+  for (int i = 0; i < n; ++i) {
+    hipError_t ej = hipEventRecord(ss.join[i], ss.st[i]);
+    if (ej == hipSuccess) ej = hipStreamWaitEvent(stream, ss.join[i], 0);
+    if (e == hipSuccess) e = ej;
+  }
+  return e;
+}
+
 // The launches of one decode step on `stream`, after every check passed:
 // input rows, then (megakernel) the counter / head / error reset and one
-// interpreter launch, or (per op) the error reset and one launch per segment;
-// then the LM head and argmax.
+// interpreter launch, (multi-stream, `ss` set) the counter / error reset and
+// the segments on the internal streams, or (per op) the error reset and one
+// launch per segment; then the LM head and argmax.
 hipError_t enqueue_decode(const mk_queue* q, const Args& a, const Table& t, int exec_mode, bool want_lm,
-                          bool want_next, hipStream_t stream) {
+                          bool want_next, hipStream_t stream, StreamSet* ss = nullptr, int n_streams = 0) {
   if (!q->cfg.has_embed) {
     // without an embedding the input rows are copied into X_0 by the first launch
     const size_t n = (size_t)a.M * a.H;
@@ -327,13 +390,15 @@ hipError_t enqueue_decode(const mk_queue* q, const Args& a, const Table& t, int 
     if (e != hipSuccess) return e;
   }
   const bool mega = exec_mode == MK_MEGAKERNEL;
-  const uint32_t nr = mega ? a.n_barriers : 0, nh = mega ? a.n_queues : 0;
+  const uint32_t nr = mega || ss ? a.n_barriers : 0, nh = mega ? a.n_queues : 0;
   hipLaunchKernelGGL(reset_kernel, dim3((nr + 255) / 256 + 1), dim3(256), 0, stream, a.counters, nr, a.heads, nh,
                      a.err);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (mega) {
     e = t.mega(a, num_cus() * g_opt.workers_per_cu, stream);
+  } else if (ss) {
+    e = enqueue_multi_stream(q, a, t, *ss, n_streams, stream);
   } else {
     for (const mk::Segment& sg : q->segments) {
       e = t.kpo(a, sg.op, sg.first, sg.count, stream);
@@ -365,8 +430,9 @@ uint64_t g_graph_clock = 0;
 hipStream_t g_capture_stream[kMaxDevices] = {};
 
 void drop_graph(GraphEntry& g) {
-  if (g.done) { hipEventSynchronize(g.done); hipEventDestroy(g.done); }
-  if (g.exec) hipGraphExecDestroy(g.exec);
+  // best effort: a failed wait or destroy leaves nothing the caller could act on
+  if (g.done) { (void)hipEventSynchronize(g.done); (void)hipEventDestroy(g.done); }
+  if (g.exec) (void)hipGraphExecDestroy(g.exec);
   g.exec = nullptr; g.done = nullptr;
 }
 
@@ -400,13 +466,13 @@ mk_status graph_step(const mk_queue* q, const Args& a, const Table& t, std::vect
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(cs, &graph);
     if (el != hipSuccess || e != hipSuccess) {
-      if (graph) hipGraphDestroy(graph);
+      if (graph) (void)hipGraphDestroy(graph);
       FAIL(MK_ELAUNCH, "capture of the per-op launches: %s", hipGetErrorString(el != hipSuccess ? el : e));
     }
     GraphEntry ne;
     ne.key = std::move(key);
     e = hipGraphInstantiate(&ne.exec, graph, nullptr, nullptr, 0);
-    hipGraphDestroy(graph);
+    (void)hipGraphDestroy(graph);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ne.done, hipEventDisableTiming);
     if (e != hipSuccess) {
       drop_graph(ne);
@@ -439,7 +505,8 @@ mk_status decode_impl(const mk_queue* q, const void* d_queue, const mk_weights* 
   const mk_config& c = q->cfg;
   if (mk_status st = check_shapes(c)) return st;
   if (batch != q->plan.rows) FAIL(MK_EINVAL, "batch %d differs from the queue's rows %d", batch, q->plan.rows);
-  if (exec_mode != MK_MEGAKERNEL && exec_mode != MK_KERNEL_PER_OP && exec_mode != MK_KERNEL_PER_OP_GRAPH)
+  if (exec_mode != MK_MEGAKERNEL && exec_mode != MK_KERNEL_PER_OP && exec_mode != MK_KERNEL_PER_OP_GRAPH &&
+      exec_mode != MK_MULTI_STREAM)
     FAIL(MK_EINVAL, "unknown exec_mode");
   if (lds_layout(q).bytes > kMaxLds) FAIL(MK_ENOTSUP, "tiles need more shared memory than a workgroup has");
   const Layout o = layout(q);
@@ -466,9 +533,20 @@ mk_status decode_impl(const mk_queue* q, const void* d_queue, const mk_weights* 
 
   const Table t = pick_table(c.dtype, a.M);
   const bool want_lm = c.has_lm_head && (d_logits || d_next);
-  hipError_t e = t.prep(a, exec_mode == MK_MEGAKERNEL ? MK_MEGAKERNEL : MK_KERNEL_PER_OP, g_opt.workers_per_cu);
+  const int prep_mode = exec_mode == MK_MEGAKERNEL ? MK_MEGAKERNEL
+                        : exec_mode == MK_MULTI_STREAM ? kMultiStreamMode : MK_KERNEL_PER_OP;
+  hipError_t e = t.prep(a, prep_mode, g_opt.workers_per_cu);
   if (e == hipSuccess && want_lm) e = t.prep_lm(a);
   if (mk_status st = prep_status(e)) return st;
+  if (exec_mode == MK_MULTI_STREAM) {
+    if (ms_grid(g_opt.streams) < 1) FAIL(MK_ENOTSUP, "%d streams leave no workgroups per kernel", g_opt.streams);
+    StreamSet* ss = nullptr;
+    e = stream_set(dev, g_opt.streams, ss);
+    if (e != hipSuccess) FAIL(MK_ELAUNCH, "internal streams: %s", hipGetErrorString(e));
+    e = enqueue_decode(q, a, t, exec_mode, want_lm, d_next != nullptr, stream, ss, g_opt.streams);
+    if (e != hipSuccess) FAIL(MK_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
+    return MK_OK;
+  }
   if (exec_mode == MK_KERNEL_PER_OP_GRAPH)
     return graph_step(q, a, t,
                       graph_key(q, dev, d_queue, w, kv, d_tokens, d_x0, d_ctx_lens, d_workspace, workspace_nbytes,
@@ -570,8 +648,8 @@ mk_status mk_decode_step_static(const mk_queue* q, const void* d_queue, const mk
                                 int32_t exec_mode, hipStream_t stream) {
   std::lock_guard<std::mutex> lk(g_mu);
   if (!q) FAIL(MK_EINVAL, "null argument");
-  if (exec_mode == MK_KERNEL_PER_OP_GRAPH)
-    FAIL(MK_EINVAL, "the static-scratch step has no graph mode (instantiating a graph allocates)");
+  if (exec_mode == MK_KERNEL_PER_OP_GRAPH || exec_mode == MK_MULTI_STREAM)
+    FAIL(MK_EINVAL, "the static-scratch step has no graph or multi-stream mode (graphs and streams allocate)");
   const size_t need = layout(q).total;
   if (need > kScratchBytes)
     FAIL(MK_EINVAL, "the step needs %zu bytes of workspace; the static scratch holds %zu", need, kScratchBytes);
@@ -772,6 +850,9 @@ mk_status mk_set_option(int32_t key, int64_t value) {
     case MK_OPT_DELAY_SEED:
       if (value < 0 || value > 0xFFFFFFFFll) FAIL(MK_EINVAL, "delay seed must fit 32 bits");
       g_opt.delay_seed = (uint32_t)value; return MK_OK;
+    case MK_OPT_STREAMS:
+      if (value < 1 || value > kMaxStreams) FAIL(MK_EINVAL, "streams must be 1..%d", kMaxStreams);
+      g_opt.streams = (int)value; return MK_OK;
     default: FAIL(MK_EINVAL, "unknown or read-only option %d", key);
   }
 }
@@ -786,6 +867,7 @@ int64_t mk_get_option(int32_t key) {
     case MK_OPT_TRACE_BYTES: return (int64_t)g_opt.trace_bytes;
     case MK_OPT_GEMV_PIPE: return g_opt.gemv_pipe;
     case MK_OPT_DELAY_SEED: return g_opt.delay_seed;
+    case MK_OPT_STREAMS: return g_opt.streams;
     default: return -1;
   }
 }

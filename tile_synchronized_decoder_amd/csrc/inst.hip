@@ -13,6 +13,6 @@
 namespace mkd {
 Table MK_CAT(table_, MK_WT_NAME, MK_NB)() {
   using LT = Launch<MK_WT, MK_NB>;
-  return {LT::prep, LT::mega, LT::kHasLoop ? LT::loop : nullptr, LT::kpo, LT::prep_lm, LT::lm};
+  return {LT::prep, LT::mega, LT::kHasLoop ? LT::loop : nullptr, LT::kpo, LT::ms, LT::prep_lm, LT::lm};
 }
 }  // namespace mkd

@@ -1407,6 +1407,43 @@ __global__ __launch_bounds__(NT) void mk_interp(Args args) {
   wait_vm<0>();                                  // no weight loads may outlive the workgroup
 }
 
+// Multi-stream mode (MegaOps abstract: dependent kernels overlap and
+// synchronise on tiles of the intermediate tensor instead of at kernel
+// boundaries): one launch per (layer, op) segment, on one of several streams;
+// its workgroups stride over the segment's instructions and every instruction
+// waits on and signals the same tile counters as in the megakernel.  The host
+// caps each launch's workgroups so that the kernels that can be running at
+// once (one per stream) are all resident together.
+template <typename WT, int NB, int OP>
+__global__ __launch_bounds__(NT) void ms_kernel(Args args, uint32_t first, uint32_t count) {
+  KArgs& a = kernel_args();
+  Smem s = make_smem(a);
+  for (uint32_t i = blockIdx.x; i < count; i += gridDim.x) {
+    // an error recorded anywhere (a wait that gave up) stops the remaining
+    // instructions instead of letting each of them wait out its own limit
+    if (threadIdx.x == 0) s.idx[0] = __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const uint32_t abort_seen = __builtin_amdgcn_readfirstlane(s.idx[0]);
+    __syncthreads();
+    if (abort_seen) break;
+    const uint32_t idx = first + i;
+    const Task in = load_instr(a, idx);
+    if (in.op != (OP == KPO_OPROJ_FUSED ? mk::OP_OPROJ : OP)) {
+      if (threadIdx.x == 0) record_error(a, ERR_OPCODE, idx, in.op, 0, 0);
+      break;                                               // uniform: every thread read the same record
+    }
+    // the GEMV ops are specialised at compile time (the O-projection of a queue
+    // without fused combines need not carry the merge's registers)
+    if constexpr (OP == mk::OP_QKV || OP == mk::OP_OPROJ || OP == mk::OP_GATEUP || OP == mk::OP_DOWN)
+      op_gemv<WT, NB>(a, s, in, idx, true, false);
+    else if constexpr (OP == KPO_OPROJ_FUSED)
+      op_gemv<WT, NB>(a, s, in, idx, true, true);
+    else
+      run_instr<WT, NB>(a, s, in, idx, true, OP);
+  }
+  wait_vm<0>();                                            // no weight loads may outlive the workgroup
+}
+
 // One launch per (layer, op): workgroup i runs instruction first + i, no waits.
 template <typename WT, int NB, int OP>
 __global__ __launch_bounds__(NT) void kpo_kernel(Args args, uint32_t first) {
@@ -1714,8 +1751,10 @@ struct PrefillLaunch {
 
 #endif  // MK_PREFILL_UNIT
 
-// Execution mode of the preparation step for the multi-step interpreter.
+// Execution modes of the preparation step beyond the public ones: the
+// multi-step interpreter and the multi-stream kernels.
 constexpr int kLoopMode = 100;
+constexpr int kMultiStreamMode = 101;
 
 template <typename WT, int NB>
 struct Launch {
@@ -1724,12 +1763,25 @@ struct Launch {
   static constexpr bool kHasLoop = sizeof(WT) == 2;
   // Everything that can refuse a call, before anything is enqueued: the shared
   // memory opt-in of every kernel the call may launch and, for the megakernel,
-  // that all of its workgroups can be resident at once.
+  // that all of its workgroups can be resident at once (for the multi-stream
+  // kernels: that `per_cu` workgroups of each fit on one compute unit, so that
+  // any `per_cu` of them, from whichever kernels, fit together).
   static hipError_t prep(const Args& a, int exec_mode, int per_cu) {
     if (exec_mode == MK_MEGAKERNEL) {
       static uint32_t granted[kMaxDevices] = {};
       hipError_t e = allow_lds(mk_interp<WT, NB>, a.lds_bytes, granted);
       return e == hipSuccess ? check_resident(mk_interp<WT, NB>, a.lds_bytes, per_cu) : e;
+    }
+    if (exec_mode == kMultiStreamMode) {
+      static uint32_t granted_ms[KPO_OPROJ_FUSED + 1][kMaxDevices] = {};
+      hipError_t e = hipSuccess;
+#define PREP_MS(OPC)                                                                                \
+      if (e == hipSuccess) e = allow_lds(ms_kernel<WT, NB, OPC>, a.lds_bytes, granted_ms[OPC]);      \
+      if (e == hipSuccess) e = check_resident(ms_kernel<WT, NB, OPC>, a.lds_bytes, per_cu);
+      PREP_MS(mk::OP_EMBED) PREP_MS(mk::OP_QKV) PREP_MS(mk::OP_ATTN) PREP_MS(mk::OP_COMBINE)
+      PREP_MS(mk::OP_OPROJ) PREP_MS(mk::OP_GATEUP) PREP_MS(mk::OP_DOWN) PREP_MS(KPO_OPROJ_FUSED)
+#undef PREP_MS
+      return e;
     }
     if (exec_mode == kLoopMode) {
       if constexpr (kHasLoop) {
@@ -1758,6 +1810,21 @@ struct Launch {
       return hipGetLastError();
     }
     return hipErrorInvalidValue;
+  }
+  // One segment of the multi-stream mode: `grid` workgroups stride over its instructions.
+  static hipError_t ms(const Args& a, uint32_t op, uint32_t first, uint32_t count, uint32_t grid, hipStream_t st) {
+    if (op == mk::OP_OPROJ && a.fuse_combine) op = KPO_OPROJ_FUSED;
+    switch (op) {
+#define MS_CASE(OPC)                                                                               \
+      case OPC:                                                                                    \
+        hipLaunchKernelGGL((ms_kernel<WT, NB, OPC>), dim3(grid), dim3(NT), a.lds_bytes, st, a, first, count); \
+        break;
+      MS_CASE(mk::OP_EMBED) MS_CASE(mk::OP_QKV) MS_CASE(mk::OP_ATTN) MS_CASE(mk::OP_COMBINE)
+      MS_CASE(mk::OP_OPROJ) MS_CASE(mk::OP_GATEUP) MS_CASE(mk::OP_DOWN) MS_CASE(KPO_OPROJ_FUSED)
+#undef MS_CASE
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
   }
   static hipError_t kpo(const Args& a, uint32_t op, uint32_t first, uint32_t count, hipStream_t st) {
     if (op == mk::OP_OPROJ && a.fuse_combine) op = KPO_OPROJ_FUSED;
@@ -1799,6 +1866,7 @@ struct Table {
   hipError_t (*mega)(const Args&, int grid, hipStream_t);
   hipError_t (*loop)(const Args&, int grid, hipStream_t);
   hipError_t (*kpo)(const Args&, uint32_t op, uint32_t first, uint32_t count, hipStream_t);
+  hipError_t (*ms)(const Args&, uint32_t op, uint32_t first, uint32_t count, uint32_t grid, hipStream_t);
   hipError_t (*prep_lm)(const Args&);
   hipError_t (*lm)(const Args&, hipStream_t);
 };

@@ -4,5 +4,5 @@
 #include "kernels.h"
 
 namespace mkd {
-Table table_prefill() { return {PrefillLaunch::prep, PrefillLaunch::mega, nullptr, PrefillLaunch::kpo, nullptr, nullptr}; }
+Table table_prefill() { return {PrefillLaunch::prep, PrefillLaunch::mega, nullptr, PrefillLaunch::kpo, nullptr, nullptr, nullptr}; }
 }  // namespace mkd
