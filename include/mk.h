@@ -101,10 +101,18 @@ typedef struct mk_plan {
   int32_t mode, rows, ctx_max;
   int32_t tq, to, tf, td, kb, bm, bn;
   int32_t n_queues;
-  int32_t fuse_combine;   /* decode: 1 = no split-combine instructions; each
-                           * O-projection tile waits on the attention split
-                           * partials and merges them while staging (0 or 1;
-                           * recorded in bit 0 of the META word after bn) */
+  int32_t fuse_combine;   /* decode: 0 = split-combine instructions (COMBINE).
+                           * 1 = none; each O-projection tile waits on the
+                           * attention split partials and merges them while
+                           * staging (bit 0 of the META word after bn).
+                           * 2 = none; every split counts its arrival on its
+                           * (row, KV head) partial tile, whose target is
+                           * then NS + 1: the split that arrives last merges
+                           * the partials into the attention output and
+                           * signals the tile once more, and the O-projection
+                           * tiles wait on those tiles and read the merged
+                           * rows (bit 2 of that word).  All three give the
+                           * same results bit for bit. */
   int32_t loop;           /* decode: 1 = a queue for mk_decode_loop (persistent
                            * multi-step decode): each step ends with LM-head
                            * tiles of 64 vocabulary rows (LMHEAD) and one argmax
@@ -125,8 +133,9 @@ typedef struct mk_queue mk_queue;   /* opaque, host memory */
  * Layout of the parts (little-endian):
  *   META    u32 magic 'TMK1', version 1, mode, n_instr, n_barriers,
  *           n_wait_ranges, n_segments, n_queues, rows, ctx_max, n_splits,
- *           n_layers, tq, to, tf, td, kb, bm, bn, flags (bit 0: fused
- *           split combines; bit 1: loop queue), then n_segments x
+ *           n_layers, tq, to, tf, td, kb, bm, bn, flags (bit 0: split
+ *           combines fused into the O-projection; bit 1: loop queue; bit 2:
+ *           split combines merged by the last split), then n_segments x
  *           {op, layer, first, count} (maximal runs of one op of one layer)
  *   INSTR   n_instr x 32 B {u16 op, u16 layer, u32 a0, a1, a2, wait_off,
  *           wait_cnt, signal, n_wait}
@@ -134,7 +143,8 @@ typedef struct mk_queue mk_queue;   /* opaque, host memory */
  *           marks barriers of the previous step (loop queues: at step t a
  *           same-step barrier is complete at target * (t + 1) signals, a
  *           previous-step one at target * t)
- *   TARGETS n_barriers x u32 (instructions that signal each barrier)
+ *   TARGETS n_barriers x u32 (instructions that signal each barrier, plus
+ *           one for a partial tile whose last split merges: flags bit 2)
  *   DEVICE  INSTR | WAITS | TARGETS, each starting on a 256-byte boundary:
  *           what mk_decode_step / mk_prefill read from d_queue.
  * Ownership: *out is a host object the caller releases with mk_queue_free.
@@ -339,8 +349,9 @@ enum {
   /* Trace mode: a device buffer (value = its address) of at least 64 bytes per
    * instruction.  While set, each megakernel instruction i writes 8 x u64 at
    * offset 64*i: (workgroup << 32 | XCD id), pop time, time its waits ended,
-   * phase A (inputs staged), phase B (main loop done), end time, 0, 0 (device
-   * wall clock, 100 MHz; a phase an op does not have stays 0).  Set the
+   * phase A (inputs staged), phase B (main loop done), end time, the time
+   * an attention split that arrived last began its merge (fuse_combine 2), 0
+   * (device wall clock, 100 MHz; a phase an op does not have stays 0).  Set the
    * address to 0 to stop. */
   MK_OPT_TRACE_BUFFER = 3,
   MK_OPT_TRACE_BYTES = 4,

@@ -8,7 +8,8 @@ summary):
 ``static_check``  decodes the serialised queue, rebuilds each instruction's
     write and read regions from its opcode and arguments as element masks (not
     boxes), and verifies that (1) every barrier's target equals the number of
-    instructions that signal it and all of them write one tile, (2) every
+    instructions that signal it (plus one for a split-partial tile whose last
+    split merges, flags bit 2) and all of them write one tile, (2) every
     element an instruction reads that some instruction writes lies in a tile
     the instruction waits on, and it waits on nothing else, (3) every producer
     it waits on sits earlier in the queue, so a global pop in queue order can
@@ -28,7 +29,9 @@ summary):
     step t needs target * (t + 1) signals, a previous-step wait target * t).
     Each instruction runs its tile body on float64 state that holds NaN until
     written, and every element carries the step that last wrote it; inputs are
-    read when the body starts and outputs land when it ends.  A read of an
+    read when the body starts and outputs land when it ends.  Under flags bit 2
+    the attention split whose signal completes its (row, KV head) merges the
+    partials into the attention output as it ends and signals once more.  A read of an
     element not written in the expected step (unwritten, stale or already
     overwritten by the next step) is reported, as is a deadlock.  The result
     can be compared bit for bit across worker counts and schedules, and with
@@ -61,7 +64,7 @@ class Parsed:
     n_splits: int
     n_layers: int
     plan: Tuple[int, ...]
-    flags: int                   # bit 0: split combines fused into the O-projection
+    flags: int                   # bit 0: combines fused into the O-projection; 1: loop; 2: last split merges
     segments: List[Tuple[int, int, int, int]]
     instr: np.ndarray            # [n, 9] int64: op, layer, a0, a1, a2, wait_off, wait_cnt, signal, n_wait
     ranges: np.ndarray           # [n_ranges, 2]
@@ -80,6 +83,10 @@ class Parsed:
     @property
     def loop(self) -> bool:
         return bool(self.flags & 2)
+
+    @property
+    def merge_last(self) -> bool:
+        return bool(self.flags & 4)
 
 
 def parse(parts: Dict[str, bytes]) -> Parsed:
@@ -160,7 +167,8 @@ class Space:
             b, g = a0, a1
             return (ATT, slice(b, b + 1), slice(g * r * hd, (g + 1) * r * hd)), [(OP, slice(b, b + 1), slice(g, g + 1))]
         if op == QS.OP_OPROJ:
-            att = (OP, allr, slice(0, nkv)) if p.flags & 1 else (ATT, allr, slice(0, nq * hd))
+            # no combine instructions (flags bit 0 or 2): the wait is on the partial tiles
+            att = (OP, allr, slice(0, nkv)) if p.flags & 5 else (ATT, allr, slice(0, nq * hd))
             return (HR, allr, slice(a0, a1)), [att, (X, allr, slice(a0, a1))]
         if op == QS.OP_GATEUP:
             return (ACT, allr, slice(a0, a1)), [(HR, allr, slice(0, H))]
@@ -227,11 +235,15 @@ def static_check(model, parts: Dict[str, bytes], max_errors: int = 20) -> List[s
             err(f"instr {i}: writes elements of another barrier's tile")
         writer[t][rs, cs] = sig
 
-    # (1) targets and tile identity
+    # (1) targets and tile identity; with merges in the last split, a partial
+    # tile is signalled once more by the merge
+    opart = {QS.tensor_order(l, QS.T_OPART) for l in range(model.n_layers)}
     for bid in range(p.n_barriers):
         who = signallers.get(bid, [])
-        if len(who) != int(p.targets[bid]):
-            err(f"barrier {bid}: target {int(p.targets[bid])} but {len(who)} signallers")
+        extra = int(p.merge_last and bool(who) and regions[who[0]] is not None and regions[who[0]][0][0] in opart)
+        if len(who) + extra != int(p.targets[bid]):
+            err(f"barrier {bid}: target {int(p.targets[bid])} but {len(who)} signallers"
+                + (" and a merge" if extra else ""))
         ws = {regions[i][0][0] for i in who if regions[i] is not None}
         if len(ws) > 1:
             err(f"barrier {bid}: signallers write different tensors")
@@ -342,9 +354,13 @@ class DecodeState:
             self.bad_reads.append(f"instr {i} (step {step}) read elements of tensor {t} not written in step {want}")
         return self.t[t][rs, cs].copy()
 
-    def body(self, i: int, step: int = 0):
-        """Compute instruction i of `step` from the current state; returns a commit closure."""
+    def body(self, i: int, step: int = 0, merge: bool = False):
+        """Compute instruction i of `step` from the current state; returns a commit
+        closure.  ``merge``: the split merge that attention instruction i performs
+        when it arrives last at its (row, KV head)."""
         op, l, a0, a1, a2 = (int(v) for v in self.p.instr[i, :5])
+        if merge:
+            op = -op
         cfg, lw = self.cfg, (self.model.layers[l] if self.model.layers else None)
         M, H, hd = self.p.rows, cfg.hidden, cfg.head_dim
         nq, nkv = cfg.n_q_heads, cfg.n_kv_heads
@@ -416,6 +432,10 @@ class DecodeState:
                     self.ver[OPT][b, g] = step
             return commit
         if op == QS.OP_COMBINE:
+            b, g = a0, a1
+            return put(ATT, slice(b, b + 1), slice(g * r * hd, (g + 1) * r * hd), merged(b, g)[None, :])
+        if op == -QS.OP_ATTN:
+            # the merge of (row b, KV head g) by its last-arriving split (flags bit 2)
             b, g = a0, a1
             return put(ATT, slice(b, b + 1), slice(g * r * hd, (g + 1) * r * hd), merged(b, g)[None, :])
         if op == QS.OP_OPROJ:
@@ -526,7 +546,13 @@ def simulate(model: N.Model, parts: Dict[str, bytes], K: np.ndarray, V: np.ndarr
         # the earliest running instruction ends: outputs land, then its barrier is signalled
         now, _, w, job = heapq.heappop(events)
         pending.pop((w, job))()
-        counters[int(p.instr[job[1], 7])] += 1
+        sig = int(p.instr[job[1], 7])
+        counters[sig] += 1
+        if (p.merge_last and int(p.instr[job[1], 0]) == QS.OP_ATTN
+                and counters[sig] == p.targets[sig] * (job[0] + 1) - 1):
+            # the last split of its (row, KV head): merge, then signal the tile again
+            st.body(job[1], job[0], merge=True)()
+            counters[sig] += 1
         nxt = pop(w)
         if nxt is not None:
             waiting[w] = nxt

@@ -30,11 +30,20 @@ What the pages leave open and this module fixes (the plainest reading):
   tiles.  The context length only enters through NS = ceil(ctx_max / KB)
   splits, so the queue is independent of the runtime context (and of the
   runtime prompt length in prefill, whose unused row blocks become no-ops).
-* With the plan's ``fuse_combine`` set (decode), the split combines are not
-  instructions of their own: each O-projection tile reads the split partials
-  of every (row, KV head) in place of the attention output and merges them
-  while staging its inputs; the attention-output tensor then has no tiles.
-  The META word after bn records the flag.
+* With the plan's ``fuse_combine`` set to 1 (decode), the split combines are
+  not instructions of their own: each O-projection tile reads the split
+  partials of every (row, KV head) in place of the attention output and
+  merges them while staging its inputs; the attention-output tensor then has
+  no tiles.  Bit 0 of the META word after bn records it.
+* With ``fuse_combine`` 2 the queue has the same instructions and wait lists
+  as with 1, and the O-projection tiles still wait on the partial tiles, but
+  the merge happens at the end of the attention: every split counts its
+  arrival on its (row, KV head) partial tile, and the split whose arrival
+  brings the count to NS merges the NS partials into that row's attention
+  output (the attention-output tensor, as with the combines) and signals the
+  tile once more.  The partial tile's target is therefore NS + 1; the
+  O-projection tiles read the merged attention output.  Bit 2 of the META
+  word records it.
 * With the plan's ``loop`` set (decode, persistent multi-step decode; the
   lecture summary's practical implications keep the host out of the hot
   loop), one queue describes one step of a run of T steps that one launch
@@ -55,12 +64,13 @@ Byte layout (little-endian), shared with the GPU library's C builder:
 
 META    u32 magic 'TMK1', version, mode, n_instr, n_barriers, n_wait_ranges, n_segments,
         n_queues, rows, ctx_max, n_splits, n_layers, tq, to, tf, td, kb, bm, bn, flags
-        (bit 0: split combines fused into the O-projection; bit 1: multi-step loop queue),
+        (bit 0: split combines fused into the O-projection; bit 1: multi-step loop queue;
+        bit 2: split combines merged by the last-arriving split),
         then n_segments x {u32 op, layer, first, count} (maximal runs of one op of one layer)
 INSTR   n_instr x 32 B {u16 op, u16 layer, u32 a0, a1, a2, wait_off, wait_cnt, signal, n_wait}
         (wait_off/wait_cnt index WAITS ranges; n_wait = barriers waited on in total)
 WAITS   n_wait_ranges x {u32 first barrier id, u32 count} (count bit 31: previous-step barriers)
-TARGETS n_barriers x u32
+TARGETS n_barriers x u32 (signalling instructions; + 1 for a partial tile under bit 2)
 """
 from __future__ import annotations
 
@@ -203,8 +213,8 @@ def _check(model, plan, mode: int, rows: int, ctx_max: int) -> None:
         raise QueueError("rows and ctx_max must be positive")
     if not 1 <= plan.n_queues <= MAX_QUEUES:
         raise QueueError("n_queues out of range")
-    if getattr(plan, "fuse_combine", 0) not in (0, 1):
-        raise QueueError("fuse_combine must be 0 or 1")
+    if getattr(plan, "fuse_combine", 0) not in (0, 1, 2):
+        raise QueueError("fuse_combine must be 0, 1 or 2")
     if getattr(plan, "loop", 0) not in (0, 1):
         raise QueueError("loop must be 0 or 1")
     if getattr(plan, "loop", 0) and (mode != MODE_DECODE or not model.has_embed or not model.has_lm_head):
@@ -320,7 +330,8 @@ def build(model, plan, mode: int, rows: int, ctx_max: int) -> Queue:
     NS = math.ceil(ctx_max / plan.kb) if mode == MODE_DECODE else 0
     instrs = (_decode_instrs(model, plan, rows, NS) if mode == MODE_DECODE
               else _prefill_instrs(model, plan, rows))
-    flags = 1 if mode == MODE_DECODE and getattr(plan, "fuse_combine", 0) else 0
+    fuse = getattr(plan, "fuse_combine", 0) if mode == MODE_DECODE else 0
+    flags = (1 if fuse == 1 else 0) | (4 if fuse == 2 else 0)
     if getattr(plan, "loop", 0):
         flags |= 2
     q = Queue(mode, rows, ctx_max, NS, model.n_layers,
@@ -335,6 +346,11 @@ def build(model, plan, mode: int, rows: int, ctx_max: int) -> Queue:
             q.targets.append(0)
         ins.signal = tile_id[ins.write]
         q.targets[ins.signal] += 1
+    if fuse == 2:
+        # the merge of the last-arriving split signals each partial tile once more
+        for ins in instrs:
+            if ins.op == OP_ATTN and ins.a2 == 0:
+                q.targets[ins.signal] += 1
 
     by_tensor: Dict[int, List[Tuple[Box, int]]] = {}
     for (t, box), bid in tile_id.items():

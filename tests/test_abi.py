@@ -113,29 +113,32 @@ def test_workspace_layout_is_consistent():
         q.workspace_offset(T.MK_T_QKV, 16)
 
 
+@pytest.mark.parametrize("fuse", [1, 2])
 @pytest.mark.parametrize("rows,ctx,plan", [
-    (1, 129, W.Plan(tq=16, to=16, tf=32, td=16, kb=32, fuse_combine=1)),
-    (3, 129, W.Plan(tq=24, to=40, tf=50, td=7, kb=64, n_queues=8, fuse_combine=1)),
-    (32, 33, W.Plan(tq=1, to=3, tf=5, td=9, kb=1, fuse_combine=1)),
+    (1, 129, W.Plan(tq=16, to=16, tf=32, td=16, kb=32)),
+    (3, 129, W.Plan(tq=24, to=40, tf=50, td=7, kb=64, n_queues=8)),
+    (32, 33, W.Plan(tq=1, to=3, tf=5, td=9, kb=1)),
 ])
-def test_builder_bytes_fused_combine(rows, ctx, plan):
-    """Queues whose split combines are fused into the O-projection: byte-identical."""
-    got, ref = _both(W.LLAMA_LAYER_F32, plan, QS.MODE_DECODE, rows, ctx)
+def test_builder_bytes_fused_combine(rows, ctx, plan, fuse):
+    """Queues without split-combine instructions (merged in the O-projection,
+    or by the last-arriving split): byte-identical."""
+    got, ref = _both(W.LLAMA_LAYER_F32, dataclasses.replace(plan, fuse_combine=fuse), QS.MODE_DECODE, rows, ctx)
     assert got == ref
 
 
-def test_builder_bytes_fused_combine_llama1b():
-    wl = W.WORKLOADS["llama1b_b1"]
-    import dataclasses
-    plan = dataclasses.replace(wl.plan, fuse_combine=1)
+@pytest.mark.parametrize("name,fuse,loop", [("llama1b_b1", 1, 0), ("llama1b_b1", 2, 0), ("llama8b_b1", 2, 0),
+                                            ("llama1b_b1", 2, 1)])
+def test_builder_bytes_fused_combine_full_shapes(name, fuse, loop):
+    wl = W.WORKLOADS[name]
+    plan = dataclasses.replace(wl.plan, fuse_combine=fuse, loop=loop)
     got, ref = _both(wl.model, plan, QS.MODE_DECODE, wl.run.batch, wl.run.ctx_max)
     assert got == ref
 
 
-def test_builder_rejects_bad_fuse_flag():
+@pytest.mark.parametrize("fuse", [-1, 3])
+def test_builder_rejects_bad_fuse_flag(fuse):
     wl = W.WORKLOADS["layer256_f32"]
-    import dataclasses
-    plan = dataclasses.replace(wl.plan, fuse_combine=2)
+    plan = dataclasses.replace(wl.plan, fuse_combine=fuse)
     with pytest.raises(T.MkError):
         T.mk_build_queue(T.make_config(wl.model), T.make_plan(plan, QS.MODE_DECODE, 1, 129))
     with pytest.raises(QS.QueueError):

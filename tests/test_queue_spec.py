@@ -302,6 +302,85 @@ def test_fused_combine_simulation_detects_missing_split_wait():
     assert CK.static_check(wl.model, mutant) != []
 
 
+# ----------------------------------------------------------------------------- merge in the last split
+
+def _merge_last(plan):
+    import dataclasses
+    return dataclasses.replace(plan, fuse_combine=2)
+
+
+def test_merge_last_queue_shape():
+    """Merge in the last split: the instructions and wait lists of the
+    O-projection-fused queue, each split-partial tile's target NS + 1 (the
+    splits and the merge), the META flag bit 2."""
+    wl = W.WORKLOADS["layer256_f32"]
+    m, M = wl.model, 3
+    q1 = QS.build(m, _fused(wl.plan), QS.MODE_DECODE, M, 129)
+    q2 = QS.build(m, _merge_last(wl.plan), QS.MODE_DECODE, M, 129)
+    assert q2.instr_bytes() == q1.instr_bytes() and q2.waits_bytes() == q1.waits_bytes()
+    opart = [k for k, (t, _) in enumerate(q2.tiles) if t == QS.tensor_order(0, QS.T_OPART)]
+    assert len(opart) == M * m.n_kv_heads
+    NS = q2.n_splits
+    assert all(q2.targets[k] == NS + 1 for k in opart)
+    assert sum(q2.targets) == len(q2.instrs) + m.n_layers * M * m.n_kv_heads
+    assert struct.unpack_from("<20I", q2.meta_bytes())[19] == 4
+    assert CK.static_check(m, q2.parts()) == []
+
+
+def test_merge_last_every_target_change_is_caught():
+    """A partial tile's target left at NS (the merge forgotten) or raised to
+    NS + 2, and any other target moved by one: refused."""
+    wl = W.WORKLOADS["layer256_f32"]
+    q = QS.build(wl.model, _merge_last(wl.plan), QS.MODE_DECODE, 1, 129)
+    parts = q.parts()
+    for b in range(len(q.targets)):
+        for d in (-1, 1):
+            t = list(q.targets)
+            t[b] += d
+            mutant = dict(parts, targets=struct.pack(f"<{len(t)}I", *t))
+            assert CK.static_check(wl.model, mutant, max_errors=1), (b, d)
+
+
+@pytest.mark.parametrize("workers", [1, 7, 256])
+def test_merge_last_simulation_matches_forward(workers):
+    """Any schedule: the last split to arrive merges, the O-projection reads
+    only merged rows (never a stale or unwritten element), the output equals
+    the plain forward pass, counters end at their targets."""
+    model, K, V, x0 = _small_inputs(gain=0.1)
+    wl = W.WORKLOADS["layer256_f32"]
+    q = QS.build(wl.model, _merge_last(wl.plan), QS.MODE_DECODE, 1, 129)
+    ref = N.decode_step(model, K.copy(), V.copy(), [128], x0=x0)
+    base = CK.simulate(model, q.parts(), K.copy(), V.copy(), [128], 1, seed=0, x0=x0)
+    assert N.max_rel_err(base.x_out, ref.x_out) < 1e-12
+    for seed in range(30 if workers > 1 else 1):
+        res = CK.simulate(model, q.parts(), K.copy(), V.copy(), [128], workers, seed=seed, x0=x0,
+                          reverse_ties=bool(seed & 1))
+        assert not res.deadlock and res.bad_reads == []
+        assert np.array_equal(res.x_out, base.x_out)
+        assert np.array_equal(res.counters, np.array(q.targets))
+
+
+def test_merge_last_simulation_detects_early_merge_and_missing_wait():
+    """Target NS (the last split taken to be the one before it): the merge
+    reads a partial not yet written.  O-projection without its partial-tile
+    waits: it reads attention rows not yet merged."""
+    model, K, V, x0 = _small_inputs()
+    wl = W.WORKLOADS["layer256_f32"]
+    q = QS.build(wl.model, _merge_last(wl.plan), QS.MODE_DECODE, 1, 129)
+    opart = {k for k, (t, _) in enumerate(q.tiles) if t == QS.tensor_order(0, QS.T_OPART)}
+    t = [v - 1 if k in opart else v for k, v in enumerate(q.targets)]
+    early = dict(q.parts(), targets=struct.pack(f"<{len(t)}I", *t))
+    i = next(k for k, ins in enumerate(q.instrs) if ins.op == QS.OP_OPROJ)
+    nowait = _with_waits(q, i, [b for b in q.wait_list(i) if b not in opart])
+    for mutant in (early, nowait):
+        seen = False
+        for seed in range(20):
+            res = CK.simulate(model, mutant, K.copy(), V.copy(), [128], 64, seed=seed, x0=x0)
+            seen |= bool(res.bad_reads) or bool(np.any(np.isnan(res.x_out)))
+        assert seen
+        assert CK.static_check(wl.model, mutant) != []
+
+
 def test_attention_splits_are_split_major_and_rotated():
     """Hand-worked order for 3 rows x 2 KV heads x 3 splits: split s starts at
     the pair s rows on and wraps, so a worker taking every n-th instruction by
@@ -429,6 +508,24 @@ def test_loop_simulation_teacher_forced_matches_oracle(workers):
             base = got
         assert all(np.array_equal(a, b) for a, b in zip(base, got))
         assert np.array_equal(Ks, Kr) and np.array_equal(Vs, Vr)
+
+
+def test_loop_merge_last_simulation_matches_oracle():
+    """Loop queue whose last split merges: at step t the last arrival sees
+    (NS + 1) t + NS - 1 earlier signals; three steps in one run equal the
+    oracle's teacher-forced steps and the counters end at 3 x targets."""
+    import dataclasses
+    q, model, K, V, tokens = _tiny(dataclasses.replace(TINY_PLAN, fuse_combine=2))
+    assert CK.static_check(TINY, q.parts()) == []
+    Kr, Vr = K.copy(), V.copy()
+    ref = [N.decode_step(model, Kr, Vr, [p + t for p in TINY_RUN.ctx0], tokens=tokens[t]) for t in range(3)]
+    for seed in range(10):
+        res = CK.simulate(model, q.parts(), K.copy(), V.copy(), TINY_RUN.ctx0, 7, seed=seed, tokens=tokens[:3],
+                          steps=3, reverse_ties=bool(seed & 1))
+        assert not res.deadlock and res.bad_reads == []
+        assert np.array_equal(res.counters, 3 * np.array(q.targets))
+        for t in range(3):
+            assert N.max_rel_err_rows(res.state.logits[t], ref[t].logits) < 1e-12
 
 
 def test_loop_simulation_greedy_feedback():

@@ -215,7 +215,7 @@ LdsLayout lds_layout(const mk_config& c, const mk_plan& p) {
   // fused split combines: the O-projection stages all of its input rows at once
   // (whole 512-column iterations) followed by every split partial of the rows
   uint32_t fused_need = 0;
-  if (p.fuse_combine) {
+  if (p.fuse_combine == 1) {
     const uint32_t r = c.n_q_heads / c.n_kv_heads, NA = c.n_q_heads * c.head_dim;
     const uint32_t NS = (p.ctx_max + p.kb - 1) / p.kb;
     fused_need = nb * ((NA + 511) / 512 * 512) + p.rows * c.n_kv_heads * NS * (r * c.head_dim + 2 * r) +
@@ -271,7 +271,8 @@ void fill_args(const mk_queue* q, const void* d_queue, const mk_weights* w, cons
   a.targets = reinterpret_cast<const uint32_t*>(qd + q->dev_targets_off);
   a.n_instr = (uint32_t)q->instr.size(); a.n_barriers = (uint32_t)q->targets.size();
   a.n_queues = (uint32_t)q->plan.n_queues;
-  a.fuse_combine = q->plan.mode == MK_DECODE && q->plan.fuse_combine;
+  a.fuse_combine = q->plan.mode == MK_DECODE && q->plan.fuse_combine == 1;
+  a.merge_last = q->plan.mode == MK_DECODE && q->plan.fuse_combine == 2;
   const LdsLayout ll = lds_layout(q);
   a.lds_res = ll.res; a.lds_x = ll.x; a.lds_union = ll.uni; a.lds_bytes = ll.bytes; a.lds_ring = ll.ring;
   a.M_cache = kv && kv->rows > 0 ? kv->rows : q->plan.rows;
@@ -390,7 +391,9 @@ hipError_t enqueue_decode(const mk_queue* q, const Args& a, const Table& t, int 
     if (e != hipSuccess) return e;
   }
   const bool mega = exec_mode == MK_MEGAKERNEL;
-  const uint32_t nr = mega || ss ? a.n_barriers : 0, nh = mega ? a.n_queues : 0;
+  // counters: the tile waits (megakernel, multi-stream) and the split arrivals
+  // of a queue whose last split merges (every mode)
+  const uint32_t nr = mega || ss || a.merge_last ? a.n_barriers : 0, nh = mega ? a.n_queues : 0;
   hipLaunchKernelGGL(reset_kernel, dim3((nr + 255) / 256 + 1), dim3(256), 0, stream, a.counters, nr, a.heads, nh,
                      a.err);
   hipError_t e = hipGetLastError();

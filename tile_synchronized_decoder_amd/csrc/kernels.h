@@ -96,6 +96,7 @@ struct Args {
   const float* lm_x;             // LM head input rows
   int gemv_pipe;                 // decode GEMV weight issue: 0, 1 pipelined; 2 compiler-ordered
   int fuse_combine;              // decode queue without split combines: O-projection merges the partials
+  int merge_last;                // decode queue without split combines: the last split to arrive merges
   uint32_t delay_seed;           // race check: seeded stall before each tile's stores (0: off)
   // persistent multi-step decode (loop queues): steps of the run, 1 = embed the
   // previous step's argmax (else tokens[step][row]), the argmax of every step
@@ -914,6 +915,9 @@ __device__ __forceinline__ float across_groups(float v) {
 // shuffles, the softmax state lives in registers per key lane group, and the
 // groups and waves merge once at the end.  The cached rows of the first 8
 // rounds are loaded before the tile waits.
+template <int HD>
+__device__ __forceinline__ void attn_arrive(KArgs& a, Smem& s, const Task in, uint32_t idx);
+
 template <typename KT, int HD>
 __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Task in, uint32_t idx, bool mega) {
   using E = Elem<KT>;
@@ -966,7 +970,8 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Task in, uint32
   if (j0 >= j1) {                                         // empty split
     for (int e = t; e < r * HD; e += NT) st_cg(slot + e, 0.f);
     if (t < r) { st_cg(slot + r * HD + t, -INFINITY); st_cg(slot + r * HD + r + t, 0.f); }
-    if (mega) signal_tile(a, in);
+    if (a.merge_last) attn_arrive<HD>(a, s, in, idx);
+    else if (mega) signal_tile(a, in);
     return;
   }
 
@@ -1180,7 +1185,8 @@ __device__ __forceinline__ void op_attn(KArgs& a, Smem& s, const Task in, uint32
     st_cg(slot + r * HD + t, M * 0.6931471805599453f);          // back to natural units
     st_cg(slot + r * HD + r + t, L);
   }
-  if (mega) signal_tile(a, in);
+  if (a.merge_last) attn_arrive<HD>(a, s, in, idx);
+  else if (mega) signal_tile(a, in);
 }
 
 // Log-sum-exp merge of NS split partials (o[r*HD], m[r], l[r] per split, slot_sz
@@ -1220,12 +1226,11 @@ __device__ __forceinline__ void combine_rows(const float* src, float* out, int r
   }
 }
 
-// COMBINE(b, g): merge the NS split partials of row b, group g into ATT_l.
+// Merge the NS split partials of row b, KV head g of layer l into ATT_l (the
+// body of a COMBINE tile, or of the split that arrives last at (b, g)).
 template <int HD>
-__device__ __forceinline__ void op_combine(KArgs& a, Smem& s, const Task in, uint32_t idx, bool mega) {
-  const int l = in.layer, b = in.a0, g = in.a1, r = a.r;
-  if (mega && !wait_tiles(a, in, idx)) return;
-  inject_delay(a, idx);
+__device__ __forceinline__ void merge_splits(KArgs& a, Smem& s, int l, int b, int g, bool mark, uint32_t idx) {
+  const int r = a.r;
   const int slot_sz = r * HD + 2 * r;
   const int total = a.NS * slot_sz;
   const float* base = a.OPART + l * a.sOP + (size_t)(b * a.nkv + g) * a.NS * slot_sz;
@@ -1233,8 +1238,21 @@ __device__ __forceinline__ void op_combine(KArgs& a, Smem& s, const Task in, uin
   // all split partials at once into shared memory (independent coherent loads)
   const bool staged = total <= s.xcap;
   if (staged) {
-    constexpr int U = 8;                                  // U loads per thread in flight at once
-    for (int e0 = threadIdx.x; e0 < total; e0 += NT * U) {
+    // 16-byte loads where the slots allow them: up to 12 K floats of partials
+    // take a single round trip per thread
+    const bool vec = (reinterpret_cast<uintptr_t>(base) & 15) == 0;
+    const int q4 = vec ? total >> 2 : 0;
+    constexpr int U4 = 12;
+    for (int u0 = threadIdx.x; u0 < q4; u0 += NT * U4) {
+      float4 v[U4];
+#pragma unroll
+      for (int j = 0; j < U4; ++j) if (u0 + j * NT < q4) v[j] = ld_cg4(base + 4 * (u0 + j * NT));
+#pragma unroll
+      for (int j = 0; j < U4; ++j)
+        if (u0 + j * NT < q4) *reinterpret_cast<float4*>(s.x + 4 * (u0 + j * NT)) = v[j];
+    }
+    constexpr int U = 8;                                  // the rest: U scalar loads in flight at once
+    for (int e0 = 4 * q4 + threadIdx.x; e0 < total; e0 += NT * U) {
       float v[U];
 #pragma unroll
       for (int j = 0; j < U; ++j) if (e0 + j * NT < total) v[j] = ld_cg(base + e0 + j * NT);
@@ -1243,13 +1261,50 @@ __device__ __forceinline__ void op_combine(KArgs& a, Smem& s, const Task in, uin
     }
     __syncthreads();
   }
-  if (mega) trace_mark(a, idx, 3);
+  if (mark) trace_mark(a, idx, 3);
   // Splits are read eight at a time with clamped indices, so the loads of a
   // group are independent of each other and of the running max / sums (one
   // shared-memory round trip per eight splits rather than per split).
   if (staged) combine_rows<HD>(s.x, out, r, a.NS, slot_sz, [](const float* p) { return *p; });
   else combine_rows<HD>(base, out, r, a.NS, slot_sz, [](const float* p) { return ld_cg(p); });
+}
+
+// COMBINE(b, g): merge the NS split partials of row b, group g into ATT_l.
+template <int HD>
+__device__ __forceinline__ void op_combine(KArgs& a, Smem& s, const Task in, uint32_t idx, bool mega) {
+  if (mega && !wait_tiles(a, in, idx)) return;
+  inject_delay(a, idx);
+  merge_splits<HD>(a, s, in.layer, in.a0, in.a1, mega, idx);
   if (mega) signal_tile(a, in);
+}
+
+// End of an attention split of a queue whose last split merges: count the
+// arrival on the (row, KV head) partial tile, whose target is NS + 1.  The
+// split whose count completes the NS arrivals (the fetch-add returns
+// target * (step + 1) - 2) merges the partials: every other split stored its
+// partial and waited for the stores' acknowledgement before its own count, so
+// the partials are in place, as for a consumer whose poll has returned.  It
+// then signals the tile once more, which is what the O-projection tiles wait
+// for.  Runs in every execution mode (the per-op kernels clear the counters
+// too).
+template <int HD>
+__device__ __forceinline__ void attn_arrive(KArgs& a, Smem& s, const Task in, uint32_t idx) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t before_last = a.targets[in.signal] * (in.step + 1) - 2;
+    const uint32_t old =
+        __hip_atomic_fetch_add(a.counters + in.signal, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s.idx[1] = old == before_last ? 1u : 0u;
+  }
+  __syncthreads();
+  const uint32_t last = __builtin_amdgcn_readfirstlane(s.idx[1]);
+  __syncthreads();
+  if (!last) return;
+  trace_mark(a, idx, 6);
+  inject_delay(a, idx + a.n_instr);
+  merge_splits<HD>(a, s, in.layer, in.a0, in.a1, false, idx);
+  signal_tile(a, in);
 }
 
 

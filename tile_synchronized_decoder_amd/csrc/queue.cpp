@@ -84,7 +84,10 @@ struct Builder {
     const uint32_t nX = cdiv(H, p.td), nQ = cdiv(NQKV, p.tq), nO = cdiv(H, p.to), nF = cdiv(F, p.tf);
     const uint32_t L0 = c.has_embed ? nX : 0;
     // fused: the split combines are dropped and each O-projection tile waits on
-    // the split partials itself (no attention-output tiles)
+    // the split partials' tiles (no attention-output tiles).  fuse_combine 1:
+    // the O-projection merges the partials itself.  2: the split whose signal
+    // completes a (row, KV head) merges them into the attention output and
+    // signals that tile once more, so its target is NS + 1.
     const bool fused = p.fuse_combine != 0;
     const uint32_t natt = fused ? 0 : M * nkv;
     const uint32_t per_layer = nQ + M * nkv + natt + nO + nF + nX;
@@ -139,7 +142,7 @@ struct Builder {
               tiles.push_back({t0, t1});
           }
           for (auto& t : tiles) att_waits[b * nkv + g].push_back({qkv_id(l, t.first), t.second - t.first + 1});
-          q->targets[op_id(l, b, g)] = NS;
+          q->targets[op_id(l, b, g)] = p.fuse_combine == 2 ? NS + 1 : NS;
         }
       for (uint32_t s = 0; s < NS; ++s)
         for (uint32_t t = 0; t < P; ++t) {
@@ -257,7 +260,7 @@ const char* validate(const mk_config& c, const mk_plan& p) {
   if (c.n_layers > 65535) return "too many layers";
   if (p.rows <= 0 || p.ctx_max <= 0) return "rows and ctx_max must be positive";
   if (p.n_queues < 1 || p.n_queues > kMaxQueues) return "n_queues out of range";
-  if (p.fuse_combine != 0 && p.fuse_combine != 1) return "fuse_combine must be 0 or 1";
+  if (p.fuse_combine < 0 || p.fuse_combine > 2) return "fuse_combine must be 0, 1 or 2";
   if (p.loop != 0 && p.loop != 1) return "loop must be 0 or 1";
   if (p.loop && (p.mode != MK_DECODE || !c.has_embed || !c.has_lm_head))
     return "a loop queue decodes a model with an embedding and an LM head";
@@ -344,7 +347,8 @@ mk_status mk_queue_export(const mk_queue* q, int32_t part, void* host_dst, size_
                         (uint32_t)p.ctx_max, q->n_splits, (uint32_t)q->cfg.n_layers,
                         (uint32_t)p.tq, (uint32_t)p.to, (uint32_t)p.tf, (uint32_t)p.td,
                         (uint32_t)p.kb, (uint32_t)p.bm, (uint32_t)p.bn,
-                        ((p.mode == MK_DECODE && p.fuse_combine) ? 1u : 0u) | (p.loop ? 2u : 0u)};
+                        ((p.mode == MK_DECODE && p.fuse_combine == 1) ? 1u : 0u) | (p.loop ? 2u : 0u) |
+                            ((p.mode == MK_DECODE && p.fuse_combine == 2) ? 4u : 0u)};
       std::memcpy(d, h, sizeof(h));
       if (!q->segments.empty()) std::memcpy(d + 80, q->segments.data(), 16 * q->segments.size());
       break;

@@ -64,6 +64,9 @@ class Plan:
     fuse_combine: decode only; 1 drops the split-combine instructions: each
     O-projection tile waits on the attention splits' partials and merges them
     itself while staging its inputs (one barrier hand-off fewer per layer).
+    2 drops them too: the split that completes a (row, KV head) merges its
+    partials into the attention output and signals the partial tile once more
+    (target NS + 1), and the O-projection tiles wait on those tiles.
     prefill_queues: sub-queues of the prefill queue (0: n_queues).  Prefill
     instructions are long, so shared sub-queues (workers pop dynamically) cost
     little and balance the causal attention tiles' unequal lengths.
