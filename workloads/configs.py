@@ -130,8 +130,14 @@ QWEN_8B = ModelConfig(
 
 
 # Plans of the benchmark workloads: one sub-queue per worker of an MI355X (256
-# compute units) and tile widths that give each GEMV op about 256 tiles.
+# compute units) and tile widths that give each GEMV op about 256 tiles.  At
+# batch 1 the last-arriving split merges the attention partials (fuse_combine
+# 2: one stage and barrier hop fewer per layer, 1% faster); with more rows
+# there are rows x KV heads merges per layer, which then land on the workers
+# whose splits end last, and separate combine tiles spread over all workers
+# are faster (5-19% at batch 4 to 32).
 PLAN_8B = Plan(tq=24, to=16, tf=56, td=16, n_queues=256)
+PLAN_8B_B1 = dataclasses.replace(PLAN_8B, fuse_combine=2)
 
 
 def _stream_ctx0(seed: int, batch: int, lo: int, hi: int) -> Tuple[int, ...]:
@@ -151,11 +157,11 @@ WORKLOADS = {
     "llama1b_b1": Workload(
         "llama1b_b1", LLAMA_1B,
         RunConfig(batch=1, ctx0=(1024,), steps=128, ctx_max=1152, seed=2),
-        Plan(tf=32, td=8, n_queues=256),
+        Plan(tf=32, td=8, n_queues=256, fuse_combine=2),
         "Llama-3-1B-shaped bf16, batch 1, 128 decode steps from a 1024-token cache"),
     "llama8b_b1": Workload(
         "llama8b_b1", LLAMA_8B,
-        RunConfig(batch=1, ctx0=(4096,), steps=128, ctx_max=4224, seed=3), PLAN_8B,
+        RunConfig(batch=1, ctx0=(4096,), steps=128, ctx_max=4224, seed=3), PLAN_8B_B1,
         "Llama-3-8B-shaped bf16, batch 1, context 4096"),
     "llama8b_b4": Workload(
         "llama8b_b4", LLAMA_8B,
@@ -168,7 +174,8 @@ WORKLOADS = {
     "qwen8b_prefill": Workload(
         "qwen8b_prefill", QWEN_8B,
         RunConfig(batch=1, ctx0=(2048,), steps=64, ctx_max=2112, seed=4, prefill_len=2048,
-                  init_cache=False), Plan(tq=24, to=16, tf=48, td=16, n_queues=256, prefill_queues=8),
+                  init_cache=False), Plan(tq=24, to=16, tf=48, td=16, n_queues=256, prefill_queues=8,
+                                          fuse_combine=2),
         "Qwen3-8B-shaped bf16 with QK-norm: prefill of 2048 tokens, then 64 decode steps"),
     "llama1b_stream_b32": Workload(
         "llama1b_stream_b32", LLAMA_1B,
