@@ -277,10 +277,15 @@ def run_workload(wl, args, modes, with_prefill=True):
         ev_end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         w0 = time.perf_counter()
+        # host time to enqueue one step: the least over the steps (a call that finds
+        # the device queue full blocks, which only adds)
+        host = []
         for t in range(K_steps):
             starts.append(torch.cuda.Event(enable_timing=True))
             starts[-1].record(stream)
+            h0 = time.perf_counter()
             step(t, mode, mids)
+            host.append(time.perf_counter() - h0)
         ev_end.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
@@ -289,7 +294,7 @@ def run_workload(wl, args, modes, with_prefill=True):
         per_step.append(starts[-1].elapsed_time(ev_end))
         res = {"ms_per_step": total_ms / K_steps, "tokens_per_s": B * K_steps / (total_ms / 1e3),
                "p50_ms": float(np.percentile(per_step, 50)), "p95_ms": float(np.percentile(per_step, 95)),
-               "host_wall_tokens_per_s": B * K_steps / wall}
+               "host_wall_tokens_per_s": B * K_steps / wall, "host_enqueue_us": 1e6 * min(host)}
         if mids:
             layers_ms = [starts[i].elapsed_time(mids[i]) for i in range(K_steps)]
             res["layers_ms"] = float(np.mean(layers_ms))           # reset + megakernel (or per-op launches)

@@ -101,10 +101,93 @@ def test_simulation_equals_longest_path_on_a_real_queue(name):
     assert step == pytest.approx(_longest_path(g, dur, 0.7))
 
 
-def test_kpo_step_counts_one_launch_per_layer_and_op():
+def test_kpo_step_counts_one_launch_per_segment():
     g = _graph([1, 2, 3, 2], [[], [], [], []], [0, 1, 2, 3], 4, 4)
-    g.layer = np.array([0, 0, 0, 1])
+    g.segments = [(1, 0, 0, 1), (2, 0, 1, 1), (3, 0, 2, 1), (2, 1, 3, 1)]
     assert P.kpo_step(g, {1: 1.0, 2: 2.0, 3: 3.0}, gap_us=0.5) == pytest.approx(1 + 2 + 3 + 2 + 4 * 0.5)
+
+
+def test_two_steps_chain_through_previous_step_waits():
+    """Loop queues: instruction 0 of step 1 waits on step 0's last barrier
+    (a previous-step range); one worker per instruction."""
+    g = _graph([2, 6], [[(1, 1 | P.PREV)], [(0, 1)]], [0, 1], 2, 2)
+    span1, _, _ = P.simulate(g, {2: 2.0, 6: 3.0}, hop=0.5, steps=1)
+    span2, start, _ = P.simulate(g, {2: 2.0, 6: 3.0}, hop=0.5, steps=2)
+    assert span1 == pytest.approx(2 + 0.5 + 3)
+    assert start[0] == pytest.approx(span1 + 0.5) and span2 == pytest.approx(2 * span1 + 0.5)
+
+
+def test_streams_partition_the_workers_and_overlap_segments():
+    """16 CUs and 2 streams: 8 workgroups per kernel.  Segment A (8 tiles of
+    2 us) and segment B (8 tiles of 3 us, each waiting on one A tile) run on
+    different streams: B's tiles start at A's ends plus the hand-off.  On one
+    stream, B's kernel starts after A's kernel ends."""
+    ops = [2] * 8 + [6] * 8
+    waits = [[]] * 8 + [[(k, 1)] for k in range(8)]
+    g = _graph(ops, waits, list(range(16)), 16, 16)
+    g.segments = [(2, 0, 0, 8), (6, 0, 8, 8)]
+    d = {2: 2.0, 6: 3.0}
+    assert P.ms_grid(2, 16) == 8 and P.ms_grid(1, 16) == 16
+    assert P.simulate_streams(g, d, 0.5, None, 2, 16, gap=1.0) == pytest.approx(1 + 2 + 0.5 + 3)
+    assert P.simulate_streams(g, d, 0.5, None, 1, 16, gap=1.0) == pytest.approx(1 + 2 + 1 + 3)
+    # two rounds: 16 tiles per segment on 8 workgroups (32 CUs, 4 streams); B's
+    # tile j + 8 waits for A's tile j + 8 (second round, ends at 4) and for its
+    # workgroup's tile j (ends at 5)
+    ops2 = [2] * 16 + [6] * 16
+    g2 = _graph(ops2, [[]] * 16 + [[(k, 1)] for k in range(16)], list(range(32)), 32, 32)
+    g2.segments = [(2, 0, 0, 16), (6, 0, 16, 16)]
+    assert P.ms_grid(4, 32) == 8
+    assert P.simulate_streams(g2, d, 0.0, None, 4, 32, gap=0.0) == pytest.approx(2 + 3 + 3)
+
+
+def _synthetic_workload(name="llama1b_b1", batch=None, n_layers=2):
+    import dataclasses
+    import tile_synchronized_decoder_amd as T
+    wl = W.configs.shrink(W.WORKLOADS[name], n_layers=n_layers, vocab=4096, batch=batch)
+    m, r, p = wl.model, wl.run, wl.plan
+    single = P.graph_from_parts(T.mk_build_queue(T.make_config(m), T.make_plan(p, T.MK_DECODE, r.batch,
+                                                                              r.ctx_max)).parts())
+    loop = P.graph_from_parts(T.mk_build_queue(T.make_config(m), T.make_plan(dataclasses.replace(p, loop=1),
+                                                                            T.MK_DECODE, r.batch, r.ctx_max)).parts())
+    t = P.Timings({1: 4.0, 2: 8.0, 3: 14.0, 4: 9.0, 5: 7.0, 6: 17.0, 7: 15.0}, lm_us=90.0, argmax_us=5.0,
+                  reset_us=4.5, ramp_us=4.0)
+    wb = {2: p.tq * m.hidden * 2, 5: p.to * m.attn_cols * 2, 6: 2 * p.tf * m.hidden * 2, 7: p.td * m.ffn * 2,
+          14: 64 * m.hidden * 2}
+    return P.Workload(name, single, loop, t, wb, 80 * 1024, r.batch, True, True)
+
+
+def test_calibration_recovers_planted_constants():
+    """Step times predicted with known constants; the fit on them returns
+    those constants (launch gaps, hand-off, occupancy, host lines)."""
+    w1 = _synthetic_workload()
+    w4 = _synthetic_workload(batch=4)
+    true = P.Calib(gap_us=0.4, graph_gap_us=0.2, hop_us=3.5, occupancy=1.3, host_call_us=25.0, host_launch_us=2.5,
+                   graph_call_us=40.0, graph_node_us=0.3)
+    meas = {d: v["step_us"] for d, v in P.predict(w1, true).items()}
+    mega4 = P.predict(w4, true, ("mega",))["mega"]["step_us"]
+    w3 = _synthetic_workload(n_layers=3)
+    host = [(w, d, v["host_us"]) for w in (w1, w4, w3) for d, v in P.predict(w, true).items() if d != "loop"]
+    got = P.calibrate(w1, meas, host, (w4, mega4))
+    for k in ("gap_us", "graph_gap_us", "hop_us", "occupancy", "host_call_us", "host_launch_us", "graph_call_us",
+              "graph_node_us"):
+        assert getattr(got, k) == pytest.approx(getattr(true, k), rel=1e-3, abs=1e-3), k
+
+
+def test_predictor_picks_on_the_committed_measurements():
+    """The committed kernel summaries and measured step times: every
+    workload's predicted best design is among the measured best (within 1%),
+    and the LM-head placement (separate kernel or inside the megakernel)
+    matches the measurement at every batch size."""
+    import os
+    prof = os.path.join(os.path.dirname(__file__), "..", "profiles")
+    names = ["layer256_f32", "llama1b_b1", "llama8b_b1", "llama8b_b4", "llama8b_b16", "llama1b_stream_b32",
+             "qwen8b_prefill"]
+    res = P.check(names, prof)
+    res.pop("calibration")
+    for n, e in res.items():
+        assert e["pick_ok"], (n, e["pick"], e["measured_best"])
+        if "measured_lm_head" in e:
+            assert e["lm_head"] == e["measured_lm_head"], n
 
 
 def test_kernel_names_map_to_ops():
@@ -132,5 +215,7 @@ def test_kernel_summary_tables_parse():
     path = os.path.join(os.path.dirname(__file__), "..", "profiles", "mk_interp_llama1b_b1_kernels.md")
     rows = P.read_kernel_stats_md(path)
     k = P.kpo_kernel_us(rows)
-    assert set(k) >= {2, 3, 4, 5, 6, 7} and all(v > 0 for v in k.values())
+    assert set(k) >= {2, 3, 5, 6, 7} and all(v > 0 for v in k.values())
     assert any("mk_interp<" in n for n, _ in rows)
+    t = P.Timings.from_rows(rows)
+    assert t.lm_us > 0 and t.argmax_us > 0 and t.reset_us > 0 and t.ramp_us == k[1]

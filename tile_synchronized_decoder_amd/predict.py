@@ -1,47 +1,68 @@
-"""Step-time predictor for a megakernel queue: one event pass over its tile graph.
+"""Step-time predictor: one event pass over a queue's tile graph per design.
 
-The "One Megakernel is Not Enough" abstract (arXiv 2610.35336) chooses where to
-cut a model into megakernels from conventional-graph profiles and standalone
-kernel timings, by simulating each candidate's tile and event graphs instead of
-running it.  This module does that for the two designs this library runs: the
-whole decode step as one megakernel, or one kernel per operator.
+The "One Megakernel is Not Enough" abstract chooses how to cut a model into
+kernels from standalone kernel timings, by simulating each candidate's tile
+and event graphs instead of running it, and checks the picks against
+measurement.  This module does that for the designs this library runs:
 
-What the queue fixes (the layout of mk_build_queue's parts):
-  * instruction i runs on worker i mod n_queues (one worker per sub-queue when
-    the queue has as many sub-queues as the grid has workgroups), in queue order;
-  * it waits on ranges of tile barriers and signals one barrier; a barrier is
-    complete once all instructions that signal it (its target) have ended.
+* ``mega``       the decode step as one persistent megakernel, then the LM
+                 head and argmax as separate kernels;
+* ``loop``       the LM head and argmax inside the megakernel (a loop queue,
+                 several steps per launch): the LM-head placement question;
+* ``kpo``        one kernel per (layer, op) segment in stream order, eager;
+* ``kpo_graph``  the same launches replayed from a HIP graph;
+* ``msS``        one kernel per segment on S streams, synchronised on tiles.
 
-Every barrier an instruction waits on is signalled only by earlier instructions
-(queue order is topological; the CPU checker verifies it), and a worker's
-previous instruction is earlier as well, so start and end times follow in a
-single pass in queue order.  Per instruction i on worker w:
+Inputs, all measured on their own: the per-op kernels of the kernel-per-op
+mode (one launch per op: rocprofv3 kernel statistics), the separate LM-head,
+argmax and counter-reset kernels, and the host's time to enqueue a step.
+Three constants come from one calibration workload and are then held fixed:
+the device gap between dependent kernel launches, the same inside a graph,
+and the megakernel's launch ramp.
 
-    free  = end of w's previous instruction (0 for its first)
-    ready = max over waited barriers b of done[b] + hop     (free if it waits on none)
-    lead  = min(prefetch[op], max(0, ready - free), dur[op])   (streamed while waiting)
-    end   = max(free, ready) + dur[op] - lead
+Model.  One instruction of op o takes dur[o] = (K_o - R) / rounds_o, where
+K_o is the op's per-op kernel time, R the time a launch of 256 near-empty
+workgroups takes (the per-op embedding kernel, else the reset kernel), and
+rounds_o = ceil(instructions / CUs).  An LM-head tile of a loop queue (no
+per-op kernel of its own) runs the decode GEMV body: its time is read off a
+straight line t0 + bytes / rate fitted to the GEMV ops' (weight bytes, dur)
+pairs.  The tile pass, per instruction i in queue order on its worker:
+
+    free  = end of the worker's previous instruction
+    ready = max over waited barriers b of done[b] + hop     (free if none)
+    lead  = min(prefetch[o], max(0, ready - free), dur[o])  (streamed while waiting)
+    end   = max(free, ready) + dur[o] - lead
     done[signal] = max(done[signal], end)
 
-dur[op] is one instruction's run time, hop the time from a producer's signal to
-a consumer seeing it and holding its inputs, prefetch[op] how much of an
-instruction's streaming fits the shared-memory ring it fills before it waits.
-The predicted step is the last end.  With kernel-per-op the same instructions
-run op by op, each op one launch whose time is a measured kernel time.
+Every waited barrier is signalled only by earlier instructions (queue order is
+topological; the CPU checker verifies it) and a worker's previous instruction
+is earlier too, so one pass in queue order gives every time.  The
+multi-stream pass is the same with each segment's instructions on the
+8 * floor(CUs / 8 / S) workgroups of its own kernel, which starts when the
+previous kernel of its stream (segment k - S) has ended.  A design's step is
+max(device time, host enqueue time): the host enqueues c_call + c_launch per
+launch, fitted to the measured enqueue times.
 
-Host only; no device code.  Inputs are the queue's exported parts and timings
-in microseconds.
+Host only; no device code.
 """
 from __future__ import annotations
 
+import json
+import math
 import re
 import struct
-from dataclasses import dataclass
+from dataclasses import dataclass, field
 from typing import Dict, List, Mapping, Optional, Sequence, Tuple
 
 import numpy as np
 
-OP_NAMES = {1: "EMBED", 2: "QKV", 3: "ATTN", 4: "COMBINE", 5: "OPROJ", 6: "GATEUP", 7: "DOWN"}
+OP_NAMES = {1: "EMBED", 2: "QKV", 3: "ATTN", 4: "COMBINE", 5: "OPROJ", 6: "GATEUP", 7: "DOWN",
+            14: "LMHEAD", 15: "ARGMAX"}
+OP_EMBED, OP_QKV, OP_ATTN, OP_COMBINE, OP_OPROJ, OP_GATEUP, OP_DOWN = 1, 2, 3, 4, 5, 6, 7
+OP_LMHEAD, OP_ARGMAX = 14, 15
+PREV = 0x80000000
+LM_TILE = 64
+XCDS = 8
 
 
 @dataclass
@@ -52,9 +73,11 @@ class Graph:
     wait_off: np.ndarray      # [n] first wait range
     wait_cnt: np.ndarray      # [n] number of wait ranges
     signal: np.ndarray        # [n] barrier signalled
-    ranges: np.ndarray        # [n_ranges, 2] (first barrier, count)
+    ranges: np.ndarray        # [n_ranges, 2] (first barrier, count with bit 31 = previous step)
     targets: np.ndarray       # [n_barriers]
     n_queues: int
+    segments: List[Tuple[int, int, int, int]] = field(default_factory=list)   # (op, layer, first, count)
+    flags: int = 0
 
 
 def graph_from_parts(parts: Mapping[str, bytes]) -> Graph:
@@ -62,87 +85,132 @@ def graph_from_parts(parts: Mapping[str, bytes]) -> Graph:
     meta = parts["meta"]
     if meta[:4] != b"TMK1":
         raise ValueError("not a queue META part")
-    n_queues = struct.unpack_from("<I", meta, 4 * 7)[0]
+    h = struct.unpack_from("<20I", meta, 0)
+    segs = [struct.unpack_from("<4I", meta, 80 + 16 * k) for k in range(h[6])]
     rec = np.frombuffer(parts["instr"], dtype="<u4").reshape(-1, 8)
     return Graph(op=(rec[:, 0] & 0xFFFF).astype(np.int64), layer=(rec[:, 0] >> 16).astype(np.int64),
                  wait_off=rec[:, 4].astype(np.int64), wait_cnt=rec[:, 5].astype(np.int64),
                  signal=rec[:, 6].astype(np.int64),
                  ranges=np.frombuffer(parts["waits"], dtype="<u4").reshape(-1, 2).astype(np.int64),
                  targets=np.frombuffer(parts["targets"], dtype="<u4").astype(np.int64),
-                 n_queues=int(n_queues))
+                 n_queues=int(h[7]), segments=[tuple(int(v) for v in s) for s in segs], flags=int(h[19]))
+
+
+def _waits(g: Graph, i: int):
+    """(same-step barrier runs, previous-step barrier runs) of instruction i."""
+    same, prev = [], []
+    for k in range(int(g.wait_off[i]), int(g.wait_off[i] + g.wait_cnt[i])):
+        f, c = int(g.ranges[k, 0]), int(g.ranges[k, 1])
+        (prev if c & PREV else same).append((f, c & ~PREV))
+    return same, prev
 
 
 def simulate(g: Graph, dur: Mapping[int, float], hop: float = 0.0,
              prefetch: Optional[Mapping[int, float]] = None,
-             n_workers: Optional[int] = None) -> Tuple[float, np.ndarray, np.ndarray]:
-    """Event pass over the schedule.  Returns (step, start, end) in the units of
-    `dur`.  With as many workers as sub-queues (the default) instruction i runs
-    on worker i mod n_queues.  With more workers than sub-queues, the workers
-    w, w + n_queues, ... share sub-queue w mod n_queues and pop from it in
-    order: each instruction goes to the one of them that is free first."""
+             n_workers: Optional[int] = None, steps: int = 1) -> Tuple[float, np.ndarray, np.ndarray]:
+    """Event pass over the megakernel's schedule.  Returns (span, start, end) in
+    the units of `dur`; start and end are those of the last step.  With as
+    many workers as sub-queues (the default) position k of the repeated queue
+    runs on worker k mod n_queues.  With more workers than sub-queues, the
+    workers w, w + n_queues, ... share sub-queue w mod n_queues and pop from it
+    in order: each instruction goes to the one of them that is free first.
+    ``steps`` > 1 (loop queues): the queue repeated, a previous-step wait
+    reading the previous step's barrier times."""
     nq = g.n_queues
     nw = n_workers or nq
     prefetch = prefetch or {}
     n = len(g.op)
+    done_prev = np.zeros(len(g.targets))
+    free = np.zeros(nw)
+    members = [np.arange(q, nw, nq) for q in range(min(nq, nw))] if nw > nq else None
+    waits = [_waits(g, i) for i in range(n)]
     start = np.zeros(n)
     end = np.zeros(n)
+    for t in range(steps):
+        done = np.zeros(len(g.targets))
+        for i in range(n):
+            k = t * n + i
+            if members is None:
+                w = k % nw
+            else:
+                mq = members[k % nq]
+                w = int(mq[np.argmin(free[mq])])
+            f = free[w]
+            ready = f
+            same, prev = waits[i]
+            for arr, runs in ((done, same), (done_prev, prev if t > 0 else [])):
+                for first, cnt in runs:
+                    ready = max(ready, float(arr[first:first + cnt].max()) + hop)
+            op = int(g.op[i])
+            d = dur[op]
+            lead = min(prefetch.get(op, 0.0), max(0.0, ready - f), d)
+            s = max(f, ready)
+            e = s + d - lead
+            start[i], end[i] = s, e
+            free[w] = e
+            sg = g.signal[i]
+            if e > done[sg]:
+                done[sg] = e
+        done_prev = done
+    return (float(free.max()) if n else 0.0), start, end
+
+
+def ms_grid(streams: int, n_cus: int, per_cu: int = 1) -> int:
+    """Workgroups per kernel of the multi-stream mode (a multiple of the XCDs)."""
+    return XCDS * ((per_cu * (n_cus // XCDS)) // streams)
+
+
+def simulate_streams(g: Graph, dur: Mapping[int, float], hop: float, prefetch: Optional[Mapping[int, float]],
+                     streams: int, n_cus: int, gap: float) -> float:
+    """Multi-stream mode: segment k is a kernel on stream k mod S with its own
+    ms_grid(S) workgroups striding over its instructions; it starts `gap`
+    after the previous kernel of its stream ends.  Returns the span."""
+    prefetch = prefetch or {}
+    G = ms_grid(streams, n_cus)
     done = np.zeros(len(g.targets))
-    free = np.zeros(nw)
-    # the workers of each sub-queue (a worker beyond the queue count shares one)
-    members = [np.arange(q, nw, nq) for q in range(min(nq, nw))] if nw > nq else None
-    rng = g.ranges
-    for i in range(n):
-        if members is None:
-            w = i % nw
-        else:
-            mq = members[i % nq]
-            w = int(mq[np.argmin(free[mq])])
-        f = free[w]
-        ready = f
-        o, c = g.wait_off[i], g.wait_cnt[i]
-        if c:
-            t = max(done[rng[k, 0]:rng[k, 0] + rng[k, 1]].max() for k in range(o, o + c)) + hop
-            ready = max(ready, t)
-        op = int(g.op[i])
-        d = dur[op]
-        lead = min(prefetch.get(op, 0.0), max(0.0, ready - f), d)
-        s = max(f, ready)
-        e = s + d - lead
-        start[i], end[i] = s, e
-        free[w] = e
-        sg = g.signal[i]
-        if e > done[sg]:
-            done[sg] = e
-    return (float(end.max()) if n else 0.0), start, end
+    sfree = [0.0] * streams
+    for k, (op, _layer, first, count) in enumerate(g.segments):
+        s = k % streams
+        kstart = sfree[s] + gap
+        wfree = [kstart] * min(G, count)
+        kend = kstart
+        for j in range(count):
+            i = first + j
+            w = j % G
+            f = wfree[w]
+            ready = f
+            for a, c in _waits(g, i)[0]:
+                ready = max(ready, float(done[a:a + c].max()) + hop)
+            d = dur[int(g.op[i])]
+            lead = min(prefetch.get(int(g.op[i]), 0.0), max(0.0, ready - f), d)
+            e = max(f, ready) + d - lead
+            wfree[w] = e
+            done[g.signal[i]] = max(done[g.signal[i]], e)
+            kend = max(kend, e)
+        sfree[s] = kend
+    return max(sfree)
 
 
 def op_counts(g: Graph) -> Dict[int, int]:
-    """Instructions per op per layer (the op's per-op launch size)."""
+    """Instructions per op in one (layer, op) segment (the op's per-op launch size)."""
     out: Dict[int, int] = {}
-    nl = int(g.layer.max()) + 1 if len(g.layer) else 1
-    for op in np.unique(g.op):
-        out[int(op)] = int((g.op == op).sum()) // (nl if op != 1 else 1)
+    for op, _layer, _first, count in g.segments:
+        out[op] = max(out.get(op, 0), count)
     return out
 
 
-def per_instruction_us(kernel_us: Mapping[int, float], counts: Mapping[int, int], n_cus: int) -> Dict[int, float]:
+def per_instruction_us(kernel_us: Mapping[int, float], counts: Mapping[int, int], n_cus: int,
+                       ramp_us: float = 0.0) -> Dict[int, float]:
     """One instruction's run time from a per-op kernel's time: a launch of n
-    instructions runs ceil(n / n_cus) rounds of concurrent workgroups."""
-    return {op: kernel_us[op] / max(1, -(-counts[op] // n_cus)) for op in kernel_us}
+    instructions pays the launch ramp once, then runs ceil(n / n_cus) rounds
+    of concurrent workgroups."""
+    return {op: max(kernel_us[op] - ramp_us, 0.05 * kernel_us[op]) / max(1, -(-counts[op] // n_cus))
+            for op in kernel_us if op in counts}
 
 
 def kpo_step(g: Graph, kernel_us: Mapping[int, float], gap_us: float) -> float:
-    """Kernel-per-op step: every (layer, op) launch in turn, plus a launch gap each."""
-    n_launch = 0
-    total = 0.0
-    seen = set()
-    for op, layer in zip(g.op.tolist(), g.layer.tolist()):
-        if (op, layer) in seen:
-            continue
-        seen.add((op, layer))
-        total += kernel_us[op]
-        n_launch += 1
-    return total + n_launch * gap_us
+    """Kernel-per-op layers: every (layer, op) launch in turn, plus a launch gap each."""
+    return sum(kernel_us[op] for op, *_ in g.segments) + len(g.segments) * gap_us
 
 
 _KPO_NAME = re.compile(r"kpo_kernel<[^,]+,\s*\d+,\s*(\d+)>")
@@ -179,46 +247,288 @@ def read_kernel_stats_md(path: str) -> List[Tuple[str, float]]:
     return out
 
 
+@dataclass
+class Timings:
+    """Standalone kernel times of one workload, µs."""
+    kernel_us: Dict[int, float]
+    lm_us: float = 0.0
+    argmax_us: float = 0.0
+    reset_us: float = 0.0
+    copy_us: float = 0.0
+    ramp_us: float = 0.0          # a launch of 256 near-empty workgroups
+
+    @staticmethod
+    def from_rows(rows: Sequence[Tuple[str, float]]) -> "Timings":
+        def avg(key):
+            v = [ns / 1000.0 for n, ns in rows if key in n]
+            return v[0] if v else 0.0
+        k = kpo_kernel_us(rows)
+        t = Timings(k, lm_us=avg("lm_head_"), argmax_us=avg("argmax_kernel"), reset_us=avg("reset_kernel"),
+                    copy_us=avg("copy_rows_kernel"))
+        t.ramp_us = k.get(OP_EMBED, t.reset_us)
+        return t
+
+
+def gemv_line(dur: Mapping[int, float], weight_bytes: Mapping[int, int]) -> Tuple[float, float]:
+    """Least-squares line dur = t0 + bytes / rate over the GEMV ops; (t0 µs, rate bytes/µs)."""
+    pts = [(weight_bytes[o], dur[o]) for o in (OP_QKV, OP_OPROJ, OP_GATEUP, OP_DOWN) if o in dur and o in weight_bytes]
+    x = np.array([p[0] for p in pts], dtype=np.float64)
+    y = np.array([p[1] for p in pts], dtype=np.float64)
+    slope, t0 = np.polyfit(x, y, 1)
+    return float(max(t0, 0.0)), float(1.0 / max(slope, 1e-12))
+
+
 def gemv_prefetch_us(dur: Mapping[int, float], weight_bytes: Mapping[int, int], ring_bytes: int) -> Dict[int, float]:
     """Time's worth of a GEMV instruction's weights that its ring holds before it
     waits: the ring's share of the instruction's weight bytes, times its run time."""
     return {op: min(1.0, ring_bytes / b) * dur[op] for op, b in weight_bytes.items() if op in dur}
 
 
-def main():
-    import argparse
+@dataclass
+class Calib:
+    """Constants fitted on calibration workloads (µs, or a factor)."""
+    gap_us: float = 0.3           # device gap between dependent launches, eager
+    graph_gap_us: float = 0.3     # the same inside a replayed graph
+    hop_us: float = 1.0           # tile hand-off: producer's signal to consumer running
+    occupancy: float = 1.0        # batched GEMV instruction in the interpreter / in its per-op kernel
+    host_call_us: float = 30.0    # host: enqueueing a step, fixed part
+    host_launch_us: float = 2.0   # host: per kernel launch
+    graph_call_us: float = 50.0   # host: a graph replay, fixed part
+    graph_node_us: float = 0.1    # host: per kernel node of the replayed graph
+
+
+@dataclass
+class Workload:
+    """What the predictor needs of one workload."""
+    name: str
+    single: Graph                 # the step's queue
+    loop: Optional[Graph]         # its loop queue (LM head inside), if the model has one
+    timings: Timings
+    weight_bytes: Dict[int, int]  # weight bytes of one instruction per GEMV op (and the LM-head tile)
+    ring_bytes: int
+    rows: int
+    has_lm: bool
+    has_embed: bool
+    n_cus: int = 256
+
+
+def _launches(w: Workload, design: str) -> float:
+    """Kernel launches the host enqueues per step."""
+    pre = 0 if w.has_embed else 1                       # input-row copy
+    lm = 2 if w.has_lm else 0
+    if design == "mega":
+        return pre + 2 + lm
+    if design in ("kpo", "kpo_graph"):
+        return pre + 1 + len(w.single.segments) + lm          # kernels (graph nodes)
+    if design == "loop":
+        return 0.0
+    if design.startswith("ms"):
+        s = int(design[2:])
+        return pre + 1 + len(w.single.segments) + 2 * s + 1 + lm
+    raise ValueError(design)
+
+
+def predict(w: Workload, c: Calib, designs: Sequence[str] = ("mega", "kpo", "kpo_graph", "loop", "ms2", "ms4"),
+            loop_steps: int = 32) -> Dict[str, Dict[str, float]]:
+    """Predicted device, host and step times (µs) of each design."""
+    t = w.timings
+    dur = per_instruction_us(t.kernel_us, op_counts(w.single), w.n_cus, t.ramp_us)
+    # the interpreter runs one wave per SIMD; a batched GEMV's per-op kernel runs
+    # several and hides more of its arithmetic latency
+    occ = c.occupancy if w.rows > 2 else 1.0
+    dur_mk = {o: v * (occ if o in (OP_QKV, OP_OPROJ, OP_GATEUP, OP_DOWN) else 1.0) for o, v in dur.items()}
+    pre = 0.0 if w.has_embed else t.copy_us
+    lm = (t.lm_us + t.argmax_us + 2 * c.gap_us) if w.has_lm else 0.0
+    pf = gemv_prefetch_us(dur_mk, w.weight_bytes, w.ring_bytes)
+    out: Dict[str, Dict[str, float]] = {}
+    for d in designs:
+        if d == "mega":
+            span, _, _ = simulate(w.single, dur_mk, c.hop_us, pf,
+                                  n_workers=w.n_cus if w.single.n_queues < w.n_cus else None)
+            # the launch of 256 persistent workgroups costs what a near-empty launch does
+            dev = pre + t.reset_us + t.ramp_us + span + lm + 2 * c.gap_us
+        elif d in ("kpo", "kpo_graph"):
+            gap = c.gap_us if d == "kpo" else c.graph_gap_us
+            lm_d = (t.lm_us + t.argmax_us + 2 * gap) if w.has_lm else 0.0
+            dev = pre + t.reset_us + kpo_step(w.single, t.kernel_us, gap) + lm_d + gap
+        elif d == "loop":
+            if w.loop is None or not w.has_lm:
+                continue
+            d2 = dict(dur_mk)
+            t0, rate = gemv_line(dur, w.weight_bytes)
+            d2[OP_LMHEAD] = (t0 + w.weight_bytes.get(OP_LMHEAD, 0) / rate) * occ
+            d2[OP_ARGMAX] = t.argmax_us
+            pf2 = gemv_prefetch_us(d2, w.weight_bytes, w.ring_bytes)
+            nw = w.n_cus if w.loop.n_queues < w.n_cus else None
+            s1, _, _ = simulate(w.loop, d2, c.hop_us, pf2, n_workers=nw, steps=1)
+            s2, _, _ = simulate(w.loop, d2, c.hop_us, pf2, n_workers=nw, steps=2)
+            per_step = s2 - s1
+            dev = per_step + (t.reset_us + t.ramp_us + s1 - per_step) / loop_steps
+        elif d.startswith("ms"):
+            # per-op kernels again (their occupancy), each paying its own launch
+            span = simulate_streams(w.single, dur, c.hop_us, gemv_prefetch_us(dur, w.weight_bytes, w.ring_bytes),
+                                    int(d[2:]), w.n_cus, c.gap_us + t.ramp_us)
+            dev = pre + t.reset_us + span + lm + 2 * c.gap_us
+        else:
+            raise ValueError(d)
+        if d == "loop":
+            host = c.host_call_us / loop_steps
+        elif d == "kpo_graph":
+            host = c.graph_call_us + c.graph_node_us * _launches(w, d)
+        else:
+            host = c.host_call_us + c.host_launch_us * _launches(w, d)
+        out[d] = {"device_us": dev, "host_us": host, "step_us": max(dev, host)}
+    return out
+
+
+def _fit(f, lo: float, hi: float, target: float) -> float:
+    """x in [lo, hi] with f(x) = target for an increasing f (bisection)."""
+    for _ in range(40):
+        mid = 0.5 * (lo + hi)
+        if f(mid) < target:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+def calibrate(w: Workload, measured_us: Mapping[str, float],
+              host_enqueue_us: Sequence[Tuple[Workload, str, float]] = (),
+              batched: Optional[Tuple[Workload, float]] = None, base: Optional[Calib] = None) -> Calib:
+    """Fit the constants: the launch gaps and the hand-off time on workload
+    ``w``'s measured steps (batch 1), the occupancy factor on a batched
+    workload's measured megakernel step, and the host line over every
+    (workload, design, enqueue µs) given, from GPU-bound workloads."""
+    c = Calib(**(base.__dict__ if base else {}))
+    t = w.timings
+    pre = 0.0 if w.has_embed else t.copy_us
+    lm_k = (t.lm_us + t.argmax_us) if w.has_lm else 0.0
+    n_lm = 2 if w.has_lm else 0
+    ksum = sum(t.kernel_us[op] for op, *_ in w.single.segments)
+    n_seg = len(w.single.segments)
+    c.gap_us = max(0.0, (measured_us["kpo"] - pre - t.reset_us - ksum - lm_k) / (n_seg + 1 + n_lm))
+    c.graph_gap_us = max(0.0, (measured_us["kpo_graph"] - pre - t.reset_us - ksum - lm_k) / (n_seg + 1 + n_lm))
+    def with_(**kw):
+        return Calib(**{**c.__dict__, **kw})
+    c.hop_us = _fit(lambda h: predict(w, with_(hop_us=h), ("mega",))["mega"]["device_us"], 0.0, 50.0,
+                    measured_us["mega"])
+    if batched is not None:
+        wb, mega_b = batched
+        c.occupancy = _fit(lambda f: predict(wb, with_(occupancy=f), ("mega",))["mega"]["device_us"], 0.5, 4.0,
+                           mega_b)
+    for graph in (False, True):
+        pts = [(_launches(wl, d), us) for wl, d, us in host_enqueue_us if (d == "kpo_graph") == graph]
+        if len({x for x, _ in pts}) >= 2:
+            slope, icpt = np.polyfit(np.array([x for x, _ in pts], dtype=np.float64),
+                                     np.array([y for _, y in pts], dtype=np.float64), 1)
+            if graph:
+                c.graph_node_us, c.graph_call_us = float(max(slope, 0.0)), float(max(icpt, 0.0))
+            else:
+                c.host_launch_us, c.host_call_us = float(max(slope, 0.0)), float(max(icpt, 0.0))
+    return c
+
+
+def co_best(times: Mapping[str, float], tol: float = 0.01) -> List[str]:
+    """The designs within `tol` of the fastest (measurements closer than that
+    are not told apart)."""
+    b = min(times.values())
+    return sorted(d for d, v in times.items() if v <= b * (1 + tol))
+
+
+def best(times: Mapping[str, float]) -> str:
+    return min(times, key=times.get)
+
+
+# ----------------------------------------------------------------------------- workloads from the library
+
+def workload(name: str, stats_rows: Sequence[Tuple[str, float]], n_cus: int = 256) -> Workload:
+    """Build the queues of a benchmark workload with the library and read its
+    standalone kernel times."""
+    import dataclasses
     import tile_synchronized_decoder_amd as T
     import workloads as W
-    ap = argparse.ArgumentParser(description="predict the megakernel decode step from per-op kernel times")
-    ap.add_argument("--workload", required=True)
-    ap.add_argument("--stats", required=True, help="kernel-time summary (.md) or rocprofv3 kernel_stats.csv "
-                                                   "holding the per-op kernels of that workload")
-    ap.add_argument("--hop", type=float, default=1.0, help="barrier hand-off, µs")
-    ap.add_argument("--cus", type=int, default=256)
-    a = ap.parse_args()
-    wl = W.WORKLOADS[a.workload]
+    wl = W.WORKLOADS[name]
     m, r, p = wl.model, wl.run, wl.plan
     q = T.mk_build_queue(T.make_config(m), T.make_plan(p, T.MK_DECODE, r.batch, r.ctx_max))
-    g = graph_from_parts(q.parts())
-    rows = read_kernel_stats_md(a.stats) if a.stats.endswith(".md") else read_kernel_stats_csv(a.stats)
-    kern = kpo_kernel_us(rows)
-    dur = per_instruction_us(kern, op_counts(g), a.cus)
+    single = graph_from_parts(q.parts())
+    loop = None
+    if m.has_embed and m.has_lm_head and m.dtype == "bf16":
+        ql = T.mk_build_queue(T.make_config(m), T.make_plan(dataclasses.replace(p, loop=1), T.MK_DECODE,
+                                                            r.batch, r.ctx_max))
+        loop = graph_from_parts(ql.parts())
     es = 2 if m.dtype == "bf16" else 4
     na = m.n_q_heads * m.head_dim
-    wbytes = {2: p.tq * m.hidden * es, 5: p.to * na * es, 6: 2 * p.tf * m.hidden * es, 7: p.td * m.ffn * es}
+    wbytes = {OP_QKV: p.tq * m.hidden * es, OP_OPROJ: p.to * na * es, OP_GATEUP: 2 * p.tf * m.hidden * es,
+              OP_DOWN: p.td * m.ffn * es, OP_LMHEAD: LM_TILE * m.hidden * es}
     ring = 4 * (20 if r.batch <= 2 else 16) * 1024          # four waves' weight rings (1 KB lines)
-    nw = a.cus if g.n_queues < a.cus else None
-    step, _, _ = simulate(g, dur, a.hop, gemv_prefetch_us(dur, wbytes, ring), n_workers=nw)
-    kpo = kpo_step(g, kern, 0.0)
-    mega = [avg / 1000.0 for name, avg in rows if "mk_interp<" in name]
-    line = {"workload": a.workload, "predicted_megakernel_us": round(step, 1), "kernel_per_op_sum_us": round(kpo, 1),
-            "pick": "megakernel" if step < kpo else "kernel-per-op"}
-    if mega:
-        line["measured_megakernel_us"] = round(mega[0], 1)
-        line["error_pct"] = round(100 * (step / mega[0] - 1), 1)
-        line["measured_pick"] = "megakernel" if mega[0] < kpo else "kernel-per-op"
-    import json
-    print(json.dumps(line))
+    return Workload(name, single, loop, Timings.from_rows(stats_rows), wbytes, ring, r.batch,
+                    m.has_lm_head, m.has_embed, n_cus)
+
+
+def read_mode_times(path: str) -> Dict[str, Dict[str, Dict[str, float]]]:
+    """Measured step times and host enqueue times, workload -> design -> {step_us, host_us},
+    from the JSON lines after the `measured:` marker of a predictor summary."""
+    out: Dict[str, Dict[str, Dict[str, float]]] = {}
+    on = False
+    with open(path) as f:
+        for line in f:
+            if line.startswith("<!-- measured"):
+                on = True
+                continue
+            if on and line.startswith("-->"):
+                break
+            if on and line.strip():
+                rec = json.loads(line)
+                out.setdefault(rec["workload"], {})[rec["design"]] = {"step_us": rec["step_us"],
+                                                                      "host_us": rec.get("host_us")}
+    return out
+
+
+def check(names: Sequence[str], profiles_dir: str, calib_on: str = "llama1b_b1",
+          calib_batched: str = "llama8b_b4") -> Dict[str, dict]:
+    """Predict every design of every workload from its kernel summary
+    (profiles/mk_interp_<name>_kernels.md), calibrating on one of them, and
+    compare with the measured times in profiles/predictor_check.md."""
+    import os
+    meas = read_mode_times(os.path.join(profiles_dir, "predictor_check.md"))
+    wls = {n: workload(n, read_kernel_stats_md(os.path.join(profiles_dir, f"mk_interp_{n}_kernels.md")))
+           for n in names}
+    # host enqueue times of GPU-bound workloads (steps far longer than enqueueing them)
+    host = [(wls[n], d, v["host_us"]) for n in names if n in meas and meas[n].get("mega", {}).get("step_us", 0) > 500
+            for d, v in meas[n].items() if v.get("host_us") and d in ("mega", "kpo", "kpo_graph", "ms2", "ms4")]
+    bat = (wls[calib_batched], meas[calib_batched]["mega"]["step_us"]) if calib_batched in wls else None
+    c = calibrate(wls[calib_on], {d: v["step_us"] for d, v in meas[calib_on].items()}, host, bat)
+    res = {"calibration": {"workloads": [calib_on, calib_batched],
+                           **{k: round(v, 3) for k, v in c.__dict__.items()}}}
+    for n in names:
+        pred = predict(wls[n], c)
+        m = {d: v["step_us"] for d, v in meas.get(n, {}).items() if d in pred}
+        p = {d: v["step_us"] for d, v in pred.items()}
+        entry = {"predicted_us": {d: round(v, 1) for d, v in p.items()},
+                 "measured_us": {d: round(v, 1) for d, v in m.items()},
+                 "error_pct": {d: round(100 * (p[d] / m[d] - 1), 1) for d in m},
+                 "pick": best({d: p[d] for d in m}), "measured_best": co_best(m) if m else []}
+        entry["pick_ok"] = entry["pick"] in entry["measured_best"]
+        if "loop" in p and "mega" in p:
+            entry["lm_head"] = "inside" if p["loop"] < p["mega"] else "separate"
+            if "loop" in m and "mega" in m:
+                entry["measured_lm_head"] = "inside" if m["loop"] < m["mega"] else "separate"
+        res[n] = entry
+    return res
+
+
+def main():
+    import argparse
+    import os
+    ap = argparse.ArgumentParser(description="predict the decode designs' step times from standalone kernel "
+                                             "timings and compare with measurement")
+    ap.add_argument("--profiles", default=os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                                       "profiles"))
+    ap.add_argument("--workloads", default="layer256_f32,llama1b_b1,llama8b_b1,llama8b_b4,llama8b_b16,"
+                                           "llama1b_stream_b32,qwen8b_prefill")
+    ap.add_argument("--calibrate-on", default="llama1b_b1")
+    a = ap.parse_args()
+    print(json.dumps(check(a.workloads.split(","), a.profiles, a.calibrate_on), indent=1))
 
 
 if __name__ == "__main__":
