@@ -103,6 +103,7 @@ inline size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
   size_t X, QKV, OPART, ATT, HRES, ACT, LMV, LMI, CTR, HEADS, ERR, total;
+  size_t LMY, LMS;                           // decode with an LM head: its rows as bf16 hi / lo, row scales
   size_t sX, sQKV, sOP, sATT, sHRES, sACT;   // per-layer strides in floats
   int lm_blocks;
   // prefill only: bf16 GEMM operands (hi and lo parts) and per-row sums of squares (after ERR)
@@ -135,6 +136,10 @@ Layout layout(const mk_queue* q) {
   o.CTR = off; off += up256(q->targets.size() * 4);
   o.HEADS = off; off += up256((size_t)q->plan.n_queues * 128);
   o.ERR = off; off += 256;
+  if (q->plan.mode == MK_DECODE && c.has_lm_head) {
+    o.LMY = off; off += up256(2 * M * c.hidden * 2);
+    o.LMS = off; off += up256(M * 4);
+  }
   if (q->plan.mode == MK_PREFILL) {
     // bf16 copies of the GEMM activation operands, written by their producer
     // tiles (with the consumer's RMSNorm gain folded in for X and HRES) as hi
@@ -256,6 +261,8 @@ void fill_args(const mk_queue* q, const void* d_queue, const mk_weights* w, cons
   a.sX = o.sX; a.sQKV = o.sQKV; a.sOP = o.sOP; a.sATT = o.sATT; a.sHRES = o.sHRES; a.sACT = o.sACT;
   a.lm_val = reinterpret_cast<float*>(ws + o.LMV); a.lm_idx = reinterpret_cast<int*>(ws + o.LMI);
   a.lm_blocks = o.lm_blocks;
+  a.lm_y = o.LMY ? reinterpret_cast<uint16_t*>(ws + o.LMY) : nullptr;
+  a.lm_rs = o.LMS ? reinterpret_cast<float*>(ws + o.LMS) : nullptr;
   if (q->plan.mode == MK_PREFILL) {
     a.XB = reinterpret_cast<uint16_t*>(ws + o.XB); a.XSS = reinterpret_cast<float*>(ws + o.XSS);
     a.HB = reinterpret_cast<uint16_t*>(ws + o.HB); a.HSS = reinterpret_cast<float*>(ws + o.HSS);
@@ -736,6 +743,8 @@ mk_status mk_lm_head(const mk_queue* q, const mk_weights* w, void* d_workspace, 
   a.X = reinterpret_cast<float*>(ws + o.X); a.sX = o.sX;
   a.lm_val = reinterpret_cast<float*>(ws + o.LMV); a.lm_idx = reinterpret_cast<int*>(ws + o.LMI);
   a.lm_blocks = o.lm_blocks; a.err = reinterpret_cast<uint32_t*>(ws + o.ERR);
+  a.lm_y = o.LMY ? reinterpret_cast<uint16_t*>(ws + o.LMY) : nullptr;
+  a.lm_rs = o.LMS ? reinterpret_cast<float*>(ws + o.LMS) : nullptr;
   a.r = c.n_q_heads / c.n_kv_heads; a.hd = c.head_dim;
   a.lm_x = a.X + (size_t)c.n_layers * a.sX;
   const LdsLayout ll = lds_layout(q);

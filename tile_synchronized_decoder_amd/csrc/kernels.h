@@ -59,6 +59,8 @@ template <int NB> constexpr int ring_lines() { return ring_lines_for(NB); }
 constexpr uint32_t ERR_TIMEOUT = 1, ERR_OPCODE = 2, ERR_CONTEXT = 3, ERR_TOKEN = 4;
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef __bf16 dbf16x8 __attribute__((ext_vector_type(8)));    // a matrix-core operand fragment
+typedef float df32x16 __attribute__((ext_vector_type(16)));    // a 32 x 32 accumulator fragment
 
 // ----------------------------------------------------------------------------- kernel arguments
 
@@ -94,6 +96,8 @@ struct Args {
   int seq_len, kv_row, M_cache;
   uint32_t lds_ring;             // bytes of the ring / prefill tile region
   const float* lm_x;             // LM head input rows
+  uint16_t* lm_y;                // [2][M][H]: the LM head's normalised rows as bf16 hi, lo (matrix-core head)
+  float* lm_rs;                  // [M]: their RMSNorm scales
   int gemv_pipe;                 // decode GEMV weight issue: 0, 1 pipelined; 2 compiler-ordered
   int fuse_combine;              // decode queue without split combines: O-projection merges the partials
   int merge_last;                // decode queue without split combines: the last split to arrive merges
@@ -1513,6 +1517,162 @@ __global__ __launch_bounds__(NT) void kpo_kernel(Args args, uint32_t first) {
   run_instr<WT, NB>(a, s, in, idx, false, OP);
 }
 
+// LM head on the matrix cores for 5 to 32 rows of bf16 weights: at several
+// rows the head is a skinny GEMM [M x H] x [H x V], which the vector units
+// run at a fraction of the HBM rate.  logits[b][v] = rms_b^-1 * sum_k y_b[k]
+// W[v][k] with y_b = x_b (.) g.  A first kernel writes y split per element into
+// bf16 hi and lo parts (each product is taken twice, as in the prefill GEMMs:
+// about 16 bits of y against the exact bf16 weights) and rms_b^-1; the
+// products accumulate in fp32.
+//
+// lm_prep_kernel: one workgroup per row.
+template <typename WT>
+__global__ __launch_bounds__(NT) void lm_prep_kernel(Args args) {
+  KArgs& a = kernel_args();
+  __shared__ float red[NWAVE];
+  const int b = blockIdx.x, H = a.H;
+  const float* x = a.lm_x + (size_t)b * H;
+  uint16_t* yh = a.lm_y + (size_t)b * H;
+  uint16_t* yl = a.lm_y + ((size_t)a.M + b) * H;
+  float ss = 0.f;
+  for (int k = 8 * threadIdx.x; k < H; k += 8 * NT) {
+    const float4 x0 = *reinterpret_cast<const float4*>(x + k), x1 = *reinterpret_cast<const float4*>(x + k + 4);
+    const float4 g0 = *reinterpret_cast<const float4*>(a.final_norm + k);
+    const float4 g1 = *reinterpret_cast<const float4*>(a.final_norm + k + 4);
+    const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    v4u hi, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ss = fmaf(xv[2 * e], xv[2 * e], ss);
+      ss = fmaf(xv[2 * e + 1], xv[2 * e + 1], ss);
+      const float y0 = xv[2 * e] * gv[2 * e], y1 = xv[2 * e + 1] * gv[2 * e + 1];
+      const uint32_t h0 = f32_to_bf16(y0), h1 = f32_to_bf16(y1);
+      hi[e] = h0 | (h1 << 16);
+      lo[e] = (uint32_t)f32_to_bf16(y0 - bf16_to_f32(h0)) | ((uint32_t)f32_to_bf16(y1 - bf16_to_f32(h1)) << 16);
+    }
+    *reinterpret_cast<v4u*>(yh + k) = hi;
+    *reinterpret_cast<v4u*>(yl + k) = lo;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float tot = 0.f;
+    for (int w = 0; w < NWAVE; ++w) tot += red[w];
+    a.lm_rs[b] = 1.0f / sqrtf(tot / (float)H + a.eps);
+  }
+}
+
+// lm_head_mfma: v_mfma_f32_32x32x16_bf16 with the vocabulary as the A rows and
+// the batch rows (zero past M) as the B columns.  Lane l holds A row / B
+// column l % 32; within a 64-column block its K step s carries columns
+// 32 (l / 32) + 8 s .. + 8 of both operands (one 64-byte piece of a weight row
+// per lane and block, the same permutation of k on both sides).  Wave w of
+// workgroup i owns vocabulary rows 512 i + 128 w .. + 128 as four 32-row
+// tiles; a block's weights and rows are loaded one block ahead.  Also writes
+// each 64-row block's (max, lowest index) per row for the argmax.
+constexpr int LMM_ROWS = 512;              // vocabulary rows per workgroup
+template <typename WT>                     // bf16 weights (uint16_t) only
+__global__ __launch_bounds__(NT) void lm_head_mfma(Args args) {
+  static_assert(sizeof(WT) == 2, "bf16 weights");
+  KArgs& a = kernel_args();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hf = lane >> 5, j = lane & 31;
+  const int H = a.H, V = a.V, M = a.M;
+  const int v0 = blockIdx.x * LMM_ROWS + wave * 128;
+  const WT* W = static_cast<const WT*>(a.lm_head);
+  const bool row_ok = j < M;
+  const uint16_t* yh = a.lm_y + (size_t)(row_ok ? j : 0) * H + 32 * hf;
+  const uint16_t* yl = a.lm_y + ((size_t)M + (row_ok ? j : 0)) * H + 32 * hf;
+  // the lane's four weight rows (clamped inside the vocabulary; rows past it are never stored)
+  const WT* wr[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) wr[t] = W + (size_t)min(v0 + 32 * t + j, V - 1) * H + 32 * hf;
+  struct Blk { v4u w[4][4]; v4u h[4], l[4]; };
+  auto load = [&](Blk& bk, int kb) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const v4u* p = reinterpret_cast<const v4u*>(wr[t] + kb);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) bk.w[t][s4] = p[s4];      // cached: the four pieces share a line
+    }
+    const v4u* ph = reinterpret_cast<const v4u*>(yh + kb);
+    const v4u* pl = reinterpret_cast<const v4u*>(yl + kb);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      bk.h[s4] = row_ok ? ph[s4] : v4u{0u, 0u, 0u, 0u};
+      bk.l[s4] = row_ok ? pl[s4] : v4u{0u, 0u, 0u, 0u};
+    }
+  };
+  df32x16 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
+  auto mul = [&](const Blk& bk) {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const dbf16x8 bh = __builtin_bit_cast(dbf16x8, bk.h[s4]), bl = __builtin_bit_cast(dbf16x8, bk.l[s4]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const dbf16x8 af = __builtin_bit_cast(dbf16x8, bk.w[t][s4]);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bh, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bl, acc[t], 0, 0, 0);
+      }
+    }
+  };
+  // blocks of 64 columns in pairs: the next block's loads go out before a block is multiplied
+  Blk ba, bb;
+  load(ba, 0);
+  for (int kb = 0; kb < H; kb += 128) {
+    load(bb, kb + 64);                                   // H is a multiple of 128
+    mul(ba);
+    if (kb + 128 < H) load(ba, kb + 128);
+    mul(bb);
+  }
+  const float sc = row_ok ? a.lm_rs[j] : 0.f;
+  float best[2] = {-INFINITY, -INFINITY};
+  int bidx[2] = {0x7FFFFFFF, 0x7FFFFFFF};
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // accumulator elements 4 q .. 4 q + 3: vocabulary rows 8 q + 4 hf .. + 3 of tile t
+      const int vr = v0 + 32 * t + 8 * q + 4 * hf;
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = acc[t][4 * q + e] * sc;
+      if (row_ok && a.logits) {
+        float* dst = a.logits + (size_t)j * V + vr;
+        if (vr + 3 < V) {
+          *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) if (vr + e < V) dst[e] = o[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (vr + e < V && (o[e] > best[t >> 1] || (o[e] == best[t >> 1] && vr + e < bidx[t >> 1]))) {
+          best[t >> 1] = o[e];
+          bidx[t >> 1] = vr + e;
+        }
+    }
+  // each 64-row block: the other half of its rows is in lane l ^ 32
+#pragma unroll
+  for (int p2 = 0; p2 < 2; ++p2) {
+    const float ov = __shfl_xor(best[p2], 32, 64);
+    const int oi = __shfl_xor(bidx[p2], 32, 64);
+    if (ov > best[p2] || (ov == best[p2] && oi < bidx[p2])) { best[p2] = ov; bidx[p2] = oi; }
+    const int blk = (v0 + 64 * p2) / LM_ROWS;
+    if (row_ok && hf == 0 && v0 + 64 * p2 < V) {
+      a.lm_val[(size_t)j * a.lm_blocks + blk] = best[p2];
+      a.lm_idx[(size_t)j * a.lm_blocks + blk] = bidx[p2];
+    }
+  }
+}
+
 // LM head: logits[b][v] = RMSNorm(X_L)[b] . W_lm[v] for 16 vocabulary rows per
 // workgroup, plus the block's (max, lowest index) per row for the argmax.
 template <typename WT, int NB>
@@ -1901,14 +2061,25 @@ struct Launch {
     return NB <= 4 && a.H % 8 == 0 && 4u * (NB * a.H + NWAVE * NB + NB + 2 * NWAVE * NB) <= 64 * 1024;
   }
   static hipError_t prep_lm(const Args& a) {
-    if (lm_regs(a)) return hipSuccess;
+    if (lm_regs(a) || lm_mfma(a)) return hipSuccess;
     static uint32_t granted[kMaxDevices] = {};
     return allow_lds(lm_head_kernel<WT, NB>, a.lds_bytes, granted);
+  }
+  // 5 to 32 rows of bf16 weights: the matrix-core LM head (H a multiple of 128)
+  static bool lm_mfma(const Args& a) {
+    return sizeof(WT) == 2 && a.M > 4 && a.M <= 32 && a.H % 128 == 0 && a.lm_y && a.lm_rs;
   }
   static hipError_t lm(const Args& a, hipStream_t st) {
     if (lm_regs(a)) {
       const uint32_t bytes = 4u * (NB * a.H + NWAVE * NB + NB + 2 * NWAVE * NB);
       hipLaunchKernelGGL((lm_head_regs<WT, NB>), dim3(a.lm_blocks), dim3(NT), bytes, st, a);
+    } else if (lm_mfma(a)) {
+      if constexpr (sizeof(WT) == 2) {
+        hipLaunchKernelGGL((lm_prep_kernel<WT>), dim3(a.M), dim3(NT), 0, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((lm_head_mfma<WT>), dim3((a.V + LMM_ROWS - 1) / LMM_ROWS), dim3(NT), 0, st, a);
+      }
     } else {
       hipLaunchKernelGGL((lm_head_kernel<WT, NB>), dim3(a.lm_blocks), dim3(NT), a.lds_bytes, st, a);
     }
