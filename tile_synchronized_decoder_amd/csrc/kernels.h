@@ -738,6 +738,160 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, 
   return true;
 }
 
+// Batched GEMV on the matrix cores (up to 32 input rows, bf16 weights, at most
+// 128 weight rows, K a multiple of 64; used for 32-row buckets).  With several input rows the vector
+// units' FMAs, not HBM, bound a GEMV; v_mfma_f32_32x32x16_bf16 takes the
+// weight rows as A rows (32 per row group) and the input rows as B columns
+// (zero past nb).  The inputs y = x (.) gain are split per element into bf16
+// hi and lo parts and each product is taken twice (about 16 bits of y against
+// the exact bf16 weights; fp32 accumulation), as in the prefill GEMMs and the
+// batched LM head.  Lane l holds A row / B column l % 32; within a 64-column
+// block its K step s carries columns 32 (l / 32) + 8 s .. + 8 of both operands
+// (one 64-byte piece of a weight row per lane and block).  The four waves take
+// contiguous quarters of the blocks and add their sums into s.res in wave
+// order; the first block's weights are loaded before the tile waits, and every
+// later block's weights and inputs one block ahead.  Leaves what gemv leaves:
+// s.res[row * NB + b] (normalised when asked) and the residual rows in s.resid.
+template <typename WT, int NB, int RPW, bool PIPE>
+__device__ __forceinline__ bool gemv_mfma(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, PIPE>& g, const float* x, int nb,
+                                          const float* gain, bool norm, bool mega, const Task in, uint32_t idx,
+                                          const float* resid, int resid_ld) {
+  constexpr int RGM = 4;                                 // row groups of 32
+  const int K = g.K, R = g.nrows;
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int hf = lane >> 5, r = lane & 31;
+  const int nblk = K / 64;
+  const int b_lo = wave * nblk / NWAVE, b_hi = (wave + 1) * nblk / NWAVE;
+  const int RG = (R + 31) / 32;
+  const WT* rp[RGM];
+  bool rok[RGM];
+#pragma unroll
+  for (int rg = 0; rg < RGM; ++rg) {
+    const int row = rg * 32 + r;
+    rok[rg] = rg < RG && row < R;
+    rp[rg] = g.row_ptr(rok[rg] ? row : 0) + 32 * hf;
+  }
+  const bool bok = r < nb;
+  const float* xr = x + (size_t)(bok ? r : 0) * K + 32 * hf;
+  struct WB { v4u w[RGM][4]; };
+  struct XB { float4 v[8]; };
+  auto load_w = [&](WB& d, int blk) {
+#pragma unroll
+    for (int rg = 0; rg < RGM; ++rg)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        d.w[rg][q] = (rok[rg] && blk < b_hi) ? reinterpret_cast<const v4u*>(rp[rg] + 64 * blk)[q]
+                                             : v4u{0u, 0u, 0u, 0u};
+  };
+  auto load_x = [&](XB& d, int blk) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      d.v[q] = (bok && blk < b_hi) ? ld_cg4(xr + 64 * blk + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  df32x16 acc[RGM];
+#pragma unroll
+  for (int rg = 0; rg < RGM; ++rg)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[rg][v] = 0.f;
+  float ss = 0.f;
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  auto mul = [&](const WB& w, const XB& xv, int blk) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 x0 = xv.v[2 * q], x1 = xv.v[2 * q + 1];
+      float y[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      if (norm) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
+      }
+      if (gain) {
+        const float* gp = gain + 64 * blk + 32 * hf + 8 * q;
+        const float4 g0 = *reinterpret_cast<const float4*>(gp), g1 = *reinterpret_cast<const float4*>(gp + 4);
+        y[0] *= g0.x; y[1] *= g0.y; y[2] *= g0.z; y[3] *= g0.w;
+        y[4] *= g1.x; y[5] *= g1.y; y[6] *= g1.z; y[7] *= g1.w;
+      }
+      v4u hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){y[2 * e], y[2 * e + 1]}, bf2));
+        hi[e] = h;
+        lo[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+            (f2){y[2 * e] - __uint_as_float(h << 16), y[2 * e + 1] - __uint_as_float(h & 0xFFFF0000u)}, bf2));
+      }
+      const dbf16x8 bh = __builtin_bit_cast(dbf16x8, hi), bl = __builtin_bit_cast(dbf16x8, lo);
+#pragma unroll
+      for (int rg = 0; rg < RGM; ++rg) {
+        if (rg < RG) {
+          const dbf16x8 af = __builtin_bit_cast(dbf16x8, w.w[rg][q]);
+          acc[rg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bh, acc[rg], 0, 0, 0);
+          acc[rg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bl, acc[rg], 0, 0, 0);
+        }
+      }
+    }
+  };
+  WB wa, wb;
+  XB xa, xb;
+  load_w(wa, b_lo);                                      // weights before the wait
+  if (mega && !wait_tiles(a, in, idx)) return false;
+  load_x(xa, b_lo);
+  // residual rows of the tile (O-projection, down), by all threads
+  if (resid) {
+    for (int e = t; e < R * nb; e += NT) {
+      const int row = e / nb, b = e - row * nb;
+      s.resid[row * NB + b] = ld_cg(resid + (size_t)b * resid_ld + row);
+    }
+  }
+  if (mega) trace_mark(a, idx, 3);
+  for (int blk = b_lo; blk < b_hi; blk += 2) {
+    load_w(wb, blk + 1);
+    load_x(xb, blk + 1);
+    mul(wa, xa, blk);
+    if (blk + 1 < b_hi) {
+      load_w(wa, blk + 2);
+      load_x(xa, blk + 2);
+      mul(wb, xb, blk + 1);
+    }
+  }
+  if (mega) trace_mark(a, idx, 4);
+  // the waves' sums into s.res, in wave order
+#pragma unroll
+  for (int w2 = 0; w2 < NWAVE; ++w2) {
+    if (wave == w2) {
+#pragma unroll
+      for (int rg = 0; rg < RGM; ++rg) {
+        if (rg >= RG) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = rg * 32 + 8 * (v / 4) + 4 * hf + (v % 4);
+          if (row < R && bok) {
+            float* p = s.res + row * NB + r;
+            *p = (w2 == 0 ? 0.f : *p) + acc[rg][v];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (norm) {
+    ss += __shfl_xor(ss, 32, 64);                        // both halves of each block
+    if (hf == 0) s.ssw[wave * 32 + r] = ss;
+    __syncthreads();
+    if (t < nb) {
+      float tot = 0.f;
+      for (int w = 0; w < NWAVE; ++w) tot += s.ssw[w * 32 + t];
+      s.ss[t] = 1.0f / sqrtf(tot / (float)K + a.eps);
+    }
+    __syncthreads();
+    for (int e = t; e < R * nb; e += NT) {
+      const int row = e / nb, b = e - row * nb;
+      s.res[row * NB + b] *= s.ss[b];
+    }
+    __syncthreads();
+  }
+  return true;
+}
+
 // Rows per wave per pass: 4 (16-row passes) up to 16 input rows, 2 for 32
 // (register pressure).  Tiles of at most 8 rows always use 2, so no wave
 // streams placeholder rows.
@@ -805,7 +959,19 @@ __device__ __forceinline__ void op_gemv_rpw(KArgs& a, Smem& s, const Task in, ui
   } else {
     x = a.ACT + l * a.sACT; resid = a.HRES + l * a.sHRES + n0; ld = a.H;
   }
-  if (!gemv<WT, NB, RPW, PIPE>(a, s, g, x, a.M, gain, gain != nullptr, mega, fused, in, idx, resid, ld)) return;
+  bool ok;
+  if constexpr (NB >= 32 && sizeof(WT) == 2) {
+    // 32 input rows on the matrix cores where the tile fits.  (At 4 and 16 rows
+    // the vector-unit GEMV, whose weight ring keeps 16 KB per wave in flight,
+    // is faster: this body's one block of look-ahead is too little there.)
+    if (!fused && g.nrows <= 128 && (g.K & 63) == 0)
+      ok = gemv_mfma<WT, NB, RPW, PIPE>(a, s, g, x, a.M, gain, gain != nullptr, mega, in, idx, resid, ld);
+    else
+      ok = gemv<WT, NB, RPW, PIPE>(a, s, g, x, a.M, gain, gain != nullptr, mega, fused, in, idx, resid, ld);
+  } else {
+    ok = gemv<WT, NB, RPW, PIPE>(a, s, g, x, a.M, gain, gain != nullptr, mega, fused, in, idx, resid, ld);
+  }
+  if (!ok) return;
   inject_delay(a, idx);
   {
     for (int e = threadIdx.x; e < n * a.M; e += NT) {
