@@ -232,6 +232,11 @@ LdsLayout lds_layout(const mk_config& c, const mk_plan& p) {
   const uint32_t r = c.n_q_heads / c.n_kv_heads, hd = c.head_dim;
   const uint32_t att = r4(r * hd) + 2 * r4(hd) + 2 * r4(hd / 2) + 2 * r4(NWAVE * ATT_MAX_R) + r4(NWAVE * r * hd);
   o.uni = std::max(o.ring / 4 + o.x, att);
+  // the matrix-core GEMV's staging (bf16 weights, batched rows), where it fits
+  if (c.dtype == MK_BF16 && nb >= MK_GEMV_MFMA_MIN_NB) {
+    const uint32_t need = gemv_mfma_floats(gemv_mfma_cc(1, nb), nb);
+    if (4 * (16 + 32 + NWAVE * 32 + 2 * o.res + need) <= kMaxLds) o.uni = std::max(o.uni, need);
+  }
   o.bytes = 4 * (16 + 32 + NWAVE * 32 + 2 * o.res + o.uni);
   if (o.x < fused_need) o.bytes = kMaxLds + 1;            // does not fit: refused by the callers
   return o;

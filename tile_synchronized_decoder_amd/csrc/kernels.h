@@ -54,6 +54,11 @@ constexpr int LM_ROWS = 64;             // vocabulary rows per LM-head workgroup
 #ifndef MK_RING_LINES_SMALL
 #define MK_RING_LINES_SMALL 20
 #endif
+// Smallest input-row bucket whose bf16 GEMVs run on the matrix cores (at one
+// and two rows the vector units keep up with HBM).
+#ifndef MK_GEMV_MFMA_MIN_NB
+#define MK_GEMV_MFMA_MIN_NB 4
+#endif
 constexpr int ring_lines_for(int nb) { return nb <= 2 ? MK_RING_LINES_SMALL : 16; }
 template <int NB> constexpr int ring_lines() { return ring_lines_for(NB); }
 constexpr uint32_t ERR_TIMEOUT = 1, ERR_OPCODE = 2, ERR_CONTEXT = 3, ERR_TOKEN = 4;
@@ -363,6 +368,8 @@ struct AttSmem {
   float* p;        // per-wave sums               [NWAVE * ATT_MAX_R]
   float* red;      // per-wave maxima             [NWAVE * ATT_MAX_R]
   float* part;     // per-wave outputs            [NWAVE * r * hd]
+  float* stage_f;  // matrix-core GEMV input staging: the whole shared region
+  int stage_floats;
 };
 struct Smem {
   uint32_t* idx;   // [0] current instruction index, [8..15] its record
@@ -400,6 +407,8 @@ __device__ __forceinline__ Smem make_smem(KArgs& a) {
   s.att.p = take(NWAVE * ATT_MAX_R);
   s.att.red = take(NWAVE * ATT_MAX_R);
   s.att.part = take(NWAVE * r * hd);
+  s.att.stage_f = reinterpret_cast<float*>(s.ring);       // weight ring, input staging and attention, as one region
+  s.att.stage_floats = (int)a.lds_union;
   return s;
 }
 
@@ -739,102 +748,167 @@ __device__ __forceinline__ bool gemv(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, 
 }
 
 // Batched GEMV on the matrix cores (up to 32 input rows, bf16 weights, at most
-// 128 weight rows, K a multiple of 64; used for 32-row buckets).  With several input rows the vector
+// 128 weight rows, K a multiple of the step width CC below).  With several input rows the vector
 // units' FMAs, not HBM, bound a GEMV; v_mfma_f32_32x32x16_bf16 takes the
-// weight rows as A rows (32 per row group) and the input rows as B columns
-// (zero past nb).  The inputs y = x (.) gain are split per element into bf16
-// hi and lo parts and each product is taken twice (about 16 bits of y against
-// the exact bf16 weights; fp32 accumulation), as in the prefill GEMMs and the
-// batched LM head.  Lane l holds A row / B column l % 32; within a 64-column
-// block its K step s carries columns 32 (l / 32) + 8 s .. + 8 of both operands
-// (one 64-byte piece of a weight row per lane and block).  The four waves take
-// contiguous quarters of the blocks and add their sums into s.res in wave
-// order; the first block's weights are loaded before the tile waits, and every
-// later block's weights and inputs one block ahead.  Leaves what gemv leaves:
-// s.res[row * NB + b] (normalised when asked) and the residual rows in s.resid.
-template <typename WT, int NB, int RPW, bool PIPE>
-__device__ __forceinline__ bool gemv_mfma(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, PIPE>& g, const float* x, int nb,
-                                          const float* gain, bool norm, bool mega, const Task in, uint32_t idx,
-                                          const float* resid, int resid_ld) {
-  constexpr int RGM = 4;                                 // row groups of 32
+// weight rows as A rows (RG groups of 32) and the input rows as B columns.
+// Each product is taken twice, with y = x (.) gain split per element into bf16
+// hi and lo parts (about 16 bits of y against the exact bf16 weights; fp32
+// accumulation), as in the prefill GEMMs and the batched LM head.  Lane l
+// holds A row / B column l % 32; within a 64-column block its K step q carries
+// columns 32 (l / 32) + 8 q .. + 8 of both operands (one 64-byte piece of a
+// weight row per lane and block).
+//
+// The work runs in steps of CC = 256 BPB columns, wave w taking BPB
+// consecutive blocks of each.  A step's weights come straight into registers
+// (one register set per step, the next step's set in flight while this one
+// is multiplied, the first before the tile waits).  Its inputs are staged in
+// shared memory (two buffers, rows padded by one float4 so that the lanes
+// reading one column of 8 rows hit distinct banks): each thread loads
+// its share of the next step's inputs (and of its gains) into registers before
+// issuing the next weight set, and after this step's products the gains go to
+// shared memory and the inputs, times their gains, to the other buffer.
+// The waves add their sums into s.res in wave order.  Leaves what gemv leaves:
+// s.res[row * NB + b] (normalised when asked) and s.resid.
+// Columns per step of the matrix-core GEMV below (256 per block of each of the
+// four waves: 4 / RG blocks, one at 3 or 4 row groups, at most 64 / NB so that
+// a thread's share of a step's inputs stays at 16 float4s), and the floats of
+// shared memory it stages (two input buffers and a step's gains) for a bucket
+// of nb input rows.
+constexpr int gemv_mfma_cc(int rg, int nb) {
+  return 256 * ((rg >= 3 ? 1 : 4 / rg) < 64 / nb ? (rg >= 3 ? 1 : 4 / rg) : 64 / nb);
+}
+constexpr int gemv_mfma_floats(int cc, int nb) { return 2 * nb * (cc + 4) + cc; }
+template <int RG, int NB>
+struct MfmaGemvShape {
+  static constexpr int CC = gemv_mfma_cc(RG, NB);       // columns per step
+  static constexpr int BPB = CC / 256;                   // blocks per wave and step
+  static constexpr int TPR = NT / NB;                    // staging threads per input row
+  static constexpr int XF = CC / 4 / TPR;                // float4s per thread and step
+};
+
+template <int RGc, bool GAIN, typename WT, int NB, int RPW, bool PIPE>
+__device__ __forceinline__ bool gemv_mfma_rg(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, PIPE>& g, const float* x,
+                                             int nb, const float* gain, bool norm, bool mega, const Task in,
+                                             uint32_t idx, const float* resid, int resid_ld) {
+  using SH = MfmaGemvShape<RGc, NB>;
+  constexpr int BPB = SH::BPB, CC = SH::CC, TPR = SH::TPR, XF = SH::XF;
+  static_assert(TPR >= 8 && TPR <= 64 && XF >= 1 && XF <= 16, "4 to 32 input rows");
   const int K = g.K, R = g.nrows;
-  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  // the thread index, opaque to the optimiser: the lane offsets below are then
+  // computed per call instead of being hoisted to the kernel's entry and
+  // spilled (a reload from scratch inside the loop waits for every load in flight)
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int hf = lane >> 5, r = lane & 31;
-  const int nblk = K / 64;
-  const int b_lo = wave * nblk / NWAVE, b_hi = (wave + 1) * nblk / NWAVE;
-  const int RG = (R + 31) / 32;
-  const WT* rp[RGM];
-  bool rok[RGM];
+  const int nstep = K / CC;                              // K is a multiple of CC (checked by the caller)
+  constexpr int PS = CC + 4;                             // padded row stride (floats)
+  float* xs = s.att.stage_f;                             // [2][NB][PS], then the step's gains [CC]
+  float4* gs = reinterpret_cast<float4*>(xs + 2 * NB * PS);
+  const WT* rp[RGc];
 #pragma unroll
-  for (int rg = 0; rg < RGM; ++rg) {
+  for (int rg = 0; rg < RGc; ++rg) {
     const int row = rg * 32 + r;
-    rok[rg] = rg < RG && row < R;
-    rp[rg] = g.row_ptr(rok[rg] ? row : 0) + 32 * hf;
+    rp[rg] = g.row_ptr(row < R ? row : 0) + 32 * hf;
   }
-  const bool bok = r < nb;
-  const float* xr = x + (size_t)(bok ? r : 0) * K + 32 * hf;
-  struct WB { v4u w[RGM][4]; };
-  struct XB { float4 v[8]; };
-  auto load_w = [&](WB& d, int blk) {
+  // Loads are unconditional, from pointers advanced in place by a uniform step
+  // (no address temporaries, so the compiler counts every load in flight and
+  // waits for exactly the set it multiplies); rows past R read row 0, unused,
+  // and the set after the last is the last again.
+  struct WB { v4u w[BPB * RGc][4]; };
+  const v4u* wp[RGc];
 #pragma unroll
-    for (int rg = 0; rg < RGM; ++rg)
+  for (int rg = 0; rg < RGc; ++rg) wp[rg] = reinterpret_cast<const v4u*>(rp[rg] + 64 * wave * BPB);
+  auto load_set = [&](WB& d, bool adv) {                 // the pointed-to set, then on to the next if adv
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        d.w[rg][q] = (rok[rg] && blk < b_hi) ? reinterpret_cast<const v4u*>(rp[rg] + 64 * blk)[q]
-                                             : v4u{0u, 0u, 0u, 0u};
+    for (int rg = 0; rg < RGc; ++rg) {
+#pragma unroll
+      for (int bi = 0; bi < BPB; ++bi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) d.w[bi * RGc + rg][q] = wp[rg][8 * bi + q];
+      wp[rg] += adv ? 32 * BPB : 0;                      // 4 BPB blocks of 8 v4u
+    }
   };
-  auto load_x = [&](XB& d, int blk) {
+  df32x16 acc[RGc];
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      d.v[q] = (bok && blk < b_hi) ? ld_cg4(xr + 64 * blk + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
-  };
-  df32x16 acc[RGM];
-#pragma unroll
-  for (int rg = 0; rg < RGM; ++rg)
+  for (int rg = 0; rg < RGc; ++rg)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[rg][v] = 0.f;
-  float ss = 0.f;
   typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
   typedef float f2 __attribute__((ext_vector_type(2)));
-  auto mul = [&](const WB& w, const XB& xv, int blk) {
+  // the lane's first column of the wave's step, in B column r's staged row
+  // (rows past nb hold row 0's inputs, unused)
+  const float4* xl = reinterpret_cast<const float4*>(xs + r * PS) + 16 * wave * BPB + 8 * hf;
+  auto mul_set = [&](const WB& d, int j) {
+    const float4* xb = xl + (j & 1) * NB * (PS / 4);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 x0 = xv.v[2 * q], x1 = xv.v[2 * q + 1];
-      float y[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      if (norm) {
+    for (int bi = 0; bi < BPB; ++bi) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
-      }
-      if (gain) {
-        const float* gp = gain + 64 * blk + 32 * hf + 8 * q;
-        const float4 g0 = *reinterpret_cast<const float4*>(gp), g1 = *reinterpret_cast<const float4*>(gp + 4);
-        y[0] *= g0.x; y[1] *= g0.y; y[2] *= g0.z; y[3] *= g0.w;
-        y[4] *= g1.x; y[5] *= g1.y; y[6] *= g1.z; y[7] *= g1.w;
-      }
-      v4u hi, lo;
+      for (int q = 0; q < 4; ++q) {
+        const float4 x0 = xb[16 * bi + 2 * q];
+        const float4 x1 = xb[16 * bi + 2 * q + 1];
+        const float y[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        v4u hi, lo;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){y[2 * e], y[2 * e + 1]}, bf2));
-        hi[e] = h;
-        lo[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
-            (f2){y[2 * e] - __uint_as_float(h << 16), y[2 * e + 1] - __uint_as_float(h & 0xFFFF0000u)}, bf2));
-      }
-      const dbf16x8 bh = __builtin_bit_cast(dbf16x8, hi), bl = __builtin_bit_cast(dbf16x8, lo);
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){y[2 * e], y[2 * e + 1]}, bf2));
+          hi[e] = h;
+          lo[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+              (f2){y[2 * e] - __uint_as_float(h << 16), y[2 * e + 1] - __uint_as_float(h & 0xFFFF0000u)}, bf2));
+        }
+        const dbf16x8 bh = __builtin_bit_cast(dbf16x8, hi), bl = __builtin_bit_cast(dbf16x8, lo);
 #pragma unroll
-      for (int rg = 0; rg < RGM; ++rg) {
-        if (rg < RG) {
-          const dbf16x8 af = __builtin_bit_cast(dbf16x8, w.w[rg][q]);
+        for (int rg = 0; rg < RGc; ++rg) {
+          const dbf16x8 af = __builtin_bit_cast(dbf16x8, d.w[bi * RGc + rg][q]);
           acc[rg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bh, acc[rg], 0, 0, 0);
           acc[rg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bl, acc[rg], 0, 0, 0);
         }
       }
     }
   };
+  // staging: thread t keeps input row t / TPR throughout (its sum of squares is
+  // one register) and the float4 slots t % TPR + TPR u of each step
+  const int sb = t / TPR, sq = t % TPR;
+  const float* xrow = x + (size_t)(sb < nb ? sb : 0) * K;
+  float4 xv[XF], gv;
+  float ssl = 0.f;
+  const float* xp = xrow + 4 * sq;
+  const float* gp = GAIN ? gain + 4 * (t % (CC / 4)) : nullptr;
+  auto issue_x = [&](bool adv) {                         // coherent loads of a step's inputs, and its gains
+#pragma unroll
+    for (int u = 0; u < XF; ++u) xv[u] = ld_cg4(xp + 4 * TPR * u);
+    xp += adv ? CC : 0;
+    if constexpr (GAIN) {
+      gv = *reinterpret_cast<const float4*>(gp);
+      gp += adv ? CC : 0;
+    }
+  };
+  // ... times the gains, into buffer j & 1; the sums of squares count only
+  // steps that exist.  Branch-free, so that no load is sunk past the next
+  // weight set (a load issued after it would wait for all of that set).
+  auto put_x = [&](int j, bool real) {
+    if constexpr (GAIN) {
+      gs[t % (CC / 4)] = gv;
+      __syncthreads();
+    }
+    float4* xw = reinterpret_cast<float4*>(xs + ((j & 1) * NB + sb) * PS) + sq;
+    const float4* gr = gs + sq;
+#pragma unroll
+    for (int u = 0; u < XF; ++u) {
+      float4 v = xv[u];
+      if constexpr (GAIN) {
+        const float sqs = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        ssl += real ? sqs : 0.f;
+        const float4 gg = gr[TPR * u];
+        v.x *= gg.x; v.y *= gg.y; v.z *= gg.z; v.w *= gg.w;
+      }
+      xw[TPR * u] = v;
+    }
+  };
   WB wa, wb;
-  XB xa, xb;
-  load_w(wa, b_lo);                                      // weights before the wait
+  load_set(wa, nstep > 1);                               // weights before the wait
   if (mega && !wait_tiles(a, in, idx)) return false;
-  load_x(xa, b_lo);
+  issue_x(nstep > 1);
   // residual rows of the tile (O-projection, down), by all threads
   if (resid) {
     for (int e = t; e < R * nb; e += NT) {
@@ -842,54 +916,75 @@ __device__ __forceinline__ bool gemv_mfma(KArgs& a, Smem& s, const Gemv<WT, NB, 
       s.resid[row * NB + b] = ld_cg(resid + (size_t)b * resid_ld + row);
     }
   }
+  put_x(0, true);
+  __syncthreads();
   if (mega) trace_mark(a, idx, 3);
-  for (int blk = b_lo; blk < b_hi; blk += 2) {
-    load_w(wb, blk + 1);
-    load_x(xb, blk + 1);
-    mul(wa, xa, blk);
-    if (blk + 1 < b_hi) {
-      load_w(wa, blk + 2);
-      load_x(xa, blk + 2);
-      mul(wb, xb, blk + 1);
-    }
+  // step j: next inputs and weights in flight, products of step j, inputs of
+  // step j + 1 into the other buffer (unrolled by two, so each register set
+  // keeps its registers)
+  auto step = [&](WB& cur, WB& nxt, int j) {
+    const bool adv = j + 2 < nstep;                      // (uniform) step j + 2 exists
+    issue_x(adv);
+    load_set(nxt, adv);
+    mul_set(cur, j);
+    put_x(j + 1, j + 1 < nstep);
+    __syncthreads();
+  };
+  for (int j = 0; j < nstep; j += 2) {
+    step(wa, wb, j);
+    if (j + 1 < nstep) step(wb, wa, j + 1);
   }
   if (mega) trace_mark(a, idx, 4);
-  // the waves' sums into s.res, in wave order
+  // each wave's sums into its own slice of the (now free) staging region, then
+  // s.res = ((w0 + w1) + w2) + w3, times the row's norm factor when asked
+  float* part = xs;                                      // [NWAVE][R][nb]
 #pragma unroll
-  for (int w2 = 0; w2 < NWAVE; ++w2) {
-    if (wave == w2) {
+  for (int rg = 0; rg < RGc; ++rg)
 #pragma unroll
-      for (int rg = 0; rg < RGM; ++rg) {
-        if (rg >= RG) continue;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = rg * 32 + 8 * (v / 4) + 4 * hf + (v % 4);
-          if (row < R && bok) {
-            float* p = s.res + row * NB + r;
-            *p = (w2 == 0 ? 0.f : *p) + acc[rg][v];
-          }
-        }
-      }
+    for (int v = 0; v < 16; ++v) {
+      const int row = rg * 32 + 8 * (v / 4) + 4 * hf + (v % 4);
+      if (row < R && r < nb) part[(wave * R + row) * nb + r] = acc[rg][v];
     }
-    __syncthreads();
+  if (GAIN && norm) {
+#pragma unroll
+    for (int off = TPR / 2; off >= 1; off >>= 1) ssl += __shfl_xor(ssl, off, 64);
+    if (sq == 0 && sb < nb) s.ss[sb] = 1.0f / sqrtf(ssl / (float)K + a.eps);
   }
-  if (norm) {
-    ss += __shfl_xor(ss, 32, 64);                        // both halves of each block
-    if (hf == 0) s.ssw[wave * 32 + r] = ss;
-    __syncthreads();
-    if (t < nb) {
-      float tot = 0.f;
-      for (int w = 0; w < NWAVE; ++w) tot += s.ssw[w * 32 + t];
-      s.ss[t] = 1.0f / sqrtf(tot / (float)K + a.eps);
-    }
-    __syncthreads();
-    for (int e = t; e < R * nb; e += NT) {
-      const int row = e / nb, b = e - row * nb;
-      s.res[row * NB + b] *= s.ss[b];
-    }
-    __syncthreads();
+  __syncthreads();
+  for (int e = t; e < R * nb; e += NT) {
+    const int row = e / nb, b = e - row * nb;
+    float v = part[e];
+#pragma unroll
+    for (int w = 1; w < NWAVE; ++w) v += part[w * R * nb + e];
+    s.res[row * NB + b] = GAIN && norm ? v * s.ss[b] : v;
   }
+  __syncthreads();
   return true;
+}
+
+// Whether the matrix-core GEMV takes a tile: K a multiple of its step width,
+// and the shared region holding its staging.
+template <int NB>
+__device__ __forceinline__ bool gemv_mfma_fits(const Smem& s, int nrows, int K) {
+  const int cc = gemv_mfma_cc((nrows + 31) / 32, NB);
+  return K % cc == 0 && gemv_mfma_floats(cc, NB) <= s.att.stage_floats;
+}
+
+template <typename WT, int NB, int RPW, bool PIPE>
+__device__ __forceinline__ bool gemv_mfma(KArgs& a, Smem& s, const Gemv<WT, NB, RPW, PIPE>& g, const float* x, int nb,
+                                          const float* gain, bool norm, bool mega, const Task in, uint32_t idx,
+                                          const float* resid, int resid_ld) {
+  // (the RMSNorm'd GEMVs carry a gain, the others none)
+#define MK_MFMA_RG(RG)                                                                             \
+  return gain ? gemv_mfma_rg<RG, true>(a, s, g, x, nb, gain, norm, mega, in, idx, resid, resid_ld) \
+              : gemv_mfma_rg<RG, false>(a, s, g, x, nb, gain, norm, mega, in, idx, resid, resid_ld)
+  switch ((g.nrows + 31) / 32) {
+    case 1: MK_MFMA_RG(1);
+    case 2: MK_MFMA_RG(2);
+    case 3: MK_MFMA_RG(3);
+    default: MK_MFMA_RG(4);
+  }
+#undef MK_MFMA_RG
 }
 
 // Rows per wave per pass: 4 (16-row passes) up to 16 input rows, 2 for 32
@@ -960,11 +1055,9 @@ __device__ __forceinline__ void op_gemv_rpw(KArgs& a, Smem& s, const Task in, ui
     x = a.ACT + l * a.sACT; resid = a.HRES + l * a.sHRES + n0; ld = a.H;
   }
   bool ok;
-  if constexpr (NB >= 32 && sizeof(WT) == 2) {
-    // 32 input rows on the matrix cores where the tile fits.  (At 4 and 16 rows
-    // the vector-unit GEMV, whose weight ring keeps 16 KB per wave in flight,
-    // is faster: this body's one block of look-ahead is too little there.)
-    if (!fused && g.nrows <= 128 && (g.K & 63) == 0)
+  if constexpr (NB >= MK_GEMV_MFMA_MIN_NB && sizeof(WT) == 2) {
+    // batched rows on the matrix cores where the tile and its staged inputs fit
+    if (!fused && g.nrows <= 128 && gemv_mfma_fits<NB>(s, g.nrows, g.K))
       ok = gemv_mfma<WT, NB, RPW, PIPE>(a, s, g, x, a.M, gain, gain != nullptr, mega, in, idx, resid, ld);
     else
       ok = gemv<WT, NB, RPW, PIPE>(a, s, g, x, a.M, gain, gain != nullptr, mega, fused, in, idx, resid, ld);
