@@ -187,7 +187,7 @@ def test_predictor_picks_on_the_committed_measurements():
     for n, e in res.items():
         assert e["pick_ok"], (n, e["pick"], e["measured_best"])
         if "measured_lm_head" in e:
-            assert e["lm_head"] == e["measured_lm_head"], n
+            assert e["measured_lm_head"] in (e["lm_head"], "either"), n
 
 
 def test_kernel_names_map_to_ops():

@@ -485,7 +485,7 @@ def read_mode_times(path: str) -> Dict[str, Dict[str, Dict[str, float]]]:
 
 
 def check(names: Sequence[str], profiles_dir: str, calib_on: str = "llama1b_b1",
-          calib_batched: str = "llama8b_b4") -> Dict[str, dict]:
+          calib_batched: str = "llama8b_b16") -> Dict[str, dict]:
     """Predict every design of every workload from its kernel summary
     (profiles/mk_interp_<name>_kernels.md), calibrating on one of them, and
     compare with the measured times in profiles/predictor_check.md."""
@@ -512,7 +512,9 @@ def check(names: Sequence[str], profiles_dir: str, calib_on: str = "llama1b_b1",
         if "loop" in p and "mega" in p:
             entry["lm_head"] = "inside" if p["loop"] < p["mega"] else "separate"
             if "loop" in m and "mega" in m:
-                entry["measured_lm_head"] = "inside" if m["loop"] < m["mega"] else "separate"
+                # within co_best's 1% the two placements are not told apart
+                tie = set(co_best({"loop": m["loop"], "mega": m["mega"]})) == {"loop", "mega"}
+                entry["measured_lm_head"] = "either" if tie else "inside" if m["loop"] < m["mega"] else "separate"
         res[n] = entry
     return res
 
