@@ -1776,9 +1776,10 @@ __global__ __launch_bounds__(NT) void kpo_kernel(Args args, uint32_t first) {
   run_instr<WT, NB>(a, s, in, idx, false, OP);
 }
 
-// LM head on the matrix cores for 5 to 32 rows of bf16 weights: at several
-// rows the head is a skinny GEMM [M x H] x [H x V], which the vector units
-// run at a fraction of the HBM rate.  logits[b][v] = rms_b^-1 * sum_k y_b[k]
+// LM head on the matrix cores for 2 to 32 rows of bf16 weights (where the
+// register-streaming kernel does not take them): at several rows the head is a
+// skinny GEMM [M x H] x [H x V], which the vector units run at a fraction of
+// the HBM rate.  logits[b][v] = rms_b^-1 * sum_k y_b[k]
 // W[v][k] with y_b = x_b (.) g.  A first kernel writes y split per element into
 // bf16 hi and lo parts (each product is taken twice, as in the prefill GEMMs:
 // about 16 bits of y against the exact bf16 weights) and rms_b^-1; the
@@ -2315,7 +2316,8 @@ struct Launch {
     return hipGetLastError();
   }
   // The LM head's kernel and its shared memory: for up to 4 rows the register
-  // streaming kernel (normalised rows + per-wave partials), else the ring GEMV.
+  // streaming kernel (normalised rows + per-wave partials) where they fit in
+  // 64 KB, else for bf16 weights the matrix cores, else the ring GEMV.
   static bool lm_regs(const Args& a) {
     return NB <= 4 && a.H % 8 == 0 && 4u * (NB * a.H + NWAVE * NB + NB + 2 * NWAVE * NB) <= 64 * 1024;
   }
@@ -2324,9 +2326,9 @@ struct Launch {
     static uint32_t granted[kMaxDevices] = {};
     return allow_lds(lm_head_kernel<WT, NB>, a.lds_bytes, granted);
   }
-  // 5 to 32 rows of bf16 weights: the matrix-core LM head (H a multiple of 128)
+  // 2 to 32 rows of bf16 weights: the matrix-core LM head (H a multiple of 128)
   static bool lm_mfma(const Args& a) {
-    return sizeof(WT) == 2 && a.M > 4 && a.M <= 32 && a.H % 128 == 0 && a.lm_y && a.lm_rs;
+    return sizeof(WT) == 2 && a.M >= 2 && a.M <= 32 && a.H % 128 == 0 && a.lm_y && a.lm_rs;
   }
   static hipError_t lm(const Args& a, hipStream_t st) {
     if (lm_regs(a)) {
