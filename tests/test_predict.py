@@ -219,3 +219,30 @@ def test_kernel_summary_tables_parse():
     assert any("mk_interp<" in n for n, _ in rows)
     t = P.Timings.from_rows(rows)
     assert t.lm_us > 0 and t.argmax_us > 0 and t.reset_us > 0 and t.ramp_us == k[1]
+
+
+def test_split_keys_follow_each_rows_context():
+    # attention instructions (row, head, split) of two rows with 100 and 300 keys, 128-key splits
+    g = _graph([3] * 6 + [5], [[]] * 7, [0] * 7, 1, 7)
+    g.args = np.array([[0, 0, 0], [0, 0, 1], [0, 0, 2], [1, 0, 0], [1, 0, 1], [1, 0, 2], [0, 0, 0]])
+    k = P.split_keys(g, [100, 300], 128)
+    assert k[:6].tolist() == [100, 0, 0, 128, 128, 44] and np.isnan(k[6])
+
+
+def test_attention_durations_match_the_per_op_kernel():
+    ramp, fixed = 5.0, 4.5
+    # one round of equal splits: each takes the kernel's net time
+    keys = np.full(256, 512.0)
+    d = P.attention_durations(105.0, ramp, keys, 1, 256, fixed)
+    assert d == pytest.approx(np.full(256, 100.0))
+    # two rounds of equal splits: the total over the CUs is the net time
+    d = P.attention_durations(105.0, ramp, np.full(512, 512.0), 1, 256, fixed)
+    assert d == pytest.approx(np.full(512, 50.0))
+    # ragged: a split with no keys costs the fixed part, and the spread total still matches
+    keys = np.r_[np.zeros(256), np.full(256, 1024.0)]
+    d = P.attention_durations(105.0, ramp, keys, 1, 256, fixed)
+    assert d[:256] == pytest.approx(np.full(256, fixed))
+    assert d.sum() / 256 == pytest.approx(100.0)
+    # two launches (layers) of one round each: per launch, as with one
+    d = P.attention_durations(105.0, ramp, np.full(512, 512.0), 2, 256, fixed)
+    assert d == pytest.approx(np.full(512, 100.0))

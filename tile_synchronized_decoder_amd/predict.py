@@ -23,7 +23,11 @@ and the megakernel's launch ramp.
 Model.  One instruction of op o takes dur[o] = (K_o - R) / rounds_o, where
 K_o is the op's per-op kernel time, R the time a launch of 256 near-empty
 workgroups takes (the per-op embedding kernel, else the reset kernel), and
-rounds_o = ceil(instructions / CUs).  An LM-head tile of a loop queue (no
+rounds_o = ceil(instructions / CUs).  Attention splits differ: split s of a
+row with P keys reduces clamp(P - s kb, 0, kb) of them, so one takes
+fixed + per_key * keys, with per_key such that the per-op launch (whose
+workgroups the hardware hands out as CUs free up) takes the larger of its
+longest split and its splits' total over the CUs.  An LM-head tile of a loop queue (no
 per-op kernel of its own) runs the decode GEMV body: its time is read off a
 straight line t0 + bytes / rate fitted to the GEMV ops' (weight bytes, dur)
 pairs.  The tile pass, per instruction i in queue order on its worker:
@@ -78,6 +82,7 @@ class Graph:
     n_queues: int
     segments: List[Tuple[int, int, int, int]] = field(default_factory=list)   # (op, layer, first, count)
     flags: int = 0
+    args: Optional[np.ndarray] = None    # [n, 3] the records' a0, a1, a2 (attention: row, KV head, split)
 
 
 def graph_from_parts(parts: Mapping[str, bytes]) -> Graph:
@@ -93,7 +98,8 @@ def graph_from_parts(parts: Mapping[str, bytes]) -> Graph:
                  signal=rec[:, 6].astype(np.int64),
                  ranges=np.frombuffer(parts["waits"], dtype="<u4").reshape(-1, 2).astype(np.int64),
                  targets=np.frombuffer(parts["targets"], dtype="<u4").astype(np.int64),
-                 n_queues=int(h[7]), segments=[tuple(int(v) for v in s) for s in segs], flags=int(h[19]))
+                 n_queues=int(h[7]), segments=[tuple(int(v) for v in s) for s in segs], flags=int(h[19]),
+                 args=rec[:, 1:4].astype(np.int64))
 
 
 def _waits(g: Graph, i: int):
@@ -107,7 +113,8 @@ def _waits(g: Graph, i: int):
 
 def simulate(g: Graph, dur: Mapping[int, float], hop: float = 0.0,
              prefetch: Optional[Mapping[int, float]] = None,
-             n_workers: Optional[int] = None, steps: int = 1) -> Tuple[float, np.ndarray, np.ndarray]:
+             n_workers: Optional[int] = None, steps: int = 1,
+             dur_i: Optional[np.ndarray] = None) -> Tuple[float, np.ndarray, np.ndarray]:
     """Event pass over the megakernel's schedule.  Returns (span, start, end) in
     the units of `dur`; start and end are those of the last step.  With as
     many workers as sub-queues (the default) position k of the repeated queue
@@ -115,7 +122,8 @@ def simulate(g: Graph, dur: Mapping[int, float], hop: float = 0.0,
     workers w, w + n_queues, ... share sub-queue w mod n_queues and pop from it
     in order: each instruction goes to the one of them that is free first.
     ``steps`` > 1 (loop queues): the queue repeated, a previous-step wait
-    reading the previous step's barrier times."""
+    reading the previous step's barrier times.  ``dur_i`` (per instruction, NaN
+    where the op's duration applies) overrides ``dur``."""
     nq = g.n_queues
     nw = n_workers or nq
     prefetch = prefetch or {}
@@ -142,7 +150,7 @@ def simulate(g: Graph, dur: Mapping[int, float], hop: float = 0.0,
                 for first, cnt in runs:
                     ready = max(ready, float(arr[first:first + cnt].max()) + hop)
             op = int(g.op[i])
-            d = dur[op]
+            d = dur[op] if dur_i is None or np.isnan(dur_i[i]) else float(dur_i[i])
             lead = min(prefetch.get(op, 0.0), max(0.0, ready - f), d)
             s = max(f, ready)
             e = s + d - lead
@@ -161,7 +169,7 @@ def ms_grid(streams: int, n_cus: int, per_cu: int = 1) -> int:
 
 
 def simulate_streams(g: Graph, dur: Mapping[int, float], hop: float, prefetch: Optional[Mapping[int, float]],
-                     streams: int, n_cus: int, gap: float) -> float:
+                     streams: int, n_cus: int, gap: float, dur_i: Optional[np.ndarray] = None) -> float:
     """Multi-stream mode: segment k is a kernel on stream k mod S with its own
     ms_grid(S) workgroups striding over its instructions; it starts `gap`
     after the previous kernel of its stream ends.  Returns the span."""
@@ -181,7 +189,7 @@ def simulate_streams(g: Graph, dur: Mapping[int, float], hop: float, prefetch: O
             ready = f
             for a, c in _waits(g, i)[0]:
                 ready = max(ready, float(done[a:a + c].max()) + hop)
-            d = dur[int(g.op[i])]
+            d = dur[int(g.op[i])] if dur_i is None or np.isnan(dur_i[i]) else float(dur_i[i])
             lead = min(prefetch.get(int(g.op[i]), 0.0), max(0.0, ready - f), d)
             e = max(f, ready) + d - lead
             wfree[w] = e
@@ -206,6 +214,51 @@ def per_instruction_us(kernel_us: Mapping[int, float], counts: Mapping[int, int]
     of concurrent workgroups."""
     return {op: max(kernel_us[op] - ramp_us, 0.05 * kernel_us[op]) / max(1, -(-counts[op] // n_cus))
             for op in kernel_us if op in counts}
+
+
+# Fixed part of an attention split (µs): reading q, k, v and rotating them after
+# its wait, merging the lane groups' and waves' softmax states, storing the
+# partial and signalling; from the batch-1 trace of the 8B step (1.5 + 3 µs).
+ATTN_FIXED_US = 4.5
+
+
+def split_keys(g: Graph, ctx: Sequence[int], kb: int) -> np.ndarray:
+    """Keys each attention instruction reduces (NaN for other ops): the split s
+    of row b covers keys [s kb, (s + 1) kb) of the row's ctx[b] (cache plus the
+    new token)."""
+    out = np.full(len(g.op), np.nan)
+    if g.args is None:
+        return out
+    at = g.op == OP_ATTN
+    b, s = g.args[at, 0], g.args[at, 2]
+    c = np.asarray(ctx, dtype=np.float64)[b]
+    out[at] = np.clip(c - s * kb, 0, kb)
+    return out
+
+
+def attention_durations(kernel_us: float, ramp_us: float, keys: np.ndarray, n_layers_ops: int, n_cus: int,
+                        fixed_us: float = ATTN_FIXED_US) -> np.ndarray:
+    """Per-instruction attention times fixed + per_key * keys (NaN elsewhere).
+    The per-op launch of one layer's splits hands workgroups out as CUs free
+    up, so its net time is the larger of its longest split and its splits' total
+    over the CUs; per_key is the value that makes that equal the measured kernel
+    time.  ``n_layers_ops``: the number of attention launches the instructions
+    span (one per layer)."""
+    out = np.full(len(keys), np.nan)
+    at = ~np.isnan(keys)
+    if not at.any():
+        return out
+    net = max(kernel_us - ramp_us, 0.05 * kernel_us)
+    k = keys[at]
+    n = k.size / max(1, n_layers_ops)                   # splits per launch
+    ksum = k.sum() / max(1, n_layers_ops)
+    kmax = float(k.max())
+    fixed = min(fixed_us, 0.9 * net)
+    p_one = (net - fixed) / kmax if kmax > 0 else np.inf        # bound by the longest split
+    p_all = (net * n_cus - fixed * n) / ksum if ksum > 0 else np.inf   # bound by the total
+    per_key = max(0.0, min(p_one, p_all))
+    out[at] = fixed + per_key * k
+    return out
 
 
 def kpo_step(g: Graph, kernel_us: Mapping[int, float], gap_us: float) -> float:
@@ -310,6 +363,8 @@ class Workload:
     has_lm: bool
     has_embed: bool
     n_cus: int = 256
+    ctx: Optional[Sequence[int]] = None   # keys each row's attention covers (cache plus the new token)
+    kb: int = 0                           # keys per attention split
 
 
 def _launches(w: Workload, design: str) -> float:
@@ -340,11 +395,20 @@ def predict(w: Workload, c: Calib, designs: Sequence[str] = ("mega", "kpo", "kpo
     pre = 0.0 if w.has_embed else t.copy_us
     lm = (t.lm_us + t.argmax_us + 2 * c.gap_us) if w.has_lm else 0.0
     pf = gemv_prefetch_us(dur_mk, w.weight_bytes, w.ring_bytes)
+
+    def attn_i(g: Graph) -> Optional[np.ndarray]:
+        # attention splits weighted by their keys (ragged contexts load workers unevenly)
+        if w.ctx is None or not w.kb or OP_ATTN not in t.kernel_us:
+            return None
+        n_launch = sum(1 for op, *_ in g.segments if op == OP_ATTN) or 1
+        return attention_durations(t.kernel_us[OP_ATTN], t.ramp_us, split_keys(g, w.ctx, w.kb), n_launch,
+                                   w.n_cus)
+    ai = attn_i(w.single)
     out: Dict[str, Dict[str, float]] = {}
     for d in designs:
         if d == "mega":
             span, _, _ = simulate(w.single, dur_mk, c.hop_us, pf,
-                                  n_workers=w.n_cus if w.single.n_queues < w.n_cus else None)
+                                  n_workers=w.n_cus if w.single.n_queues < w.n_cus else None, dur_i=ai)
             # the launch of 256 persistent workgroups costs what a near-empty launch does
             dev = pre + t.reset_us + t.ramp_us + span + lm + 2 * c.gap_us
         elif d in ("kpo", "kpo_graph"):
@@ -360,14 +424,15 @@ def predict(w: Workload, c: Calib, designs: Sequence[str] = ("mega", "kpo", "kpo
             d2[OP_ARGMAX] = t.argmax_us
             pf2 = gemv_prefetch_us(d2, w.weight_bytes, w.ring_bytes)
             nw = w.n_cus if w.loop.n_queues < w.n_cus else None
-            s1, _, _ = simulate(w.loop, d2, c.hop_us, pf2, n_workers=nw, steps=1)
-            s2, _, _ = simulate(w.loop, d2, c.hop_us, pf2, n_workers=nw, steps=2)
+            li = attn_i(w.loop)
+            s1, _, _ = simulate(w.loop, d2, c.hop_us, pf2, n_workers=nw, steps=1, dur_i=li)
+            s2, _, _ = simulate(w.loop, d2, c.hop_us, pf2, n_workers=nw, steps=2, dur_i=li)
             per_step = s2 - s1
             dev = per_step + (t.reset_us + t.ramp_us + s1 - per_step) / loop_steps
         elif d.startswith("ms"):
             # per-op kernels again (their occupancy), each paying its own launch
             span = simulate_streams(w.single, dur, c.hop_us, gemv_prefetch_us(dur, w.weight_bytes, w.ring_bytes),
-                                    int(d[2:]), w.n_cus, c.gap_us + t.ramp_us)
+                                    int(d[2:]), w.n_cus, c.gap_us + t.ramp_us, dur_i=ai)
             dev = pre + t.reset_us + span + lm + 2 * c.gap_us
         else:
             raise ValueError(d)
@@ -461,8 +526,9 @@ def workload(name: str, stats_rows: Sequence[Tuple[str, float]], n_cus: int = 25
     wbytes = {OP_QKV: p.tq * m.hidden * es, OP_OPROJ: p.to * na * es, OP_GATEUP: 2 * p.tf * m.hidden * es,
               OP_DOWN: p.td * m.ffn * es, OP_LMHEAD: LM_TILE * m.hidden * es}
     ring = 4 * (20 if r.batch <= 2 else 16) * 1024          # four waves' weight rings (1 KB lines)
+    ctx = [c0 + 1 for c0 in r.ctx0]                        # the first timed step's keys per row
     return Workload(name, single, loop, Timings.from_rows(stats_rows), wbytes, ring, r.batch,
-                    m.has_lm_head, m.has_embed, n_cus)
+                    m.has_lm_head, m.has_embed, n_cus, ctx=ctx, kb=p.kb)
 
 
 def read_mode_times(path: str) -> Dict[str, Dict[str, Dict[str, float]]]:

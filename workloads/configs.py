@@ -135,9 +135,16 @@ QWEN_8B = ModelConfig(
 # 2: one stage and barrier hop fewer per layer, 1% faster); with more rows
 # there are rows x KV heads merges per layer, which then land on the workers
 # whose splits end last, and separate combine tiles spread over all workers
-# are faster (5-19% at batch 4 to 32).
+# are faster (5-19% at batch 4 to 32).  With several rows the split size
+# is chosen so that rows x KV heads x splits about fills the 256 workers once
+# (8B at context 4224: 576 keys at batch 4, 2112 at batch 16): per-split work
+# (waiting, staging q, merging lane groups, writing partials) then repeats
+# fewer times per row; at batch 1 the 256-key splits keep their 1-round
+# balance with merges in the last split.
 PLAN_8B = Plan(tq=24, to=16, tf=56, td=16, n_queues=256)
 PLAN_8B_B1 = dataclasses.replace(PLAN_8B, fuse_combine=2)
+PLAN_8B_B4 = dataclasses.replace(PLAN_8B, kb=576)
+PLAN_8B_B16 = dataclasses.replace(PLAN_8B, kb=2112)
 
 
 def _stream_ctx0(seed: int, batch: int, lo: int, hi: int) -> Tuple[int, ...]:
@@ -165,11 +172,11 @@ WORKLOADS = {
         "Llama-3-8B-shaped bf16, batch 1, context 4096"),
     "llama8b_b4": Workload(
         "llama8b_b4", LLAMA_8B,
-        RunConfig(batch=4, ctx0=(4096,) * 4, steps=128, ctx_max=4224, seed=3), PLAN_8B,
+        RunConfig(batch=4, ctx0=(4096,) * 4, steps=128, ctx_max=4224, seed=3), PLAN_8B_B4,
         "Llama-3-8B-shaped bf16, batch 4, context 4096"),
     "llama8b_b16": Workload(
         "llama8b_b16", LLAMA_8B,
-        RunConfig(batch=16, ctx0=(4096,) * 16, steps=128, ctx_max=4224, seed=3), PLAN_8B,
+        RunConfig(batch=16, ctx0=(4096,) * 16, steps=128, ctx_max=4224, seed=3), PLAN_8B_B16,
         "Llama-3-8B-shaped bf16, batch 16, context 4096"),
     "qwen8b_prefill": Workload(
         "qwen8b_prefill", QWEN_8B,
@@ -180,7 +187,7 @@ WORKLOADS = {
     "llama1b_stream_b32": Workload(
         "llama1b_stream_b32", LLAMA_1B,
         RunConfig(batch=32, ctx0=_stream_ctx0(5, 32, 256, 8192), steps=256, ctx_max=8448, seed=5),
-        Plan(tf=32, td=8, kb=1024, n_queues=256),
+        Plan(tf=32, td=8, kb=2048, n_queues=256),
         "Llama-3-1B-shaped bf16 streaming decode, batch 32, contexts U{256..8192}, 256 steps"),
 }
 
