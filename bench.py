@@ -235,7 +235,7 @@ def run_workload(wl, args, modes, with_prefill=True):
             # the LM head and argmax inside it (teacher-forced with the same token ids)
             if not (m.has_embed and m.has_lm_head and m.dtype == "bf16"):
                 continue
-            ql = T.mk_build_queue(T.make_config(m), T.make_plan(dataclasses.replace(wl.plan, loop=1), T.MK_DECODE,
+            ql = T.mk_build_queue(T.make_config(m), T.make_plan(dataclasses.replace(wl.plan, loop=1, attn_pop=0), T.MK_DECODE,
                                                                 r.batch, r.ctx_max))
             dql, wsl = D.upload_queue(ql), D.workspace(ql)
             lg_all = torch.empty((K_steps, B, m.vocab), dtype=torch.float32, device="cuda")

@@ -120,6 +120,21 @@ typedef struct mk_plan {
                            * tiles wait on the previous step's argmax (flagged
                            * waits); needs an embedding and an LM head (0 or 1;
                            * recorded in bit 1 of the META word after bn) */
+  int32_t attn_pop;       /* decode, single-step queues: 1 = in the megakernel, a
+                           * layer's attention splits are handed out at run time
+                           * ("Production Megakernels" lecture summary, Technical
+                           * details: cores pop work atomically, so faster ones
+                           * pick up the slack).  The first worker to reach one
+                           * of its split positions in a layer takes splits in
+                           * queue order from a per-layer counter until none are
+                           * left, then skips its other split positions of that
+                           * layer.  Each split still waits on and signals its own
+                           * tiles, so results equal the static order's bit for
+                           * bit; with ragged contexts the workers' loads even
+                           * out.  Needs one sub-queue per worker (else the order
+                           * stays static); the other modes keep one split per
+                           * workgroup.  0 or 1; bit 3 of the META word after bn;
+                           * not with loop. */
 } mk_plan;
 
 typedef struct mk_queue mk_queue;   /* opaque, host memory */

@@ -65,7 +65,8 @@ Byte layout (little-endian), shared with the GPU library's C builder:
 META    u32 magic 'TMK1', version, mode, n_instr, n_barriers, n_wait_ranges, n_segments,
         n_queues, rows, ctx_max, n_splits, n_layers, tq, to, tf, td, kb, bm, bn, flags
         (bit 0: split combines fused into the O-projection; bit 1: multi-step loop queue;
-        bit 2: split combines merged by the last-arriving split),
+        bit 2: split combines merged by the last-arriving split; bit 3: attention
+        splits handed out at run time, same instructions),
         then n_segments x {u32 op, layer, first, count} (maximal runs of one op of one layer)
 INSTR   n_instr x 32 B {u16 op, u16 layer, u32 a0, a1, a2, wait_off, wait_cnt, signal, n_wait}
         (wait_off/wait_cnt index WAITS ranges; n_wait = barriers waited on in total)
@@ -219,6 +220,10 @@ def _check(model, plan, mode: int, rows: int, ctx_max: int) -> None:
         raise QueueError("loop must be 0 or 1")
     if getattr(plan, "loop", 0) and (mode != MODE_DECODE or not model.has_embed or not model.has_lm_head):
         raise QueueError("a loop queue decodes a model with an embedding and an LM head")
+    if getattr(plan, "attn_pop", 0) not in (0, 1):
+        raise QueueError("attn_pop must be 0 or 1")
+    if getattr(plan, "attn_pop", 0) and (mode != MODE_DECODE or getattr(plan, "loop", 0)):
+        raise QueueError("attn_pop is for single-step decode queues")
     if mode == MODE_DECODE:
         if rows > MAX_DECODE_ROWS:
             raise QueueError("decode rows above the maximum")
@@ -334,6 +339,8 @@ def build(model, plan, mode: int, rows: int, ctx_max: int) -> Queue:
     flags = (1 if fuse == 1 else 0) | (4 if fuse == 2 else 0)
     if getattr(plan, "loop", 0):
         flags |= 2
+    if getattr(plan, "attn_pop", 0):
+        flags |= 8                    # run-time hand-out of the splits: the same instructions
     q = Queue(mode, rows, ctx_max, NS, model.n_layers,
               (plan.tq, plan.to, plan.tf, plan.td, plan.kb, plan.bm, plan.bn), plan.n_queues, flags)
 

@@ -6,6 +6,7 @@ import dataclasses
 import os
 import re
 
+import numpy as np
 import pytest
 
 import tile_synchronized_decoder_amd as T
@@ -219,3 +220,50 @@ def test_builder_rejects_loop_without_lm_head():
     with pytest.raises(T.MkError):
         T.mk_build_queue(T.make_config(wl.model), T.make_plan(dataclasses.replace(wl.plan, loop=1), T.MK_DECODE,
                                                               1, 129))
+
+
+@pytest.mark.parametrize("name", ["llama1b_stream_b32", "llama8b_b1"])
+def test_builder_bytes_attn_pop(name):
+    """Run-time split hand-out: the same instructions, waits and targets as the
+    static queue, with bit 3 of the META flags word set; both builders agree."""
+    wl = W.WORKLOADS[name]
+    plan = dataclasses.replace(wl.plan, attn_pop=1)
+    got, ref = _both(wl.model, plan, QS.MODE_DECODE, wl.run.batch, wl.run.ctx_max)
+    assert got == ref
+    static, _ = _both(wl.model, dataclasses.replace(wl.plan, attn_pop=0), QS.MODE_DECODE, wl.run.batch,
+                      wl.run.ctx_max)
+    for part in got:
+        if part != "meta":
+            assert got[part] == static[part], part
+    flags = np.frombuffer(got["meta"][:80], dtype="<u4")[19]
+    assert flags & 8 and not np.frombuffer(static["meta"][:80], dtype="<u4")[19] & 8
+
+
+@pytest.mark.parametrize("bad", [dict(attn_pop=2), dict(attn_pop=-1), dict(attn_pop=1, loop=1)])
+def test_builder_rejects_bad_attn_pop(bad):
+    wl = W.WORKLOADS["llama1b_b1"]
+    plan = dataclasses.replace(wl.plan, **bad)
+    with pytest.raises(T.MkError):
+        T.mk_build_queue(T.make_config(wl.model), T.make_plan(plan, QS.MODE_DECODE, 1, wl.run.ctx_max))
+    with pytest.raises(QS.QueueError):
+        QS.build(wl.model, plan, QS.MODE_DECODE, 1, wl.run.ctx_max)
+
+
+def test_prefill_rejects_attn_pop():
+    wl = W.WORKLOADS["qwen8b_prefill"]
+    plan = dataclasses.replace(wl.plan, attn_pop=1)
+    with pytest.raises(T.MkError):
+        T.mk_build_queue(T.make_config(wl.model), T.make_plan(plan, QS.MODE_PREFILL, 256, 512))
+    with pytest.raises(QS.QueueError):
+        QS.build(wl.model, plan, QS.MODE_PREFILL, 256, 512)
+
+
+def test_workspace_holds_the_split_counters():
+    wl = W.WORKLOADS["llama1b_stream_b32"]
+    mk = lambda pop: T.mk_build_queue(T.make_config(wl.model),
+                                      T.make_plan(dataclasses.replace(wl.plan, attn_pop=pop), T.MK_DECODE,
+                                                  wl.run.batch, wl.run.ctx_max))
+    q0, q1 = mk(0), mk(1)
+    # one 128-byte counter line per layer after the sub-queue heads
+    grow = q1.workspace_offset(T.MK_T_ERROR) - q0.workspace_offset(T.MK_T_ERROR)
+    assert grow == ((256 + 16) * 128 + 255) // 256 * 256 - (256 * 128 + 255) // 256 * 256

@@ -404,3 +404,35 @@ def test_kpo_graph_replays_match_eager_and_megakernel():
     c.ws = torch.zeros_like(c.ws)
     again = run(T.MK_KERNEL_PER_OP_GRAPH)
     assert all(np.array_equal(x, y) for a, b in zip(eager, again) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("fuse", [0, 2])
+def test_attn_pop_matches_static_order_and_oracle(fuse):
+    """Attention splits handed out at run time (plan attn_pop): with ragged
+    contexts over 128-key splits the megakernel's results equal the static
+    order's and the per-op kernels' bit for bit, and the oracle's."""
+    from _gpucase import make_case, log
+    ctx0 = (1024, 37, 600, 1, 300, 900)
+    wl = W.shrink(W.WORKLOADS["llama1b_b1"], n_layers=2, vocab=4096, batch=len(ctx0), ctx0=ctx0, steps=1,
+                  name="llama1b_L2_B6_pop")
+    plans = {pop: W.Plan(tf=32, td=8, kb=128, n_queues=256, fuse_combine=fuse, attn_pop=pop) for pop in (0, 1)}
+    res = {}
+    for pop, plan in plans.items():
+        c = make_case(dataclasses.replace(wl, plan=plan))
+        for mode in (T.MK_MEGAKERNEL, T.MK_KERNEL_PER_OP):
+            c.reset_kv()
+            c.step(0, list(ctx0), mode)
+            err = T.mk_device_error(c.q, c.ws)
+            assert err.code == 0, (err.code, err.instr)
+            res[(pop, mode)] = (c.logits.cpu().numpy().copy(), c.tensor(T.MK_T_X, 2, 2048), c.kv_host()[0].copy())
+        if pop:
+            model = c.oracle_model()
+            tr = N.decode_step(model, c.K0.copy(), c.V0.copy(), list(ctx0), tokens=c.tokens[0])
+            c.reset_kv()
+            c.step(0, list(ctx0), T.MK_MEGAKERNEL)
+            check_step(c, tr, TOL_BF16)
+    ref = res[(0, T.MK_MEGAKERNEL)]
+    for key, got in res.items():
+        for a, b in zip(ref, got):
+            assert np.array_equal(a, b), key
+    log(f"    attn_pop, fuse {fuse}: megakernel and per-op, static and run-time hand-out identical")

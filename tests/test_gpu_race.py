@@ -13,8 +13,9 @@ any window in which a consumer could read a tile before its producer wrote it:
 
 Each poisoned, delayed run must give outputs bit-identical to a clean run, with
 no NaN, and the counters must end at their targets.  The runs cover the fp32
-layer and a two-layer 1B-shaped model, with one static sub-queue per worker and
-with shared sub-queues (dynamic pops), and the prefill interpreter.  A stress
+layer and a two-layer 1B-shaped model, with one static sub-queue per worker,
+with shared sub-queues (dynamic pops) and with the attention splits handed out
+at run time, and the prefill interpreter.  A stress
 run stops at its first failure.
 """
 import dataclasses
@@ -44,6 +45,8 @@ def _decode_cases():
     base = W.shrink(W.WORKLOADS["llama1b_b1"], n_layers=2, vocab=4096, batch=1, ctx0=(1024,), steps=1)
     b4 = W.shrink(W.WORKLOADS["llama1b_b1"], n_layers=2, vocab=4096, batch=4, ctx0=(1024, 37, 600, 1),
                   steps=1, name="llama1b_L2_B4")
+    b6 = W.shrink(W.WORKLOADS["llama1b_b1"], n_layers=2, vocab=4096, batch=6, ctx0=(1024, 37, 600, 1, 300, 900),
+                  steps=1, name="llama1b_L2_B6")
     return {
         "f32_layer_static": dataclasses.replace(f32, plan=dataclasses.replace(f32.plan, n_queues=ncu)),
         "f32_layer_shared8": dataclasses.replace(f32, plan=dataclasses.replace(f32.plan, n_queues=8)),
@@ -51,6 +54,11 @@ def _decode_cases():
         "bf16_1b_b4_shared8": dataclasses.replace(b4, plan=W.Plan(n_queues=8)),
         "bf16_1b_b1_fused_static": dataclasses.replace(base, plan=W.Plan(tf=32, td=8, n_queues=ncu,
                                                                          fuse_combine=1)),
+        # splits handed out at run time (ragged contexts, 128-key splits), with
+        # split combines and with the merge in the last split
+        "bf16_1b_b6_attn_pop": dataclasses.replace(b6, plan=W.Plan(tf=32, td=8, kb=128, n_queues=ncu, attn_pop=1)),
+        "bf16_1b_b6_attn_pop_merge": dataclasses.replace(b6, plan=W.Plan(tf=32, td=8, kb=128, n_queues=ncu,
+                                                                         attn_pop=1, fuse_combine=2)),
     }
 
 

@@ -35,7 +35,8 @@ def make_config(model) -> mk_config:
 
 def make_plan(plan, mode: int, rows: int, ctx_max: int) -> mk_plan:
     return mk_plan(mode, rows, ctx_max, plan.tq, plan.to, plan.tf, plan.td, plan.kb, plan.bm,
-                   plan.bn, plan.n_queues, getattr(plan, "fuse_combine", 0), getattr(plan, "loop", 0))
+                   plan.bn, plan.n_queues, getattr(plan, "fuse_combine", 0), getattr(plan, "loop", 0),
+                   getattr(plan, "attn_pop", 0))
 
 
 class Queue:

@@ -33,7 +33,7 @@ class mk_config(C.Structure):
 
 class mk_plan(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("mode", "rows", "ctx_max", "tq", "to", "tf", "td", "kb",
-                                         "bm", "bn", "n_queues", "fuse_combine", "loop")]
+                                         "bm", "bn", "n_queues", "fuse_combine", "loop", "attn_pop")]
 
 
 class mk_weights(C.Structure):

@@ -134,7 +134,8 @@ Layout layout(const mk_queue* q) {
   o.LMV = off; off += up256(M * o.lm_blocks * 4);
   o.LMI = off; off += up256(M * o.lm_blocks * 4);
   o.CTR = off; off += up256(q->targets.size() * 4);
-  o.HEADS = off; off += up256((size_t)q->plan.n_queues * 128);
+  // sub-queue heads, then (run-time split hand-out) one split counter per layer
+  o.HEADS = off; off += up256((size_t)(q->plan.n_queues + (q->plan.attn_pop ? L : 0)) * 128);
   o.ERR = off; off += 256;
   if (q->plan.mode == MK_DECODE && c.has_lm_head) {
     o.LMY = off; off += up256(2 * M * c.hidden * 2);
@@ -285,6 +286,22 @@ void fill_args(const mk_queue* q, const void* d_queue, const mk_weights* w, cons
   a.n_queues = (uint32_t)q->plan.n_queues;
   a.fuse_combine = q->plan.mode == MK_DECODE && q->plan.fuse_combine == 1;
   a.merge_last = q->plan.mode == MK_DECODE && q->plan.fuse_combine == 2;
+  // run-time split hand-out: the layers' attention segments, of equal size and
+  // evenly spaced (as the decode builder lays them out); else the static order
+  a.attn_pop = 0;
+  if (q->plan.mode == MK_DECODE && q->plan.attn_pop) {
+    std::vector<const mk::Segment*> at;
+    for (const mk::Segment& sg : q->segments)
+      if (sg.op == mk::OP_ATTN) at.push_back(&sg);
+    bool ok = !at.empty() && at.size() == (size_t)c.n_layers;
+    const uint32_t stride = at.size() > 1 ? at[1]->first - at[0]->first : 0;
+    for (size_t l = 0; ok && l < at.size(); ++l)
+      ok = at[l]->layer == l && at[l]->count == at[0]->count && at[l]->first == at[0]->first + l * stride;
+    if (ok) {
+      a.attn_pop = 1;
+      a.attn_first = at[0]->first; a.attn_stride = stride; a.attn_count = at[0]->count;
+    }
+  }
   const LdsLayout ll = lds_layout(q);
   a.lds_res = ll.res; a.lds_x = ll.x; a.lds_union = ll.uni; a.lds_bytes = ll.bytes; a.lds_ring = ll.ring;
   a.M_cache = kv && kv->rows > 0 ? kv->rows : q->plan.rows;
@@ -405,7 +422,9 @@ hipError_t enqueue_decode(const mk_queue* q, const Args& a, const Table& t, int 
   const bool mega = exec_mode == MK_MEGAKERNEL;
   // counters: the tile waits (megakernel, multi-stream) and the split arrivals
   // of a queue whose last split merges (every mode)
-  const uint32_t nr = mega || ss || a.merge_last ? a.n_barriers : 0, nh = mega ? a.n_queues : 0;
+  // heads: the sub-queues' pop counters and the layers' split counters
+  const uint32_t nr = mega || ss || a.merge_last ? a.n_barriers : 0;
+  const uint32_t nh = mega ? a.n_queues + (a.attn_pop ? (uint32_t)a.L : 0) : 0;
   hipLaunchKernelGGL(reset_kernel, dim3((nr + 255) / 256 + 1), dim3(256), 0, stream, a.counters, nr, a.heads, nh,
                      a.err);
   hipError_t e = hipGetLastError();

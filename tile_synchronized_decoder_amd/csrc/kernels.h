@@ -106,6 +106,11 @@ struct Args {
   int gemv_pipe;                 // decode GEMV weight issue: 0, 1 pipelined; 2 compiler-ordered
   int fuse_combine;              // decode queue without split combines: O-projection merges the partials
   int merge_last;                // decode queue without split combines: the last split to arrive merges
+  // megakernel, one sub-queue per worker: a layer's attention splits (the
+  // instructions attn_first + l * attn_stride + [0, attn_count)) are handed out
+  // from the layer's counter heads[(n_queues + l) * 32]
+  int attn_pop;
+  uint32_t attn_first, attn_stride, attn_count;
   uint32_t delay_seed;           // race check: seeded stall before each tile's stores (0: off)
   // persistent multi-step decode (loop queues): steps of the run, 1 = embed the
   // previous step's argmax (else tokens[step][row]), the argmax of every step
@@ -1652,7 +1657,7 @@ __device__ __forceinline__ void run_instr(KArgs& a, Smem& s, const Task in, uint
 // k / n_instr; the repeated queue is still in topological order (a step's
 // embedding waits only on the previous step's argmax), so the same argument
 // holds and the host launches once for all steps.
-template <typename WT, int NB, bool LOOP = false>
+template <typename WT, int NB, bool LOOP = false, bool POP = false>
 __global__ __launch_bounds__(NT) void mk_interp(Args args) {
   Smem s = make_smem(kernel_args());
   const uint32_t nq = args.n_queues;
@@ -1710,16 +1715,65 @@ __global__ __launch_bounds__(NT) void mk_interp(Args args) {
     const uint32_t idx = instr_of(pos);
     if (!fixed) in = load_instr(a, idx);
     if constexpr (LOOP) in.step = pos / a.n_instr;
-    unsigned long long t0 = 0;
-    if (a.trace) t0 = wall_clock64();
-    run_instr<WT, NB, LOOP>(a, s, in, idx, true, 0);
-    if (a.trace && threadIdx.x == 0) {
-      unsigned long long* rec = a.trace + TRACE_WORDS * (size_t)idx;
-      uint32_t xcc;
-      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-      rec[0] = ((unsigned long long)blockIdx.x << 32) | (xcc & 0xF);
-      rec[1] = t0;
-      rec[5] = wall_clock64();
+    if constexpr (!POP) {
+      unsigned long long t0 = 0;
+      if (a.trace) t0 = wall_clock64();
+      run_instr<WT, NB, LOOP>(a, s, in, idx, true, 0);
+      if (a.trace && threadIdx.x == 0) {
+        unsigned long long* rec = a.trace + TRACE_WORDS * (size_t)idx;
+        uint32_t xcc;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+        rec[0] = ((unsigned long long)blockIdx.x << 32) | (xcc & 0xF);
+        rec[1] = t0;
+        rec[5] = wall_clock64();
+      }
+      continue;
+    }
+    // Run-time hand-out of a layer's splits (the POP variant: plan attn_pop,
+    // one sub-queue per worker): at its first split position of a layer the
+    // worker takes splits in queue order from the layer's counter until none
+    // are left (each still waits on and signals its own tiles), then skips its
+    // other positions in the layer's split segment, which the counter has
+    // handed out.  One call site of the op bodies serves both orders.
+    const bool pop = fixed && in.op == mk::OP_ATTN;
+    const uint32_t f0 = pop ? a.attn_first + in.layer * a.attn_stride : 0, cnt = a.attn_count;
+    Task cur = in;
+    uint32_t id = idx;
+    for (;;) {
+      if (pop) {
+        if (threadIdx.x == 0) {                  // (a recorded error ends the hand-out)
+          const uint32_t t = __hip_atomic_fetch_add(a.heads + (a.n_queues + in.layer) * 32, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+          s.idx[2] = aborted(a) ? cnt : t;
+        }
+        __syncthreads();
+        const uint32_t tk = __builtin_amdgcn_readfirstlane(s.idx[2]);
+        __syncthreads();
+        if (tk >= cnt) break;
+        id = f0 + tk;
+        cur = load_instr(a, id);
+      }
+      unsigned long long t0 = 0;
+      if (a.trace) t0 = wall_clock64();
+      run_instr<WT, NB, LOOP>(a, s, cur, id, true, 0);
+      if (a.trace && threadIdx.x == 0) {
+        unsigned long long* rec = a.trace + TRACE_WORDS * (size_t)id;
+        uint32_t xcc;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+        rec[0] = ((unsigned long long)blockIdx.x << 32) | (xcc & 0xF);
+        rec[1] = t0;
+        rec[5] = wall_clock64();
+      }
+      if (!pop) break;
+    }
+    if (pop) {
+      // the first iteration whose position lies past the segment runs next
+      it = (f0 + cnt - qi + nq - 1) / nq - 1;
+      if (threadIdx.x < 8) {
+        const uint64_t j = (uint64_t)qi + (uint64_t)(it + 1) * nq;
+        word = j < total ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.instr + instr_of(j)) + threadIdx.x)
+                         : 0u;
+      }
     }
   }
   wait_vm<0>();                                  // no weight loads may outlive the workgroup
@@ -2243,6 +2297,11 @@ struct Launch {
   // any `per_cu` of them, from whichever kernels, fit together).
   static hipError_t prep(const Args& a, int exec_mode, int per_cu) {
     if (exec_mode == MK_MEGAKERNEL) {
+      if (a.attn_pop) {
+        static uint32_t granted[kMaxDevices] = {};
+        hipError_t e = allow_lds(mk_interp<WT, NB, false, true>, a.lds_bytes, granted);
+        return e == hipSuccess ? check_resident(mk_interp<WT, NB, false, true>, a.lds_bytes, per_cu) : e;
+      }
       static uint32_t granted[kMaxDevices] = {};
       hipError_t e = allow_lds(mk_interp<WT, NB>, a.lds_bytes, granted);
       return e == hipSuccess ? check_resident(mk_interp<WT, NB>, a.lds_bytes, per_cu) : e;
@@ -2275,7 +2334,10 @@ struct Launch {
     return e;
   }
   static hipError_t mega(const Args& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((mk_interp<WT, NB>), dim3(grid), dim3(NT), a.lds_bytes, st, a);
+    if (a.attn_pop)      // splits handed out at run time (a variant of its own: the default path's code is untouched)
+      hipLaunchKernelGGL((mk_interp<WT, NB, false, true>), dim3(grid), dim3(NT), a.lds_bytes, st, a);
+    else
+      hipLaunchKernelGGL((mk_interp<WT, NB>), dim3(grid), dim3(NT), a.lds_bytes, st, a);
     return hipGetLastError();
   }
   // Persistent multi-step decode: the interpreter over a loop queue, a.steps times.

@@ -262,6 +262,8 @@ const char* validate(const mk_config& c, const mk_plan& p) {
   if (p.n_queues < 1 || p.n_queues > kMaxQueues) return "n_queues out of range";
   if (p.fuse_combine < 0 || p.fuse_combine > 2) return "fuse_combine must be 0, 1 or 2";
   if (p.loop != 0 && p.loop != 1) return "loop must be 0 or 1";
+  if (p.attn_pop != 0 && p.attn_pop != 1) return "attn_pop must be 0 or 1";
+  if (p.attn_pop && (p.mode != MK_DECODE || p.loop)) return "attn_pop is for single-step decode queues";
   if (p.loop && (p.mode != MK_DECODE || !c.has_embed || !c.has_lm_head))
     return "a loop queue decodes a model with an embedding and an LM head";
   if (p.mode == MK_DECODE) {
@@ -348,7 +350,7 @@ mk_status mk_queue_export(const mk_queue* q, int32_t part, void* host_dst, size_
                         (uint32_t)p.tq, (uint32_t)p.to, (uint32_t)p.tf, (uint32_t)p.td,
                         (uint32_t)p.kb, (uint32_t)p.bm, (uint32_t)p.bn,
                         ((p.mode == MK_DECODE && p.fuse_combine == 1) ? 1u : 0u) | (p.loop ? 2u : 0u) |
-                            ((p.mode == MK_DECODE && p.fuse_combine == 2) ? 4u : 0u)};
+                            ((p.mode == MK_DECODE && p.fuse_combine == 2) ? 4u : 0u) | (p.attn_pop ? 8u : 0u)};
       std::memcpy(d, h, sizeof(h));
       if (!q->segments.empty()) std::memcpy(d + 80, q->segments.data(), 16 * q->segments.size());
       break;

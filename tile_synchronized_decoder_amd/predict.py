@@ -114,7 +114,8 @@ def _waits(g: Graph, i: int):
 def simulate(g: Graph, dur: Mapping[int, float], hop: float = 0.0,
              prefetch: Optional[Mapping[int, float]] = None,
              n_workers: Optional[int] = None, steps: int = 1,
-             dur_i: Optional[np.ndarray] = None) -> Tuple[float, np.ndarray, np.ndarray]:
+             dur_i: Optional[np.ndarray] = None,
+             pop_segments: Sequence[Tuple[int, int]] = ()) -> Tuple[float, np.ndarray, np.ndarray]:
     """Event pass over the megakernel's schedule.  Returns (span, start, end) in
     the units of `dur`; start and end are those of the last step.  With as
     many workers as sub-queues (the default) position k of the repeated queue
@@ -123,7 +124,10 @@ def simulate(g: Graph, dur: Mapping[int, float], hop: float = 0.0,
     in order: each instruction goes to the one of them that is free first.
     ``steps`` > 1 (loop queues): the queue repeated, a previous-step wait
     reading the previous step's barrier times.  ``dur_i`` (per instruction, NaN
-    where the op's duration applies) overrides ``dur``."""
+    where the op's duration applies) overrides ``dur``.  ``pop_segments``
+    (first, count): segments handed out at run time (one sub-queue per worker):
+    the workers holding a position in the segment take its instructions in
+    queue order, each going to the one of them that is free first."""
     nq = g.n_queues
     nw = n_workers or nq
     prefetch = prefetch or {}
@@ -134,9 +138,30 @@ def simulate(g: Graph, dur: Mapping[int, float], hop: float = 0.0,
     waits = [_waits(g, i) for i in range(n)]
     start = np.zeros(n)
     end = np.zeros(n)
+    pop_at = {f: c for f, c in pop_segments if c > 0}
     for t in range(steps):
         done = np.zeros(len(g.targets))
-        for i in range(n):
+        i = 0
+        while i < n:
+            if i in pop_at and members is None:
+                cnt = pop_at[i]
+                part = np.unique((t * n + i + np.arange(min(cnt, nw))) % nw)
+                for j in range(i, i + cnt):
+                    w = int(part[np.argmin(free[part])])
+                    f = free[w]
+                    ready = f
+                    for first, c in waits[j][0]:
+                        ready = max(ready, float(done[first:first + c].max()) + hop)
+                    op = int(g.op[j])
+                    d = dur[op] if dur_i is None or np.isnan(dur_i[j]) else float(dur_i[j])
+                    s = max(f, ready)
+                    e = s + d
+                    start[j], end[j] = s, e
+                    free[w] = e
+                    if e > done[g.signal[j]]:
+                        done[g.signal[j]] = e
+                i += cnt
+                continue
             k = t * n + i
             if members is None:
                 w = k % nw
@@ -159,6 +184,7 @@ def simulate(g: Graph, dur: Mapping[int, float], hop: float = 0.0,
             sg = g.signal[i]
             if e > done[sg]:
                 done[sg] = e
+            i += 1
         done_prev = done
     return (float(free.max()) if n else 0.0), start, end
 
@@ -365,6 +391,7 @@ class Workload:
     n_cus: int = 256
     ctx: Optional[Sequence[int]] = None   # keys each row's attention covers (cache plus the new token)
     kb: int = 0                           # keys per attention split
+    attn_pop: bool = False                # the megakernel hands the splits out at run time
 
 
 def _launches(w: Workload, design: str) -> float:
@@ -384,8 +411,11 @@ def _launches(w: Workload, design: str) -> float:
 
 
 def predict(w: Workload, c: Calib, designs: Sequence[str] = ("mega", "kpo", "kpo_graph", "loop", "ms2", "ms4"),
-            loop_steps: int = 32) -> Dict[str, Dict[str, float]]:
-    """Predicted device, host and step times (µs) of each design."""
+            loop_steps: int = 32, host_us: Optional[Mapping[str, Optional[float]]] = None
+            ) -> Dict[str, Dict[str, float]]:
+    """Predicted device, host and step times (µs) of each design.  ``host_us``:
+    the workload's own measured host enqueue time per design, where there is
+    one (measured on the host alone); else the fitted host lines."""
     t = w.timings
     dur = per_instruction_us(t.kernel_us, op_counts(w.single), w.n_cus, t.ramp_us)
     # the interpreter runs one wave per SIMD; a batched GEMV's per-op kernel runs
@@ -407,8 +437,11 @@ def predict(w: Workload, c: Calib, designs: Sequence[str] = ("mega", "kpo", "kpo
     out: Dict[str, Dict[str, float]] = {}
     for d in designs:
         if d == "mega":
+            pops = [(f, cnt) for op, _l, f, cnt in w.single.segments if op == OP_ATTN] \
+                if w.attn_pop and w.single.n_queues >= w.n_cus else []
             span, _, _ = simulate(w.single, dur_mk, c.hop_us, pf,
-                                  n_workers=w.n_cus if w.single.n_queues < w.n_cus else None, dur_i=ai)
+                                  n_workers=w.n_cus if w.single.n_queues < w.n_cus else None, dur_i=ai,
+                                  pop_segments=pops)
             # the launch of 256 persistent workgroups costs what a near-empty launch does
             dev = pre + t.reset_us + t.ramp_us + span + lm + 2 * c.gap_us
         elif d in ("kpo", "kpo_graph"):
@@ -436,7 +469,9 @@ def predict(w: Workload, c: Calib, designs: Sequence[str] = ("mega", "kpo", "kpo
             dev = pre + t.reset_us + span + lm + 2 * c.gap_us
         else:
             raise ValueError(d)
-        if d == "loop":
+        if host_us and host_us.get(d) is not None:
+            host = float(host_us[d])
+        elif d == "loop":
             host = c.host_call_us / loop_steps
         elif d == "kpo_graph":
             host = c.graph_call_us + c.graph_node_us * _launches(w, d)
@@ -518,7 +553,7 @@ def workload(name: str, stats_rows: Sequence[Tuple[str, float]], n_cus: int = 25
     single = graph_from_parts(q.parts())
     loop = None
     if m.has_embed and m.has_lm_head and m.dtype == "bf16":
-        ql = T.mk_build_queue(T.make_config(m), T.make_plan(dataclasses.replace(p, loop=1), T.MK_DECODE,
+        ql = T.mk_build_queue(T.make_config(m), T.make_plan(dataclasses.replace(p, loop=1, attn_pop=0), T.MK_DECODE,
                                                             r.batch, r.ctx_max))
         loop = graph_from_parts(ql.parts())
     es = 2 if m.dtype == "bf16" else 4
@@ -528,7 +563,7 @@ def workload(name: str, stats_rows: Sequence[Tuple[str, float]], n_cus: int = 25
     ring = 4 * (20 if r.batch <= 2 else 16) * 1024          # four waves' weight rings (1 KB lines)
     ctx = [c0 + 1 for c0 in r.ctx0]                        # the first timed step's keys per row
     return Workload(name, single, loop, Timings.from_rows(stats_rows), wbytes, ring, r.batch,
-                    m.has_lm_head, m.has_embed, n_cus, ctx=ctx, kb=p.kb)
+                    m.has_lm_head, m.has_embed, n_cus, ctx=ctx, kb=p.kb, attn_pop=bool(getattr(p, "attn_pop", 0)))
 
 
 def read_mode_times(path: str) -> Dict[str, Dict[str, Dict[str, float]]]:
@@ -567,7 +602,7 @@ def check(names: Sequence[str], profiles_dir: str, calib_on: str = "llama1b_b1",
     res = {"calibration": {"workloads": [calib_on, calib_batched],
                            **{k: round(v, 3) for k, v in c.__dict__.items()}}}
     for n in names:
-        pred = predict(wls[n], c)
+        pred = predict(wls[n], c, host_us={d: v.get("host_us") for d, v in meas.get(n, {}).items()})
         m = {d: v["step_us"] for d, v in meas.get(n, {}).items() if d in pred}
         p = {d: v["step_us"] for d, v in pred.items()}
         entry = {"predicted_us": {d: round(v, 1) for d, v in p.items()},

@@ -73,6 +73,9 @@ class Plan:
     loop: decode only; 1 builds a queue for persistent multi-step decode: each
     step ends with LM-head tiles (64 vocabulary rows each) and one argmax per
     row, and the next step's embedding tiles wait on the previous step's argmax.
+    attn_pop: decode only, single-step queues; 1 hands a layer's attention
+    splits out at run time in the megakernel (workers take them from a
+    per-layer counter), so that ragged contexts load the workers evenly.
     """
     tq: int = 16
     to: int = 16
@@ -85,6 +88,7 @@ class Plan:
     fuse_combine: int = 0
     prefill_queues: int = 0
     loop: int = 0
+    attn_pop: int = 0
 
     def for_prefill(self) -> "Plan":
         """The plan of the prefill queue (its own sub-queue count)."""
@@ -187,7 +191,7 @@ WORKLOADS = {
     "llama1b_stream_b32": Workload(
         "llama1b_stream_b32", LLAMA_1B,
         RunConfig(batch=32, ctx0=_stream_ctx0(5, 32, 256, 8192), steps=256, ctx_max=8448, seed=5),
-        Plan(tf=32, td=8, kb=2048, n_queues=256),
+        Plan(tf=32, td=8, kb=2048, n_queues=256, attn_pop=1),
         "Llama-3-1B-shaped bf16 streaming decode, batch 32, contexts U{256..8192}, 256 steps"),
 }
 
