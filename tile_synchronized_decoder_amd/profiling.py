@@ -36,7 +36,7 @@ def kernel_sources_sha() -> str:
     return h.hexdigest()
 
 
-def stats_markdown(path: str, command: str, top: int = 16) -> str:
+def stats_markdown(path: str, command: str, top: int = 24) -> str:
     rows = list(csv.DictReader(open(path)))
     out = ["# Kernel time summary", "", "Command:", "", "```", command, "```", "",
            "| kernel | calls | avg (us) | min (us) | max (us) | total % |", "|---|---|---|---|---|---|"]
