@@ -56,8 +56,9 @@ def _run_loop(c, tokens, feedback, steps=STEPS):
     return lg.cpu().numpy(), nx.cpu().numpy(), c.tensor(T.MK_T_X, c.m.n_layers, c.m.hidden)
 
 
-@pytest.mark.parametrize("batch,ctx0,nq", [(1, (1024,), 256), (3, (900, 31, 511), 8)],
-                         ids=["b1_static", "b3_shared8"])
+@pytest.mark.parametrize("batch,ctx0,nq", [(1, (1024,), 256), (3, (900, 31, 511), 8),
+                                           (20, tuple(900 - 41 * b for b in range(20)), 256)],
+                         ids=["b1_static", "b3_shared8", "b20_static"])
 def test_loop_teacher_forced_matches_oracle(batch, ctx0, nq):
     from _gpucase import log
     c = _case(batch, ctx0, nq)
