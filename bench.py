@@ -262,10 +262,16 @@ def run_workload(wl, args, modes, with_prefill=True):
             log(f"[bench] {wl.name} loop: {total_ms / K_steps:.4f} ms/step ({K_steps} steps in one launch)")
             del wsl, lg_all
             continue
+        T.mk_set_option(T.MK_OPT_MEGAKERNELS, 1)
         if name.startswith("ms"):
             # multi-stream mode: one kernel per segment on `streams` internal streams, tile waits
             T.mk_set_option(T.MK_OPT_STREAMS, int(name[2:]))
             mode = T.MK_MULTI_STREAM
+        elif name.startswith("mega") and name != "mega":
+            # a composition of megakernels: `megaK` cuts each step into K launches at layer
+            # boundaries
+            T.mk_set_option(T.MK_OPT_MEGAKERNELS, int(name[4:]))
+            mode = T.MK_MEGAKERNEL
         else:
             mode = mode_of[name]
         for t in range(args.warmup):
@@ -302,6 +308,7 @@ def run_workload(wl, args, modes, with_prefill=True):
         results[name] = res
         err = T.mk_device_error(q, ws)
         assert err.code == 0, f"device error {err.code} in mode {name}"
+        T.mk_set_option(T.MK_OPT_MEGAKERNELS, 1)
         log(f"[bench] {wl.name} {name}: {res['ms_per_step']:.4f} ms/step, {res['tokens_per_s']:.1f} tok/s")
 
     mega = results.get("mega", next(iter(results.values())))
@@ -355,8 +362,9 @@ def main():
                     help="decode GEMV weight issue: 0 or 1 pipelined (default), 2 compiler-ordered")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
-    ap.add_argument("--modes", default="mega,kpo,kpo_graph,loop,ms2,ms4",
-                    help="mega, kpo, kpo_graph, loop, and msS: the multi-stream mode on S streams")
+    ap.add_argument("--modes", default="mega,kpo,kpo_graph,loop,ms2,ms4,mega2,mega4",
+                    help="mega, kpo, kpo_graph, loop, msS: the multi-stream mode on S streams, and "
+                         "megaK: a composition of K megakernels per step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the modes, copy MIB MiB device to device three times: a plain copy "
                          "kernel of known size that hardware byte counters can be scaled by")

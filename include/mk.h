@@ -382,7 +382,16 @@ enum {
    * Results are identical to a run without it; 0 (default) turns it off. */
   MK_OPT_DELAY_SEED = 6,
   /* Internal streams of MK_MULTI_STREAM, 1..8 (default 2). */
-  MK_OPT_STREAMS = 7
+  MK_OPT_STREAMS = 7,
+  /* MK_MEGAKERNEL: megakernel launches per decode step, 1..8 (default 1).  With
+   * K > 1 the step is a composition of K megakernels ("One Megakernel is Not
+   * Enough" abstract: cutting the model into several megakernels), cut at layer
+   * boundaries: launch k runs the instructions of layers [k L / K, (k + 1) L / K),
+   * the first also the embedding, in stream order, so tiles of earlier
+   * launches are complete before a later one starts; results are identical bit
+   * for bit.  Needs a single-step queue with one sub-queue per worker and at
+   * most L launches (else MK_ENOTSUP). */
+  MK_OPT_MEGAKERNELS = 8
 };
 /* Errors: MK_EINVAL for an unknown or read-only key or a value out of range. */
 mk_status mk_set_option(int32_t key, int64_t value);

@@ -261,3 +261,41 @@ def test_popped_segment_goes_to_the_first_free_worker():
     popped, start, _ = P.simulate(g, {3: 1.0}, dur_i=dur_i, pop_segments=[(0, 4)])
     assert static == pytest.approx(6.0) and popped == pytest.approx(5.0)
     assert start.tolist() == pytest.approx([0, 0, 1, 2])
+
+
+def test_cut_holds_every_worker_until_the_previous_launch_ends():
+    # four independent instructions of 3, 1, 1, 1 us on two workers: one launch
+    # takes 4 us (worker 0: 3 + 1); cut before position 2, the second launch
+    # starts when the first has ended (3 us) plus 0.5 us of launch cost
+    g = _graph([2, 2, 2, 2], [[], [], [], []], [0, 1, 2, 3], 4, 2)
+    dur_i = np.array([3.0, 1.0, 1.0, 1.0])
+    one, _, _ = P.simulate(g, {2: 1.0}, dur_i=dur_i)
+    two, start, _ = P.simulate(g, {2: 1.0}, dur_i=dur_i, cuts=[2], cut_us=0.5)
+    assert one == pytest.approx(4.0) and two == pytest.approx(4.5)
+    assert start.tolist() == pytest.approx([0, 0, 3.5, 3.5])
+
+
+def test_layer_cuts_start_launches_at_layer_boundaries():
+    wl = W.configs.shrink(W.WORKLOADS["llama1b_b1"], n_layers=4, vocab=256)
+    m, r = wl.model, wl.run
+    q = T.mk_build_queue(T.make_config(m), T.make_plan(wl.plan, T.MK_DECODE, r.batch, r.ctx_max))
+    g = P.graph_from_parts(q.parts())
+    for k, layers in ((2, [2]), (3, [1, 2]), (4, [1, 2, 3])):
+        cuts = P.layer_cuts(g, k)
+        assert [int(g.layer[c]) for c in cuts] == layers
+        for c, l in zip(cuts, layers):
+            assert int(g.op[c]) == P.OP_QKV
+            before = g.op[:c] != P.OP_EMBED
+            assert (g.layer[:c][before] < l).all() and (g.layer[c:] >= l).all()
+    # with free launches a composition is no faster than one launch; without
+    # hand-off time each launch's cost adds once per cut (the rest is a shift),
+    # and a hand-off shorter than the launch cost hides in it
+    rng = np.random.default_rng(3)
+    dur = {op: float(rng.uniform(1, 10)) for op in range(1, 8)}
+    cuts = P.layer_cuts(g, 4)
+    for hop in (0.0, 0.3):
+        one, _, _ = P.simulate(g, dur, hop=hop)
+        free4, _, _ = P.simulate(g, dur, hop=hop, cuts=cuts, cut_us=0.0)
+        cost4, _, _ = P.simulate(g, dur, hop=hop, cuts=cuts, cut_us=2.0)
+        assert one <= free4 + 1e-9
+        assert cost4 == pytest.approx(free4 + 3 * (2.0 - hop))

@@ -77,6 +77,7 @@ struct Options {
   int gemv_pipe = 0;                     // 0, 1: pipelined issue; 2: compiler-ordered issue
   uint32_t delay_seed = 0;               // race check: seeded stalls before tile stores
   int streams = 2;                       // multi-stream mode: internal streams per device
+  int megakernels = 1;                   // megakernel mode: launches per step, cut at layer boundaries
 };
 Options g_opt;
 
@@ -302,6 +303,7 @@ void fill_args(const mk_queue* q, const void* d_queue, const mk_weights* w, cons
       a.attn_first = at[0]->first; a.attn_stride = stride; a.attn_count = at[0]->count;
     }
   }
+  a.range_begin = 0; a.range_end = (uint32_t)q->instr.size();
   const LdsLayout ll = lds_layout(q);
   a.lds_res = ll.res; a.lds_x = ll.x; a.lds_union = ll.uni; a.lds_bytes = ll.bytes; a.lds_ring = ll.ring;
   a.M_cache = kv && kv->rows > 0 ? kv->rows : q->plan.rows;
@@ -360,6 +362,14 @@ mk_status prep_status(hipError_t e) {
 // segment enqueued earlier, which is active or done: no workgroup waits on one
 // that cannot be scheduled.
 constexpr int kMaxStreams = 8;
+constexpr int kMaxMegakernels = 8;
+
+// First instruction of layer l's ops (past the embedding tiles) in a decode queue.
+uint32_t layer_first(const mk_queue* q, int l) {
+  for (const mk::Segment& sg : q->segments)
+    if ((int)sg.layer == l && sg.op != mk::OP_EMBED) return sg.first;
+  return (uint32_t)q->instr.size();
+}
 constexpr int kXcds = 8;
 struct StreamSet {
   hipStream_t st[kMaxStreams] = {};
@@ -429,7 +439,17 @@ hipError_t enqueue_decode(const mk_queue* q, const Args& a, const Table& t, int 
                      a.err);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (mega) {
+  if (mega && g_opt.megakernels > 1) {
+    // a composition of megakernels: launch k runs the layers [k L / K, (k + 1) L / K)
+    // (the embedding with the first); kernel order covers the waits across launches
+    const int K = g_opt.megakernels, L = q->cfg.n_layers;
+    for (int k = 0; k < K && e == hipSuccess; ++k) {
+      Args ak = a;
+      ak.range_begin = k == 0 ? 0u : layer_first(q, k * L / K);
+      ak.range_end = k == K - 1 ? (uint32_t)q->instr.size() : layer_first(q, (k + 1) * L / K);
+      e = t.mega(ak, num_cus() * g_opt.workers_per_cu, stream);
+    }
+  } else if (mega) {
     e = t.mega(a, num_cus() * g_opt.workers_per_cu, stream);
   } else if (ss) {
     e = enqueue_multi_stream(q, a, t, *ss, n_streams, stream);
@@ -555,6 +575,11 @@ mk_status decode_impl(const mk_queue* q, const void* d_queue, const mk_weights* 
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) FAIL(MK_ELAUNCH, "no current device");
   if (exec_mode == MK_MEGAKERNEL && num_cus() * g_opt.workers_per_cu < q->plan.n_queues)
     FAIL(MK_EINVAL, "fewer workers than sub-queues");
+  if (exec_mode == MK_MEGAKERNEL && g_opt.megakernels > 1) {
+    if (num_cus() * g_opt.workers_per_cu != q->plan.n_queues)
+      FAIL(MK_ENOTSUP, "a composition of megakernels needs one sub-queue per worker");
+    if (g_opt.megakernels > c.n_layers) FAIL(MK_ENOTSUP, "more megakernels than layers");
+  }
 
   Args a{};
   fill_args(q, d_queue, w, kv, d_workspace, o, a);
@@ -889,6 +914,9 @@ mk_status mk_set_option(int32_t key, int64_t value) {
     case MK_OPT_STREAMS:
       if (value < 1 || value > kMaxStreams) FAIL(MK_EINVAL, "streams must be 1..%d", kMaxStreams);
       g_opt.streams = (int)value; return MK_OK;
+    case MK_OPT_MEGAKERNELS:
+      if (value < 1 || value > kMaxMegakernels) FAIL(MK_EINVAL, "megakernels must be 1..%d", kMaxMegakernels);
+      g_opt.megakernels = (int)value; return MK_OK;
     default: FAIL(MK_EINVAL, "unknown or read-only option %d", key);
   }
 }
@@ -904,6 +932,7 @@ int64_t mk_get_option(int32_t key) {
     case MK_OPT_GEMV_PIPE: return g_opt.gemv_pipe;
     case MK_OPT_DELAY_SEED: return g_opt.delay_seed;
     case MK_OPT_STREAMS: return g_opt.streams;
+    case MK_OPT_MEGAKERNELS: return g_opt.megakernels;
     default: return -1;
   }
 }

@@ -111,6 +111,10 @@ struct Args {
   // from the layer's counter heads[(n_queues + l) * 32]
   int attn_pop;
   uint32_t attn_first, attn_stride, attn_count;
+  // megakernel (one sub-queue per worker, not loop queues): the launch runs the
+  // queue positions [range_begin, range_end) (all of them, unless the step is
+  // a composition of several megakernels cut at layer boundaries)
+  uint32_t range_begin, range_end;
   uint32_t delay_seed;           // race check: seeded stall before each tile's stores (0: off)
   // persistent multi-step decode (loop queues): steps of the run, 1 = embed the
   // previous step's argmax (else tokens[step][row]), the argmax of every step
@@ -1662,7 +1666,7 @@ __global__ __launch_bounds__(NT) void mk_interp(Args args) {
   Smem s = make_smem(kernel_args());
   const uint32_t nq = args.n_queues;
   const uint32_t qi = blockIdx.x % nq;
-  const uint64_t total = LOOP ? (uint64_t)args.n_instr * (uint64_t)args.steps : args.n_instr;
+  const uint64_t total = LOOP ? (uint64_t)args.n_instr * (uint64_t)args.steps : args.range_end;
   // One sub-queue per worker: the worker runs positions qi, qi + nq, ... and
   // needs no pops; each instruction's record is loaded one iteration ahead.
   const bool fixed = nq == gridDim.x;
@@ -1677,11 +1681,14 @@ __global__ __launch_bounds__(NT) void mk_interp(Args args) {
     KArgs& a = kernel_args();
     k_next = __hip_atomic_fetch_add(a.heads + qi * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (fixed && threadIdx.x < 8 && qi < total) {
+  // a launch of a composition starts at its range's first position of this worker
+  const uint32_t it0 = (!LOOP && fixed && args.range_begin > qi) ? (args.range_begin - qi + nq - 1) / nq : 0;
+  if (fixed && threadIdx.x < 8 && (uint64_t)qi + (uint64_t)it0 * nq < total) {
     KArgs& a = kernel_args();
-    word = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.instr + instr_of(qi)) + threadIdx.x);
+    word = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.instr + instr_of(qi + it0 * nq)) +
+                                      threadIdx.x);
   }
-  for (uint32_t it = 0;; ++it) {
+  for (uint32_t it = it0;; ++it) {
     KArgs& a = kernel_args();
     const uint64_t fi = (uint64_t)qi + (uint64_t)it * nq;         // fixed order: this iteration's position
     if (threadIdx.x == 0) {

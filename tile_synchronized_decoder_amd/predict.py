@@ -11,14 +11,17 @@ measurement.  This module does that for the designs this library runs:
                  several steps per launch): the LM-head placement question;
 * ``kpo``        one kernel per (layer, op) segment in stream order, eager;
 * ``kpo_graph``  the same launches replayed from a HIP graph;
-* ``msS``        one kernel per segment on S streams, synchronised on tiles.
+* ``msS``        one kernel per segment on S streams, synchronised on tiles;
+* ``megaK``      a composition of K megakernels per step, cut at layer
+                 boundaries (launch k runs layers [k L / K, (k + 1) L / K)).
 
 Inputs, all measured on their own: the per-op kernels of the kernel-per-op
 mode (one launch per op: rocprofv3 kernel statistics), the separate LM-head,
 argmax and counter-reset kernels, and the host's time to enqueue a step.
-Three constants come from one calibration workload and are then held fixed:
-the device gap between dependent kernel launches, the same inside a graph,
-and the megakernel's launch ramp.
+Constants come from one calibration workload and are then held fixed: the
+device gap between dependent kernel launches, the same inside a graph, the
+tile hand-off time, and the start of a persistent launch; an occupancy factor
+for batched GEMVs comes from one batched workload.
 
 Model.  One instruction of op o takes dur[o] = (K_o - R) / rounds_o, where
 K_o is the op's per-op kernel time, R the time a launch of 256 near-empty
@@ -40,7 +43,11 @@ pairs.  The tile pass, per instruction i in queue order on its worker:
 
 Every waited barrier is signalled only by earlier instructions (queue order is
 topological; the CPU checker verifies it) and a worker's previous instruction
-is earlier too, so one pass in queue order gives every time.  The
+is earlier too, so one pass in queue order gives every time.  A composition
+of megakernels is the same pass with every worker held, at each cut, until
+the previous launch's last instruction has ended, plus a launch gap, the
+ramp of a new launch of 256 workgroups and the persistent launch's own start
+beyond that ramp (a constant fitted on the calibration workload).  The
 multi-stream pass is the same with each segment's instructions on the
 8 * floor(CUs / 8 / S) workgroups of its own kernel, which starts when the
 previous kernel of its stream (segment k - S) has ended.  A design's step is
@@ -115,7 +122,8 @@ def simulate(g: Graph, dur: Mapping[int, float], hop: float = 0.0,
              prefetch: Optional[Mapping[int, float]] = None,
              n_workers: Optional[int] = None, steps: int = 1,
              dur_i: Optional[np.ndarray] = None,
-             pop_segments: Sequence[Tuple[int, int]] = ()) -> Tuple[float, np.ndarray, np.ndarray]:
+             pop_segments: Sequence[Tuple[int, int]] = (),
+             cuts: Sequence[int] = (), cut_us: float = 0.0) -> Tuple[float, np.ndarray, np.ndarray]:
     """Event pass over the megakernel's schedule.  Returns (span, start, end) in
     the units of `dur`; start and end are those of the last step.  With as
     many workers as sub-queues (the default) position k of the repeated queue
@@ -127,7 +135,10 @@ def simulate(g: Graph, dur: Mapping[int, float], hop: float = 0.0,
     where the op's duration applies) overrides ``dur``.  ``pop_segments``
     (first, count): segments handed out at run time (one sub-queue per worker):
     the workers holding a position in the segment take its instructions in
-    queue order, each going to the one of them that is free first."""
+    queue order, each going to the one of them that is free first.  ``cuts``
+    (single step): positions where a new launch of a composition starts; no
+    worker starts there or later before every earlier instruction has ended
+    and ``cut_us`` more has passed."""
     nq = g.n_queues
     nw = n_workers or nq
     prefetch = prefetch or {}
@@ -139,10 +150,13 @@ def simulate(g: Graph, dur: Mapping[int, float], hop: float = 0.0,
     start = np.zeros(n)
     end = np.zeros(n)
     pop_at = {f: c for f, c in pop_segments if c > 0}
+    cut_at = set(int(c) for c in cuts if 0 < c < n)
     for t in range(steps):
         done = np.zeros(len(g.targets))
         i = 0
         while i < n:
+            if i in cut_at:
+                free[:] = free.max() + cut_us
             if i in pop_at and members is None:
                 cnt = pop_at[i]
                 part = np.unique((t * n + i + np.arange(min(cnt, nw))) % nw)
@@ -187,6 +201,17 @@ def simulate(g: Graph, dur: Mapping[int, float], hop: float = 0.0,
             i += 1
         done_prev = done
     return (float(free.max()) if n else 0.0), start, end
+
+
+def layer_cuts(g: Graph, launches: int) -> List[int]:
+    """Queue positions where launches 1..K-1 of a composition of K megakernels
+    start: the first non-embedding instruction of layer k L / K."""
+    n_layers = int(g.layer.max()) + 1 if len(g.layer) else 0
+    first = {}
+    for op, layer, f, _cnt in g.segments:
+        if op != OP_EMBED:
+            first[layer] = min(first.get(layer, f), f)
+    return [first[k * n_layers // launches] for k in range(1, launches)]
 
 
 def ms_grid(streams: int, n_cus: int, per_cu: int = 1) -> int:
@@ -369,6 +394,7 @@ class Calib:
     gap_us: float = 0.3           # device gap between dependent launches, eager
     graph_gap_us: float = 0.3     # the same inside a replayed graph
     hop_us: float = 1.0           # tile hand-off: producer's signal to consumer running
+    mega_launch_us: float = 0.0   # a megakernel launch's start beyond a near-empty launch's ramp
     occupancy: float = 1.0        # batched GEMV instruction in the interpreter / in its per-op kernel
     host_call_us: float = 30.0    # host: enqueueing a step, fixed part
     host_launch_us: float = 2.0   # host: per kernel launch
@@ -400,6 +426,8 @@ def _launches(w: Workload, design: str) -> float:
     lm = 2 if w.has_lm else 0
     if design == "mega":
         return pre + 2 + lm
+    if design.startswith("mega"):
+        return pre + 1 + int(design[4:]) + lm
     if design in ("kpo", "kpo_graph"):
         return pre + 1 + len(w.single.segments) + lm          # kernels (graph nodes)
     if design == "loop":
@@ -410,7 +438,8 @@ def _launches(w: Workload, design: str) -> float:
     raise ValueError(design)
 
 
-def predict(w: Workload, c: Calib, designs: Sequence[str] = ("mega", "kpo", "kpo_graph", "loop", "ms2", "ms4"),
+def predict(w: Workload, c: Calib, designs: Sequence[str] = ("mega", "kpo", "kpo_graph", "loop", "ms2", "ms4",
+                                                              "mega2", "mega3", "mega4"),
             loop_steps: int = 32, host_us: Optional[Mapping[str, Optional[float]]] = None
             ) -> Dict[str, Dict[str, float]]:
     """Predicted device, host and step times (µs) of each design.  ``host_us``:
@@ -436,12 +465,17 @@ def predict(w: Workload, c: Calib, designs: Sequence[str] = ("mega", "kpo", "kpo
     ai = attn_i(w.single)
     out: Dict[str, Dict[str, float]] = {}
     for d in designs:
-        if d == "mega":
+        if d.startswith("mega"):
             pops = [(f, cnt) for op, _l, f, cnt in w.single.segments if op == OP_ATTN] \
                 if w.attn_pop and w.single.n_queues >= w.n_cus else []
+            k = 1 if d == "mega" else int(d[4:])
+            if k > 1 and (w.single.n_queues != w.n_cus or k > int(w.single.layer.max()) + 1):
+                continue                                # the library refuses it
+            cuts = layer_cuts(w.single, k) if k > 1 else []
             span, _, _ = simulate(w.single, dur_mk, c.hop_us, pf,
                                   n_workers=w.n_cus if w.single.n_queues < w.n_cus else None, dur_i=ai,
-                                  pop_segments=pops)
+                                  pop_segments=pops, cuts=cuts,
+                                  cut_us=c.gap_us + t.ramp_us + c.mega_launch_us)
             # the launch of 256 persistent workgroups costs what a near-empty launch does
             dev = pre + t.reset_us + t.ramp_us + span + lm + 2 * c.gap_us
         elif d in ("kpo", "kpo_graph"):
@@ -512,6 +546,12 @@ def calibrate(w: Workload, measured_us: Mapping[str, float],
         return Calib(**{**c.__dict__, **kw})
     c.hop_us = _fit(lambda h: predict(w, with_(hop_us=h), ("mega",))["mega"]["device_us"], 0.0, 50.0,
                     measured_us["mega"])
+    if "mega2" in measured_us:
+        # what a cut costs beyond the drain, the gap and a near-empty launch: the
+        # persistent launch's own start (the library refuses compositions of
+        # shared sub-queues, so a plan with them has no mega2)
+        c.mega_launch_us = _fit(lambda x: predict(w, with_(mega_launch_us=x), ("mega2",))["mega2"]["device_us"],
+                                0.0, 100.0, measured_us["mega2"])
     if batched is not None:
         wb, mega_b = batched
         c.occupancy = _fit(lambda f: predict(wb, with_(occupancy=f), ("mega",))["mega"]["device_us"], 0.5, 4.0,
@@ -596,7 +636,8 @@ def check(names: Sequence[str], profiles_dir: str, calib_on: str = "llama1b_b1",
            for n in names}
     # host enqueue times of GPU-bound workloads (steps far longer than enqueueing them)
     host = [(wls[n], d, v["host_us"]) for n in names if n in meas and meas[n].get("mega", {}).get("step_us", 0) > 500
-            for d, v in meas[n].items() if v.get("host_us") and d in ("mega", "kpo", "kpo_graph", "ms2", "ms4")]
+            for d, v in meas[n].items() if v.get("host_us") and d in ("mega", "kpo", "kpo_graph", "ms2", "ms4",
+                                                                       "mega2", "mega3", "mega4")]
     bat = (wls[calib_batched], meas[calib_batched]["mega"]["step_us"]) if calib_batched in wls else None
     c = calibrate(wls[calib_on], {d: v["step_us"] for d, v in meas[calib_on].items()}, host, bat)
     res = {"calibration": {"workloads": [calib_on, calib_batched],
