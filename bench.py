@@ -156,7 +156,8 @@ def run_workload(wl, args, modes, with_prefill=True):
         ptok = torch.from_numpy(W.gen.prefill_tokens(m, r)).cuda()
         plg = torch.empty((m.vocab,), dtype=torch.float32, device="cuda")
         pnx = torch.empty((1,), dtype=torch.int32, device="cuda")
-        prefill_res = {"tokens": S, "flops": prefill_flops(m, S), "modes": {}}
+        prefill_res = {"tokens": S, "flops": prefill_flops(m, S), "modes": {},
+                       "lo_parts_mask": int(T.mk_get_option(T.MK_OPT_PREFILL_LO))}
         for name in ("mega", "kpo"):
             mode = T.MK_MEGAKERNEL if name == "mega" else T.MK_KERNEL_PER_OP
             for _ in range(2):
@@ -360,6 +361,9 @@ def main():
     ap.add_argument("--tiles", default="", help="override tile widths, e.g. tq=16,to=8,tf=16,td=8,kb=256")
     ap.add_argument("--gemv-pipe", type=int, default=0,
                     help="decode GEMV weight issue: 0 or 1 pipelined (default), 2 compiler-ordered")
+    ap.add_argument("--prefill-lo", type=int, default=None,
+                    help="prefill GEMMs taking both bf16 parts of their activations, a mask (1 QKV, 2 O, "
+                         "4 gate/up, 8 down; default: the library's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--modes", default="mega,kpo,kpo_graph,loop,ms2,ms4,mega2,mega4",
@@ -389,6 +393,8 @@ def main():
     torch.cuda.set_device(0)
     T.mk_set_option(T.MK_OPT_WORKERS_PER_CU, args.workers_per_cu)
     T.mk_set_option(T.MK_OPT_GEMV_PIPE, args.gemv_pipe)
+    if args.prefill_lo is not None:
+        T.mk_set_option(T.MK_OPT_PREFILL_LO, args.prefill_lo)
     modes = args.modes.split(",")
 
     head = run_workload(wl, args, modes)

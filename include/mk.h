@@ -391,7 +391,12 @@ enum {
    * launches are complete before a later one starts; results are identical bit
    * for bit.  Needs a single-step queue with one sub-queue per worker and at
    * most L launches (else MK_ENOTSUP). */
-  MK_OPT_MEGAKERNELS = 8
+  MK_OPT_MEGAKERNELS = 8,
+  /* mk_prefill: which GEMMs take both bf16 parts (hi, lo) of their fp32
+   * activations, a bit mask (1 QKV, 2 O-projection, 4 gate/up, 8 down; default
+   * 15, all).  A GEMM whose bit is clear takes the hi parts only: its
+   * activations are rounded to bf16 and it runs half the matrix-core products. */
+  MK_OPT_PREFILL_LO = 9
 };
 /* Errors: MK_EINVAL for an unknown or read-only key or a value out of range. */
 mk_status mk_set_option(int32_t key, int64_t value);

@@ -154,7 +154,8 @@ def test_options_validate_and_round_trip():
                            (T.MK_OPT_SPIN_LIMIT, (1, 1 << 20), (0,)),
                            (T.MK_OPT_DELAY_SEED, (0, 7, 0xFFFFFFFF), (-1, 1 << 32)),
                            (T.MK_OPT_STREAMS, (1, 8, 2), (0, 9)),
-                           (T.MK_OPT_MEGAKERNELS, (2, 8, 1), (0, 9))):
+                           (T.MK_OPT_MEGAKERNELS, (2, 8, 1), (0, 9)),
+                           (T.MK_OPT_PREFILL_LO, (0, 7, 15), (-1, 16))):
         old = T.mk_get_option(key)
         try:
             for v in good:

@@ -237,3 +237,30 @@ def test_prefill_rejects_hidden_not_multiple_of_128(small):
         T.mk_prefill(q, small.dq, small.dm.w, small.dkv.kv, tok, 16, 0, small.ws, small.logits, small.nxt,
                      T.MK_MEGAKERNEL)
     assert ei.value.status == T.MK_ENOTSUP
+
+
+@pytest.mark.parametrize("lo_mask", [0, 7, 11])
+def test_prefill_hi_parts_only_meets_oracle(small, lo_mask):
+    """GEMMs whose bit is clear in MK_OPT_PREFILL_LO take the hi parts of their
+    activations only (rounded to bf16): the result changes against taking both
+    parts, still meets the oracle on the short model in both modes, and the two
+    modes agree bit for bit."""
+    seq_len, kv_row = 200, 1
+    tr, K, V = oracle_prefill(small, seq_len, kv_row)
+    small.reset()
+    small.prefill(seq_len, kv_row, T.MK_MEGAKERNEL)
+    both = small.snapshot(seq_len)
+    snaps = {}
+    T.mk_set_option(T.MK_OPT_PREFILL_LO, lo_mask)
+    try:
+        for mode, name in ((T.MK_MEGAKERNEL, "mega"), (T.MK_KERNEL_PER_OP, "kpo")):
+            small.reset()
+            small.prefill(seq_len, kv_row, mode)
+            snaps[name] = small.snapshot(seq_len)
+            compare(small, snaps[name], tr, K, V, seq_len, kv_row)
+    finally:
+        T.mk_set_option(T.MK_OPT_PREFILL_LO, 15)
+    for key in snaps["mega"]:
+        assert np.array_equal(snaps["mega"][key], snaps["kpo"][key]), f"modes differ in {key}"
+    last = f"x{small.m.n_layers}"
+    assert not np.array_equal(snaps["mega"][last], both[last]), "the option changed nothing"

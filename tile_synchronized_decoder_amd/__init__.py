@@ -18,7 +18,7 @@ from ._lib import (MK_OK, MK_EINVAL, MK_ENOMEM, MK_ELAUNCH, MK_EDEVICE, MK_ENOTS
                    MK_T_ACT, MK_T_ATT, MK_T_COUNTERS, MK_T_ERROR, MK_T_HEADS, MK_T_HRES,
                    MK_T_OPART, MK_T_QKV, MK_T_X, MK_OPT_NUM_CUS, MK_OPT_SPIN_LIMIT, MK_OPT_TRACE_BUFFER,
                    MK_OPT_TRACE_BYTES, MK_OPT_GEMV_PIPE, MK_OPT_DELAY_SEED, MK_OPT_STREAMS,
-                   MK_OPT_MEGAKERNELS,
+                   MK_OPT_MEGAKERNELS, MK_OPT_PREFILL_LO,
                    MK_OPT_WORKERS_PER_CU, MkError, mk_config, mk_dev_error, mk_kv, mk_plan,
                    mk_weights)
 

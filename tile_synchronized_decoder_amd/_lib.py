@@ -20,7 +20,8 @@ MK_STATIC_SCRATCH_BYTES = 64 << 20
 (MK_T_X, MK_T_QKV, MK_T_OPART, MK_T_ATT, MK_T_HRES, MK_T_ACT, MK_T_COUNTERS, MK_T_HEADS,
  MK_T_ERROR, MK_T_LMPART) = range(10)
 (MK_OPT_WORKERS_PER_CU, MK_OPT_SPIN_LIMIT, MK_OPT_NUM_CUS, MK_OPT_TRACE_BUFFER, MK_OPT_TRACE_BYTES,
- MK_OPT_GEMV_PIPE, MK_OPT_DELAY_SEED, MK_OPT_STREAMS, MK_OPT_MEGAKERNELS) = range(9)
+ MK_OPT_GEMV_PIPE, MK_OPT_DELAY_SEED, MK_OPT_STREAMS, MK_OPT_MEGAKERNELS,
+ MK_OPT_PREFILL_LO) = range(10)
 
 
 class mk_config(C.Structure):

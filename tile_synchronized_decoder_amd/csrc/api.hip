@@ -78,6 +78,7 @@ struct Options {
   uint32_t delay_seed = 0;               // race check: seeded stalls before tile stores
   int streams = 2;                       // multi-stream mode: internal streams per device
   int megakernels = 1;                   // megakernel mode: launches per step, cut at layer boundaries
+  uint32_t prefill_lo = 15;              // prefill GEMMs taking the lo parts of their activations
 };
 Options g_opt;
 
@@ -837,6 +838,7 @@ mk_status mk_prefill(const mk_queue* q, const void* d_queue, const mk_weights* w
   Args a{};
   fill_args(q, d_queue, w, kv, d_workspace, o, a);
   a.tokens = d_tokens; a.seq_len = seq_len; a.kv_row = kv_row; a.M_cache = kv->rows;
+  a.prefill_lo = g_opt.prefill_lo;
   a.spin_limit = g_opt.spin_limit;
   a.gemv_pipe = g_opt.gemv_pipe;
   a.delay_seed = g_opt.delay_seed;
@@ -917,6 +919,9 @@ mk_status mk_set_option(int32_t key, int64_t value) {
     case MK_OPT_MEGAKERNELS:
       if (value < 1 || value > kMaxMegakernels) FAIL(MK_EINVAL, "megakernels must be 1..%d", kMaxMegakernels);
       g_opt.megakernels = (int)value; return MK_OK;
+    case MK_OPT_PREFILL_LO:
+      if (value < 0 || value > 15) FAIL(MK_EINVAL, "prefill lo-part mask must be 0..15");
+      g_opt.prefill_lo = (uint32_t)value; return MK_OK;
     default: FAIL(MK_EINVAL, "unknown or read-only option %d", key);
   }
 }
@@ -933,6 +938,7 @@ int64_t mk_get_option(int32_t key) {
     case MK_OPT_DELAY_SEED: return g_opt.delay_seed;
     case MK_OPT_STREAMS: return g_opt.streams;
     case MK_OPT_MEGAKERNELS: return g_opt.megakernels;
+    case MK_OPT_PREFILL_LO: return g_opt.prefill_lo;
     default: return -1;
   }
 }

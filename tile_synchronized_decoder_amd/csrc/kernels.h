@@ -104,6 +104,7 @@ struct Args {
   uint16_t* lm_y;                // [2][M][H]: the LM head's normalised rows as bf16 hi, lo (matrix-core head)
   float* lm_rs;                  // [M]: their RMSNorm scales
   int gemv_pipe;                 // decode GEMV weight issue: 0, 1 pipelined; 2 compiler-ordered
+  uint32_t prefill_lo;           // prefill GEMMs taking their activations' lo parts (P_LO_* bits)
   int fuse_combine;              // decode queue without split combines: O-projection merges the partials
   int merge_last;                // decode queue without split combines: the last split to arrive merges
   // megakernel, one sub-queue per worker: a layer's attention splits (the

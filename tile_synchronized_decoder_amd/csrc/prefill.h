@@ -12,7 +12,10 @@
 // them is exact once the other operand is.  Every activation operand y (fp32)
 // therefore enters the matrix cores as a pair hi = bf16(y), lo = bf16(y - hi):
 // y - (hi + lo) is below 2^-16 |y|, and each product is taken twice, hi W and
-// lo W, into one fp32 accumulator.  Producer tiles write both parts.
+// lo W, into one fp32 accumulator.  Producer tiles write both parts.  A
+// consumer op whose bit is clear in prefill_lo takes the hi parts only (its
+// activations rounded to bf16, half the matrix-core work and activation
+// traffic).
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, wave64): operand A supplies
 // rows i = lane % 32 with k = 8 * (lane / 32) .. + 8, operand B columns
@@ -30,6 +33,9 @@ constexpr int PBM = 128;        // rows of a prefill tile
 constexpr int PBN = 128;        // output columns of a prefill GEMM tile (one head for QKV)
 constexpr int PKS = 64;         // K step (one 128-byte bf16 row chunk set)
 constexpr int PKB = 64;         // keys per attention block
+
+// prefill_lo bits: the GEMMs that take the lo parts of their activations
+constexpr uint32_t P_LO_QKV = 1, P_LO_OPROJ = 2, P_LO_GATEUP = 4, P_LO_DOWN = 8;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
@@ -137,19 +143,22 @@ __device__ __forceinline__ void p_issue_b(const PGemm& g, uint8_t* b, int ks, in
 // launch by their producer tiles, with device-coherent stores, and are read
 // only after those tiles' barriers (see ld_act).
 constexpr int PA_LO = PBM * 128;                 // byte offset of the lo parts in an activation stage
+// NP = 1 issues the hi parts only.
+template <int NP>
 __device__ __forceinline__ void p_issue_a(const PGemm& g, uint8_t* abuf, int ks, int wave, int lane) {
   for (int d = wave; d < PBM / 8; d += NWAVE) {
     const int row = d * 8 + lane / 8;
     const int c = (lane % 8) ^ (row & 7);
     const size_t o = (size_t)(g.r0 + (row < g.rows ? row : 0)) * g.K + ks * PKS + c * 8;
     dma_lds16<0>(g.xb + o, abuf + d * 1024);
-    dma_lds16<0>(g.xl + o, abuf + PA_LO + d * 1024);
+    if constexpr (NP == 2) dma_lds16<0>(g.xl + o, abuf + PA_LO + d * 1024);
   }
 }
 
 // One K step of the tile on the matrix cores: the hi parts of the activation
-// fragments against the weights, then the lo parts against the same weights.
-template <bool TWO>
+// fragments against the weights, then (NP = 2) the lo parts against the same
+// weights.
+template <bool TWO, int NP>
 __device__ __forceinline__ void p_mfma_step(const uint8_t* a, const uint8_t* b, PAcc& acc, PAcc& acc_up,
                                             int wm, int wn, int lane) {
 #pragma unroll
@@ -163,7 +172,7 @@ __device__ __forceinline__ void p_mfma_step(const uint8_t* a, const uint8_t* b, 
       for (int ni = 0; ni < 2; ++ni) bup[ni] = ld_frag(b, PBN + wn * 64 + ni * 32 + (lane & 31), chunk);
     }
 #pragma unroll
-    for (int part = 0; part < 2; ++part) {
+    for (int part = 0; part < NP; ++part) {
       bf16x8 af[2];
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) af[mi] = ld_frag(a + part * PA_LO, wm * 64 + mi * 32 + (lane & 31), chunk);
@@ -202,8 +211,10 @@ __device__ __forceinline__ float* p_row_stats(Smem& s, bool two_mats) {
 // activations after it.  Leaves the row scales (RMSNorm factors, or 1) in
 // p_row_stats()[NT ..].
 // TWO: gate/up (two weight matrices, acc_up accumulates the second); the
-// others pass their one accumulator twice and never touch acc_up.
-template <bool TWO>
+// others pass their one accumulator twice and never touch acc_up.  NP: the
+// activation parts taken (2: hi and lo, 1: hi only, the activations rounded
+// to bf16).
+template <bool TWO, int NP>
 __device__ __forceinline__ bool p_gemm(KArgs& a, Smem& s, const PGemm& g, PAcc& acc, PAcc& acc_up, bool mega,
                                        const Task in, uint32_t idx) {
   constexpr int S = TWO ? 2 : 3;                         // stages (matches p_stages)
@@ -245,7 +256,7 @@ __device__ __forceinline__ bool p_gemm(KArgs& a, Smem& s, const PGemm& g, PAcc& 
     const float sum = half ? other + tot : tot + other;
     if (half == 0) rs[NT + row] = g.ss ? 1.0f / sqrtf(sum / (float)g.K + a.eps) : 1.0f;
   }
-  for (int k = 0; k < D && k < nks; ++k) p_issue_a(g, abase + k * PA_STAGE, k, wave, lane);
+  for (int k = 0; k < D && k < nks; ++k) p_issue_a<NP>(g, abase + k * PA_STAGE, k, wave, lane);
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -253,7 +264,7 @@ __device__ __forceinline__ bool p_gemm(KArgs& a, Smem& s, const PGemm& g, PAcc& 
       acc.c[mi][ni] = (f32x16){};
       if constexpr (TWO) acc_up.c[mi][ni] = (f32x16){};
     }
-  constexpr int NA_ = 2 * PBM / 8 / NWAVE;               // activation DMAs (hi + lo) per wave per step
+  constexpr int NA_ = NP * PBM / 8 / NWAVE;              // activation DMAs (hi, lo) per wave per step
   // Issue order so far: the weights of steps 0 .. D-1 (before the wait), then
   // their activations.  Step 0 has landed once only the activations of steps
   // 1 .. D-1 may be outstanding; from then on each loop step issues (weights,
@@ -267,9 +278,9 @@ __device__ __forceinline__ bool p_gemm(KArgs& a, Smem& s, const PGemm& g, PAcc& 
     const int cd = cur + D >= S ? cur + D - S : cur + D;
     if (ahead) {
       p_issue_b(g, bbase + cd * bbytes, ks + D, wave, lane);
-      p_issue_a(g, abase + cd * PA_STAGE, ks + D, wave, lane);
+      p_issue_a<NP>(g, abase + cd * PA_STAGE, ks + D, wave, lane);
     }
-    p_mfma_step<TWO>(abase + cur * PA_STAGE, bbase + cur * bbytes, acc, acc_up, wm, wn, lane);
+    p_mfma_step<TWO, NP>(abase + cur * PA_STAGE, bbase + cur * bbytes, acc, acc_up, wm, wn, lane);
     if (more) {
       // step ks + 1's loads have landed once only step ks + D's (if D > 1) may be outstanding
       if (D == 1 || !ahead) wait_vm<0>();
@@ -460,7 +471,8 @@ __device__ __forceinline__ void op_p_qkv(KArgs& a, Smem& s, const Task in, uint3
   PGemm g{a.XB + l * a.sXB, a.XBL + l * a.sXB, a.XSS + l * a.sXSS, (a.H + PBN - 1) / PBN,
           static_cast<const uint16_t*>(a.wqkv) + (size_t)l * a.NQKV * a.H, nullptr, n0, a.NQKV, a.H, r0, rows};
   PAcc acc;
-  if (!p_gemm<false>(a, s, g, acc, acc, mega, in, idx)) return;
+  if (!((a.prefill_lo & P_LO_QKV) ? p_gemm<false, 2>(a, s, g, acc, acc, mega, in, idx)
+                                  : p_gemm<false, 1>(a, s, g, acc, acc, mega, in, idx))) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
   const float* rs = p_row_stats(s, false) + NT;
   // stage the scaled tile (fp32 [128][128]) over the operand buffers
@@ -551,7 +563,9 @@ __device__ __forceinline__ void op_p_resid(KArgs& a, Smem& s, const Task in, uin
           nullptr, 0,
           static_cast<const uint16_t*>(down ? a.wdown : a.wo) + (size_t)l * a.H * K, nullptr, n0, a.H, K, r0, rows};
   PAcc acc;
-  if (!p_gemm<false>(a, s, g, acc, acc, mega, in, idx)) return;
+  if (!((a.prefill_lo & (down ? P_LO_DOWN : P_LO_OPROJ)) ? p_gemm<false, 2>(a, s, g, acc, acc, mega, in, idx)
+                                                         : p_gemm<false, 1>(a, s, g, acc, acc, mega, in, idx)))
+    return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
   float* ct = reinterpret_cast<float*>(s.ring);          // [128][128] fp32 over the operand stages
 #pragma unroll
@@ -588,7 +602,8 @@ __device__ __forceinline__ void op_p_gateup(KArgs& a, Smem& s, const Task in, ui
           static_cast<const uint16_t*>(a.wgate) + (size_t)l * a.F * a.H,
           static_cast<const uint16_t*>(a.wup) + (size_t)l * a.F * a.H, n0, a.F, a.H, r0, rows};
   PAcc acc, up;
-  if (!p_gemm<true>(a, s, g, acc, up, mega, in, idx)) return;
+  if (!((a.prefill_lo & P_LO_GATEUP) ? p_gemm<true, 2>(a, s, g, acc, up, mega, in, idx)
+                                     : p_gemm<true, 1>(a, s, g, acc, up, mega, in, idx))) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
   const float* rs = p_row_stats(s, true) + NT;
   float* ct = reinterpret_cast<float*>(s.ring);          // [128][128] fp32 over the operand stages
