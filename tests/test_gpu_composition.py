@@ -42,6 +42,7 @@ def _cases():
                   name="llama1b_L4_B1")
     b4 = W.shrink(W.WORKLOADS["llama1b_stream_b32"], n_layers=4, vocab=4096, batch=4,
                   ctx0=(3000, 37, 600, 1), steps=1, name="llama1b_L4_B4")
+    b4 = dataclasses.replace(b4, plan=dataclasses.replace(b4.plan, kb=512))     # several splits per row
     e8 = W.shrink(W.WORKLOADS["llama8b_b1"], n_layers=3, vocab=4096, steps=1, name="llama8b_L3_B1")
     return {
         "bf16_1b_b1_combine": dataclasses.replace(b1, plan=W.Plan(tf=32, td=8, n_queues=ncu)),
