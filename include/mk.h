@@ -390,7 +390,10 @@ enum {
    * the first also the embedding, in stream order, so tiles of earlier
    * launches are complete before a later one starts; results are identical bit
    * for bit.  Needs a single-step queue with one sub-queue per worker and at
-   * most L launches (else MK_ENOTSUP). */
+   * most L launches (else MK_ENOTSUP).  An error recorded by one launch stops
+   * it; each worker of a later launch of the step then spends at most one
+   * barrier spin limit before it stops too, and mk_device_error reports the
+   * first error. */
   MK_OPT_MEGAKERNELS = 8,
   /* mk_prefill: which GEMMs take both bf16 parts (hi, lo) of their fp32
    * activations, a bit mask (1 QKV, 2 O-projection, 4 gate/up, 8 down; default
