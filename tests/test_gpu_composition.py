@@ -134,3 +134,31 @@ def test_composition_refusals():
     assert e.value.status == T.MK_ENOTSUP
     T.mk_set_option(T.MK_OPT_MEGAKERNELS, 1)
     _run(c, 1)
+
+
+def test_composition_through_the_static_scratch_entry():
+    """mk_decode_step_static runs the same compositions: with two launches per
+    step its logits, argmax and new cache entries equal one launch on a
+    caller-allocated workspace, bit for bit."""
+    from _gpucase import make_case
+    c = make_case(_cases()["bf16_1b_b1_merge_last"], gain_jitter=0.1)
+    assert c.q.workspace_nbytes() <= T.MK_STATIC_SCRATCH_BYTES
+    ref = _run(c, 1)
+    B = c.wl.run.batch
+    c.reset_kv()
+    lg = torch.full_like(c.logits, float("nan"))
+    nx = torch.full_like(c.nxt, -1)
+    err = torch.full((8,), 0xFFFF, dtype=torch.int32, device="cuda")
+    tok = torch.from_numpy(c.tokens[0].astype(np.int32)).cuda()
+    cl = torch.tensor(list(c.wl.run.ctx0), dtype=torch.int32, device="cuda")
+    T.mk_set_option(T.MK_OPT_MEGAKERNELS, 2)
+    try:
+        T.mk_decode_step_static(c.q, c.dq, c.dm.w, c.dkv.kv, tok, None, cl, B, lg, nx, err, T.MK_MEGAKERNEL)
+        torch.cuda.synchronize()
+    finally:
+        T.mk_set_option(T.MK_OPT_MEGAKERNELS, 1)
+    assert (err.cpu().numpy() == 0).all()
+    k, v = c.kv_host()
+    assert np.array_equal(lg.cpu().numpy(), ref["logits"])
+    assert np.array_equal(nx.cpu().numpy(), ref["next"])
+    assert np.array_equal(k, ref["k"]) and np.array_equal(v, ref["v"])
